@@ -1,0 +1,255 @@
+"""CPU oracle for the BitLinear forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it.
+
+The arithmetic lives in ``ugref.c`` (plain scalar loops, fp32 in the fixed
+orders documented there); this module only marshals numpy arrays in and out
+through ctypes.  Each function cites the passage of the pages it follows:
+
+* "ultragraph - when the graph is the 1-bit LLM, part 2", section
+  "the bytes" -- absmean ternary weights, per-row absmax int8 activations,
+  the [-127, 127] range, dequantization by one scalar multiply;
+* same page, section "autograd on a byte-graph" -- y = (x_q W_q^T)(s beta);
+* same page, section "attention, as graph ops" -- RMSNorm with fp32 gain;
+* "ultragraph-1bit 0.12.0" README, sections "A whole ternary GPT" and
+  "Layout" -- five ternary values per byte.
+
+Parity unpinned: the exact fp32 bits of the RMSNorm output (and so of
+``rmsnorm_quant_act``) and of beta are fixed only by the summation orders this
+oracle states; the pages give no order.  Their pins are bounds (fsum within
+the rounding-error bound, float64 RMSNorm within its bound) and exact special
+cases, not exact bits.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_i8p = ctypes.POINTER(ctypes.c_int8)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+        _build.build()
+    lib = ctypes.CDLL(path)
+    sig = {
+        "ugref_quant_act": (None, [_f32p, _i64, _i64, _i64, _f32, _i8p, _i64, _f32p]),
+        "ugref_rmsnorm": (None, [_f32p, _i64, _f32p, _i64, _i64, _f32, _f32p, _i64]),
+        "ugref_row_sum_squares": (_f32, [_f32p, _i64]),
+        "ugref_rmsnorm_quant_act": (None, [_f32p, _i64, _f32p, _i64, _i64, _f32, _f32,
+                                           _i8p, _i64, _f32p]),
+        "ugref_absmean_sum": (_f32, [_f32p, _i64, _i64, _i64, _f32p]),
+        "ugref_quant_weight_absmean": (None, [_f32p, _i64, _i64, _i64, _f32, _i8p, _i64,
+                                              _f32p]),
+        "ugref_pack_trits": (_i64, [_i8p, _i64, _i64, _i64, _u8p, _i64]),
+        "ugref_unpack_trits": (_i64, [_u8p, _i64, _i64, _i64, _i8p, _i64]),
+        "ugref_matmul_i32": (None, [_i8p, _i64, _i8p, _i64, _i64, _i64, _i64, _i32p, _i64]),
+        "ugref_matmul_i32_pairs": (None, [_i8p, _i64, _i8p, _i64, _i64, _i64p, _i64p, _i64,
+                                          _i32p]),
+        "ugref_epilogue": (None, [_i32p, _i64, _f32p, _f32, _i64, _i64, _f32p, _i64]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _c2d(a, dtype):
+    a = np.asarray(a)
+    if a.dtype != dtype:
+        raise TypeError("expected %s, got %s" % (dtype, a.dtype))
+    if a.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    return np.ascontiguousarray(a)
+
+
+def quant_act(x, eps=1e-5):
+    """Per-row absmax int8 quantization ("the bytes": s = max|x|/127 + eps,
+    x_q = clip(round(x/s), -127, 127)).  Returns (x_q int8 [M,K], s fp32 [M])."""
+    x = _c2d(x, np.float32)
+    M, K = x.shape
+    xq = np.empty((M, K), np.int8)
+    s = np.empty(M, np.float32)
+    _load().ugref_quant_act(_ptr(x, ctypes.c_float), K, M, K, float(np.float32(eps)),
+                            _ptr(xq, ctypes.c_int8), K, _ptr(s, ctypes.c_float))
+    return xq, s
+
+
+def row_sum_squares(x_row):
+    """Sum of squares of one row in the fixed slot order used by rmsnorm()."""
+    x = np.ascontiguousarray(np.asarray(x_row, np.float32).reshape(-1))
+    return np.float32(_load().ugref_row_sum_squares(_ptr(x, ctypes.c_float), x.size))
+
+
+def rmsnorm(x, g=None, eps_n=1e-5):
+    """RMSNorm with fp32 gain ("attention, as graph ops"):
+    x / sqrt(mean(x^2) + eps) * g.  g=None means ones."""
+    x = _c2d(x, np.float32)
+    M, K = x.shape
+    gp = None
+    if g is not None:
+        g = np.ascontiguousarray(np.asarray(g, np.float32).reshape(K))
+        gp = _ptr(g, ctypes.c_float)
+    xn = np.empty((M, K), np.float32)
+    _load().ugref_rmsnorm(_ptr(x, ctypes.c_float), K, gp, M, K, float(np.float32(eps_n)),
+                          _ptr(xn, ctypes.c_float), K)
+    return xn
+
+
+def rmsnorm_quant_act(x, g=None, eps_n=1e-5, eps=1e-5):
+    """RMSNorm followed by per-row absmax quantization of its output."""
+    x = _c2d(x, np.float32)
+    M, K = x.shape
+    gp = None
+    if g is not None:
+        g = np.ascontiguousarray(np.asarray(g, np.float32).reshape(K))
+        gp = _ptr(g, ctypes.c_float)
+    xq = np.empty((M, K), np.int8)
+    s = np.empty(M, np.float32)
+    _load().ugref_rmsnorm_quant_act(_ptr(x, ctypes.c_float), K, gp, M, K,
+                                    float(np.float32(eps_n)), float(np.float32(eps)),
+                                    _ptr(xq, ctypes.c_int8), K, _ptr(s, ctypes.c_float))
+    return xq, s
+
+
+def absmean_sum(W, return_chunks=False):
+    """Sum of |W| over the whole tensor in the fixed two-stage order."""
+    W = _c2d(W, np.float32)
+    N, K = W.shape
+    nchunks = -(-(N * K) // 8192)
+    S = np.empty(max(nchunks, 1), np.float32)
+    T = np.float32(_load().ugref_absmean_sum(_ptr(W, ctypes.c_float), K, N, K,
+                                             _ptr(S, ctypes.c_float)))
+    return (T, S[:nchunks]) if return_chunks else T
+
+
+def quant_weight_absmean(W, eps=1e-5):
+    """Absmean ternary quantization ("the bytes": beta = mean|W| + eps,
+    W_q = clip(round(W/beta), -1, 1)).  Returns (W_q int8 [N,K], beta fp32)."""
+    W = _c2d(W, np.float32)
+    N, K = W.shape
+    wq = np.empty((N, K), np.int8)
+    beta = np.empty(1, np.float32)
+    _load().ugref_quant_weight_absmean(_ptr(W, ctypes.c_float), K, N, K,
+                                       float(np.float32(eps)), _ptr(wq, ctypes.c_int8), K,
+                                       _ptr(beta, ctypes.c_float))
+    return wq, beta[0]
+
+
+def packed_pitch(K, align=16):
+    """Smallest row pitch in bytes >= ceil(K/5) that is a multiple of align."""
+    g = -(-K // 5)
+    return -(-g // align) * align
+
+
+def pack_trits(wq, ldp=None):
+    """Five trits per byte (README "A whole ternary GPT", pack.py).
+    Returns (packed uint8 [N, ldp], number of entries outside {-1,0,1})."""
+    wq = _c2d(wq, np.int8)
+    N, K = wq.shape
+    if ldp is None:
+        ldp = packed_pitch(K)
+    packed = np.empty((N, ldp), np.uint8)
+    bad = _load().ugref_pack_trits(_ptr(wq, ctypes.c_int8), K, N, K,
+                                   _ptr(packed, ctypes.c_uint8), ldp)
+    return packed, int(bad)
+
+
+def unpack_trits(packed, K):
+    """Inverse of pack_trits.  Returns (W_q int8 [N,K], number of codes > 242)."""
+    packed = _c2d(packed, np.uint8)
+    N, ldp = packed.shape
+    wq = np.empty((N, K), np.int8)
+    bad = _load().ugref_unpack_trits(_ptr(packed, ctypes.c_uint8), ldp, N, K,
+                                     _ptr(wq, ctypes.c_int8), K)
+    return wq, int(bad)
+
+
+def matmul_i32(xq, wq):
+    """acc = x_q W_q^T in exact integers ("autograd on a byte-graph")."""
+    xq = _c2d(xq, np.int8)
+    wq = _c2d(wq, np.int8)
+    M, K = xq.shape
+    N, K2 = wq.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    acc = np.empty((M, N), np.int32)
+    _load().ugref_matmul_i32(_ptr(xq, ctypes.c_int8), K, _ptr(wq, ctypes.c_int8), K,
+                             M, N, K, _ptr(acc, ctypes.c_int32), N)
+    return acc
+
+
+def matmul_i32_pairs(xq, wq, mi, ni):
+    """acc[mi[p], ni[p]] for a list of index pairs."""
+    xq = _c2d(xq, np.int8)
+    wq = _c2d(wq, np.int8)
+    K = xq.shape[1]
+    if wq.shape[1] != K:
+        raise ValueError("K mismatch")
+    mi = np.ascontiguousarray(np.asarray(mi, np.int64))
+    ni = np.ascontiguousarray(np.asarray(ni, np.int64))
+    if mi.shape != ni.shape:
+        raise ValueError("index shape mismatch")
+    out = np.empty(mi.size, np.int32)
+    _load().ugref_matmul_i32_pairs(_ptr(xq, ctypes.c_int8), K, _ptr(wq, ctypes.c_int8), K,
+                                   K, _ptr(mi, ctypes.c_int64), _ptr(ni, ctypes.c_int64),
+                                   mi.size, _ptr(out, ctypes.c_int32))
+    return out
+
+
+def epilogue(acc, s, beta):
+    """y = fl((float)acc * fl(s * beta)) -- the rescale of
+    y = (x_q W_q^T)(s beta)."""
+    acc = _c2d(acc, np.int32)
+    M, N = acc.shape
+    s = np.ascontiguousarray(np.asarray(s, np.float32).reshape(M))
+    y = np.empty((M, N), np.float32)
+    _load().ugref_epilogue(_ptr(acc, ctypes.c_int32), N, _ptr(s, ctypes.c_float),
+                           float(np.float32(beta)), M, N, _ptr(y, ctypes.c_float), N)
+    return y
+
+
+def bitlinear(x, W, eps=1e-5):
+    """The whole forward: quantize x per row and W by absmean, integer
+    matmul, rescale.  Returns dict of every intermediate."""
+    xq, s = quant_act(x, eps)
+    wq, beta = quant_weight_absmean(W, eps)
+    acc = matmul_i32(xq, wq)
+    y = epilogue(acc, s, beta)
+    return dict(xq=xq, s=s, wq=wq, beta=beta, acc=acc, y=y)
+
+
+def num_threads():
+    """Threads OpenMP will use for the oracle in this process."""
+    v = os.environ.get("OMP_NUM_THREADS")
+    if v:
+        try:
+            return int(v)
+        except ValueError:
+            pass
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1

@@ -1,0 +1,364 @@
+/*
+ * ugref -- the CPU oracle for the BitLinear forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code, header, table or helper with the HIP
+ * library: everything below is written out as plain scalar loops so that a
+ * reader can check it against the pages by eye.
+ *
+ * Sources (the pages are the authority on what is computed):
+ *   - "ultragraph - when the graph is the 1-bit LLM, part 2", section
+ *     "the bytes": absmean ternary weight quantization (beta = mean|W| + eps,
+ *     W_q = clip(round(W/beta), -1, 1)), dequantization as one scalar
+ *     multiply, and per-row absmax int8 activation quantization
+ *     (s = max|x|/127 + eps, x_q = clip(round(x/s), -127, 127)), with the
+ *     symmetric range [-127, 127].
+ *   - same page, section "autograd on a byte-graph": the integer forward
+ *     y = (x_q W_q^T)(s beta) (+ b; no bias here).
+ *   - same page, section "attention, as graph ops": RMSNorm with a learnable
+ *     fp32 gain, and the per-token (per-row) scale.
+ *   - "ultragraph-1bit 0.12.0" README, sections "A whole ternary GPT" and
+ *     "Layout" (pack.py): weights stored 5 ternary values per byte.
+ *
+ * Readings where the pages leave a step open (each is listed in the design
+ * document):
+ *   - every floating-point step is one IEEE-754 binary32 operation with
+ *     round-to-nearest-even; no FMA contraction (built with
+ *     -ffp-contract=off), no flush-to-zero;
+ *   - round() is round-half-to-even (rintf in the default rounding mode);
+ *   - s = fl(fl(a / 127) + eps) and beta = fl(fl(T / n) + eps), divisions
+ *     correctly rounded, never a reciprocal multiply;
+ *   - the whole-tensor sum of |W| and the per-row sum of squares are
+ *     added in the fixed orders spelled out at absmean_sum() and
+ *     rmsnorm_row() below;
+ *   - the 5-trits-per-byte code of trits t_0..t_4 (t_0 at the lowest K) is
+ *     121 + sum_j t_j 3^j; trits past K are 0; row bytes past ceil(K/5) are
+ *     121; codes 243..255 are invalid and decode to five zero trits;
+ *   - y = fl((float)acc * fl(s * beta)).
+ *
+ * OpenMP runs only over independent rows or independent chunks, so every
+ * result is bit-identical at any thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* ------------------------------------------------------------------ */
+/* Activation quantization (per-token absmax)                           */
+/* ------------------------------------------------------------------ */
+
+/* One row: a = max|x_k|; s = fl(fl(a/127) + eps);
+ * x_q[k] = clamp(rint(fl(x_k / s)), -127, 127). */
+static float quant_act_row(const float *x, int64_t K, float eps, int8_t *xq)
+{
+    float a = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float v = fabsf(x[k]);
+        if (v > a)
+            a = v;
+    }
+    float a_over = a / 127.0f;
+    float s = a_over + eps;
+    for (int64_t k = 0; k < K; ++k) {
+        float q = x[k] / s;
+        float r = rintf(q);
+        if (r > 127.0f)
+            r = 127.0f;
+        if (r < -127.0f)
+            r = -127.0f;
+        xq[k] = (int8_t)r;
+    }
+    return s;
+}
+
+void ugref_quant_act(const float *x, int64_t ldx, int64_t M, int64_t K,
+                     float eps, int8_t *xq, int64_t ldq, float *s)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        s[m] = quant_act_row(x + m * ldx, K, eps, xq + m * ldq);
+}
+
+/* ------------------------------------------------------------------ */
+/* RMSNorm (fp32 gain) feeding the activation quantizer                */
+/* ------------------------------------------------------------------ */
+
+/* Sum of squares of one row in the fixed order used throughout:
+ * element k belongs to slot t = floor(k/4) mod 256; each slot adds its
+ * fl(x_k * x_k) from +0 in increasing k; then the 256 slots are folded
+ * pairwise, slot t += slot t+h for h = 128, 64, ..., 1. */
+static float row_sum_squares(const float *x, int64_t K)
+{
+    float p[256];
+    for (int t = 0; t < 256; ++t)
+        p[t] = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        int t = (int)((k / 4) % 256);
+        float sq = x[k] * x[k];
+        p[t] = p[t] + sq;
+    }
+    for (int h = 128; h >= 1; h /= 2)
+        for (int t = 0; t < h; ++t)
+            p[t] = p[t] + p[t + h];
+    return p[0];
+}
+
+/* RMSNorm(x) = x / sqrt(mean(x^2) + eps_n) * g, with
+ * ms = fl(T / K), r = sqrt(fl(ms + eps_n)) correctly rounded,
+ * x_n = fl(fl(x / r) * g).  g == NULL means a gain of ones. */
+static void rmsnorm_row(const float *x, const float *g, int64_t K,
+                        float eps_n, float *xn)
+{
+    float T = row_sum_squares(x, K);
+    float ms = T / (float)K;
+    float r = sqrtf(ms + eps_n);
+    for (int64_t k = 0; k < K; ++k) {
+        float v = x[k] / r;
+        xn[k] = g ? v * g[k] : v;
+    }
+}
+
+void ugref_rmsnorm(const float *x, int64_t ldx, const float *g, int64_t M,
+                   int64_t K, float eps_n, float *xn, int64_t ldn)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        rmsnorm_row(x + m * ldx, g, K, eps_n, xn + m * ldn);
+}
+
+float ugref_row_sum_squares(const float *x, int64_t K)
+{
+    return row_sum_squares(x, K);
+}
+
+void ugref_rmsnorm_quant_act(const float *x, int64_t ldx, const float *g,
+                             int64_t M, int64_t K, float eps_n, float eps,
+                             int8_t *xq, int64_t ldq, float *s)
+{
+#pragma omp parallel
+    {
+        float *xn = (float *)malloc((size_t)(K > 0 ? K : 1) * sizeof(float));
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            rmsnorm_row(x + m * ldx, g, K, eps_n, xn);
+            s[m] = quant_act_row(xn, K, eps, xq + m * ldq);
+        }
+        free(xn);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Absmean ternary weight quantization                                 */
+/* ------------------------------------------------------------------ */
+
+#define UGREF_CHUNK 8192
+
+/* |W| of flat element e of the row-major [N, K] matrix (pitch ldw);
+ * elements at or past n = N*K are +0. */
+static float abs_at(const float *W, int64_t ldw, int64_t K, int64_t n,
+                    int64_t e)
+{
+    if (e >= n)
+        return 0.0f;
+    int64_t row = e / K, col = e % K;
+    return fabsf(W[row * ldw + col]);
+}
+
+/* Stage 1 of the fixed summation order: chunk c holds flat elements
+ * [8192c, 8192c + 8192).  Lane t in [0,256) keeps four running sums
+ * acc_j, j in [0,4); for i = 0..7 it adds element 8192c + 1024i + 4t + j
+ * to acc_j.  Lane t's value is fl(fl(acc_0+acc_1) + fl(acc_2+acc_3));
+ * the 256 lane values are folded pairwise (t += t+h, h = 128..1). */
+static float chunk_sum(const float *W, int64_t ldw, int64_t K, int64_t n,
+                       int64_t c)
+{
+    float p[256];
+    for (int t = 0; t < 256; ++t) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < 8; ++i)
+            for (int j = 0; j < 4; ++j) {
+                int64_t e = c * UGREF_CHUNK + 1024 * (int64_t)i + 4 * t + j;
+                acc[j] = acc[j] + abs_at(W, ldw, K, n, e);
+            }
+        float lo = acc[0] + acc[1];
+        float hi = acc[2] + acc[3];
+        p[t] = lo + hi;
+    }
+    for (int h = 128; h >= 1; h /= 2)
+        for (int t = 0; t < h; ++t)
+            p[t] = p[t] + p[t + h];
+    return p[0];
+}
+
+/* Stage 2: lane t in [0,256) adds the chunk sums t, t+256, t+512, ...
+ * from +0 in that order; the lanes are folded pairwise as above. */
+static float combine_chunks(const float *S, int64_t nchunks)
+{
+    float p[256];
+    for (int t = 0; t < 256; ++t) {
+        float acc = 0.0f;
+        for (int64_t c = t; c < nchunks; c += 256)
+            acc = acc + S[c];
+        p[t] = acc;
+    }
+    for (int h = 128; h >= 1; h /= 2)
+        for (int t = 0; t < h; ++t)
+            p[t] = p[t] + p[t + h];
+    return p[0];
+}
+
+/* T = sum |W| over the whole N x K tensor in the order above.  The
+ * per-chunk sums are also returned through S when S is not NULL. */
+float ugref_absmean_sum(const float *W, int64_t ldw, int64_t N, int64_t K,
+                        float *S_out)
+{
+    int64_t n = N * K;
+    int64_t nchunks = (n + UGREF_CHUNK - 1) / UGREF_CHUNK;
+    float *S = (float *)malloc((size_t)(nchunks > 0 ? nchunks : 1) * sizeof(float));
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < nchunks; ++c)
+        S[c] = chunk_sum(W, ldw, K, n, c);
+    float T = combine_chunks(S, nchunks);
+    if (S_out)
+        for (int64_t c = 0; c < nchunks; ++c)
+            S_out[c] = S[c];
+    free(S);
+    return T;
+}
+
+/* beta = fl(fl(T / (float)n) + eps);
+ * W_q = clamp(rint(fl(W / beta)), -1, 1), one byte per trit. */
+void ugref_quant_weight_absmean(const float *W, int64_t ldw, int64_t N,
+                                int64_t K, float eps, int8_t *wq, int64_t ldq,
+                                float *beta_out)
+{
+    float T = ugref_absmean_sum(W, ldw, N, K, NULL);
+    float mean = T / (float)(N * K);
+    float beta = mean + eps;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < N; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            float q = W[r * ldw + k] / beta;
+            float t = rintf(q);
+            if (t > 1.0f)
+                t = 1.0f;
+            if (t < -1.0f)
+                t = -1.0f;
+            wq[r * ldq + k] = (int8_t)t;
+        }
+    *beta_out = beta;
+}
+
+/* ------------------------------------------------------------------ */
+/* Five trits per byte                                                 */
+/* ------------------------------------------------------------------ */
+
+/* Row n, byte g holds the trits of K positions 5g .. 5g+4:
+ * code = 121 + t_0 + 3 t_1 + 9 t_2 + 27 t_3 + 81 t_4 (trits past K are 0).
+ * Bytes g in [ceil(K/5), ldp) are 121.  An entry outside {-1,0,1} is
+ * counted and packed as its value clamped to [-1, 1].  Returns the count. */
+int64_t ugref_pack_trits(const int8_t *wq, int64_t ldq, int64_t N, int64_t K,
+                         uint8_t *packed, int64_t ldp)
+{
+    int64_t groups = (K + 4) / 5;
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t r = 0; r < N; ++r) {
+        for (int64_t g = 0; g < ldp; ++g) {
+            int code = 121;
+            if (g < groups) {
+                int pow3 = 1;
+                for (int j = 0; j < 5; ++j) {
+                    int64_t k = 5 * g + j;
+                    int t = 0;
+                    if (k < K) {
+                        t = wq[r * ldq + k];
+                        if (t < -1 || t > 1) {
+                            ++bad;
+                            t = t < -1 ? -1 : 1;
+                        }
+                    }
+                    code += t * pow3;
+                    pow3 *= 3;
+                }
+            }
+            packed[r * ldp + g] = (uint8_t)code;
+        }
+    }
+    return bad;
+}
+
+/* Inverse of ugref_pack_trits for the first K positions of each row.
+ * A code above 242 among the first ceil(K/5) bytes of a row is counted and
+ * decodes to five zero trits.  Returns the count. */
+int64_t ugref_unpack_trits(const uint8_t *packed, int64_t ldp, int64_t N,
+                           int64_t K, int8_t *wq, int64_t ldq)
+{
+    int64_t groups = (K + 4) / 5;
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t r = 0; r < N; ++r) {
+        for (int64_t g = 0; g < groups; ++g) {
+            int code = packed[r * ldp + g];
+            if (code > 242) {
+                ++bad;
+                code = 121;
+            }
+            int digits = code; /* base-3 digits d_j = t_j + 1 */
+            for (int j = 0; j < 5; ++j) {
+                int64_t k = 5 * g + j;
+                int d = digits % 3;
+                digits /= 3;
+                if (k < K)
+                    wq[r * ldq + k] = (int8_t)(d - 1);
+            }
+        }
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------ */
+/* Integer matmul and the rescale                                      */
+/* ------------------------------------------------------------------ */
+
+/* acc[m][n] = sum_k x_q[m][k] * W_q[n][k], exact in integers. */
+void ugref_matmul_i32(const int8_t *xq, int64_t ldx, const int8_t *wq,
+                      int64_t ldw, int64_t M, int64_t N, int64_t K,
+                      int32_t *acc, int64_t ldacc)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; ++k)
+                sum += (int64_t)xq[m * ldx + k] * (int64_t)wq[n * ldw + k];
+            acc[m * ldacc + n] = (int32_t)sum;
+        }
+}
+
+/* The same sums for a list of (m, n) pairs only. */
+void ugref_matmul_i32_pairs(const int8_t *xq, int64_t ldx, const int8_t *wq,
+                            int64_t ldw, int64_t K, const int64_t *mi,
+                            const int64_t *ni, int64_t count, int32_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < count; ++p) {
+        int64_t sum = 0;
+        for (int64_t k = 0; k < K; ++k)
+            sum += (int64_t)xq[mi[p] * ldx + k] * (int64_t)wq[ni[p] * ldw + k];
+        out[p] = (int32_t)sum;
+    }
+}
+
+/* y[m][n] = fl((float)acc[m][n] * fl(s[m] * beta)). */
+void ugref_epilogue(const int32_t *acc, int64_t ldacc, const float *s,
+                    float beta, int64_t M, int64_t N, float *y, int64_t ldy)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float scale = s[m] * beta;
+        for (int64_t n = 0; n < N; ++n)
+            y[m * ldy + n] = (float)acc[m * ldacc + n] * scale;
+    }
+}
