@@ -1,0 +1,301 @@
+"""Benchmark of the BitLinear forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  Workloads (default: decode_stack):
+  decode_stack  batch-1 decode pass over 8 x {384->1152, 384->384,
+                384->1536, 1536->384} + a 384->4096 head, weights 5 trits per
+                byte; a step = per-row int8 quantization of each matrix's input
+                plus the GEMV of every matrix (33 x); each step reads its own
+                copy of the weights so they stream from HBM (cold).
+                value = packed-weight GB/s.
+  sweep         decode GEMV at M in {1,4,16,64} x the three 2B-class shapes
+                (cold, cycling weight copies); value = weight GB/s over all
+                12 points.
+  prefill       M=4096 act quant + int8 MFMA GEMM for 2560->6912 and
+                6912->2560; value = int8 TOP/s.
+  stack         30 layers x {2560->6912, 6912->2560}: requantize the fp32
+                masters, RMSNorm + act quant + GEMM chained at M=2048;
+                value = int8 TOP/s of the whole step.
+  tiny          x[32,128] W[512,128]: the full path incl. weight quant.
+
+Inputs are seeded synthetic tensors (bitlinear_matmul_amd.inputs) already
+resident in HBM when timing starts.  Timing: W untimed steps, then K steps
+between torch.cuda.synchronize() calls (HIP events on the stream the
+kernels run on).  The dominant kernel's roofline fraction uses algorithmic
+bytes (or ops) per launch over its average launch duration, measured here
+with HIP events.  The CPU oracle is timed on a bounded sample of the same
+workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "BitLinear GEMV weight GB/s (decode) and GEMM int8 TOPS (prefill), % roofline"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+COLD_BYTES = 2 << 30  # weight copies to cycle through: >= 8x the 256 MB MALL
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", default="decode_stack",
+                   choices=["decode_stack", "sweep", "prefill", "stack", "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+def time_graph(torch, g, stream):
+    """Replay a captured graph once between events on its stream; ms."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def capture(torch, fn):
+    """Capture fn() (which launches libug kernels on the current stream)
+    into a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+# ---------------------------------------------------------------------------
+# decode_stack
+# ---------------------------------------------------------------------------
+def setup_decode_stack(torch, ug, inputs, n_copies):
+    dev = torch.device("cuda:0")
+    mats = []
+    for (layer, mi, name, K, N) in inputs.decode_stack_shapes():
+        x, W = inputs.decode_stack_matrix(layer, mi, K, N)
+        Wd = torch.from_numpy(W).to(dev)
+        wq, beta = ug.ug_quant_weight_absmean(Wd)
+        pk = ug.ug_pack_trits(wq)
+        mats.append(dict(K=K, N=N, x=torch.from_numpy(x).to(dev), pk0=pk, beta=beta,
+                         xq=ug.empty_pitched(1, K, torch.int8, dev),
+                         s=torch.empty(1, dtype=torch.float32, device=dev),
+                         y=ug.empty_pitched(1, N, torch.float32, dev),
+                         W=W, x_host=x))
+        del Wd, wq
+    # weight copies (cold streaming): copy c of matrix i
+    for m in mats:
+        m["pk"] = [m["pk0"]] + [m["pk0"].clone() for _ in range(n_copies - 1)]
+    torch.cuda.synchronize()
+    per_pass_bytes = sum(m["N"] * (-(-m["K"] // 5)) for m in mats)
+    return mats, per_pass_bytes
+
+
+def decode_stack_pass(ug, mats, c, gemv_only=False):
+    for m in mats:
+        if not gemv_only:
+            ug.ug_quant_act(m["x"], 1e-5, xq=m["xq"], s=m["s"])
+        ug.ug_bitlinear_gemv(m["xq"], m["s"], m["pk"][c], ug.UG_W_PACK5, m["beta"], K=m["K"],
+                             y=m["y"])
+
+
+def gemv_alg_bytes(M, N, K, packed=True):
+    wb = N * (-(-K // 5)) if packed else N * K
+    return wb + M * K + 4 * M + 4 + 4 * M * N
+
+
+def cpu_decode_stack(oracle, mats, seconds):
+    # oracle state: quantized weights of each matrix (setup, untimed)
+    prep = []
+    for m in mats:
+        wq, beta = oracle.quant_weight_absmean(m["W"])
+        pk, _ = oracle.pack_trits(wq)
+        prep.append((m["x_host"], pk, m["K"], beta))
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for (x, pk, K, beta) in prep:
+            xq, s = oracle.quant_act(x)
+            wq, _ = oracle.unpack_trits(pk, K)
+            oracle.epilogue(oracle.matmul_i32(xq, wq), s, beta)
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return passes, time.perf_counter() - t0
+
+
+def run_decode_stack(args, torch, ug, inputs):
+    steps = args.steps if args.steps is not None else 200
+    warm = args.warmup if args.warmup is not None else 20
+    # bytes of one stored copy
+    per_copy = sum(N * ug.packed_pitch(K) for (_, _, _, K, N) in inputs.decode_stack_shapes())
+    n_copies = min(max(1, COLD_BYTES // per_copy), warm + steps)
+    mats, per_pass_bytes = setup_decode_stack(torch, ug, inputs, n_copies)
+    log("decode_stack: %d matrices, %d packed weight bytes per pass, %d copies"
+        % (len(mats), per_pass_bytes, n_copies))
+    g_warm = capture(torch, lambda: [decode_stack_pass(ug, mats, c % n_copies)
+                                     for c in range(warm)])
+    g_run = capture(torch, lambda: [decode_stack_pass(ug, mats, (warm + c) % n_copies)
+                                    for c in range(steps)])
+    g_gemv = capture(torch, lambda: [decode_stack_pass(ug, mats, (warm + c) % n_copies, True)
+                                     for c in range(steps)])
+    stream = torch.cuda.current_stream()
+    time_graph(torch, g_warm, stream)
+    ms = time_graph(torch, g_run, stream)
+    log("decode_stack: %d steps in %.3f ms" % (steps, ms))
+    # dominant kernel: the GEMV, timed alone (33 launches per pass)
+    gemv_ms = time_graph(torch, g_gemv, stream)
+    launches = steps * len(mats)
+    gemv_bytes = sum(gemv_alg_bytes(1, m["N"], m["K"]) for m in mats) * steps
+    avg_launch_s = gemv_ms / 1e3 / launches
+    achieved = gemv_bytes / launches / avg_launch_s / 1e9
+    value = per_pass_bytes * steps / (ms / 1e3) / 1e9
+    out = dict(value=value, unit="GB/s", ms_per_step=ms / steps, steps=steps, warmup=warm,
+               dtype="int8xtrit->int32, f32 scale",
+               config={"workload": "decode_stack", "batch": 1, "matrices": len(mats),
+                       "weight_format": "pack5", "packed_weight_bytes_per_step": per_pass_bytes,
+                       "weight_copies_cycled": n_copies, "regime": "cold (HBM)",
+                       "us_per_token_pass": ms * 1e3 / steps},
+               roofline=dict(bound="hbm", kernel="gemv_kernel<PACK5>", achieved=achieved,
+                             peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
+                             traffic=None, avg_launch_us=avg_launch_s * 1e6,
+                             alg_bytes_per_launch=gemv_bytes / launches))
+    if not args.no_cpu_baseline:
+        import oracle
+        passes, secs = cpu_decode_stack(oracle, mats, args.cpu_seconds)
+        out["cpu_baseline"] = dict(value=per_pass_bytes * passes / secs / 1e9, unit="GB/s",
+                                   cores=oracle.num_threads(), kind="oracle",
+                                   sample="%d full decode passes (33 x quant + unpack + int "
+                                          "matmul + rescale) in %.1f s" % (passes, secs))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def run_prefill(args, torch, ug, inputs):
+    steps = args.steps if args.steps is not None else 20
+    warm = args.warmup if args.warmup is not None else 3
+    dev = torch.device("cuda:0")
+    layers = []
+    for j in (0, 1):
+        x, W, _ = inputs.prefill_inputs(j)
+        K, N = inputs.PREFILL_SHAPES[j]
+        wq, beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
+        layers.append(dict(K=K, N=N, x=torch.from_numpy(x).to(dev), wq=wq, beta=beta,
+                           xq=ug.empty_pitched(x.shape[0], K, torch.int8, dev),
+                           s=torch.empty(x.shape[0], dtype=torch.float32, device=dev),
+                           y=ug.empty_pitched(x.shape[0], N, torch.float32, dev),
+                           x_host=x, W=W))
+    M = inputs.PREFILL_M
+    ops_per_step = sum(2 * M * l["N"] * l["K"] for l in layers)
+
+    def step():
+        for l in layers:
+            ug.ug_quant_act(l["x"], 1e-5, xq=l["xq"], s=l["s"])
+            ug.ug_bitlinear_gemm(l["xq"], l["s"], l["wq"], ug.UG_W_I8, l["beta"], y=l["y"])
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    # GEMM alone
+    e0.record(stream)
+    for _ in range(steps):
+        for l in layers:
+            ug.ug_bitlinear_gemm(l["xq"], l["s"], l["wq"], ug.UG_W_I8, l["beta"], y=l["y"])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / (2 * steps)
+    achieved = ops_per_step / 2 / (gemm_ms / 1e3) / 1e12
+    out = dict(value=ops_per_step * steps / (ms / 1e3) / 1e12, unit="TOP/s",
+               ms_per_step=ms / steps, steps=steps, warmup=warm, dtype="int8 MFMA -> int32",
+               config={"workload": "prefill", "M": M, "shapes_KxN": [[l["K"], l["N"]]
+                                                                     for l in layers],
+                       "weight_format": "i8"},
+               roofline=dict(bound="mfma", kernel="gemm_i8_kernel", achieved=achieved,
+                             peak=INT8_PEAK_TOPS, unit="TOP/s", frac=achieved / INT8_PEAK_TOPS,
+                             traffic=None, avg_launch_us=gemm_ms * 1e3,
+                             alg_ops_per_launch=ops_per_step / 2))
+    if not args.no_cpu_baseline:
+        import oracle
+        # bounded sample: the first rows of each layer's x through the oracle
+        rows = 0
+        t0 = time.perf_counter()
+        ops = 0
+        prep = [(l["x_host"], oracle.quant_weight_absmean(l["W"])) for l in layers]
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds and rows < M:
+            for (x, (wq, beta)) in prep:
+                xq, s = oracle.quant_act(x[rows:rows + 64])
+                oracle.epilogue(oracle.matmul_i32(xq, wq), s, beta)
+                ops += 2 * xq.shape[0] * wq.shape[0] * wq.shape[1]
+            rows += 64
+        secs = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(value=ops / secs / 1e12, unit="TOP/s",
+                                   cores=oracle.num_threads(), kind="oracle",
+                                   sample="first %d of 4096 rows of both layers (quant + int "
+                                          "matmul + rescale) in %.1f s" % (rows, secs))
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from bitlinear_matmul_amd import inputs, ug
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ug.lib()
+    runners = {"decode_stack": run_decode_stack, "prefill": run_prefill}
+    if args.workload not in runners:
+        print("workload %s not implemented yet" % args.workload, file=sys.stderr)
+        sys.exit(2)
+    res = runners[args.workload](args, torch, ug, inputs)
+    line = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+            "steps": res["steps"], "warmup": res["warmup"], "ms_per_step": res["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
+            "config": res["config"], "roofline": res["roofline"]}
+    if "cpu_baseline" in res:
+        line["cpu_baseline"] = res["cpu_baseline"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

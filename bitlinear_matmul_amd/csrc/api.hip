@@ -1,0 +1,174 @@
+// extern "C" entry points of libug: argument validation, then the kernel
+// launches on the caller's stream.  Every argument error is reported before
+// anything is launched; no entry point allocates or synchronizes.
+#include <cmath>
+#include <cstdint>
+
+#include "ug_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline ug_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return UG_OK;
+  g_last_hip_error = (int32_t)e;
+  return UG_ERR_HIP;
+}
+
+// Pointer present and 16-byte aligned.
+inline bool ptr_ok(const void *p) { return p != nullptr && aligned16(p); }
+// Optional pointer: absent, or 16-byte aligned.
+inline bool opt_ok(const void *p) { return p == nullptr || aligned16(p); }
+// Optional 4-byte counter.
+inline bool counter_ok(const void *p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
+// A present fp32 scalar/vector (s, beta): 4-byte alignment is enough.
+inline bool f32_ok(const void *p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
+
+inline bool eps_ok(float e) { return std::isfinite(e) && e > 0.0f; }
+
+// Pitch checks: ld >= cols and a multiple of `mult`.
+inline bool pitch_ok(int64_t ld, int64_t cols, int64_t mult) {
+  return ld >= cols && ld % mult == 0;
+}
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t ug_version(void) { return 10000; }
+
+const char *ug_status_string(ug_status st) {
+  switch (st) {
+    case UG_OK: return "UG_OK";
+    case UG_ERR_INVALID_ARG: return "UG_ERR_INVALID_ARG: invalid pointer, size, pitch, alignment or format";
+    case UG_ERR_UNSUPPORTED: return "UG_ERR_UNSUPPORTED: size outside what the exact arithmetic holds";
+    case UG_ERR_WORKSPACE: return "UG_ERR_WORKSPACE: workspace missing or too small";
+    case UG_ERR_HIP: return "UG_ERR_HIP: HIP launch or runtime error (see ug_last_hip_error)";
+    default: return "unknown ug_status";
+  }
+}
+
+int32_t ug_last_hip_error(void) { return g_last_hip_error; }
+
+ug_status ug_quant_act(const float *x, int64_t ldx, int64_t M, int64_t K, float eps, int8_t *xq,
+                       int64_t ldq, float *s, void *stream) {
+  if (!ptr_ok(x) || !ptr_ok(xq) || !f32_ok(s)) return UG_ERR_INVALID_ARG;
+  if (M < 1 || K < 1 || M > INT32_MAX) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldx, K, 4) || !pitch_ok(ldq, K, 16) || !eps_ok(eps)) return UG_ERR_INVALID_ARG;
+  return hip_status(ug::launch_quant_act(x, ldx, M, K, eps, xq, ldq, s, as_stream(stream)));
+}
+
+ug_status ug_rmsnorm_quant_act(const float *x, int64_t ldx, const float *g, int64_t M, int64_t K,
+                               float eps_norm, float eps, int8_t *xq, int64_t ldq, float *s,
+                               void *stream) {
+  if (!ptr_ok(x) || !opt_ok(g) || !ptr_ok(xq) || !f32_ok(s)) return UG_ERR_INVALID_ARG;
+  if (M < 1 || K < 1 || M > INT32_MAX) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldx, K, 4) || !pitch_ok(ldq, K, 16)) return UG_ERR_INVALID_ARG;
+  if (!eps_ok(eps) || !eps_ok(eps_norm)) return UG_ERR_INVALID_ARG;
+  if ((float)K != (double)K) return UG_ERR_UNSUPPORTED;
+  return hip_status(ug::launch_rmsnorm_quant_act(x, ldx, g, M, K, eps_norm, eps, xq, ldq, s,
+                                                 as_stream(stream)));
+}
+
+size_t ug_quant_weight_absmean_workspace_size(int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || N > INT64_MAX / K) return 0;
+  const int64_t chunks = ug::ceil_div(N * K, ug::kAbsmeanChunk);
+  return (size_t)(4 * ug::round_up(chunks, ug::kAbsmeanLanes));
+}
+
+ug_status ug_quant_weight_absmean(const float *W, int64_t ldw, int64_t N, int64_t K, float eps,
+                                  int8_t *wq, int64_t ldq, float *beta, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  if (!ptr_ok(W) || !ptr_ok(wq) || !f32_ok(beta)) return UG_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > INT64_MAX / K) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldw, K, 4) || !pitch_ok(ldq, K, 16) || !eps_ok(eps)) return UG_ERR_INVALID_ARG;
+  const int64_t n = N * K;
+  if ((double)(float)n != (double)n || n > (INT64_C(1) << 40)) return UG_ERR_UNSUPPORTED;
+  if (ug::ceil_div(n, ug::kAbsmeanChunk) > INT32_MAX) return UG_ERR_UNSUPPORTED;
+  const size_t need = ug_quant_weight_absmean_workspace_size(N, K);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return UG_ERR_WORKSPACE;
+  return hip_status(ug::launch_absmean(W, ldw, N, K, eps, wq, ldq, beta, (float *)ws,
+                                       as_stream(stream)));
+}
+
+ug_status ug_pack_trits(const int8_t *wq, int64_t ldq, int64_t N, int64_t K, uint8_t *packed,
+                        int64_t ldp, int32_t *bad_count, void *stream) {
+  if (!ptr_ok(wq) || !ptr_ok(packed) || !counter_ok(bad_count)) return UG_ERR_INVALID_ARG;
+  if (N < 1 || K < 1) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldq, K, 16) || !pitch_ok(ldp, ug::ceil_div(K, 5), 16)) return UG_ERR_INVALID_ARG;
+  return hip_status(ug::launch_pack(wq, ldq, N, K, packed, ldp, bad_count, as_stream(stream)));
+}
+
+ug_status ug_unpack_trits(const uint8_t *packed, int64_t ldp, int64_t N, int64_t K, int8_t *wq,
+                          int64_t ldq, int32_t *bad_count, void *stream) {
+  if (!ptr_ok(wq) || !ptr_ok(packed) || !counter_ok(bad_count)) return UG_ERR_INVALID_ARG;
+  if (N < 1 || K < 1) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldq, K, 16) || !pitch_ok(ldp, ug::ceil_div(K, 5), 16)) return UG_ERR_INVALID_ARG;
+  return hip_status(ug::launch_unpack(packed, ldp, N, K, wq, ldq, bad_count, as_stream(stream)));
+}
+
+namespace {
+
+// Shared validation of the two matmul entry points.
+ug_status check_matmul(const int8_t *xq, int64_t ldx, const float *s, const void *w, int32_t wfmt,
+                       int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
+                       const int32_t *acc, int64_t ldacc, const float *y, int64_t ldy) {
+  if (!ptr_ok(xq) || !f32_ok(s) || !ptr_ok(w) || !f32_ok(beta)) return UG_ERR_INVALID_ARG;
+  if (!opt_ok(acc) || !opt_ok(y) || (acc == nullptr && y == nullptr)) return UG_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1) return UG_ERR_INVALID_ARG;
+  if (wfmt != UG_W_I8 && wfmt != UG_W_PACK5) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldx, K, 16)) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldw, wfmt == UG_W_PACK5 ? ug::ceil_div(K, 5) : K, 16)) return UG_ERR_INVALID_ARG;
+  if (acc && !pitch_ok(ldacc, N, 4)) return UG_ERR_INVALID_ARG;
+  if (y && !pitch_ok(ldy, N, 4)) return UG_ERR_INVALID_ARG;
+  if (K > UG_MAX_K) return UG_ERR_UNSUPPORTED;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return UG_ERR_UNSUPPORTED;
+  return UG_OK;
+}
+
+}  // namespace
+
+ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s, const void *w,
+                            int32_t wfmt, int64_t ldw, const float *beta, int64_t M, int64_t N,
+                            int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy,
+                            void *stream) {
+  ug_status st = check_matmul(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy);
+  if (st != UG_OK) return st;
+  if (M > UG_GEMV_MAX_M) return UG_ERR_INVALID_ARG;
+  return hip_status(ug::launch_gemv(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy,
+                                    as_stream(stream)));
+}
+
+size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t wfmt) {
+  (void)M;
+  if (N < 1 || K < 1 || wfmt != UG_W_PACK5) return 0;
+  return (size_t)(N * ug::round_up(K, 16));
+}
+
+ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const void *w,
+                            int32_t wfmt, int64_t ldw, const float *beta, int64_t M, int64_t N,
+                            int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy,
+                            void *ws, size_t ws_bytes, void *stream) {
+  ug_status st = check_matmul(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy);
+  if (st != UG_OK) return st;
+  hipStream_t hs = as_stream(stream);
+  if (wfmt == UG_W_PACK5) {
+    const size_t need = ug_bitlinear_gemm_workspace_size(M, N, K, wfmt);
+    if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return UG_ERR_WORKSPACE;
+    const int64_t ldu = ug::round_up(K, 16);
+    int8_t *wu = (int8_t *)ws;
+    hipError_t e = ug::launch_unpack((const uint8_t *)w, ldw, N, K, wu, ldu, nullptr, hs);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(
+        ug::launch_gemm_i8(xq, ldx, s, wu, ldu, beta, M, N, K, acc, ldacc, y, ldy, hs));
+  }
+  return hip_status(ug::launch_gemm_i8(xq, ldx, s, (const int8_t *)w, ldw, beta, M, N, K, acc,
+                                       ldacc, y, ldy, hs));
+}
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+// Per-token activation quantizers (gfx950).
+//
+// "ultragraph - when the graph is the 1-bit LLM, part 2", section "the
+// bytes": s = max|x|/127 + eps, x_q = clip(round(x/s), -127, 127), one scale
+// per row ("attention, as graph ops": per-token scales keep rows
+// independent).  The RMSNorm variant applies x / sqrt(mean x^2 + eps) * g
+// first (same page, "attention, as graph ops").
+//
+// HBM-bound: 4 bytes read + 1 byte written per element.  A row is read from
+// HBM once: each thread keeps its float4 slices in registers between the
+// max-reduction and the quantization.  Rows longer than the register budget
+// are read twice (the second read mostly hits L2).
+#include "ug_internal.h"
+
+namespace ug {
+namespace {
+
+__device__ inline float4 ld4(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+
+// Quantize one float to an int8 code with the row scale s.
+__device__ inline int q8(float v, float s) { return rint_clamp(v / s, -127.0f, 127.0f); }
+
+__device__ inline void store_q4(int8_t *dst, int64_t k, int64_t K, float4 v, float s) {
+  int a = q8(v.x, s), b = q8(v.y, s), c = q8(v.z, s), d = q8(v.w, s);
+  if (k + 3 < K) {
+    uint32_t packed = (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) |
+                      ((uint32_t)(c & 0xff) << 16) | ((uint32_t)(d & 0xff) << 24);
+    *reinterpret_cast<uint32_t *>(dst + k) = packed;
+  } else {
+    dst[k] = (int8_t)a;
+    if (k + 1 < K) dst[k + 1] = (int8_t)b;
+    if (k + 2 < K) dst[k + 2] = (int8_t)c;
+  }
+}
+
+// Zero the lanes of v at positions >= K (row pad or past the row).
+__device__ inline float4 mask4(float4 v, int64_t k, int64_t K) {
+  if (k + 3 >= K) {
+    if (k + 1 >= K) v.y = 0.0f;
+    if (k + 2 >= K) v.z = 0.0f;
+    if (k + 3 >= K) v.w = 0.0f;
+  }
+  return v;
+}
+
+__device__ inline float amax4(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// TPR threads per row (64: one wave per row, 4 rows per block; 256: one
+// block per row).  VPT = float4 slices held per thread.  If K > TPR*4*VPT the
+// row is streamed twice.
+template <int TPR, int VPT>
+__global__ __launch_bounds__(256) void quant_act_kernel(const float *__restrict__ x, int64_t ldx,
+                                                        int64_t M, int64_t K, float eps,
+                                                        int8_t *__restrict__ xq, int64_t ldq,
+                                                        float *__restrict__ s) {
+  constexpr int RPB = 256 / TPR;
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int lane_in_row = tid % TPR;
+  const int64_t m = (int64_t)blockIdx.x * RPB + tid / TPR;
+  const bool row_ok = m < M;
+  const float *xr = x + (row_ok ? m : 0) * ldx;
+  const int64_t nvec = (K + 3) / 4;
+  const bool fits = nvec <= (int64_t)TPR * VPT;
+
+  float4 v[VPT];
+  float a = 0.0f;
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t f = lane_in_row + (int64_t)i * TPR;
+      if (row_ok && f < nvec) {
+        v[i] = mask4(ld4(xr + 4 * f), 4 * f, K);
+        a = fmaxf(a, amax4(v[i]));
+      } else {
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  } else {
+    for (int64_t f = lane_in_row; f < nvec; f += TPR)
+      if (row_ok) a = fmaxf(a, amax4(mask4(ld4(xr + 4 * f), 4 * f, K)));
+  }
+  a = wave_max(a);
+  if (TPR == 256) {
+    if ((tid & 63) == 0) red[tid >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
+  // s = fl(fl(a / 127) + eps): correctly rounded division, then the add.
+  const float a127 = a / 127.0f;
+  const float sc = a127 + eps;
+  if (!row_ok) return;
+  if (lane_in_row == 0) s[m] = sc;
+  int8_t *qr = xq + m * ldq;
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t f = lane_in_row + (int64_t)i * TPR;
+      if (f < nvec) store_q4(qr, 4 * f, K, v[i], sc);
+    }
+  } else {
+    for (int64_t f = lane_in_row; f < nvec; f += TPR)
+      store_q4(qr, 4 * f, K, mask4(ld4(xr + 4 * f), 4 * f, K), sc);
+  }
+}
+
+// RMSNorm + quantization; one 256-thread block per row.  Thread t owns the
+// float4 slices f = t + 256 i, i.e. the elements k with floor(k/4) mod 256
+// = t, which it squares and adds from +0 in increasing k; fold256() then
+// folds the 256 slot sums in the documented order.
+template <int VPT>
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const float *__restrict__ x, int64_t ldx,
+                                                            const float *__restrict__ g, int64_t M,
+                                                            int64_t K, float eps_n, float eps,
+                                                            int8_t *__restrict__ xq, int64_t ldq,
+                                                            float *__restrict__ s) {
+  __shared__ float lds[256];
+  const int t = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const float *xr = x + m * ldx;
+  const int64_t nvec = (K + 3) / 4;
+  const bool fits = nvec <= 256LL * VPT;
+
+  float4 v[VPT];
+  float acc = 0.0f;
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t f = t + 256LL * i;
+      if (f < nvec) {
+        v[i] = mask4(ld4(xr + 4 * f), 4 * f, K);
+        float q0 = v[i].x * v[i].x;
+        acc = acc + q0;
+        float q1 = v[i].y * v[i].y;
+        acc = acc + q1;
+        float q2 = v[i].z * v[i].z;
+        acc = acc + q2;
+        float q3 = v[i].w * v[i].w;
+        acc = acc + q3;
+      } else {
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  } else {
+    for (int64_t f = t; f < nvec; f += 256) {
+      float4 u = mask4(ld4(xr + 4 * f), 4 * f, K);
+      float q0 = u.x * u.x;
+      acc = acc + q0;
+      float q1 = u.y * u.y;
+      acc = acc + q1;
+      float q2 = u.z * u.z;
+      acc = acc + q2;
+      float q3 = u.w * u.w;
+      acc = acc + q3;
+    }
+  }
+  // Masked lanes contribute +0 (0*0), which leaves a sum >= +0 unchanged.
+  const float T = fold256(acc, lds);
+  const float ms = T / (float)K;
+  const float r = sqrtf(ms + eps_n);
+
+  auto norm4 = [&](float4 u, int64_t k) {
+    float4 o;
+    o.x = u.x / r;
+    o.y = u.y / r;
+    o.z = u.z / r;
+    o.w = u.w / r;
+    if (g) {
+      // g holds exactly K floats: no vector read past its end.
+      float4 gg;
+      if (k + 3 < K) {
+        gg = ld4(g + k);
+      } else {
+        gg.x = g[k];
+        gg.y = k + 1 < K ? g[k + 1] : 0.0f;
+        gg.z = k + 2 < K ? g[k + 2] : 0.0f;
+        gg.w = 0.0f;
+      }
+      o.x = o.x * gg.x;
+      o.y = o.y * gg.y;
+      o.z = o.z * gg.z;
+      o.w = o.w * gg.w;
+    }
+    return o;
+  };
+
+  float a = 0.0f;
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t f = t + 256LL * i;
+      if (f < nvec) {
+        v[i] = norm4(v[i], 4 * f);
+        a = fmaxf(a, amax4(v[i]));
+      }
+    }
+  } else {
+    for (int64_t f = t; f < nvec; f += 256)
+      a = fmaxf(a, amax4(norm4(mask4(ld4(xr + 4 * f), 4 * f, K), 4 * f)));
+  }
+  a = wave_max(a);
+  if ((t & 63) == 0) lds[t >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(lds[0], lds[1]), fmaxf(lds[2], lds[3]));
+  const float a127 = a / 127.0f;
+  const float sc = a127 + eps;
+  if (t == 0) s[m] = sc;
+  int8_t *qr = xq + m * ldq;
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t f = t + 256LL * i;
+      if (f < nvec) store_q4(qr, 4 * f, K, v[i], sc);
+    }
+  } else {
+    for (int64_t f = t; f < nvec; f += 256)
+      store_q4(qr, 4 * f, K, norm4(mask4(ld4(xr + 4 * f), 4 * f, K), 4 * f), sc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const float *x, int64_t ldx, int64_t M, int64_t K, float eps,
+                            int8_t *xq, int64_t ldq, float *s, hipStream_t st) {
+  const int64_t nvec = ceil_div(K, 4);
+  if (nvec <= 64) {
+    hipLaunchKernelGGL((quant_act_kernel<64, 1>), dim3(ceil_div(M, 4)), dim3(256), 0, st, x, ldx,
+                       M, K, eps, xq, ldq, s);
+  } else if (nvec <= 128) {
+    hipLaunchKernelGGL((quant_act_kernel<64, 2>), dim3(ceil_div(M, 4)), dim3(256), 0, st, x, ldx,
+                       M, K, eps, xq, ldq, s);
+  } else if (nvec <= 256) {
+    hipLaunchKernelGGL((quant_act_kernel<64, 4>), dim3(ceil_div(M, 4)), dim3(256), 0, st, x, ldx,
+                       M, K, eps, xq, ldq, s);
+  } else if (nvec <= 512) {
+    hipLaunchKernelGGL((quant_act_kernel<256, 2>), dim3(M), dim3(256), 0, st, x, ldx, M, K, eps,
+                       xq, ldq, s);
+  } else if (nvec <= 1024) {
+    hipLaunchKernelGGL((quant_act_kernel<256, 4>), dim3(M), dim3(256), 0, st, x, ldx, M, K, eps,
+                       xq, ldq, s);
+  } else {
+    hipLaunchKernelGGL((quant_act_kernel<256, 8>), dim3(M), dim3(256), 0, st, x, ldx, M, K, eps,
+                       xq, ldq, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant_act(const float *x, int64_t ldx, const float *g, int64_t M,
+                                    int64_t K, float eps_n, float eps, int8_t *xq, int64_t ldq,
+                                    float *s, hipStream_t st) {
+  const int64_t nvec = ceil_div(K, 4);
+  if (nvec <= 256) {
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<1>), dim3(M), dim3(256), 0, st, x, ldx, g, M, K,
+                       eps_n, eps, xq, ldq, s);
+  } else if (nvec <= 512) {
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<2>), dim3(M), dim3(256), 0, st, x, ldx, g, M, K,
+                       eps_n, eps, xq, ldq, s);
+  } else if (nvec <= 1024) {
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<4>), dim3(M), dim3(256), 0, st, x, ldx, g, M, K,
+                       eps_n, eps, xq, ldq, s);
+  } else {
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<8>), dim3(M), dim3(256), 0, st, x, ldx, g, M, K,
+                       eps_n, eps, xq, ldq, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ug

@@ -1,0 +1,248 @@
+"""Python binding of libug (``include/ug.h``): argument marshalling only.
+
+Each function has the name of the C entry point it calls.  Tensors are
+torch tensors on the GPU; the binding reads their pointers, shapes and row
+pitches, allocates outputs with torch when the caller passes none (torch is
+the device-memory and stream provider), and calls the C ABI on torch's
+current stream.  Every step of the computation runs in libug's HIP kernels;
+there is no fallback: if ``libug.so`` is missing or a call fails, this raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libug.so")
+
+UG_OK = 0
+UG_ERR_INVALID_ARG = 1
+UG_ERR_UNSUPPORTED = 2
+UG_ERR_WORKSPACE = 3
+UG_ERR_HIP = 4
+
+UG_W_I8 = 0
+UG_W_PACK5 = 1
+
+UG_MAX_K = 132104
+UG_GEMV_MAX_M = 64
+
+# Every symbol the header declares, with (restype, argtypes).
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+SIGNATURES = {
+    "ug_version": (_i32, []),
+    "ug_status_string": (ctypes.c_char_p, [_i32]),
+    "ug_last_hip_error": (_i32, []),
+    "ug_quant_act": (_i32, [_vp, _i64, _i64, _i64, _f32, _vp, _i64, _vp, _vp]),
+    "ug_rmsnorm_quant_act": (_i32, [_vp, _i64, _vp, _i64, _i64, _f32, _f32, _vp, _i64, _vp, _vp]),
+    "ug_quant_weight_absmean_workspace_size": (_sz, [_i64, _i64]),
+    "ug_quant_weight_absmean": (_i32, [_vp, _i64, _i64, _i64, _f32, _vp, _i64, _vp, _vp, _sz,
+                                       _vp]),
+    "ug_pack_trits": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "ug_unpack_trits": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "ug_bitlinear_gemv": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
+                                 _i64, _vp, _i64, _vp]),
+    "ug_bitlinear_gemm_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "ug_bitlinear_gemm": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
+                                 _i64, _vp, _i64, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class UgError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = "%s failed: %s" % (where, status_string(status))
+        if status == UG_ERR_HIP:
+            msg += " (hipError %d)" % lib().ug_last_hip_error()
+        super().__init__(msg)
+
+
+def lib():
+    """The loaded libug.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libug.so is not built (%s); run __graft_entry__.build()"
+                               % LIB_PATH)
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_string(st):
+    return lib().ug_status_string(int(st)).decode()
+
+
+def _check(st, where):
+    if st != UG_OK:
+        raise UgError(st, where)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _ld(t):
+    """Row pitch (elements) of a 2-D tensor with unit column stride."""
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def round_up(a, b):
+    return -(-a // b) * b
+
+
+def empty_pitched(rows, cols, dtype, device, align_bytes=16):
+    """[rows, cols] view of a [rows, ld] allocation, ld*itemsize a multiple of
+    align_bytes (the pitches the ABI wants)."""
+    item = torch.empty((), dtype=dtype).element_size()
+    ld = round_up(cols * item, align_bytes) // item
+    return torch.empty((rows, ld), dtype=dtype, device=device)[:, :cols]
+
+
+def packed_pitch(K):
+    """Smallest valid UG_W_PACK5 row pitch (bytes) for K inputs."""
+    return round_up(-(-K // 5), 16)
+
+
+def ug_version():
+    return lib().ug_version()
+
+
+def ug_last_hip_error():
+    return lib().ug_last_hip_error()
+
+
+def ug_quant_act(x, eps=1e-5, xq=None, s=None, stream=None):
+    """Per-row absmax int8 quantization.  x fp32 [M,K] -> (xq int8 [M,K],
+    s fp32 [M])."""
+    M, K = x.shape
+    if xq is None:
+        xq = empty_pitched(M, K, torch.int8, x.device)
+    if s is None:
+        s = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().ug_quant_act(_p(x), _ld(x), M, K, eps, _p(xq), _ld(xq), _p(s), _stream(stream)),
+           "ug_quant_act")
+    return xq, s
+
+
+def ug_rmsnorm_quant_act(x, g=None, eps_norm=1e-5, eps=1e-5, xq=None, s=None, stream=None):
+    """RMSNorm (fp32 gain g, None = ones) fused with per-row quantization."""
+    M, K = x.shape
+    if xq is None:
+        xq = empty_pitched(M, K, torch.int8, x.device)
+    if s is None:
+        s = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().ug_rmsnorm_quant_act(_p(x), _ld(x), _p(g), M, K, eps_norm, eps, _p(xq), _ld(xq),
+                                      _p(s), _stream(stream)), "ug_rmsnorm_quant_act")
+    return xq, s
+
+
+def ug_quant_weight_absmean_workspace_size(N, K):
+    return lib().ug_quant_weight_absmean_workspace_size(N, K)
+
+
+def ug_quant_weight_absmean(W, eps=1e-5, wq=None, beta=None, ws=None, stream=None):
+    """Absmean ternary quantization.  W fp32 [N,K] -> (wq int8 [N,K],
+    beta fp32 [1] on the device)."""
+    N, K = W.shape
+    if wq is None:
+        wq = empty_pitched(N, K, torch.int8, W.device)
+    if beta is None:
+        beta = torch.empty(1, dtype=torch.float32, device=W.device)
+    need = ug_quant_weight_absmean_workspace_size(N, K)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=W.device)
+    _check(lib().ug_quant_weight_absmean(_p(W), _ld(W), N, K, eps, _p(wq), _ld(wq), _p(beta),
+                                         _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "ug_quant_weight_absmean")
+    return wq, beta
+
+
+def ug_pack_trits(wq, packed=None, bad_count=None, stream=None):
+    """One trit per byte -> five trits per byte.  Returns packed uint8
+    [N, ldp] (the full pitched rows)."""
+    N, K = wq.shape
+    if packed is None:
+        packed = torch.empty((N, packed_pitch(K)), dtype=torch.uint8, device=wq.device)
+    _check(lib().ug_pack_trits(_p(wq), _ld(wq), N, K, _p(packed), _ld(packed), _p(bad_count),
+                               _stream(stream)), "ug_pack_trits")
+    return packed
+
+
+def ug_unpack_trits(packed, K, wq=None, bad_count=None, stream=None):
+    """Five trits per byte -> one trit per byte, int8 [N, K]."""
+    N = packed.shape[0]
+    if wq is None:
+        wq = empty_pitched(N, K, torch.int8, packed.device)
+    _check(lib().ug_unpack_trits(_p(packed), _ld(packed), N, K, _p(wq), _ld(wq), _p(bad_count),
+                                 _stream(stream)), "ug_unpack_trits")
+    return wq
+
+
+def _weight_args(w, wfmt, K):
+    if wfmt == UG_W_PACK5:
+        return w.shape[0], _ld(w)
+    if w.shape[1] != K:
+        raise ValueError("int8 weight must be [N, K]")
+    return w.shape[0], _ld(w)
+
+
+def ug_bitlinear_gemv(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=False,
+                      want_y=True, stream=None):
+    """Decode GEMV: xq int8 [M,K] (M <= 64), w int8 [N,K] or packed uint8
+    [N,ldp] -> (acc int32 [M,N] or None, y fp32 [M,N] or None)."""
+    M = xq.shape[0]
+    K = xq.shape[1] if K is None else K
+    N, ldw = _weight_args(w, wfmt, K)
+    if want_acc and acc is None:
+        acc = empty_pitched(M, N, torch.int32, xq.device)
+    if want_y and y is None:
+        y = empty_pitched(M, N, torch.float32, xq.device)
+    _check(lib().ug_bitlinear_gemv(_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), M, N, K,
+                                   _p(acc), _ld(acc) if acc is not None else 0, _p(y),
+                                   _ld(y) if y is not None else 0, _stream(stream)),
+           "ug_bitlinear_gemv")
+    return acc, y
+
+
+def ug_bitlinear_gemm_workspace_size(M, N, K, wfmt):
+    return lib().ug_bitlinear_gemm_workspace_size(M, N, K, wfmt)
+
+
+def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=False,
+                      want_y=True, ws=None, stream=None):
+    """Prefill GEMM (int8 MFMA): same arguments as the GEMV, any M."""
+    M = xq.shape[0]
+    K = xq.shape[1] if K is None else K
+    N, ldw = _weight_args(w, wfmt, K)
+    if want_acc and acc is None:
+        acc = empty_pitched(M, N, torch.int32, xq.device)
+    if want_y and y is None:
+        y = empty_pitched(M, N, torch.float32, xq.device)
+    need = ug_bitlinear_gemm_workspace_size(M, N, K, wfmt)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=xq.device)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().ug_bitlinear_gemm(_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), M, N, K,
+                                   _p(acc), _ld(acc) if acc is not None else 0, _p(y),
+                                   _ld(y) if y is not None else 0, _p(ws), ws_bytes,
+                                   _stream(stream)), "ug_bitlinear_gemm")
+    return acc, y

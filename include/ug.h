@@ -1,0 +1,199 @@
+/*
+ * ug.h -- C ABI of libug, the BitLinear forward pass on AMD Instinct MI355X
+ * (gfx950): per-token int8 activation quantization, absmean ternary weight
+ * quantization, 5-trits-per-byte weight packing, and the int8 x ternary
+ * matmul with int32 accumulation and the s*beta rescale.
+ *
+ * What is computed follows "ultragraph - when the graph is the 1-bit LLM,
+ * part 2" (sections "the bytes", "autograd on a byte-graph", "attention, as
+ * graph ops") and the "ultragraph-1bit 0.12.0" README (sections "A whole
+ * ternary GPT" and "Layout", pack.py).  Every floating-point step is one
+ * IEEE-754 binary32 operation, round to nearest even, no FMA contraction,
+ * no flush-to-zero; round() is round-half-to-even.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *    library keeps no reference after the call returns and never allocates
+ *    device memory; scratch comes from a caller workspace whose size a
+ *    *_workspace_size() query returns.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the null stream).  Nothing synchronizes with the host; outputs
+ *    are valid once the stream reaches the call.
+ *  - Matrices are row-major.  A matrix of R rows with pitch ld occupies
+ *    R*ld elements (every row, the last included, owns its full pitch; the
+ *    library may READ pad elements [cols, ld) of any row but never writes
+ *    them and never lets their values change a result).
+ *  - Alignment: every matrix base pointer is 16-byte aligned; the fp32
+ *    vectors s and beta and the int32 counters need 4-byte alignment; fp32
+ *    and int32 pitches are multiples of 4 elements; int8/uint8 pitches are
+ *    multiples of 16 bytes.
+ *  - Weights are stored [N][K] (out x in, K contiguous): y = x W^T.
+ *  - Scalars s and beta live in device memory, so the quantizers chain into
+ *    the matmul without a host round trip.
+ *  - Inputs must be finite (NaN/Inf are outside the contract); subnormals
+ *    are inside it and are never flushed.
+ *  - Errors in the arguments are returned before anything is launched.
+ *    Data-dependent problems (bad trits, bad codes) are counted into an
+ *    optional caller device counter instead.
+ *  - Calls are thread-safe: the library holds no mutable global state
+ *    except a per-thread copy of the last HIP error.
+ */
+#ifndef UG_H
+#define UG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ug_status;
+
+enum {
+    UG_OK = 0,
+    UG_ERR_INVALID_ARG = 1, /* null pointer, bad size/pitch/alignment/format */
+    UG_ERR_UNSUPPORTED = 2, /* a size the exact arithmetic cannot hold      */
+    UG_ERR_WORKSPACE = 3,   /* workspace missing or too small               */
+    UG_ERR_HIP = 4          /* a HIP launch/runtime error; see ug_last_hip_error() */
+};
+
+/* Weight storage formats. */
+enum {
+    UG_W_I8 = 0,   /* one trit per byte: int8 two's complement -1, 0, +1
+                      ("the bytes": each ternary value in a full byte)     */
+    UG_W_PACK5 = 1 /* five trits per byte (README "A whole ternary GPT"):
+                      byte g of a row holds K positions 5g..5g+4 as
+                      121 + t0 + 3 t1 + 9 t2 + 27 t3 + 81 t4 (t0 = lowest K);
+                      trits past K are 0; row bytes [ceil(K/5), ld) are pad;
+                      codes 243..255 are invalid and act as five 0 trits.  */
+};
+
+/* Largest K the matmuls accept: 127*K < 2^24 keeps (float)acc exact. */
+#define UG_MAX_K 132104
+
+/* Largest activation row count of the decode GEMV. */
+#define UG_GEMV_MAX_M 64
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t ug_version(void);
+
+/* Static description of a status code. */
+const char *ug_status_string(ug_status st);
+
+/* hipError_t of the last UG_ERR_HIP returned on the calling thread. */
+int32_t ug_last_hip_error(void);
+
+/*
+ * Per-token (per-row) absmax int8 activation quantization
+ * ("the bytes" and "attention, as graph ops": one scale per row):
+ *     a_m = max_k |x[m][k]|,   s[m] = fl(fl(a_m / 127) + eps),
+ *     xq[m][k] = clamp(rint(fl(x[m][k] / s[m])), -127, 127).
+ *  x   fp32 [M][ldx] in;  xq int8 [M][ldq] out;  s fp32 [M] out.
+ *  M, K >= 1; ldx >= K; ldq >= K; eps > 0 and finite.
+ * Rows are independent: row m's outputs depend only on row m.
+ */
+ug_status ug_quant_act(const float *x, int64_t ldx, int64_t M, int64_t K,
+                       float eps, int8_t *xq, int64_t ldq, float *s,
+                       void *stream);
+
+/*
+ * RMSNorm with fp32 gain g ("attention, as graph ops") fused with the
+ * activation quantizer above.  Per row:
+ *     T  = sum_k fl(x_k * x_k), added in the fixed order: element k goes to
+ *          slot floor(k/4) mod 256, each slot sums its terms from +0 in
+ *          increasing k, then slots fold pairwise (t += t+h, h = 128..1);
+ *     r  = sqrt(fl(fl(T / K) + eps_norm))   (correctly rounded);
+ *     xn = fl(fl(x_k / r) * g[k])          (g == NULL: xn = fl(x_k / r));
+ * then ug_quant_act's steps on xn.  xn itself is not stored.
+ *  g fp32 [K] or NULL; eps_norm > 0, eps > 0, finite.
+ */
+ug_status ug_rmsnorm_quant_act(const float *x, int64_t ldx, const float *g,
+                               int64_t M, int64_t K, float eps_norm,
+                               float eps, int8_t *xq, int64_t ldq, float *s,
+                               void *stream);
+
+/* Bytes of workspace ug_quant_weight_absmean needs for an N x K weight:
+ * 4 * ceil(ceil(N*K / 8192) / 256) * 256.  Returns 0 for invalid sizes. */
+size_t ug_quant_weight_absmean_workspace_size(int64_t N, int64_t K);
+
+/*
+ * Absmean ternary weight quantization ("the bytes"):
+ *     T    = sum |W| over all n = N*K elements in the fixed two-stage order:
+ *            flatten row-major, split into chunks of 8192 (the last padded
+ *            with +0); in chunk c lane t in [0,256) keeps four sums acc_j
+ *            and adds element 8192c + 1024i + 4t + j to acc_j for
+ *            i = 0..7; lane value fl(fl(acc0+acc1) + fl(acc2+acc3)); lanes
+ *            fold pairwise (t += t+h, h = 128..1).  Then lane t sums chunk
+ *            sums t, t+256, ... from +0 and the lanes fold the same way;
+ *     beta = fl(fl(T / (float)n) + eps)   (written to *beta, device);
+ *     wq   = clamp(rint(fl(W / beta)), -1, 1)   (UG_W_I8).
+ *  W fp32 [N][ldw] in; wq int8 [N][ldq] out; beta fp32 [1] out;
+ *  ws: device workspace of ws_bytes >= the size query.
+ *  UG_ERR_UNSUPPORTED if n is not exactly representable in fp32.
+ */
+ug_status ug_quant_weight_absmean(const float *W, int64_t ldw, int64_t N,
+                                  int64_t K, float eps, int8_t *wq,
+                                  int64_t ldq, float *beta, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+/*
+ * Pack one-trit-per-byte weights into UG_W_PACK5 (README "A whole ternary
+ * GPT"; "Layout": pack.py).  wq int8 [N][ldq] in; packed uint8 [N][ldp]
+ * out, ldp >= ceil(K/5); bytes [ceil(K/5), ldp) of every row are written as
+ * 121.  An entry outside {-1,0,1} is packed as its value clamped to [-1,1]
+ * and, if bad_count != NULL, added to *bad_count (device int32, not reset).
+ */
+ug_status ug_pack_trits(const int8_t *wq, int64_t ldq, int64_t N, int64_t K,
+                        uint8_t *packed, int64_t ldp, int32_t *bad_count,
+                        void *stream);
+
+/*
+ * Inverse of ug_pack_trits: writes wq[n][k] for k < K.  A code above 242
+ * among the first ceil(K/5) bytes of a row decodes to five 0 trits and, if
+ * bad_count != NULL, is added to *bad_count.  Pad bytes are not read.
+ */
+ug_status ug_unpack_trits(const uint8_t *packed, int64_t ldp, int64_t N,
+                          int64_t K, int8_t *wq, int64_t ldq,
+                          int32_t *bad_count, void *stream);
+
+/*
+ * Decode GEMV: the integer forward y = (x_q W_q^T)(s beta) ("autograd on a
+ * byte-graph", no bias) for a few activation rows:
+ *     acc[m][n] = sum_k xq[m][k] * W_q[n][k]      (int32, exact),
+ *     y[m][n]   = fl((float)acc[m][n] * fl(s[m] * beta)).
+ *  xq int8 [M][ldx]; s fp32 [M]; beta fp32 [1] (device);
+ *  w: wfmt == UG_W_I8: int8 [N][ldw]; UG_W_PACK5: uint8 [N][ldw] bytes,
+ *     ldw >= ceil(K/5);
+ *  acc int32 [M][ldacc] out or NULL; y fp32 [M][ldy] out or NULL (not both
+ *  NULL).  1 <= M <= UG_GEMV_MAX_M; 1 <= K <= UG_MAX_K.
+ */
+ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s,
+                            const void *w, int32_t wfmt, int64_t ldw,
+                            const float *beta, int64_t M, int64_t N,
+                            int64_t K, int32_t *acc, int64_t ldacc, float *y,
+                            int64_t ldy, void *stream);
+
+/* Bytes of workspace ug_bitlinear_gemm needs (0 for UG_W_I8). */
+size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
+                                        int32_t wfmt);
+
+/*
+ * Prefill GEMM: the same result as ug_bitlinear_gemv for any M >= 1, as a
+ * dense int8 contraction on the matrix cores (ternary values are exact in
+ * int8).  Same arguments, plus the workspace (used by UG_W_PACK5 to hold the
+ * decoded int8 weights).
+ */
+ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s,
+                            const void *w, int32_t wfmt, int64_t ldw,
+                            const float *beta, int64_t M, int64_t N,
+                            int64_t K, int32_t *acc, int64_t ldacc, float *y,
+                            int64_t ldy, void *ws, size_t ws_bytes,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UG_H */

@@ -1,0 +1,267 @@
+"""Op-level parity of the HIP path against the CPU oracle, called through
+the C ABI, on seeded inputs spanning several tiles, ragged tails and the
+degenerate cases of each step.  Bit-exact for x_q, s, beta, W_q, packed
+bytes and int32 accumulators; fp32 y within 1e-6 relative (expected exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bitlinear_matmul_amd import ug
+from gpu_util import (assert_bits_equal, assert_y_close, host, pitched, scalar_dev, vec)
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(*a):
+    print("case:", *a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# activation quantization
+# ---------------------------------------------------------------------------
+ACT_SHAPES = [(32, 128), (1, 384), (1, 1536), (7, 13), (3, 1), (5, 4097), (3, 40000),
+              (64, 6912), (513, 2560), (2, 1024), (9, 1023)]
+
+
+@pytest.mark.parametrize("M,K", ACT_SHAPES)
+def test_quant_act_parity(dev, M, K):
+    _print_case("quant_act", M, K)
+    rng = np.random.default_rng([100, M, K])
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if K > 8:
+        x[:, rng.choice(K, max(1, K // 100), replace=False)] *= np.float32(20)
+    if M > 2:
+        x[1] = 0.0                                          # all-zero row
+        x[2] *= np.float32(1e-39)                           # subnormal row
+    xq_d, s_d = ug.ug_quant_act(pitched(x), 1e-5)
+    xq_r, s_r = oracle.quant_act(x, 1e-5)
+    assert_bits_equal(host(s_d), s_r, "s")
+    assert_bits_equal(host(xq_d), xq_r, "x_q")
+
+
+def test_quant_act_golden_ties(dev):
+    scale = np.float32(2.0 ** 20)
+    ratios = np.array([127, 2.5, 3.5, -0.5, 0.5, -1.5, 126.5, -2.5, 1, 0, -127, 64.5])
+    x = (ratios * float(scale)).astype(np.float32)[None, :]
+    xq_d, s_d = ug.ug_quant_act(pitched(x), 1e-5)
+    assert host(s_d)[0] == scale
+    assert host(xq_d)[0].tolist() == [127, 2, 4, 0, 0, -2, 126, -2, 1, 0, -127, 64]
+
+
+def test_quant_act_rows_independent(dev):
+    rng = np.random.default_rng(101)
+    x = rng.standard_normal((16, 2560), dtype=np.float32)
+    a, sa = ug.ug_quant_act(pitched(x))
+    x[5] *= np.float32(100)
+    b, sb = ug.ug_quant_act(pitched(x))
+    a, b, sa, sb = host(a), host(b), host(sa), host(sb)
+    keep = np.arange(16) != 5
+    assert np.array_equal(a[keep], b[keep]) and np.array_equal(sa[keep], sb[keep])
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm + quantization
+# ---------------------------------------------------------------------------
+RMS_SHAPES = [(4, 2560), (3, 6912), (5, 1001), (2, 9000), (6, 1), (8, 384), (2048, 2560)]
+
+
+@pytest.mark.parametrize("M,K", RMS_SHAPES)
+@pytest.mark.parametrize("with_gain", [False, True])
+def test_rmsnorm_quant_parity(dev, M, K, with_gain):
+    _print_case("rmsnorm_quant", M, K, with_gain)
+    rng = np.random.default_rng([102, M, K])
+    x = rng.standard_normal((M, K), dtype=np.float32) * np.float32(3)
+    if M > 2:
+        x[1] = np.float32(0.75)                              # constant row
+    g = None
+    if with_gain:
+        g = np.float32(1) + rng.standard_normal(K, dtype=np.float32) * np.float32(0.1)
+    xq_d, s_d = ug.ug_rmsnorm_quant_act(pitched(x), vec(g) if g is not None else None)
+    xq_r, s_r = oracle.rmsnorm_quant_act(x, g)
+    assert_bits_equal(host(s_d), s_r, "s")
+    assert_bits_equal(host(xq_d), xq_r, "x_q")
+
+
+# ---------------------------------------------------------------------------
+# absmean ternary quantization
+# ---------------------------------------------------------------------------
+W_SHAPES = [(512, 128), (1152, 384), (384, 1536), (6912, 2560), (2560, 6912), (300, 7), (1, 1),
+            (2600, 1000), (3, 8193)]
+
+
+@pytest.mark.parametrize("N,K", W_SHAPES)
+def test_absmean_parity(dev, N, K):
+    _print_case("absmean", N, K)
+    rng = np.random.default_rng([103, N, K])
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    wq_d, beta_d = ug.ug_quant_weight_absmean(pitched(W))
+    wq_r, beta_r = oracle.quant_weight_absmean(W)
+    assert_bits_equal(host(beta_d), np.array([beta_r], np.float32), "beta")
+    assert_bits_equal(host(wq_d), wq_r, "W_q")
+
+
+def test_absmean_pitched_input(dev):
+    """A row pitch larger than K takes the strided path; same bits."""
+    rng = np.random.default_rng(104)
+    N, K = 700, 1000
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    Wd = ug.empty_pitched(N, K, torch.float32, torch.device("cuda:0"), 64)  # ld = 1008
+    Wd.copy_(torch.from_numpy(W))
+    assert Wd.stride(0) != K
+    wq_d, beta_d = ug.ug_quant_weight_absmean(Wd)
+    wq_r, beta_r = oracle.quant_weight_absmean(W)
+    assert host(beta_d)[0] == beta_r
+    assert_bits_equal(host(wq_d), wq_r, "W_q")
+
+
+def test_absmean_special_cases(dev):
+    # 2^25 ones: exact 2^25 in the fixed order
+    W = torch.ones((4096, 8192), dtype=torch.float32, device="cuda:0")
+    wq, beta = ug.ug_quant_weight_absmean(W)
+    assert host(beta)[0] == np.float32(1.0) + np.float32(1e-5)
+    assert bool((wq == 1).all())
+    del W, wq
+    # zeros -> beta = eps, W_q = 0
+    wq, beta = ug.ug_quant_weight_absmean(torch.zeros((64, 96), dtype=torch.float32,
+                                                      device="cuda:0"))
+    assert host(beta)[0] == np.float32(1e-5) and bool((wq == 0).all())
+    # ties: W/beta = +-0.5 -> 0, +-1.5 -> +-1
+    r = np.array([0.5, -0.5, 1.5, -1.5, 1, -1, 0, 2])
+    W = (r * 2.0 ** 20).astype(np.float32)[None, :]
+    wq, beta = ug.ug_quant_weight_absmean(pitched(W))
+    assert host(beta)[0] == np.float32(2.0 ** 20)
+    assert host(wq)[0].tolist() == [0, 0, 1, -1, 1, -1, 0, 1]
+
+
+# ---------------------------------------------------------------------------
+# pack / unpack
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K", [(243, 5), (512, 128), (6912, 2560), (2560, 6912), (9, 7),
+                                 (5, 1), (33, 81)])
+def test_pack_parity(dev, N, K):
+    _print_case("pack", N, K)
+    rng = np.random.default_rng([105, N, K])
+    wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    if N == 243 and K == 5:
+        wq = np.array(np.meshgrid(*[[-1, 0, 1]] * 5, indexing="ij")).reshape(5, -1).T.astype(
+            np.int8)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    pk_d = ug.ug_pack_trits(pitched(wq), bad_count=bad)
+    pk_r, bad_r = oracle.pack_trits(wq, ldp=pk_d.shape[1])
+    assert_bits_equal(host(pk_d), pk_r, "packed")
+    assert host(bad)[0] == bad_r == 0
+    un_d = ug.ug_unpack_trits(pk_d, K, bad_count=bad)
+    assert_bits_equal(host(un_d), wq, "unpacked")
+    assert host(bad)[0] == 0
+
+
+def test_pack_bad_entries_and_unpack_bad_codes(dev):
+    rng = np.random.default_rng(106)
+    wq = rng.integers(-1, 2, size=(40, 37)).astype(np.int8)
+    wq[0, 0], wq[3, 36], wq[39, 5], wq[7, 7] = 2, -5, 127, -128
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    pk = ug.ug_pack_trits(pitched(wq), bad_count=bad)
+    pk_r, bad_r = oracle.pack_trits(wq, ldp=pk.shape[1])
+    assert bad_r == 4 and host(bad)[0] == 4
+    assert_bits_equal(host(pk), pk_r, "packed")
+    # all 256 codes
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    codes_p = np.full((1, 256), 121, np.uint8)
+    codes_p[:] = codes
+    bad.zero_()
+    K = 5 * 256
+    un = ug.ug_unpack_trits(pitched(codes_p), K, bad_count=bad)
+    un_r, bad_r = oracle.unpack_trits(codes_p, K)
+    assert bad_r == 13 and host(bad)[0] == 13
+    assert_bits_equal(host(un), un_r, "unpacked")
+
+
+# ---------------------------------------------------------------------------
+# GEMV / GEMM
+# ---------------------------------------------------------------------------
+def _rand_problem(rng, M, N, K):
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    wq = (rng.integers(-1, 2, size=(N, K))).astype(np.int8)
+    s = (rng.random(M, dtype=np.float32) * np.float32(0.05) + np.float32(1e-3))
+    beta = np.float32(0.0159)
+    return xq, wq, s, beta
+
+
+GEMV_CASES = [(1, 6912, 2560), (1, 2560, 6912), (4, 1152, 384), (3, 385, 1001), (5, 64, 7),
+              (16, 512, 128), (64, 300, 2560), (2, 17, 81), (1, 4096, 384), (33, 1000, 160)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_CASES)
+@pytest.mark.parametrize("fmt", [ug.UG_W_PACK5, ug.UG_W_I8])
+def test_gemv_parity(dev, M, N, K, fmt):
+    _print_case("gemv", M, N, K, fmt)
+    rng = np.random.default_rng([107, M, N, K])
+    xq, wq, s, beta = _rand_problem(rng, M, N, K)
+    if fmt == ug.UG_W_PACK5:
+        pk, _ = oracle.pack_trits(wq)
+        w = pitched(pk)
+    else:
+        w = pitched(wq)
+    acc_d, y_d = ug.ug_bitlinear_gemv(pitched(xq), vec(s), w, fmt, scalar_dev(beta), K=K,
+                                      want_acc=True)
+    acc_r = oracle.matmul_i32(xq, wq)
+    y_r = oracle.epilogue(acc_r, s, beta)
+    assert_bits_equal(host(acc_d), acc_r, "acc")
+    assert_y_close(host(y_d), y_r, "y")
+    assert_bits_equal(host(y_d), y_r, "y bits")
+
+
+def test_gemv_invalid_codes_and_garbage_pad(dev):
+    """Codes 243..255 act as five zero trits; pad bytes past ceil(K/5) and
+    trits past K never change the result."""
+    rng = np.random.default_rng(108)
+    M, N, K = 3, 70, 101  # 21 bytes used per row, pitch 32
+    xq, wq, s, beta = _rand_problem(rng, M, N, K)
+    pk, _ = oracle.pack_trits(wq)
+    pk[:, 21:] = rng.integers(0, 256, size=(N, pk.shape[1] - 21))  # garbage pad
+    pk[5, 3] = 250                                                   # invalid code
+    pk[9, 0] = 243
+    wq_eff, bad = oracle.unpack_trits(pk, K)
+    assert bad == 2
+    _, y_d = ug.ug_bitlinear_gemv(pitched(xq), vec(s), pitched(pk), ug.UG_W_PACK5,
+                                  scalar_dev(beta), K=K)
+    acc_r = oracle.matmul_i32(xq, wq_eff)
+    assert_bits_equal(host(y_d), oracle.epilogue(acc_r, s, beta), "y")
+
+
+GEMM_CASES = [(1, 64, 64), (33, 129, 100), (128, 512, 128), (300, 64, 2560), (257, 1000, 1536),
+              (512, 6912, 2560), (200, 2560, 6912)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+@pytest.mark.parametrize("fmt", [ug.UG_W_I8, ug.UG_W_PACK5])
+def test_gemm_parity(dev, M, N, K, fmt):
+    _print_case("gemm", M, N, K, fmt)
+    rng = np.random.default_rng([109, M, N, K])
+    xq, wq, s, beta = _rand_problem(rng, M, N, K)
+    w = pitched(oracle.pack_trits(wq)[0]) if fmt == ug.UG_W_PACK5 else pitched(wq)
+    acc_d, y_d = ug.ug_bitlinear_gemm(pitched(xq), vec(s), w, fmt, scalar_dev(beta), K=K,
+                                      want_acc=True)
+    acc_r = oracle.matmul_i32(xq, wq)
+    y_r = oracle.epilogue(acc_r, s, beta)
+    assert_bits_equal(host(acc_d), acc_r, "acc")
+    assert_y_close(host(y_d), y_r, "y")
+    assert_bits_equal(host(y_d), y_r, "y bits")
+
+
+def test_gemm_extreme_values(dev):
+    """|acc| at its largest: x_q = +-127 everywhere against all +-1 rows."""
+    M, N, K = 64, 64, 6912
+    xq = np.full((M, K), 127, np.int8)
+    xq[1::2] = -127
+    wq = np.ones((N, K), np.int8)
+    wq[::3] = -1
+    s = np.full(M, np.float32(0.5))
+    acc_d, _ = ug.ug_bitlinear_gemm(pitched(xq), vec(s), pitched(wq), ug.UG_W_I8,
+                                    scalar_dev(np.float32(1)), want_acc=True)
+    assert_bits_equal(host(acc_d), oracle.matmul_i32(xq, wq), "acc")
+    acc_v, _ = ug.ug_bitlinear_gemv(pitched(xq), vec(s), pitched(wq), ug.UG_W_I8,
+                                    scalar_dev(np.float32(1)), want_acc=True)
+    assert_bits_equal(host(acc_v), oracle.matmul_i32(xq, wq), "acc gemv")
