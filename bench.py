@@ -93,38 +93,40 @@ def capture(torch, fn):
 # decode_stack
 # ---------------------------------------------------------------------------
 def setup_decode_stack(torch, ug, inputs, n_copies):
+    """Quantize + pack every matrix once (deployed weights), then make
+    n_copies copies of the packed set and one grouped plan per copy: a plan
+    quantizes the 33 fp32 inputs and runs the 33 GEMVs in one launch."""
     dev = torch.device("cuda:0")
     mats = []
     for (layer, mi, name, K, N) in inputs.decode_stack_shapes():
         x, W = inputs.decode_stack_matrix(layer, mi, K, N)
-        Wd = torch.from_numpy(W).to(dev)
-        wq, beta = ug.ug_quant_weight_absmean(Wd)
+        wq, beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
         pk = ug.ug_pack_trits(wq)
-        mats.append(dict(K=K, N=N, x=torch.from_numpy(x).to(dev), pk0=pk, beta=beta,
+        mats.append(dict(K=K, N=N, x=torch.from_numpy(x).to(dev), pk=pk, beta=beta,
                          xq=ug.empty_pitched(1, K, torch.int8, dev),
                          s=torch.empty(1, dtype=torch.float32, device=dev),
-                         y=ug.empty_pitched(1, N, torch.float32, dev),
-                         W=W, x_host=x))
-        del Wd, wq
-    # weight copies (cold streaming): copy c of matrix i
-    for m in mats:
-        m["pk"] = [m["pk0"]] + [m["pk0"].clone() for _ in range(n_copies - 1)]
+                         y=ug.empty_pitched(1, N, torch.float32, dev), W=W, x_host=x))
+        del wq
+    plans = []
+    for c in range(n_copies):
+        probs = []
+        for m in mats:
+            w = m["pk"] if c == 0 else m["pk"].clone()
+            probs.append(dict(x=m["x"], w=w, wfmt=ug.UG_W_PACK5, beta=m["beta"], K=m["K"],
+                              y=m["y"], xq=m["xq"], s=m["s"]))
+        plans.append(ug.ug_gemv_plan_init(probs))
     torch.cuda.synchronize()
     per_pass_bytes = sum(m["N"] * (-(-m["K"] // 5)) for m in mats)
-    return mats, per_pass_bytes
+    return mats, plans, per_pass_bytes
 
 
-def decode_stack_pass(ug, mats, c, gemv_only=False):
-    for m in mats:
-        if not gemv_only:
-            ug.ug_quant_act(m["x"], 1e-5, xq=m["xq"], s=m["s"])
-        ug.ug_bitlinear_gemv(m["xq"], m["s"], m["pk"][c], ug.UG_W_PACK5, m["beta"], K=m["K"],
-                             y=m["y"])
-
-
-def gemv_alg_bytes(M, N, K, packed=True):
+def gemv_alg_bytes(M, N, K, packed=True, fp32_x=False):
+    """Algorithmic bytes of one GEMV: packed (or 1 B/trit) weights, the
+    activations (fp32 when quantized in the launch, else int8 + scales),
+    beta and the fp32 output."""
     wb = N * (-(-K // 5)) if packed else N * K
-    return wb + M * K + 4 * M + 4 + 4 * M * N
+    xb = 4 * M * K if fp32_x else M * K + 4 * M
+    return wb + xb + 4 + 4 * M * N
 
 
 def cpu_decode_stack(oracle, mats, seconds):
@@ -150,39 +152,36 @@ def cpu_decode_stack(oracle, mats, seconds):
 def run_decode_stack(args, torch, ug, inputs):
     steps = args.steps if args.steps is not None else 200
     warm = args.warmup if args.warmup is not None else 20
-    # bytes of one stored copy
     per_copy = sum(N * ug.packed_pitch(K) for (_, _, _, K, N) in inputs.decode_stack_shapes())
     n_copies = min(max(1, COLD_BYTES // per_copy), warm + steps)
-    mats, per_pass_bytes = setup_decode_stack(torch, ug, inputs, n_copies)
-    log("decode_stack: %d matrices, %d packed weight bytes per pass, %d copies"
-        % (len(mats), per_pass_bytes, n_copies))
-    g_warm = capture(torch, lambda: [decode_stack_pass(ug, mats, c % n_copies)
+    mats, plans, per_pass_bytes = setup_decode_stack(torch, ug, inputs, n_copies)
+    log("decode_stack: %d matrices, %d packed weight bytes per pass, %d copies, grid %d"
+        % (len(mats), per_pass_bytes, n_copies, plans[0].info.grid))
+    g_warm = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[c % n_copies])
                                      for c in range(warm)])
-    g_run = capture(torch, lambda: [decode_stack_pass(ug, mats, (warm + c) % n_copies)
+    g_run = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[(warm + c) % n_copies])
                                     for c in range(steps)])
-    g_gemv = capture(torch, lambda: [decode_stack_pass(ug, mats, (warm + c) % n_copies, True)
-                                     for c in range(steps)])
     stream = torch.cuda.current_stream()
     time_graph(torch, g_warm, stream)
     ms = time_graph(torch, g_run, stream)
     log("decode_stack: %d steps in %.3f ms" % (steps, ms))
-    # dominant kernel: the GEMV, timed alone (33 launches per pass)
-    gemv_ms = time_graph(torch, g_gemv, stream)
-    launches = steps * len(mats)
-    gemv_bytes = sum(gemv_alg_bytes(1, m["N"], m["K"]) for m in mats) * steps
-    avg_launch_s = gemv_ms / 1e3 / launches
-    achieved = gemv_bytes / launches / avg_launch_s / 1e9
+    # The step is one launch of the grouped kernel, so the kernel's average
+    # launch duration is the step time (inter-launch gap included).
+    alg = sum(gemv_alg_bytes(1, m["N"], m["K"], fp32_x=True) for m in mats)
+    avg_launch_s = ms / 1e3 / steps
+    achieved = alg / avg_launch_s / 1e9
     value = per_pass_bytes * steps / (ms / 1e3) / 1e9
     out = dict(value=value, unit="GB/s", ms_per_step=ms / steps, steps=steps, warmup=warm,
-               dtype="int8xtrit->int32, f32 scale",
+               dtype="int8 x trit -> int32 (MFMA), fp32 scales",
                config={"workload": "decode_stack", "batch": 1, "matrices": len(mats),
                        "weight_format": "pack5", "packed_weight_bytes_per_step": per_pass_bytes,
-                       "weight_copies_cycled": n_copies, "regime": "cold (HBM)",
+                       "launches_per_step": 1, "weight_copies_cycled": n_copies,
+                       "regime": "cold (each step reads its own weight copy from HBM)",
                        "us_per_token_pass": ms * 1e3 / steps},
-               roofline=dict(bound="hbm", kernel="gemv_kernel<PACK5>", achieved=achieved,
-                             peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
-                             traffic=None, avg_launch_us=avg_launch_s * 1e6,
-                             alg_bytes_per_launch=gemv_bytes / launches))
+               roofline=dict(bound="hbm", kernel="gemv_grouped_kernel<PACK5,1>",
+                             achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=achieved / HBM_PEAK_GBS, traffic=None,
+                             avg_launch_us=avg_launch_s * 1e6, alg_bytes_per_launch=alg))
     if not args.no_cpu_baseline:
         import oracle
         passes, secs = cpu_decode_stack(oracle, mats, args.cpu_seconds)
@@ -191,6 +190,80 @@ def run_decode_stack(args, torch, ug, inputs):
                                    sample="%d full decode passes (33 x quant + unpack + int "
                                           "matmul + rescale) in %.1f s" % (passes, secs))
     return out
+
+
+# ---------------------------------------------------------------------------
+# sweep: decode GEMV at M in {1,4,16,64} x three 2B-class shapes
+# ---------------------------------------------------------------------------
+def run_sweep(args, torch, ug, inputs):
+    """Per point: (a) one GEMV call, cold, latency per call; (b) streaming:
+    a grouped launch over G distinct weight copies (G * bytes >= 128 MB),
+    steps cycling through enough copies to exceed the MALL."""
+    steps = args.steps if args.steps is not None else 10
+    warm = args.warmup if args.warmup is not None else 2
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    points = []
+    tot_bytes = 0.0
+    tot_s = 0.0
+    for si, (K, N) in enumerate(inputs.SWEEP_SHAPES):
+        x64, W = inputs.sweep_inputs(si, 64)
+        wq, beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
+        pk = ug.ug_pack_trits(wq)
+        del wq
+        wbytes = N * (-(-K // 5))
+        G = max(1, (128 << 20) // (N * ug.packed_pitch(K)))
+        n_sets = max(2, min(warm + steps, (COLD_BYTES // (G * N * ug.packed_pitch(K))) + 1))
+        copies = [[pk.clone() for _ in range(G)] for _ in range(n_sets)]
+        for M in inputs.SWEEP_MS:
+            xq, s = ug.ug_quant_act(torch.from_numpy(x64[:M].copy()).to(dev))
+            y = ug.empty_pitched(M, N, torch.float32, dev)
+            try:
+                plans = [ug.ug_gemv_plan_init([dict(xq=xq, s=s, w=w, wfmt=ug.UG_W_PACK5,
+                                                    beta=beta, K=K, y=y) for w in cs])
+                         for cs in copies]
+            except ug.UgError:
+                plans = None
+            if plans is not None:
+                g = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[c % n_sets])
+                                            for c in range(warm + steps)])
+                ms = time_graph(torch, g, stream)
+                launch_us = ms * 1e3 / (warm + steps)
+                gbs = wbytes * G / (launch_us * 1e-6) / 1e9
+                alg = gemv_alg_bytes(M, N, K) * G
+                del g
+            else:
+                launch_us, gbs, alg = None, None, None
+            # single-call latency, cold copies
+            g1 = capture(torch, lambda: [ug.ug_bitlinear_gemv(
+                xq, s, copies[c % n_sets][c % G], ug.UG_W_PACK5, beta, K=K, y=y)
+                for c in range(warm + steps)])
+            ms1 = time_graph(torch, g1, stream)
+            del g1
+            call_us = ms1 * 1e3 / (warm + steps)
+            pt = {"M": M, "K": K, "N": N, "call_us": call_us,
+                  "call_weight_GBps": wbytes / (call_us * 1e-6) / 1e9,
+                  "grouped_G": G if plans else 0, "grouped_launch_us": launch_us,
+                  "grouped_weight_GBps": gbs}
+            log("sweep", pt)
+            points.append(pt)
+            if plans is not None:
+                tot_bytes += wbytes * G
+                tot_s += launch_us * 1e-6
+                if M == 1 and si == 0:
+                    dom = dict(bound="hbm", kernel="gemv_grouped_kernel<PACK5,1>",
+                               achieved=alg / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
+                               unit="GB/s", frac=alg / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                               traffic=None, avg_launch_us=launch_us, alg_bytes_per_launch=alg,
+                               point="M=1 K=2560 N=6912, %d copies per launch" % G)
+        del copies
+        torch.cuda.empty_cache()
+    value = tot_bytes / tot_s / 1e9
+    return dict(value=value, unit="GB/s", ms_per_step=tot_s * 1e3 / len(points), steps=steps,
+                warmup=warm, dtype="int8 x trit -> int32 (MFMA), fp32 scales",
+                config={"workload": "sweep", "points": points, "weight_format": "pack5",
+                        "regime": "cold; value = grouped streaming over all points"},
+                roofline=dom)
 
 
 # ---------------------------------------------------------------------------
@@ -282,7 +355,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     ug.lib()
-    runners = {"decode_stack": run_decode_stack, "prefill": run_prefill}
+    runners = {"decode_stack": run_decode_stack, "prefill": run_prefill, "sweep": run_sweep}
     if args.workload not in runners:
         print("workload %s not implemented yet" % args.workload, file=sys.stderr)
         sys.exit(2)

@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libug.so")
-SOURCES = ["api.hip", "quant_act.hip", "absmean.hip", "pack.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quant_act.hip", "absmean.hip", "pack.hip", "gemv_mfma.hip", "gemm.hip"]
 ARCH = os.environ.get("UG_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -3,6 +3,7 @@
 // anything is launched; no entry point allocates or synchronizes.
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "ug_internal.h"
 
@@ -140,8 +141,97 @@ ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s, const
   ug_status st = check_matmul(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy);
   if (st != UG_OK) return st;
   if (M > UG_GEMV_MAX_M) return UG_ERR_INVALID_ARG;
+  // the kernel addresses weights and activations with 32-bit buffer offsets
+  if (N * ldw >= (INT64_C(1) << 31) || M * ldx >= (INT64_C(1) << 31)) return UG_ERR_UNSUPPORTED;
   return hip_status(ug::launch_gemv(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy,
                                     as_stream(stream)));
+}
+
+size_t ug_gemv_plan_size(int32_t count) {
+  if (count < 1) return 0;
+  return (size_t)count * sizeof(ug::GemvDesc);
+}
+
+ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void *plan,
+                            size_t plan_bytes, ug_gemv_plan_info *info) {
+  if (problems == nullptr || info == nullptr || count < 1) return UG_ERR_INVALID_ARG;
+  if (plan == nullptr || !aligned16(plan) || plan_bytes < ug_gemv_plan_size(count))
+    return UG_ERR_WORKSPACE;
+  std::vector<ug::GemvDesc> descs((size_t)count);
+  std::vector<int> items((size_t)count);
+  int variant = -1;
+  for (int32_t i = 0; i < count; ++i) {
+    const ug_gemv_problem &p = problems[i];
+    const bool fused = p.x != nullptr;
+    const int8_t *xq_in = fused ? (p.xq ? p.xq : (const int8_t *)p.x) : p.xq;
+    const float *s_in = fused ? (p.s ? p.s : (const float *)p.x) : p.s;
+    const int64_t ldxq = fused && !p.xq ? ug::round_up(p.K, 16) : p.ldxq;
+    ug_status st = check_matmul(xq_in, ldxq, s_in, p.w, p.wfmt, p.ldw, p.beta, p.M, p.N, p.K,
+                                p.acc, p.ldacc, p.y, p.ldy);
+    if (st != UG_OK) return st;
+    if (p.M > UG_GEMV_MAX_M) return UG_ERR_INVALID_ARG;
+    if (fused) {
+      if (!ptr_ok(p.x) || !pitch_ok(p.ldx, p.K, 4) || !eps_ok(p.eps)) return UG_ERR_INVALID_ARG;
+      if (!ug::gemv_stages_x(p.wfmt, p.M, p.K)) return UG_ERR_UNSUPPORTED;
+    }
+    if (p.N * p.ldw >= (INT64_C(1) << 31) || p.M * ldxq >= (INT64_C(1) << 31))
+      return UG_ERR_UNSUPPORTED;
+    ug::GemvDesc d{};
+    d.x = p.x;
+    d.ldx = p.ldx;
+    d.xq = fused ? p.xq : p.xq;
+    d.ldxq = p.xq ? p.ldxq : 0;
+    d.s = p.s;
+    d.w = (const uint8_t *)p.w;
+    d.ldw = p.ldw;
+    d.beta = p.beta;
+    d.acc = p.acc;
+    d.ldacc = p.ldacc;
+    d.y = p.y;
+    d.ldy = p.ldy;
+    d.eps = p.eps;
+    d.wfmt = p.wfmt;
+    d.M = (int32_t)p.M;
+    d.N = (int32_t)p.N;
+    d.K = (int32_t)p.K;
+    ug::gemv_mfma_plan(d);
+    const int v = 16 * d.wfmt + d.mb;
+    if (variant >= 0 && v != variant) return UG_ERR_INVALID_ARG;
+    variant = v;
+    items[(size_t)i] = d.items;
+    descs[(size_t)i] = d;
+  }
+  // Items per block such that the whole group runs in one round of blocks
+  // (one per CU); every block works on one problem.
+  const int ipb = ug::gemv_items_per_block(items.data(), count, ug::kGemvBlocks);
+  int64_t blocks = 0, total_items = 0;
+  for (auto &d : descs) {
+    d.ipb = ipb;
+    d.blocks = (d.items + ipb - 1) / ipb;
+    d.block_begin = (int32_t)blocks;
+    blocks += d.blocks;
+    total_items += d.items;
+  }
+  if (blocks > INT32_MAX || total_items > INT32_MAX) return UG_ERR_UNSUPPORTED;
+  hipError_t e = hipMemcpy(plan, descs.data(), descs.size() * sizeof(ug::GemvDesc),
+                           hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_status(e);
+  info->count = count;
+  info->total_items = (int32_t)total_items;
+  info->variant = variant;
+  info->grid = (int32_t)blocks;
+  return UG_OK;
+}
+
+ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *info,
+                                    void *stream) {
+  if (plan == nullptr || !aligned16(plan) || info == nullptr) return UG_ERR_INVALID_ARG;
+  if (info->count < 1 || info->total_items < 1 || info->grid < 1) return UG_ERR_INVALID_ARG;
+  const int fmt = info->variant >> 4, mb = info->variant & 15;
+  if ((fmt != UG_W_I8 && fmt != UG_W_PACK5) || (mb != 1 && mb != 2 && mb != 4))
+    return UG_ERR_INVALID_ARG;
+  return hip_status(ug::launch_gemv_grouped((const ug::GemvDesc *)plan, info->count, info->grid,
+                                            info->variant, as_stream(stream)));
 }
 
 size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t wfmt) {

@@ -33,6 +33,43 @@ hipError_t launch_pack(const int8_t *wq, int64_t ldq, int64_t N, int64_t K,
 hipError_t launch_unpack(const uint8_t *packed, int64_t ldp, int64_t N,
                          int64_t K, int8_t *wq, int64_t ldq, int32_t *bad,
                          hipStream_t st);
+// One GEMV problem as the matrix-core GEMV kernel sees it (device-side
+// descriptor; also the element of a grouped plan).
+struct GemvDesc {
+  const float *x;      // fp32 activations quantized inside the launch, or null
+  int64_t ldx;
+  const int8_t *xq;    // int8 activations (x == null), else optional output
+  int64_t ldxq;
+  float *s;            // row scales: input (x == null) or optional output
+  const uint8_t *w;    // weights, UG_W_I8 or UG_W_PACK5 rows of ldw bytes
+  int64_t ldw;
+  const float *beta;
+  int32_t *acc;
+  int64_t ldacc;
+  float *y;
+  int64_t ldy;
+  float eps;           // activation-quantization eps (x != null)
+  int32_t wfmt;
+  int32_t M, N, K;
+  int32_t mb;          // 16-row activation blocks: 1, 2 or 4
+  int32_t items;       // work items (pairs of 16-row groups) of this problem
+  int32_t ipb;         // items per block
+  int32_t blocks;      // blocks working on this problem
+  int32_t block_begin; // grouped plan: first block of this problem
+};
+
+constexpr int kGemvBlocks = 256;  // one GEMV block per CU
+
+// Fills mb and items of d.
+void gemv_mfma_plan(GemvDesc &d);
+// Fewest items per block (a multiple of 8) keeping sum_p ceil(items_p /
+// ipb) <= cus.
+int gemv_items_per_block(const int *items, int count, int cus);
+// Whether the activations of a problem fit the kernel's LDS staging area
+// (required when the launch quantizes fp32 activations).
+bool gemv_stages_x(int wfmt, int64_t M, int64_t K);
+hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, int32_t count, int32_t grid,
+                               int32_t fmt_mb, hipStream_t st);
 hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const void *w, int wfmt, int64_t ldw, const float *beta,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,

@@ -47,11 +47,27 @@ SIGNATURES = {
     "ug_bitlinear_gemv": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
                                  _i64, _vp, _i64, _vp]),
     "ug_bitlinear_gemm_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "ug_gemv_plan_size": (_sz, [_i32]),
+    "ug_gemv_plan_init": (_i32, [_vp, _i32, _vp, _sz, _vp]),
+    "ug_bitlinear_gemv_grouped": (_i32, [_vp, _vp, _vp]),
     "ug_bitlinear_gemm": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
                                  _i64, _vp, _i64, _vp, _sz, _vp]),
 }
 
 _lib = None
+
+
+class GemvProblem(ctypes.Structure):
+    """ug_gemv_problem (include/ug.h)."""
+    _fields_ = [("x", _vp), ("ldx", _i64), ("eps", _f32), ("xq", _vp), ("ldxq", _i64),
+                ("s", _vp), ("w", _vp), ("wfmt", _i32), ("ldw", _i64), ("beta", _vp),
+                ("M", _i64), ("N", _i64), ("K", _i64), ("acc", _vp), ("ldacc", _i64),
+                ("y", _vp), ("ldy", _i64)]
+
+
+class GemvPlanInfo(ctypes.Structure):
+    """ug_gemv_plan_info (include/ug.h)."""
+    _fields_ = [("count", _i32), ("total_items", _i32), ("variant", _i32), ("grid", _i32)]
 
 
 class UgError(RuntimeError):
@@ -246,3 +262,52 @@ def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=F
                                    _ld(y) if y is not None else 0, _p(ws), ws_bytes,
                                    _stream(stream)), "ug_bitlinear_gemm")
     return acc, y
+
+
+class GemvPlan:
+    """A grouped-GEMV plan: the device descriptor buffer (a torch tensor)
+    plus the host launch info, and the tensors it names (kept alive)."""
+
+    def __init__(self, buf, info, keep):
+        self.buf = buf
+        self.info = info
+        self.keep = keep
+
+
+def ug_gemv_plan_size(count):
+    return lib().ug_gemv_plan_size(count)
+
+
+def ug_gemv_plan_init(problems, device=None):
+    """problems: list of dicts with keys x (fp32 [M,K] to quantize in the
+    launch) or xq+s (pre-quantized), w, wfmt, beta, K, y, and optionally
+    acc, xq/s as outputs when x is given, eps.  Returns a GemvPlan."""
+    arr = (GemvProblem * len(problems))()
+    keep = []
+    for i, p in enumerate(problems):
+        x, xq, s, w, y, acc = (p.get(k) for k in ("x", "xq", "s", "w", "y", "acc"))
+        ref = x if x is not None else xq
+        M = ref.shape[0]
+        K = p.get("K", ref.shape[1])
+        wfmt = p["wfmt"]
+        N = w.shape[0]
+        arr[i] = GemvProblem(
+            x=_p(x).value, ldx=_ld(x) if x is not None else 0, eps=p.get("eps", 1e-5),
+            xq=_p(xq).value, ldxq=_ld(xq) if xq is not None else 0, s=_p(s).value,
+            w=_p(w).value, wfmt=wfmt, ldw=_ld(w), beta=_p(p["beta"]).value, M=M, N=N, K=K,
+            acc=_p(acc).value, ldacc=_ld(acc) if acc is not None else 0,
+            y=_p(y).value, ldy=_ld(y) if y is not None else 0)
+        keep.append(p)
+    size = ug_gemv_plan_size(len(problems))
+    dev = device or ref.device
+    buf = torch.empty(size, dtype=torch.uint8, device=dev)
+    info = GemvPlanInfo()
+    _check(lib().ug_gemv_plan_init(ctypes.cast(arr, _vp), len(problems), _p(buf), size,
+                                   ctypes.byref(info)), "ug_gemv_plan_init")
+    return GemvPlan(buf, info, keep)
+
+
+def ug_bitlinear_gemv_grouped(plan, stream=None):
+    """One launch of every problem of a GemvPlan."""
+    _check(lib().ug_bitlinear_gemv_grouped(_p(plan.buf), ctypes.byref(plan.info),
+                                           _stream(stream)), "ug_bitlinear_gemv_grouped")

@@ -66,8 +66,11 @@ enum {
     UG_W_PACK5 = 1 /* five trits per byte (README "A whole ternary GPT"):
                       byte g of a row holds K positions 5g..5g+4 as
                       121 + t0 + 3 t1 + 9 t2 + 27 t3 + 81 t4 (t0 = lowest K);
-                      trits past K are 0; row bytes [ceil(K/5), ld) are pad;
-                      codes 243..255 are invalid and act as five 0 trits.  */
+                      trits past K are 0; row bytes [ceil(K/5), ld) are pad.
+                      Codes 243..255 are invalid: ug_unpack_trits counts them
+                      and writes five 0 trits; the matmuls' results for a
+                      row holding one are unspecified (other rows are exact,
+                      no access leaves the buffers).                        */
 };
 
 /* Largest K the matmuls accept: 127*K < 2^24 keeps (float)acc exact. */
@@ -174,6 +177,74 @@ ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s,
                             const float *beta, int64_t M, int64_t N,
                             int64_t K, int32_t *acc, int64_t ldacc, float *y,
                             int64_t ldy, void *stream);
+
+/*
+ * Grouped decode GEMV: several independent ug_bitlinear_gemv problems (for
+ * example every matrix of a batch-1 decode pass) in ONE launch, each with
+ * its own activations, weights, beta and outputs.  A problem may hand over
+ * fp32 activations instead of x_q: then the launch also performs
+ * ug_quant_act's per-row absmax quantization of them (same arithmetic, same
+ * bits), so quantization + GEMV of the whole group is a single kernel.
+ *
+ * ug_gemv_problem (host struct; all pointers device pointers):
+ *   x, ldx, eps  fp32 [M][ldx] activations to quantize in the launch, or
+ *                x == NULL to use xq/s as inputs;
+ *   xq, ldxq     int8 [M][ldxq]: input when x == NULL, else optional output
+ *                of the quantized activations (NULL: not written);
+ *   s            fp32 [M]: input when x == NULL, else optional output;
+ *   w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy: as ug_bitlinear_gemv.
+ * Every problem of a group has the same wfmt and the same activation-row
+ * class (M <= 16, 17..32 or 33..64).  With x != NULL the quantized rows
+ * must fit the kernel's 64 KB staging area: M * Kp <= 65536 with
+ * Kp = 320 * ceil(ceil(K/5) / 64) (UG_W_PACK5) or 64 * ceil(K / 64)
+ * (UG_W_I8), else UG_ERR_UNSUPPORTED.  Weights of N * ldw >= 2^31 bytes or
+ * activations of M * ldxq >= 2^31 bytes are UG_ERR_UNSUPPORTED (32-bit
+ * offsets), here and in ug_bitlinear_gemv.
+ */
+typedef struct ug_gemv_problem {
+    const float *x;
+    int64_t ldx;
+    float eps;
+    int8_t *xq;
+    int64_t ldxq;
+    float *s;
+    const void *w;
+    int32_t wfmt;
+    int64_t ldw;
+    const float *beta;
+    int64_t M, N, K;
+    int32_t *acc;
+    int64_t ldacc;
+    float *y;
+    int64_t ldy;
+} ug_gemv_problem;
+
+/* What the launch needs besides the device plan (filled by plan_init). */
+typedef struct ug_gemv_plan_info {
+    int32_t count;        /* problems                                  */
+    int32_t total_items;  /* work items over all problems              */
+    int32_t variant;      /* kernel variant (format and row class)     */
+    int32_t grid;         /* blocks to launch                          */
+} ug_gemv_plan_info;
+
+/* Device bytes a plan of `count` problems occupies (0 if count < 1). */
+size_t ug_gemv_plan_size(int32_t count);
+
+/*
+ * Validates `count` host problems, lays out their tiling and copies the
+ * plan to the device buffer `plan` (16-byte aligned, >= ug_gemv_plan_size).
+ * A set-up call: it blocks until the plan is on the device.  The plan stays
+ * valid as long as the buffers it names do; replaying the grouped launch
+ * (for example from a captured HIP graph) needs no further host work.
+ */
+ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count,
+                            void *plan, size_t plan_bytes,
+                            ug_gemv_plan_info *info);
+
+/* One launch of every problem of a plan on `stream`. */
+ug_status ug_bitlinear_gemv_grouped(const void *plan,
+                                    const ug_gemv_plan_info *info,
+                                    void *stream);
 
 /* Bytes of workspace ug_bitlinear_gemm needs (0 for UG_W_I8). */
 size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K,

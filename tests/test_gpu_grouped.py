@@ -1,0 +1,139 @@
+"""Grouped decode GEMV (ug_gemv_plan_init + ug_bitlinear_gemv_grouped):
+several independent problems in one launch, optionally quantizing fp32
+activations inside the launch.  Every problem is compared with the CPU
+oracle: x_q, s, int32 accumulators bit-exact, y within 1e-6 relative."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bitlinear_matmul_amd import inputs, ug
+from gpu_util import assert_bits_equal, assert_y_close, host, pitched, scalar_dev, vec
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(*a):
+    print("case:", *a, flush=True)
+
+
+def test_decode_stack_one_launch_fused_quant(dev):
+    """All 33 matrices of the batch-1 decode pass, fp32 activations in, one
+    launch: act quant + GEMV."""
+    probs, refs = [], []
+    for (layer, mi, name, K, N) in inputs.decode_stack_shapes():
+        x, W = inputs.decode_stack_matrix(layer, mi, K, N)
+        wq_r, beta_r = oracle.quant_weight_absmean(W)
+        pk_r, _ = oracle.pack_trits(wq_r)
+        p = dict(x=pitched(x), w=pitched(pk_r), wfmt=ug.UG_W_PACK5, beta=scalar_dev(beta_r),
+                 K=K, xq=ug.empty_pitched(1, K, torch.int8, dev),
+                 s=torch.empty(1, dtype=torch.float32, device=dev),
+                 y=ug.empty_pitched(1, N, torch.float32, dev),
+                 acc=ug.empty_pitched(1, N, torch.int32, dev))
+        probs.append(p)
+        xq_r, s_r = oracle.quant_act(x)
+        acc_r = oracle.matmul_i32(xq_r, wq_r)
+        refs.append((xq_r, s_r, acc_r, oracle.epilogue(acc_r, s_r, beta_r)))
+    plan = ug.ug_gemv_plan_init(probs)
+    assert plan.info.count == 33
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for i, (p, (xq_r, s_r, acc_r, y_r)) in enumerate(zip(probs, refs)):
+        assert_bits_equal(host(p["xq"]), xq_r, "x_q %d" % i)
+        assert_bits_equal(host(p["s"]), s_r, "s %d" % i)
+        assert_bits_equal(host(p["acc"]), acc_r, "acc %d" % i)
+        assert_y_close(host(p["y"]), y_r, "y %d" % i)
+        assert_bits_equal(host(p["y"]), y_r, "y bits %d" % i)
+    # replay: same bits
+    y0 = [host(p["y"]).copy() for p in probs]
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for p, a in zip(probs, y0):
+        assert_bits_equal(host(p["y"]), a, "replay")
+
+
+GROUPS = [
+    # (wfmt, M, list of (N, K)) -- M fixes the activation-row class
+    (ug.UG_W_PACK5, 1, [(6912, 2560), (2560, 6912), (2560, 2560), (17, 7), (100, 81)]),
+    (ug.UG_W_PACK5, 4, [(6912, 2560), (2560, 6912), (1000, 1001)]),
+    (ug.UG_W_PACK5, 16, [(512, 384), (2560, 6912), (33, 1536)]),
+    (ug.UG_W_PACK5, 20, [(300, 2560), (64, 3000)]),
+    (ug.UG_W_PACK5, 64, [(256, 1280), (100, 320), (16, 7)]),
+    (ug.UG_W_I8, 1, [(512, 128), (2560, 4000), (70, 33)]),
+    (ug.UG_W_I8, 16, [(1000, 1024), (64, 4096)]),
+    (ug.UG_W_I8, 33, [(128, 640), (99, 100)]),
+]
+
+
+@pytest.mark.parametrize("gi", range(len(GROUPS)))
+@pytest.mark.parametrize("fused", [False, True])
+def test_grouped_parity(dev, gi, fused):
+    wfmt, M, shapes = GROUPS[gi]
+    _case("grouped", gi, wfmt, M, fused)
+    rng = np.random.default_rng([300, gi, int(fused)])
+    probs, refs = [], []
+    for (N, K) in shapes:
+        kp = (64 * -(-K // 64)) if wfmt == ug.UG_W_I8 else 320 * -(-(-(-K // 5)) // 64)
+        if fused and M * kp > 65536:   # the documented staging limit
+            continue
+        x = rng.standard_normal((M, K), dtype=np.float32)
+        wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        beta = np.float32(0.015 + 0.001 * len(probs))
+        xq_r, s_r = oracle.quant_act(x)
+        w = pitched(oracle.pack_trits(wq)[0]) if wfmt == ug.UG_W_PACK5 else pitched(wq)
+        p = dict(w=w, wfmt=wfmt, beta=scalar_dev(beta), K=K,
+                 y=ug.empty_pitched(M, N, torch.float32, dev),
+                 acc=ug.empty_pitched(M, N, torch.int32, dev))
+        if fused:
+            p.update(x=pitched(x), xq=ug.empty_pitched(M, K, torch.int8, dev),
+                     s=torch.empty(M, dtype=torch.float32, device=dev))
+        else:
+            p.update(xq=pitched(xq_r), s=vec(s_r))
+        probs.append(p)
+        acc_r = oracle.matmul_i32(xq_r, wq)
+        refs.append((xq_r, s_r, acc_r, oracle.epilogue(acc_r, s_r, beta)))
+    if not probs:
+        pytest.skip("no problem small enough for fused quantization")
+    plan = ug.ug_gemv_plan_init(probs)
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for i, (p, (xq_r, s_r, acc_r, y_r)) in enumerate(zip(probs, refs)):
+        if fused:
+            assert_bits_equal(host(p["xq"]), xq_r, "x_q %d" % i)
+            assert_bits_equal(host(p["s"]), s_r, "s %d" % i)
+        assert_bits_equal(host(p["acc"]), acc_r, "acc %d" % i)
+        assert_y_close(host(p["y"]), y_r, "y %d" % i)
+
+
+def test_grouped_many_problems_multi_item_blocks(dev):
+    """A group large enough that every block walks several items."""
+    rng = np.random.default_rng(301)
+    K, N, G = 2560, 6912, 48
+    wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    pk = pitched(oracle.pack_trits(wq)[0])
+    xs = [rng.standard_normal((1, K), dtype=np.float32) for _ in range(G)]
+    probs = [dict(x=pitched(x), w=pk, wfmt=ug.UG_W_PACK5, beta=scalar_dev(np.float32(0.02)),
+                  K=K, y=ug.empty_pitched(1, N, torch.float32, dev)) for x in xs]
+    plan = ug.ug_gemv_plan_init(probs)
+    assert plan.info.grid < plan.info.total_items
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for i in (0, 17, G - 1):
+        xq_r, s_r = oracle.quant_act(xs[i])
+        y_r = oracle.epilogue(oracle.matmul_i32(xq_r, wq), s_r, np.float32(0.02))
+        assert_bits_equal(host(probs[i]["y"]), y_r, "y %d" % i)
+
+
+def test_grouped_plan_rejects(dev):
+    rng = np.random.default_rng(302)
+    wq = rng.integers(-1, 2, size=(64, 256)).astype(np.int8)
+    x = pitched(rng.standard_normal((1, 256), dtype=np.float32))
+    y = ug.empty_pitched(1, 64, torch.float32, dev)
+    b = scalar_dev(np.float32(0.02))
+    p8 = dict(x=x, w=pitched(wq), wfmt=ug.UG_W_I8, beta=b, y=y)
+    p5 = dict(x=x, w=pitched(oracle.pack_trits(wq)[0]), wfmt=ug.UG_W_PACK5, beta=b, K=256, y=y)
+    with pytest.raises(ug.UgError) as e:
+        ug.ug_gemv_plan_init([p8, p5])   # mixed formats
+    assert e.value.status == ug.UG_ERR_INVALID_ARG
+    big = dict(x=pitched(rng.standard_normal((17, 4000), dtype=np.float32)),
+               w=pitched(rng.integers(-1, 2, size=(8, 4000)).astype(np.int8)), wfmt=ug.UG_W_I8,
+               beta=b, y=ug.empty_pitched(17, 8, torch.float32, dev))
+    with pytest.raises(ug.UgError) as e:
+        ug.ug_gemv_plan_init([big])      # fused quant with M*K > 65536
+    assert e.value.status == ug.UG_ERR_UNSUPPORTED

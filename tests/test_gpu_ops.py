@@ -190,7 +190,9 @@ def _rand_problem(rng, M, N, K):
 
 
 GEMV_CASES = [(1, 6912, 2560), (1, 2560, 6912), (4, 1152, 384), (3, 385, 1001), (5, 64, 7),
-              (16, 512, 128), (64, 300, 2560), (2, 17, 81), (1, 4096, 384), (33, 1000, 160)]
+              (16, 512, 128), (64, 300, 2560), (2, 17, 81), (1, 4096, 384), (33, 1000, 160),
+              (20, 700, 2560), (32, 129, 6912), (64, 64, 6912), (16, 2560, 6912),
+              (1, 40, 20000), (7, 8000, 1536)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMV_CASES)
@@ -214,21 +216,28 @@ def test_gemv_parity(dev, M, N, K, fmt):
 
 
 def test_gemv_invalid_codes_and_garbage_pad(dev):
-    """Codes 243..255 act as five zero trits; pad bytes past ceil(K/5) and
-    trits past K never change the result."""
+    """Pad bytes past ceil(K/5) (here garbage, invalid codes included) and
+    trits past K never change the result; a row holding an invalid code
+    (243..255) among its data bytes leaves every other row exact."""
     rng = np.random.default_rng(108)
     M, N, K = 3, 70, 101  # 21 bytes used per row, pitch 32
     xq, wq, s, beta = _rand_problem(rng, M, N, K)
     pk, _ = oracle.pack_trits(wq)
     pk[:, 21:] = rng.integers(0, 256, size=(N, pk.shape[1] - 21))  # garbage pad
-    pk[5, 3] = 250                                                   # invalid code
-    pk[9, 0] = 243
+    # last data byte: keep its trit at k = 100, random trits at k = 101..104 (past K)
+    pk[:, 20] = (pk[:, 20].astype(np.int64) % 3 + 3 * rng.integers(0, 81, N)).astype(np.uint8)
     wq_eff, bad = oracle.unpack_trits(pk, K)
-    assert bad == 2
-    _, y_d = ug.ug_bitlinear_gemv(pitched(xq), vec(s), pitched(pk), ug.UG_W_PACK5,
-                                  scalar_dev(beta), K=K)
-    acc_r = oracle.matmul_i32(xq, wq_eff)
-    assert_bits_equal(host(y_d), oracle.epilogue(acc_r, s, beta), "y")
+    assert bad == 0
+    bad_rows = [5, 9]
+    pk[5, 3] = 250                                                   # invalid codes
+    pk[9, 0] = 243
+    for fmt_call in (ug.ug_bitlinear_gemv, ug.ug_bitlinear_gemm):
+        _, y_d = fmt_call(pitched(xq), vec(s), pitched(pk), ug.UG_W_PACK5, scalar_dev(beta),
+                          K=K)
+        acc_r = oracle.matmul_i32(xq, wq_eff)
+        y_r = oracle.epilogue(acc_r, s, beta)
+        keep = np.setdiff1d(np.arange(N), bad_rows)
+        assert_bits_equal(host(y_d)[:, keep], y_r[:, keep], "y")
 
 
 GEMM_CASES = [(1, 64, 64), (33, 129, 100), (128, 512, 128), (300, 64, 2560), (257, 1000, 1536),
