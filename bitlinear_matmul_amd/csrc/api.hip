@@ -158,7 +158,6 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
   if (plan == nullptr || !aligned16(plan) || plan_bytes < ug_gemv_plan_size(count))
     return UG_ERR_WORKSPACE;
   std::vector<ug::GemvDesc> descs((size_t)count);
-  std::vector<int> items((size_t)count);
   int variant = -1;
   for (int32_t i = 0; i < count; ++i) {
     const ug_gemv_problem &p = problems[i];
@@ -198,21 +197,17 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
     const int v = 16 * d.wfmt + d.mb;
     if (variant >= 0 && v != variant) return UG_ERR_INVALID_ARG;
     variant = v;
-    items[(size_t)i] = d.items;
     descs[(size_t)i] = d;
   }
-  // Items per block such that the whole group runs in one round of blocks
-  // (one per CU); every block works on one problem.
-  const int ipb = ug::gemv_items_per_block(items.data(), count, ug::kGemvBlocks);
-  int64_t blocks = 0, total_items = 0;
+  // Blocks take balanced ranges of the items of all problems (one round,
+  // one block per CU).
+  int64_t total_items = 0;
   for (auto &d : descs) {
-    d.ipb = ipb;
-    d.blocks = (d.items + ipb - 1) / ipb;
-    d.block_begin = (int32_t)blocks;
-    blocks += d.blocks;
+    d.item_begin = (int32_t)total_items;
     total_items += d.items;
   }
-  if (blocks > INT32_MAX || total_items > INT32_MAX) return UG_ERR_UNSUPPORTED;
+  if (total_items > INT32_MAX) return UG_ERR_UNSUPPORTED;
+  const int64_t blocks = ug::gemv_grid(total_items);
   hipError_t e = hipMemcpy(plan, descs.data(), descs.size() * sizeof(ug::GemvDesc),
                            hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_status(e);
@@ -230,8 +225,9 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *i
   const int fmt = info->variant >> 4, mb = info->variant & 15;
   if ((fmt != UG_W_I8 && fmt != UG_W_PACK5) || (mb != 1 && mb != 2 && mb != 4))
     return UG_ERR_INVALID_ARG;
-  return hip_status(ug::launch_gemv_grouped((const ug::GemvDesc *)plan, info->count, info->grid,
-                                            info->variant, as_stream(stream)));
+  return hip_status(ug::launch_gemv_grouped((const ug::GemvDesc *)plan, info->count,
+                                            info->total_items, info->grid, info->variant,
+                                            as_stream(stream)));
 }
 
 size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t wfmt) {

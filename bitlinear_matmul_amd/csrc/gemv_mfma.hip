@@ -27,7 +27,7 @@
 //   and a wave's 64 reads fall in 64 different banks.
 //
 // Work: a block of 8 waves (one block per CU) takes a range of items of one
-// problem; an item is 2 row groups (32 weight rows) over the whole K, split
+// problem; an item is 2 or 4 row groups (32 or 64 weight rows) over the whole K, split
 // into units of SC steps.  Each wave walks its items' units keeping the
 // weights of the next two units in flight (buffer loads: lanes past the row,
 // past N or past the work read zeros without touching memory, so the loop
@@ -48,7 +48,6 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kRepl = 64;          // table replicas: one per lane of a wave
 constexpr int kXsBytes = 65536;    // staged activations
 constexpr int kZero = kXsBytes;    // 80 zero bytes right after them
-constexpr int kRGW = 2;            // row groups per item
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every buffer used here
 
 template <int FMT>
@@ -68,10 +67,11 @@ struct Fmt<UG_W_I8> {
 
 template <int FMT, int MB>
 struct Cfg {
+  static constexpr int RGW = 2;  // row groups per item (they share each activation read)
   // steps per unit (three units of weights are in flight per wave)
   static constexpr int SC = FMT == UG_W_PACK5 ? (MB == 1 ? 4 : (MB == 2 ? 2 : 1)) : (MB == 4 ? 2 : 4);
   // independent MFMA chains per output tile
-  static constexpr int NACC = FMT == UG_W_PACK5 ? (MB == 1 ? 5 : (MB == 2 ? 2 : 1)) : 2;
+  static constexpr int NACC = FMT == UG_W_PACK5 ? (MB == 1 ? 2 : (MB == 2 ? 2 : 1)) : 2;
 };
 
 __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int K) {
@@ -178,9 +178,9 @@ struct Smem {
 // first block.  Ends with a barrier.
 template <int FMT>
 __device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool staged,
-                                      bool write_outputs) {
+                                      bool write_outputs, bool build_table) {
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
-  if (FMT == UG_W_PACK5 && tid < 256) sh.lut_tmp[tid] = lut4_entry(tid);
+  if (FMT == UG_W_PACK5 && build_table && tid < 256) sh.lut_tmp[tid] = lut4_entry(tid);
   if (tid < 64) sh.cm[tid] = 0;
   if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
   if (d.x) {  // row scales s = fl(fl(max|x| / 127) + eps), one wave per row
@@ -200,7 +200,7 @@ __device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool sta
     }
   }
   __syncthreads();
-  if (FMT == UG_W_PACK5) {  // 64 replicas in 16-byte chunks, consecutive lanes
+  if (FMT == UG_W_PACK5 && build_table) {  // 64 replicas in 16-byte chunks, consecutive lanes
     uint4 *chunks = reinterpret_cast<uint4 *>(sh.lut);
 #pragma unroll
     for (int i = 0; i < 256 * kRepl / 4 / kThreads; ++i) {
@@ -288,6 +288,7 @@ struct Wave {
   static constexpr int F1 = Fmt<FMT>::kFrag;
   static constexpr int SC = Cfg<FMT, MB>::SC;
   static constexpr int NACC = Cfg<FMT, MB>::NACC;
+  static constexpr int kRGW = Cfg<FMT, MB>::RGW;
 
   int S, NC, rowb16, Kp;
   bool staged;
@@ -359,34 +360,50 @@ struct Wave {
     }
   }
 
-  // Multiply-accumulate one unit (SC steps of both row groups).
+  // Multiply-accumulate one unit (SC steps of every row group of the item).
+  // The table reads of the next (step, row group) pair are issued before the
+  // MFMAs of the current one.
   __device__ __forceinline__ void compute(const GemvDesc &d, const int8_t *xs, const char *lut,
                                           int ch, const uint4 (&wb)[kRGW][SC],
                                           v4i (&acc)[kRGW][MB][NACC]) {
     const uint32_t lr4 = 4u * (threadIdx.x & 63);
-#pragma unroll
-    for (int s = 0; s < SC; ++s) {
-      const int st = ch * SC + s;
+    if (FMT == UG_W_PACK5) {
+      constexpr int NP = SC * kRGW;
+      uint32_t T[2][20];
+      auto dec = [&](int p, uint32_t(&t)[20]) {
+        const uint4 &w = wb[p % kRGW][p / kRGW];
+        decode4(w.x, lut, lr4, t, t[16]);
+        decode4(w.y, lut, lr4, t + 4, t[17]);
+        decode4(w.z, lut, lr4, t + 8, t[18]);
+        decode4(w.w, lut, lr4, t + 12, t[19]);
+      };
       v4i xf[MB][F1];
+      dec(0, T[0]);
 #pragma unroll
-      for (int b = 0; b < MB; ++b) xfrags(d, xs, st, b, xf[b]);
+      for (int p = 0; p < NP; ++p) {
+        const int s = p / kRGW, r = p % kRGW;
+        if (r == 0)
 #pragma unroll
-      for (int r = 0; r < kRGW; ++r) {
-        if (FMT == UG_W_PACK5) {
-          uint32_t t[20];
-          decode4(wb[r][s].x, lut, lr4, t, t[16]);
-          decode4(wb[r][s].y, lut, lr4, t + 4, t[17]);
-          decode4(wb[r][s].z, lut, lr4, t + 8, t[18]);
-          decode4(wb[r][s].w, lut, lr4, t + 12, t[19]);
+          for (int b = 0; b < MB; ++b) xfrags(d, xs, ch * SC + s, b, xf[b]);
+        if (p + 1 < NP) dec(p + 1, T[(p + 1) & 1]);
+        const uint32_t(&t)[20] = T[p & 1];
 #pragma unroll
-          for (int j = 0; j < 5; ++j) {
-            const v4i B = {(int)t[4 * j], (int)t[4 * j + 1], (int)t[4 * j + 2], (int)t[4 * j + 3]};
+        for (int j = 0; j < 5; ++j) {
+          const v4i B = {(int)t[4 * j], (int)t[4 * j + 1], (int)t[4 * j + 2], (int)t[4 * j + 3]};
 #pragma unroll
-            for (int b = 0; b < MB; ++b)
-              acc[r][b][j % NACC] =
-                  __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[b][j], B, acc[r][b][j % NACC], 0, 0, 0);
-          }
-        } else {
+          for (int b = 0; b < MB; ++b)
+            acc[r][b][j % NACC] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[b][j], B, acc[r][b][j % NACC], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < SC; ++s) {
+        v4i xf[MB][F1];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) xfrags(d, xs, ch * SC + s, b, xf[b]);
+#pragma unroll
+        for (int r = 0; r < kRGW; ++r) {
           const v4i B = {(int)wb[r][s].x, (int)wb[r][s].y, (int)wb[r][s].z, (int)wb[r][s].w};
 #pragma unroll
           for (int b = 0; b < MB; ++b)
@@ -427,28 +444,24 @@ struct Wave {
   }
 };
 
-// Block `lb` of problem d: items [lb * ipb, min((lb + 1) * ipb, items)),
-// wave w taking items w, w + 8, ... of that range; each item is NC units.
+// Items [i0, i1) of problem d: wave w takes items i0 + w, i0 + w + 8, ...,
+// each NC units, with the weights of the next two units in flight.
 template <int FMT, int MB>
-__device__ __forceinline__ void gemv_block(const GemvDesc &d, int lb) {
+__device__ __forceinline__ void gemv_items(const GemvDesc &d, Smem<FMT> &sh, bool staged,
+                                           int i0, int i1) {
   using W = Wave<FMT, MB>;
-  constexpr int SC = W::SC, NACC = W::NACC;
-  __shared__ Smem<FMT> sh;
-  const bool staged = stages_x(FMT, d.M, d.K);
-  setup<FMT>(d, sh, staged, lb == 0);
+  constexpr int SC = W::SC, NACC = W::NACC, kRGW = W::kRGW;
   W wv;
   wv.init(d, staged);
   const int wave = uniform(threadIdx.x >> 6);
-  const int ib = lb * d.ipb;
-  const int ie = min(ib + d.ipb, d.items);
-  const int my_items = ib + wave < ie ? (ie - ib - wave + kWaves - 1) / kWaves : 0;
+  const int my_items = i0 + wave < i1 ? (i1 - i0 - wave + kWaves - 1) / kWaves : 0;
   const int U = uniform(my_items * wv.NC);
   const float beta = d.beta[0];
   const char *lut = reinterpret_cast<const char *>(sh.lut);
 
   uint4 A[kRGW][SC], B[kRGW][SC], C[kRGW][SC];
   v4i acc[kRGW][MB][NACC];
-  auto unit_item = [&](int u) { return ib + wave + kWaves * (u / wv.NC); };
+  auto unit_item = [&](int u) { return i0 + wave + kWaves * (u / wv.NC); };
   auto unit_ch = [&](int u) { return u % wv.NC; };
   auto issue = [&](int u, uint4(&buf)[kRGW][SC]) {
     wv.issue(d, unit_item(u), unit_ch(u), u < U, buf);
@@ -481,79 +494,86 @@ __device__ __forceinline__ void gemv_block(const GemvDesc &d, int lb) {
   }
 }
 
+// Block b of nb takes the global items [b T / nb, (b + 1) T / nb) of the
+// plan (T items over all problems, problem p owning [item_begin, +items)),
+// crossing into the next problem when its range does.
 template <int FMT, int MB>
-__global__ __launch_bounds__(kThreads) void gemv_single_kernel(GemvDesc d) {
-  gemv_block<FMT, MB>(d, blockIdx.x);
-}
-
-// Grouped: plan[p] owns blocks [block_begin, block_begin + blocks); a block
-// finds its problem once, by binary search.
-template <int FMT, int MB>
-__global__ __launch_bounds__(kThreads) void gemv_grouped_kernel(const GemvDesc *__restrict__ plan,
-                                                                int count) {
-  const int b = blockIdx.x;
-  int lo = 0, hi = count - 1;
+__device__ __forceinline__ void gemv_block(const GemvDesc *plan, int count, int64_t T, int b,
+                                           int nb) {
+  __shared__ Smem<FMT> sh;
+  const int g0 = (int)(T * b / nb), g1 = (int)(T * (b + 1) / nb);
+  if (g0 >= g1) return;
+  int lo = 0, hi = count - 1;  // problem holding item g0
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (plan[mid].block_begin <= b)
+    if (plan[mid].item_begin <= g0)
       lo = mid;
     else
       hi = mid - 1;
   }
-  const GemvDesc d = plan[lo];
-  const int lb = b - d.block_begin;
-  if (lb >= d.blocks) return;
-  gemv_block<FMT, MB>(d, lb);
+  bool first = true;
+  for (int p = lo, g = g0; g < g1 && p < count; ++p) {
+    const GemvDesc d = plan[p];
+    const int e = min(g1, d.item_begin + d.items);
+    if (e <= g) continue;
+    if (!first) __syncthreads();  // the previous problem's staged rows are done
+    const bool staged = stages_x(FMT, d.M, d.K);
+    setup<FMT>(d, sh, staged, g == d.item_begin, first);
+    first = false;
+    gemv_items<FMT, MB>(d, sh, staged, g - d.item_begin, e - d.item_begin);
+    g = e;
+  }
+}
+
+template <int FMT, int MB>
+__global__ __launch_bounds__(kThreads) void gemv_single_kernel(GemvDesc d) {
+  gemv_block<FMT, MB>(&d, 1, d.items, blockIdx.x, gridDim.x);
+}
+
+template <int FMT, int MB>
+__global__ __launch_bounds__(kThreads) void gemv_grouped_kernel(const GemvDesc *__restrict__ plan,
+                                                                int count, int total) {
+  gemv_block<FMT, MB>(plan, count, total, blockIdx.x, gridDim.x);
 }
 
 template <int FMT>
-hipError_t launch_single_fmt(const GemvDesc &d, hipStream_t st) {
+hipError_t launch_single_fmt(const GemvDesc &d, int grid, hipStream_t st) {
   switch (d.mb) {
-    case 1: hipLaunchKernelGGL((gemv_single_kernel<FMT, 1>), dim3(d.blocks), dim3(kThreads), 0, st, d); break;
-    case 2: hipLaunchKernelGGL((gemv_single_kernel<FMT, 2>), dim3(d.blocks), dim3(kThreads), 0, st, d); break;
-    default: hipLaunchKernelGGL((gemv_single_kernel<FMT, 4>), dim3(d.blocks), dim3(kThreads), 0, st, d); break;
+    case 1: hipLaunchKernelGGL((gemv_single_kernel<FMT, 1>), dim3(grid), dim3(kThreads), 0, st, d); break;
+    case 2: hipLaunchKernelGGL((gemv_single_kernel<FMT, 2>), dim3(grid), dim3(kThreads), 0, st, d); break;
+    default: hipLaunchKernelGGL((gemv_single_kernel<FMT, 4>), dim3(grid), dim3(kThreads), 0, st, d); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Blocks for a set of problems with `items` each: the fewest items per block
-// (a multiple of the 8 waves) that keeps the whole launch within `cus`
-// blocks, so every block runs in one round.
-int gemv_items_per_block(const int *items, int count, int cus) {
-  int64_t total = 0;
-  for (int i = 0; i < count; ++i) total += items[i];
-  int lo = 1, hi = (int)((total + kWaves - 1) / kWaves) + 1;  // in units of 8 items
-  while (lo < hi) {
-    const int mid = (lo + hi) / 2;
-    int64_t blocks = 0;
-    for (int i = 0; i < count; ++i) blocks += (items[i] + kWaves * mid - 1) / (kWaves * mid);
-    if (blocks <= cus)
-      hi = mid;
-    else
-      lo = mid + 1;
-  }
-  return kWaves * lo;
+// Blocks for T items: one per CU when there are enough items, else one per
+// 4 items (a small group is latency-bound: more CUs, shorter waits).
+int gemv_grid(int64_t total_items) {
+  const int64_t by_items = (total_items + 3) / 4;
+  return (int)(by_items < kGemvBlocks ? (by_items < 1 ? 1 : by_items) : kGemvBlocks);
 }
 
 void gemv_mfma_plan(GemvDesc &d) {
   d.mb = d.M <= 16 ? 1 : (d.M <= 32 ? 2 : 4);
+  const int rgw = d.wfmt == UG_W_PACK5 ? (d.mb == 1 ? Cfg<UG_W_PACK5, 1>::RGW : Cfg<UG_W_PACK5, 2>::RGW)
+                                       : Cfg<UG_W_I8, 1>::RGW;
   const int RG = (d.N + 15) / 16;
-  d.items = (RG + kRGW - 1) / kRGW;
+  d.items = (RG + rgw - 1) / rgw;
 }
 
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
   return K <= UG_MAX_K && M <= 64 && stages_x(wfmt, (int)M, (int)K);
 }
 
-hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, int32_t count, int32_t grid,
-                               int32_t fmt_mb, hipStream_t st) {
+hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, int32_t count, int32_t total_items,
+                               int32_t grid, int32_t fmt_mb, hipStream_t st) {
   // fmt_mb = 16 * wfmt + mb (every problem of a plan shares both)
   const int fmt = fmt_mb >> 4, mb = fmt_mb & 15;
   dim3 g(grid), b(kThreads);
 #define UG_GROUPED(F, MBV) \
-  hipLaunchKernelGGL((gemv_grouped_kernel<F, MBV>), g, b, 0, st, plan_dev, count)
+  hipLaunchKernelGGL((gemv_grouped_kernel<F, MBV>), g, b, 0, st, plan_dev, count, total_items)
   if (fmt == UG_W_PACK5) {
     if (mb == 1) UG_GROUPED(UG_W_PACK5, 1);
     else if (mb == 2) UG_GROUPED(UG_W_PACK5, 2);
@@ -587,11 +607,10 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
   d.N = (int32_t)N;
   d.K = (int32_t)K;
   gemv_mfma_plan(d);
-  d.ipb = gemv_items_per_block(&d.items, 1, kGemvBlocks);
-  d.blocks = (d.items + d.ipb - 1) / d.ipb;
-  d.block_begin = 0;
-  if (wfmt == UG_W_PACK5) return launch_single_fmt<UG_W_PACK5>(d, st);
-  return launch_single_fmt<UG_W_I8>(d, st);
+  d.item_begin = 0;
+  const int grid = gemv_grid(d.items);
+  if (wfmt == UG_W_PACK5) return launch_single_fmt<UG_W_PACK5>(d, grid, st);
+  return launch_single_fmt<UG_W_I8>(d, grid, st);
 }
 
 }  // namespace ug

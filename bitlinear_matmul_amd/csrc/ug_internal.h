@@ -52,24 +52,21 @@ struct GemvDesc {
   int32_t wfmt;
   int32_t M, N, K;
   int32_t mb;          // 16-row activation blocks: 1, 2 or 4
-  int32_t items;       // work items (pairs of 16-row groups) of this problem
-  int32_t ipb;         // items per block
-  int32_t blocks;      // blocks working on this problem
-  int32_t block_begin; // grouped plan: first block of this problem
+  int32_t items;       // work items (sets of 16-row groups) of this problem
+  int32_t item_begin;  // first item of this problem in a grouped plan
 };
 
 constexpr int kGemvBlocks = 256;  // one GEMV block per CU
 
 // Fills mb and items of d.
 void gemv_mfma_plan(GemvDesc &d);
-// Fewest items per block (a multiple of 8) keeping sum_p ceil(items_p /
-// ipb) <= cus.
-int gemv_items_per_block(const int *items, int count, int cus);
+// Blocks to launch for a plan of `total_items` items.
+int gemv_grid(int64_t total_items);
 // Whether the activations of a problem fit the kernel's LDS staging area
 // (required when the launch quantizes fp32 activations).
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K);
-hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, int32_t count, int32_t grid,
-                               int32_t fmt_mb, hipStream_t st);
+hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, int32_t count, int32_t total_items,
+                               int32_t grid, int32_t fmt_mb, hipStream_t st);
 hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const void *w, int wfmt, int64_t ldw, const float *beta,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,
