@@ -80,11 +80,19 @@ __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int K) {
 __host__ __device__ __forceinline__ int steps_of(int fmt, int K) {
   return (row_bytes_of(fmt, K) + 63) / 64;
 }
-__host__ __device__ __forceinline__ int staged_kp(int fmt, int K) {
-  return steps_of(fmt, K) * (fmt == UG_W_PACK5 ? 320 : 64);
+__host__ __device__ __forceinline__ int sc_of(int fmt, int mb) {
+  return fmt == UG_W_PACK5 ? (mb == 1 ? Cfg<UG_W_PACK5, 1>::SC : (mb == 2 ? Cfg<UG_W_PACK5, 2>::SC : Cfg<UG_W_PACK5, 4>::SC))
+                           : (mb == 1 ? Cfg<UG_W_I8, 1>::SC : (mb == 2 ? Cfg<UG_W_I8, 2>::SC : Cfg<UG_W_I8, 4>::SC));
 }
+// Staged row length: whole units of steps, zero past K, so every step a
+// wave multiplies has activations (zeros past K) inside its row.
+__host__ __device__ __forceinline__ int staged_kp(int fmt, int mb, int K) {
+  const int sc = sc_of(fmt, mb);
+  return ((steps_of(fmt, K) + sc - 1) / sc) * sc * (fmt == UG_W_PACK5 ? 320 : 64);
+}
+__host__ __device__ __forceinline__ int mb_of(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 __host__ __device__ __forceinline__ bool stages_x(int fmt, int M, int K) {
-  return (int64_t)M * staged_kp(fmt, K) <= kXsBytes;
+  return (int64_t)M * staged_kp(fmt, mb_of(M), K) <= kXsBytes;
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -213,7 +221,7 @@ __device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool sta
     // window = 80 (five trits per byte) or 16 (one per byte) K positions;
     // every thread stages whole windows, all its loads issued first
     constexpr int WIN = FMT == UG_W_PACK5 ? 80 : 16;
-    const int Kp = staged_kp(FMT, d.K);
+    const int Kp = staged_kp(FMT, mb_of(d.M), d.K);
     const int wpr = Kp / WIN;  // windows per row
     const int nwin = d.M * wpr;
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
@@ -268,7 +276,7 @@ __device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool sta
       for (int m = tid; m < d.M; m += kThreads) d.s[m] = sh.sm[m];
     if (d.xq) {  // undo the staging permutation: read back per K position
       int8_t *xq = const_cast<int8_t *>(d.xq);
-      const int Kp = staged_kp(FMT, d.K);
+      const int Kp = staged_kp(FMT, mb_of(d.M), d.K);
       for (int idx = tid; idx < d.M * d.K; idx += kThreads) {
         const int m = idx / d.K, k = idx - m * d.K;
         int off = k;
@@ -290,73 +298,83 @@ struct Wave {
   static constexpr int NACC = Cfg<FMT, MB>::NACC;
   static constexpr int kRGW = Cfg<FMT, MB>::RGW;
 
-  int S, NC, rowb16, Kp;
+  int S, NC, Kp;
   bool staged;
+  int xbase[MB];  // staged: LDS offset of this lane's activation row (step 0)
   __amdgpu_buffer_rsrc_t wr, xr;
 
   __device__ __forceinline__ void init(const GemvDesc &d, bool stg) {
+    const int lane = threadIdx.x & 63, q = lane >> 4;
     S = steps_of(FMT, d.K);
     NC = (S + SC - 1) / SC;
-    rowb16 = (row_bytes_of(FMT, d.K) + 15) & ~15;
-    Kp = staged_kp(FMT, d.K);
+    Kp = staged_kp(FMT, MB, d.K);
     staged = stg;
     wr = buffer_rsrc(d.w, (uint32_t)((int64_t)d.N * d.ldw));
     xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      // rows past M read row M-1: MFMA output row m depends only on input
+      // row m, and rows past M are never stored
+      const int m = min(16 * b + (lane & 15), d.M - 1);
+      xbase[b] = m * Kp + q * Fmt<FMT>::kLaneK;
+    }
   }
 
-  // Weight loads of unit (item, chunk); ok == false loads zeros only.
+  // Weight loads of unit (item, chunk).  The whole offset is a per-lane
+  // value (row offset + step offset), so the buffer's range check sees it:
+  // rows past N and bytes past the end of the matrix read zeros, bytes past
+  // a row's data (into the next row) meet zero activations.  ok == false
+  // (past this wave's work): every offset is pushed past the buffer.
   __device__ __forceinline__ void issue(const GemvDesc &d, int item, int ch, bool ok,
                                         uint4 (&wb)[kRGW][SC]) {
     const int lane = threadIdx.x & 63, q = lane >> 4;
 #pragma unroll
     for (int r = 0; r < kRGW; ++r) {
       const int n = (item * kRGW + r) * 16 + (lane & 15);
-      const uint32_t base = (uint32_t)(n * (int)d.ldw + 16 * q);
+      // unsigned (wrapping) arithmetic: an offset that wraps into the buffer
+      // reads real weights for a row past N, whose results are never stored
+      const uint32_t voff = (uint32_t)n * (uint32_t)d.ldw + 16u * q + (ok ? 0u : kOOB);
 #pragma unroll
-      for (int s = 0; s < SC; ++s) {
-        const int st = ch * SC + s;
-        const bool in = ok && n < d.N && 64 * st + 16 * q < rowb16;
-        wb[r][s] = buffer_load16(wr, in ? base + 64u * st : kOOB);
-      }
+      for (int s = 0; s < SC; ++s) wb[r][s] = buffer_load16(wr, voff + (uint32_t)(64 * (ch * SC + s)));
     }
   }
 
-  // Activation fragments of step st for M-block b (zero past M, past K or
-  // past the last step).
+  // Activation fragments of step st for M-block b.
   __device__ __forceinline__ void xfrags(const GemvDesc &d, const int8_t *xs, int st, int b,
                                          v4i (&xf)[F1]) {
+    if (staged) {
+      const int off = xbase[b] + st * Fmt<FMT>::kStepK;
+#pragma unroll
+      for (int j = 0; j < F1; ++j) xf[j] = *reinterpret_cast<const v4i *>(xs + off + 16 * j);
+      return;
+    }
+    // straight from x_q: 80 (or 16) positions, masked past K, permuted in
+    // registers
     const int lane = threadIdx.x & 63, q = lane >> 4;
     const int m = 16 * b + (lane & 15);
     const bool ok = m < d.M && st < S;
-    if (staged) {
-      const int off = ok ? m * Kp + st * Fmt<FMT>::kStepK + q * Fmt<FMT>::kLaneK : kZero;
+    const int p0 = st * Fmt<FMT>::kStepK + q * Fmt<FMT>::kLaneK;
+    uint32_t X[4 * F1];
 #pragma unroll
-      for (int j = 0; j < F1; ++j) xf[j] = *reinterpret_cast<const v4i *>(xs + off + 16 * j);
+    for (int c = 0; c < F1; ++c) {
+      const int p = p0 + 16 * c;
+      const uint4 v = buffer_load16(xr, ok && p < d.K ? (uint32_t)(m * d.ldxq + p) : kOOB);
+      uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kb = d.K - p - 4 * e;  // bytes of this dword inside the row
+        X[4 * c + e] =
+            w4[e] & (kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb)))));
+      }
+    }
+    if (FMT == UG_W_PACK5) {
+      uint32_t F[20];
+      permute80(reinterpret_cast<const uint32_t(&)[20]>(X), F);
+#pragma unroll
+      for (int j = 0; j < 5; ++j)
+        xf[j] = v4i{(int)F[4 * j], (int)F[4 * j + 1], (int)F[4 * j + 2], (int)F[4 * j + 3]};
     } else {
-      // straight from x_q: 80 (or 16) positions, permuted in registers
-      const int p0 = st * Fmt<FMT>::kStepK + q * Fmt<FMT>::kLaneK;
-      uint32_t X[4 * F1];
-#pragma unroll
-      for (int c = 0; c < F1; ++c) {
-        const int p = p0 + 16 * c;
-        const uint4 v = buffer_load16(xr, ok && p < d.K ? (uint32_t)(m * d.ldxq + p) : kOOB);
-        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kb = d.K - p - 4 * e;  // bytes of this dword inside the row
-          X[4 * c + e] =
-              w4[e] & (kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb)))));
-        }
-      }
-      if (FMT == UG_W_PACK5) {
-        uint32_t F[20];
-        permute80(reinterpret_cast<const uint32_t(&)[20]>(X), F);
-#pragma unroll
-        for (int j = 0; j < 5; ++j)
-          xf[j] = v4i{(int)F[4 * j], (int)F[4 * j + 1], (int)F[4 * j + 2], (int)F[4 * j + 3]};
-      } else {
-        xf[0] = v4i{(int)X[0], (int)X[1], (int)X[2], (int)X[3]};
-      }
+      xf[0] = v4i{(int)X[0], (int)X[1], (int)X[2], (int)X[3]};
     }
   }
 
@@ -461,14 +479,18 @@ __device__ __forceinline__ void gemv_items(const GemvDesc &d, Smem<FMT> &sh, boo
 
   uint4 A[kRGW][SC], B[kRGW][SC], C[kRGW][SC];
   v4i acc[kRGW][MB][NACC];
-  auto unit_item = [&](int u) { return i0 + wave + kWaves * (u / wv.NC); };
-  auto unit_ch = [&](int u) { return u % wv.NC; };
-  auto issue = [&](int u, uint4(&buf)[kRGW][SC]) {
-    wv.issue(d, unit_item(u), unit_ch(u), u < U, buf);
+  const int NC = wv.NC;
+  // issue position (item, chunk) and process position, advanced unit by unit
+  int iss_it = i0 + wave, iss_ch = 0, pro_it = i0 + wave, pro_ch = 0;
+  auto issue = [&](uint4(&buf)[kRGW][SC]) {
+    wv.issue(d, iss_it, iss_ch, iss_it < i1, buf);
+    if (++iss_ch == NC) {
+      iss_ch = 0;
+      iss_it += kWaves;
+    }
   };
-  auto process = [&](int u, const uint4(&buf)[kRGW][SC]) {
-    const int ch = unit_ch(u);
-    if (ch == 0) {
+  auto process = [&](const uint4(&buf)[kRGW][SC]) {
+    if (pro_ch == 0) {
 #pragma unroll
       for (int r = 0; r < kRGW; ++r)
 #pragma unroll
@@ -476,20 +498,24 @@ __device__ __forceinline__ void gemv_items(const GemvDesc &d, Smem<FMT> &sh, boo
 #pragma unroll
           for (int a = 0; a < NACC; ++a) acc[r][b][a] = v4i{0, 0, 0, 0};
     }
-    wv.compute(d, sh.xs, lut, ch, buf, acc);
-    if (ch == wv.NC - 1) wv.store(d, unit_item(u), acc, sh.sm, sh.cm, beta);
+    wv.compute(d, sh.xs, lut, pro_ch, buf, acc);
+    if (pro_ch == NC - 1) wv.store(d, pro_it, acc, sh.sm, sh.cm, beta);
+    if (++pro_ch == NC) {
+      pro_ch = 0;
+      pro_it += kWaves;
+    }
   };
-  issue(0, A);
-  issue(1, B);
+  issue(A);
+  issue(B);
   for (int u = 0; u < U;) {
-    issue(u + 2, C);
-    process(u, A);
+    issue(C);
+    process(A);
     if (++u >= U) break;
-    issue(u + 2, A);
-    process(u, B);
+    issue(A);
+    process(B);
     if (++u >= U) break;
-    issue(u + 2, B);
-    process(u, C);
+    issue(B);
+    process(C);
     ++u;
   }
 }

@@ -50,6 +50,14 @@ def test_decode_stack_one_launch_fused_quant(dev):
         assert_bits_equal(host(p["y"]), a, "replay")
 
 
+def _staged_kp(wfmt, M, K):
+    rb = -(-K // 5) if wfmt == ug.UG_W_PACK5 else K
+    cls = 0 if M <= 16 else (1 if M <= 32 else 2)
+    u = (4, 2, 1)[cls] if wfmt == ug.UG_W_PACK5 else (4, 4, 2)[cls]
+    steps = -(-rb // 64)
+    return (320 if wfmt == ug.UG_W_PACK5 else 64) * u * -(-steps // u)
+
+
 GROUPS = [
     # (wfmt, M, list of (N, K)) -- M fixes the activation-row class
     (ug.UG_W_PACK5, 1, [(6912, 2560), (2560, 6912), (2560, 2560), (17, 7), (100, 81)]),
@@ -71,8 +79,7 @@ def test_grouped_parity(dev, gi, fused):
     rng = np.random.default_rng([300, gi, int(fused)])
     probs, refs = [], []
     for (N, K) in shapes:
-        kp = (64 * -(-K // 64)) if wfmt == ug.UG_W_I8 else 320 * -(-(-(-K // 5)) // 64)
-        if fused and M * kp > 65536:   # the documented staging limit
+        if fused and M * _staged_kp(wfmt, M, K) > 65536:   # the documented staging limit
             continue
         x = rng.standard_normal((M, K), dtype=np.float32)
         wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
