@@ -5,6 +5,8 @@
 #include <cstdint>
 #include <vector>
 
+#include <cstring>
+
 #include "ug_internal.h"
 
 namespace {
@@ -149,7 +151,7 @@ ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s, const
 
 size_t ug_gemv_plan_size(int32_t count) {
   if (count < 1) return 0;
-  return (size_t)count * sizeof(ug::GemvDesc);
+  return (size_t)count * sizeof(ug::GemvDesc) + ug::kGemvBlocks * sizeof(ug::GemvBlock);
 }
 
 ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void *plan,
@@ -158,7 +160,6 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
   if (plan == nullptr || !aligned16(plan) || plan_bytes < ug_gemv_plan_size(count))
     return UG_ERR_WORKSPACE;
   std::vector<ug::GemvDesc> descs((size_t)count);
-  int variant = -1;
   for (int32_t i = 0; i < count; ++i) {
     const ug_gemv_problem &p = problems[i];
     const bool fused = p.x != nullptr;
@@ -172,13 +173,14 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
     if (fused) {
       if (!ptr_ok(p.x) || !pitch_ok(p.ldx, p.K, 4) || !eps_ok(p.eps)) return UG_ERR_INVALID_ARG;
       if (!ug::gemv_stages_x(p.wfmt, p.M, p.K)) return UG_ERR_UNSUPPORTED;
+      if (p.M * p.ldx * 4 >= (INT64_C(1) << 31)) return UG_ERR_UNSUPPORTED;
     }
     if (p.N * p.ldw >= (INT64_C(1) << 31) || p.M * ldxq >= (INT64_C(1) << 31))
       return UG_ERR_UNSUPPORTED;
     ug::GemvDesc d{};
     d.x = p.x;
     d.ldx = p.ldx;
-    d.xq = fused ? p.xq : p.xq;
+    d.xq = p.xq;
     d.ldxq = p.xq ? p.ldxq : 0;
     d.s = p.s;
     d.w = (const uint8_t *)p.w;
@@ -193,40 +195,43 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
     d.M = (int32_t)p.M;
     d.N = (int32_t)p.N;
     d.K = (int32_t)p.K;
-    ug::gemv_mfma_plan(d);
-    const int v = 16 * d.wfmt + d.mb;
-    if (variant >= 0 && v != variant) return UG_ERR_INVALID_ARG;
-    variant = v;
     descs[(size_t)i] = d;
   }
-  // Blocks take balanced ranges of the items of all problems (one round,
-  // one block per CU).
+  // the split (fine or stream), items, and the block table: descriptors
+  // first, then kGemvBlocks table entries
+  std::vector<ug::GemvBlock> blocks;
+  const int variant = ug::gemv_plan(descs.data(), count, blocks);
+  if (variant < 0) return UG_ERR_INVALID_ARG;
+  if (blocks.empty() || blocks.size() > (size_t)ug::kGemvBlocks) return UG_ERR_UNSUPPORTED;
   int64_t total_items = 0;
-  for (auto &d : descs) {
-    d.item_begin = (int32_t)total_items;
-    total_items += d.items;
-  }
+  for (const auto &d : descs) total_items += d.items;
   if (total_items > INT32_MAX) return UG_ERR_UNSUPPORTED;
-  const int64_t blocks = ug::gemv_grid(total_items);
-  hipError_t e = hipMemcpy(plan, descs.data(), descs.size() * sizeof(ug::GemvDesc),
-                           hipMemcpyHostToDevice);
+  std::vector<uint8_t> host(ug_gemv_plan_size(count), 0);
+  std::memcpy(host.data(), descs.data(), descs.size() * sizeof(ug::GemvDesc));
+  std::memcpy(host.data() + descs.size() * sizeof(ug::GemvDesc), blocks.data(),
+              blocks.size() * sizeof(ug::GemvBlock));
+  hipError_t e = hipMemcpy(plan, host.data(), host.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_status(e);
   info->count = count;
   info->total_items = (int32_t)total_items;
   info->variant = variant;
-  info->grid = (int32_t)blocks;
+  info->grid = (int32_t)blocks.size();
   return UG_OK;
 }
 
 ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *info,
                                     void *stream) {
   if (plan == nullptr || !aligned16(plan) || info == nullptr) return UG_ERR_INVALID_ARG;
-  if (info->count < 1 || info->total_items < 1 || info->grid < 1) return UG_ERR_INVALID_ARG;
-  const int fmt = info->variant >> 4, mb = info->variant & 15;
-  if ((fmt != UG_W_I8 && fmt != UG_W_PACK5) || (mb != 1 && mb != 2 && mb != 4))
+  if (info->count < 1 || info->total_items < 1 || info->grid < 1 ||
+      info->grid > ug::kGemvBlocks)
     return UG_ERR_INVALID_ARG;
-  return hip_status(ug::launch_gemv_grouped((const ug::GemvDesc *)plan, info->count,
-                                            info->total_items, info->grid, info->variant,
+  const int fine = info->variant >> 8, fmt = (info->variant >> 4) & 15, mb = info->variant & 15;
+  if ((fine != 0 && fine != 1) || (fmt != UG_W_I8 && fmt != UG_W_PACK5) ||
+      (mb != 1 && mb != 2 && mb != 4) || (fine && mb != 1))
+    return UG_ERR_INVALID_ARG;
+  const ug::GemvDesc *descs = (const ug::GemvDesc *)plan;
+  const ug::GemvBlock *blocks = (const ug::GemvBlock *)(descs + info->count);
+  return hip_status(ug::launch_gemv_grouped(descs, blocks, info->count, info->grid, info->variant,
                                             as_stream(stream)));
 }
 

@@ -26,15 +26,22 @@
 //   lane l reads replica l: one v_perm forms each address (b * 256 + 4 l)
 //   and a wave's 64 reads fall in 64 different banks.
 //
-// Work: a block of 8 waves (one block per CU) takes a range of items of one
-// problem; an item is 2 or 4 row groups (32 or 64 weight rows) over the whole K, split
-// into units of SC steps.  Each wave walks its items' units keeping the
-// weights of the next two units in flight (buffer loads: lanes past the row,
-// past N or past the work read zeros without touching memory, so the loop
-// has no branches).  The 64 KB table and the staged activations are built
-// once per block and shared by its 8 waves.  Activations may arrive as fp32:
-// the block then quantizes the rows itself with ug_quant_act's arithmetic,
-// so act quant + GEMV of a whole group is one launch.
+// Work: one block of 8 waves per CU.  Two ways to split a launch:
+//   stream: a block takes a range of items (32 weight rows over the whole
+//     K); each wave walks whole items unit by unit (SC steps), keeping the
+//     weights of the next two units in flight.  For groups with megabytes of
+//     weights per CU.
+//   fine: a block takes up to 16 items of 16 rows of one problem, and its
+//     waves split the (item, step) pieces evenly, so every wave issues all
+//     its weight loads at once and the K steps of one item run on several
+//     waves; partial int32 sums meet in LDS.  For decode-sized groups, where
+//     the launch is one HBM round trip long.
+// Loads are buffer loads: lanes past the row, past N or past the work read
+// zeros without touching memory, so the loops have no branches.  The 64 KB
+// table and the staged activations are built once per block and shared by
+// its 8 waves.  Activations may arrive as fp32: the block then quantizes the
+// rows itself with ug_quant_act's arithmetic, so act quant + GEMV of a whole
+// group is one launch.
 #include "ug_internal.h"
 
 namespace ug {
@@ -49,6 +56,8 @@ constexpr int kRepl = 64;          // table replicas: one per lane of a wave
 constexpr int kXsBytes = 65536;    // staged activations
 constexpr int kZero = kXsBytes;    // 80 zero bytes right after them
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every buffer used here
+constexpr int kFineItems = 16;   // fine split: items (16-row groups) per block
+constexpr int kFinePieces = 8;   // fine split: (item, step) pieces per wave
 
 template <int FMT>
 struct Fmt;
@@ -65,13 +74,15 @@ struct Fmt<UG_W_I8> {
   static constexpr int kLaneK = 16;
 };
 
-template <int FMT, int MB>
+template <int FMT, int MB, bool FINE>
 struct Cfg {
-  static constexpr int RGW = 2;  // row groups per item (they share each activation read)
+  // row groups per item (they share each activation read)
+  static constexpr int RGW = FINE ? 1 : 2;
   // steps per unit (three units of weights are in flight per wave)
-  static constexpr int SC = FMT == UG_W_PACK5 ? (MB == 1 ? 4 : (MB == 2 ? 2 : 1)) : (MB == 4 ? 2 : 4);
+  static constexpr int SC =
+      FINE ? 1 : (FMT == UG_W_PACK5 ? (MB == 1 ? 4 : (MB == 2 ? 2 : 1)) : (MB == 4 ? 2 : 4));
   // independent MFMA chains per output tile
-  static constexpr int NACC = FMT == UG_W_PACK5 ? (MB == 1 ? 2 : (MB == 2 ? 2 : 1)) : 2;
+  static constexpr int NACC = FMT == UG_W_PACK5 && MB == 4 ? 1 : 2;
 };
 
 __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int K) {
@@ -81,11 +92,18 @@ __host__ __device__ __forceinline__ int steps_of(int fmt, int K) {
   return (row_bytes_of(fmt, K) + 63) / 64;
 }
 __host__ __device__ __forceinline__ int sc_of(int fmt, int mb) {
-  return fmt == UG_W_PACK5 ? (mb == 1 ? Cfg<UG_W_PACK5, 1>::SC : (mb == 2 ? Cfg<UG_W_PACK5, 2>::SC : Cfg<UG_W_PACK5, 4>::SC))
-                           : (mb == 1 ? Cfg<UG_W_I8, 1>::SC : (mb == 2 ? Cfg<UG_W_I8, 2>::SC : Cfg<UG_W_I8, 4>::SC));
+  return fmt == UG_W_PACK5
+             ? (mb == 1 ? Cfg<UG_W_PACK5, 1, false>::SC
+                        : (mb == 2 ? Cfg<UG_W_PACK5, 2, false>::SC : Cfg<UG_W_PACK5, 4, false>::SC))
+             : (mb == 1 ? Cfg<UG_W_I8, 1, false>::SC
+                        : (mb == 2 ? Cfg<UG_W_I8, 2, false>::SC : Cfg<UG_W_I8, 4, false>::SC));
 }
-// Staged row length: whole units of steps, zero past K, so every step a
-// wave multiplies has activations (zeros past K) inside its row.
+// Staged row length of the stream split: whole units of steps, zero past K,
+// so every step a wave multiplies has activations (zeros past K) inside its
+// row.  The fine split stages whole steps: fine_kp.
+__host__ __device__ __forceinline__ int fine_kp(int fmt, int K) {
+  return steps_of(fmt, K) * (fmt == UG_W_PACK5 ? 320 : 64);
+}
 __host__ __device__ __forceinline__ int staged_kp(int fmt, int mb, int K) {
   const int sc = sc_of(fmt, mb);
   return ((steps_of(fmt, K) + sc - 1) / sc) * sc * (fmt == UG_W_PACK5 ? 320 : 64);
@@ -108,6 +126,9 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ float4 buffer_load16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 // t0..t3 of code e as int8 bytes; codes 243..255 give zeros here (their d4
@@ -176,35 +197,122 @@ struct Smem {
   uint32_t lut[FMT == UG_W_PACK5 ? 256 * kRepl : 1];
   uint32_t lut_tmp[FMT == UG_W_PACK5 ? 256 : 1];
   alignas(16) int8_t xs[kXsBytes + 80];  // staged rows, then 80 zero bytes
-  float sm[64];
-  int cm[64];
+  alignas(16) int slots[kFineItems * 256];  // fine split: [item][m][n] int32 sums
+  float part[kWaves][64];                   // per-wave row maxima (fused quantization)
+  float sm[64];                             // row scales s
+  int cm[64];                               // five-trit correction sum_g x[5g+4]
 };
 
-// Block set-up: decode table, row scales (fused quantization), staged and
-// permuted activations with the d4 correction cm[m] = sum_g x[5g+4], and the
-// quantized activations / scales as outputs when this is the problem's
-// first block.  Ends with a barrier.
+// s = fl(fl(max|x| / 127) + eps) of row m from the per-wave maxima.
 template <int FMT>
-__device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool staged,
-                                      bool write_outputs, bool build_table) {
+__device__ __forceinline__ float row_scale(const Smem<FMT> &sh, int m, float eps) {
+  float a = sh.part[0][m];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) a = fmaxf(a, sh.part[w][m]);
+  const float a127 = a / 127.0f;
+  return a127 + eps;
+}
+
+// Block set-up for problem d: decode table (first problem of the block),
+// row scales (fused quantization, else the given s), the activation rows
+// staged in LDS (Kp bytes per row, zeros past K; five trits per byte: every
+// 80-position window permuted as the decoded weights are) with the d4
+// correction cm[m] = sum_g x[5g+4], and zeroed reduction slots.  Every
+// thread issues its loads together.  Ends with a barrier.
+template <int FMT>
+__device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool staged, int Kp,
+                                      bool build_table, bool zero_slots) {
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   if (FMT == UG_W_PACK5 && build_table && tid < 256) sh.lut_tmp[tid] = lut4_entry(tid);
   if (tid < 64) sh.cm[tid] = 0;
   if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
-  if (d.x) {  // row scales s = fl(fl(max|x| / 127) + eps), one wave per row
-    for (int m = wave; m < d.M; m += kWaves) {
-      const float *xr = d.x + (int64_t)m * d.ldx;
-      float a = 0.0f;
-      for (int k = 4 * lane; k < d.K; k += 256) {
-        const float4 v = *reinterpret_cast<const float4 *>(xr + k);
-        a = fmaxf(a, fabsf(v.x));
-        if (k + 1 < d.K) a = fmaxf(a, fabsf(v.y));
-        if (k + 2 < d.K) a = fmaxf(a, fabsf(v.z));
-        if (k + 3 < d.K) a = fmaxf(a, fabsf(v.w));
+  if (zero_slots)
+    for (int i = tid; i < kFineItems * 64; i += kThreads)
+      reinterpret_cast<uint4 *>(sh.slots)[i] = make_uint4(0, 0, 0, 0);
+  const int Kp4 = Kp >> 2;  // dwords per staged row
+  if (d.x) {
+    // Pass 1: row maxima.  Tile t = (row m, 256 positions c): lane l reads
+    // the float4 at 256 c + 4 l; a wave keeps 8 tiles in flight.
+    const int T4 = (d.K + 255) >> 8, nt = d.M * T4;
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.x, (uint32_t)((int64_t)d.M * d.ldx * 4));
+    sh.part[wave][lane] = 0.0f;
+    const bool one = nt <= 8 * kWaves;  // one batch: keep the values for pass 2
+    float4 v[8];
+    for (int t0 = wave; t0 < nt; t0 += 8 * kWaves) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + i * kWaves, m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
+        // a float4 at k < K is inside the row (ldx >= round_up(K, 4))
+        v[i] = buffer_load16f(xr, t < nt && k < d.K ? (uint32_t)((m * (int)d.ldx + k) * 4) : kOOB);
       }
-      a = wave_max(a);
-      const float a127 = a / 127.0f;
-      if (lane == 0) sh.sm[m] = a127 + d.eps;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + i * kWaves;
+        if (t < nt) {
+          const int m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
+          float a = fabsf(v[i].x);  // zero when k >= K
+          if (k + 1 < d.K) a = fmaxf(a, fabsf(v[i].y));
+          if (k + 2 < d.K) a = fmaxf(a, fabsf(v[i].z));
+          if (k + 3 < d.K) a = fmaxf(a, fabsf(v[i].w));
+          a = wave_max(a);
+          if (lane == 0) sh.part[wave][m] = fmaxf(sh.part[wave][m], a);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < d.M) sh.sm[tid] = row_scale(sh, tid, d.eps);
+    // Pass 2: quantize into the staging rows, K order (from registers when
+    // pass 1 was one batch).
+    for (int t0 = wave; t0 < nt; t0 += 8 * kWaves) {
+      if (!one) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int t = t0 + i * kWaves, m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
+          v[i] = buffer_load16f(xr, t < nt && k < d.K ? (uint32_t)((m * (int)d.ldx + k) * 4) : kOOB);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + i * kWaves;
+        if (t < nt) {
+          const int m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
+          const float s = row_scale(sh, m, d.eps);
+          if (k < d.K)
+            *reinterpret_cast<uint32_t *>(sh.xs + m * Kp + k) =
+                pack4(q8(v[i].x, s), k + 1 < d.K ? q8(v[i].y, s) : 0,
+                      k + 2 < d.K ? q8(v[i].z, s) : 0, k + 3 < d.K ? q8(v[i].w, s) : 0);
+        }
+      }
+    }
+    // zeros from the first whole dword past K to the end of the staged row
+    const int kz = (d.K + 3) >> 2, nz = Kp4 - kz;
+    for (int i = tid; i < d.M * nz; i += kThreads) {
+      const int m = i / nz;
+      reinterpret_cast<uint32_t *>(sh.xs + m * Kp)[kz + (i - m * nz)] = 0u;
+    }
+  } else {
+    if (tid < d.M) sh.sm[tid] = d.s[tid];
+    if (staged) {  // copy x_q rows, 8 dwords in flight per thread
+      const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
+      const int n4 = d.M * Kp4;
+      for (int i0 = tid; i0 < n4; i0 += 8 * kThreads) {
+        uint32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = i0 + i * kThreads, m = idx / Kp4, k = 4 * (idx - m * Kp4);
+          // 4 bytes at k < K are inside the row (ldxq >= round_up(K, 16))
+          v[i] = buffer_load4(xr, idx < n4 && k < d.K ? (uint32_t)(m * (int)d.ldxq + k) : kOOB);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = i0 + i * kThreads, m = idx / Kp4, k = 4 * (idx - m * Kp4);
+          if (idx < n4) {
+            uint32_t w = v[i];
+            if (k + 4 > d.K) w &= k >= d.K ? 0u : (0xffffffffu >> (8 * (k + 4 - d.K)));
+            reinterpret_cast<uint32_t *>(sh.xs + m * Kp)[k >> 2] = w;
+          }
+        }
+      }
     }
   }
   __syncthreads();
@@ -217,97 +325,73 @@ __device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool sta
       chunks[c] = make_uint4(v, v, v, v);
     }
   }
-  if (staged) {
-    // window = 80 (five trits per byte) or 16 (one per byte) K positions;
-    // every thread stages whole windows, all its loads issued first
-    constexpr int WIN = FMT == UG_W_PACK5 ? 80 : 16;
-    const int Kp = staged_kp(FMT, mb_of(d.M), d.K);
-    const int wpr = Kp / WIN;  // windows per row
-    const int nwin = d.M * wpr;
-    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
-    for (int w0 = tid; w0 < nwin; w0 += kThreads) {
-      const int m = w0 / wpr, k0 = (w0 - m * wpr) * WIN;
-      uint32_t X[WIN / 4];
-      if (d.x) {
-        const float *xrow = d.x + (int64_t)m * d.ldx;
-        const float s = sh.sm[m];
-        float4 f[WIN / 4];
+  if (FMT == UG_W_PACK5) {
+    if (staged) {  // permute every 80-position window in place, one window per thread
+      const int wpr = Kp / 80, nwin = d.M * wpr;
+      for (int w0 = tid; w0 < nwin; w0 += kThreads) {
+        const int m = w0 / wpr;
+        uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * Kp + (w0 - m * wpr) * 80);
+        uint32_t X[20], F[20];
 #pragma unroll
-        for (int i = 0; i < WIN / 4; ++i)  // float4 at k < K is in-bounds (ldx >= round_up(K,4))
-          f[i] = k0 + 4 * i < d.K ? *reinterpret_cast<const float4 *>(xrow + k0 + 4 * i)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int i = 0; i < WIN / 4; ++i) {
-          const int k = k0 + 4 * i;
-          X[i] = pack4(k < d.K ? q8(f[i].x, s) : 0, k + 1 < d.K ? q8(f[i].y, s) : 0,
-                       k + 2 < d.K ? q8(f[i].z, s) : 0, k + 3 < d.K ? q8(f[i].w, s) : 0);
+        for (int i = 0; i < 5; ++i) {
+          const uint4 q = win[i];
+          X[4 * i] = q.x; X[4 * i + 1] = q.y; X[4 * i + 2] = q.z; X[4 * i + 3] = q.w;
         }
-      } else {
+        permute80(X, F);
 #pragma unroll
-        for (int i = 0; i < WIN / 4; ++i) {
-          const int k = k0 + 4 * i;  // 4 bytes at k < K are in-bounds (ldxq >= round_up(K,16))
-          uint32_t v = buffer_load4(xr, k < d.K ? (uint32_t)(m * d.ldxq + k) : kOOB);
-          if (k + 4 > d.K) v &= k >= d.K ? 0u : (0xffffffffu >> (8 * (k + 4 - d.K)));
-          X[i] = v;
-        }
-      }
-      uint4 *dst = reinterpret_cast<uint4 *>(sh.xs + m * Kp + k0);
-      if (FMT == UG_W_PACK5) {
-        uint32_t F[20];
-        permute80(reinterpret_cast<const uint32_t(&)[20]>(X), F);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) dst[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
+        for (int i = 0; i < 5; ++i) win[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
         atomicAdd(&sh.cm[m], byte_sum4(F[16]) + byte_sum4(F[17]) + byte_sum4(F[18]) + byte_sum4(F[19]));
-      } else {
-        dst[0] = make_uint4(X[0], X[1], X[2], X[3]);
+      }
+    } else {  // correction straight from x_q
+      for (int m = wave; m < d.M; m += kWaves) {
+        int sum = 0;
+        for (int k = 5 * lane + 4; k < d.K; k += 5 * 64) sum += d.xq[(int64_t)m * d.ldxq + k];
+        sum = wave_sum_i32(sum);
+        if (lane == 0) sh.cm[m] = sum;
       }
     }
-  } else if (FMT == UG_W_PACK5) {  // correction straight from x_q
-    for (int m = wave; m < d.M; m += kWaves) {
-      int sum = 0;
-      for (int k = 5 * lane + 4; k < d.K; k += 5 * 64) sum += d.xq[(int64_t)m * d.ldxq + k];
-      sum = wave_sum_i32(sum);
-      if (lane == 0) sh.cm[m] = sum;
-    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (write_outputs && d.x) {
-    if (d.s)
-      for (int m = tid; m < d.M; m += kThreads) d.s[m] = sh.sm[m];
-    if (d.xq) {  // undo the staging permutation: read back per K position
-      int8_t *xq = const_cast<int8_t *>(d.xq);
-      const int Kp = staged_kp(FMT, mb_of(d.M), d.K);
-      for (int idx = tid; idx < d.M * d.K; idx += kThreads) {
-        const int m = idx / d.K, k = idx - m * d.K;
-        int off = k;
-        if (FMT == UG_W_PACK5) {
-          const int w = k / 80, r = k - 80 * w, g = r / 5, t = r - 5 * g;
-          // t < 4: fragment g/4, dword g%4, byte t; t == 4: fragment 4, dword g/4, byte g%4
-          off = 80 * w + (t < 4 ? 16 * (g >> 2) + 4 * (g & 3) + t : 64 + 4 * (g >> 2) + (g & 3));
-        }
-        xq[(int64_t)m * d.ldxq + k] = sh.xs[m * Kp + off];
+}
+
+// The quantized activations and scales as outputs (fused quantization, the
+// problem's first block): undo the staging permutation per K position.
+template <int FMT>
+__device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<FMT> &sh, int Kp) {
+  const int tid = threadIdx.x;
+  if (d.s)
+    for (int m = tid; m < d.M; m += kThreads) d.s[m] = sh.sm[m];
+  if (d.xq) {
+    int8_t *xq = const_cast<int8_t *>(d.xq);
+    for (int idx = tid; idx < d.M * d.K; idx += kThreads) {
+      const int m = idx / d.K, k = idx - m * d.K;
+      int off = k;
+      if (FMT == UG_W_PACK5) {
+        const int w = k / 80, r = k - 80 * w, g = r / 5, t = r - 5 * g;
+        // t < 4: fragment g/4, dword g%4, byte t; t == 4: fragment 4, dword g/4, byte g%4
+        off = 80 * w + (t < 4 ? 16 * (g >> 2) + 4 * (g & 3) + t : 64 + 4 * (g >> 2) + (g & 3));
       }
+      xq[(int64_t)m * d.ldxq + k] = sh.xs[m * Kp + off];
     }
   }
 }
 
-template <int FMT, int MB>
+template <int FMT, int MB, bool FINE>
 struct Wave {
   static constexpr int F1 = Fmt<FMT>::kFrag;
-  static constexpr int SC = Cfg<FMT, MB>::SC;
-  static constexpr int NACC = Cfg<FMT, MB>::NACC;
-  static constexpr int kRGW = Cfg<FMT, MB>::RGW;
+  static constexpr int SC = Cfg<FMT, MB, FINE>::SC;
+  static constexpr int NACC = Cfg<FMT, MB, FINE>::NACC;
+  static constexpr int kRGW = Cfg<FMT, MB, FINE>::RGW;
 
-  int S, NC, Kp;
+  int S, NC;
   bool staged;
   int xbase[MB];  // staged: LDS offset of this lane's activation row (step 0)
   __amdgpu_buffer_rsrc_t wr, xr;
 
-  __device__ __forceinline__ void init(const GemvDesc &d, bool stg) {
+  __device__ __forceinline__ void init(const GemvDesc &d, bool stg, int Kp) {
     const int lane = threadIdx.x & 63, q = lane >> 4;
     S = steps_of(FMT, d.K);
     NC = (S + SC - 1) / SC;
-    Kp = staged_kp(FMT, MB, d.K);
     staged = stg;
     wr = buffer_rsrc(d.w, (uint32_t)((int64_t)d.N * d.ldw));
     xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
@@ -342,7 +426,7 @@ struct Wave {
   // Activation fragments of step st for M-block b.
   __device__ __forceinline__ void xfrags(const GemvDesc &d, const int8_t *xs, int st, int b,
                                          v4i (&xf)[F1]) {
-    if (staged) {
+    if (FINE || staged) {
       const int off = xbase[b] + st * Fmt<FMT>::kStepK;
 #pragma unroll
       for (int j = 0; j < F1; ++j) xf[j] = *reinterpret_cast<const v4i *>(xs + off + 16 * j);
@@ -451,8 +535,7 @@ struct Wave {
             const int val = FMT == UG_W_PACK5 ? v[r] - cm[m] : v[r];
             if (d.acc) d.acc[(int64_t)m * d.ldacc + n] = val;
             if (d.y) {
-              const float sv = d.x ? sm[m] : d.s[m];
-              const float scale = sv * beta;
+              const float scale = sm[m] * beta;
               d.y[(int64_t)m * d.ldy + n] = (float)val * scale;
             }
           }
@@ -462,34 +545,34 @@ struct Wave {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Stream split.
+//
 // Items [i0, i1) of problem d: wave w takes items i0 + w, i0 + w + 8, ...,
-// each NC units, with the weights of the next two units in flight.
+// each NC units, with the weights of the next two units in flight.  start()
+// issues the first two units' loads, so they travel while the block sets up.
 template <int FMT, int MB>
-__device__ __forceinline__ void gemv_items(const GemvDesc &d, Smem<FMT> &sh, bool staged,
-                                           int i0, int i1) {
-  using W = Wave<FMT, MB>;
-  constexpr int SC = W::SC, NACC = W::NACC, kRGW = W::kRGW;
+struct ItemLoop {
+  using W = Wave<FMT, MB, false>;
+  static constexpr int SC = W::SC, NACC = W::NACC, kRGW = W::kRGW;
   W wv;
-  wv.init(d, staged);
-  const int wave = uniform(threadIdx.x >> 6);
-  const int my_items = i0 + wave < i1 ? (i1 - i0 - wave + kWaves - 1) / kWaves : 0;
-  const int U = uniform(my_items * wv.NC);
-  const float beta = d.beta[0];
-  const char *lut = reinterpret_cast<const char *>(sh.lut);
-
   uint4 A[kRGW][SC], B[kRGW][SC], C[kRGW][SC];
   v4i acc[kRGW][MB][NACC];
-  const int NC = wv.NC;
+  float beta;
+  int i1, U;
   // issue position (item, chunk) and process position, advanced unit by unit
-  int iss_it = i0 + wave, iss_ch = 0, pro_it = i0 + wave, pro_ch = 0;
-  auto issue = [&](uint4(&buf)[kRGW][SC]) {
+  int iss_it, iss_ch, pro_it, pro_ch;
+
+  __device__ __forceinline__ void issue(const GemvDesc &d, uint4 (&buf)[kRGW][SC]) {
     wv.issue(d, iss_it, iss_ch, iss_it < i1, buf);
-    if (++iss_ch == NC) {
+    if (++iss_ch == wv.NC) {
       iss_ch = 0;
       iss_it += kWaves;
     }
-  };
-  auto process = [&](const uint4(&buf)[kRGW][SC]) {
+  }
+
+  __device__ __forceinline__ void process(const GemvDesc &d, const Smem<FMT> &sh,
+                                          const uint4 (&buf)[kRGW][SC]) {
     if (pro_ch == 0) {
 #pragma unroll
       for (int r = 0; r < kRGW; ++r)
@@ -498,108 +581,280 @@ __device__ __forceinline__ void gemv_items(const GemvDesc &d, Smem<FMT> &sh, boo
 #pragma unroll
           for (int a = 0; a < NACC; ++a) acc[r][b][a] = v4i{0, 0, 0, 0};
     }
-    wv.compute(d, sh.xs, lut, pro_ch, buf, acc);
-    if (pro_ch == NC - 1) wv.store(d, pro_it, acc, sh.sm, sh.cm, beta);
-    if (++pro_ch == NC) {
+    wv.compute(d, sh.xs, reinterpret_cast<const char *>(sh.lut), pro_ch, buf, acc);
+    if (pro_ch == wv.NC - 1) wv.store(d, pro_it, acc, sh.sm, sh.cm, beta);
+    if (++pro_ch == wv.NC) {
       pro_ch = 0;
       pro_it += kWaves;
     }
-  };
-  issue(A);
-  issue(B);
-  for (int u = 0; u < U;) {
-    issue(C);
-    process(A);
-    if (++u >= U) break;
-    issue(A);
-    process(B);
-    if (++u >= U) break;
-    issue(B);
-    process(C);
-    ++u;
   }
-}
 
-// Block b of nb takes the global items [b T / nb, (b + 1) T / nb) of the
-// plan (T items over all problems, problem p owning [item_begin, +items)),
-// crossing into the next problem when its range does.
-template <int FMT, int MB>
-__device__ __forceinline__ void gemv_block(const GemvDesc *plan, int count, int64_t T, int b,
-                                           int nb) {
-  __shared__ Smem<FMT> sh;
-  const int g0 = (int)(T * b / nb), g1 = (int)(T * (b + 1) / nb);
-  if (g0 >= g1) return;
-  int lo = 0, hi = count - 1;  // problem holding item g0
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (plan[mid].item_begin <= g0)
-      lo = mid;
-    else
-      hi = mid - 1;
+  __device__ __forceinline__ void start(const GemvDesc &d, bool staged, int Kp, int i0, int i1_) {
+    wv.init(d, staged, Kp);
+    const int wave = uniform(threadIdx.x >> 6);
+    const int my_items = i0 + wave < i1_ ? (i1_ - i0 - wave + kWaves - 1) / kWaves : 0;
+    U = uniform(my_items * wv.NC);
+    i1 = i1_;
+    iss_it = pro_it = i0 + wave;
+    iss_ch = pro_ch = 0;
+    issue(d, A);
+    issue(d, B);
+    beta = d.beta[0];
   }
+
+  // Needs the block's set-up (table, staged rows) to be complete.
+  __device__ __forceinline__ void run(const GemvDesc &d, const Smem<FMT> &sh) {
+    for (int u = 0; u < U;) {
+      issue(d, C);
+      process(d, sh, A);
+      if (++u >= U) break;
+      issue(d, A);
+      process(d, sh, B);
+      if (++u >= U) break;
+      issue(d, B);
+      process(d, sh, C);
+      ++u;
+    }
+  }
+};
+
+// The block takes the global items [g0, g1) of the plan (problem p holds
+// item g0; problem q owns [item_begin, +items)), crossing into the next
+// problem when its range does.
+template <int FMT, int MB>
+__device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, int p, int g0,
+                                             int g1) {
+  __shared__ Smem<FMT> sh;
   bool first = true;
-  for (int p = lo, g = g0; g < g1 && p < count; ++p) {
+  for (int g = g0; g < g1 && p < count; ++p) {
     const GemvDesc d = plan[p];
     const int e = min(g1, d.item_begin + d.items);
     if (e <= g) continue;
-    if (!first) __syncthreads();  // the previous problem's staged rows are done
     const bool staged = stages_x(FMT, d.M, d.K);
-    setup<FMT>(d, sh, staged, g == d.item_begin, first);
+    const int Kp = staged_kp(FMT, MB, d.K);
+    ItemLoop<FMT, MB> loop;
+    loop.start(d, staged, Kp, g - d.item_begin, e - d.item_begin);
+    if (!first) __syncthreads();  // the previous problem's staged rows are done
+    setup<FMT>(d, sh, staged, Kp, first, false);
     first = false;
-    gemv_items<FMT, MB>(d, sh, staged, g - d.item_begin, e - d.item_begin);
+    loop.run(d, sh);
+    if (d.x && g == d.item_begin) write_act_outputs<FMT>(d, sh, Kp);
     g = e;
   }
 }
 
 template <int FMT, int MB>
-__global__ __launch_bounds__(kThreads) void gemv_single_kernel(GemvDesc d) {
-  gemv_block<FMT, MB>(&d, 1, d.items, blockIdx.x, gridDim.x);
+__global__ __launch_bounds__(kThreads) void gemv_stream_single(GemvDesc d) {
+  const int64_t T = d.items;
+  const int g0 = (int)(T * blockIdx.x / gridDim.x), g1 = (int)(T * (blockIdx.x + 1) / gridDim.x);
+  if (g0 < g1) stream_block<FMT, MB>(&d, 1, 0, g0, g1);
 }
 
 template <int FMT, int MB>
-__global__ __launch_bounds__(kThreads) void gemv_grouped_kernel(const GemvDesc *__restrict__ plan,
-                                                                int count, int total) {
-  gemv_block<FMT, MB>(plan, count, total, blockIdx.x, gridDim.x);
+__global__ __launch_bounds__(kThreads) void gemv_stream_grouped(const GemvDesc *__restrict__ plan,
+                                                                const GemvBlock *__restrict__ blocks,
+                                                                int count) {
+  const GemvBlock bl = blocks[blockIdx.x];
+  if (bl.i0 < bl.i1) stream_block<FMT, MB>(plan, count, bl.p, bl.i0, bl.i1);
+}
+
+// ---------------------------------------------------------------------------
+// Fine split (M <= 16, staged activations).
+//
+// Items [i0, i1) of problem d (16 rows each), S steps per item: piece
+// p = (item i0 + p / S, step p % S).  Wave w takes pieces [w P / 8,
+// (w + 1) P / 8) of the block's P, loads them all before the set-up, and adds
+// its partial sums to the item's LDS slot whenever its next piece belongs to
+// another item.  After a barrier the block writes every item's outputs.
+template <int FMT>
+__device__ __forceinline__ void fine_block(const GemvDesc &d, int i0, int i1) {
+  using W = Wave<FMT, 1, true>;
+  constexpr int NACC = W::NACC;
+  __shared__ Smem<FMT> sh;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const int S = steps_of(FMT, d.K), Kp = fine_kp(FMT, d.K);
+  const int P = (i1 - i0) * S;
+  const int p0 = uniform(wave * P / kWaves), p1 = uniform((wave + 1) * P / kWaves);
+  W wv;
+  wv.init(d, true, Kp);
+  uint4 wb[kFinePieces][1][1];
+  {
+    int it = p0 / S, st = p0 - it * S;
+#pragma unroll
+    for (int j = 0; j < kFinePieces; ++j) {
+      wv.issue(d, i0 + it, st, p0 + j < p1, wb[j]);
+      if (++st == S) {
+        st = 0;
+        ++it;
+      }
+    }
+  }
+  const float beta = d.beta[0];
+  setup<FMT>(d, sh, true, Kp, true, true);
+  const char *lut = reinterpret_cast<const char *>(sh.lut);
+  v4i acc[1][1][NACC];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) acc[0][0][a] = v4i{0, 0, 0, 0};
+  int it = p0 / S, st = p0 - it * S;
+#pragma unroll
+  for (int j = 0; j < kFinePieces; ++j) {
+    if (p0 + j < p1) {
+      wv.compute(d, sh.xs, lut, st, wb[j], acc);
+      if (p0 + j + 1 == p1 || st + 1 == S) {  // last piece of this item here
+        v4i v = acc[0][0][0];
+#pragma unroll
+        for (int a = 1; a < NACC; ++a) v += acc[0][0][a];
+        const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * q + r < d.M) atomicAdd(&sh.slots[it * 256 + (4 * q + r) * 16 + n], v[r]);
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[0][0][a] = v4i{0, 0, 0, 0};
+      }
+      if (++st == S) {
+        st = 0;
+        ++it;
+      }
+    }
+  }
+  __syncthreads();
+  const int per_item = d.M * 16;
+  for (int idx = tid; idx < (i1 - i0) * per_item; idx += kThreads) {
+    const int li = idx / per_item, rem = idx - li * per_item, m = rem >> 4, n = rem & 15;
+    const int ng = (i0 + li) * 16 + n;
+    if (ng < d.N) {
+      int val = sh.slots[li * 256 + m * 16 + n];
+      if (FMT == UG_W_PACK5) val -= sh.cm[m];
+      if (d.acc) d.acc[(int64_t)m * d.ldacc + ng] = val;
+      if (d.y) {
+        const float scale = sh.sm[m] * beta;
+        d.y[(int64_t)m * d.ldy + ng] = (float)val * scale;
+      }
+    }
+  }
+  if (d.x && i0 == 0) write_act_outputs<FMT>(d, sh, Kp);
 }
 
 template <int FMT>
-hipError_t launch_single_fmt(const GemvDesc &d, int grid, hipStream_t st) {
-  switch (d.mb) {
-    case 1: hipLaunchKernelGGL((gemv_single_kernel<FMT, 1>), dim3(grid), dim3(kThreads), 0, st, d); break;
-    case 2: hipLaunchKernelGGL((gemv_single_kernel<FMT, 2>), dim3(grid), dim3(kThreads), 0, st, d); break;
-    default: hipLaunchKernelGGL((gemv_single_kernel<FMT, 4>), dim3(grid), dim3(kThreads), 0, st, d); break;
+__global__ __launch_bounds__(kThreads) void gemv_fine_single(GemvDesc d, int ipb) {
+  const int i0 = blockIdx.x * ipb, i1 = min(d.items, i0 + ipb);
+  if (i0 < i1) fine_block<FMT>(d, i0, i1);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void gemv_fine_grouped(const GemvDesc *__restrict__ plan,
+                                                              const GemvBlock *__restrict__ blocks) {
+  const GemvBlock bl = blocks[blockIdx.x];
+  if (bl.i0 < bl.i1) {
+    const GemvDesc d = plan[bl.p];
+    fine_block<FMT>(d, bl.i0, bl.i1);
   }
-  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+// Fine split of a group: items per block for every problem, or false when
+// the group is too large for it (then the stream split runs).  Blocks of
+// about T / 256 pieces each, at most kFineItems items, one problem each.
+bool plan_fine(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
+  int64_t T = 0;
+  for (int i = 0; i < count; ++i) {
+    const GemvDesc &d = descs[i];
+    if (d.M > 16 || (int64_t)d.M * fine_kp(d.wfmt, d.K) > kXsBytes) return false;
+    T += (int64_t)((d.N + 15) / 16) * steps_of(d.wfmt, d.K);
+  }
+  if (T > (int64_t)kGemvBlocks * kWaves * kFinePieces) return false;
+  std::vector<int> ipb((size_t)count);
+  for (int64_t target = (T + kGemvBlocks - 1) / kGemvBlocks;; ++target) {
+    if (target > (int64_t)kWaves * kFinePieces) return false;
+    int64_t nb = 0;
+    bool fits = true;
+    for (int i = 0; i < count; ++i) {
+      const int S = steps_of(descs[i].wfmt, descs[i].K), items = (descs[i].N + 15) / 16;
+      int k = (int)(target / S);
+      k = k < 1 ? 1 : (k > kFineItems ? kFineItems : k);
+      k = k > items ? items : k;
+      // every wave's share of a block's pieces must fit its registers
+      if ((k * S + kWaves - 1) / kWaves > kFinePieces) fits = false;
+      ipb[(size_t)i] = k;
+      nb += (items + k - 1) / k;
+    }
+    if (!fits) return false;
+    if (nb <= kGemvBlocks) break;
+  }
+  blocks.clear();
+  for (int i = 0; i < count; ++i) {
+    const int items = (descs[i].N + 15) / 16;
+    descs[i].mb = 1;
+    descs[i].items = items;
+    for (int a = 0; a < items; a += ipb[(size_t)i])
+      blocks.push_back(GemvBlock{i, a, std::min(items, a + ipb[(size_t)i]), 0});
+  }
+  return true;
 }
 
 }  // namespace
 
-// Blocks for T items: one per CU when there are enough items, else one per
-// 4 items (a small group is latency-bound: more CUs, shorter waits).
+// Blocks for T items of the stream split: one per CU when there are enough
+// items, else one per 4 items.
 int gemv_grid(int64_t total_items) {
   const int64_t by_items = (total_items + 3) / 4;
   return (int)(by_items < kGemvBlocks ? (by_items < 1 ? 1 : by_items) : kGemvBlocks);
 }
 
-void gemv_mfma_plan(GemvDesc &d) {
-  d.mb = d.M <= 16 ? 1 : (d.M <= 32 ? 2 : 4);
-  const int rgw = d.wfmt == UG_W_PACK5 ? (d.mb == 1 ? Cfg<UG_W_PACK5, 1>::RGW : Cfg<UG_W_PACK5, 2>::RGW)
-                                       : Cfg<UG_W_I8, 1>::RGW;
-  const int RG = (d.N + 15) / 16;
-  d.items = (RG + rgw - 1) / rgw;
+int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
+  const int fmt = descs[0].wfmt;
+  for (int i = 1; i < count; ++i)
+    if (descs[i].wfmt != fmt) return -1;
+  int64_t total = 0;
+  if (plan_fine(descs, count, blocks)) {
+    for (int i = 0; i < count; ++i) {
+      descs[i].item_begin = (int32_t)total;
+      total += descs[i].items;
+    }
+    return 256 + 16 * fmt + 1;
+  }
+  const int mb = mb_of(descs[0].M);
+  for (int i = 0; i < count; ++i) {
+    GemvDesc &d = descs[i];
+    d.mb = mb_of(d.M);
+    if (d.mb != mb) return -1;
+    const int rg = (d.N + 15) / 16;
+    d.items = (rg + 1) / 2;  // two row groups per item
+    d.item_begin = (int32_t)total;
+    total += d.items;
+  }
+  if (total > INT32_MAX) return -1;
+  const int grid = gemv_grid(total);
+  blocks.clear();
+  int p = 0;
+  for (int b = 0; b < grid; ++b) {
+    const int g0 = (int)(total * b / grid), g1 = (int)(total * (b + 1) / grid);
+    while (p + 1 < count && descs[p + 1].item_begin <= g0) ++p;
+    blocks.push_back(GemvBlock{p, g0, g1, 0});
+  }
+  return 16 * fmt + mb;
 }
 
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
   return K <= UG_MAX_K && M <= 64 && stages_x(wfmt, (int)M, (int)K);
 }
 
-hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, int32_t count, int32_t total_items,
-                               int32_t grid, int32_t fmt_mb, hipStream_t st) {
-  // fmt_mb = 16 * wfmt + mb (every problem of a plan shares both)
-  const int fmt = fmt_mb >> 4, mb = fmt_mb & 15;
+hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const GemvBlock *blocks_dev, int32_t count,
+                               int32_t grid, int32_t variant, hipStream_t st) {
+  const bool fine = variant >> 8;
+  const int fmt = (variant >> 4) & 15, mb = variant & 15;
   dim3 g(grid), b(kThreads);
+  if (fine) {
+    if (fmt == UG_W_PACK5)
+      hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5>), g, b, 0, st, plan_dev, blocks_dev);
+    else
+      hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8>), g, b, 0, st, plan_dev, blocks_dev);
+    return hipGetLastError();
+  }
 #define UG_GROUPED(F, MBV) \
-  hipLaunchKernelGGL((gemv_grouped_kernel<F, MBV>), g, b, 0, st, plan_dev, count, total_items)
+  hipLaunchKernelGGL((gemv_stream_grouped<F, MBV>), g, b, 0, st, plan_dev, blocks_dev, count)
   if (fmt == UG_W_PACK5) {
     if (mb == 1) UG_GROUPED(UG_W_PACK5, 1);
     else if (mb == 2) UG_GROUPED(UG_W_PACK5, 2);
@@ -632,11 +887,31 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
   d.M = (int32_t)M;
   d.N = (int32_t)N;
   d.K = (int32_t)K;
-  gemv_mfma_plan(d);
-  d.item_begin = 0;
-  const int grid = gemv_grid(d.items);
-  if (wfmt == UG_W_PACK5) return launch_single_fmt<UG_W_PACK5>(d, grid, st);
-  return launch_single_fmt<UG_W_I8>(d, grid, st);
+  std::vector<GemvBlock> blocks;
+  const int variant = gemv_plan(&d, 1, blocks);
+  if (variant < 0) return hipErrorInvalidValue;
+  const int grid = (int)blocks.size();
+  dim3 g(grid), b(kThreads);
+  if (variant >> 8) {
+    const int ipb = blocks[0].i1 - blocks[0].i0;  // one problem: equal blocks, the last maybe short
+    if (wfmt == UG_W_PACK5)
+      hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5>), g, b, 0, st, d, ipb);
+    else
+      hipLaunchKernelGGL((gemv_fine_single<UG_W_I8>), g, b, 0, st, d, ipb);
+    return hipGetLastError();
+  }
+#define UG_SINGLE(F, MBV) hipLaunchKernelGGL((gemv_stream_single<F, MBV>), g, b, 0, st, d)
+  if (wfmt == UG_W_PACK5) {
+    if (d.mb == 1) UG_SINGLE(UG_W_PACK5, 1);
+    else if (d.mb == 2) UG_SINGLE(UG_W_PACK5, 2);
+    else UG_SINGLE(UG_W_PACK5, 4);
+  } else {
+    if (d.mb == 1) UG_SINGLE(UG_W_I8, 1);
+    else if (d.mb == 2) UG_SINGLE(UG_W_I8, 2);
+    else UG_SINGLE(UG_W_I8, 4);
+  }
+#undef UG_SINGLE
+  return hipGetLastError();
 }
 
 }  // namespace ug

@@ -4,6 +4,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <vector>
 #include <stdint.h>
 
 #include "../../include/ug.h"
@@ -56,17 +59,26 @@ struct GemvDesc {
   int32_t item_begin;  // first item of this problem in a grouped plan
 };
 
-constexpr int kGemvBlocks = 256;  // one GEMV block per CU
+constexpr int kGemvBlocks = 256;  // at most one GEMV block per CU
 
-// Fills mb and items of d.
-void gemv_mfma_plan(GemvDesc &d);
-// Blocks to launch for a plan of `total_items` items.
+// One block of a GEMV launch: problem p and its item range [i0, i1) (fine
+// split), or the first problem p and the plan-wide item range (stream split).
+struct GemvBlock {
+  int32_t p, i0, i1, pad;
+};
+
+// Plans a group of problems for the matrix-core GEMV: picks the split (fine
+// or stream), fills mb, items and item_begin of every descriptor and one
+// GemvBlock per block to launch.  Returns the variant
+// (256 * fine + 16 * wfmt + mb), or -1 if the problems cannot share a launch.
+int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks);
+// Blocks to launch for `total_items` items of the stream split.
 int gemv_grid(int64_t total_items);
 // Whether the activations of a problem fit the kernel's LDS staging area
 // (required when the launch quantizes fp32 activations).
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K);
-hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, int32_t count, int32_t total_items,
-                               int32_t grid, int32_t fmt_mb, hipStream_t st);
+hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const GemvBlock *blocks_dev, int32_t count,
+                               int32_t grid, int32_t variant, hipStream_t st);
 hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const void *w, int wfmt, int64_t ldw, const float *beta,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,
