@@ -225,8 +225,10 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *i
   if (info->count < 1 || info->total_items < 1 || info->grid < 1 ||
       info->grid > ug::kGemvBlocks)
     return UG_ERR_INVALID_ARG;
-  const int fine = info->variant >> 8, fmt = (info->variant >> 4) & 15, mb = info->variant & 15;
-  if ((fine != 0 && fine != 1) || (fmt != UG_W_I8 && fmt != UG_W_PACK5) ||
+  // variant = 512 * fused + 256 * fine + 16 * wfmt + mb (fused only with fine)
+  const int hi = info->variant >> 8, fine = hi & 1, fmt = (info->variant >> 4) & 15,
+            mb = info->variant & 15;
+  if (hi > 3 || (hi == 2) || (fmt != UG_W_I8 && fmt != UG_W_PACK5) ||
       (mb != 1 && mb != 2 && mb != 4) || (fine && mb != 1))
     return UG_ERR_INVALID_ARG;
   const ug::GemvDesc *descs = (const ug::GemvDesc *)plan;

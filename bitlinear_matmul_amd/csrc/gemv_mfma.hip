@@ -115,6 +115,15 @@ __host__ __device__ __forceinline__ bool stages_x(int fmt, int M, int K) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Descriptor pointers are generic; every access through them goes through
+// these global-address-space views, so the compiler emits global (not flat)
+// memory instructions.  A flat access in flight makes every later wait for
+// a load a wait for all loads, which would serialize the weight pipeline.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *gp(T *p) {
+  return (__attribute__((address_space(1))) T *)p;
+}
+
 // Raw buffer resource over [base, base + bytes): a load past the end returns
 // zeros without a memory access (gfx9 descriptor word 3).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
@@ -213,15 +222,113 @@ __device__ __forceinline__ float row_scale(const Smem<FMT> &sh, int m, float eps
   return a127 + eps;
 }
 
-// Block set-up for problem d: decode table (first problem of the block),
-// row scales (fused quantization, else the given s), the activation rows
-// staged in LDS (Kp bytes per row, zeros past K; five trits per byte: every
-// 80-position window permuted as the decoded weights are) with the d4
-// correction cm[m] = sum_g x[5g+4], and zeroed reduction slots.  Every
-// thread issues its loads together.  Ends with a barrier.
+// Block set-up for problem d, in two halves.  setup_issue() issues the
+// first batch of activation loads; the caller then issues its weight loads,
+// so that waiting for the activations never waits for the weights (loads
+// complete in issue order).  setup_finish() builds the decode table (first
+// problem of the block), the row scales (fused quantization, else the given
+// s), the activation rows staged in LDS (Kp bytes per row, zeros past K;
+// five trits per byte: every 80-position window permuted as the decoded
+// weights are) with the d4 correction cm[m] = sum_g x[5g+4], and zeroed
+// reduction slots, and ends with a barrier.
+//
+// Fused quantization reads x in tiles t = (row m, 256 positions c): lane l
+// takes the float4 at 256 c + 4 l, a wave keeps 8 tiles in flight.
+struct XBatch {
+  float4 f[8];    // fused: the first 8 tiles of this wave
+  uint32_t q[8];  // x_q given: the first 8 dwords of this thread
+};
+
+__device__ __forceinline__ float4 load_tile(const GemvDesc &d, __amdgpu_buffer_rsrc_t xr, int t,
+                                            int T4, int nt) {
+  const int m = t / T4, k = (t - m * T4) * 256 + 4 * (threadIdx.x & 63);
+  // a float4 at k < K is inside the row (ldx >= round_up(K, 4))
+  return buffer_load16f(xr, t < nt && k < d.K ? (uint32_t)((m * (int)d.ldx + k) * 4) : kOOB);
+}
+
+__device__ __forceinline__ uint32_t load_xq4(const GemvDesc &d, __amdgpu_buffer_rsrc_t xr, int idx,
+                                             int Kp4, int n4) {
+  const int m = idx / Kp4, k = 4 * (idx - m * Kp4);
+  // 4 bytes at k < K are inside the row (ldxq >= round_up(K, 16))
+  return buffer_load4(xr, idx < n4 && k < d.K ? (uint32_t)(m * (int)d.ldxq + k) : kOOB);
+}
+
+// Both batches are issued without a branch (the one not needed reads past
+// its buffer, i.e. nothing), so every path sees the same loads in flight
+// and waiting for them never has to wait for the caller's later loads.
+__device__ __forceinline__ void setup_issue(const GemvDesc &d, bool staged, int Kp, XBatch &xb) {
+  const int tid = threadIdx.x, wave = uniform(tid >> 6);
+  const int T4 = (d.K + 255) >> 8, nt = d.x ? d.M * T4 : 0;
+  const __amdgpu_buffer_rsrc_t xr =
+      buffer_rsrc(d.x, d.x ? (uint32_t)((int64_t)d.M * d.ldx * 4) : 0u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xb.f[i] = load_tile(d, xr, wave + i * kWaves, T4, nt);
+  const int Kp4 = Kp >> 2, n4 = !d.x && staged ? d.M * Kp4 : 0;
+  const __amdgpu_buffer_rsrc_t qr =
+      buffer_rsrc(d.xq, n4 ? (uint32_t)((int64_t)d.M * d.ldxq) : 0u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xb.q[i] = load_xq4(d, qr, tid + i * kThreads, Kp4, n4);
+}
+
+// Pass 1 on 8 tiles t0 + i * 8: per-wave row maxima.
 template <int FMT>
-__device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool staged, int Kp,
-                                      bool build_table, bool zero_slots) {
+__device__ __forceinline__ void absmax_tiles(const GemvDesc &d, Smem<FMT> &sh, const float4 (&v)[8],
+                                             int t0, int T4, int nt) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + i * kWaves;
+    if (t < nt) {
+      const int m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
+      float a = fabsf(v[i].x);  // zero when k >= K
+      if (k + 1 < d.K) a = fmaxf(a, fabsf(v[i].y));
+      if (k + 2 < d.K) a = fmaxf(a, fabsf(v[i].z));
+      if (k + 3 < d.K) a = fmaxf(a, fabsf(v[i].w));
+      a = wave_max(a);
+      if (lane == 0) sh.part[wave][m] = fmaxf(sh.part[wave][m], a);
+    }
+  }
+}
+
+// Pass 2 on 8 tiles: quantize into the staging rows, K order.
+template <int FMT>
+__device__ __forceinline__ void quant_tiles(const GemvDesc &d, Smem<FMT> &sh, const float4 (&v)[8],
+                                            int t0, int T4, int nt, int Kp) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + i * kWaves;
+    if (t < nt) {
+      const int m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
+      const float s = row_scale(sh, m, d.eps);
+      if (k < d.K)
+        *reinterpret_cast<uint32_t *>(sh.xs + m * Kp + k) =
+            pack4(q8(v[i].x, s), k + 1 < d.K ? q8(v[i].y, s) : 0, k + 2 < d.K ? q8(v[i].z, s) : 0,
+                  k + 3 < d.K ? q8(v[i].w, s) : 0);
+    }
+  }
+}
+
+// 8 dwords of x_q rows into the staging rows (zeros past K).
+template <int FMT>
+__device__ __forceinline__ void copy_xq4(const GemvDesc &d, Smem<FMT> &sh, const uint32_t (&v)[8],
+                                         int i0, int Kp4, int n4) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = i0 + i * kThreads, m = idx / Kp4, k = 4 * (idx - m * Kp4);
+    if (idx < n4) {
+      uint32_t w = v[i];
+      if (k + 4 > d.K) w &= k >= d.K ? 0u : (0xffffffffu >> (8 * (k + 4 - d.K)));
+      reinterpret_cast<uint32_t *>(sh.xs + m * 4 * Kp4)[k >> 2] = w;
+    }
+  }
+}
+
+// PRE: the first batch is in xb (setup_issue); else every batch is loaded
+// here, which keeps the registers free for a caller short of them.
+template <int FMT, bool PRE>
+__device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, bool staged, int Kp,
+                                             bool build_table, bool zero_slots, const XBatch &xb) {
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   if (FMT == UG_W_PACK5 && build_table && tid < 256) sh.lut_tmp[tid] = lut4_entry(tid);
   if (tid < 64) sh.cm[tid] = 0;
@@ -231,58 +338,24 @@ __device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool sta
       reinterpret_cast<uint4 *>(sh.slots)[i] = make_uint4(0, 0, 0, 0);
   const int Kp4 = Kp >> 2;  // dwords per staged row
   if (d.x) {
-    // Pass 1: row maxima.  Tile t = (row m, 256 positions c): lane l reads
-    // the float4 at 256 c + 4 l; a wave keeps 8 tiles in flight.
     const int T4 = (d.K + 255) >> 8, nt = d.M * T4;
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.x, (uint32_t)((int64_t)d.M * d.ldx * 4));
     sh.part[wave][lane] = 0.0f;
-    const bool one = nt <= 8 * kWaves;  // one batch: keep the values for pass 2
-    float4 v[8];
-    for (int t0 = wave; t0 < nt; t0 += 8 * kWaves) {
+    if (PRE) absmax_tiles(d, sh, xb.f, wave, T4, nt);
+    for (int t0 = PRE ? wave + 8 * kWaves : wave; t0 < nt; t0 += 8 * kWaves) {
+      float4 v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = t0 + i * kWaves, m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
-        // a float4 at k < K is inside the row (ldx >= round_up(K, 4))
-        v[i] = buffer_load16f(xr, t < nt && k < d.K ? (uint32_t)((m * (int)d.ldx + k) * 4) : kOOB);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = t0 + i * kWaves;
-        if (t < nt) {
-          const int m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
-          float a = fabsf(v[i].x);  // zero when k >= K
-          if (k + 1 < d.K) a = fmaxf(a, fabsf(v[i].y));
-          if (k + 2 < d.K) a = fmaxf(a, fabsf(v[i].z));
-          if (k + 3 < d.K) a = fmaxf(a, fabsf(v[i].w));
-          a = wave_max(a);
-          if (lane == 0) sh.part[wave][m] = fmaxf(sh.part[wave][m], a);
-        }
-      }
+      for (int i = 0; i < 8; ++i) v[i] = load_tile(d, xr, t0 + i * kWaves, T4, nt);
+      absmax_tiles(d, sh, v, t0, T4, nt);
     }
     __syncthreads();
     if (tid < d.M) sh.sm[tid] = row_scale(sh, tid, d.eps);
-    // Pass 2: quantize into the staging rows, K order (from registers when
-    // pass 1 was one batch).
-    for (int t0 = wave; t0 < nt; t0 += 8 * kWaves) {
-      if (!one) {
+    if (PRE) quant_tiles(d, sh, xb.f, wave, T4, nt, Kp);
+    for (int t0 = PRE ? wave + 8 * kWaves : wave; t0 < nt; t0 += 8 * kWaves) {
+      float4 v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int t = t0 + i * kWaves, m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
-          v[i] = buffer_load16f(xr, t < nt && k < d.K ? (uint32_t)((m * (int)d.ldx + k) * 4) : kOOB);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = t0 + i * kWaves;
-        if (t < nt) {
-          const int m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
-          const float s = row_scale(sh, m, d.eps);
-          if (k < d.K)
-            *reinterpret_cast<uint32_t *>(sh.xs + m * Kp + k) =
-                pack4(q8(v[i].x, s), k + 1 < d.K ? q8(v[i].y, s) : 0,
-                      k + 2 < d.K ? q8(v[i].z, s) : 0, k + 3 < d.K ? q8(v[i].w, s) : 0);
-        }
-      }
+      for (int i = 0; i < 8; ++i) v[i] = load_tile(d, xr, t0 + i * kWaves, T4, nt);
+      quant_tiles(d, sh, v, t0, T4, nt, Kp);
     }
     // zeros from the first whole dword past K to the end of the staged row
     const int kz = (d.K + 3) >> 2, nz = Kp4 - kz;
@@ -291,27 +364,16 @@ __device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool sta
       reinterpret_cast<uint32_t *>(sh.xs + m * Kp)[kz + (i - m * nz)] = 0u;
     }
   } else {
-    if (tid < d.M) sh.sm[tid] = d.s[tid];
-    if (staged) {  // copy x_q rows, 8 dwords in flight per thread
-      const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
+    if (tid < d.M) sh.sm[tid] = gp(d.s)[tid];
+    if (staged) {
       const int n4 = d.M * Kp4;
-      for (int i0 = tid; i0 < n4; i0 += 8 * kThreads) {
+      const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
+      if (PRE) copy_xq4(d, sh, xb.q, tid, Kp4, n4);
+      for (int i0 = PRE ? tid + 8 * kThreads : tid; i0 < n4; i0 += 8 * kThreads) {
         uint32_t v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int idx = i0 + i * kThreads, m = idx / Kp4, k = 4 * (idx - m * Kp4);
-          // 4 bytes at k < K are inside the row (ldxq >= round_up(K, 16))
-          v[i] = buffer_load4(xr, idx < n4 && k < d.K ? (uint32_t)(m * (int)d.ldxq + k) : kOOB);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int idx = i0 + i * kThreads, m = idx / Kp4, k = 4 * (idx - m * Kp4);
-          if (idx < n4) {
-            uint32_t w = v[i];
-            if (k + 4 > d.K) w &= k >= d.K ? 0u : (0xffffffffu >> (8 * (k + 4 - d.K)));
-            reinterpret_cast<uint32_t *>(sh.xs + m * Kp)[k >> 2] = w;
-          }
-        }
+        for (int i = 0; i < 8; ++i) v[i] = load_xq4(d, xr, i0 + i * kThreads, Kp4, n4);
+        copy_xq4(d, sh, v, i0, Kp4, n4);
       }
     }
   }
@@ -345,7 +407,7 @@ __device__ __forceinline__ void setup(const GemvDesc &d, Smem<FMT> &sh, bool sta
     } else {  // correction straight from x_q
       for (int m = wave; m < d.M; m += kWaves) {
         int sum = 0;
-        for (int k = 5 * lane + 4; k < d.K; k += 5 * 64) sum += d.xq[(int64_t)m * d.ldxq + k];
+        for (int k = 5 * lane + 4; k < d.K; k += 5 * 64) sum += gp(d.xq)[(int64_t)m * d.ldxq + k];
         sum = wave_sum_i32(sum);
         if (lane == 0) sh.cm[m] = sum;
       }
@@ -360,7 +422,7 @@ template <int FMT>
 __device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<FMT> &sh, int Kp) {
   const int tid = threadIdx.x;
   if (d.s)
-    for (int m = tid; m < d.M; m += kThreads) d.s[m] = sh.sm[m];
+    for (int m = tid; m < d.M; m += kThreads) gp(d.s)[m] = sh.sm[m];
   if (d.xq) {
     int8_t *xq = const_cast<int8_t *>(d.xq);
     for (int idx = tid; idx < d.M * d.K; idx += kThreads) {
@@ -371,7 +433,7 @@ __device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<
         // t < 4: fragment g/4, dword g%4, byte t; t == 4: fragment 4, dword g/4, byte g%4
         off = 80 * w + (t < 4 ? 16 * (g >> 2) + 4 * (g & 3) + t : 64 + 4 * (g >> 2) + (g & 3));
       }
-      xq[(int64_t)m * d.ldxq + k] = sh.xs[m * Kp + off];
+      gp(xq)[(int64_t)m * d.ldxq + k] = sh.xs[m * Kp + off];
     }
   }
 }
@@ -533,10 +595,10 @@ struct Wave {
           const int m = 16 * b + 4 * q + r;
           if (n < d.N && m < d.M) {
             const int val = FMT == UG_W_PACK5 ? v[r] - cm[m] : v[r];
-            if (d.acc) d.acc[(int64_t)m * d.ldacc + n] = val;
+            if (d.acc) gp(d.acc)[(int64_t)m * d.ldacc + n] = val;
             if (d.y) {
               const float scale = sm[m] * beta;
-              d.y[(int64_t)m * d.ldy + n] = (float)val * scale;
+              gp(d.y)[(int64_t)m * d.ldy + n] = (float)val * scale;
             }
           }
         }
@@ -599,7 +661,7 @@ struct ItemLoop {
     iss_ch = pro_ch = 0;
     issue(d, A);
     issue(d, B);
-    beta = d.beta[0];
+    beta = gp(d.beta)[0];
   }
 
   // Needs the block's set-up (table, staged rows) to be complete.
@@ -632,10 +694,11 @@ __device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, in
     if (e <= g) continue;
     const bool staged = stages_x(FMT, d.M, d.K);
     const int Kp = staged_kp(FMT, MB, d.K);
+    XBatch xb;  // unused: the set-up loads its own batches here
     ItemLoop<FMT, MB> loop;
     loop.start(d, staged, Kp, g - d.item_begin, e - d.item_begin);
     if (!first) __syncthreads();  // the previous problem's staged rows are done
-    setup<FMT>(d, sh, staged, Kp, first, false);
+    setup_finish<FMT, false>(d, sh, staged, Kp, first, false, xb);
     first = false;
     loop.run(d, sh);
     if (d.x && g == d.item_begin) write_act_outputs<FMT>(d, sh, Kp);
@@ -661,12 +724,256 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_grouped(const GemvDesc *
 // ---------------------------------------------------------------------------
 // Fine split (M <= 16, staged activations).
 //
+// A decode-sized launch is one chain of dependent steps per wave, and a wave
+// issues at most one instruction every four cycles, so this path keeps the
+// instruction count of every step small: no lane divides by a run-time
+// value, and the problem's kind (fp32 activations or x_q) is a template
+// parameter instead of a branch.
+
+// A wave's share of the tiles of the staged rows: tiles [t, te) of the M * T
+// tiles (row m = t / T, chunk c = t % T), taken 8 at a time with (m, c)
+// advanced by increments: one division per wave.
+struct TileWalk {
+  int t, te, m, c, T;
+  __device__ __forceinline__ void init(int nt, int T_) {
+    const int wave = uniform(threadIdx.x >> 6);
+    T = T_;
+    t = (wave * nt) / kWaves;
+    te = ((wave + 1) * nt) / kWaves;
+    m = t / T;
+    c = t - m * T;
+  }
+};
+struct TileBatch {
+  bool ok[8];
+  int m[8], c[8];
+};
+__device__ __forceinline__ void next8(TileWalk &w, TileBatch &b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    b.ok[i] = w.t + i < w.te;
+    b.m[i] = w.m;
+    b.c[i] = w.c;
+    if (++w.c == w.T) {
+      w.c = 0;
+      ++w.m;
+    }
+  }
+  w.t += 8;
+}
+
+// fp32 tiles: 256 positions, lane l the float4 at 256 c + 4 l (a float4 at
+// k < K is inside the row: ldx >= round_up(K, 4)).  x_q tiles: 1024 bytes,
+// lane l the 16 bytes at 1024 c + 16 l (inside the row when k < K: ldxq >=
+// round_up(K, 16)).
+template <bool FUSED>
+__device__ __forceinline__ void load_batch(const GemvDesc &d, __amdgpu_buffer_rsrc_t xr,
+                                           const TileBatch &b, uint4 (&u)[8]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (FUSED) {
+      const int k = b.c[i] * 256 + 4 * lane;
+      u[i] = buffer_load16(xr, b.ok[i] && k < d.K ? (uint32_t)((b.m[i] * (int)d.ldx + k) * 4) : kOOB);
+    } else {
+      const int k = b.c[i] * 1024 + 16 * lane;
+      u[i] = buffer_load16(xr, b.ok[i] && k < d.K ? (uint32_t)(b.m[i] * (int)d.ldxq + k) : kOOB);
+    }
+  }
+}
+
+template <bool FUSED>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const GemvDesc &d) {
+  return FUSED ? buffer_rsrc(d.x, (uint32_t)((int64_t)d.M * d.ldx * 4))
+               : buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
+}
+
+template <bool FUSED>
+__device__ __forceinline__ int tiles_per_row(int Kp) {
+  return FUSED ? (Kp + 255) >> 8 : (Kp + 1023) >> 10;  // the tiles cover whole staged rows
+}
+
+// Pass 1 of fused quantization: per-wave row maxima.
+template <int FMT>
+__device__ __forceinline__ void fine_absmax(const GemvDesc &d, Smem<FMT> &sh, const TileBatch &b,
+                                            const uint4 (&u)[8]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (b.ok[i]) {
+      const float4 v = __builtin_bit_cast(float4, u[i]);
+      const int k = b.c[i] * 256 + 4 * lane;
+      float a = fabsf(v.x);  // zero when k >= K
+      if (k + 1 < d.K) a = fmaxf(a, fabsf(v.y));
+      if (k + 2 < d.K) a = fmaxf(a, fabsf(v.z));
+      if (k + 3 < d.K) a = fmaxf(a, fabsf(v.w));
+      a = wave_max(a);
+      if (lane == 0) sh.part[wave][b.m[i]] = fmaxf(sh.part[wave][b.m[i]], a);
+    }
+  }
+}
+
+// Pass 2: quantized dwords into the staged rows (zeros past K), and into x_q
+// when the block writes the outputs.
+template <int FMT>
+__device__ __forceinline__ void fine_quant(const GemvDesc &d, Smem<FMT> &sh, const TileBatch &b,
+                                           const uint4 (&u)[8], int Kp, bool outputs) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = b.m[i], k = b.c[i] * 256 + 4 * lane;
+    if (b.ok[i] && k < Kp) {
+      const float4 v = __builtin_bit_cast(float4, u[i]);
+      const float s = row_scale(sh, m, d.eps);
+      const uint32_t w = k < d.K ? pack4(q8(v.x, s), k + 1 < d.K ? q8(v.y, s) : 0,
+                                         k + 2 < d.K ? q8(v.z, s) : 0, k + 3 < d.K ? q8(v.w, s) : 0)
+                                 : 0u;
+      *reinterpret_cast<uint32_t *>(sh.xs + m * Kp + k) = w;
+      if (outputs && k < d.K) {
+        int8_t *row = const_cast<int8_t *>(d.xq) + (int64_t)m * d.ldxq;
+        if (k + 4 <= d.K) {
+          *gp(reinterpret_cast<uint32_t *>(row + k)) = w;  // rows are 16-byte aligned
+        } else {
+          for (int j = 0; k + j < d.K; ++j) gp(row)[k + j] = (int8_t)(w >> (8 * j));
+        }
+      }
+    }
+  }
+}
+
+// x_q tiles into the staged rows, bytes past K zeroed.
+template <int FMT>
+__device__ __forceinline__ void fine_copy(const GemvDesc &d, Smem<FMT> &sh, const TileBatch &b,
+                                          const uint4 (&u)[8], int Kp) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = b.c[i] * 1024 + 16 * lane;
+    if (b.ok[i] && k < Kp) {
+      uint32_t w4[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kb = d.K - k - 4 * e;  // bytes of this dword inside the row
+        w4[e] &= kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb))));
+      }
+      *reinterpret_cast<uint4 *>(sh.xs + b.m[i] * Kp + k) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
+}
+
+// The first batch of a wave's activation tiles, issued by the caller before
+// its weight loads: loads complete in issue order, so waiting for these
+// never waits for the weights.
+template <bool FUSED>
+__device__ __forceinline__ void fine_issue_x(const GemvDesc &d, int Kp, TileWalk &walk,
+                                             TileBatch &b0, uint4 (&u0)[8]) {
+  walk.init(d.M * tiles_per_row<FUSED>(Kp), tiles_per_row<FUSED>(Kp));
+  next8(walk, b0);
+  load_batch<FUSED>(d, x_rsrc<FUSED>(d), b0, u0);
+}
+
+// Block set-up of the fine split: decode table, row scales, staged rows
+// from the wave's tiles (the first batch already loaded), the five-trit
+// permutation with the correction cm, zeroed slots.  s_in: with x_q given,
+// thread m < M holds s[m].  Ends with a barrier.
+template <int FMT, bool FUSED>
+__device__ __forceinline__ void fine_setup(const GemvDesc &d, Smem<FMT> &sh, int Kp,
+                                           bool first_block, const TileWalk &walk,
+                                           const TileBatch &b0, const uint4 (&u0)[8],
+                                           float s_in) {
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  if (FMT == UG_W_PACK5 && tid < 256) sh.lut_tmp[tid] = lut4_entry(tid);
+  if (tid < 64) sh.cm[tid] = 0;
+  if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
+#pragma unroll
+  for (int i = 0; i < kFineItems * 64 / kThreads; ++i)
+    reinterpret_cast<uint4 *>(sh.slots)[tid + i * kThreads] = make_uint4(0, 0, 0, 0);
+  const __amdgpu_buffer_rsrc_t xr = x_rsrc<FUSED>(d);
+  if (FUSED) {
+    sh.part[wave][lane] = 0.0f;
+    fine_absmax(d, sh, b0, u0);
+    TileWalk w = walk;
+    while (w.t < w.te) {
+      TileBatch b;
+      uint4 u[8];
+      next8(w, b);
+      load_batch<true>(d, xr, b, u);
+      fine_absmax(d, sh, b, u);
+    }
+    __syncthreads();
+    const bool outputs = first_block && d.xq;
+    if (tid < d.M) {
+      const float s = row_scale(sh, tid, d.eps);
+      sh.sm[tid] = s;
+      if (first_block && d.s) gp(d.s)[tid] = s;
+    }
+    fine_quant(d, sh, b0, u0, Kp, outputs);
+    w = walk;
+    while (w.t < w.te) {
+      TileBatch b;
+      uint4 u[8];
+      next8(w, b);
+      load_batch<true>(d, xr, b, u);
+      fine_quant(d, sh, b, u, Kp, outputs);
+    }
+  } else {
+    if (tid < d.M) sh.sm[tid] = s_in;
+    fine_copy(d, sh, b0, u0, Kp);
+    TileWalk w = walk;
+    while (w.t < w.te) {
+      TileBatch b;
+      uint4 u[8];
+      next8(w, b);
+      load_batch<false>(d, xr, b, u);
+      fine_copy(d, sh, b, u, Kp);
+    }
+  }
+  __syncthreads();
+  if (FMT == UG_W_PACK5) {
+    uint4 *chunks = reinterpret_cast<uint4 *>(sh.lut);  // 64 replicas, 16-byte chunks
+#pragma unroll
+    for (int i = 0; i < 256 * kRepl / 4 / kThreads; ++i) {
+      const int c = tid + kThreads * i;
+      const uint32_t v = sh.lut_tmp[c >> 4];
+      chunks[c] = make_uint4(v, v, v, v);
+    }
+    // every 80-position window permuted in place: thread per window, the
+    // windows of one row on consecutive threads
+    const int wpr = Kp / 80;
+    int m = 0, w0 = tid;
+    while (w0 >= wpr && m < d.M) {  // row of this thread's first window (few steps: wpr >= 1)
+      w0 -= wpr;
+      ++m;
+    }
+    for (; m < d.M; ) {
+      uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * Kp + w0 * 80);
+      uint32_t X[20], F[20];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const uint4 q = win[i];
+        X[4 * i] = q.x; X[4 * i + 1] = q.y; X[4 * i + 2] = q.z; X[4 * i + 3] = q.w;
+      }
+      permute80(X, F);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) win[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
+      atomicAdd(&sh.cm[m], byte_sum4(F[16]) + byte_sum4(F[17]) + byte_sum4(F[18]) + byte_sum4(F[19]));
+      w0 += kThreads;
+      while (w0 >= wpr && m < d.M) {
+        w0 -= wpr;
+        ++m;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Items [i0, i1) of problem d (16 rows each), S steps per item: piece
 // p = (item i0 + p / S, step p % S).  Wave w takes pieces [w P / 8,
-// (w + 1) P / 8) of the block's P, loads them all before the set-up, and adds
-// its partial sums to the item's LDS slot whenever its next piece belongs to
-// another item.  After a barrier the block writes every item's outputs.
-template <int FMT>
+// (w + 1) P / 8) of the block's P, issues all their weight loads first (the
+// set-up's activation loads follow them), and adds its partial sums to the
+// item's LDS slot whenever its next piece belongs to another item.  After a
+// barrier the block writes every item's outputs.
+template <int FMT, bool FUSED>
 __device__ __forceinline__ void fine_block(const GemvDesc &d, int i0, int i1) {
   using W = Wave<FMT, 1, true>;
   constexpr int NACC = W::NACC;
@@ -675,11 +982,17 @@ __device__ __forceinline__ void fine_block(const GemvDesc &d, int i0, int i1) {
   const int S = steps_of(FMT, d.K), Kp = fine_kp(FMT, d.K);
   const int P = (i1 - i0) * S;
   const int p0 = uniform(wave * P / kWaves), p1 = uniform((wave + 1) * P / kWaves);
+  const int it0 = p0 / S, st0 = p0 - it0 * S;
+  const float s_in = !FUSED && tid < d.M ? gp(d.s)[tid] : 0.0f;
+  TileWalk walk;
+  TileBatch b0;
+  uint4 x0[8];
+  fine_issue_x<FUSED>(d, Kp, walk, b0, x0);
   W wv;
   wv.init(d, true, Kp);
   uint4 wb[kFinePieces][1][1];
   {
-    int it = p0 / S, st = p0 - it * S;
+    int it = it0, st = st0;
 #pragma unroll
     for (int j = 0; j < kFinePieces; ++j) {
       wv.issue(d, i0 + it, st, p0 + j < p1, wb[j]);
@@ -689,13 +1002,13 @@ __device__ __forceinline__ void fine_block(const GemvDesc &d, int i0, int i1) {
       }
     }
   }
-  const float beta = d.beta[0];
-  setup<FMT>(d, sh, true, Kp, true, true);
+  const float beta = gp(d.beta)[0];
+  fine_setup<FMT, FUSED>(d, sh, Kp, i0 == 0, walk, b0, x0, s_in);
   const char *lut = reinterpret_cast<const char *>(sh.lut);
   v4i acc[1][1][NACC];
 #pragma unroll
   for (int a = 0; a < NACC; ++a) acc[0][0][a] = v4i{0, 0, 0, 0};
-  int it = p0 / S, st = p0 - it * S;
+  int it = it0, st = st0;
 #pragma unroll
   for (int j = 0; j < kFinePieces; ++j) {
     if (p0 + j < p1) {
@@ -718,37 +1031,28 @@ __device__ __forceinline__ void fine_block(const GemvDesc &d, int i0, int i1) {
     }
   }
   __syncthreads();
-  const int per_item = d.M * 16;
-  for (int idx = tid; idx < (i1 - i0) * per_item; idx += kThreads) {
-    const int li = idx / per_item, rem = idx - li * per_item, m = rem >> 4, n = rem & 15;
-    const int ng = (i0 + li) * 16 + n;
+  if (tid < (i1 - i0) * 16) {  // thread (item, n) writes column n of the item, every row
+    const int li = tid >> 4, n = tid & 15, ng = (i0 + li) * 16 + n;
     if (ng < d.N) {
-      int val = sh.slots[li * 256 + m * 16 + n];
-      if (FMT == UG_W_PACK5) val -= sh.cm[m];
-      if (d.acc) d.acc[(int64_t)m * d.ldacc + ng] = val;
-      if (d.y) {
-        const float scale = sh.sm[m] * beta;
-        d.y[(int64_t)m * d.ldy + ng] = (float)val * scale;
+      for (int m = 0; m < d.M; ++m) {
+        const int val = sh.slots[li * 256 + m * 16 + n] - (FMT == UG_W_PACK5 ? sh.cm[m] : 0);
+        if (d.acc) gp(d.acc)[(int64_t)m * d.ldacc + ng] = val;
+        if (d.y) gp(d.y)[(int64_t)m * d.ldy + ng] = (float)val * (sh.sm[m] * beta);
       }
     }
   }
-  if (d.x && i0 == 0) write_act_outputs<FMT>(d, sh, Kp);
 }
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void gemv_fine_single(GemvDesc d, int ipb) {
   const int i0 = blockIdx.x * ipb, i1 = min(d.items, i0 + ipb);
-  if (i0 < i1) fine_block<FMT>(d, i0, i1);
+  if (i0 < i1) fine_block<FMT, false>(d, i0, i1);
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void gemv_fine_grouped(const GemvDesc *__restrict__ plan,
-                                                              const GemvBlock *__restrict__ blocks) {
+template <int FMT, bool FUSED>
+__global__ __launch_bounds__(kThreads) void gemv_fine_grouped(const GemvBlock *__restrict__ blocks) {
   const GemvBlock bl = blocks[blockIdx.x];
-  if (bl.i0 < bl.i1) {
-    const GemvDesc d = plan[bl.p];
-    fine_block<FMT>(d, bl.i0, bl.i1);
-  }
+  if (bl.i0 < bl.i1) fine_block<FMT, FUSED>(bl.d, bl.i0, bl.i1);
 }
 
 // ---------------------------------------------------------------------------
@@ -762,6 +1066,7 @@ bool plan_fine(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
   for (int i = 0; i < count; ++i) {
     const GemvDesc &d = descs[i];
     if (d.M > 16 || (int64_t)d.M * fine_kp(d.wfmt, d.K) > kXsBytes) return false;
+    if ((d.x != nullptr) != (descs[0].x != nullptr)) return false;  // one kind per launch
     T += (int64_t)((d.N + 15) / 16) * steps_of(d.wfmt, d.K);
   }
   if (T > (int64_t)kGemvBlocks * kWaves * kFinePieces) return false;
@@ -789,7 +1094,7 @@ bool plan_fine(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
     descs[i].mb = 1;
     descs[i].items = items;
     for (int a = 0; a < items; a += ipb[(size_t)i])
-      blocks.push_back(GemvBlock{i, a, std::min(items, a + ipb[(size_t)i]), 0});
+      blocks.push_back(GemvBlock{descs[i], i, a, std::min(items, a + ipb[(size_t)i]), 0});
   }
   return true;
 }
@@ -813,7 +1118,7 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
       descs[i].item_begin = (int32_t)total;
       total += descs[i].items;
     }
-    return 256 + 16 * fmt + 1;
+    return (descs[0].x ? 512 : 0) + 256 + 16 * fmt + 1;
   }
   const int mb = mb_of(descs[0].M);
   for (int i = 0; i < count; ++i) {
@@ -832,7 +1137,7 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
   for (int b = 0; b < grid; ++b) {
     const int g0 = (int)(total * b / grid), g1 = (int)(total * (b + 1) / grid);
     while (p + 1 < count && descs[p + 1].item_begin <= g0) ++p;
-    blocks.push_back(GemvBlock{p, g0, g1, 0});
+    blocks.push_back(GemvBlock{descs[p], p, g0, g1, 0});
   }
   return 16 * fmt + mb;
 }
@@ -843,14 +1148,17 @@ bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
 
 hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const GemvBlock *blocks_dev, int32_t count,
                                int32_t grid, int32_t variant, hipStream_t st) {
-  const bool fine = variant >> 8;
+  const bool fine = (variant >> 8) & 1, fused = (variant >> 9) & 1;
   const int fmt = (variant >> 4) & 15, mb = variant & 15;
   dim3 g(grid), b(kThreads);
   if (fine) {
-    if (fmt == UG_W_PACK5)
-      hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5>), g, b, 0, st, plan_dev, blocks_dev);
-    else
-      hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8>), g, b, 0, st, plan_dev, blocks_dev);
+    if (fmt == UG_W_PACK5) {
+      if (fused) hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5, true>), g, b, 0, st, blocks_dev);
+      else hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5, false>), g, b, 0, st, blocks_dev);
+    } else {
+      if (fused) hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8, true>), g, b, 0, st, blocks_dev);
+      else hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8, false>), g, b, 0, st, blocks_dev);
+    }
     return hipGetLastError();
   }
 #define UG_GROUPED(F, MBV) \
@@ -892,7 +1200,7 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
   if (variant < 0) return hipErrorInvalidValue;
   const int grid = (int)blocks.size();
   dim3 g(grid), b(kThreads);
-  if (variant >> 8) {
+  if ((variant >> 8) & 1) {
     const int ipb = blocks[0].i1 - blocks[0].i0;  // one problem: equal blocks, the last maybe short
     if (wfmt == UG_W_PACK5)
       hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5>), g, b, 0, st, d, ipb);

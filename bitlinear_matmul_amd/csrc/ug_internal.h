@@ -62,15 +62,18 @@ struct GemvDesc {
 constexpr int kGemvBlocks = 256;  // at most one GEMV block per CU
 
 // One block of a GEMV launch: problem p and its item range [i0, i1) (fine
-// split), or the first problem p and the plan-wide item range (stream split).
+// split), or the first problem p and the plan-wide item range (stream split),
+// with a copy of problem p's descriptor (one load at block start).
 struct GemvBlock {
+  GemvDesc d;
   int32_t p, i0, i1, pad;
 };
 
 // Plans a group of problems for the matrix-core GEMV: picks the split (fine
 // or stream), fills mb, items and item_begin of every descriptor and one
 // GemvBlock per block to launch.  Returns the variant
-// (256 * fine + 16 * wfmt + mb), or -1 if the problems cannot share a launch.
+// (512 * fused + 256 * fine + 16 * wfmt + mb; fused: the fine split with fp32
+// activations), or -1 if the problems cannot share a launch.
 int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks);
 // Blocks to launch for `total_items` items of the stream split.
 int gemv_grid(int64_t total_items);
