@@ -58,7 +58,54 @@ def parse():
                    choices=["decode_stack", "sweep", "prefill", "stack", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="first run one plain 256 MiB device copy (a known-size kernel that "
+                        "calibrates the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
     return p.parse_args()
+
+
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
+# of this script (FETCH_SIZE, then WRITE_SIZE), each scaled by the reading of
+# the same counter for a plain 256 MiB copy in the same run (--copy-probe).
+# Valid only for the kernel sources they were taken on: `src_sha` is the
+# SHA-256 of the kernel's source file; any other source reports null.
+TRAFFIC = {
+    # profiles/gemv_fine_grouped_decode_stack.md: 2105.6 KiB fetched x 1.9997,
+    # 146.4 KiB written x 1.0000
+    "decode_stack": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
+                         src_sha="af54f1408d60cc969bb186a8b73ea40b3a3cad5854ea1e4d32bdc30cf139fac3",
+                         bytes_per_launch=4461598),
+    # profiles/gemm_i8_prefill.md: mean of both shapes, 161171.9 KiB fetched
+    # x 1.9997, 75780.8 KiB written x 1.0000
+    "prefill": dict(src="bitlinear_matmul_amd/csrc/gemm.hip",
+                    src_sha="4e8b5895b1adf511f4ee0e00e61ceec4075b7a30d3c6db665e77ba3bddba50c0",
+                    bytes_per_launch=407625154),
+}
+
+
+def source_sha(relpath):
+    import hashlib
+    with open(os.path.join(ROOT, relpath), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload):
+    t = TRAFFIC.get(workload)
+    if t is None or source_sha(t["src"]) != t["src_sha"]:
+        return None
+    return t["bytes_per_launch"]
+
+
+def copy_probe(torch):
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy probe: %d bytes read, %d bytes written" % (n, n))
+    del a, b
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
@@ -165,6 +212,12 @@ def run_decode_stack(args, torch, ug, inputs):
     time_graph(torch, g_warm, stream)
     ms = time_graph(torch, g_run, stream)
     log("decode_stack: %d steps in %.3f ms" % (steps, ms))
+    # hot regime: one weight copy, resident in L2 / MALL (the realistic
+    # regime for a 3 MB model); reported beside the cold value
+    g_hot = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[0]) for _ in range(steps)])
+    time_graph(torch, g_hot, stream)
+    ms_hot = time_graph(torch, g_hot, stream)
+    del g_hot
     # The step is one launch of the grouped kernel, so the kernel's average
     # launch duration is the step time (inter-launch gap included).
     alg = sum(gemv_alg_bytes(1, m["N"], m["K"], fp32_x=True) for m in mats)
@@ -172,15 +225,17 @@ def run_decode_stack(args, torch, ug, inputs):
     achieved = alg / avg_launch_s / 1e9
     value = per_pass_bytes * steps / (ms / 1e3) / 1e9
     out = dict(value=value, unit="GB/s", ms_per_step=ms / steps, steps=steps, warmup=warm,
-               dtype="int8 x trit -> int32 (MFMA), fp32 scales",
+               dtype="i8 (int32 accumulate)",
                config={"workload": "decode_stack", "batch": 1, "matrices": len(mats),
                        "weight_format": "pack5", "packed_weight_bytes_per_step": per_pass_bytes,
                        "launches_per_step": 1, "weight_copies_cycled": n_copies,
                        "regime": "cold (each step reads its own weight copy from HBM)",
-                       "us_per_token_pass": ms * 1e3 / steps},
-               roofline=dict(bound="hbm", kernel="gemv_grouped_kernel<PACK5,1>",
+                       "us_per_token_pass": ms * 1e3 / steps,
+                       "hot_us_per_token_pass": ms_hot * 1e3 / steps,
+                       "hot_weight_GBps": per_pass_bytes * steps / (ms_hot / 1e3) / 1e9},
+               roofline=dict(bound="hbm", kernel="gemv_fine_grouped<PACK5, fused>",
                              achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=achieved / HBM_PEAK_GBS, traffic=None,
+                             frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("decode_stack"),
                              avg_launch_us=avg_launch_s * 1e6, alg_bytes_per_launch=alg))
     if not args.no_cpu_baseline:
         import oracle
@@ -251,16 +306,17 @@ def run_sweep(args, torch, ug, inputs):
                 tot_bytes += wbytes * G
                 tot_s += launch_us * 1e-6
                 if M == 1 and si == 0:
-                    dom = dict(bound="hbm", kernel="gemv_grouped_kernel<PACK5,1>",
+                    dom = dict(bound="hbm", kernel="gemv_stream_grouped<PACK5, 1>",
                                achieved=alg / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
                                unit="GB/s", frac=alg / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                               traffic=None, avg_launch_us=launch_us, alg_bytes_per_launch=alg,
+                               traffic=traffic_for("sweep"), avg_launch_us=launch_us,
+                               alg_bytes_per_launch=alg,
                                point="M=1 K=2560 N=6912, %d copies per launch" % G)
         del copies
         torch.cuda.empty_cache()
     value = tot_bytes / tot_s / 1e9
     return dict(value=value, unit="GB/s", ms_per_step=tot_s * 1e3 / len(points), steps=steps,
-                warmup=warm, dtype="int8 x trit -> int32 (MFMA), fp32 scales",
+                warmup=warm, dtype="i8 (int32 accumulate)",
                 config={"workload": "sweep", "points": points, "weight_format": "pack5",
                         "regime": "cold; value = grouped streaming over all points"},
                 roofline=dom)
@@ -312,13 +368,13 @@ def run_prefill(args, torch, ug, inputs):
     gemm_ms = e0.elapsed_time(e1) / (2 * steps)
     achieved = ops_per_step / 2 / (gemm_ms / 1e3) / 1e12
     out = dict(value=ops_per_step * steps / (ms / 1e3) / 1e12, unit="TOP/s",
-               ms_per_step=ms / steps, steps=steps, warmup=warm, dtype="int8 MFMA -> int32",
+               ms_per_step=ms / steps, steps=steps, warmup=warm, dtype="i8 (int32 accumulate)",
                config={"workload": "prefill", "M": M, "shapes_KxN": [[l["K"], l["N"]]
                                                                      for l in layers],
                        "weight_format": "i8"},
                roofline=dict(bound="mfma", kernel="gemm_i8_kernel", achieved=achieved,
                              peak=INT8_PEAK_TOPS, unit="TOP/s", frac=achieved / INT8_PEAK_TOPS,
-                             traffic=None, avg_launch_us=gemm_ms * 1e3,
+                             traffic=traffic_for("prefill"), avg_launch_us=gemm_ms * 1e3,
                              alg_ops_per_launch=ops_per_step / 2))
     if not args.no_cpu_baseline:
         import oracle
@@ -342,6 +398,171 @@ def run_prefill(args, torch, ug, inputs):
     return out
 
 
+# ---------------------------------------------------------------------------
+# stack: 30 layers x {2560->6912, 6912->2560} at M=2048 with requantization
+# ---------------------------------------------------------------------------
+def run_stack(args, torch, ug, inputs):
+    """One step: requantize all 60 fp32 masters (absmean + ternary), then the
+    chain of 60 x (RMSNorm + act quant + int8 GEMM) from x0."""
+    steps = args.steps if args.steps is not None else 3
+    warm = args.warmup if args.warmup is not None else 1
+    dev = torch.device("cuda:0")
+    M = inputs.STACK_M
+    mats = []
+    for layer in range(inputs.STACK_LAYERS):
+        for which in (0, 1):
+            K, N = inputs.STACK_SHAPES[which]
+            W = torch.from_numpy(inputs.stack_master(layer, which)).to(dev)
+            mats.append(dict(K=K, N=N, W=W, wq=ug.empty_pitched(N, K, torch.int8, dev),
+                             beta=torch.empty(1, dtype=torch.float32, device=dev),
+                             xq=ug.empty_pitched(M, K, torch.int8, dev),
+                             s=torch.empty(M, dtype=torch.float32, device=dev),
+                             y=ug.empty_pitched(M, N, torch.float32, dev)))
+    ws = torch.empty(max(ug.ug_quant_weight_absmean_workspace_size(m["N"], m["K"]) for m in mats),
+                     dtype=torch.uint8, device=dev)
+    x0 = torch.from_numpy(inputs.stack_x0()).to(dev)
+    ops_per_step = sum(2 * M * m["N"] * m["K"] for m in mats)
+    log("stack: %d BitLinears, %.3g int8 ops per step" % (len(mats), ops_per_step))
+
+    def requant():
+        for m in mats:
+            ug.ug_quant_weight_absmean(m["W"], wq=m["wq"], beta=m["beta"], ws=ws)
+
+    def chain(gemm_only=False):
+        x = x0
+        for m in mats:
+            if not gemm_only:
+                ug.ug_rmsnorm_quant_act(x, xq=m["xq"], s=m["s"])
+            ug.ug_bitlinear_gemm(m["xq"], m["s"], m["wq"], ug.UG_W_I8, m["beta"], y=m["y"])
+            x = m["y"]
+
+    stream = torch.cuda.current_stream()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for _ in range(warm):
+        requant()
+        chain()
+    torch.cuda.synchronize()
+    t_req = t_chain = 0.0
+    e_all0, e_all1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_all0.record(stream)
+    for _ in range(steps):
+        e[0].record(stream)
+        requant()
+        e[1].record(stream)
+        chain()
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        t_req += e[0].elapsed_time(e[1])
+        t_chain += e[1].elapsed_time(e[2])
+    e_all1.record(stream)
+    torch.cuda.synchronize()
+    ms = t_req + t_chain
+    # the GEMMs alone (the dominant kernel), same chain of operands
+    e[0].record(stream)
+    for _ in range(steps):
+        chain(gemm_only=True)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = e[0].elapsed_time(e[1]) / (steps * len(mats))
+    req_bytes = sum(9 * m["N"] * m["K"] for m in mats)
+    act_bytes = sum(4 * M * m["K"] + M * m["K"] + 4 * M for m in mats)
+    achieved = ops_per_step / len(mats) / (gemm_ms / 1e3) / 1e12
+    out = dict(value=ops_per_step * steps / (ms / 1e3) / 1e12, unit="TOP/s",
+               ms_per_step=ms / steps, steps=steps, warmup=warm, dtype="i8 (int32 accumulate)",
+               config={"workload": "stack", "layers": inputs.STACK_LAYERS, "M": M,
+                       "shapes_KxN": [list(x) for x in inputs.STACK_SHAPES],
+                       "weight_format": "i8", "requant_ms_per_step": t_req / steps,
+                       "requant_GBps": req_bytes * steps / (t_req / 1e3) / 1e9,
+                       "chain_ms_per_step": t_chain / steps,
+                       "gemm_us_per_launch": gemm_ms * 1e3,
+                       "act_quant_alg_bytes_per_step": act_bytes},
+               roofline=dict(bound="mfma", kernel="gemm_i8_kernel", achieved=achieved,
+                             peak=INT8_PEAK_TOPS, unit="TOP/s", frac=achieved / INT8_PEAK_TOPS,
+                             traffic=traffic_for("stack"), avg_launch_us=gemm_ms * 1e3,
+                             alg_ops_per_launch=ops_per_step / len(mats)))
+    if not args.no_cpu_baseline:
+        import oracle
+        # bounded sample: layer 0 (both BitLinears) at the first rows of x0,
+        # including the requantization of its two masters
+        x = inputs.stack_x0()
+        masters = [inputs.stack_master(0, w) for w in (0, 1)]
+        rows, ops = 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds and rows < M:
+            xr = x[rows:rows + 64]
+            for Wm in masters:
+                wq, beta = oracle.quant_weight_absmean(Wm)
+                xq, s = oracle.rmsnorm_quant_act(xr)
+                xr = oracle.epilogue(oracle.matmul_i32(xq, wq), s, beta)
+                ops += 2 * xq.shape[0] * wq.shape[0] * wq.shape[1]
+            rows += 64
+        secs = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(value=ops / secs / 1e12, unit="TOP/s",
+                                   cores=oracle.num_threads(), kind="oracle",
+                                   sample="layer 0 (requant of both masters + RMSNorm/quant + "
+                                          "int matmul + rescale, both BitLinears) on %d of "
+                                          "2048 rows per pass, %.1f s" % (rows, secs))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# tiny: x[32,128], W[512,128], one trit per byte, the whole path
+# ---------------------------------------------------------------------------
+def run_tiny(args, torch, ug, inputs):
+    steps = args.steps if args.steps is not None else 200
+    warm = args.warmup if args.warmup is not None else 20
+    dev = torch.device("cuda:0")
+    x, W = inputs.tiny_layer()
+    xd, Wd = torch.from_numpy(x).to(dev), torch.from_numpy(W).to(dev)
+    M, K = x.shape
+    N = W.shape[0]
+    wq = ug.empty_pitched(N, K, torch.int8, dev)
+    beta = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(ug.ug_quant_weight_absmean_workspace_size(N, K), dtype=torch.uint8, device=dev)
+    xq = ug.empty_pitched(M, K, torch.int8, dev)
+    s = torch.empty(M, dtype=torch.float32, device=dev)
+    y = ug.empty_pitched(M, N, torch.float32, dev)
+
+    def step():
+        ug.ug_quant_weight_absmean(Wd, wq=wq, beta=beta, ws=ws)
+        ug.ug_quant_act(xd, 1e-5, xq=xq, s=s)
+        ug.ug_bitlinear_gemm(xq, s, wq, ug.UG_W_I8, beta, y=y)
+
+    stream = torch.cuda.current_stream()
+    g = capture(torch, lambda: [step() for _ in range(steps)])
+    time_graph(torch, g, stream)
+    ms = time_graph(torch, g, stream)
+    g2 = capture(torch, lambda: [ug.ug_bitlinear_gemm(xq, s, wq, ug.UG_W_I8, beta, y=y)
+                                 for _ in range(steps)])
+    time_graph(torch, g2, stream)
+    gemm_ms = time_graph(torch, g2, stream) / steps
+    ops = 2 * M * N * K
+    out = dict(value=ops * steps / (ms / 1e3) / 1e12, unit="TOP/s", ms_per_step=ms / steps,
+               steps=steps, warmup=warm, dtype="i8 (int32 accumulate)",
+               config={"workload": "tiny", "M": M, "K": K, "N": N, "weight_format": "i8",
+                       "launches_per_step": 4, "us_per_step": ms * 1e3 / steps,
+                       "regime": "launch-bound (a parity-sized layer)"},
+               roofline=dict(bound="mfma", kernel="gemm_i8_kernel",
+                             achieved=ops / (gemm_ms / 1e3) / 1e12, peak=INT8_PEAK_TOPS,
+                             unit="TOP/s", frac=ops / (gemm_ms / 1e3) / 1e12 / INT8_PEAK_TOPS,
+                             traffic=None, avg_launch_us=gemm_ms * 1e3, alg_ops_per_launch=ops))
+    if not args.no_cpu_baseline:
+        import oracle
+        n = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            wq_r, b_r = oracle.quant_weight_absmean(W)
+            xq_r, s_r = oracle.quant_act(x)
+            oracle.epilogue(oracle.matmul_i32(xq_r, wq_r), s_r, b_r)
+            n += 1
+        secs = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(value=ops * n / secs / 1e12, unit="TOP/s",
+                                   cores=oracle.num_threads(), kind="oracle",
+                                   sample="%d whole steps (weight quant + act quant + matmul + "
+                                          "rescale) in %.1f s" % (n, secs))
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -355,10 +576,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     ug.lib()
-    runners = {"decode_stack": run_decode_stack, "prefill": run_prefill, "sweep": run_sweep}
-    if args.workload not in runners:
-        print("workload %s not implemented yet" % args.workload, file=sys.stderr)
-        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(torch)
+    runners = {"decode_stack": run_decode_stack, "prefill": run_prefill, "sweep": run_sweep,
+               "stack": run_stack, "tiny": run_tiny}
     res = runners[args.workload](args, torch, ug, inputs)
     line = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
             "steps": res["steps"], "warmup": res["warmup"], "ms_per_step": res["ms_per_step"],
