@@ -372,7 +372,7 @@ def run_prefill(args, torch, ug, inputs):
                config={"workload": "prefill", "M": M, "shapes_KxN": [[l["K"], l["N"]]
                                                                      for l in layers],
                        "weight_format": "i8"},
-               roofline=dict(bound="mfma", kernel="gemm_i8_kernel", achieved=achieved,
+               roofline=dict(bound="mfma", kernel="gemm_i8_large", achieved=achieved,
                              peak=INT8_PEAK_TOPS, unit="TOP/s", frac=achieved / INT8_PEAK_TOPS,
                              traffic=traffic_for("prefill"), avg_launch_us=gemm_ms * 1e3,
                              alg_ops_per_launch=ops_per_step / 2))
@@ -476,7 +476,7 @@ def run_stack(args, torch, ug, inputs):
                        "chain_ms_per_step": t_chain / steps,
                        "gemm_us_per_launch": gemm_ms * 1e3,
                        "act_quant_alg_bytes_per_step": act_bytes},
-               roofline=dict(bound="mfma", kernel="gemm_i8_kernel", achieved=achieved,
+               roofline=dict(bound="mfma", kernel="gemm_i8_large", achieved=achieved,
                              peak=INT8_PEAK_TOPS, unit="TOP/s", frac=achieved / INT8_PEAK_TOPS,
                              traffic=traffic_for("stack"), avg_launch_us=gemm_ms * 1e3,
                              alg_ops_per_launch=ops_per_step / len(mats)))

@@ -133,11 +133,283 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large GEMM on v_mfma_i32_32x32x32_i8 (the 16x16x64 form issues at half the
+// int8 rate on gfx950).  Lane l of that MFMA holds A row l%32 and B column
+// l%32 at K bytes [16 (l/32), +16), and accumulator element i of lane l is
+// D[8 (i/4) + 4 (l/32) + i%4][l%32].
+//
+// 256 x 256 output tile per 256-thread block, 2 x 2 waves of 128 x 128
+// (4 x 4 MFMA tiles, 256 int32 accumulators per lane, held in AGPRs; one
+// wave per SIMD).  K step 64.  LDS holds each operand tile fragment-native:
+// the 32 rows x 32 K bytes that one MFMA reads are one 1 KB block in which
+// lane l's 16 bytes sit at 16 l, so every fragment read is one contiguous,
+// conflict-free ds_read_b128.  Global loads are coalesced (a wave reads 16
+// rows x 64 bytes) into registers two steps ahead, and written to the other
+// LDS stage after this step's MFMAs; one barrier per step.  Buffer loads:
+// rows past M or N read zeros; activation bytes past K are masked (weight
+// bytes past K then multiply zeros).  Blocks are mapped to tiles so that the
+// blocks one XCD runs together cover a compact rectangle of tiles.
+constexpr int LBM = 256, LBN = 256, LBK = 64;
+constexpr int LTHREADS = 256;
+constexpr int LTILE = LBM * LBK;  // bytes of one operand tile per stage
+constexpr int kXcds = 8;          // blocks are dealt to the XCDs round-robin
+constexpr int kGroupM = 4;        // tile rows per group of the tile order
+
+typedef int v4i_ __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Zero the bytes of a 16-byte piece at K positions >= K (k0 = its first).
+__device__ __forceinline__ uint4 mask_k(uint4 v, int k0, int K) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int kb = K - k0 - 4 * e;  // bytes of this dword inside the row
+    w[e] &= kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb))));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(LTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__restrict__ s,
+                   const int8_t *__restrict__ w, int64_t ldw, const float *__restrict__ beta, int M,
+                   int N, int K, int32_t *__restrict__ acc, int64_t ldacc, float *__restrict__ y,
+                   int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) int8_t As[2][LTILE];
+  __shared__ __attribute__((aligned(16))) int8_t Bs[2][LTILE];
+  __shared__ float scale[LBM];
+
+  // tile of this block: XCD x takes tiles [x * per, (x + 1) * per) of the
+  // grouped order (kGroupM tile rows, then along N)
+  const int nbm = (M + LBM - 1) / LBM, nbn = (N + LBN - 1) / LBN, T = nbm * nbn;
+  const int per = (T + kXcds - 1) / kXcds;
+  const int t = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (t >= T) return;
+  const int group = t / (kGroupM * nbn), first_m = group * kGroupM;
+  const int gm = min(kGroupM, nbm - first_m), r = t - group * kGroupM * nbn;
+  const int tm = (first_m + r % gm) * LBM, tn = (r / gm) * LBN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;  // 2 x 2 waves
+  const __amdgpu_buffer_rsrc_t ar = rsrc(xq, (int64_t)M * ldx);
+  const __amdgpu_buffer_rsrc_t br = rsrc(w, (int64_t)N * ldw);
+  {
+    const int m = tm + tid;
+    scale[tid] = m < M ? s[m] * beta[0] : 0.0f;
+  }
+
+  // global -> LDS: 1024 pieces of 16 B per operand and step, 4 per thread.
+  // Load i of wave w covers rows 16 (4 i + w) + [0, 16) x 64 bytes; lane l
+  // takes row (l & 7) + 8 (l >> 5), chunk (l >> 3) & 3, so that every 8
+  // consecutive lanes write 8 consecutive 16-byte slots of the
+  // fragment-native layout (conflict-free ds_write_b128).
+  uint32_t aoff[4], boff[4];
+  int lds[4], pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * (4 * i + wid) + (lane & 7) + 8 * (lane >> 5), ch = (lane >> 3) & 3;
+    pk[i] = 16 * ch;
+    aoff[i] = tm + row < M ? (uint32_t)((tm + row) * ldx + 16 * ch) : 0x80000000u;
+    boff[i] = tn + row < N ? (uint32_t)((tn + row) * ldw + 16 * ch) : 0x80000000u;
+    // block (row group, K half) of 1 KB, then slot (K half of the MFMA, row)
+    lds[i] = (((row >> 5) * 2 + (ch >> 1)) * 64 + (ch & 1) * 32 + (row & 31)) * 16;
+  }
+  const int nk = (K + LBK - 1) / LBK;
+  auto load = [&](int k, uint4(&a)[4], uint4(&b)[4]) {
+    const int k0 = k * LBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = bload16(ar, aoff[i] + k0);
+      b[i] = bload16(br, boff[i] + k0);
+    }
+  };
+  // activation bytes past K are zeroed here, when the step's loads are used
+  auto store = [&](int k, int8_t *A, int8_t *B, const uint4(&a)[4], const uint4(&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4 *>(A + lds[i]) = mask_k(a[i], k * LBK + pk[i], K);
+      *reinterpret_cast<uint4 *>(B + lds[i]) = b[i];
+    }
+  };
+
+  v16i c[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) c[i][j][e] = 0;
+
+  // Fragments of K half h of the step in `stage`.
+  auto frags = [&](const int8_t *A, const int8_t *B, int h, v4i_(&a)[4], v4i_(&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const v4i_ *>(A + ((wm * 4 + i) * 2 + h) * 1024 + 16 * lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const v4i_ *>(B + ((wn * 4 + j) * 2 + h) * 1024 + 16 * lane);
+  };
+  auto mfmas = [&](const v4i_(&a)[4], const v4i_(&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], c[i][j], 0, 0, 0);
+  };
+
+  // Step k (its data in LDS stage A/B, its half-0 fragments a0/b0 already in
+  // registers).  Three register buffers rotate: the one holding step k+1 is
+  // written to the other LDS stage and then reloaded with step k+4, so each
+  // global load has three steps to arrive.
+  //   half 0: 16 MFMAs, interleaved with writing step k+1 into the other
+  //           stage (read last in step k-1) and reading the half-1 fragments;
+  //   half 1: 16 MFMAs, interleaved with the loads of step k+4;
+  //   barrier, then the half-0 fragments of step k+1.
+  // Loads and stores for steps past the last one are harmless (they read
+  // zeros or other rows, and fill a stage nobody reads), so the steps carry
+  // no conditions.
+  v4i_ a0[4], b0[4], a1[4], b1[4];
+  auto step = [&](int k, const int8_t *A, const int8_t *B, int8_t *An, int8_t *Bn, uint4(&ra)[4],
+                  uint4(&rb)[4]) {
+    mfmas(a0, b0);
+    store(k + 1, An, Bn, ra, rb);
+    frags(A, B, 1, a1, b1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    load(k + 4, ra, rb);
+    mfmas(a1, b1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+    __syncthreads();
+    frags(An, Bn, 0, a0, b0);
+  };
+
+  uint4 ra0[4], rb0[4], ra1[4], rb1[4], ra2[4], rb2[4];
+  load(0, ra0, rb0);
+  load(1, ra1, rb1);
+  load(2, ra2, rb2);
+  store(0, As[0], Bs[0], ra0, rb0);
+  load(3, ra0, rb0);
+  __syncthreads();
+  frags(As[0], Bs[0], 0, a0, b0);
+  int8_t *A = As[0], *B = Bs[0], *An = As[1], *Bn = Bs[1];
+  auto swap = [&]() {
+    int8_t *t0 = A, *t1 = B;
+    A = An;
+    B = Bn;
+    An = t0;
+    Bn = t1;
+  };
+  int k = 0;
+  for (; k + 3 <= nk; k += 3) {  // whole triples: the same loads in flight at every entry
+    step(k, A, B, An, Bn, ra1, rb1);  // step k+1 is in buffer (k+1) % 3 == 1
+    swap();
+    step(k + 1, A, B, An, Bn, ra2, rb2);
+    swap();
+    step(k + 2, A, B, An, Bn, ra0, rb0);
+    swap();
+  }
+  if (k < nk) {
+    step(k, A, B, An, Bn, ra1, rb1);
+    swap();
+    if (k + 1 < nk) step(k + 1, A, B, An, Bn, ra2, rb2);
+  }
+
+  // Epilogue.  Element e of lane l in tile (i, j) is row 8 (e/4) + 4 (l/32)
+  // + e%4, column l%32.  Each 32 x 32 tile goes through a per-wave 32 x 36
+  // LDS buffer, so that each lane stores 16-byte pieces of rows (a wave keeps
+  // at most 63 memory operations in flight: 4-byte stores would leave the
+  // epilogue waiting on write latency), with a compact per-tile body (this
+  // code runs once per block, from a cold instruction cache).
+  __syncthreads();  // every wave is done with the LDS stages
+  float *tb = reinterpret_cast<float *>(&As[0][0]) + wid * (32 * 36);
+  int *tbi = reinterpret_cast<int *>(tb);
+  auto put = [&](int r0, int c0, const float4 &v, bool is_acc) {
+    // lane's 4 values: row r0, columns c0..c0+3 (block-relative)
+    const int m = tm + r0, n = tn + c0;
+    if (m >= M) return;
+    if (n + 3 < N) {
+      if (is_acc)
+        *reinterpret_cast<int4 *>(&acc[(int64_t)m * ldacc + n]) = __builtin_bit_cast(int4, v);
+      else
+        *reinterpret_cast<float4 *>(&y[(int64_t)m * ldy + n]) = v;
+    } else {
+      const float f[4] = {v.x, v.y, v.z, v.w};
+      for (int t = 0; t < 4 && n + t < N; ++t) {
+        if (is_acc)
+          acc[(int64_t)m * ldacc + n + t] = __builtin_bit_cast(int, f[t]);
+        else
+          y[(int64_t)m * ldy + n + t] = f[t];
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r0 = wm * 128 + 32 * i;  // first row of the tile row (block-relative)
+    float sc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = scale[r0 + 4 * (lane >> 5) + 8 * (e >> 2) + (e & 3)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c0 = wn * 128 + 32 * j;
+      if (y) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          tb[(4 * (lane >> 5) + 8 * (e >> 2) + (e & 3)) * 36 + (lane & 31)] = (float)c[i][j][e] * sc[e];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = (lane >> 3) + 8 * q;
+          put(r0 + rr, c0 + 4 * (lane & 7), *reinterpret_cast<const float4 *>(&tb[rr * 36 + 4 * (lane & 7)]), false);
+        }
+      }
+      if (acc) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          tbi[(4 * (lane >> 5) + 8 * (e >> 2) + (e & 3)) * 36 + (lane & 31)] = c[i][j][e];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = (lane >> 3) + 8 * q;
+          put(r0 + rr, c0 + 4 * (lane & 7), *reinterpret_cast<const float4 *>(&tb[rr * 36 + 4 * (lane & 7)]), true);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const int8_t *w,
                           int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
                           int32_t *acc, int64_t ldacc, float *y, int64_t ldy, hipStream_t st) {
+  // the large tiles pay off once there are enough of them; they address
+  // the operands with 32-bit buffer offsets
+  if (M >= 512 && N >= 512 && M * ldx < (INT64_C(1) << 31) && N * ldw < (INT64_C(1) << 31) &&
+      M <= INT32_MAX && N <= INT32_MAX) {
+    const int64_t T = ceil_div(M, LBM) * ceil_div(N, LBN);
+    const int64_t blocks = ceil_div(T, kXcds) * kXcds;
+    hipLaunchKernelGGL(gemm_i8_large, dim3((unsigned)blocks), dim3(LTHREADS), 0, st, xq, ldx, s,
+                       w, ldw, beta, (int)M, (int)N, (int)K, acc, ldacc, y, ldy);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(M, BM));
   hipLaunchKernelGGL(gemm_i8_kernel, grid, dim3(256), 0, st, xq, ldx, s, w, ldw, beta, M, N, K,
                      acc, ldacc, y, ldy);

@@ -240,8 +240,11 @@ def test_gemv_invalid_codes_and_garbage_pad(dev):
         assert_bits_equal(host(y_d)[:, keep], y_r[:, keep], "y")
 
 
+# the last four use the 256 x 256-tile kernel (M, N >= 512), with ragged M, N
+# and K edges and the XCD tile order over a grid that is not a multiple of 8
 GEMM_CASES = [(1, 64, 64), (33, 129, 100), (128, 512, 128), (300, 64, 2560), (257, 1000, 1536),
-              (512, 6912, 2560), (200, 2560, 6912)]
+              (200, 2560, 6912), (512, 6912, 2560), (600, 700, 197), (1100, 1300, 1000),
+              (2048, 2560, 6912)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
