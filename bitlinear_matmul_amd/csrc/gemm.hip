@@ -141,15 +141,31 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
 //
 // 256 x 256 output tile per 256-thread block, 2 x 2 waves of 128 x 128
 // (4 x 4 MFMA tiles, 256 int32 accumulators per lane, held in AGPRs; one
-// wave per SIMD).  K step 64.  LDS holds each operand tile fragment-native:
-// the 32 rows x 32 K bytes that one MFMA reads are one 1 KB block in which
-// lane l's 16 bytes sit at 16 l, so every fragment read is one contiguous,
-// conflict-free ds_read_b128.  Global loads are coalesced (a wave reads 16
-// rows x 64 bytes) into registers two steps ahead, and written to the other
-// LDS stage after this step's MFMAs; one barrier per step.  Buffer loads:
-// rows past M or N read zeros; activation bytes past K are masked (weight
-// bytes past K then multiply zeros).  Blocks are mapped to tiles so that the
-// blocks one XCD runs together cover a compact rectangle of tiles.
+// wave per SIMD).  K step 64, four LDS stages per operand.
+//
+// Operands go from global memory straight into LDS (buffer loads with the
+// LDS destination bit), so no register staging and no LDS store
+// instructions.  One such load moves 1 KB: lane l's 16 bytes land at 16 l.
+// A stage holds 256 rows x 64 bytes; within row r the 16-byte chunk x sits at
+// slot x ^ ((r >> 2) & 3), which makes every MFMA fragment read a
+// conflict-free ds_read_b128 (16 consecutive lanes cover all 64 banks) while
+// each load still fetches whole 64-byte row pieces.
+//
+// Step k: MFMAs of its first K half run while the second half's fragments
+// are read; then each wave waits for its own loads of step k+1, one barrier
+// makes them visible block-wide (and frees the stage read in step k-1), the
+// loads of step k+3 are issued into that stage, and the second-half MFMAs run
+// while the first-half fragments of step k+1 are read.  Loads therefore have
+// two steps to arrive.  Past the last step the loads repeat the last step's
+// data into stages nobody reads again, so every step issues the same number
+// of loads and the wait counts stay exact.
+//
+// Edges: buffer loads of rows past M or N return zeros (or leave old data:
+// either way only rows and columns that are never stored see it).  In the
+// last step the activation bytes past K are zeroed in LDS before use, so
+// whatever the weight rows hold there multiplies zeros.  Blocks are mapped to
+// tiles so that the blocks one XCD runs together cover a compact rectangle
+// of tiles.
 constexpr int LBM = 256, LBN = 256, LBK = 64;
 constexpr int LTHREADS = 256;
 constexpr int LTILE = LBM * LBK;  // bytes of one operand tile per stage
@@ -158,14 +174,26 @@ constexpr int kGroupM = 4;        // tile rows per group of the tile order
 
 typedef int v4i_ __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+// Workgroup barrier that orders the compiler's memory operations but adds no
+// waits of its own: the waits that make LDS data visible are explicit.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Zero the bytes of a 16-byte piece at K positions >= K (k0 = its first).
 __device__ __forceinline__ uint4 mask_k(uint4 v, int k0, int K) {
@@ -183,8 +211,10 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
                    const int8_t *__restrict__ w, int64_t ldw, const float *__restrict__ beta, int M,
                    int N, int K, int32_t *__restrict__ acc, int64_t ldacc, float *__restrict__ y,
                    int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) int8_t As[2][LTILE];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][LTILE];
+  // four stages per operand, as separate arrays so that the compiler can
+  // tell a load into one stage from reads of another
+  __shared__ __attribute__((aligned(1024))) int8_t A0[LTILE], A1[LTILE], A2[LTILE], A3[LTILE];
+  __shared__ __attribute__((aligned(1024))) int8_t B0[LTILE], B1[LTILE], B2[LTILE], B3[LTILE];
   __shared__ float scale[LBM];
 
   // tile of this block: XCD x takes tiles [x * per, (x + 1) * per) of the
@@ -206,37 +236,37 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
     scale[tid] = m < M ? s[m] * beta[0] : 0.0f;
   }
 
-  // global -> LDS: 1024 pieces of 16 B per operand and step, 4 per thread.
-  // Load i of wave w covers rows 16 (4 i + w) + [0, 16) x 64 bytes; lane l
-  // takes row (l & 7) + 8 (l >> 5), chunk (l >> 3) & 3, so that every 8
-  // consecutive lanes write 8 consecutive 16-byte slots of the
-  // fragment-native layout (conflict-free ds_write_b128).
+  // Loads: 16 per operand and step, 4 per wave; load j fills rows
+  // 16 j + [0, 16) of the stage.  Lane l lands at row 16 j + l/4, slot l%4,
+  // so it fetches chunk (l%4) ^ ((l/16)%4) of that row.
   uint32_t aoff[4], boff[4];
-  int lds[4], pk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = 16 * (4 * i + wid) + (lane & 7) + 8 * (lane >> 5), ch = (lane >> 3) & 3;
-    pk[i] = 16 * ch;
-    aoff[i] = tm + row < M ? (uint32_t)((tm + row) * ldx + 16 * ch) : 0x80000000u;
-    boff[i] = tn + row < N ? (uint32_t)((tn + row) * ldw + 16 * ch) : 0x80000000u;
-    // block (row group, K half) of 1 KB, then slot (K half of the MFMA, row)
-    lds[i] = (((row >> 5) * 2 + (ch >> 1)) * 64 + (ch & 1) * 32 + (row & 31)) * 16;
+    const int row = 16 * (4 * wid + i) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    aoff[i] = tm + row < M ? (uint32_t)((tm + row) * ldx + 16 * chunk) : 0x80000000u;
+    boff[i] = tn + row < N ? (uint32_t)((tn + row) * ldw + 16 * chunk) : 0x80000000u;
   }
   const int nk = (K + LBK - 1) / LBK;
-  auto load = [&](int k, uint4(&a)[4], uint4(&b)[4]) {
-    const int k0 = k * LBK;
+  const int kv = K - (nk - 1) * LBK;  // valid K bytes of the last step, 1..64
+  auto load = [&](int k, int8_t *As, int8_t *Bs) {
+    const uint32_t k0 = (uint32_t)min(k, nk - 1) * LBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      a[i] = bload16(ar, aoff[i] + k0);
-      b[i] = bload16(br, boff[i] + k0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)(As + (4 * wid + i) * 1024), 16,
+                                               aoff[i] + k0, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(Bs + (4 * wid + i) * 1024), 16,
+                                               boff[i] + k0, 0, 0, 0);
     }
   };
-  // activation bytes past K are zeroed here, when the step's loads are used
-  auto store = [&](int k, int8_t *A, int8_t *B, const uint4(&a)[4], const uint4(&b)[4]) {
+  // zero the activation bytes at step positions >= kv (one row per thread)
+  auto fix_tail = [&](int8_t *As) {
+    const int sw = (tid >> 2) & 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4 *>(A + lds[i]) = mask_k(a[i], k * LBK + pk[i], K);
-      *reinterpret_cast<uint4 *>(B + lds[i]) = b[i];
+    for (int x = 0; x < 4; ++x) {
+      if (16 * x + 16 <= kv) continue;
+      uint4 *p = reinterpret_cast<uint4 *>(As + tid * 64 + 16 * (x ^ sw));
+      *p = mask_k(*p, 16 * x, kv);
     }
   };
 
@@ -248,14 +278,20 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
 #pragma unroll
       for (int e = 0; e < 16; ++e) c[i][j][e] = 0;
 
-  // Fragments of K half h of the step in `stage`.
-  auto frags = [&](const int8_t *A, const int8_t *B, int h, v4i_(&a)[4], v4i_(&b)[4]) {
+  // Fragment addresses: tile i of K half h of a stage is at row
+  // 32 i + (l & 31), chunk 2 h + (l >> 5), in its swizzled slot.
+  int fa[2], fb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const v4i_ *>(A + ((wm * 4 + i) * 2 + h) * 1024 + 16 * lane);
+  for (int h = 0; h < 2; ++h) {
+    const int slot = 16 * ((2 * h + (lane >> 5)) ^ ((lane >> 2) & 3));
+    fa[h] = (wm * 128 + (lane & 31)) * 64 + slot;
+    fb[h] = (wn * 128 + (lane & 31)) * 64 + slot;
+  }
+  auto frags = [&](const int8_t *As, const int8_t *Bs, int h, v4i_(&a)[4], v4i_(&b)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const v4i_ *>(B + ((wn * 4 + j) * 2 + h) * 1024 + 16 * lane);
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v4i_ *>(As + fa[h] + 2048 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const v4i_ *>(Bs + fb[h] + 2048 * j);
   };
   auto mfmas = [&](const v4i_(&a)[4], const v4i_(&b)[4]) {
 #pragma unroll
@@ -265,74 +301,61 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
         c[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], c[i][j], 0, 0, 0);
   };
 
-  // Step k (its data in LDS stage A/B, its half-0 fragments a0/b0 already in
-  // registers).  Three register buffers rotate: the one holding step k+1 is
-  // written to the other LDS stage and then reloaded with step k+4, so each
-  // global load has three steps to arrive.
-  //   half 0: 16 MFMAs, interleaved with writing step k+1 into the other
-  //           stage (read last in step k-1) and reading the half-1 fragments;
-  //   half 1: 16 MFMAs, interleaved with the loads of step k+4;
-  //   barrier, then the half-0 fragments of step k+1.
-  // Loads and stores for steps past the last one are harmless (they read
-  // zeros or other rows, and fill a stage nobody reads), so the steps carry
-  // no conditions.
   v4i_ a0[4], b0[4], a1[4], b1[4];
-  auto step = [&](int k, const int8_t *A, const int8_t *B, int8_t *An, int8_t *Bn, uint4(&ra)[4],
-                  uint4(&rb)[4]) {
+  // step k reads stage (A, B); step k+1 is in (An, Bn); step k+3 goes to (Ad, Bd)
+  auto step = [&](int k, const int8_t *Ac, const int8_t *Bc, int8_t *An, int8_t *Bn, int8_t *Ad,
+                  int8_t *Bd) {
     mfmas(a0, b0);
-    store(k + 1, An, Bn, ra, rb);
-    frags(A, B, 1, a1, b1);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-    }
+    frags(Ac, Bc, 1, a1, b1);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
-    load(k + 4, ra, rb);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    wait_vmcnt<8>();  // this wave's loads of step k+1 (those of k+2 may be in flight)
+    block_barrier();
+    if (k + 1 == nk - 1 && kv < LBK) {
+      fix_tail(An);
+      wait_lgkmcnt0();
+      block_barrier();
+    }
+    load(k + 3, Ad, Bd);
     mfmas(a1, b1);
+    frags(An, Bn, 0, a0, b0);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
-    __syncthreads();
-    frags(An, Bn, 0, a0, b0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (LDS-destination loads)
+    }
   };
 
-  uint4 ra0[4], rb0[4], ra1[4], rb1[4], ra2[4], rb2[4];
-  load(0, ra0, rb0);
-  load(1, ra1, rb1);
-  load(2, ra2, rb2);
-  store(0, As[0], Bs[0], ra0, rb0);
-  load(3, ra0, rb0);
-  __syncthreads();
-  frags(As[0], Bs[0], 0, a0, b0);
-  int8_t *A = As[0], *B = Bs[0], *An = As[1], *Bn = Bs[1];
-  auto swap = [&]() {
-    int8_t *t0 = A, *t1 = B;
-    A = An;
-    B = Bn;
-    An = t0;
-    Bn = t1;
-  };
+  load(0, A0, B0);
+  load(1, A1, B1);
+  load(2, A2, B2);
+  wait_vmcnt<16>();
+  block_barrier();
+  if (nk == 1 && kv < LBK) {
+    fix_tail(A0);
+    wait_lgkmcnt0();
+    block_barrier();
+  }
+  frags(A0, B0, 0, a0, b0);
   int k = 0;
-  for (; k + 3 <= nk; k += 3) {  // whole triples: the same loads in flight at every entry
-    step(k, A, B, An, Bn, ra1, rb1);  // step k+1 is in buffer (k+1) % 3 == 1
-    swap();
-    step(k + 1, A, B, An, Bn, ra2, rb2);
-    swap();
-    step(k + 2, A, B, An, Bn, ra0, rb0);
-    swap();
+  for (; k + 4 <= nk; k += 4) {
+    step(k, A0, B0, A1, B1, A3, B3);
+    step(k + 1, A1, B1, A2, B2, A0, B0);
+    step(k + 2, A2, B2, A3, B3, A1, B1);
+    step(k + 3, A3, B3, A0, B0, A2, B2);
   }
-  if (k < nk) {
-    step(k, A, B, An, Bn, ra1, rb1);
-    swap();
-    if (k + 1 < nk) step(k + 1, A, B, An, Bn, ra2, rb2);
-  }
+  if (k < nk) step(k, A0, B0, A1, B1, A3, B3);
+  if (k + 1 < nk) step(k + 1, A1, B1, A2, B2, A0, B0);
+  if (k + 2 < nk) step(k + 2, A2, B2, A3, B3, A1, B1);
 
   // Epilogue.  Element e of lane l in tile (i, j) is row 8 (e/4) + 4 (l/32)
   // + e%4, column l%32.  Each 32 x 32 tile goes through a per-wave 32 x 36
@@ -340,8 +363,10 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
   // at most 63 memory operations in flight: 4-byte stores would leave the
   // epilogue waiting on write latency), with a compact per-tile body (this
   // code runs once per block, from a cold instruction cache).
-  __syncthreads();  // every wave is done with the LDS stages
-  float *tb = reinterpret_cast<float *>(&As[0][0]) + wid * (32 * 36);
+  wait_vmcnt<0>();  // the trailing loads into unused stages have landed
+  wait_lgkmcnt0();
+  block_barrier();  // and every wave is done with the stages
+  float *tb = reinterpret_cast<float *>(wid == 0 ? A0 : wid == 1 ? A1 : wid == 2 ? A2 : A3);
   int *tbi = reinterpret_cast<int *>(tb);
   auto put = [&](int r0, int c0, const float4 &v, bool is_acc) {
     // lane's 4 values: row r0, columns c0..c0+3 (block-relative)
