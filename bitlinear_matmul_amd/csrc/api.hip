@@ -238,9 +238,9 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *i
 }
 
 size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t wfmt) {
-  (void)M;
-  if (N < 1 || K < 1 || wfmt != UG_W_PACK5) return 0;
-  return (size_t)(N * ug::round_up(K, 16));
+  if (M < 1 || N < 1 || K < 1 || (wfmt != UG_W_I8 && wfmt != UG_W_PACK5)) return 0;
+  const size_t dec = wfmt == UG_W_PACK5 ? (size_t)(N * ug::round_up(K, 16)) : 0;
+  return ug::gemm_split_bytes(M, N, K) + dec;
 }
 
 ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const void *w,
@@ -250,18 +250,29 @@ ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const
   ug_status st = check_matmul(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy);
   if (st != UG_OK) return st;
   hipStream_t hs = as_stream(stream);
+  const size_t dec = wfmt == UG_W_PACK5 ? (size_t)(N * ug::round_up(K, 16)) : 0;
+  if (ws != nullptr && !aligned16(ws)) return UG_ERR_WORKSPACE;
+  if (wfmt == UG_W_PACK5 && (ws == nullptr || ws_bytes < dec)) return UG_ERR_WORKSPACE;
+  // With room for both, the work-split area sits at the start of the
+  // workspace and the decoded weights follow it; otherwise the decoded
+  // weights start the workspace and every block computes whole tiles.
+  void *split = nullptr;
+  size_t dec_off = 0;
+  const size_t split_bytes = ug::gemm_split_bytes(M, N, K);
+  if (split_bytes != 0 && ws != nullptr && ws_bytes >= split_bytes + dec) {
+    split = ws;
+    dec_off = split_bytes;
+  }
   if (wfmt == UG_W_PACK5) {
-    const size_t need = ug_bitlinear_gemm_workspace_size(M, N, K, wfmt);
-    if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return UG_ERR_WORKSPACE;
     const int64_t ldu = ug::round_up(K, 16);
-    int8_t *wu = (int8_t *)ws;
+    int8_t *wu = static_cast<int8_t *>(ws) + dec_off;
     hipError_t e = ug::launch_unpack((const uint8_t *)w, ldw, N, K, wu, ldu, nullptr, hs);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(
-        ug::launch_gemm_i8(xq, ldx, s, wu, ldu, beta, M, N, K, acc, ldacc, y, ldy, hs));
+    return hip_status(ug::launch_gemm_i8(xq, ldx, s, wu, ldu, beta, M, N, K, acc, ldacc, y, ldy,
+                                         split, hs));
   }
   return hip_status(ug::launch_gemm_i8(xq, ldx, s, (const int8_t *)w, ldw, beta, M, N, K, acc,
-                                       ldacc, y, ldy, hs));
+                                       ldacc, y, ldy, split, hs));
 }
 
 }  // extern "C"

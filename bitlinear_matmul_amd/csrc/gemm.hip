@@ -17,6 +17,9 @@
 // the current one run.
 #include "ug_internal.h"
 
+#include <cstdlib>
+#include <type_traits>
+
 namespace ug {
 namespace {
 
@@ -206,61 +209,85 @@ __device__ __forceinline__ uint4 mask_k(uint4 v, int k0, int K) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Work split.  The T output tiles are ordered (kGroupM tile rows, then along
+// N) and each one's nk K steps are cut into S equal-as-possible ranges:
+// block v (after the XCD remap below) computes split s = v / T of tile
+// t = v % T.  Splitting by whole K ranges keeps the blocks that run at the
+// same time on the same K steps of neighbouring tiles, so they keep sharing
+// operand rows in L2.  With S = 1 each block computes a whole tile; with
+// S > 1 a tile's blocks leave int32 partial tiles in the workspace, bump the
+// tile's counter, and move on, so no block ever waits for another.  The last
+// one in adds the partials (integer sums: exact in any order), writes the
+// tile, and sets the counter back to zero, which leaves the workspace ready
+// for the next call.
+constexpr int kTileInts = LBM * LBN;  // int32 entries of a partial tile
+
 __global__ __launch_bounds__(LTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__restrict__ s,
                    const int8_t *__restrict__ w, int64_t ldw, const float *__restrict__ beta, int M,
                    int N, int K, int32_t *__restrict__ acc, int64_t ldacc, float *__restrict__ y,
-                   int64_t ldy) {
+                   int64_t ldy, int S, int32_t *__restrict__ part, int *__restrict__ cnt) {
   // four stages per operand, as separate arrays so that the compiler can
   // tell a load into one stage from reads of another
   __shared__ __attribute__((aligned(1024))) int8_t A0[LTILE], A1[LTILE], A2[LTILE], A3[LTILE];
   __shared__ __attribute__((aligned(1024))) int8_t B0[LTILE], B1[LTILE], B2[LTILE], B3[LTILE];
   __shared__ float scale[LBM];
+  __shared__ int last_flag;
 
-  // tile of this block: XCD x takes tiles [x * per, (x + 1) * per) of the
-  // grouped order (kGroupM tile rows, then along N)
   const int nbm = (M + LBM - 1) / LBM, nbn = (N + LBN - 1) / LBN, T = nbm * nbn;
-  const int per = (T + kXcds - 1) / kXcds;
-  const int t = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
-  if (t >= T) return;
-  const int group = t / (kGroupM * nbn), first_m = group * kGroupM;
-  const int gm = min(kGroupM, nbm - first_m), r = t - group * kGroupM * nbn;
-  const int tm = (first_m + r % gm) * LBM, tn = (r / gm) * LBN;
+  const int nk = (K + LBK - 1) / LBK;
+  const int kv = K - (nk - 1) * LBK;  // valid K bytes of the last step, 1..64
+  // XCD x runs blocks x, x + 8, ...: give it the contiguous share
+  // [x per, (x + 1) per) of the work, so that its L2 sees neighbouring tiles
+  const int per = (int)(gridDim.x / kXcds);
+  const int vb = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (vb >= T * S) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;  // 2 x 2 waves
+  // Thread coordinates, re-read through an empty asm at the top of every
+  // segment: the compiler then cannot hoist the many addresses derived from
+  // them out of the segment loop, where they would stay live (and spill)
+  // across both the K loop and the output pass.
+  int tid, lane, wid, wm, wn;  // wid, wm, wn wave-uniform; 2 x 2 waves
+  auto refresh = [&]() __attribute__((always_inline)) {
+    int t_ = (int)threadIdx.x;
+    asm volatile("" : "+v"(t_));
+    tid = t_;
+    lane = t_ & 63;
+    const int w_ = __builtin_amdgcn_readfirstlane(t_ >> 6);
+    wid = w_;
+    wm = w_ >> 1;
+    wn = w_ & 1;
+  };
   const __amdgpu_buffer_rsrc_t ar = rsrc(xq, (int64_t)M * ldx);
   const __amdgpu_buffer_rsrc_t br = rsrc(w, (int64_t)N * ldw);
-  {
-    const int m = tm + tid;
-    scale[tid] = m < M ? s[m] * beta[0] : 0.0f;
-  }
+  const float bs = beta[0];
 
   // Loads: 16 per operand and step, 4 per wave; load j fills rows
   // 16 j + [0, 16) of the stage.  Lane l lands at row 16 j + l/4, slot l%4,
   // so it fetches chunk (l%4) ^ ((l/16)%4) of that row.
   uint32_t aoff[4], boff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * (4 * wid + i) + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-    aoff[i] = tm + row < M ? (uint32_t)((tm + row) * ldx + 16 * chunk) : 0x80000000u;
-    boff[i] = tn + row < N ? (uint32_t)((tn + row) * ldw + 16 * chunk) : 0x80000000u;
-  }
-  const int nk = (K + LBK - 1) / LBK;
-  const int kv = K - (nk - 1) * LBK;  // valid K bytes of the last step, 1..64
-  auto load = [&](int k, int8_t *As, int8_t *Bs) {
-    const uint32_t k0 = (uint32_t)min(k, nk - 1) * LBK;
+  int kend = 0;  // loads clamp to the last step of the current segment
+  // This wave's 4 KB part of a stage, from an opaque copy of the thread
+  // index: a uniform value the compiler recomputes where it is used (one
+  // scalar add per load) instead of keeping 32 hoisted sums in registers.
+  auto wave_base = [&]() __attribute__((always_inline)) {
+    int t_ = (int)threadIdx.x;
+    asm volatile("" : "+v"(t_));
+    return __builtin_amdgcn_readfirstlane((t_ >> 6) * 4096);
+  };
+  auto load = [&](int k, int8_t *As, int8_t *Bs) __attribute__((always_inline)) {
+    const uint32_t k0 = (uint32_t)min(k, kend - 1) * LBK;
+    const int wb = wave_base();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)(As + (4 * wid + i) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)(As + wb + i * 1024), 16,
                                                aoff[i] + k0, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(Bs + (4 * wid + i) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(Bs + wb + i * 1024), 16,
                                                boff[i] + k0, 0, 0, 0);
     }
   };
   // zero the activation bytes at step positions >= kv (one row per thread)
-  auto fix_tail = [&](int8_t *As) {
+  auto fix_tail = [&](int8_t *As) __attribute__((always_inline)) {
     const int sw = (tid >> 2) & 3;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -271,48 +298,53 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
   };
 
   v16i c[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) c[i][j][e] = 0;
 
-  // Fragment addresses: tile i of K half h of a stage is at row
-  // 32 i + (l & 31), chunk 2 h + (l >> 5), in its swizzled slot.
-  int fa[2], fb[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int slot = 16 * ((2 * h + (lane >> 5)) ^ ((lane >> 2) & 3));
-    fa[h] = (wm * 128 + (lane & 31)) * 64 + slot;
-    fb[h] = (wn * 128 + (lane & 31)) * 64 + slot;
-  }
-  auto frags = [&](const int8_t *As, const int8_t *Bs, int h, v4i_(&a)[4], v4i_(&b)[4]) {
+  int fa[2], fb[2];  // fragment addresses (set per segment)
+  auto frags = [&](const int8_t *As, const int8_t *Bs, int h, v4i_(&a)[4], v4i_(&b)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v4i_ *>(As + fa[h] + 2048 * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const v4i_ *>(Bs + fb[h] + 2048 * j);
   };
-  auto mfmas = [&](const v4i_(&a)[4], const v4i_(&b)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        c[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], c[i][j], 0, 0, 0);
+
+  // The issue order inside a step is written out and pinned: MFMA g,
+  // then (for g < 8) fragment read g, or (g >= 8) load g-8.  The pins
+  // (scheduling barriers that only let plain ALU work move) keep the
+  // compiler from regrouping the reads behind the MFMAs that need them
+  // (mask: only non-matrix vector ALU and scalar ALU work may cross).
+  auto pin = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0x0006); };
+  auto mfma_g = [&](const v4i_(&a)[4], const v4i_(&b)[4], int g) __attribute__((always_inline)) {
+    c[g >> 2][g & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[g >> 2], b[g & 3], c[g >> 2][g & 3],
+                                                             0, 0, 0);
+  };
+  auto frag_g = [&](const int8_t *As, const int8_t *Bs, int h, v4i_(&a)[4], v4i_(&b)[4], int g) __attribute__((always_inline)) {
+    if (g < 4)
+      a[g] = *reinterpret_cast<const v4i_ *>(As + fa[h] + 2048 * g);
+    else
+      b[g - 4] = *reinterpret_cast<const v4i_ *>(Bs + fb[h] + 2048 * (g - 4));
+  };
+  auto load_g = [&](int k, int8_t *As, int8_t *Bs, int wb, int g) __attribute__((always_inline)) {
+    const uint32_t k0 = (uint32_t)min(k, kend - 1) * LBK;
+    const int i = g >> 1;
+    if (g & 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(Bs + wb + i * 1024), 16,
+                                               boff[i] + k0, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void *)(As + wb + i * 1024), 16,
+                                               aoff[i] + k0, 0, 0, 0);
   };
 
   v4i_ a0[4], b0[4], a1[4], b1[4];
-  // step k reads stage (A, B); step k+1 is in (An, Bn); step k+3 goes to (Ad, Bd)
+  // step k reads stage (Ac, Bc); step k+1 is in (An, Bn); step k+3 goes to (Ad, Bd)
   auto step = [&](int k, const int8_t *Ac, const int8_t *Bc, int8_t *An, int8_t *Bn, int8_t *Ad,
-                  int8_t *Bd) {
-    mfmas(a0, b0);
-    frags(Ac, Bc, 1, a1, b1);
+                  int8_t *Bd) __attribute__((always_inline)) {
+    pin();
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    for (int g = 0; g < 16; ++g) {
+      mfma_g(a0, b0, g);
+      if (g < 8) frag_g(Ac, Bc, 1, a1, b1, g);
+      pin();
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     wait_vmcnt<8>();  // this wave's loads of step k+1 (those of k+2 may be in flight)
     block_barrier();
     if (k + 1 == nk - 1 && kv < LBK) {
@@ -320,119 +352,333 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
       wait_lgkmcnt0();
       block_barrier();
     }
-    load(k + 3, Ad, Bd);
-    mfmas(a1, b1);
-    frags(An, Bn, 0, a0, b0);
+    const int wb = wave_base();
+    pin();
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (LDS-destination loads)
+    for (int g = 0; g < 16; ++g) {
+      mfma_g(a1, b1, g);
+      if (g < 8)
+        frag_g(An, Bn, 0, a0, b0, g);
+      else
+        load_g(k + 3, Ad, Bd, wb, g - 8);
+      pin();
     }
   };
 
-  load(0, A0, B0);
-  load(1, A1, B1);
-  load(2, A2, B2);
-  wait_vmcnt<16>();
-  block_barrier();
-  if (nk == 1 && kv < LBK) {
-    fix_tail(A0);
+  // Accumulate steps [ks, ke) of the tile at (tm, tn) into c.  The stages
+  // are free on entry (every wave has passed a barrier after its last LDS
+  // read of them).
+  auto mainloop = [&](int tm, int tn, int ks, int ke) __attribute__((always_inline)) {
+    // Load i of this wave: rows 16 (4 wid + i) + l/4, chunk (l%4) ^ ((l/16)%4).
+    const int lrow = 16 * 4 * wid + (lane >> 2), lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = lrow + 16 * i;
+      aoff[i] = tm + row < M ? (uint32_t)((tm + row) * ldx + 16 * lchunk) : 0x80000000u;
+      boff[i] = tn + row < N ? (uint32_t)((tn + row) * ldw + 16 * lchunk) : 0x80000000u;
+    }
+    kend = ke;
+    // Fragment addresses: tile i of K half h of a stage is at row
+    // 32 i + (l & 31), chunk 2 h + (l >> 5), in its swizzled slot.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int slot = 16 * ((2 * h + (lane >> 5)) ^ ((lane >> 2) & 3));
+      fa[h] = (wm * 128 + (lane & 31)) * 64 + slot;
+      fb[h] = (wn * 128 + (lane & 31)) * 64 + slot;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c[i][j][e] = 0;
+    load(ks, A0, B0);
+    load(ks + 1, A1, B1);
+    load(ks + 2, A2, B2);
+    wait_vmcnt<16>();
+    block_barrier();
+    if (ks == nk - 1 && kv < LBK) {
+      fix_tail(A0);
+      wait_lgkmcnt0();
+      block_barrier();
+    }
+    frags(A0, B0, 0, a0, b0);
+    int k = ks;
+    for (; k + 4 <= ke; k += 4) {
+      step(k, A0, B0, A1, B1, A3, B3);
+      step(k + 1, A1, B1, A2, B2, A0, B0);
+      step(k + 2, A2, B2, A3, B3, A1, B1);
+      step(k + 3, A3, B3, A0, B0, A2, B2);
+    }
+    if (k < ke) step(k, A0, B0, A1, B1, A3, B3);
+    if (k + 1 < ke) step(k + 1, A1, B1, A2, B2, A0, B0);
+    if (k + 2 < ke) step(k + 2, A2, B2, A3, B3, A1, B1);
+    // the trailing loads into unused stages have landed and every wave is
+    // done with the stages
+    wait_vmcnt<0>();
     wait_lgkmcnt0();
     block_barrier();
-  }
-  frags(A0, B0, 0, a0, b0);
-  int k = 0;
-  for (; k + 4 <= nk; k += 4) {
-    step(k, A0, B0, A1, B1, A3, B3);
-    step(k + 1, A1, B1, A2, B2, A0, B0);
-    step(k + 2, A2, B2, A3, B3, A1, B1);
-    step(k + 3, A3, B3, A0, B0, A2, B2);
-  }
-  if (k < nk) step(k, A0, B0, A1, B1, A3, B3);
-  if (k + 1 < nk) step(k + 1, A1, B1, A2, B2, A0, B0);
-  if (k + 2 < nk) step(k + 2, A2, B2, A3, B3, A1, B1);
-
-  // Epilogue.  Element e of lane l in tile (i, j) is row 8 (e/4) + 4 (l/32)
-  // + e%4, column l%32.  Each 32 x 32 tile goes through a per-wave 32 x 36
-  // LDS buffer, so that each lane stores 16-byte pieces of rows (a wave keeps
-  // at most 63 memory operations in flight: 4-byte stores would leave the
-  // epilogue waiting on write latency), with a compact per-tile body (this
-  // code runs once per block, from a cold instruction cache).
-  wait_vmcnt<0>();  // the trailing loads into unused stages have landed
-  wait_lgkmcnt0();
-  block_barrier();  // and every wave is done with the stages
-  float *tb = reinterpret_cast<float *>(wid == 0 ? A0 : wid == 1 ? A1 : wid == 2 ? A2 : A3);
-  int *tbi = reinterpret_cast<int *>(tb);
-  auto put = [&](int r0, int c0, const float4 &v, bool is_acc) {
-    // lane's 4 values: row r0, columns c0..c0+3 (block-relative)
-    const int m = tm + r0, n = tn + c0;
-    if (m >= M) return;
-    if (n + 3 < N) {
-      if (is_acc)
-        *reinterpret_cast<int4 *>(&acc[(int64_t)m * ldacc + n]) = __builtin_bit_cast(int4, v);
-      else
-        *reinterpret_cast<float4 *>(&y[(int64_t)m * ldy + n]) = v;
-    } else {
-      const float f[4] = {v.x, v.y, v.z, v.w};
-      for (int t = 0; t < 4 && n + t < N; ++t) {
-        if (is_acc)
-          acc[(int64_t)m * ldacc + n + t] = __builtin_bit_cast(int, f[t]);
-        else
-          y[(int64_t)m * ldy + n + t] = f[t];
-      }
-    }
   };
+
+  // Partial tiles keep the accumulator layout: piece (i, j, q) of wave w is
+  // 1 KB at ((w * 16 + 4 i + j) * 4 + q) KB, lane l's four ints at 16 l.
+  // (The block that finishes a tile has written its own share too, and
+  // refills its accumulators with the sum of all shares read back, rather
+  // than adding into them: in-place vector ALU updates would pull the
+  // accumulators out of the AGPRs.)  Byte offsets into the partial area fit
+  // 32 bits: it holds at most 256 tiles of 256 KB.
+  // Partial tiles move with device-scope (sc1) buffer stores and loads,
+  // which go to memory rather than staying in (or being served from) one
+  // XCD's L2; a writer's vmcnt(0) before it bumps the counter then orders
+  // its stores before the counter update, and the block that sees the
+  // final count reads every share from memory.  This avoids writing back
+  // and invalidating whole L2s, which a fence at device scope would do.
+  const __amdgpu_buffer_rsrc_t prs = rsrc(part, (int64_t)T * S * kTileInts * 4);
+  constexpr int kSc1 = 16;  // cache-policy bit: device scope
+  auto write_partial = [&](uint32_t slot_bytes) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r0 = wm * 128 + 32 * i;  // first row of the tile row (block-relative)
-    float sc[16];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sc[e] = scale[r0 + 4 * (lane >> 5) + 8 * (e >> 2) + (e & 3)];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c0 = wn * 128 + 32 * j;
-      if (y) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          tb[(4 * (lane >> 5) + 8 * (e >> 2) + (e & 3)) * 36 + (lane & 31)] = (float)c[i][j][e] * sc[e];
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int rr = (lane >> 3) + 8 * q;
-          put(r0 + rr, c0 + 4 * (lane & 7), *reinterpret_cast<const float4 *>(&tb[rr * 36 + 4 * (lane & 7)]), false);
+          const v4i_ d = {c[i][j][4 * q], c[i][j][4 * q + 1], c[i][j][4 * q + 2],
+                          c[i][j][4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              d, prs, slot_bytes + 4 * (((wid * 16 + 4 * i + j) * 4 + q) * 256 + 4 * lane), 0,
+              kSc1);
+        }
+  };
+
+  // Epilogue.  Element e of lane l in MFMA tile (i, j) is row 8 (e/4) +
+  // 4 (l/32) + e%4, column l%32.  Each tile row i of a wave (32 rows x 128
+  // columns) is transposed through the wave's own 16 KB of LDS, then every
+  // lane stores 16-byte pieces: one store instruction writes two 512-byte
+  // row pieces.  All LDS addresses are one per-lane base plus constants.
+  // Bounds are checked only in tiles that cross the edge of the output.
+  // src(i, v) fills v[j][e] = element e of MFMA tile (i, j) of this wave.
+  auto epilogue = [&](int tm, int tn, auto &&src) __attribute__((always_inline)) {
+    refresh();
+    {
+      const int m = tm + tid;
+      scale[tid] = m < M ? s[m] * bs : 0.0f;
+    }
+    wait_lgkmcnt0();
+    block_barrier();
+    float *tb = reinterpret_cast<float *>(wid == 0 ? A0 : wid == 1 ? A1 : wid == 2 ? A2 : A3);
+    const bool interior = tm + LBM <= M && tn + LBN <= N;
+    const int rsub = lane >> 5, col4 = 4 * (lane & 31);
+    float *wbase = tb + 512 * rsub + (lane & 31);  // row 4 rsub, column l%32
+    const float *rbase = tb + 128 * rsub + col4;   // row rsub, columns col4..+3
+    const float *sbase = scale + wm * 128 + 4 * rsub;
+    // one copy of the pass for tiles inside the output (no checks) and one
+    // for tiles on its edge, so that the checks stay out of the fast path
+    auto pass = [&](auto inside) __attribute__((always_inline)) {
+      constexpr bool kInside = decltype(inside)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = wm * 128 + 32 * i;  // first row of the tile row (block-relative)
+        const int c0 = wn * 128;
+#pragma unroll
+        for (int out = 0; out < 2; ++out) {
+          if (out == 0 && !y) continue;
+          if (out == 1 && !acc) continue;
+          int v[4][16];
+          src(i, v);
+          float sc[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sc[e] = sbase[32 * i + 8 * (e >> 2) + (e & 3)];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              wbase[1024 * (e >> 2) + 128 * (e & 3) + 32 * j] =
+                  out == 0 ? (float)v[j][e] * sc[e] : __builtin_bit_cast(float, v[j][e]);
+          // (a wave's LDS accesses complete in order: no wait between them)
+          const int64_t ld = out == 0 ? ldy : ldacc;
+          float *obase = out == 0 ? y : reinterpret_cast<float *>(acc);
+          // rows are 16-byte aligned: the pitch is a multiple of 4 elements
+          float *orow = obase + (int64_t)(tm + r0 + rsub) * ld + tn + c0 + col4;
+#pragma unroll
+          for (int pc = 0; pc < 16; ++pc) {
+            const float4 o = *reinterpret_cast<const float4 *>(rbase + 256 * pc);
+            float *dst = orow + (int64_t)(2 * pc) * ld;
+            if (kInside) {
+              *reinterpret_cast<float4 *>(__builtin_assume_aligned(dst, 16)) = o;
+            } else {
+              const int m = tm + r0 + 2 * pc + rsub, n = tn + c0 + col4;
+              if (m < M) {
+                if (n + 3 < N) {
+                  *reinterpret_cast<float4 *>(__builtin_assume_aligned(dst, 16)) = o;
+                } else {
+                  const float f[4] = {o.x, o.y, o.z, o.w};
+                  for (int t4 = 0; t4 < 4 && n + t4 < N; ++t4) dst[t4] = f[t4];
+                }
+              }
+            }
+          }
         }
       }
-      if (acc) {
+    };
+    if (interior)
+      pass(std::integral_constant<bool, true>());
+    else
+      pass(std::integral_constant<bool, false>());
+    // the next segment's loads may overwrite the transpose buffers
+    wait_lgkmcnt0();
+    block_barrier();
+  };
+
+  const int t = vb % T, split = vb / T;
+  const int ks = (int)((int64_t)split * nk / S), ke = (int)((int64_t)(split + 1) * nk / S);
+  const int group = t / (kGroupM * nbn), first_m = group * kGroupM;
+  const int gm = min(kGroupM, nbm - first_m), r = t - group * kGroupM * nbn;
+  const int tm = (first_m + r % gm) * LBM, tn = (r / gm) * LBN;
+  refresh();
+  mainloop(tm, tn, ks, ke);
+  bool finish = S == 1;
+  if (!finish) {
+    // share of split s of this tile: partial slot s T + t
+    write_partial((uint32_t)vb * (uint32_t)(kTileInts * 4));
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tid == 0)
+      last_flag =
+          __hip_atomic_fetch_add(&cnt[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    __syncthreads();
+    finish = last_flag;
+    if (finish) {
+      // the last block in: c = sum of every share (its own included), two
+      // shares in flight at a time (a missing second one reads zeros)
+      if (tid == 0) __hip_atomic_store(&cnt[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          tbi[(4 * (lane >> 5) + 8 * (e >> 2) + (e & 3)) * 36 + (lane & 31)] = c[i][j][e];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = 4 * ((wid * 16 + 4 * i) * 1024 + 4 * lane);
+        int v[4][16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int rr = (lane >> 3) + 8 * q;
-          put(r0 + rr, c0 + 4 * (lane & 7), *reinterpret_cast<const float4 *>(&tb[rr * 36 + 4 * (lane & 7)]), true);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[j][e] = 0;
+        for (int sp = 0; sp < S; sp += 2) {
+          const uint32_t o0 = (uint32_t)(sp * T + t) * (uint32_t)(kTileInts * 4) + lo;
+          const uint32_t o1 =
+              sp + 1 < S ? (uint32_t)((sp + 1) * T + t) * (uint32_t)(kTileInts * 4) + lo
+                         : 0x80000000u;
+          v4i_ x0[16], x1[16];
+#pragma unroll
+          for (int jq = 0; jq < 16; ++jq) {
+            x0[jq] = __builtin_amdgcn_raw_buffer_load_b128(prs, o0 + 1024 * jq, 0, kSc1);
+            x1[jq] = __builtin_amdgcn_raw_buffer_load_b128(prs, o1 + 1024 * jq, 0, kSc1);
+          }
+#pragma unroll
+          for (int jq = 0; jq < 16; ++jq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[jq >> 2][4 * (jq & 3) + e] += x0[jq][e] + x1[jq][e];
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) c[i][j][e] = v[j][e];
       }
     }
   }
+  if (finish)
+    epilogue(tm, tn, [&](int i, int(&v)[4][16]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[j][e] = c[i][j][e];
+    });
 }
 
 }  // namespace
 
+namespace {
+
+constexpr int kSplitMaxBlocks = 256;  // blocks (and partial tiles) of a split launch
+constexpr int kSplitCounterBytes = 4 * kSplitMaxBlocks;
+
+// the large tiles pay off once there are enough of them; they address the
+// operands with 32-bit buffer offsets
+bool large_tiles(int64_t M, int64_t N, int64_t ldx, int64_t ldw) {
+  return M >= 512 && N >= 512 && M * ldx < (INT64_C(1) << 31) &&
+         N * ldw < (INT64_C(1) << 31) && M <= INT32_MAX && N <= INT32_MAX;
+}
+
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// K splits per tile: the S (T S <= kSplitMaxBlocks, S <= nk) with the least
+// estimated time, in K steps: rounds of blocks x (steps per block + output
+// pass), plus, when split, one partial tile written per block and S read
+// back by the finishing block.  The weights are measured costs on MI355X.
+int choose_splits(int64_t T, int64_t nk, int cus) {
+  constexpr int64_t kEpi = 7, kWrite = 7, kRead = 5;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int64_t S = 1; S <= nk && S <= kSplitMaxBlocks; ++S) {
+    if (S > 1 && T * S > kSplitMaxBlocks) break;
+    const int64_t rounds = ceil_div(T * S, cus);
+    const int64_t cost =
+        rounds * (ceil_div(nk, S) + kEpi) + (S > 1 ? kWrite + kRead * S : 0);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = (int)S;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+// The area has a fixed layout (counters at offset 0, then the partial
+// tiles), so that calls of any shape that share a workspace agree on where
+// the counters are.
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 512 || N < 512 || K < 1) return 0;
+  const int64_t T = ceil_div(M, LBM) * ceil_div(N, LBN);
+  if (2 * T > kSplitMaxBlocks) return 0;
+  return (size_t)(kSplitCounterBytes + (int64_t)kSplitMaxBlocks * kTileInts * 4);
+}
+
 hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const int8_t *w,
                           int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
-                          int32_t *acc, int64_t ldacc, float *y, int64_t ldy, hipStream_t st) {
-  // the large tiles pay off once there are enough of them; they address
-  // the operands with 32-bit buffer offsets
-  if (M >= 512 && N >= 512 && M * ldx < (INT64_C(1) << 31) && N * ldw < (INT64_C(1) << 31) &&
-      M <= INT32_MAX && N <= INT32_MAX) {
+                          int32_t *acc, int64_t ldacc, float *y, int64_t ldy, void *split,
+                          hipStream_t st) {
+  if (large_tiles(M, N, ldx, ldw)) {
     const int64_t T = ceil_div(M, LBM) * ceil_div(N, LBN);
-    const int64_t blocks = ceil_div(T, kXcds) * kXcds;
+    const int64_t nk = ceil_div(K, LBK);
+    const int cus = device_cus();
+    int S = split != nullptr && 2 * T <= kSplitMaxBlocks && cus > 0
+                ? choose_splits(T, nk, cus)
+                : 1;
+    // test hook: UG_GEMM_FORCE_SPLITS=n asks for n splits where they fit
+    if (split != nullptr && 2 * T <= kSplitMaxBlocks) {
+      if (const char *f = std::getenv("UG_GEMM_FORCE_SPLITS")) {
+        const long n = std::strtol(f, nullptr, 10);
+        if (n >= 1 && n <= nk && T * n <= kSplitMaxBlocks) S = (int)n;
+      }
+    }
+    int32_t *part = nullptr;
+    int *cnt = nullptr;
+    if (S > 1) {
+      cnt = static_cast<int *>(split);
+      part = reinterpret_cast<int32_t *>(static_cast<char *>(split) + kSplitCounterBytes);
+    }
+    const int64_t blocks = ceil_div(T * S, kXcds) * kXcds;
     hipLaunchKernelGGL(gemm_i8_large, dim3((unsigned)blocks), dim3(LTHREADS), 0, st, xq, ldx, s,
-                       w, ldw, beta, (int)M, (int)N, (int)K, acc, ldacc, y, ldy);
+                       w, ldw, beta, (int)M, (int)N, (int)K, acc, ldacc, y, ldy, S, part, cnt);
     return hipGetLastError();
   }
   dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(M, BM));

@@ -243,9 +243,28 @@ def ug_bitlinear_gemm_workspace_size(M, N, K, wfmt):
     return lib().ug_bitlinear_gemm_workspace_size(M, N, K, wfmt)
 
 
+_gemm_ws_cache = {}
+
+
+def gemm_workspace(need, device):
+    """The per-device GEMM workspace: zero-filled once, grown on demand.
+    Every call leaves its counter area zero again, so one buffer serves all
+    calls that do not overlap in time; calls running concurrently on
+    different streams must each pass their own zero-filled buffer."""
+    key = (device.type, device.index)
+    t = _gemm_ws_cache.get(key)
+    if t is None or t.numel() < need:
+        t = torch.zeros(need, dtype=torch.uint8, device=device)
+        _gemm_ws_cache[key] = t
+    return t
+
+
 def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=False,
-                      want_y=True, ws=None, stream=None):
-    """Prefill GEMM (int8 MFMA): same arguments as the GEMV, any M."""
+                      want_y=True, ws=None, split=True, stream=None):
+    """Prefill GEMM (int8 MFMA): same arguments as the GEMV, any M.
+    ws: workspace (default: the shared per-device one); split=False passes
+    only what UG_W_PACK5 decoding needs, so every block computes whole
+    tiles."""
     M = xq.shape[0]
     K = xq.shape[1] if K is None else K
     N, ldw = _weight_args(w, wfmt, K)
@@ -254,12 +273,19 @@ def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=F
     if want_y and y is None:
         y = empty_pitched(M, N, torch.float32, xq.device)
     need = ug_bitlinear_gemm_workspace_size(M, N, K, wfmt)
+    if not split:
+        # a private buffer for the decoded weights alone: written at offset
+        # 0, it must not land on the shared workspace's counters
+        need = N * (-(-K // 16) * 16) if wfmt == UG_W_PACK5 else 0
+        if ws is None and need:
+            ws = torch.empty(need, dtype=torch.uint8, device=xq.device)
     if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=xq.device)
-    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+        ws = gemm_workspace(need, xq.device)
+    ws_bytes = min(ws.numel() * ws.element_size(), need) if ws is not None else 0
     _check(lib().ug_bitlinear_gemm(_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), M, N, K,
                                    _p(acc), _ld(acc) if acc is not None else 0, _p(y),
-                                   _ld(y) if y is not None else 0, _p(ws), ws_bytes,
+                                   _ld(y) if y is not None else 0,
+                                   _p(ws) if ws_bytes else None, ws_bytes,
                                    _stream(stream)), "ug_bitlinear_gemm")
     return acc, y
 

@@ -64,6 +64,37 @@ def test_workspace_formulas(ug):
     assert L.ug_quant_weight_absmean_workspace_size(0, 5) == 0
     assert L.ug_bitlinear_gemm_workspace_size(16, 100, 37, ug.UG_W_I8) == 0
     assert L.ug_bitlinear_gemm_workspace_size(16, 100, 37, ug.UG_W_PACK5) == 100 * 48
+    # problems of 512 x 512 up to 128 tiles of 256 x 256 add the K-split
+    # area in front: 1 KB of tile counters and 256 partial tiles of 256 KB
+    split = 1024 + 256 * 256 * 256 * 4
+    for M, N, K in ((512, 512, 64), (2048, 2560, 6912), (600, 700, 197), (256 * 8, 256 * 16, 64)):
+        assert L.ug_bitlinear_gemm_workspace_size(M, N, K, ug.UG_W_I8) == split
+        dec = N * (-(-K // 16) * 16)
+        assert L.ug_bitlinear_gemm_workspace_size(M, N, K, ug.UG_W_PACK5) == split + dec
+    assert L.ug_bitlinear_gemm_workspace_size(511, 4096, 64, ug.UG_W_I8) == 0
+    assert L.ug_bitlinear_gemm_workspace_size(256 * 8, 256 * 16 + 1, 64, ug.UG_W_I8) == 0
+    assert L.ug_bitlinear_gemm_workspace_size(4096, 6912, 2560, ug.UG_W_I8) == 0
+
+
+def test_k_split_ranges_cover_each_tile_once():
+    """Host mirror of the K split: block v computes steps
+    [s nk / S, (s+1) nk / S) of tile v % T with s = v // T; for every S <= nk
+    the ranges of a tile are non-empty and cover [0, nk) once, in order, and
+    the partial slots v = s T + t are distinct."""
+    for T, nk in ((80, 108), (30, 16), (9, 4), (1, 1), (54, 40)):
+        for S in range(1, min(nk, 256 // T) + 1):
+            slots = set()
+            for t in range(T):
+                prev = 0
+                for sp in range(S):
+                    v = sp * T + t
+                    assert v % T == t and v // T == sp
+                    ks, ke = sp * nk // S, (sp + 1) * nk // S
+                    assert ks == prev and ke > ks
+                    prev = ke
+                    slots.add(v)
+                assert prev == nk
+            assert slots == set(range(T * S))
 
 
 # Fake device addresses: aligned and misaligned.  They are never

@@ -263,6 +263,36 @@ def test_gemm_parity(dev, M, N, K, fmt):
     assert_bits_equal(host(y_d), y_r, "y bits")
 
 
+@pytest.mark.parametrize("M,N,K,splits", [(2048, 2560, 6912, None), (512, 6912, 2560, None),
+                                          (1100, 1300, 1000, 2), (1100, 1300, 1000, 5),
+                                          (600, 700, 197, 4), (512, 512, 64, 1)])
+def test_gemm_split_matches_whole_tiles(dev, M, N, K, splits, monkeypatch):
+    """K-split launches (a tile's K steps shared by several blocks, finished
+    by the last one in) give the same bits as one whole tile per block, and
+    leave the shared workspace ready: a second, smaller call through the
+    same workspace is right too.  splits=None keeps the library's choice;
+    otherwise UG_GEMM_FORCE_SPLITS asks for that many (odd counts, counts
+    that do not divide the K steps, one K step per split with the K tail in
+    the last one)."""
+    _print_case("gemm split", M, N, K, splits)
+    if splits is not None:
+        monkeypatch.setenv("UG_GEMM_FORCE_SPLITS", str(splits))
+    rng = np.random.default_rng([113, M, N, K])
+    xq, wq, s, beta = _rand_problem(rng, M, N, K)
+    args = (pitched(xq), vec(s), pitched(wq), ug.UG_W_I8, scalar_dev(beta))
+    acc_s, y_s = ug.ug_bitlinear_gemm(*args, want_acc=True)
+    acc_w, y_w = ug.ug_bitlinear_gemm(*args, want_acc=True, split=False)
+    assert_bits_equal(host(acc_s), host(acc_w), "acc split vs whole")
+    assert_bits_equal(host(y_s), host(y_w), "y split vs whole")
+    acc_r = oracle.matmul_i32(xq, wq)
+    assert_bits_equal(host(acc_s), acc_r, "acc")
+    m2, n2 = max(512, M // 2 + 3), max(512, N // 2 + 5)
+    acc2, y2 = ug.ug_bitlinear_gemm(pitched(xq[:m2]), vec(s[:m2]), pitched(wq[:n2]), ug.UG_W_I8,
+                                    scalar_dev(beta), want_acc=True)
+    assert_bits_equal(host(acc2), acc_r[:m2, :n2], "acc second call")
+    assert_bits_equal(host(y2), oracle.epilogue(acc_r[:m2, :n2], s[:m2], beta), "y second call")
+
+
 def test_gemm_extreme_values(dev):
     """|acc| at its largest: x_q = +-127 everywhere against all +-1 rows."""
     M, N, K = 64, 64, 6912
