@@ -240,7 +240,7 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *i
 size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t wfmt) {
   if (M < 1 || N < 1 || K < 1 || (wfmt != UG_W_I8 && wfmt != UG_W_PACK5)) return 0;
   const size_t dec = wfmt == UG_W_PACK5 ? (size_t)(N * ug::round_up(K, 16)) : 0;
-  return ug::gemm_split_bytes(M, N, K) + dec;
+  return (M >= 512 && N >= 512 ? ug::gemm_split_area_bytes() : 0) + dec;
 }
 
 ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const void *w,
@@ -253,15 +253,16 @@ ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const
   const size_t dec = wfmt == UG_W_PACK5 ? (size_t)(N * ug::round_up(K, 16)) : 0;
   if (ws != nullptr && !aligned16(ws)) return UG_ERR_WORKSPACE;
   if (wfmt == UG_W_PACK5 && (ws == nullptr || ws_bytes < dec)) return UG_ERR_WORKSPACE;
-  // With room for both, the work-split area sits at the start of the
-  // workspace and the decoded weights follow it; otherwise the decoded
-  // weights start the workspace and every block computes whole tiles.
+  // Layout, decided by the workspace size alone (so that calls of any shape
+  // sharing one workspace agree): with room for both, the split area starts
+  // the workspace and the decoded weights follow it; otherwise the decoded
+  // weights start it and no block shares a tile.
   void *split = nullptr;
   size_t dec_off = 0;
-  const size_t split_bytes = ug::gemm_split_bytes(M, N, K);
-  if (split_bytes != 0 && ws != nullptr && ws_bytes >= split_bytes + dec) {
+  const size_t area = ug::gemm_split_area_bytes();
+  if (ws != nullptr && ws_bytes >= area + dec) {
     split = ws;
-    dec_off = split_bytes;
+    dec_off = area;
   }
   if (wfmt == UG_W_PACK5) {
     const int64_t ldu = ug::round_up(K, 16);

@@ -17,6 +17,7 @@
 // the current one run.
 #include "ug_internal.h"
 
+#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 
@@ -217,16 +218,17 @@ __device__ __forceinline__ uint4 mask_k(uint4 v, int k0, int K) {
 // operand rows in L2.  With S = 1 each block computes a whole tile; with
 // S > 1 a tile's blocks leave int32 partial tiles in the workspace, bump the
 // tile's counter, and move on, so no block ever waits for another.  The last
-// one in adds the partials (integer sums: exact in any order), writes the
-// tile, and sets the counter back to zero, which leaves the workspace ready
-// for the next call.
+// one in adds the partials (integer sums: exact in any order) and writes the
+// tile.  Counters are tagged with the launch, so the workspace needs no
+// clearing between calls.
 constexpr int kTileInts = LBM * LBN;  // int32 entries of a partial tile
 
 __global__ __launch_bounds__(LTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__restrict__ s,
                    const int8_t *__restrict__ w, int64_t ldw, const float *__restrict__ beta, int M,
                    int N, int K, int32_t *__restrict__ acc, int64_t ldacc, float *__restrict__ y,
-                   int64_t ldy, int S, int32_t *__restrict__ part, int *__restrict__ cnt) {
+                   int64_t ldy, int S, int32_t *__restrict__ part,
+                   unsigned long long *__restrict__ cnt, unsigned long long epoch) {
   // four stages per operand, as separate arrays so that the compiler can
   // tell a load into one stage from reads of another
   __shared__ __attribute__((aligned(1024))) int8_t A0[LTILE], A1[LTILE], A2[LTILE], A3[LTILE];
@@ -542,15 +544,26 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
     write_partial((uint32_t)vb * (uint32_t)(kTileInts * 4));
     wait_vmcnt<0>();
     __syncthreads();
-    if (tid == 0)
-      last_flag =
-          __hip_atomic_fetch_add(&cnt[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    if (tid == 0) {
+      // Counter word: (launch epoch << 8) | arrivals.  A word carrying
+      // another epoch (an earlier launch, or whatever the workspace held)
+      // counts as zero arrivals, so the counters need no clearing.
+      unsigned long long v = __hip_atomic_load(&cnt[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned long long nv;
+      do {
+        nv = (v >> 8) == epoch ? v + 1 : (epoch << 8) | 1;
+      } while (!__hip_atomic_compare_exchange_strong(&cnt[t], &v, nv, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      last_flag = ((v >> 8) == epoch ? (int)(v & 255) : 0) == S - 1;
+    }
     __syncthreads();
     finish = last_flag;
     if (finish) {
       // the last block in: c = sum of every share (its own included), two
       // shares in flight at a time (a missing second one reads zeros)
-      if (tid == 0) __hip_atomic_store(&cnt[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // (a replay of the same launch, e.g. from a captured graph, reuses
+      // the epoch: leave the word at zero arrivals)
+      if (tid == 0) __hip_atomic_store(&cnt[t], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t lo = 4 * ((wid * 16 + 4 * i) * 1024 + 4 * lane);
@@ -596,7 +609,7 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
 namespace {
 
 constexpr int kSplitMaxBlocks = 256;  // blocks (and partial tiles) of a split launch
-constexpr int kSplitCounterBytes = 4 * kSplitMaxBlocks;
+constexpr int kSplitCounterBytes = 8 * kSplitMaxBlocks;
 
 // the large tiles pay off once there are enough of them; they address the
 // operands with 32-bit buffer offsets
@@ -617,6 +630,14 @@ int device_cus() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+// Launch epochs of split launches: 56-bit, never 0, one per launch in the
+// process.
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> e{0};
+  unsigned long long v = (e.fetch_add(1) + 1) & ((1ull << 56) - 1);
+  return v == 0 ? 1 : v;
 }
 
 // K splits per tile: the S (T S <= kSplitMaxBlocks, S <= nk) with the least
@@ -643,12 +664,12 @@ int choose_splits(int64_t T, int64_t nk, int cus) {
 }  // namespace
 
 // The area has a fixed layout (counters at offset 0, then the partial
-// tiles), so that calls of any shape that share a workspace agree on where
-// the counters are.
-size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 512 || N < 512 || K < 1) return 0;
-  const int64_t T = ceil_div(M, LBM) * ceil_div(N, LBN);
-  if (2 * T > kSplitMaxBlocks) return 0;
+// tiles) and size, so that calls of any shape that share a workspace agree
+// on where the counters are.
+size_t gemm_split_area_bytes() {
+  static_assert(kSplitCounterBytes + (int64_t)kSplitMaxBlocks * kTileInts * 4 ==
+                    (int64_t)UG_GEMM_SPLIT_AREA,
+                "split area layout and ug.h disagree");
   return (size_t)(kSplitCounterBytes + (int64_t)kSplitMaxBlocks * kTileInts * 4);
 }
 
@@ -671,14 +692,15 @@ hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const i
       }
     }
     int32_t *part = nullptr;
-    int *cnt = nullptr;
+    unsigned long long *cnt = nullptr;
     if (S > 1) {
-      cnt = static_cast<int *>(split);
+      cnt = static_cast<unsigned long long *>(split);
       part = reinterpret_cast<int32_t *>(static_cast<char *>(split) + kSplitCounterBytes);
     }
     const int64_t blocks = ceil_div(T * S, kXcds) * kXcds;
     hipLaunchKernelGGL(gemm_i8_large, dim3((unsigned)blocks), dim3(LTHREADS), 0, st, xq, ldx, s,
-                       w, ldw, beta, (int)M, (int)N, (int)K, acc, ldacc, y, ldy, S, part, cnt);
+                       w, ldw, beta, (int)M, (int)N, (int)K, acc, ldacc, y, ldy, S, part, cnt,
+                       S > 1 ? next_epoch() : 0ull);
     return hipGetLastError();
   }
   dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(M, BM));

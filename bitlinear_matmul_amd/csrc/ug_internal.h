@@ -86,12 +86,11 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const void *w, int wfmt, int64_t ldw, const float *beta,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,
                        int64_t ldacc, float *y, int64_t ldy, hipStream_t st);
-// Bytes of the optional work-split area of a GEMM (tile counters at offset
-// 0, then two partial tiles per block; the same layout for every shape);
-// 0 when the problem cannot use it.
-size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K);
-// split: NULL, or gemm_split_bytes(M, N, K) bytes whose counters are zero
-// (every launch leaves them zero again).
+// Bytes of the GEMM's K-split area (tile counters at offset 0, then one
+// partial tile per block); the same size and layout for every shape.
+size_t gemm_split_area_bytes();
+// split: NULL, or gemm_split_area_bytes() bytes of device memory (any
+// contents: counters are tagged per launch).
 hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s,
                           const int8_t *w, int64_t ldw, const float *beta,
                           int64_t M, int64_t N, int64_t K, int32_t *acc,

@@ -247,14 +247,13 @@ _gemm_ws_cache = {}
 
 
 def gemm_workspace(need, device):
-    """The per-device GEMM workspace: zero-filled once, grown on demand.
-    Every call leaves its counter area zero again, so one buffer serves all
-    calls that do not overlap in time; calls running concurrently on
-    different streams must each pass their own zero-filled buffer."""
+    """The per-device GEMM workspace, grown on demand.  One buffer serves
+    all calls that do not overlap in time; calls running concurrently on
+    different streams must each pass their own buffer."""
     key = (device.type, device.index)
     t = _gemm_ws_cache.get(key)
     if t is None or t.numel() < need:
-        t = torch.zeros(need, dtype=torch.uint8, device=device)
+        t = torch.empty(need, dtype=torch.uint8, device=device)
         _gemm_ws_cache[key] = t
     return t
 
@@ -281,7 +280,8 @@ def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=F
             ws = torch.empty(need, dtype=torch.uint8, device=xq.device)
     if ws is None and need:
         ws = gemm_workspace(need, xq.device)
-    ws_bytes = min(ws.numel() * ws.element_size(), need) if ws is not None else 0
+    # the whole buffer: the library lays it out by its size alone
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().ug_bitlinear_gemm(_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), M, N, K,
                                    _p(acc), _ld(acc) if acc is not None else 0, _p(y),
                                    _ld(y) if y is not None else 0,

@@ -248,15 +248,31 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan,
                                     const ug_gemv_plan_info *info,
                                     void *stream);
 
-/* Bytes of workspace ug_bitlinear_gemm needs (0 for UG_W_I8). */
+/*
+ * Bytes of workspace ug_bitlinear_gemm can use: for M, N >= 512 the K-split
+ * area (UG_GEMM_SPLIT_AREA bytes), plus, for UG_W_PACK5, N*round_up(K,16)
+ * bytes of decoded weights.  0 for UG_W_I8 below 512 x 512.
+ */
 size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
                                         int32_t wfmt);
+
+/* Size of the K-split area: 2 KB of tile counters, then 256 partial tiles of
+ * 256 x 256 int32. */
+#define UG_GEMM_SPLIT_AREA (2048 + 256 * 256 * 256 * 4)
 
 /*
  * Prefill GEMM: the same result as ug_bitlinear_gemv for any M >= 1, as a
  * dense int8 contraction on the matrix cores (ternary values are exact in
- * int8).  Same arguments, plus the workspace (used by UG_W_PACK5 to hold the
- * decoded int8 weights).
+ * int8).  Same arguments, plus the workspace ws (device memory, 16-byte
+ * aligned, any contents; NULL allowed for UG_W_I8):
+ *   - ws_bytes >= UG_GEMM_SPLIT_AREA + decoded bytes: the split area starts
+ *     ws and the decoded weights (UG_W_PACK5) follow it.  Problems with few
+ *     output tiles may then share a tile's K steps between blocks ("K
+ *     split"; integer partial sums, so the result is the same bits).
+ *   - otherwise the decoded weights start ws and every block computes whole
+ *     tiles.
+ * UG_ERR_WORKSPACE if UG_W_PACK5 gets less than the decoded bytes or ws is
+ * misaligned.  Calls that run at the same time must not share a workspace.
  */
 ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s,
                             const void *w, int32_t wfmt, int64_t ldw,

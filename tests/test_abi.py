@@ -64,16 +64,15 @@ def test_workspace_formulas(ug):
     assert L.ug_quant_weight_absmean_workspace_size(0, 5) == 0
     assert L.ug_bitlinear_gemm_workspace_size(16, 100, 37, ug.UG_W_I8) == 0
     assert L.ug_bitlinear_gemm_workspace_size(16, 100, 37, ug.UG_W_PACK5) == 100 * 48
-    # problems of 512 x 512 up to 128 tiles of 256 x 256 add the K-split
-    # area in front: 1 KB of tile counters and 256 partial tiles of 256 KB
-    split = 1024 + 256 * 256 * 256 * 4
-    for M, N, K in ((512, 512, 64), (2048, 2560, 6912), (600, 700, 197), (256 * 8, 256 * 16, 64)):
+    # problems of at least 512 x 512 add the K-split area in front: 2 KB of
+    # tile counters and 256 partial tiles of 256 KB
+    split = 2048 + 256 * 256 * 256 * 4
+    for M, N, K in ((512, 512, 64), (2048, 2560, 6912), (600, 700, 197), (4096, 6912, 2560)):
         assert L.ug_bitlinear_gemm_workspace_size(M, N, K, ug.UG_W_I8) == split
         dec = N * (-(-K // 16) * 16)
         assert L.ug_bitlinear_gemm_workspace_size(M, N, K, ug.UG_W_PACK5) == split + dec
     assert L.ug_bitlinear_gemm_workspace_size(511, 4096, 64, ug.UG_W_I8) == 0
-    assert L.ug_bitlinear_gemm_workspace_size(256 * 8, 256 * 16 + 1, 64, ug.UG_W_I8) == 0
-    assert L.ug_bitlinear_gemm_workspace_size(4096, 6912, 2560, ug.UG_W_I8) == 0
+    assert L.ug_bitlinear_gemm_workspace_size(4096, 511, 64, ug.UG_W_PACK5) == 511 * 64
 
 
 def test_k_split_ranges_cover_each_tile_once():

@@ -293,6 +293,45 @@ def test_gemm_split_matches_whole_tiles(dev, M, N, K, splits, monkeypatch):
     assert_bits_equal(host(y2), oracle.epilogue(acc_r[:m2, :n2], s[:m2], beta), "y second call")
 
 
+def test_gemm_split_after_packed_calls(dev):
+    """Packed-weight calls that decode weights into the shared workspace
+    (one too large to split, one that splits) must leave the split counters
+    alone: a split call afterwards still matches one whole tile per block."""
+    rng = np.random.default_rng(117)
+    xb, wb, sb, bb = _rand_problem(rng, 2048, 6912, 640)
+    pk = pitched(oracle.pack_trits(wb)[0])
+    _, yb = ug.ug_bitlinear_gemm(pitched(xb), vec(sb), pk, ug.UG_W_PACK5, scalar_dev(bb), K=640)
+    _, yb8 = ug.ug_bitlinear_gemm(pitched(xb), vec(sb), pitched(wb), ug.UG_W_I8, scalar_dev(bb))
+    assert_bits_equal(host(yb), host(yb8), "large packed vs bytes")
+    xq, wq, s, beta = _rand_problem(rng, 512, 6912, 2560)
+    pk2 = pitched(oracle.pack_trits(wq)[0])
+    acc5, _ = ug.ug_bitlinear_gemm(pitched(xq), vec(s), pk2, ug.UG_W_PACK5, scalar_dev(beta),
+                                   K=2560, want_acc=True)
+    args = (pitched(xq), vec(s), pitched(wq), ug.UG_W_I8, scalar_dev(beta))
+    acc_s, _ = ug.ug_bitlinear_gemm(*args, want_acc=True)
+    acc_w, _ = ug.ug_bitlinear_gemm(*args, want_acc=True, split=False)
+    assert_bits_equal(host(acc5), host(acc_w), "packed split vs whole")
+    assert_bits_equal(host(acc_s), host(acc_w), "split vs whole after packed calls")
+
+
+def test_gemm_split_any_workspace_contents(dev, monkeypatch):
+    """The split counters carry the launch they belong to, so a workspace
+    full of arbitrary bytes (or of counters from earlier launches) is fine."""
+    monkeypatch.setenv("UG_GEMM_FORCE_SPLITS", "3")
+    rng = np.random.default_rng(119)
+    M, N, K = 1024, 1024, 1536
+    xq, wq, s, beta = _rand_problem(rng, M, N, K)
+    need = ug.ug_bitlinear_gemm_workspace_size(M, N, K, ug.UG_W_I8)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=g).to("cuda:0")
+    args = (pitched(xq), vec(s), pitched(wq), ug.UG_W_I8, scalar_dev(beta))
+    acc_r = oracle.matmul_i32(xq, wq)
+    for rep in range(3):
+        acc_s, _ = ug.ug_bitlinear_gemm(*args, want_acc=True, ws=ws)
+        assert_bits_equal(host(acc_s), acc_r, "acc, garbage workspace, call %d" % rep)
+        ws[:2048] = torch.randint(0, 256, (2048,), dtype=torch.uint8, generator=g).to("cuda:0")
+
+
 def test_gemm_extreme_values(dev):
     """|acc| at its largest: x_q = +-127 everywhere against all +-1 rows."""
     M, N, K = 64, 64, 6912
