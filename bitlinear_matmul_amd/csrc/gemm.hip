@@ -18,6 +18,7 @@
 #include "ug_internal.h"
 
 #include <atomic>
+#include <cstdio>
 #include <cstdlib>
 #include <type_traits>
 
@@ -143,9 +144,11 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
 // l%32 at K bytes [16 (l/32), +16), and accumulator element i of lane l is
 // D[8 (i/4) + 4 (l/32) + i%4][l%32].
 //
-// 256 x 256 output tile per 256-thread block, 2 x 2 waves of 128 x 128
-// (4 x 4 MFMA tiles, 256 int32 accumulators per lane, held in AGPRs; one
-// wave per SIMD).  K step 64, four LDS stages per operand.
+// Output tiles of 256 rows x BN = 32 NT columns per 256-thread block, four
+// waves in a WM x WN grid, each with IT x JT MFMA tiles (int32 accumulators
+// in AGPRs; one wave per SIMD): 256 x 256 as 2 x 2 waves of 4 x 4 tiles, and
+// 256 x 160 as 4 x 1 waves of 2 x 5, which lets N = 2560 fill the GPU with
+// whole rounds of tiles.  K step 64, four LDS stages per operand.
 //
 // Operands go from global memory straight into LDS (buffer loads with the
 // LDS destination bit), so no register staging and no LDS store
@@ -170,9 +173,9 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
 // whatever the weight rows hold there multiplies zeros.  Blocks are mapped to
 // tiles so that the blocks one XCD runs together cover a compact rectangle
 // of tiles.
-constexpr int LBM = 256, LBN = 256, LBK = 64;
+constexpr int LBM = 256, LBK = 64;
 constexpr int LTHREADS = 256;
-constexpr int LTILE = LBM * LBK;  // bytes of one operand tile per stage
+constexpr int LTILE = LBM * LBK;  // bytes of one operand tile per stage (B uses BN rows)
 constexpr int kXcds = 8;          // blocks are dealt to the XCDs round-robin
 constexpr int kGroupM = 4;        // tile rows per group of the tile order
 
@@ -221,14 +224,29 @@ __device__ __forceinline__ uint4 mask_k(uint4 v, int k0, int K) {
 // one in adds the partials (integer sums: exact in any order) and writes the
 // tile.  Counters are tagged with the launch, so the workspace needs no
 // clearing between calls.
-constexpr int kTileInts = LBM * LBN;  // int32 entries of a partial tile
+template <int WM, int NT>
+struct TileShape {
+  static constexpr int WN = 4 / WM;       // waves along N
+  static constexpr int IT = 8 / WM;       // MFMA row tiles per wave
+  static constexpr int JT = NT / WN;      // MFMA column tiles per wave
+  static constexpr int BN = 32 * NT;      // tile columns
+  static constexpr int NMF = IT * JT;     // MFMAs per K half
+  static constexpr int NFR = IT + JT;     // fragment reads per K half
+  static constexpr int kTileInts = LBM * BN;
+  static_assert(WM * WN == 4 && NT % WN == 0 && NT <= 8, "tile shape");
+  static_assert(NMF >= NFR && NMF >= 8 && NMF <= 16, "issue slots per K half");
+};
 
+template <int WM, int NT>
 __global__ __launch_bounds__(LTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__restrict__ s,
                    const int8_t *__restrict__ w, int64_t ldw, const float *__restrict__ beta, int M,
                    int N, int K, int32_t *__restrict__ acc, int64_t ldacc, float *__restrict__ y,
                    int64_t ldy, int S, int32_t *__restrict__ part,
                    unsigned long long *__restrict__ cnt, unsigned long long epoch) {
+  using TS = TileShape<WM, NT>;
+  constexpr int WN = TS::WN, IT = TS::IT, JT = TS::JT, BN = TS::BN, NMF = TS::NMF,
+                NFR = TS::NFR;
   // four stages per operand, as separate arrays so that the compiler can
   // tell a load into one stage from reads of another
   __shared__ __attribute__((aligned(1024))) int8_t A0[LTILE], A1[LTILE], A2[LTILE], A3[LTILE];
@@ -236,7 +254,7 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
   __shared__ float scale[LBM];
   __shared__ int last_flag;
 
-  const int nbm = (M + LBM - 1) / LBM, nbn = (N + LBN - 1) / LBN, T = nbm * nbn;
+  const int nbm = (M + LBM - 1) / LBM, nbn = (N + BN - 1) / BN, T = nbm * nbn;
   const int nk = (K + LBK - 1) / LBK;
   const int kv = K - (nk - 1) * LBK;  // valid K bytes of the last step, 1..64
   // XCD x runs blocks x, x + 8, ...: give it the contiguous share
@@ -245,11 +263,10 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
   const int vb = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
   if (vb >= T * S) return;
 
-  // Thread coordinates, re-read through an empty asm at the top of every
-  // segment: the compiler then cannot hoist the many addresses derived from
-  // them out of the segment loop, where they would stay live (and spill)
-  // across both the K loop and the output pass.
-  int tid, lane, wid, wm, wn;  // wid, wm, wn wave-uniform; 2 x 2 waves
+  // Thread coordinates, read through an empty asm, so that the compiler
+  // recomputes the addresses derived from them where they are used instead
+  // of keeping them all live from the kernel's start.
+  int tid, lane, wid, wm, wn;  // wid, wm, wn wave-uniform
   auto refresh = [&]() __attribute__((always_inline)) {
     int t_ = (int)threadIdx.x;
     asm volatile("" : "+v"(t_));
@@ -257,8 +274,8 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
     lane = t_ & 63;
     const int w_ = __builtin_amdgcn_readfirstlane(t_ >> 6);
     wid = w_;
-    wm = w_ >> 1;
-    wn = w_ & 1;
+    wm = w_ / WN;
+    wn = w_ % WN;
   };
   const __amdgpu_buffer_rsrc_t ar = rsrc(xq, (int64_t)M * ldx);
   const __amdgpu_buffer_rsrc_t br = rsrc(w, (int64_t)N * ldw);
@@ -266,9 +283,11 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
 
   // Loads: 16 per operand and step, 4 per wave; load j fills rows
   // 16 j + [0, 16) of the stage.  Lane l lands at row 16 j + l/4, slot l%4,
-  // so it fetches chunk (l%4) ^ ((l/16)%4) of that row.
+  // so it fetches chunk (l%4) ^ ((l/16)%4) of that row.  Weight rows past
+  // the tile's BN (or past N) get an offset past the buffer: no memory
+  // traffic, and nobody reads those LDS rows.
   uint32_t aoff[4], boff[4];
-  int kend = 0;  // loads clamp to the last step of the current segment
+  int kend = 0;  // loads clamp to the last step of the block's K range
   // This wave's 4 KB part of a stage, from an opaque copy of the thread
   // index: a uniform value the compiler recomputes where it is used (one
   // scalar add per load) instead of keeping 32 hoisted sums in registers.
@@ -299,31 +318,37 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
     }
   };
 
-  v16i c[4][4];
+  v16i c[IT][JT];
 
-  int fa[2], fb[2];  // fragment addresses (set per segment)
-  auto frags = [&](const int8_t *As, const int8_t *Bs, int h, v4i_(&a)[4], v4i_(&b)[4]) __attribute__((always_inline)) {
+  // Fragment addresses (set per block): MFMA row tile i of K half h of a
+  // stage is at row (this wave's first row) + 32 i + (l & 31), chunk
+  // 2 h + (l >> 5), in its swizzled slot; column tile j likewise.
+  int fa[2], fb[2];
+  auto frags = [&](const int8_t *As, const int8_t *Bs, int h, v4i_(&a)[IT], v4i_(&b)[JT])
+                   __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const v4i_ *>(As + fa[h] + 2048 * i);
+    for (int i = 0; i < IT; ++i) a[i] = *reinterpret_cast<const v4i_ *>(As + fa[h] + 2048 * i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const v4i_ *>(Bs + fb[h] + 2048 * j);
+    for (int j = 0; j < JT; ++j) b[j] = *reinterpret_cast<const v4i_ *>(Bs + fb[h] + 2048 * j);
   };
 
-  // The issue order inside a step is written out and pinned: MFMA g,
-  // then (for g < 8) fragment read g, or (g >= 8) load g-8.  The pins
-  // (scheduling barriers that only let plain ALU work move) keep the
-  // compiler from regrouping the reads behind the MFMAs that need them
-  // (mask: only non-matrix vector ALU and scalar ALU work may cross).
+  // The issue order inside a K half is written out and pinned: MFMA g,
+  // then (g < NFR) fragment read g and/or (g >= NMF - 8) load g - (NMF - 8).
+  // The pins (scheduling barriers that only let non-matrix vector ALU and
+  // scalar ALU work move) keep the compiler from regrouping the reads
+  // behind the MFMAs that need them.
   auto pin = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0x0006); };
-  auto mfma_g = [&](const v4i_(&a)[4], const v4i_(&b)[4], int g) __attribute__((always_inline)) {
-    c[g >> 2][g & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[g >> 2], b[g & 3], c[g >> 2][g & 3],
-                                                             0, 0, 0);
+  auto mfma_g = [&](const v4i_(&a)[IT], const v4i_(&b)[JT], int g)
+                    __attribute__((always_inline)) {
+    c[g / JT][g % JT] =
+        __builtin_amdgcn_mfma_i32_32x32x32_i8(a[g / JT], b[g % JT], c[g / JT][g % JT], 0, 0, 0);
   };
-  auto frag_g = [&](const int8_t *As, const int8_t *Bs, int h, v4i_(&a)[4], v4i_(&b)[4], int g) __attribute__((always_inline)) {
-    if (g < 4)
+  auto frag_g = [&](const int8_t *As, const int8_t *Bs, int h, v4i_(&a)[IT], v4i_(&b)[JT], int g)
+                    __attribute__((always_inline)) {
+    if (g < IT)
       a[g] = *reinterpret_cast<const v4i_ *>(As + fa[h] + 2048 * g);
     else
-      b[g - 4] = *reinterpret_cast<const v4i_ *>(Bs + fb[h] + 2048 * (g - 4));
+      b[g - IT] = *reinterpret_cast<const v4i_ *>(Bs + fb[h] + 2048 * (g - IT));
   };
   auto load_g = [&](int k, int8_t *As, int8_t *Bs, int wb, int g) __attribute__((always_inline)) {
     const uint32_t k0 = (uint32_t)min(k, kend - 1) * LBK;
@@ -336,15 +361,15 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
                                                aoff[i] + k0, 0, 0, 0);
   };
 
-  v4i_ a0[4], b0[4], a1[4], b1[4];
+  v4i_ a0[IT], b0[JT], a1[IT], b1[JT];
   // step k reads stage (Ac, Bc); step k+1 is in (An, Bn); step k+3 goes to (Ad, Bd)
   auto step = [&](int k, const int8_t *Ac, const int8_t *Bc, int8_t *An, int8_t *Bn, int8_t *Ad,
                   int8_t *Bd) __attribute__((always_inline)) {
     pin();
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < NMF; ++g) {
       mfma_g(a0, b0, g);
-      if (g < 8) frag_g(Ac, Bc, 1, a1, b1, g);
+      if (g < NFR) frag_g(Ac, Bc, 1, a1, b1, g);
       pin();
     }
     wait_vmcnt<8>();  // this wave's loads of step k+1 (those of k+2 may be in flight)
@@ -357,19 +382,15 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
     const int wb = wave_base();
     pin();
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < NMF; ++g) {
       mfma_g(a1, b1, g);
-      if (g < 8)
-        frag_g(An, Bn, 0, a0, b0, g);
-      else
-        load_g(k + 3, Ad, Bd, wb, g - 8);
+      if (g < NFR) frag_g(An, Bn, 0, a0, b0, g);
+      if (g >= NMF - 8) load_g(k + 3, Ad, Bd, wb, g - (NMF - 8));
       pin();
     }
   };
 
-  // Accumulate steps [ks, ke) of the tile at (tm, tn) into c.  The stages
-  // are free on entry (every wave has passed a barrier after its last LDS
-  // read of them).
+  // Accumulate steps [ks, ke) of the tile at (tm, tn) into c.
   auto mainloop = [&](int tm, int tn, int ks, int ke) __attribute__((always_inline)) {
     // Load i of this wave: rows 16 (4 wid + i) + l/4, chunk (l%4) ^ ((l/16)%4).
     const int lrow = 16 * 4 * wid + (lane >> 2), lchunk = (lane & 3) ^ ((lane >> 4) & 3);
@@ -377,21 +398,20 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
     for (int i = 0; i < 4; ++i) {
       const int row = lrow + 16 * i;
       aoff[i] = tm + row < M ? (uint32_t)((tm + row) * ldx + 16 * lchunk) : 0x80000000u;
-      boff[i] = tn + row < N ? (uint32_t)((tn + row) * ldw + 16 * lchunk) : 0x80000000u;
+      boff[i] = row < BN && tn + row < N ? (uint32_t)((tn + row) * ldw + 16 * lchunk)
+                                         : 0x80000000u;
     }
     kend = ke;
-    // Fragment addresses: tile i of K half h of a stage is at row
-    // 32 i + (l & 31), chunk 2 h + (l >> 5), in its swizzled slot.
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int slot = 16 * ((2 * h + (lane >> 5)) ^ ((lane >> 2) & 3));
-      fa[h] = (wm * 128 + (lane & 31)) * 64 + slot;
-      fb[h] = (wn * 128 + (lane & 31)) * 64 + slot;
+      fa[h] = (wm * 32 * IT + (lane & 31)) * 64 + slot;
+      fb[h] = (wn * 32 * JT + (lane & 31)) * 64 + slot;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JT; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) c[i][j][e] = 0;
     load(ks, A0, B0);
@@ -423,42 +443,44 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
   };
 
   // Partial tiles keep the accumulator layout: piece (i, j, q) of wave w is
-  // 1 KB at ((w * 16 + 4 i + j) * 4 + q) KB, lane l's four ints at 16 l.
+  // 1 KB at ((w NMF + JT i + j) * 4 + q) KB, lane l's four ints at 16 l.
   // (The block that finishes a tile has written its own share too, and
   // refills its accumulators with the sum of all shares read back, rather
   // than adding into them: in-place vector ALU updates would pull the
   // accumulators out of the AGPRs.)  Byte offsets into the partial area fit
-  // 32 bits: it holds at most 256 tiles of 256 KB.
+  // 32 bits: it holds at most 256 tiles of at most 256 KB.
   // Partial tiles move with device-scope (sc1) buffer stores and loads,
   // which go to memory rather than staying in (or being served from) one
   // XCD's L2; a writer's vmcnt(0) before it bumps the counter then orders
   // its stores before the counter update, and the block that sees the
   // final count reads every share from memory.  This avoids writing back
   // and invalidating whole L2s, which a fence at device scope would do.
-  const __amdgpu_buffer_rsrc_t prs = rsrc(part, (int64_t)T * S * kTileInts * 4);
+  const __amdgpu_buffer_rsrc_t prs = rsrc(part, (int64_t)T * S * TS::kTileInts * 4);
   constexpr int kSc1 = 16;  // cache-policy bit: device scope
+  constexpr uint32_t kSlotBytes = TS::kTileInts * 4;
   auto write_partial = [&](uint32_t slot_bytes) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JT; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const v4i_ d = {c[i][j][4 * q], c[i][j][4 * q + 1], c[i][j][4 * q + 2],
                           c[i][j][4 * q + 3]};
           __builtin_amdgcn_raw_buffer_store_b128(
-              d, prs, slot_bytes + 4 * (((wid * 16 + 4 * i + j) * 4 + q) * 256 + 4 * lane), 0,
+              d, prs, slot_bytes + 4 * (((wid * NMF + JT * i + j) * 4 + q) * 256 + 4 * lane), 0,
               kSc1);
         }
   };
 
   // Epilogue.  Element e of lane l in MFMA tile (i, j) is row 8 (e/4) +
-  // 4 (l/32) + e%4, column l%32.  Each tile row i of a wave (32 rows x 128
-  // columns) is transposed through the wave's own 16 KB of LDS, then every
-  // lane stores 16-byte pieces: one store instruction writes two 512-byte
-  // row pieces.  All LDS addresses are one per-lane base plus constants.
-  // Bounds are checked only in tiles that cross the edge of the output.
-  // src(i, v) fills v[j][e] = element e of MFMA tile (i, j) of this wave.
+  // 4 (l/32) + e%4, column l%32.  A wave's output goes out in pieces of one
+  // MFMA row tile (32 rows) by nj = 4, 2 or 1 column tiles (W = 32 nj
+  // columns), each transposed through the wave's own 16 KB of LDS, after
+  // which every lane stores 16-byte pieces of rows (an instruction covers
+  // 256 / W rows of W floats).  All LDS addresses are one per-lane base plus
+  // constants.  Bounds are checked only in tiles on the edge of the output.
+  // src(i, j0, v) fills v[jj][e] = element e of MFMA tile (i, j0 + jj).
   auto epilogue = [&](int tm, int tn, auto &&src) __attribute__((always_inline)) {
     refresh();
     {
@@ -468,80 +490,93 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
     wait_lgkmcnt0();
     block_barrier();
     float *tb = reinterpret_cast<float *>(wid == 0 ? A0 : wid == 1 ? A1 : wid == 2 ? A2 : A3);
-    const bool interior = tm + LBM <= M && tn + LBN <= N;
-    const int rsub = lane >> 5, col4 = 4 * (lane & 31);
-    float *wbase = tb + 512 * rsub + (lane & 31);  // row 4 rsub, column l%32
-    const float *rbase = tb + 128 * rsub + col4;   // row rsub, columns col4..+3
-    const float *sbase = scale + wm * 128 + 4 * rsub;
-    // one copy of the pass for tiles inside the output (no checks) and one
-    // for tiles on its edge, so that the checks stay out of the fast path
-    auto pass = [&](auto inside) __attribute__((always_inline)) {
+    const bool interior = tm + LBM <= M && tn + BN <= N;
+    const int rsub = lane >> 5;
+    const float *sbase = scale + wm * 32 * IT + 4 * rsub;
+    // one piece: MFMA row tile i, column tiles j0 .. j0 + NJ - 1
+    auto piece = [&](auto inside, auto nj_tag, int i, int j0) __attribute__((always_inline)) {
       constexpr bool kInside = decltype(inside)::value;
+      constexpr int NJ = decltype(nj_tag)::value;
+      constexpr int W = 32 * NJ;       // columns of the piece
+      constexpr int LPR = W / 4;       // lanes per row when reading back
+      constexpr int RPI = 64 / LPR;    // rows per read instruction
+      const int r0 = wm * 32 * IT + 32 * i;  // first row of the piece (block-relative)
+      const int c0 = wn * 32 * JT + 32 * j0;
+      float *wbase = tb + 4 * rsub * W + (lane & 31);
+      const int rrow = lane / LPR, col4 = 4 * (lane % LPR);
+      const float *rbase = tb + rrow * W + col4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = wm * 128 + 32 * i;  // first row of the tile row (block-relative)
-        const int c0 = wn * 128;
+      for (int out = 0; out < 2; ++out) {
+        if (out == 0 && !y) continue;
+        if (out == 1 && !acc) continue;
+        int v[4][16];
+        src(i, j0, v);
+        float sc[16];
 #pragma unroll
-        for (int out = 0; out < 2; ++out) {
-          if (out == 0 && !y) continue;
-          if (out == 1 && !acc) continue;
-          int v[4][16];
-          src(i, v);
-          float sc[16];
+        for (int e = 0; e < 16; ++e) sc[e] = sbase[32 * i + 8 * (e >> 2) + (e & 3)];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) sc[e] = sbase[32 * i + 8 * (e >> 2) + (e & 3)];
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int e = 0; e < 16; ++e)
+            wbase[(8 * (e >> 2) + (e & 3)) * W + 32 * jj] =
+                out == 0 ? (float)v[jj][e] * sc[e] : __builtin_bit_cast(float, v[jj][e]);
+        // (a wave's LDS accesses complete in order: no wait between them)
+        const int64_t ld = out == 0 ? ldy : ldacc;
+        float *obase = out == 0 ? y : reinterpret_cast<float *>(acc);
+        // rows are 16-byte aligned: the pitch is a multiple of 4 elements
+        float *orow = obase + (int64_t)(tm + r0 + rrow) * ld + tn + c0 + col4;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              wbase[1024 * (e >> 2) + 128 * (e & 3) + 32 * j] =
-                  out == 0 ? (float)v[j][e] * sc[e] : __builtin_bit_cast(float, v[j][e]);
-          // (a wave's LDS accesses complete in order: no wait between them)
-          const int64_t ld = out == 0 ? ldy : ldacc;
-          float *obase = out == 0 ? y : reinterpret_cast<float *>(acc);
-          // rows are 16-byte aligned: the pitch is a multiple of 4 elements
-          float *orow = obase + (int64_t)(tm + r0 + rsub) * ld + tn + c0 + col4;
-#pragma unroll
-          for (int pc = 0; pc < 16; ++pc) {
-            const float4 o = *reinterpret_cast<const float4 *>(rbase + 256 * pc);
-            float *dst = orow + (int64_t)(2 * pc) * ld;
-            if (kInside) {
-              *reinterpret_cast<float4 *>(__builtin_assume_aligned(dst, 16)) = o;
-            } else {
-              const int m = tm + r0 + 2 * pc + rsub, n = tn + c0 + col4;
-              if (m < M) {
-                if (n + 3 < N) {
-                  *reinterpret_cast<float4 *>(__builtin_assume_aligned(dst, 16)) = o;
-                } else {
-                  const float f[4] = {o.x, o.y, o.z, o.w};
-                  for (int t4 = 0; t4 < 4 && n + t4 < N; ++t4) dst[t4] = f[t4];
-                }
+        for (int pc = 0; pc < 32 / RPI; ++pc) {
+          const float4 o = *reinterpret_cast<const float4 *>(rbase + RPI * W * pc);
+          float *dst = orow + (int64_t)(RPI * pc) * ld;
+          if (kInside) {
+            *reinterpret_cast<float4 *>(__builtin_assume_aligned(dst, 16)) = o;
+          } else {
+            const int m = tm + r0 + RPI * pc + rrow, n = tn + c0 + col4;
+            if (m < M) {
+              if (n + 3 < N) {
+                *reinterpret_cast<float4 *>(__builtin_assume_aligned(dst, 16)) = o;
+              } else {
+                const float f[4] = {o.x, o.y, o.z, o.w};
+                for (int t4 = 0; t4 < 4 && n + t4 < N; ++t4) dst[t4] = f[t4];
               }
             }
           }
         }
       }
     };
+    // one copy of the pass for tiles inside the output (no checks) and one
+    // for tiles on its edge, so that the checks stay out of the fast path
+    auto pass = [&](auto inside) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        if constexpr (JT >= 4) piece(inside, std::integral_constant<int, 4>(), i, 0);
+        if constexpr (JT >= 8) piece(inside, std::integral_constant<int, 4>(), i, 4);
+        if constexpr (JT % 4 >= 2)
+          piece(inside, std::integral_constant<int, 2>(), i, JT - JT % 4);
+        if constexpr (JT % 2 == 1) piece(inside, std::integral_constant<int, 1>(), i, JT - 1);
+      }
+    };
     if (interior)
       pass(std::integral_constant<bool, true>());
     else
       pass(std::integral_constant<bool, false>());
-    // the next segment's loads may overwrite the transpose buffers
+    // the stages may be reused after this
     wait_lgkmcnt0();
     block_barrier();
   };
 
+  refresh();
   const int t = vb % T, split = vb / T;
   const int ks = (int)((int64_t)split * nk / S), ke = (int)((int64_t)(split + 1) * nk / S);
   const int group = t / (kGroupM * nbn), first_m = group * kGroupM;
   const int gm = min(kGroupM, nbm - first_m), r = t - group * kGroupM * nbn;
-  const int tm = (first_m + r % gm) * LBM, tn = (r / gm) * LBN;
-  refresh();
+  const int tm = (first_m + r % gm) * LBM, tn = (r / gm) * BN;
   mainloop(tm, tn, ks, ke);
   bool finish = S == 1;
   if (!finish) {
     // share of split s of this tile: partial slot s T + t
-    write_partial((uint32_t)vb * (uint32_t)(kTileInts * 4));
+    write_partial((uint32_t)vb * kSlotBytes);
     wait_vmcnt<0>();
     __syncthreads();
     if (tid == 0) {
@@ -560,47 +595,54 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
     finish = last_flag;
     if (finish) {
       // the last block in: c = sum of every share (its own included), two
-      // shares in flight at a time (a missing second one reads zeros)
+      // shares in flight at a time (a missing second one reads zeros), in
+      // pieces of up to 4 MFMA tiles
       // (a replay of the same launch, e.g. from a captured graph, reuses
       // the epoch: leave the word at zero arrivals)
       if (tid == 0) __hip_atomic_store(&cnt[t], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      auto refill = [&](int i, auto nj_tag, int j0) __attribute__((always_inline)) {
+        constexpr int NJ = decltype(nj_tag)::value;
+        const uint32_t lo = 4 * ((wid * NMF + JT * i + j0) * 1024 + 4 * lane);
+        int v[NJ][16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = 4 * ((wid * 16 + 4 * i) * 1024 + 4 * lane);
-        int v[4][16];
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) v[j][e] = 0;
+          for (int e = 0; e < 16; ++e) v[jj][e] = 0;
         for (int sp = 0; sp < S; sp += 2) {
-          const uint32_t o0 = (uint32_t)(sp * T + t) * (uint32_t)(kTileInts * 4) + lo;
+          const uint32_t o0 = (uint32_t)(sp * T + t) * kSlotBytes + lo;
           const uint32_t o1 =
-              sp + 1 < S ? (uint32_t)((sp + 1) * T + t) * (uint32_t)(kTileInts * 4) + lo
-                         : 0x80000000u;
-          v4i_ x0[16], x1[16];
+              sp + 1 < S ? (uint32_t)((sp + 1) * T + t) * kSlotBytes + lo : 0x80000000u;
+          v4i_ x0[4 * NJ], x1[4 * NJ];
 #pragma unroll
-          for (int jq = 0; jq < 16; ++jq) {
+          for (int jq = 0; jq < 4 * NJ; ++jq) {
             x0[jq] = __builtin_amdgcn_raw_buffer_load_b128(prs, o0 + 1024 * jq, 0, kSc1);
             x1[jq] = __builtin_amdgcn_raw_buffer_load_b128(prs, o1 + 1024 * jq, 0, kSc1);
           }
 #pragma unroll
-          for (int jq = 0; jq < 16; ++jq)
+          for (int jq = 0; jq < 4 * NJ; ++jq)
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[jq >> 2][4 * (jq & 3) + e] += x0[jq][e] + x1[jq][e];
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) c[i][j][e] = v[j][e];
+          for (int e = 0; e < 16; ++e) c[i][j0 + jj][e] = v[jj][e];
+      };
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        if constexpr (JT >= 4) refill(i, std::integral_constant<int, 4>(), 0);
+        if constexpr (JT >= 8) refill(i, std::integral_constant<int, 4>(), 4);
+        if constexpr (JT % 4 >= 2) refill(i, std::integral_constant<int, 2>(), JT - JT % 4);
+        if constexpr (JT % 2 == 1) refill(i, std::integral_constant<int, 1>(), JT - 1);
       }
     }
   }
   if (finish)
-    epilogue(tm, tn, [&](int i, int(&v)[4][16]) {
+    epilogue(tm, tn, [&](int i, int j0, int(&v)[4][16]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[j][e] = c[i][j][e];
+        for (int e = 0; e < 16; ++e) v[jj][e] = j0 + jj < JT ? c[i][j0 + jj][e] : 0;
     });
 }
 
@@ -640,25 +682,62 @@ unsigned long long next_epoch() {
   return v == 0 ? 1 : v;
 }
 
-// K splits per tile: the S (T S <= kSplitMaxBlocks, S <= nk) with the least
-// estimated time, in K steps: rounds of blocks x (steps per block + output
-// pass), plus, when split, one partial tile written per block and S read
-// back by the finishing block.  The weights are measured costs on MI355X.
-int choose_splits(int64_t T, int64_t nk, int cus) {
-  constexpr int64_t kEpi = 7, kWrite = 7, kRead = 5;
-  int best = 1;
-  int64_t best_cost = INT64_MAX;
-  for (int64_t S = 1; S <= nk && S <= kSplitMaxBlocks; ++S) {
-    if (S > 1 && T * S > kSplitMaxBlocks) break;
-    const int64_t rounds = ceil_div(T * S, cus);
-    const int64_t cost =
-        rounds * (ceil_div(nk, S) + kEpi) + (S > 1 ? kWrite + kRead * S : 0);
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = (int)S;
+// The large-tile shapes: waves along M, MFMA column tiles of the block,
+// and measured costs on MI355X at full load: cycles per K step and
+// microseconds per output pass of a tile.
+struct LargeShape {
+  int wm, nt;
+  double step_cycles, epi_us;
+};
+constexpr LargeShape kShapes[2] = {{2, 8, 1316, 6.5}, {4, 5, 1104, 4.1}};  // 256 x 256, 160
+constexpr int kNumShapes = 2;
+constexpr int64_t kMaxSlotBytes = (int64_t)LBM * 256 * 4;  // largest partial tile
+
+// Tile shape and K splits: the (shape, S) with the least estimated time (in
+// microseconds, at the 1.8 GHz the matrix cores hold under full load):
+// rounds of blocks x (K steps per block + output pass), plus, when split,
+// moving the partial tiles (each written once and read once by the
+// finishing block, at ~4 TB/s) and ~3 us of hand-over.  Ties keep the wider
+// tile and fewer splits.
+struct LargePlan {
+  int shape, S;
+  int64_t T;
+};
+LargePlan plan_large(int64_t M, int64_t N, int64_t nk, bool can_split, int cus) {
+  LargePlan best{0, 1, 0};
+  double best_us = 1e300;
+  for (int sh = 0; sh < kNumShapes; ++sh) {
+    const int64_t nt = kShapes[sh].nt;
+    const int64_t T = ceil_div(M, LBM) * ceil_div(N, 32 * nt);
+    const double step_us = kShapes[sh].step_cycles / 1800.0;
+    for (int64_t S = 1; S <= nk && S <= kSplitMaxBlocks; ++S) {
+      if (S > 1 && (!can_split || T * S > kSplitMaxBlocks)) break;
+      const int64_t rounds = ceil_div(T * S, cus);
+      double us = (double)rounds * ((double)ceil_div(nk, S) * step_us + kShapes[sh].epi_us);
+      if (S > 1) us += 2.0 * (double)(T * S) * (double)(LBM * 32 * nt * 4) / 4.0e6 + 3.0;
+      if (us < best_us) {
+        best_us = us;
+        best = {sh, (int)S, T};
+      }
     }
   }
   return best;
+}
+
+template <int WM, int NT>
+void launch_large(const LargePlan &p, hipStream_t st, const int8_t *xq, int64_t ldx,
+                  const float *s, const int8_t *w, int64_t ldw, const float *beta, int64_t M,
+                  int64_t N, int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy,
+                  int32_t *part, unsigned long long *cnt, unsigned long long epoch) {
+  const int64_t blocks = ceil_div(p.T * p.S, kXcds) * kXcds;
+  hipLaunchKernelGGL((gemm_i8_large<WM, NT>), dim3((unsigned)blocks), dim3(LTHREADS), 0, st, xq,
+                     ldx, s, w, ldw, beta, (int)M, (int)N, (int)K, acc, ldacc, y, ldy, p.S, part,
+                     cnt, epoch);
+}
+
+long env_int(const char *name, long dflt) {
+  const char *f = std::getenv(name);
+  return f ? std::strtol(f, nullptr, 10) : dflt;
 }
 
 }  // namespace
@@ -667,10 +746,10 @@ int choose_splits(int64_t T, int64_t nk, int cus) {
 // tiles) and size, so that calls of any shape that share a workspace agree
 // on where the counters are.
 size_t gemm_split_area_bytes() {
-  static_assert(kSplitCounterBytes + (int64_t)kSplitMaxBlocks * kTileInts * 4 ==
+  static_assert(kSplitCounterBytes + kSplitMaxBlocks * kMaxSlotBytes ==
                     (int64_t)UG_GEMM_SPLIT_AREA,
                 "split area layout and ug.h disagree");
-  return (size_t)(kSplitCounterBytes + (int64_t)kSplitMaxBlocks * kTileInts * 4);
+  return (size_t)(kSplitCounterBytes + kSplitMaxBlocks * kMaxSlotBytes);
 }
 
 hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const int8_t *w,
@@ -678,29 +757,37 @@ hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const i
                           int32_t *acc, int64_t ldacc, float *y, int64_t ldy, void *split,
                           hipStream_t st) {
   if (large_tiles(M, N, ldx, ldw)) {
-    const int64_t T = ceil_div(M, LBM) * ceil_div(N, LBN);
     const int64_t nk = ceil_div(K, LBK);
     const int cus = device_cus();
-    int S = split != nullptr && 2 * T <= kSplitMaxBlocks && cus > 0
-                ? choose_splits(T, nk, cus)
-                : 1;
-    // test hook: UG_GEMM_FORCE_SPLITS=n asks for n splits where they fit
-    if (split != nullptr && 2 * T <= kSplitMaxBlocks) {
-      if (const char *f = std::getenv("UG_GEMM_FORCE_SPLITS")) {
-        const long n = std::strtol(f, nullptr, 10);
-        if (n >= 1 && n <= nk && T * n <= kSplitMaxBlocks) S = (int)n;
-      }
+    LargePlan p = plan_large(M, N, nk, split != nullptr, cus > 0 ? cus : 256);
+    // test hooks: UG_GEMM_FORCE_SHAPE = 0, 1 (256 x 256, 256 x 160 tiles)
+    // and UG_GEMM_FORCE_SPLITS = n ask for that shape / split count where
+    // they fit
+    const long fs = env_int("UG_GEMM_FORCE_SHAPE", -1), fk = env_int("UG_GEMM_FORCE_SPLITS", -1);
+    if (fs >= 0 && fs < kNumShapes) {
+      p.shape = (int)fs;
+      p.T = ceil_div(M, LBM) * ceil_div(N, 32 * kShapes[fs].nt);
+      p.S = 1;
     }
+    if (fk >= 1 && split != nullptr && fk <= nk && p.T * fk <= kSplitMaxBlocks) p.S = (int)fk;
     int32_t *part = nullptr;
     unsigned long long *cnt = nullptr;
-    if (S > 1) {
+    unsigned long long epoch = 0;
+    if (p.S > 1) {
       cnt = static_cast<unsigned long long *>(split);
       part = reinterpret_cast<int32_t *>(static_cast<char *>(split) + kSplitCounterBytes);
+      epoch = next_epoch();
     }
-    const int64_t blocks = ceil_div(T * S, kXcds) * kXcds;
-    hipLaunchKernelGGL(gemm_i8_large, dim3((unsigned)blocks), dim3(LTHREADS), 0, st, xq, ldx, s,
-                       w, ldw, beta, (int)M, (int)N, (int)K, acc, ldacc, y, ldy, S, part, cnt,
-                       S > 1 ? next_epoch() : 0ull);
+    if (env_int("UG_GEMM_VERBOSE", 0))
+      std::fprintf(stderr, "ug gemm M=%lld N=%lld K=%lld: tile 256x%d, %lld tiles, %d K splits\n",
+                   (long long)M, (long long)N, (long long)K, 32 * kShapes[p.shape].nt,
+                   (long long)p.T, p.S);
+    if (p.shape == 0)
+      launch_large<2, 8>(p, st, xq, ldx, s, w, ldw, beta, M, N, K, acc, ldacc, y, ldy, part, cnt,
+                         epoch);
+    else
+      launch_large<4, 5>(p, st, xq, ldx, s, w, ldw, beta, M, N, K, acc, ldacc, y, ldy, part, cnt,
+                         epoch);
     return hipGetLastError();
   }
   dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(M, BM));

@@ -293,6 +293,25 @@ def test_gemm_split_matches_whole_tiles(dev, M, N, K, splits, monkeypatch):
     assert_bits_equal(host(y2), oracle.epilogue(acc_r[:m2, :n2], s[:m2], beta), "y second call")
 
 
+@pytest.mark.parametrize("shape", [0, 1])
+@pytest.mark.parametrize("M,N,K,splits", [(600, 700, 197, 1), (1100, 1300, 1000, 1),
+                                          (1100, 1300, 1000, 3), (512, 2560, 6912, 2)])
+def test_gemm_tile_shapes(dev, shape, M, N, K, splits, monkeypatch):
+    """Each large-tile shape (256 x 256 and 256 x 160 output tiles),
+    whole or K-split, against the oracle: ragged M, N and K edges, partial
+    tiles of every column-piece width in the output pass."""
+    _print_case("gemm shape", shape, M, N, K, splits)
+    monkeypatch.setenv("UG_GEMM_FORCE_SHAPE", str(shape))
+    monkeypatch.setenv("UG_GEMM_FORCE_SPLITS", str(splits))
+    rng = np.random.default_rng([127, M, N, K])
+    xq, wq, s, beta = _rand_problem(rng, M, N, K)
+    acc_d, y_d = ug.ug_bitlinear_gemm(pitched(xq), vec(s), pitched(wq), ug.UG_W_I8,
+                                      scalar_dev(beta), want_acc=True)
+    acc_r = oracle.matmul_i32(xq, wq)
+    assert_bits_equal(host(acc_d), acc_r, "acc")
+    assert_bits_equal(host(y_d), oracle.epilogue(acc_r, s, beta), "y")
+
+
 def test_gemm_split_after_packed_calls(dev):
     """Packed-weight calls that decode weights into the shared workspace
     (one too large to split, one that splits) must leave the split counters
