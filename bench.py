@@ -75,11 +75,11 @@ TRAFFIC = {
     "decode_stack": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
                          src_sha="af54f1408d60cc969bb186a8b73ea40b3a3cad5854ea1e4d32bdc30cf139fac3",
                          bytes_per_launch=4461598),
-    # profiles/gemm_i8_prefill.md: mean of both shapes, 161171.9 KiB fetched
-    # x 1.9997, 75780.8 KiB written x 1.0000
+    # profiles/gemm_i8_large_prefill.md: mean of both shapes, 60190.6 KiB
+    # fetched x 1.9997, 75776.0 KiB written x 1.0000
     "prefill": dict(src="bitlinear_matmul_amd/csrc/gemm.hip",
-                    src_sha="4e8b5895b1adf511f4ee0e00e61ceec4075b7a30d3c6db665e77ba3bddba50c0",
-                    bytes_per_launch=407625154),
+                    src_sha="11ab35c8fe414afb87b67a3d95e82774ae246e31de0d9e609a3908b361837e64",
+                    bytes_per_launch=200846379),
 }
 
 
