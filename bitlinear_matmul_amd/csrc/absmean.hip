@@ -4,15 +4,15 @@
 // bytes": beta = (1/n) sum_i |W_i| + eps, W_q = clip(round(W/beta), -1, 1);
 // one beta per weight tensor.
 //
-// Three launches, no host synchronization, no atomics on values:
+// Two launches, no host synchronization, no atomics on values:
 //   stage 1  one 256-thread block per 8192-element chunk; thread t keeps four
 //            sums and adds element 8192c + 1024i + 4t + j (i = 0..7) to sum j
 //            -- eight coalesced float4 loads per thread -- then the block
 //            folds its 256 lane values pairwise;
-//   stage 2  one block sums the chunk sums (lane t: chunks t, t+256, ...),
-//            folds, and writes beta = fl(fl(T/n) + eps) to device memory;
-//   quant    elementwise W_q = clamp(rint(W/beta), -1, 1), beta read from
-//            device memory.
+//   quant    every block first forms beta the same way (lane t sums the
+//            chunk sums t, t+256, ..., the block folds them, beta =
+//            fl(fl(T/n) + eps); block 0 stores it), then quantizes its share
+//            of the elements: W_q = clamp(rint(W/beta), -1, 1).
 // Traffic: 4 B/element read twice (the second read mostly hits the MALL for
 // tensors that fit) plus 1 B/element written.
 #include "ug_internal.h"
@@ -67,46 +67,88 @@ __global__ __launch_bounds__(256) void absmean_stage1(const float *__restrict__ 
   if (t == 0) partials[c] = p;
 }
 
-__global__ __launch_bounds__(256) void absmean_stage2(const float *__restrict__ partials,
-                                                      int64_t nchunks, float n_f, float eps,
-                                                      float *__restrict__ beta) {
-  __shared__ float lds[256];
+// beta from the chunk sums, in the fixed order (every block gets the same bits).
+__device__ inline float beta_from(const float *__restrict__ partials, int64_t nchunks, float n_f,
+                                  float eps, float *lds) {
   const int t = threadIdx.x;
   float acc = 0.0f;
   for (int64_t c = t; c < nchunks; c += 256) acc = acc + partials[c];
   const float T = fold256(acc, lds);
-  if (t == 0) {
-    const float mean = T / n_f;
-    beta[0] = mean + eps;
-  }
+  const float mean = T / n_f;
+  return mean + eps;
 }
 
 __device__ inline int tern(float w, float b) { return rint_clamp(w / b, -1.0f, 1.0f); }
 
-// One thread per 4 consecutive elements of a row; rows are split into
-// ceil(K/4) vector slots.
+// The same code without the division in almost every case: with
+// q' = w * rb (rb = v_rcp_f32(b), at most 1 ulp from 1/b), |q' - fl(w/b)|
+// stays below 2.5 ulp of |q'|, so only |q'| within kBand of 1/2 (the one
+// rounding boundary that survives the clamp to [-1, 1]) needs the exact
+// quotient; elsewhere the code is sign(q') if |q'| > 1/2, else 0.  Used
+// only for a normal beta of moderate size (the caller checks), so that rb
+// is finite and accurate; NaN elements take the exact path.
+constexpr float kBand = 6.103515625e-05f;  // 2^-14
+__device__ inline int tern_fast(float w, float b, float rb) {
+  const float q = w * rb;
+  const float aq = fabsf(q);
+  if (__builtin_expect(!(fabsf(aq - 0.5f) > kBand), 0)) return tern(w, b);
+  return aq > 0.5f ? (q > 0.0f ? 1 : -1) : 0;
+}
+
+__device__ inline uint32_t tern4(float4 v, float b, float rb, bool fast) {
+  int q0, q1, q2, q3;
+  if (fast) {
+    q0 = tern_fast(v.x, b, rb);
+    q1 = tern_fast(v.y, b, rb);
+    q2 = tern_fast(v.z, b, rb);
+    q3 = tern_fast(v.w, b, rb);
+  } else {
+    q0 = tern(v.x, b);
+    q1 = tern(v.y, b);
+    q2 = tern(v.z, b);
+    q3 = tern(v.w, b);
+  }
+  return (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) | ((uint32_t)(q2 & 0xff) << 16) |
+         ((uint32_t)(q3 & 0xff) << 24);
+}
+
+// Grid-stride over float4 slots.  Contiguous tensors (ldw == ldq == K) are
+// walked as one flat array; pitched ones as ceil(K/4) slots per row.
 __global__ __launch_bounds__(256) void ternary_quant(const float *__restrict__ W, int64_t ldw,
                                                      int64_t N, int64_t K,
-                                                     const float *__restrict__ beta_p,
+                                                     const float *__restrict__ partials,
+                                                     int64_t nchunks, float n_f, float eps,
+                                                     float *__restrict__ beta_out,
                                                      int8_t *__restrict__ wq, int64_t ldq) {
-  const float b = beta_p[0];
+  __shared__ float lds[256];
+  const float b = beta_from(partials, nchunks, n_f, eps, lds);
+  if (blockIdx.x == 0 && threadIdx.x == 0) beta_out[0] = b;
+  const bool fast = b >= 0x1p-100f && b <= 0x1p100f;
+  const float rb = fast ? __builtin_amdgcn_rcpf(b) : 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  if (ldw == K && ldq == K) {
+    const int64_t n = N * K, n4 = n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
+      *reinterpret_cast<uint32_t *>(wq + 4 * i) = tern4(ld4(W + 4 * i), b, rb, fast);
+    // the last n % 4 elements
+    const int64_t e = 4 * n4 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e < n) wq[e] = (int8_t)tern(W[e], b);
+    return;
+  }
   const int64_t kv = (K + 3) / 4;
   const int64_t total = N * kv;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * 256) {
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += stride) {
     const int64_t r = idx / kv;
     const int64_t k = (idx - r * kv) * 4;
     const float4 v = ld4(W + r * ldw + k);  // in-bounds: ldw >= round_up(K, 4)
-    const int q0 = tern(v.x, b), q1 = tern(v.y, b), q2 = tern(v.z, b), q3 = tern(v.w, b);
+    const uint32_t p = tern4(v, b, rb, fast);
     int8_t *dst = wq + r * ldq + k;
     if (k + 3 < K) {
-      const uint32_t p = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
-                         ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
       *reinterpret_cast<uint32_t *>(dst) = p;
     } else {
-      dst[0] = (int8_t)q0;
-      if (k + 1 < K) dst[1] = (int8_t)q1;
-      if (k + 2 < K) dst[2] = (int8_t)q2;
+      dst[0] = (int8_t)(p & 0xff);
+      if (k + 1 < K) dst[1] = (int8_t)((p >> 8) & 0xff);
+      if (k + 2 < K) dst[2] = (int8_t)((p >> 16) & 0xff);
     }
   }
 }
@@ -121,14 +163,13 @@ hipError_t launch_absmean(const float *W, int64_t ldw, int64_t N, int64_t K, flo
   hipLaunchKernelGGL(absmean_stage1, dim3(nchunks), dim3(256), 0, st, W, ldw, N, K, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(absmean_stage2, dim3(1), dim3(256), 0, st, partials, nchunks, (float)n,
-                     eps, beta);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t total = N * ceil_div(K, 4);
+  // every quantization block re-forms beta from the chunk sums: keep them
+  // few (4 per CU), each streaming a long range
+  const int64_t total = ldw == K && ldq == K ? ceil_div(n, 4) : N * ceil_div(K, 4);
   int64_t blocks = ceil_div(total, 256);
-  if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL(ternary_quant, dim3(blocks), dim3(256), 0, st, W, ldw, N, K, beta, wq, ldq);
+  if (blocks > 256 * 4) blocks = 256 * 4;
+  hipLaunchKernelGGL(ternary_quant, dim3(blocks), dim3(256), 0, st, W, ldw, N, K, partials,
+                     nchunks, (float)n, eps, beta, wq, ldq);
   return hipGetLastError();
 }
 

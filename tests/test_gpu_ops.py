@@ -50,6 +50,41 @@ def test_quant_act_golden_ties(dev):
     assert host(xq_d)[0].tolist() == [127, 2, 4, 0, 0, -2, 126, -2, 1, 0, -127, 64]
 
 
+@pytest.mark.parametrize("K", [64, 2560, 6912])
+def test_quant_act_near_ties(dev, K):
+    """Values whose quotient x/s sits on, or a few ulps either side of, every
+    half-integer k + 1/2 (|k| <= 127), for row scales of several binades:
+    the kernels round through a reciprocal and form the exact quotient only
+    near such points, so this is where a wrong tie band would show."""
+    rng = np.random.default_rng([105, K])
+    rows = []
+    for amax in (127.0, 1.0, 3.0e-3, 6.5e4, 0.7):
+        a = np.float32(amax)
+        s = np.float32(np.float32(a / np.float32(127)) + np.float32(1e-5))
+        halves = np.arange(-127, 127, dtype=np.float64) + 0.5
+        base = (halves * np.float64(s)).astype(np.float32)
+        cand = [base]
+        for d in (1, 2, 3, 5, 8):
+            cand.append(np.nextafter(base, np.float32(np.inf)))
+            cand.append(np.nextafter(base, np.float32(-np.inf)))
+            base = cand[-2]
+        vals = np.concatenate(cand)
+        vals = vals[np.abs(vals) <= a]
+        row = rng.choice(vals, size=K).astype(np.float32)
+        row[0] = a                                           # fixes the row max
+        rows.append(row)
+    x = np.stack(rows)
+    xq_d, s_d = ug.ug_quant_act(pitched(x), 1e-5)
+    xq_r, s_r = oracle.quant_act(x, 1e-5)
+    assert_bits_equal(host(s_d), s_r, "s")
+    assert_bits_equal(host(xq_d), xq_r, "x_q")
+    g = np.ones(K, np.float32)
+    xq_n, s_n = ug.ug_rmsnorm_quant_act(pitched(x), vec(g))
+    xq_nr, s_nr = oracle.rmsnorm_quant_act(x, g)
+    assert_bits_equal(host(s_n), s_nr, "s (rmsnorm)")
+    assert_bits_equal(host(xq_n), xq_nr, "x_q (rmsnorm)")
+
+
 def test_quant_act_rows_independent(dev):
     rng = np.random.default_rng(101)
     x = rng.standard_normal((16, 2560), dtype=np.float32)
