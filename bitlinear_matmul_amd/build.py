@@ -30,7 +30,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-FILE_FLAGS = {"gemm.hip": ["-mllvm", "-enable-post-misched=false"]}
+# gemm.hip: keep the K loop's pinned issue order (no post-RA rescheduling).
+# gemv_mfma.hip: the hardware preloads the first two kernel-argument dwords
+# (the block table pointer) into SGPRs, saving a memory round trip at the
+# start of every block of a decode launch.
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "-enable-post-misched=false"],
+              "gemv_mfma.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
 
 
 def sources(src_dir=CSRC):

@@ -39,6 +39,12 @@ inline bool pitch_ok(int64_t ld, int64_t cols, int64_t mult) {
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// The block table of a plan at `plan`: the first 128-byte boundary after the
+// descriptors (plan is 16-byte aligned, so at most 112 bytes of padding).
+size_t plan_table_offset(const void *plan, int32_t count) {
+  const uintptr_t end = (uintptr_t)plan + (size_t)count * sizeof(ug::GemvDesc);
+  return (size_t)(((end + 127) & ~(uintptr_t)127) - (uintptr_t)plan);
+}
 }  // namespace
 
 extern "C" {
@@ -151,7 +157,10 @@ ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s, const
 
 size_t ug_gemv_plan_size(int32_t count) {
   if (count < 1) return 0;
-  return (size_t)count * sizeof(ug::GemvDesc) + ug::kGemvBlocks * sizeof(ug::GemvBlock);
+  // descriptors, up to 112 bytes of padding, then the block table at a
+  // 128-byte boundary (GemvBlock entries: stream split; FineBlock: fine)
+  const size_t entry = std::max(sizeof(ug::GemvBlock), sizeof(ug::FineBlock));
+  return (size_t)count * sizeof(ug::GemvDesc) + 112 + ug::kGemvBlocks * entry;
 }
 
 ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void *plan,
@@ -200,22 +209,27 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
   // the split (fine or stream), items, and the block table: descriptors
   // first, then kGemvBlocks table entries
   std::vector<ug::GemvBlock> blocks;
-  const int variant = ug::gemv_plan(descs.data(), count, blocks);
+  std::vector<ug::FineBlock> fine;
+  const int variant = ug::gemv_plan(descs.data(), count, blocks, fine);
   if (variant < 0) return UG_ERR_INVALID_ARG;
-  if (blocks.empty() || blocks.size() > (size_t)ug::kGemvBlocks) return UG_ERR_UNSUPPORTED;
+  const size_t nblocks = fine.empty() ? blocks.size() : fine.size();
+  if (nblocks == 0 || nblocks > (size_t)ug::kGemvBlocks) return UG_ERR_UNSUPPORTED;
   int64_t total_items = 0;
   for (const auto &d : descs) total_items += d.items;
   if (total_items > INT32_MAX) return UG_ERR_UNSUPPORTED;
   std::vector<uint8_t> host(ug_gemv_plan_size(count), 0);
   std::memcpy(host.data(), descs.data(), descs.size() * sizeof(ug::GemvDesc));
-  std::memcpy(host.data() + descs.size() * sizeof(ug::GemvDesc), blocks.data(),
-              blocks.size() * sizeof(ug::GemvBlock));
+  const size_t toff = plan_table_offset(plan, count);
+  if (fine.empty())
+    std::memcpy(host.data() + toff, blocks.data(), blocks.size() * sizeof(ug::GemvBlock));
+  else
+    std::memcpy(host.data() + toff, fine.data(), fine.size() * sizeof(ug::FineBlock));
   hipError_t e = hipMemcpy(plan, host.data(), host.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_status(e);
   info->count = count;
   info->total_items = (int32_t)total_items;
   info->variant = variant;
-  info->grid = (int32_t)blocks.size();
+  info->grid = (int32_t)nblocks;
   return UG_OK;
 }
 
@@ -232,8 +246,8 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *i
       (mb != 1 && mb != 2 && mb != 4) || (fine && mb != 1))
     return UG_ERR_INVALID_ARG;
   const ug::GemvDesc *descs = (const ug::GemvDesc *)plan;
-  const ug::GemvBlock *blocks = (const ug::GemvBlock *)(descs + info->count);
-  return hip_status(ug::launch_gemv_grouped(descs, blocks, info->count, info->grid, info->variant,
+  const void *table = (const char *)plan + plan_table_offset(plan, info->count);
+  return hip_status(ug::launch_gemv_grouped(descs, table, info->count, info->grid, info->variant,
                                             as_stream(stream)));
 }
 

@@ -14,17 +14,21 @@
 //   One trit per byte: those 16 bytes are the B operand (K positions
 //   64 st + 16 q + [0,16)).
 //   Five trits per byte: the 16 bytes hold 80 trits.  Byte b gives t0..t3
-//   from a 256-entry table of int8x4 in LDS and d4 = floor(b / 81) = t4 + 1,
-//   computed four bytes at a time in 16-bit lanes as (b * 203) >> 14.  Byte
-//   i of dword j gives dword i of B operand j (j < 4); the d4 bytes of dword
-//   j give dword j of B operand 4.  The activations are stored in LDS already
-//   permuted the same way (each 80-position window as fragment 0..3 holding
+//   as int8x4 from a 256-entry table in LDS, and t4 = floor(b / 81) - 1:
+//   fine split, from the same (wide) table entry; stream split, computed
+//   four bytes at a time (the quotient in 16-bit lanes as (b * 203) >> 14,
+//   the -1 borrow-free in every byte), since it keeps more weights in
+//   registers.  Byte i of dword j gives dword i of B operand j (j < 4); the
+//   t4 bytes of dword j give dword j of B operand 4.  The activations are stored in LDS already permuted
+//   the same way (each 80-position window as fragment 0..3 holding
 //   x[5g .. 5g+3] of its bytes g, then fragment 4 holding the x[5g+4]), so
-//   every MFMA adds products of matching K positions, and the d4 = t4 + 1
-//   offset is removed at the end by subtracting sum_g x[5g+4] once per row.
-//   The table is replicated 64 times (code e, replica r at e * 64 + r) and
-//   lane l reads replica l: one v_perm forms each address (b * 256 + 4 l)
-//   and a wave's 64 reads fall in 64 different banks.
+//   every MFMA adds products of matching K positions.
+//   The table fills 64 KB: wide (t0..t3, then t4 in all four bytes), 32
+//   replicas of each 8-byte entry (code e, replica r at byte e * 256 + 8 r),
+//   lane l reads replica l % 32, and each half wave's 32 eight-byte reads
+//   (an LDS pass) fall in 64 different banks; narrow (t0..t3), 64 replicas
+//   at e * 256 + 4 r, lane l reads replica l.  Either way one v_perm forms
+//   each address.
 //
 // Work: one block of 8 waves per CU.  Two ways to split a launch:
 //   stream: a block takes a range of items (32 weight rows over the whole
@@ -52,7 +56,13 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRepl = 64;          // table replicas: one per lane of a wave
+// The fine split's blocks: 8 waves.  (16 are slower: every wave's uniform
+// bookkeeping runs on the CU's one scalar unit.)
+constexpr int kFineThreads = 512;
+constexpr int kFineWaves = kFineThreads / 64;
+constexpr int kFineWaveShift = 3;  // work splits by wave: (w * P) >> 3
+static_assert(kFineWaves == kGemvFineWaves && kFineWaves == 1 << kFineWaveShift, "fine waves");
+constexpr int kTableBytes = 65536;  // the decode table in LDS (wide or narrow)
 constexpr int kXsBytes = 65536;    // staged activations
 constexpr int kZero = kXsBytes;    // 80 zero bytes right after them
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every buffer used here
@@ -115,6 +125,14 @@ __host__ __device__ __forceinline__ bool stages_x(int fmt, int M, int K) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// x kept in a vector register: arithmetic on the result runs on the wave's
+// SIMD instead of the CU's one scalar unit, which every wave of the block
+// shares (uniform bookkeeping repeated by 8 waves queues up there).
+__device__ __forceinline__ int in_vgpr(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Descriptor pointers are generic; every access through them goes through
 // these global-address-space views, so the compiler emits global (not flat)
 // memory instructions.  A flat access in flight makes every later wait for
@@ -140,13 +158,13 @@ __device__ __forceinline__ float4 buffer_load16f(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// t0..t3 of code e as int8 bytes; codes 243..255 give zeros here (their d4
-// is 3: matmul results for invalid codes are unspecified).
-__device__ __forceinline__ uint32_t lut4_entry(int e) {
+// Table entry of code e: t0..t3 as int8 bytes, and t4 in every byte of
+// the second dword.  Codes 243..255 give zeros (matmul results for invalid
+// codes are unspecified).
+constexpr uint32_t lut_t0123(int e) {
   uint32_t v = 0;
   if (e <= 242) {
     int c = e;
-#pragma unroll
     for (int j = 0; j < 4; ++j) {
       v |= ((uint32_t)((c % 3) - 1) & 0xffu) << (8 * j);
       c /= 3;
@@ -154,18 +172,48 @@ __device__ __forceinline__ uint32_t lut4_entry(int e) {
   }
   return v;
 }
-
-__device__ __forceinline__ int q8(float v, float s) { return rint_clamp(v / s, -127.0f, 127.0f); }
+constexpr uint32_t lut_t4(int e) {
+  return e <= 242 ? ((uint32_t)(e / 81 - 1) & 0xffu) * 0x01010101u : 0u;
+}
+// All 256 entries, computed by the compiler: a block fills its LDS replicas
+// with loads from this table instead of per-lane arithmetic.
+struct LutTable {
+  uint2 v[256];
+  constexpr LutTable() : v() {
+    for (int e = 0; e < 256; ++e) {
+      v[e].x = lut_t0123(e);
+      v[e].y = lut_t4(e);
+    }
+  }
+};
+__constant__ const LutTable kLut{};
 
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int e) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
          ((uint32_t)(e & 0xff) << 24);
 }
 
-// Four packed bytes -> t[0..3] = t0..t3 of bytes 0..3 (table), d4 = their
-// four top digits.  lr4 = 4 * lane.
-__device__ __forceinline__ void decode4(uint32_t w, const char *lut, uint32_t lr4, uint32_t *t,
-                                        uint32_t &d4) {
+// Four packed bytes -> t[0..3] = t0..t3 of bytes 0..3, t4 = their four top
+// trits, from the wide table.  lr8 = 8 * (lane % 32).
+__device__ __forceinline__ void decode4_wide(uint32_t w, const char *lut, uint32_t lr8, uint32_t *t,
+                                             uint32_t &t4) {
+  // byte address b * 256 + 8 * (lane % 32) (selector bytes: 0 = lr8 byte 0,
+  // 4+i = byte i of w, 12 = zero)
+  const uint2 e0 = *reinterpret_cast<const uint2 *>(lut + __builtin_amdgcn_perm(w, lr8, 0x0c0c0400u));
+  const uint2 e1 = *reinterpret_cast<const uint2 *>(lut + __builtin_amdgcn_perm(w, lr8, 0x0c0c0500u));
+  const uint2 e2 = *reinterpret_cast<const uint2 *>(lut + __builtin_amdgcn_perm(w, lr8, 0x0c0c0600u));
+  const uint2 e3 = *reinterpret_cast<const uint2 *>(lut + __builtin_amdgcn_perm(w, lr8, 0x0c0c0700u));
+  t[0] = e0.x;
+  t[1] = e1.x;
+  t[2] = e2.x;
+  t[3] = e3.x;
+  // byte i from entry i's t4 dword: bytes 0, 1 of (e0, e1), bytes 2, 3 of (e2, e3)
+  t4 = __builtin_amdgcn_perm(e1.y, e0.y, 0x0c0c0500u) | __builtin_amdgcn_perm(e3.y, e2.y, 0x07020c0cu);
+}
+
+// The same from the narrow table, t4 computed.  lr4 = 4 * lane.
+__device__ __forceinline__ void decode4_narrow(uint32_t w, const char *lut, uint32_t lr4,
+                                               uint32_t *t, uint32_t &t4) {
   // byte address b * 256 + 4 * lane (selector bytes: 0 = lr4 byte 0,
   // 4+i = byte i of w, 12 = zero)
   t[0] = *reinterpret_cast<const uint32_t *>(lut + __builtin_amdgcn_perm(w, lr4, 0x0c0c0400u));
@@ -177,7 +225,10 @@ __device__ __forceinline__ void decode4(uint32_t w, const char *lut, uint32_t lr
   us2 o = __builtin_bit_cast(us2, __builtin_amdgcn_perm(0u, w, 0x0c030c01u));  // b1, b3
   e = (e * (unsigned short)203) >> (unsigned short)14;
   o = (o * (unsigned short)203) >> (unsigned short)14;
-  d4 = __builtin_bit_cast(uint32_t, e) | (__builtin_bit_cast(uint32_t, o) << 8);
+  const uint32_t d4 = __builtin_bit_cast(uint32_t, e) | (__builtin_bit_cast(uint32_t, o) << 8);
+  // d4 - 1 in every byte: each byte of d4 ^ 0x80.. is 0x80 + d4 >= 1, so
+  // subtracting 1 per byte borrows across no byte boundary
+  t4 = ((d4 ^ 0x80808080u) - 0x01010101u) ^ 0x80808080u;
 }
 
 // 80 activations (20 dwords, K order) -> the five 16-byte fragments in the
@@ -196,28 +247,47 @@ __device__ __forceinline__ void permute80(const uint32_t (&X)[20], uint32_t (&F)
                 (X[5 * i + 4] & 0xff000000u);
 }
 
-__device__ __forceinline__ int byte_sum4(uint32_t v) {
-  return (int)(int8_t)(v & 0xff) + (int)(int8_t)((v >> 8) & 0xff) +
-         (int)(int8_t)((v >> 16) & 0xff) + (int)(int8_t)(v >> 24);
-}
-
-template <int FMT>
+template <int FMT, int NW = kWaves>
 struct Smem {
-  uint32_t lut[FMT == UG_W_PACK5 ? 256 * kRepl : 1];
-  uint32_t lut_tmp[FMT == UG_W_PACK5 ? 256 : 1];
+  uint4 lut[FMT == UG_W_PACK5 ? kTableBytes / 16 : 1];  // the decode table
   alignas(16) int8_t xs[kXsBytes + 80];  // staged rows, then 80 zero bytes
   alignas(16) int slots[kFineItems * 256];  // fine split: [item][m][n] int32 sums
-  float part[kWaves][64];                   // per-wave row maxima (fused quantization)
+  float part[NW][64];                       // per-wave row maxima (fused quantization)
   float sm[64];                             // row scales s
-  int cm[64];                               // five-trit correction sum_g x[5g+4]
 };
 
-// s = fl(fl(max|x| / 127) + eps) of row m from the per-wave maxima.
+// The decode table in 16-byte chunks, chunk c holding code c / 16
+// (256 bytes per code): wide, entries for lanes 2 (c % 16) and
+// 2 (c % 16) + 1 (mod 32); narrow, for lanes 4 (c % 16) .. +3.
+// Consecutive threads write consecutive chunks.
+template <int NT>
+constexpr int kTablePer = kTableBytes / 16 / NT;  // chunks per thread of an NT-thread block
+template <int NT>
+__device__ __forceinline__ void table_load(uint2 (&v)[kTablePer<NT>]) {
+#pragma unroll
+  for (int i = 0; i < kTablePer<NT>; ++i) v[i] = kLut.v[(threadIdx.x + NT * i) >> 4];
+}
+template <int NT, bool WIDE, int FMT, int NW>
+__device__ __forceinline__ void table_store(Smem<FMT, NW> &sh, const uint2 (&v)[kTablePer<NT>]) {
+#pragma unroll
+  for (int i = 0; i < kTablePer<NT>; ++i)
+    sh.lut[threadIdx.x + NT * i] = WIDE ? make_uint4(v[i].x, v[i].y, v[i].x, v[i].y)
+                                        : make_uint4(v[i].x, v[i].x, v[i].x, v[i].x);
+}
+// The stream split's (narrow) table.
 template <int FMT>
-__device__ __forceinline__ float row_scale(const Smem<FMT> &sh, int m, float eps) {
+__device__ __forceinline__ void build_table(Smem<FMT> &sh) {
+  uint2 v[kTablePer<kThreads>];
+  table_load<kThreads>(v);
+  table_store<kThreads, false>(sh, v);
+}
+
+// s = fl(fl(max|x| / 127) + eps) of row m from the per-wave maxima.
+template <int FMT, int NW>
+__device__ __forceinline__ float row_scale(const Smem<FMT, NW> &sh, int m, float eps) {
   float a = sh.part[0][m];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) a = fmaxf(a, sh.part[w][m]);
+  for (int w = 1; w < NW; ++w) a = fmaxf(a, sh.part[w][m]);
   const float a127 = a / 127.0f;
   return a127 + eps;
 }
@@ -229,8 +299,7 @@ __device__ __forceinline__ float row_scale(const Smem<FMT> &sh, int m, float eps
 // problem of the block), the row scales (fused quantization, else the given
 // s), the activation rows staged in LDS (Kp bytes per row, zeros past K;
 // five trits per byte: every 80-position window permuted as the decoded
-// weights are) with the d4 correction cm[m] = sum_g x[5g+4], and zeroed
-// reduction slots, and ends with a barrier.
+// weights are) and zeroed reduction slots, and ends with a barrier.
 //
 // Fused quantization reads x in tiles t = (row m, 256 positions c): lane l
 // takes the float4 at 256 c + 4 l, a wave keeps 8 tiles in flight.
@@ -328,10 +397,9 @@ __device__ __forceinline__ void copy_xq4(const GemvDesc &d, Smem<FMT> &sh, const
 // here, which keeps the registers free for a caller short of them.
 template <int FMT, bool PRE>
 __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, bool staged, int Kp,
-                                             bool build_table, bool zero_slots, const XBatch &xb) {
+                                             bool table, bool zero_slots, const XBatch &xb) {
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
-  if (FMT == UG_W_PACK5 && build_table && tid < 256) sh.lut_tmp[tid] = lut4_entry(tid);
-  if (tid < 64) sh.cm[tid] = 0;
+  if (FMT == UG_W_PACK5 && table) build_table(sh);
   if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
   if (zero_slots)
     for (int i = tid; i < kFineItems * 64; i += kThreads)
@@ -378,39 +446,20 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
     }
   }
   __syncthreads();
-  if (FMT == UG_W_PACK5 && build_table) {  // 64 replicas in 16-byte chunks, consecutive lanes
-    uint4 *chunks = reinterpret_cast<uint4 *>(sh.lut);
+  if (FMT == UG_W_PACK5 && staged) {  // permute every 80-position window in place, one per thread
+    const int wpr = Kp / 80, nwin = d.M * wpr;
+    for (int w0 = tid; w0 < nwin; w0 += kThreads) {
+      const int m = w0 / wpr;
+      uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * Kp + (w0 - m * wpr) * 80);
+      uint32_t X[20], F[20];
 #pragma unroll
-    for (int i = 0; i < 256 * kRepl / 4 / kThreads; ++i) {
-      const int c = tid + kThreads * i;
-      const uint32_t v = sh.lut_tmp[c >> 4];
-      chunks[c] = make_uint4(v, v, v, v);
-    }
-  }
-  if (FMT == UG_W_PACK5) {
-    if (staged) {  // permute every 80-position window in place, one window per thread
-      const int wpr = Kp / 80, nwin = d.M * wpr;
-      for (int w0 = tid; w0 < nwin; w0 += kThreads) {
-        const int m = w0 / wpr;
-        uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * Kp + (w0 - m * wpr) * 80);
-        uint32_t X[20], F[20];
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          const uint4 q = win[i];
-          X[4 * i] = q.x; X[4 * i + 1] = q.y; X[4 * i + 2] = q.z; X[4 * i + 3] = q.w;
-        }
-        permute80(X, F);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) win[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
-        atomicAdd(&sh.cm[m], byte_sum4(F[16]) + byte_sum4(F[17]) + byte_sum4(F[18]) + byte_sum4(F[19]));
+      for (int i = 0; i < 5; ++i) {
+        const uint4 q = win[i];
+        X[4 * i] = q.x; X[4 * i + 1] = q.y; X[4 * i + 2] = q.z; X[4 * i + 3] = q.w;
       }
-    } else {  // correction straight from x_q
-      for (int m = wave; m < d.M; m += kWaves) {
-        int sum = 0;
-        for (int k = 5 * lane + 4; k < d.K; k += 5 * 64) sum += gp(d.xq)[(int64_t)m * d.ldxq + k];
-        sum = wave_sum_i32(sum);
-        if (lane == 0) sh.cm[m] = sum;
-      }
+      permute80(X, F);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) win[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
     }
     __syncthreads();
   }
@@ -536,10 +585,10 @@ struct Wave {
       uint32_t T[2][20];
       auto dec = [&](int p, uint32_t(&t)[20]) {
         const uint4 &w = wb[p % kRGW][p / kRGW];
-        decode4(w.x, lut, lr4, t, t[16]);
-        decode4(w.y, lut, lr4, t + 4, t[17]);
-        decode4(w.z, lut, lr4, t + 8, t[18]);
-        decode4(w.w, lut, lr4, t + 12, t[19]);
+        decode4_narrow(w.x, lut, lr4, t, t[16]);
+        decode4_narrow(w.y, lut, lr4, t + 4, t[17]);
+        decode4_narrow(w.z, lut, lr4, t + 8, t[18]);
+        decode4_narrow(w.w, lut, lr4, t + 12, t[19]);
       };
       v4i xf[MB][F1];
       dec(0, T[0]);
@@ -580,7 +629,7 @@ struct Wave {
 
   // Lane (n = l%16, q = l/16) holds D[m = 16 b + 4 q + r][n].
   __device__ __forceinline__ void store(const GemvDesc &d, int item, v4i (&acc)[kRGW][MB][NACC],
-                                        const float *sm, const int *cm, float beta) {
+                                        const float *sm, float beta) {
     const int lane = threadIdx.x & 63, q = lane >> 4;
 #pragma unroll
     for (int rg = 0; rg < kRGW; ++rg) {
@@ -594,7 +643,7 @@ struct Wave {
         for (int r = 0; r < 4; ++r) {
           const int m = 16 * b + 4 * q + r;
           if (n < d.N && m < d.M) {
-            const int val = FMT == UG_W_PACK5 ? v[r] - cm[m] : v[r];
+            const int val = v[r];
             if (d.acc) gp(d.acc)[(int64_t)m * d.ldacc + n] = val;
             if (d.y) {
               const float scale = sm[m] * beta;
@@ -644,7 +693,7 @@ struct ItemLoop {
           for (int a = 0; a < NACC; ++a) acc[r][b][a] = v4i{0, 0, 0, 0};
     }
     wv.compute(d, sh.xs, reinterpret_cast<const char *>(sh.lut), pro_ch, buf, acc);
-    if (pro_ch == wv.NC - 1) wv.store(d, pro_it, acc, sh.sm, sh.cm, beta);
+    if (pro_ch == wv.NC - 1) wv.store(d, pro_it, acc, sh.sm, beta);
     if (++pro_ch == wv.NC) {
       pro_ch = 0;
       pro_it += kWaves;
@@ -724,33 +773,59 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_grouped(const GemvDesc *
 // ---------------------------------------------------------------------------
 // Fine split (M <= 16, staged activations).
 //
-// A decode-sized launch is one chain of dependent steps per wave, and a wave
-// issues at most one instruction every four cycles, so this path keeps the
-// instruction count of every step small: no lane divides by a run-time
-// value, and the problem's kind (fp32 activations or x_q) is a template
-// parameter instead of a branch.
+// A decode-sized launch is one chain of dependent steps per block: fetch the
+// block's descriptor, issue the activation and weight loads, stage the
+// activations, multiply, reduce, store.  This path keeps that chain short:
+// the descriptor (FineBlock) is one 128-byte fetch that holds every derived
+// value (no lane divides by a run-time value), the decode table and the
+// zeroed slots are written while it is in flight, the weight loads leave as
+// soon as it arrives, and the activations are quantized (or copied) straight
+// into their permuted LDS positions, so the set-up has one barrier (two
+// with fp32 activations, whose row maxima need one).  The problem's kind
+// (fp32 activations or x_q) is a template parameter instead of a branch.
 
-// A wave's share of the tiles of the staged rows: tiles [t, te) of the M * T
-// tiles (row m = t / T, chunk c = t % T), taken 8 at a time with (m, c)
-// advanced by increments: one division per wave.
+// Four activation codes (the bytes of v) of positions k .. k+3 (k % 4 == 0)
+// into the staged row at `row`.  Five trits per byte: inside its 80-position
+// window x[5g + e] goes to byte 4g + e (e < 4) or 64 + g (e == 4), the order
+// of the decoded weight fragments; one trit per byte: K order.
+template <int FMT>
+__device__ __forceinline__ void stage4(int8_t *row, int k, uint32_t v) {
+  if (FMT != UG_W_PACK5) {
+    *reinterpret_cast<uint32_t *>(row + k) = v;
+    return;
+  }
+  const int win = k / 80, r = k - 80 * win;  // the four share a window (80 % 4 == 0)
+  int g = r / 5, e = r - 5 * g;
+  int8_t *base = row + 80 * win;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    base[e < 4 ? 4 * g + e : 64 + g] = (int8_t)(v >> (8 * j));
+    if (++e == 5) {
+      e = 0;
+      ++g;
+    }
+  }
+}
+
+// A wave's activation tiles: [t, te) of the block's M * T tiles (row m =
+// t / T, chunk c = t % T), taken NB at a time, (m, c) advanced by
+// increments from the start the planner computed.  Batches: fp32 tiles 4
+// (a decode-sized problem gives a wave at most 4), x_q tiles 8 (8 waves
+// times 8 KB cover the whole staging area: always one batch).
+template <bool FUSED>
+constexpr int kTileBatch = FUSED ? 4 : 8;
 struct TileWalk {
   int t, te, m, c, T;
-  __device__ __forceinline__ void init(int nt, int T_) {
-    const int wave = uniform(threadIdx.x >> 6);
-    T = T_;
-    t = (wave * nt) / kWaves;
-    te = ((wave + 1) * nt) / kWaves;
-    m = t / T;
-    c = t - m * T;
-  }
 };
+template <int NB>
 struct TileBatch {
-  bool ok[8];
-  int m[8], c[8];
+  bool ok[NB];
+  int m[NB], c[NB];
 };
-__device__ __forceinline__ void next8(TileWalk &w, TileBatch &b) {
+template <int NB>
+__device__ __forceinline__ void next_batch(TileWalk &w, TileBatch<NB> &b) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NB; ++i) {
     b.ok[i] = w.t + i < w.te;
     b.m[i] = w.m;
     b.c[i] = w.c;
@@ -759,82 +834,70 @@ __device__ __forceinline__ void next8(TileWalk &w, TileBatch &b) {
       ++w.m;
     }
   }
-  w.t += 8;
+  w.t += NB;
 }
 
 // fp32 tiles: 256 positions, lane l the float4 at 256 c + 4 l (a float4 at
-// k < K is inside the row: ldx >= round_up(K, 4)).  x_q tiles: 1024 bytes,
-// lane l the 16 bytes at 1024 c + 16 l (inside the row when k < K: ldxq >=
-// round_up(K, 16)).
-template <bool FUSED>
-__device__ __forceinline__ void load_batch(const GemvDesc &d, __amdgpu_buffer_rsrc_t xr,
-                                           const TileBatch &b, uint4 (&u)[8]) {
+// k < K is inside the row: the row pitch is at least round_up(K, 4) floats).
+// x_q tiles: 1024 bytes, lane l the 16 bytes at 1024 c + 16 l (inside the
+// row when k < K: pitch >= round_up(K, 16)).  ldx in bytes.
+template <bool FUSED, int NB>
+__device__ __forceinline__ void load_batch(__amdgpu_buffer_rsrc_t xr, int ldx, int K,
+                                           const TileBatch<NB> &b, uint4 (&u)[NB]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (FUSED) {
-      const int k = b.c[i] * 256 + 4 * lane;
-      u[i] = buffer_load16(xr, b.ok[i] && k < d.K ? (uint32_t)((b.m[i] * (int)d.ldx + k) * 4) : kOOB);
-    } else {
-      const int k = b.c[i] * 1024 + 16 * lane;
-      u[i] = buffer_load16(xr, b.ok[i] && k < d.K ? (uint32_t)(b.m[i] * (int)d.ldxq + k) : kOOB);
-    }
+  for (int i = 0; i < NB; ++i) {
+    const int k = FUSED ? b.c[i] * 256 + 4 * lane : b.c[i] * 1024 + 16 * lane;
+    // a tile past the wave's share starts past the buffer (selects, no
+    // branch: every offset below 2^31 + 2^18 reads nothing past it)
+    const uint32_t row = b.ok[i] ? (uint32_t)(b.m[i] * ldx) : kOOB;
+    u[i] = buffer_load16(xr, k < K ? row + (uint32_t)(FUSED ? 4 * k : k) : kOOB);
   }
 }
 
-template <bool FUSED>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const GemvDesc &d) {
-  return FUSED ? buffer_rsrc(d.x, (uint32_t)((int64_t)d.M * d.ldx * 4))
-               : buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
-}
-
-template <bool FUSED>
-__device__ __forceinline__ int tiles_per_row(int Kp) {
-  return FUSED ? (Kp + 255) >> 8 : (Kp + 1023) >> 10;  // the tiles cover whole staged rows
-}
-
 // Pass 1 of fused quantization: per-wave row maxima.
-template <int FMT>
-__device__ __forceinline__ void fine_absmax(const GemvDesc &d, Smem<FMT> &sh, const TileBatch &b,
-                                            const uint4 (&u)[8]) {
+template <int FMT, int NB>
+__device__ __forceinline__ void fine_absmax(Smem<FMT, kFineWaves> &sh, const TileBatch<NB> &b, const uint4 (&u)[NB],
+                                            int K) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NB; ++i) {
     if (b.ok[i]) {
       const float4 v = __builtin_bit_cast(float4, u[i]);
       const int k = b.c[i] * 256 + 4 * lane;
       float a = fabsf(v.x);  // zero when k >= K
-      if (k + 1 < d.K) a = fmaxf(a, fabsf(v.y));
-      if (k + 2 < d.K) a = fmaxf(a, fabsf(v.z));
-      if (k + 3 < d.K) a = fmaxf(a, fabsf(v.w));
+      if (k + 1 < K) a = fmaxf(a, fabsf(v.y));
+      if (k + 2 < K) a = fmaxf(a, fabsf(v.z));
+      if (k + 3 < K) a = fmaxf(a, fabsf(v.w));
       a = wave_max(a);
       if (lane == 0) sh.part[wave][b.m[i]] = fmaxf(sh.part[wave][b.m[i]], a);
     }
   }
 }
 
-// Pass 2: quantized dwords into the staged rows (zeros past K), and into x_q
-// when the block writes the outputs.
-template <int FMT>
-__device__ __forceinline__ void fine_quant(const GemvDesc &d, Smem<FMT> &sh, const TileBatch &b,
-                                           const uint4 (&u)[8], int Kp, bool outputs) {
+// Pass 2: codes into the staged rows (zeros past K), and into x_q when the
+// block writes it.  The codes are ug_quant_act's, bit for bit.
+template <int FMT, int NB>
+__device__ __forceinline__ void fine_quant(Smem<FMT, kFineWaves> &sh, const TileBatch<NB> &b, const uint4 (&u)[NB],
+                                           int K, int Kp, float eps, int8_t *xq_out, int ldxq_out) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const int m = b.m[i], k = b.c[i] * 256 + 4 * lane;
     if (b.ok[i] && k < Kp) {
       const float4 v = __builtin_bit_cast(float4, u[i]);
-      const float s = row_scale(sh, m, d.eps);
-      const uint32_t w = k < d.K ? pack4(q8(v.x, s), k + 1 < d.K ? q8(v.y, s) : 0,
-                                         k + 2 < d.K ? q8(v.z, s) : 0, k + 3 < d.K ? q8(v.w, s) : 0)
-                                 : 0u;
-      *reinterpret_cast<uint32_t *>(sh.xs + m * Kp + k) = w;
-      if (outputs && k < d.K) {
-        int8_t *row = const_cast<int8_t *>(d.xq) + (int64_t)m * d.ldxq;
-        if (k + 4 <= d.K) {
+      const float s = row_scale(sh, m, eps);
+      int c0, c1, c2, c3;
+      q8x4(v, s, c0, c1, c2, c3);
+      const uint32_t w = pack4(k < K ? c0 : 0, k + 1 < K ? c1 : 0, k + 2 < K ? c2 : 0,
+                               k + 3 < K ? c3 : 0);
+      stage4<FMT>(sh.xs + m * Kp, k, w);
+      if (xq_out && k < K) {
+        int8_t *row = xq_out + m * ldxq_out;
+        if (k + 4 <= K) {
           *gp(reinterpret_cast<uint32_t *>(row + k)) = w;  // rows are 16-byte aligned
         } else {
-          for (int j = 0; k + j < d.K; ++j) gp(row)[k + j] = (int8_t)(w >> (8 * j));
+          for (int j = 0; k + j < K; ++j) gp(row)[k + j] = (int8_t)(w >> (8 * j));
         }
       }
     }
@@ -842,237 +905,302 @@ __device__ __forceinline__ void fine_quant(const GemvDesc &d, Smem<FMT> &sh, con
 }
 
 // x_q tiles into the staged rows, bytes past K zeroed.
-template <int FMT>
-__device__ __forceinline__ void fine_copy(const GemvDesc &d, Smem<FMT> &sh, const TileBatch &b,
-                                          const uint4 (&u)[8], int Kp) {
+template <int FMT, int NB>
+__device__ __forceinline__ void fine_copy(Smem<FMT, kFineWaves> &sh, const TileBatch<NB> &b, const uint4 (&u)[NB],
+                                          int K, int Kp) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NB; ++i) {
     const int k = b.c[i] * 1024 + 16 * lane;
-    if (b.ok[i] && k < Kp) {
-      uint32_t w4[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+    if (b.ok[i] && k < Kp) {  // Kp % 16 == 0: the 16 bytes are all inside or all past
+      const uint32_t w4[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int kb = d.K - k - 4 * e;  // bytes of this dword inside the row
-        w4[e] &= kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb))));
+        const int kb = K - k - 4 * e;  // bytes of this dword inside the row
+        stage4<FMT>(sh.xs + b.m[i] * Kp, k + 4 * e,
+                    w4[e] & (kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb))))));
       }
-      *reinterpret_cast<uint4 *>(sh.xs + b.m[i] * Kp + k) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
   }
 }
 
-// The first batch of a wave's activation tiles, issued by the caller before
-// its weight loads: loads complete in issue order, so waiting for these
-// never waits for the weights.
-template <bool FUSED>
-__device__ __forceinline__ void fine_issue_x(const GemvDesc &d, int Kp, TileWalk &walk,
-                                             TileBatch &b0, uint4 (&u0)[8]) {
-  walk.init(d.M * tiles_per_row<FUSED>(Kp), tiles_per_row<FUSED>(Kp));
-  next8(walk, b0);
-  load_batch<FUSED>(d, x_rsrc<FUSED>(d), b0, u0);
+// The activation fragments of one step from the staged rows (xoff: this
+// lane's row and K offset of the step).
+template <int FMT>
+__device__ __forceinline__ void fine_xfrags(const int8_t *xs, int xoff,
+                                            v4i (&xf)[Fmt<FMT>::kFrag]) {
+#pragma unroll
+  for (int j = 0; j < Fmt<FMT>::kFrag; ++j) xf[j] = *reinterpret_cast<const v4i *>(xs + xoff + 16 * j);
 }
 
-// Block set-up of the fine split: decode table, row scales, staged rows
-// from the wave's tiles (the first batch already loaded), the five-trit
-// permutation with the correction cm, zeroed slots.  s_in: with x_q given,
-// thread m < M holds s[m].  Ends with a barrier.
-template <int FMT, bool FUSED>
-__device__ __forceinline__ void fine_setup(const GemvDesc &d, Smem<FMT> &sh, int Kp,
-                                           bool first_block, const TileWalk &walk,
-                                           const TileBatch &b0, const uint4 (&u0)[8],
-                                           float s_in) {
-  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
-  if (FMT == UG_W_PACK5 && tid < 256) sh.lut_tmp[tid] = lut4_entry(tid);
-  if (tid < 64) sh.cm[tid] = 0;
-  if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
+// One (item, step) piece: the step's activation fragments times the decoded
+// weights, into acc (two independent chains).
+template <int FMT>
+__device__ __forceinline__ void fine_piece(const v4i (&xf)[Fmt<FMT>::kFrag], const char *lut,
+                                           const uint4 &w, v4i (&acc)[2]) {
+  acc[0] = acc[1] = v4i{0, 0, 0, 0};
+  if (FMT == UG_W_PACK5) {
+    const uint32_t lr8 = 8u * (threadIdx.x & 31);
+    uint32_t t[20];
+    decode4_wide(w.x, lut, lr8, t, t[16]);
+    decode4_wide(w.y, lut, lr8, t + 4, t[17]);
+    decode4_wide(w.z, lut, lr8, t + 8, t[18]);
+    decode4_wide(w.w, lut, lr8, t + 12, t[19]);
 #pragma unroll
-  for (int i = 0; i < kFineItems * 64 / kThreads; ++i)
-    reinterpret_cast<uint4 *>(sh.slots)[tid + i * kThreads] = make_uint4(0, 0, 0, 0);
-  const __amdgpu_buffer_rsrc_t xr = x_rsrc<FUSED>(d);
-  if (FUSED) {
-    sh.part[wave][lane] = 0.0f;
-    fine_absmax(d, sh, b0, u0);
-    TileWalk w = walk;
-    while (w.t < w.te) {
-      TileBatch b;
-      uint4 u[8];
-      next8(w, b);
-      load_batch<true>(d, xr, b, u);
-      fine_absmax(d, sh, b, u);
-    }
-    __syncthreads();
-    const bool outputs = first_block && d.xq;
-    if (tid < d.M) {
-      const float s = row_scale(sh, tid, d.eps);
-      sh.sm[tid] = s;
-      if (first_block && d.s) gp(d.s)[tid] = s;
-    }
-    fine_quant(d, sh, b0, u0, Kp, outputs);
-    w = walk;
-    while (w.t < w.te) {
-      TileBatch b;
-      uint4 u[8];
-      next8(w, b);
-      load_batch<true>(d, xr, b, u);
-      fine_quant(d, sh, b, u, Kp, outputs);
+    for (int j = 0; j < 5; ++j) {
+      const v4i B = {(int)t[4 * j], (int)t[4 * j + 1], (int)t[4 * j + 2], (int)t[4 * j + 3]};
+      acc[j & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[j], B, acc[j & 1], 0, 0, 0);
     }
   } else {
-    if (tid < d.M) sh.sm[tid] = s_in;
-    fine_copy(d, sh, b0, u0, Kp);
-    TileWalk w = walk;
-    while (w.t < w.te) {
-      TileBatch b;
-      uint4 u[8];
-      next8(w, b);
-      load_batch<false>(d, xr, b, u);
-      fine_copy(d, sh, b, u, Kp);
-    }
-  }
-  __syncthreads();
-  if (FMT == UG_W_PACK5) {
-    uint4 *chunks = reinterpret_cast<uint4 *>(sh.lut);  // 64 replicas, 16-byte chunks
-#pragma unroll
-    for (int i = 0; i < 256 * kRepl / 4 / kThreads; ++i) {
-      const int c = tid + kThreads * i;
-      const uint32_t v = sh.lut_tmp[c >> 4];
-      chunks[c] = make_uint4(v, v, v, v);
-    }
-    // every 80-position window permuted in place: thread per window, the
-    // windows of one row on consecutive threads
-    const int wpr = Kp / 80;
-    int m = 0, w0 = tid;
-    while (w0 >= wpr && m < d.M) {  // row of this thread's first window (few steps: wpr >= 1)
-      w0 -= wpr;
-      ++m;
-    }
-    for (; m < d.M; ) {
-      uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * Kp + w0 * 80);
-      uint32_t X[20], F[20];
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const uint4 q = win[i];
-        X[4 * i] = q.x; X[4 * i + 1] = q.y; X[4 * i + 2] = q.z; X[4 * i + 3] = q.w;
-      }
-      permute80(X, F);
-#pragma unroll
-      for (int i = 0; i < 5; ++i) win[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
-      atomicAdd(&sh.cm[m], byte_sum4(F[16]) + byte_sum4(F[17]) + byte_sum4(F[18]) + byte_sum4(F[19]));
-      w0 += kThreads;
-      while (w0 >= wpr && m < d.M) {
-        w0 -= wpr;
-        ++m;
-      }
-    }
-    __syncthreads();
+    const v4i B = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+    acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[0], B, acc[0], 0, 0, 0);
   }
 }
 
-// Items [i0, i1) of problem d (16 rows each), S steps per item: piece
-// p = (item i0 + p / S, step p % S).  Wave w takes pieces [w P / 8,
-// (w + 1) P / 8) of the block's P, issues all their weight loads first (the
-// set-up's activation loads follow them), and adds its partial sums to the
-// item's LDS slot whenever its next piece belongs to another item.  After a
-// barrier the block writes every item's outputs.
+// Adds a piece's sums (lane (n, q) holds rows 4q .. 4q+3 of column n) to
+// the item's LDS slot.  The test is uniform (r < M, not 4q + r < M): the
+// slot has room for 16 rows, and rows past M are never read.
+__device__ __forceinline__ void fine_flush(int *slots, int it, int M, const v4i (&acc)[2]) {
+  const v4i v = acc[0] + acc[1];
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (r < M) atomicAdd(&slots[it * 256 + (4 * q + r) * 16 + n], v[r]);
+}
+
+// The block of descriptor b; ws = this wave's wave_start word; lut = this
+// thread's decode table chunks (table_load, five trits per byte).  Pieces
+// in step-major order, p = (step p / items, item p % items), of the block's
+// P = items * S: wave w takes [w P / 8, (w + 1) P / 8) and issues all their
+// weight loads at once (after the activation loads).  Consecutive pieces of
+// a wave share their step, so the wave reads a step's activation fragments
+// from LDS once for all its items; each piece's sums go to its item's LDS
+// slot (flushed one piece later, when its MFMAs are done).  After a barrier
+// the block writes every item's outputs.
 template <int FMT, bool FUSED>
-__device__ __forceinline__ void fine_block(const GemvDesc &d, int i0, int i1) {
-  using W = Wave<FMT, 1, true>;
-  constexpr int NACC = W::NACC;
-  __shared__ Smem<FMT> sh;
+__device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
+                                           const uint2 (&lut_chunks)[kTablePer<kFineThreads>]) {
+  __shared__ Smem<FMT, kFineWaves> sh;
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
-  const int S = steps_of(FMT, d.K), Kp = fine_kp(FMT, d.K);
-  const int P = (i1 - i0) * S;
-  const int p0 = uniform(wave * P / kWaves), p1 = uniform((wave + 1) * P / kWaves);
-  const int it0 = p0 / S, st0 = p0 - it0 * S;
-  const float s_in = !FUSED && tid < d.M ? gp(d.s)[tid] : 0.0f;
-  TileWalk walk;
-  TileBatch b0;
-  uint4 x0[8];
-  fine_issue_x<FUSED>(d, Kp, walk, b0, x0);
-  W wv;
-  wv.init(d, true, Kp);
-  uint4 wb[kFinePieces][1][1];
+  // the table's and the descriptor's loads (the caller's) leave first
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int M = b.shape & 0xff, items = (b.shape >> 8) & 0xff, S = b.shape >> 16, K = b.K;
+  const int Kp = S * Fmt<FMT>::kStepK;  // staged row: whole steps, zeros past K
+  const int P = items * S;
+  const int p0 = (wave * P) >> kFineWaveShift, p1 = ((wave + 1) * P) >> kFineWaveShift;
+  const int T = FUSED ? (Kp + 255) >> 8 : (Kp + 1023) >> 10;  // tiles cover whole staged rows
+  const int nt = M * T;
+  const float s_in = !FUSED && tid < M ? gp(b.s)[tid] : 0.0f;
+
+  // activation loads, then weight loads: loads complete in issue order, so
+  // waiting for the activations never waits for the weights
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(b.x, (uint32_t)(M * b.ldx));
+  TileWalk walk{(wave * nt) >> kFineWaveShift, ((wave + 1) * nt) >> kFineWaveShift,
+                in_vgpr((ws >> 16) & 0xff), in_vgpr(ws >> 24), T};
+  constexpr int NB = kTileBatch<FUSED>;
+  TileBatch<NB> b0;
+  uint4 x0[NB];
+  next_batch(walk, b0);
+  const TileWalk rest = walk;  // the tiles after the first batch
+  load_batch<FUSED>(xr, b.ldx, K, b0, x0);
+  __builtin_amdgcn_sched_barrier(0);  // the activation loads leave first
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(b.w, (uint32_t)(b.N * b.ldw));
+  uint4 wb[kFinePieces];
   {
-    int it = it0, st = st0;
+    // unsigned (wrapping) offsets: an offset that wraps into the buffer
+    // reads real weights for a row past N, whose results are never stored;
+    // pieces past the wave's share read past the buffer (nothing)
+    // (the pieces' bookkeeping in vector registers, see in_vgpr)
+    const uint32_t ldw = (uint32_t)b.ldw, item_step = 16u * ldw;
+    const uint32_t wrap_step = 64u - (uint32_t)(items - 1) * item_step;  // to item 0 of the next step
+    int it = in_vgpr(ws & 0xff);
+    uint32_t voff = (uint32_t)(b.i0 * 16 + (lane & 15)) * ldw + 16u * (lane >> 4) +
+                    (uint32_t)it * item_step + 64u * ((ws >> 8) & 0xff);
 #pragma unroll
     for (int j = 0; j < kFinePieces; ++j) {
-      wv.issue(d, i0 + it, st, p0 + j < p1, wb[j]);
-      if (++st == S) {
-        st = 0;
-        ++it;
-      }
+      wb[j] = buffer_load16(wr, p0 + j < p1 ? voff : kOOB);
+      const bool wrap = ++it == items;
+      it = wrap ? 0 : it;
+      voff += wrap ? wrap_step : item_step;
     }
   }
-  const float beta = gp(d.beta)[0];
-  fine_setup<FMT, FUSED>(d, sh, Kp, i0 == 0, walk, b0, x0, s_in);
-  const char *lut = reinterpret_cast<const char *>(sh.lut);
-  v4i acc[1][1][NACC];
+  // a vector load (after the weights, used after them): a scalar one would
+  // make the set-up's first LDS wait also wait for it
+  const float beta = __builtin_bit_cast(float, buffer_load4(buffer_rsrc(b.beta, 4), 0));
+
+  // LDS set-up that needs nothing from the activations: the table (its
+  // loads were issued first, so waiting for them waits for nothing later)
+  // and zeroed slots
+  if (FMT == UG_W_PACK5) table_store<kFineThreads, true>(sh, lut_chunks);
 #pragma unroll
-  for (int a = 0; a < NACC; ++a) acc[0][0][a] = v4i{0, 0, 0, 0};
-  int it = it0, st = st0;
+  for (int i = 0; i < kFineItems * 64 / kFineThreads; ++i)
+    reinterpret_cast<uint4 *>(sh.slots)[tid + i * kFineThreads] = make_uint4(0, 0, 0, 0);
+  if (FUSED) sh.part[wave][lane] = 0.0f;  // this wave's own row maxima
+
+  // staged rows
+  if (FUSED) {
+    fine_absmax(sh, b0, x0, K);
+    for (TileWalk w = rest; w.t < w.te;) {
+      TileBatch<NB> bb;
+      uint4 u[NB];
+      next_batch(w, bb);
+      load_batch<true>(xr, b.ldx, K, bb, u);
+      fine_absmax(sh, bb, u, K);
+    }
+    __syncthreads();  // row maxima
+    if (tid < M) {
+      const float s = row_scale(sh, tid, b.eps);
+      sh.sm[tid] = s;
+      if (b.s) gp(b.s)[tid] = s;
+    }
+    fine_quant(sh, b0, x0, K, Kp, b.eps, b.xq_out, b.ldxq_out);
+    for (TileWalk w = rest; w.t < w.te;) {
+      TileBatch<NB> bb;
+      uint4 u[NB];
+      next_batch(w, bb);
+      load_batch<true>(xr, b.ldx, K, bb, u);
+      fine_quant(sh, bb, u, K, Kp, b.eps, b.xq_out, b.ldxq_out);
+    }
+  } else {
+    if (tid < M) sh.sm[tid] = s_in;
+    fine_copy(sh, b0, x0, K, Kp);
+    for (TileWalk w = rest; w.t < w.te;) {
+      TileBatch<NB> bb;
+      uint4 u[NB];
+      next_batch(w, bb);
+      load_batch<false>(xr, b.ldx, K, bb, u);
+      fine_copy(sh, bb, u, K, Kp);
+    }
+  }
+  __syncthreads();  // table, slots, scales and staged rows
+
+  const char *lut = reinterpret_cast<const char *>(sh.lut);
+  // rows past M read row M-1: MFMA output row m depends only on input row m,
+  // and rows past M are never stored
+  const int xoff = min(lane & 15, M - 1) * Kp + (lane >> 4) * Fmt<FMT>::kLaneK;
+  v4i xf[Fmt<FMT>::kFrag];
+  v4i acc[2], prev[2];
+  int it = ws & 0xff, st = (ws >> 8) & 0xff, xst = -1, prev_it = 0;
 #pragma unroll
   for (int j = 0; j < kFinePieces; ++j) {
     if (p0 + j < p1) {
-      wv.compute(d, sh.xs, lut, st, wb[j], acc);
-      if (p0 + j + 1 == p1 || st + 1 == S) {  // last piece of this item here
-        v4i v = acc[0][0][0];
-#pragma unroll
-        for (int a = 1; a < NACC; ++a) v += acc[0][0][a];
-        const int n = lane & 15, q = lane >> 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * q + r < d.M) atomicAdd(&sh.slots[it * 256 + (4 * q + r) * 16 + n], v[r]);
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) acc[0][0][a] = v4i{0, 0, 0, 0};
+      if (st != xst) {  // a new step: its fragments serve the following pieces too
+        fine_xfrags<FMT>(sh.xs, xoff + st * Fmt<FMT>::kStepK, xf);
+        xst = st;
       }
-      if (++st == S) {
-        st = 0;
-        ++it;
+      fine_piece<FMT>(xf, lut, wb[j], acc);
+      if (j > 0) fine_flush(sh.slots, prev_it, M, prev);
+      prev[0] = acc[0];
+      prev[1] = acc[1];
+      prev_it = it;
+      if (++it == items) {
+        it = 0;
+        ++st;
       }
     }
   }
+  if (p0 < p1) fine_flush(sh.slots, prev_it, M, prev);
   __syncthreads();
-  if (tid < (i1 - i0) * 16) {  // thread (item, n) writes column n of the item, every row
-    const int li = tid >> 4, n = tid & 15, ng = (i0 + li) * 16 + n;
-    if (ng < d.N) {
-      for (int m = 0; m < d.M; ++m) {
-        const int val = sh.slots[li * 256 + m * 16 + n] - (FMT == UG_W_PACK5 ? sh.cm[m] : 0);
-        if (d.acc) gp(d.acc)[(int64_t)m * d.ldacc + ng] = val;
-        if (d.y) gp(d.y)[(int64_t)m * d.ldy + ng] = (float)val * (sh.sm[m] * beta);
+  if (tid < items * 16) {  // thread (item, n) writes column n of the item, every row
+    const int li = tid >> 4, n = tid & 15, ng = (b.i0 + li) * 16 + n;
+    if (ng < b.N) {
+      for (int m = 0; m < M; ++m) {
+        const int val = sh.slots[li * 256 + m * 16 + n];
+        if (b.acc) gp(b.acc)[(int64_t)m * b.ldacc + ng] = val;
+        if (b.y) gp(b.y)[(int64_t)m * b.ldy + ng] = (float)val * (sh.sm[m] * beta);
       }
     }
   }
 }
 
+// One problem: every block but the last takes the items of b.shape from
+// blockIdx.x times that count (b.wave_start); the last takes last.items
+// (last.wave_start).
+struct FineTail {
+  uint32_t wave_start[kFineWaves];
+  int32_t items;
+};
+
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void gemv_fine_single(GemvDesc d, int ipb) {
-  const int i0 = blockIdx.x * ipb, i1 = min(d.items, i0 + ipb);
-  if (i0 < i1) fine_block<FMT, false>(d, i0, i1);
+__global__ __launch_bounds__(kFineThreads) void gemv_fine_single(const FineBlock b, const FineTail last) {
+  uint2 lut[kTablePer<kFineThreads>];
+  if (FMT == UG_W_PACK5) table_load<kFineThreads>(lut);
+  const bool is_last = blockIdx.x + 1 == gridDim.x;
+  const int wave = uniform(threadIdx.x >> 6);
+  // indexed in the argument segment itself (a modified copy would be
+  // indexed in scratch memory)
+  const uint32_t ws = is_last ? last.wave_start[wave] : b.wave_start[wave];
+  FineBlock mine = b;
+  mine.i0 = blockIdx.x * ((b.shape >> 8) & 0xff);
+  if (is_last) mine.shape = (b.shape & 0xffff00ffu) | ((uint32_t)last.items << 8);
+  fine_block<FMT, false>(mine, ws, lut);
 }
 
 template <int FMT, bool FUSED>
-__global__ __launch_bounds__(kThreads) void gemv_fine_grouped(const GemvBlock *__restrict__ blocks) {
-  const GemvBlock bl = blocks[blockIdx.x];
-  if (bl.i0 < bl.i1) fine_block<FMT, FUSED>(bl.d, bl.i0, bl.i1);
+__global__ __launch_bounds__(kFineThreads) void gemv_fine_grouped(const FineBlock *__restrict__ blocks) {
+  uint2 lut[kTablePer<kFineThreads>];  // the table's loads first: both fetches travel together
+  if (FMT == UG_W_PACK5) table_load<kFineThreads>(lut);
+  const FineBlock b = blocks[blockIdx.x];
+  fine_block<FMT, FUSED>(b, blocks[blockIdx.x].wave_start[uniform(threadIdx.x >> 6)], lut);
 }
 
 // ---------------------------------------------------------------------------
 // Host side.
 
+// The FineBlock of items [i0, i1) of problem d; `first`: the problem's
+// first block (the one that writes the fused quantization's outputs).
+FineBlock fine_block_of(const GemvDesc &d, int i0, int i1, bool first) {
+  const bool fused = d.x != nullptr;
+  FineBlock f{};
+  f.x = fused ? (const void *)d.x : (const void *)d.xq;
+  f.w = d.w;
+  f.beta = d.beta;
+  f.y = d.y;
+  f.acc = d.acc;
+  f.s = fused ? (first ? d.s : nullptr) : d.s;
+  f.xq_out = fused && first ? const_cast<int8_t *>(d.xq) : nullptr;
+  f.ldx = (int32_t)(fused ? 4 * d.ldx : d.ldxq);
+  f.ldw = (int32_t)d.ldw;
+  f.ldy = (int32_t)d.ldy;
+  f.ldacc = (int32_t)d.ldacc;
+  f.ldxq_out = fused ? (int32_t)d.ldxq : 0;
+  f.eps = d.eps;
+  f.N = d.N;
+  f.K = d.K;
+  f.i0 = i0;
+  const int S = steps_of(d.wfmt, d.K), P = (i1 - i0) * S, Kp = fine_kp(d.wfmt, d.K);
+  const int T = fused ? (Kp + 255) >> 8 : (Kp + 1023) >> 10, nt = d.M * T;
+  f.shape = (uint32_t)d.M | ((uint32_t)(i1 - i0) << 8) | ((uint32_t)S << 16);
+  for (int w = 0; w < kFineWaves; ++w) {
+    const int p0 = (w * P) >> kFineWaveShift, t0 = (w * nt) >> kFineWaveShift;
+    // pieces in step-major order: p = step * items + item
+    const int items = i1 - i0;
+    f.wave_start[w] = (uint32_t)(p0 % items) | ((uint32_t)(p0 / items) << 8) |
+                      ((uint32_t)(t0 / T) << 16) | ((uint32_t)(t0 % T) << 24);
+  }
+  return f;
+}
+
 // Fine split of a group: items per block for every problem, or false when
 // the group is too large for it (then the stream split runs).  Blocks of
 // about T / 256 pieces each, at most kFineItems items, one problem each.
-bool plan_fine(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
+bool plan_fine(GemvDesc *descs, int count, std::vector<FineBlock> &blocks) {
   int64_t T = 0;
   for (int i = 0; i < count; ++i) {
     const GemvDesc &d = descs[i];
     if (d.M > 16 || (int64_t)d.M * fine_kp(d.wfmt, d.K) > kXsBytes) return false;
     if ((d.x != nullptr) != (descs[0].x != nullptr)) return false;  // one kind per launch
+    // the block descriptor holds 32-bit pitches
+    if (d.ldy >= (INT64_C(1) << 31) || d.ldacc >= (INT64_C(1) << 31) ||
+        d.ldxq >= (INT64_C(1) << 31) || 4 * d.ldx >= (INT64_C(1) << 31))
+      return false;
     T += (int64_t)((d.N + 15) / 16) * steps_of(d.wfmt, d.K);
   }
-  if (T > (int64_t)kGemvBlocks * kWaves * kFinePieces) return false;
+  if (T > (int64_t)kGemvBlocks * kFineWaves * kFinePieces) return false;
   std::vector<int> ipb((size_t)count);
   for (int64_t target = (T + kGemvBlocks - 1) / kGemvBlocks;; ++target) {
-    if (target > (int64_t)kWaves * kFinePieces) return false;
+    if (target > (int64_t)kFineWaves * kFinePieces) return false;
     int64_t nb = 0;
     bool fits = true;
     for (int i = 0; i < count; ++i) {
@@ -1080,8 +1208,9 @@ bool plan_fine(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
       int k = (int)(target / S);
       k = k < 1 ? 1 : (k > kFineItems ? kFineItems : k);
       k = k > items ? items : k;
-      // every wave's share of a block's pieces must fit its registers
-      if ((k * S + kWaves - 1) / kWaves > kFinePieces) fits = false;
+      // every wave's share of a block's pieces must fit its registers (so
+      // a block has at most 64 pieces and an item at most 64 steps)
+      if ((k * S + kFineWaves - 1) / kFineWaves > kFinePieces) fits = false;
       ipb[(size_t)i] = k;
       nb += (items + k - 1) / k;
     }
@@ -1094,7 +1223,7 @@ bool plan_fine(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
     descs[i].mb = 1;
     descs[i].items = items;
     for (int a = 0; a < items; a += ipb[(size_t)i])
-      blocks.push_back(GemvBlock{descs[i], i, a, std::min(items, a + ipb[(size_t)i]), 0});
+      blocks.push_back(fine_block_of(descs[i], a, std::min(items, a + ipb[(size_t)i]), a == 0));
   }
   return true;
 }
@@ -1108,12 +1237,14 @@ int gemv_grid(int64_t total_items) {
   return (int)(by_items < kGemvBlocks ? (by_items < 1 ? 1 : by_items) : kGemvBlocks);
 }
 
-int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
+int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
+              std::vector<FineBlock> &fine) {
   const int fmt = descs[0].wfmt;
   for (int i = 1; i < count; ++i)
     if (descs[i].wfmt != fmt) return -1;
   int64_t total = 0;
-  if (plan_fine(descs, count, blocks)) {
+  blocks.clear();
+  if (plan_fine(descs, count, fine)) {
     for (int i = 0; i < count; ++i) {
       descs[i].item_begin = (int32_t)total;
       total += descs[i].items;
@@ -1132,7 +1263,7 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks) {
   }
   if (total > INT32_MAX) return -1;
   const int grid = gemv_grid(total);
-  blocks.clear();
+  fine.clear();
   int p = 0;
   for (int b = 0; b < grid; ++b) {
     const int g0 = (int)(total * b / grid), g1 = (int)(total * (b + 1) / grid);
@@ -1146,21 +1277,24 @@ bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
   return K <= UG_MAX_K && M <= 64 && stages_x(wfmt, (int)M, (int)K);
 }
 
-hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const GemvBlock *blocks_dev, int32_t count,
+hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int32_t count,
                                int32_t grid, int32_t variant, hipStream_t st) {
   const bool fine = (variant >> 8) & 1, fused = (variant >> 9) & 1;
   const int fmt = (variant >> 4) & 15, mb = variant & 15;
   dim3 g(grid), b(kThreads);
   if (fine) {
+    const FineBlock *fb = static_cast<const FineBlock *>(table);
+    b = dim3(kFineThreads);
     if (fmt == UG_W_PACK5) {
-      if (fused) hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5, true>), g, b, 0, st, blocks_dev);
-      else hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5, false>), g, b, 0, st, blocks_dev);
+      if (fused) hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5, true>), g, b, 0, st, fb);
+      else hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5, false>), g, b, 0, st, fb);
     } else {
-      if (fused) hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8, true>), g, b, 0, st, blocks_dev);
-      else hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8, false>), g, b, 0, st, blocks_dev);
+      if (fused) hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8, true>), g, b, 0, st, fb);
+      else hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8, false>), g, b, 0, st, fb);
     }
     return hipGetLastError();
   }
+  const GemvBlock *blocks_dev = static_cast<const GemvBlock *>(table);
 #define UG_GROUPED(F, MBV) \
   hipLaunchKernelGGL((gemv_stream_grouped<F, MBV>), g, b, 0, st, plan_dev, blocks_dev, count)
   if (fmt == UG_W_PACK5) {
@@ -1196,18 +1330,23 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
   d.N = (int32_t)N;
   d.K = (int32_t)K;
   std::vector<GemvBlock> blocks;
-  const int variant = gemv_plan(&d, 1, blocks);
+  std::vector<FineBlock> fine;
+  const int variant = gemv_plan(&d, 1, blocks, fine);
   if (variant < 0) return hipErrorInvalidValue;
-  const int grid = (int)blocks.size();
-  dim3 g(grid), b(kThreads);
   if ((variant >> 8) & 1) {
-    const int ipb = blocks[0].i1 - blocks[0].i0;  // one problem: equal blocks, the last maybe short
+    // one problem: equal blocks, the last maybe shorter
+    FineTail last{};
+    std::copy(fine.back().wave_start, fine.back().wave_start + kFineWaves, last.wave_start);
+    last.items = (int32_t)((fine.back().shape >> 8) & 0xff);
+    dim3 g((unsigned)fine.size()), b(kFineThreads);
     if (wfmt == UG_W_PACK5)
-      hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5>), g, b, 0, st, d, ipb);
+      hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5>), g, b, 0, st, fine[0], last);
     else
-      hipLaunchKernelGGL((gemv_fine_single<UG_W_I8>), g, b, 0, st, d, ipb);
+      hipLaunchKernelGGL((gemv_fine_single<UG_W_I8>), g, b, 0, st, fine[0], last);
     return hipGetLastError();
   }
+  const int grid = (int)blocks.size();
+  dim3 g(grid), b(kThreads);
 #define UG_SINGLE(F, MBV) hipLaunchKernelGGL((gemv_stream_single<F, MBV>), g, b, 0, st, d)
   if (wfmt == UG_W_PACK5) {
     if (d.mb == 1) UG_SINGLE(UG_W_PACK5, 1);

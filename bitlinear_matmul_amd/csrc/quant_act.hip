@@ -19,42 +19,12 @@ __device__ inline float4 ld4(const float *p) {
   return *reinterpret_cast<const float4 *>(p);
 }
 
-// Quantize one float to an int8 code with the row scale s.
-__device__ inline int q8(float v, float s) { return rint_clamp(v / s, -127.0f, 127.0f); }
-
-// The same code without the division in almost every case.  q' = v * rs,
-// with rs = v_rcp_f32(s) (at most 1 ulp from 1/s), is within
-// 1.5 ulp + 0.5 ulp of the correctly rounded quotient fl(v/s): below 3.1e-5
-// wherever |v/s| < 128.  rint(fl(v/s)) can differ from rint(q') only if a
-// half-integer lies between them, so when q' is more than kTieBand from
-// every half-integer the codes agree; otherwise (about 1e-4 of the values)
-// the exact quotient is formed.  Above 127.5 both sides clamp to 127 (and
-// likewise below -127.5), NaN and infinities take the same clamp in both.
-// Used only for rows whose scale is a normal number of moderate size
-// (the caller checks), so that rs is finite and accurate.
-constexpr float kTieBand = 6.103515625e-05f;  // 2^-14, twice the bound above
-__device__ inline int q8_fast(float v, float s, float rs) {
-  const float q = v * rs;
-  const float r = rintf(q);
-  if (__builtin_expect(fabsf(q - r) > 0.5f - kTieBand, 0)) return q8(v, s);
-  return (int)fminf(fmaxf(r, -127.0f), 127.0f);
-}
-__device__ inline bool scale_fast_ok(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
+// q8 and q8x4 (the row codes with and without the division) come from
+// ug_internal.h, shared with the fused GEMV.
 
 __device__ inline void store_q4(int8_t *dst, int64_t k, int64_t K, float4 v, float s) {
   int a, b, c, d;
-  if (scale_fast_ok(s)) {
-    const float rs = __builtin_amdgcn_rcpf(s);
-    a = q8_fast(v.x, s, rs);
-    b = q8_fast(v.y, s, rs);
-    c = q8_fast(v.z, s, rs);
-    d = q8_fast(v.w, s, rs);
-  } else {
-    a = q8(v.x, s);
-    b = q8(v.y, s);
-    c = q8(v.z, s);
-    d = q8(v.w, s);
-  }
+  q8x4(v, s, a, b, c, d);
   if (k + 3 < K) {
     uint32_t packed = (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) |
                       ((uint32_t)(c & 0xff) << 16) | ((uint32_t)(d & 0xff) << 24);

@@ -59,7 +59,35 @@ struct GemvDesc {
   int32_t item_begin;  // first item of this problem in a grouped plan
 };
 
-constexpr int kGemvBlocks = 256;  // at most one GEMV block per CU
+constexpr int kGemvBlocks = 256;    // at most one GEMV block per CU
+constexpr int kGemvFineWaves = 8;   // waves of a fine-split GEMV block
+
+// One block of the fine GEMV split: every value its waves need, precomputed,
+// in 128 bytes that the planner places at a 128-byte boundary, so the
+// block reads all of it in one scalar round trip.
+struct FineBlock {
+  const void *x;       // fp32 activations (quantized in the launch) or x_q
+  const uint8_t *w;    // weight rows of ldw bytes
+  const float *beta;
+  float *y;            // [M][ldy], or null
+  int32_t *acc;        // [M][ldacc], or null
+  float *s;            // x_q given: its row scales; fp32 given: output or null
+  int8_t *xq_out;      // fp32 given: x_q output [M][ldxq_out], or null
+  int32_t ldx;         // bytes between activation rows
+  int32_t ldw, ldy, ldacc, ldxq_out;
+  float eps;
+  int32_t N, K;
+  int32_t i0;          // the block's first item (16 weight rows)
+  // M | items << 8 | S << 16: activation rows (1..16), items of the block
+  // (1..16), K steps (64 weight bytes of a row) per item (one dword: scalar
+  // loads fetch whole dwords)
+  uint32_t shape;
+  // wave w: byte 0 = item (from i0) and byte 1 = step of its first piece
+  // (a block orders its pieces step-major);
+  // byte 2 = row and byte 3 = chunk of its first activation tile
+  uint32_t wave_start[kGemvFineWaves];
+};
+static_assert(sizeof(FineBlock) == 128, "a fine block is one 128-byte fetch");
 
 // One block of a GEMV launch: problem p and its item range [i0, i1) (fine
 // split), or the first problem p and the plan-wide item range (stream split),
@@ -71,16 +99,21 @@ struct GemvBlock {
 
 // Plans a group of problems for the matrix-core GEMV: picks the split (fine
 // or stream), fills mb, items and item_begin of every descriptor and one
-// GemvBlock per block to launch.  Returns the variant
+// table entry per block to launch.  Returns the variant
 // (512 * fused + 256 * fine + 16 * wfmt + mb; fused: the fine split with fp32
 // activations), or -1 if the problems cannot share a launch.
-int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks);
+// The fine split fills `fine` (and leaves `blocks` empty), the stream split
+// fills `blocks`.
+int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
+              std::vector<FineBlock> &fine);
 // Blocks to launch for `total_items` items of the stream split.
 int gemv_grid(int64_t total_items);
 // Whether the activations of a problem fit the kernel's LDS staging area
 // (required when the launch quantizes fp32 activations).
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K);
-hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const GemvBlock *blocks_dev, int32_t count,
+// table: the plan's GemvBlock table (stream split) or FineBlock table (fine
+// split, 128-byte aligned).
+hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int32_t count,
                                int32_t grid, int32_t variant, hipStream_t st);
 hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const void *w, int wfmt, int64_t ldw, const float *beta,
@@ -145,6 +178,51 @@ __device__ inline int rint_clamp(float q, float lo, float hi) {
   float r = rintf(q);
   r = fminf(fmaxf(r, lo), hi);
   return (int)r;
+}
+
+// Activation code of v with the row scale s: clamp(rint(v / s), -127, 127).
+__device__ inline int q8(float v, float s) { return rint_clamp(v / s, -127.0f, 127.0f); }
+
+// The same code without the division in almost every case.  q' = v * rs,
+// with rs = v_rcp_f32(s) (at most 1 ulp from 1/s), is within
+// 1.5 ulp + 0.5 ulp of the correctly rounded quotient fl(v/s): below 3.1e-5
+// wherever |v/s| < 128.  rint(fl(v/s)) can differ from rint(q') only if a
+// half-integer lies between them, so when q' is more than kTieBand from
+// every half-integer the codes agree; otherwise (about 1e-4 of the values)
+// the exact quotient is formed.  Above 127.5 both sides clamp to 127 (and
+// likewise below -127.5), NaN and infinities take the same clamp in both.
+// Only for scales with scale_fast_ok(s), so that rs is finite and accurate.
+constexpr float kTieBand = 6.103515625e-05f;  // 2^-14, twice the bound above
+__device__ inline int q8_fast(float v, float s, float rs) {
+  const float q = v * rs;
+  const float r = rintf(q);
+  if (__builtin_expect(fabsf(q - r) > 0.5f - kTieBand, 0)) return q8(v, s);
+  return (int)fminf(fmaxf(r, -127.0f), 127.0f);
+}
+__device__ inline bool scale_fast_ok(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
+
+// The codes of four values with one scale: q8 of each, bit for bit.  The
+// fast products decide all four unless the scale is out of the fast range
+// or a product lies near a tie (q8_fast's test); then all four take the
+// exact quotient.  One branch per four codes instead of one per code.
+__device__ inline void q8x4(float4 v, float s, int &a, int &b, int &c, int &d) {
+  const float rs = __builtin_amdgcn_rcpf(s);
+  const float qa = v.x * rs, qb = v.y * rs, qc = v.z * rs, qd = v.w * rs;
+  const float ra = rintf(qa), rb = rintf(qb), rc = rintf(qc), rd = rintf(qd);
+  const float lim = 0.5f - kTieBand;
+  const bool exact = !scale_fast_ok(s) | (fabsf(qa - ra) > lim) | (fabsf(qb - rb) > lim) |
+                     (fabsf(qc - rc) > lim) | (fabsf(qd - rd) > lim);
+  if (__builtin_expect(exact, 0)) {
+    a = q8(v.x, s);
+    b = q8(v.y, s);
+    c = q8(v.z, s);
+    d = q8(v.w, s);
+  } else {
+    a = (int)fminf(fmaxf(ra, -127.0f), 127.0f);
+    b = (int)fminf(fmaxf(rb, -127.0f), 127.0f);
+    c = (int)fminf(fmaxf(rc, -127.0f), 127.0f);
+    d = (int)fminf(fmaxf(rd, -127.0f), 127.0f);
+  }
 }
 
 }  // namespace ug

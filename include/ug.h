@@ -236,8 +236,10 @@ size_t ug_gemv_plan_size(int32_t count);
  * Validates `count` host problems, lays out their tiling and copies the
  * plan to the device buffer `plan` (16-byte aligned, >= ug_gemv_plan_size).
  * A set-up call: it blocks until the plan is on the device.  The plan stays
- * valid as long as the buffers it names do; replaying the grouped launch
- * (for example from a captured HIP graph) needs no further host work.
+ * valid as long as the buffers it names do, at the address it was written
+ * to (its block table sits at a 128-byte boundary inside the buffer, so a
+ * copy elsewhere is not a plan); replaying the grouped launch (for example
+ * from a captured HIP graph) needs no further host work.
  */
 ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count,
                             void *plan, size_t plan_bytes,
