@@ -68,6 +68,10 @@ constexpr int kZero = kXsBytes;    // 80 zero bytes right after them
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every buffer used here
 constexpr int kFineItems = 16;   // fine split: items (16-row groups) per block
 constexpr int kFinePieces = 8;   // fine split: (item, step) pieces per wave
+// The short variant of the fine split: at most 4 pieces and (decode-sized
+// activations) 2 tiles per wave, so every wave issues half the loads.
+constexpr int kShortPieces = 4;
+constexpr int kShortTiles = 2;
 
 template <int FMT>
 struct Fmt;
@@ -256,30 +260,25 @@ struct Smem {
   float sm[64];                             // row scales s
 };
 
-// The decode table in 16-byte chunks, chunk c holding code c / 16
-// (256 bytes per code): wide, entries for lanes 2 (c % 16) and
-// 2 (c % 16) + 1 (mod 32); narrow, for lanes 4 (c % 16) .. +3.
-// Consecutive threads write consecutive chunks.
-template <int NT>
-constexpr int kTablePer = kTableBytes / 16 / NT;  // chunks per thread of an NT-thread block
-template <int NT>
-__device__ __forceinline__ void table_load(uint2 (&v)[kTablePer<NT>]) {
+// The decode table in 16-byte chunks, chunk j of code e at e * 16 + j
+// (256 bytes per code): wide, entries for lanes 2j and 2j + 1 (mod 32);
+// narrow, for lanes 4j .. 4j + 3.  Thread t fills the 8 chunks
+// (8 (t % 2) + i + e) % 16, i < 8, of code e = t / 2: one table load per
+// thread, and the lanes of an LDS pass write different chunk positions,
+// so all 64 banks.
+static_assert(kThreads == 512 && kFineThreads == 512, "two threads per table code");
+__device__ __forceinline__ uint2 table_load() { return kLut.v[threadIdx.x >> 1]; }
+template <bool WIDE, int FMT, int NW>
+__device__ __forceinline__ void table_store(Smem<FMT, NW> &sh, uint2 v) {
+  const int e = threadIdx.x >> 1, rot = 8 * (threadIdx.x & 1) + e;
+  const uint4 q = WIDE ? make_uint4(v.x, v.y, v.x, v.y) : make_uint4(v.x, v.x, v.x, v.x);
 #pragma unroll
-  for (int i = 0; i < kTablePer<NT>; ++i) v[i] = kLut.v[(threadIdx.x + NT * i) >> 4];
-}
-template <int NT, bool WIDE, int FMT, int NW>
-__device__ __forceinline__ void table_store(Smem<FMT, NW> &sh, const uint2 (&v)[kTablePer<NT>]) {
-#pragma unroll
-  for (int i = 0; i < kTablePer<NT>; ++i)
-    sh.lut[threadIdx.x + NT * i] = WIDE ? make_uint4(v[i].x, v[i].y, v[i].x, v[i].y)
-                                        : make_uint4(v[i].x, v[i].x, v[i].x, v[i].x);
+  for (int i = 0; i < 8; ++i) sh.lut[e * 16 + ((rot + i) & 15)] = q;
 }
 // The stream split's (narrow) table.
 template <int FMT>
 __device__ __forceinline__ void build_table(Smem<FMT> &sh) {
-  uint2 v[kTablePer<kThreads>];
-  table_load<kThreads>(v);
-  table_store<kThreads, false>(sh, v);
+  table_store<false>(sh, table_load());
 }
 
 // s = fl(fl(max|x| / 127) + eps) of row m from the per-wave maxima.
@@ -969,7 +968,7 @@ __device__ __forceinline__ void fine_flush(int *slots, int it, int M, const v4i 
 }
 
 // The block of descriptor b; ws = this wave's wave_start word; lut = this
-// thread's decode table chunks (table_load, five trits per byte).  Pieces
+// thread's decode table entry (table_load, five trits per byte).  Pieces
 // in step-major order, p = (step p / items, item p % items), of the block's
 // P = items * S: wave w takes [w P / 8, (w + 1) P / 8) and issues all their
 // weight loads at once (after the activation loads).  Consecutive pieces of
@@ -977,9 +976,10 @@ __device__ __forceinline__ void fine_flush(int *slots, int it, int M, const v4i 
 // from LDS once for all its items; each piece's sums go to its item's LDS
 // slot (flushed one piece later, when its MFMAs are done).  After a barrier
 // the block writes every item's outputs.
-template <int FMT, bool FUSED>
+template <int FMT, bool FUSED, bool SHORT>
 __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
-                                           const uint2 (&lut_chunks)[kTablePer<kFineThreads>]) {
+                                           uint2 lut_entry) {
+  constexpr int MP = SHORT ? kShortPieces : kFinePieces;  // weight loads per wave
   __shared__ Smem<FMT, kFineWaves> sh;
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   // the table's and the descriptor's loads (the caller's) leave first
@@ -998,7 +998,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(b.x, (uint32_t)(M * b.ldx));
   TileWalk walk{(wave * nt) >> kFineWaveShift, ((wave + 1) * nt) >> kFineWaveShift,
                 in_vgpr((ws >> 16) & 0xff), in_vgpr(ws >> 24), T};
-  constexpr int NB = kTileBatch<FUSED>;
+  constexpr int NB = SHORT ? kShortTiles : kTileBatch<FUSED>;
   TileBatch<NB> b0;
   uint4 x0[NB];
   next_batch(walk, b0);
@@ -1006,7 +1006,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
   load_batch<FUSED>(xr, b.ldx, K, b0, x0);
   __builtin_amdgcn_sched_barrier(0);  // the activation loads leave first
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(b.w, (uint32_t)(b.N * b.ldw));
-  uint4 wb[kFinePieces];
+  uint4 wb[MP];
   {
     // unsigned (wrapping) offsets: an offset that wraps into the buffer
     // reads real weights for a row past N, whose results are never stored;
@@ -1018,7 +1018,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
     uint32_t voff = (uint32_t)(b.i0 * 16 + (lane & 15)) * ldw + 16u * (lane >> 4) +
                     (uint32_t)it * item_step + 64u * ((ws >> 8) & 0xff);
 #pragma unroll
-    for (int j = 0; j < kFinePieces; ++j) {
+    for (int j = 0; j < MP; ++j) {
       wb[j] = buffer_load16(wr, p0 + j < p1 ? voff : kOOB);
       const bool wrap = ++it == items;
       it = wrap ? 0 : it;
@@ -1032,7 +1032,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
   // LDS set-up that needs nothing from the activations: the table (its
   // loads were issued first, so waiting for them waits for nothing later)
   // and zeroed slots
-  if (FMT == UG_W_PACK5) table_store<kFineThreads, true>(sh, lut_chunks);
+  if (FMT == UG_W_PACK5) table_store<true>(sh, lut_entry);
 #pragma unroll
   for (int i = 0; i < kFineItems * 64 / kFineThreads; ++i)
     reinterpret_cast<uint4 *>(sh.slots)[tid + i * kFineThreads] = make_uint4(0, 0, 0, 0);
@@ -1083,7 +1083,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
   v4i acc[2], prev[2];
   int it = ws & 0xff, st = (ws >> 8) & 0xff, xst = -1, prev_it = 0;
 #pragma unroll
-  for (int j = 0; j < kFinePieces; ++j) {
+  for (int j = 0; j < MP; ++j) {
     if (p0 + j < p1) {
       if (st != xst) {  // a new step: its fragments serve the following pieces too
         fine_xfrags<FMT>(sh.xs, xoff + st * Fmt<FMT>::kStepK, xf);
@@ -1122,10 +1122,9 @@ struct FineTail {
   int32_t items;
 };
 
-template <int FMT>
+template <int FMT, bool SHORT>
 __global__ __launch_bounds__(kFineThreads) void gemv_fine_single(const FineBlock b, const FineTail last) {
-  uint2 lut[kTablePer<kFineThreads>];
-  if (FMT == UG_W_PACK5) table_load<kFineThreads>(lut);
+  const uint2 lut = FMT == UG_W_PACK5 ? table_load() : uint2{0, 0};
   const bool is_last = blockIdx.x + 1 == gridDim.x;
   const int wave = uniform(threadIdx.x >> 6);
   // indexed in the argument segment itself (a modified copy would be
@@ -1134,15 +1133,15 @@ __global__ __launch_bounds__(kFineThreads) void gemv_fine_single(const FineBlock
   FineBlock mine = b;
   mine.i0 = blockIdx.x * ((b.shape >> 8) & 0xff);
   if (is_last) mine.shape = (b.shape & 0xffff00ffu) | ((uint32_t)last.items << 8);
-  fine_block<FMT, false>(mine, ws, lut);
+  fine_block<FMT, false, SHORT>(mine, ws, lut);
 }
 
-template <int FMT, bool FUSED>
+template <int FMT, bool FUSED, bool SHORT>
 __global__ __launch_bounds__(kFineThreads) void gemv_fine_grouped(const FineBlock *__restrict__ blocks) {
-  uint2 lut[kTablePer<kFineThreads>];  // the table's loads first: both fetches travel together
-  if (FMT == UG_W_PACK5) table_load<kFineThreads>(lut);
+  // the table's load first: both fetches travel together
+  const uint2 lut = FMT == UG_W_PACK5 ? table_load() : uint2{0, 0};
   const FineBlock b = blocks[blockIdx.x];
-  fine_block<FMT, FUSED>(b, blocks[blockIdx.x].wave_start[uniform(threadIdx.x >> 6)], lut);
+  fine_block<FMT, FUSED, SHORT>(b, blocks[blockIdx.x].wave_start[uniform(threadIdx.x >> 6)], lut);
 }
 
 // ---------------------------------------------------------------------------
@@ -1249,7 +1248,17 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
       descs[i].item_begin = (int32_t)total;
       total += descs[i].items;
     }
-    return (descs[0].x ? 512 : 0) + 256 + 16 * fmt + 1;
+    // the short variant when every wave of every block fits it
+    bool short_ok = true;
+    for (const FineBlock &f : fine) {
+      const int M = f.shape & 0xff, items = (f.shape >> 8) & 0xff, S = f.shape >> 16;
+      const int Kp = S * (fmt == UG_W_PACK5 ? 320 : 64);
+      const int T = descs[0].x ? (Kp + 255) >> 8 : (Kp + 1023) >> 10;
+      if ((items * S + kFineWaves - 1) / kFineWaves > kShortPieces ||
+          (M * T + kFineWaves - 1) / kFineWaves > kShortTiles)
+        short_ok = false;
+    }
+    return (short_ok ? 1024 : 0) + (descs[0].x ? 512 : 0) + 256 + 16 * fmt + 1;
   }
   const int mb = mb_of(descs[0].M);
   for (int i = 0; i < count; ++i) {
@@ -1279,19 +1288,21 @@ bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
 
 hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int32_t count,
                                int32_t grid, int32_t variant, hipStream_t st) {
-  const bool fine = (variant >> 8) & 1, fused = (variant >> 9) & 1;
+  const bool fine = (variant >> 8) & 1, fused = (variant >> 9) & 1, shrt = (variant >> 10) & 1;
   const int fmt = (variant >> 4) & 15, mb = variant & 15;
   dim3 g(grid), b(kThreads);
   if (fine) {
     const FineBlock *fb = static_cast<const FineBlock *>(table);
     b = dim3(kFineThreads);
+#define UG_FINE(F, FU, SH) hipLaunchKernelGGL((gemv_fine_grouped<F, FU, SH>), g, b, 0, st, fb)
     if (fmt == UG_W_PACK5) {
-      if (fused) hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5, true>), g, b, 0, st, fb);
-      else hipLaunchKernelGGL((gemv_fine_grouped<UG_W_PACK5, false>), g, b, 0, st, fb);
+      if (fused) { if (shrt) UG_FINE(UG_W_PACK5, true, true); else UG_FINE(UG_W_PACK5, true, false); }
+      else { if (shrt) UG_FINE(UG_W_PACK5, false, true); else UG_FINE(UG_W_PACK5, false, false); }
     } else {
-      if (fused) hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8, true>), g, b, 0, st, fb);
-      else hipLaunchKernelGGL((gemv_fine_grouped<UG_W_I8, false>), g, b, 0, st, fb);
+      if (fused) { if (shrt) UG_FINE(UG_W_I8, true, true); else UG_FINE(UG_W_I8, true, false); }
+      else { if (shrt) UG_FINE(UG_W_I8, false, true); else UG_FINE(UG_W_I8, false, false); }
     }
+#undef UG_FINE
     return hipGetLastError();
   }
   const GemvBlock *blocks_dev = static_cast<const GemvBlock *>(table);
@@ -1339,10 +1350,14 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
     std::copy(fine.back().wave_start, fine.back().wave_start + kFineWaves, last.wave_start);
     last.items = (int32_t)((fine.back().shape >> 8) & 0xff);
     dim3 g((unsigned)fine.size()), b(kFineThreads);
-    if (wfmt == UG_W_PACK5)
-      hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5>), g, b, 0, st, fine[0], last);
-    else
-      hipLaunchKernelGGL((gemv_fine_single<UG_W_I8>), g, b, 0, st, fine[0], last);
+    const bool shrt = (variant >> 10) & 1;
+    if (wfmt == UG_W_PACK5) {
+      if (shrt) hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5, true>), g, b, 0, st, fine[0], last);
+      else hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5, false>), g, b, 0, st, fine[0], last);
+    } else {
+      if (shrt) hipLaunchKernelGGL((gemv_fine_single<UG_W_I8, true>), g, b, 0, st, fine[0], last);
+      else hipLaunchKernelGGL((gemv_fine_single<UG_W_I8, false>), g, b, 0, st, fine[0], last);
+    }
     return hipGetLastError();
   }
   const int grid = (int)blocks.size();

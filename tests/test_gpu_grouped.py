@@ -109,6 +109,47 @@ def test_grouped_parity(dev, gi, fused):
         assert_y_close(host(p["y"]), y_r, "y %d" % i)
 
 
+# (M, N, K, fused, short): one problem each; plan.info.variant bit 8 = fine
+# split, bit 10 = its short variant (at most 4 pieces and 2 activation tiles
+# per wave).
+FINE_VARIANTS = [
+    (1, 2560, 2560, True, True),     # decode-sized
+    (4, 1000, 384, True, True),      # 12 fp32 tiles: 2 per wave
+    (1, 16, 20000, False, False),    # one item of 63 steps: 8 pieces per wave
+    (16, 6912, 2560, False, False),  # 48 x_q tiles: 6 per wave
+    (16, 512, 2560, True, False),    # 160 fp32 tiles: 20 per wave (3 batches)
+]
+
+
+@pytest.mark.parametrize("ci", range(len(FINE_VARIANTS)))
+def test_fine_variants(dev, ci):
+    M, N, K, fused, short = FINE_VARIANTS[ci]
+    _case("fine variant", M, N, K, fused, short)
+    rng = np.random.default_rng([303, ci])
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    beta = np.float32(0.02)
+    xq_r, s_r = oracle.quant_act(x)
+    p = dict(w=pitched(oracle.pack_trits(wq)[0]), wfmt=ug.UG_W_PACK5, beta=scalar_dev(beta),
+             K=K, y=ug.empty_pitched(M, N, torch.float32, dev),
+             acc=ug.empty_pitched(M, N, torch.int32, dev))
+    if fused:
+        p.update(x=pitched(x), xq=ug.empty_pitched(M, K, torch.int8, dev),
+                 s=torch.empty(M, dtype=torch.float32, device=dev))
+    else:
+        p.update(xq=pitched(xq_r), s=vec(s_r))
+    plan = ug.ug_gemv_plan_init([p])
+    assert (plan.info.variant >> 8) & 1 == 1, "fine split"
+    assert bool((plan.info.variant >> 10) & 1) == short, "variant %#x" % plan.info.variant
+    ug.ug_bitlinear_gemv_grouped(plan)
+    if fused:
+        assert_bits_equal(host(p["xq"]), xq_r, "x_q")
+        assert_bits_equal(host(p["s"]), s_r, "s")
+    acc_r = oracle.matmul_i32(xq_r, wq)
+    assert_bits_equal(host(p["acc"]), acc_r, "acc")
+    assert_y_close(host(p["y"]), oracle.epilogue(acc_r, s_r, beta), "y")
+
+
 def test_grouped_many_problems_multi_item_blocks(dev):
     """A group large enough that every block walks several items."""
     rng = np.random.default_rng(301)
