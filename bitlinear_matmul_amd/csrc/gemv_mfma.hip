@@ -155,6 +155,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// The weights: each byte is read once per launch, so the loads carry the
+// non-temporal hint (aux bit 1): the L2 keeps them only briefly.
+__device__ __forceinline__ uint4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
@@ -1019,7 +1024,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
                     (uint32_t)it * item_step + 64u * ((ws >> 8) & 0xff);
 #pragma unroll
     for (int j = 0; j < MP; ++j) {
-      wb[j] = buffer_load16(wr, p0 + j < p1 ? voff : kOOB);
+      wb[j] = buffer_load16_stream(wr, p0 + j < p1 ? voff : kOOB);
       const bool wrap = ++it == items;
       it = wrap ? 0 : it;
       voff += wrap ? wrap_step : item_step;
