@@ -70,11 +70,11 @@ def parse():
 # Valid only for the kernel sources they were taken on: `src_sha` is the
 # SHA-256 of the kernel's source file; any other source reports null.
 TRAFFIC = {
-    # profiles/gemv_fine_grouped_decode_stack.md: 2105.6 KiB fetched x 1.9997,
+    # profiles/gemv_fine_grouped_decode_stack.md: 2014.5 KiB fetched x 1.9997,
     # 146.4 KiB written x 1.0000
     "decode_stack": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
-                         src_sha="af54f1408d60cc969bb186a8b73ea40b3a3cad5854ea1e4d32bdc30cf139fac3",
-                         bytes_per_launch=4461598),
+                         src_sha="e5409d63276e96404888ddb6e492d3f2dae922e9298d14557197d758e1f852c3",
+                         bytes_per_launch=4274961),
     # profiles/gemm_i8_large_prefill.md: mean of both shapes, 60190.6 KiB
     # fetched x 1.9997, 75776.0 KiB written x 1.0000
     "prefill": dict(src="bitlinear_matmul_amd/csrc/gemm.hip",
@@ -233,7 +233,7 @@ def run_decode_stack(args, torch, ug, inputs):
                        "us_per_token_pass": ms * 1e3 / steps,
                        "hot_us_per_token_pass": ms_hot * 1e3 / steps,
                        "hot_weight_GBps": per_pass_bytes * steps / (ms_hot / 1e3) / 1e9},
-               roofline=dict(bound="hbm", kernel="gemv_fine_grouped<PACK5, fused>",
+               roofline=dict(bound="hbm", kernel="gemv_fine_grouped<PACK5, fused, short>",
                              achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("decode_stack"),
                              avg_launch_us=avg_launch_s * 1e6, alg_bytes_per_launch=alg))
