@@ -163,10 +163,26 @@ __device__ inline float fold256(float v, float *lds) {
   return r;
 }
 
+// Max over the 64 lanes of a wave, returned to every lane.  Registers only
+// (cross-lane shuffles through ds_bpermute would be LDS round trips, queued
+// behind whatever else the block has sent to LDS): DPP butterflies give
+// every lane its 16-lane row's max, then the four row maxima are read out.
+template <int CTRL>
+__device__ inline float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xf, 0xf, false));
+}
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) v = fmaxf(v, __shfl_xor(v, h, 64));
-  return v;
+  v = fmaxf(v, dpp_f32<0xb1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4e>(v));   // quad_perm [2,3,0,1]: quad max
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror: max of 8
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror: max of the 16-lane row
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ inline int wave_sum_i32(int v) {
