@@ -267,18 +267,36 @@ struct Smem {
 
 // The decode table in 16-byte chunks, chunk j of code e at e * 16 + j
 // (256 bytes per code): wide, entries for lanes 2j and 2j + 1 (mod 32);
-// narrow, for lanes 4j .. 4j + 3.  Thread t fills the 8 chunks
-// (8 (t % 2) + i + e) % 16, i < 8, of code e = t / 2: one table load per
-// thread, and the lanes of an LDS pass write different chunk positions,
-// so all 64 banks.
-static_assert(kThreads == 512 && kFineThreads == 512, "two threads per table code");
-__device__ __forceinline__ uint2 table_load() { return kLut.v[threadIdx.x >> 1]; }
+// narrow, for lanes 4j .. 4j + 3.  Thread t writes chunks t + 512 i, i < 8
+// (consecutive lanes, consecutive chunks: no bank conflicts), i.e. code
+// 4 (w + 8 i) + r for wave w and 16-lane row r.  One table load per thread:
+// lane p of row r loads the code its row writes at step p % 8, and at step
+// i every lane of the row takes lane i's value (DPP row broadcast).
+static_assert(kThreads == 512 && kFineThreads == 512, "8 waves write the table");
+__device__ __forceinline__ uint2 table_load() {
+  const int t = threadIdx.x;
+  return kLut.v[4 * ((t >> 6) + 8 * (t & 7)) + ((t >> 4) & 3)];
+}
+template <int I>
+__device__ __forceinline__ uint32_t row_broadcast(uint32_t v) {  // lane I of each 16-lane row
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + I, 0xf, 0xf, false);
+}
+template <bool WIDE, int I, int FMT, int NW>
+__device__ __forceinline__ void table_store_step(Smem<FMT, NW> &sh, uint2 v) {
+  const uint32_t lo = row_broadcast<I>(v.x), hi = row_broadcast<I>(v.y);
+  sh.lut[threadIdx.x + 512 * I] = WIDE ? make_uint4(lo, hi, lo, hi) : make_uint4(lo, lo, lo, lo);
+}
+// (with every lane active: the broadcasts read other lanes)
 template <bool WIDE, int FMT, int NW>
 __device__ __forceinline__ void table_store(Smem<FMT, NW> &sh, uint2 v) {
-  const int e = threadIdx.x >> 1, rot = 8 * (threadIdx.x & 1) + e;
-  const uint4 q = WIDE ? make_uint4(v.x, v.y, v.x, v.y) : make_uint4(v.x, v.x, v.x, v.x);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sh.lut[e * 16 + ((rot + i) & 15)] = q;
+  table_store_step<WIDE, 0>(sh, v);
+  table_store_step<WIDE, 1>(sh, v);
+  table_store_step<WIDE, 2>(sh, v);
+  table_store_step<WIDE, 3>(sh, v);
+  table_store_step<WIDE, 4>(sh, v);
+  table_store_step<WIDE, 5>(sh, v);
+  table_store_step<WIDE, 6>(sh, v);
+  table_store_step<WIDE, 7>(sh, v);
 }
 // The stream split's (narrow) table.
 template <int FMT>
