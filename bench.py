@@ -73,8 +73,8 @@ TRAFFIC = {
     # profiles/gemv_fine_grouped_decode_stack.md: 2014.5 KiB fetched x 1.9997,
     # 146.4 KiB written x 1.0000
     "decode_stack": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
-                         src_sha="e5409d63276e96404888ddb6e492d3f2dae922e9298d14557197d758e1f852c3",
-                         bytes_per_launch=4274961),
+                         src_sha="1a9dc3fa26df027211cf44664a3ce20f0a4fc167751eddb7d2e1c562f383d49f",
+                         bytes_per_launch=4274936),
     # profiles/gemm_i8_large_prefill.md: mean of both shapes, 60190.6 KiB
     # fetched x 1.9997, 75776.0 KiB written x 1.0000
     "prefill": dict(src="bitlinear_matmul_amd/csrc/gemm.hip",
