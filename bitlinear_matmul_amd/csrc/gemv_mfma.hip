@@ -94,7 +94,7 @@ struct Cfg {
   static constexpr int RGW = FINE ? 1 : 2;
   // steps per unit (three units of weights are in flight per wave)
   static constexpr int SC =
-      FINE ? 1 : (FMT == UG_W_PACK5 ? (MB == 1 ? 4 : (MB == 2 ? 2 : 1)) : (MB == 4 ? 2 : 4));
+      FINE ? 1 : (FMT == UG_W_PACK5 ? (MB == 4 ? 1 : 2) : (MB == 4 ? 2 : 4));
   // independent MFMA chains per output tile
   static constexpr int NACC = FMT == UG_W_PACK5 && MB == 4 ? 1 : 2;
 };
@@ -104,6 +104,13 @@ __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int K) {
 }
 __host__ __device__ __forceinline__ int steps_of(int fmt, int K) {
   return (row_bytes_of(fmt, K) + 63) / 64;
+}
+__host__ __device__ __forceinline__ int rgw_of(int fmt, int mb) {  // row groups per stream item
+  return fmt == UG_W_PACK5
+             ? (mb == 1 ? Cfg<UG_W_PACK5, 1, false>::RGW
+                        : (mb == 2 ? Cfg<UG_W_PACK5, 2, false>::RGW : Cfg<UG_W_PACK5, 4, false>::RGW))
+             : (mb == 1 ? Cfg<UG_W_I8, 1, false>::RGW
+                        : (mb == 2 ? Cfg<UG_W_I8, 2, false>::RGW : Cfg<UG_W_I8, 4, false>::RGW));
 }
 __host__ __device__ __forceinline__ int sc_of(int fmt, int mb) {
   return fmt == UG_W_PACK5
@@ -1288,8 +1295,8 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
     GemvDesc &d = descs[i];
     d.mb = mb_of(d.M);
     if (d.mb != mb) return -1;
-    const int rg = (d.N + 15) / 16;
-    d.items = (rg + 1) / 2;  // two row groups per item
+    const int rg = (d.N + 15) / 16, rgw = rgw_of(d.wfmt, d.mb);
+    d.items = (rg + rgw - 1) / rgw;  // rgw row groups per item
     d.item_begin = (int32_t)total;
     total += d.items;
   }

@@ -199,7 +199,7 @@ ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s,
  * UG_ERR_UNSUPPORTED.  Kp = S * U * ceil(ceil(B / 64) / U) with B the packed
  * row length (ceil(K/5) for UG_W_PACK5, K for UG_W_I8), S = 320 (UG_W_PACK5)
  * or 64 (UG_W_I8), and U the steps per unit of the row class: UG_W_PACK5
- * U = 4, 2, 1 for M <= 16, 17..32, 33..64; UG_W_I8 U = 4, 4, 2.  Weights of N * ldw >= 2^31 bytes or
+ * U = 2, 2, 1 for M <= 16, 17..32, 33..64; UG_W_I8 U = 4, 4, 2.  Weights of N * ldw >= 2^31 bytes or
  * activations of M * ldxq >= 2^31 bytes are UG_ERR_UNSUPPORTED (32-bit
  * offsets), here and in ug_bitlinear_gemv.
  */

@@ -53,7 +53,7 @@ def test_decode_stack_one_launch_fused_quant(dev):
 def _staged_kp(wfmt, M, K):
     rb = -(-K // 5) if wfmt == ug.UG_W_PACK5 else K
     cls = 0 if M <= 16 else (1 if M <= 32 else 2)
-    u = (4, 2, 1)[cls] if wfmt == ug.UG_W_PACK5 else (4, 4, 2)[cls]
+    u = (2, 2, 1)[cls] if wfmt == ug.UG_W_PACK5 else (4, 4, 2)[cls]
     steps = -(-rb // 64)
     return (320 if wfmt == ug.UG_W_PACK5 else 64) * u * -(-steps // u)
 
