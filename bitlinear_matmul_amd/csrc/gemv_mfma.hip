@@ -758,6 +758,236 @@ struct ItemLoop {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Chunked stream: for launches with problems whose activation rows do not
+// fit the staging area (x_q input; M * Kp > 64 KB), where the stream split
+// would read every activation fragment from memory once per piece.  Waves
+// take a problem's items in rounds (wave w: item i0 + w + 8 r); each round
+// walks K in chunks of CH steps.  The block stages a chunk's activations
+// (all rows, permuted like the staged rows) once in LDS for its 8 waves,
+// loading the next chunk's activations and weights while it computes the
+// current one.  Its own kernels, so its registers are its own.
+template <int FMT, int MB>
+struct Chunk {
+  static constexpr int RG = Cfg<FMT, MB, false>::RGW;  // row groups per item
+  static constexpr int CH = FMT == UG_W_PACK5 && MB == 4 ? 2 : 4;  // steps per chunk
+  static constexpr int ROWS = 16 * MB;
+  static constexpr int SB = FMT == UG_W_PACK5 ? 320 : 64;  // staged bytes per row and step
+  static constexpr int CB = CH * SB;                        // staged bytes per row and chunk
+  static constexpr int UB = FMT == UG_W_PACK5 ? 80 : 16;    // staging unit (bytes)
+  static constexpr int UPR = CB / UB;                        // units per row and chunk
+  static constexpr int NU = (ROWS * UPR + kThreads - 1) / kThreads;  // units per thread
+  static constexpr int UV = UB / 16;                         // 16-byte loads per unit
+  static_assert(ROWS * CB <= kXsBytes, "a chunk fits the staging area");
+};
+
+// Loads (issue) this thread's staging units of chunk c: unit u = tid + 512 i
+// is row u / UPR, unit u % UPR of the chunk (K positions from c * CH * step).
+template <int FMT, int MB>
+__device__ __forceinline__ void chunk_load(const GemvDesc &d, __amdgpu_buffer_rsrc_t xr, int c,
+                                           uint4 (&v)[Chunk<FMT, MB>::NU][Chunk<FMT, MB>::UV]) {
+  using C = Chunk<FMT, MB>;
+#pragma unroll
+  for (int i = 0; i < C::NU; ++i) {
+    const int u = threadIdx.x + kThreads * i, m = u / C::UPR;
+    const int k = c * C::CB + (u - m * C::UPR) * C::UB;  // K position (int8 byte) of the unit
+#pragma unroll
+    for (int j = 0; j < C::UV; ++j) {
+      const int kj = k + 16 * j;
+      // a 16-byte load at kj < K is inside the row (ldxq >= round_up(K, 16))
+      v[i][j] = buffer_load16(xr, m < d.M && kj < d.K ? (uint32_t)(m * (int)d.ldxq + kj) : kOOB);
+    }
+  }
+}
+
+// Stores the loaded units into the staged chunk: bytes past K zeroed,
+// five trits per byte: every 80-position window permuted as the weights
+// decode.
+template <int FMT, int MB>
+__device__ __forceinline__ void chunk_store(const GemvDesc &d, int8_t *xs, int c,
+                                            const uint4 (&v)[Chunk<FMT, MB>::NU][Chunk<FMT, MB>::UV]) {
+  using C = Chunk<FMT, MB>;
+#pragma unroll
+  for (int i = 0; i < C::NU; ++i) {
+    const int u = threadIdx.x + kThreads * i, m = u / C::UPR, w = u - m * C::UPR;
+    if (m < d.M) {
+      const int k = c * C::CB + w * C::UB;
+      uint32_t X[4 * C::UV];
+#pragma unroll
+      for (int j = 0; j < C::UV; ++j) {
+        const uint32_t w4[4] = {v[i][j].x, v[i][j].y, v[i][j].z, v[i][j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kb = d.K - k - 16 * j - 4 * e;  // bytes of this dword inside the row
+          X[4 * j + e] = w4[e] & (kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb)))));
+        }
+      }
+      uint4 *dst = reinterpret_cast<uint4 *>(xs + m * C::CB + w * C::UB);
+      if (FMT == UG_W_PACK5) {
+        uint32_t F[20];
+        permute80(reinterpret_cast<const uint32_t(&)[20]>(X), F);
+#pragma unroll
+        for (int j = 0; j < 5; ++j) dst[j] = make_uint4(F[4 * j], F[4 * j + 1], F[4 * j + 2], F[4 * j + 3]);
+      } else {
+        dst[0] = make_uint4(X[0], X[1], X[2], X[3]);
+      }
+    }
+  }
+}
+
+template <int FMT, int MB>
+__device__ __forceinline__ void chunked_items(const GemvDesc &d, Smem<FMT> &sh, int i0, int i1) {
+  using C = Chunk<FMT, MB>;
+  constexpr int RG = C::RG, CH = C::CH, F1 = Fmt<FMT>::kFrag;
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, q = lane >> 4;
+  const int S = steps_of(FMT, d.K), NCH = (S + CH - 1) / CH;
+  const int rounds = (i1 - i0 + kWaves - 1) / kWaves, T = rounds * NCH;
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(d.w, (uint32_t)((int64_t)d.N * d.ldw));
+  const float beta = gp(d.beta)[0];
+  const char *lut = reinterpret_cast<const char *>(sh.lut);
+  const uint32_t lr4 = 4u * (uint32_t)lane;
+  // this lane's staged row (rows past M read row M-1: MFMA row m depends
+  // only on input row m, and rows past M are never stored)
+  int xrow[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) xrow[b] = min(16 * b + (lane & 15), d.M - 1) * C::CB;
+
+  // weights of (round r, chunk c): row group g of the wave's item, the
+  // chunk's steps; steps past S and items past i1 read nothing
+  auto wload = [&](int r, int c, uint4 (&w)[RG][CH]) __attribute__((always_inline)) {
+    const int item = i0 + wave + kWaves * r;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const uint32_t n = (uint32_t)((item * RG + g) * 16 + (lane & 15));
+      const uint32_t base = n * (uint32_t)d.ldw + 16u * q;
+#pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        const int st = c * CH + s;
+        w[g][s] = buffer_load16(wr, item < i1 && st < S ? base + 64u * st : kOOB);
+      }
+    }
+  };
+
+  uint4 xv[C::NU][C::UV];
+  uint4 wcur[RG][CH], wnext[RG][CH];
+  chunk_load<FMT, MB>(d, xr, 0, xv);
+  wload(0, 0, wcur);
+  v4i acc[RG][MB];
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[g][b] = v4i{0, 0, 0, 0};
+  int r = 0, c = 0;
+  for (int t = 0; t < T; ++t) {
+    __syncthreads();  // the previous chunk's reads of the staging area are done
+    chunk_store<FMT, MB>(d, sh.xs, c, xv);
+    const int c1 = c + 1 == NCH ? 0 : c + 1, r1 = c + 1 == NCH ? r + 1 : r;
+    if (t + 1 < T) {  // the next chunk's activations and weights travel meanwhile
+      chunk_load<FMT, MB>(d, xr, c1, xv);
+      wload(r1, c1, wnext);
+    }
+    __syncthreads();  // the staged chunk is complete
+    if (i0 + wave + kWaves * r < i1) {
+#pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        if (c * CH + s < S) {
+          uint32_t tdec[RG][4 * F1];
+#pragma unroll
+          for (int g = 0; g < RG; ++g) {
+            if (FMT == UG_W_PACK5) {
+              decode4_narrow(wcur[g][s].x, lut, lr4, tdec[g], tdec[g][16]);
+              decode4_narrow(wcur[g][s].y, lut, lr4, tdec[g] + 4, tdec[g][17]);
+              decode4_narrow(wcur[g][s].z, lut, lr4, tdec[g] + 8, tdec[g][18]);
+              decode4_narrow(wcur[g][s].w, lut, lr4, tdec[g] + 12, tdec[g][19]);
+            } else {
+              tdec[g][0] = wcur[g][s].x;
+              tdec[g][1] = wcur[g][s].y;
+              tdec[g][2] = wcur[g][s].z;
+              tdec[g][3] = wcur[g][s].w;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < F1; ++j) {
+            v4i xf[MB];
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+              xf[b] = *reinterpret_cast<const v4i *>(sh.xs + xrow[b] + s * C::SB + q * Fmt<FMT>::kLaneK + 16 * j);
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+              const v4i B = {(int)tdec[g][4 * j], (int)tdec[g][4 * j + 1], (int)tdec[g][4 * j + 2],
+                             (int)tdec[g][4 * j + 3]};
+#pragma unroll
+              for (int b = 0; b < MB; ++b)
+                acc[g][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[b], B, acc[g][b], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (c + 1 == NCH) {  // the item is complete: lane (n, q) holds rows 16 b + 4 q + e of column n
+        const int item = i0 + wave + kWaves * r;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+          const int n = (item * RG + g) * 16 + (lane & 15);
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = 16 * b + 4 * q + e;
+              if (n < d.N && m < d.M) {
+                const int val = acc[g][b][e];
+                if (d.acc) gp(d.acc)[(int64_t)m * d.ldacc + n] = val;
+                if (d.y) gp(d.y)[(int64_t)m * d.ldy + n] = (float)val * (sh.sm[m] * beta);
+              }
+            }
+            acc[g][b] = v4i{0, 0, 0, 0};
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+      for (int s = 0; s < CH; ++s) wcur[g][s] = wnext[g][s];
+    r = r1;
+    c = c1;
+  }
+}
+
+// The block's global items [g0, g1) of the plan, problem by problem.
+template <int FMT, int MB>
+__device__ __forceinline__ void chunked_block(const GemvDesc *plan, int count, int p, int g0,
+                                              int g1) {
+  __shared__ Smem<FMT> sh;
+  bool first = true;
+  for (int g = g0; g < g1 && p < count; ++p) {
+    const GemvDesc d = plan[p];
+    const int e = min(g1, d.item_begin + d.items);
+    if (e <= g) continue;
+    XBatch xb;  // unused
+    if (!first) __syncthreads();  // the previous problem is done with the staging area
+    setup_finish<FMT, false>(d, sh, false, 0, first, false, xb);  // table, scales
+    first = false;
+    chunked_items<FMT, MB>(d, sh, g - d.item_begin, e - d.item_begin);
+    g = e;
+  }
+}
+
+template <int FMT, int MB>
+__global__ __launch_bounds__(kThreads) void gemv_chunked_single(GemvDesc d) {
+  const int64_t T = d.items;
+  const int g0 = (int)(T * blockIdx.x / gridDim.x), g1 = (int)(T * (blockIdx.x + 1) / gridDim.x);
+  if (g0 < g1) chunked_block<FMT, MB>(&d, 1, 0, g0, g1);
+}
+
+template <int FMT, int MB>
+__global__ __launch_bounds__(kThreads) void gemv_chunked_grouped(const GemvDesc *__restrict__ plan,
+                                                                 const GemvBlock *__restrict__ blocks,
+                                                                 int count) {
+  const GemvBlock bl = blocks[blockIdx.x];
+  if (bl.i0 < bl.i1) chunked_block<FMT, MB>(plan, count, bl.p, bl.i0, bl.i1);
+}
+
 // The block takes the global items [g0, g1) of the plan (problem p holds
 // item g0; problem q owns [item_begin, +items)), crossing into the next
 // problem when its range does.
@@ -1291,10 +1521,12 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
     return (short_ok ? 1024 : 0) + (descs[0].x ? 512 : 0) + 256 + 16 * fmt + 1;
   }
   const int mb = mb_of(descs[0].M);
+  bool chunked = false;  // some problem's activations do not fit the staging area
   for (int i = 0; i < count; ++i) {
     GemvDesc &d = descs[i];
     d.mb = mb_of(d.M);
     if (d.mb != mb) return -1;
+    if (!stages_x(d.wfmt, d.M, d.K)) chunked = true;
     const int rg = (d.N + 15) / 16, rgw = rgw_of(d.wfmt, d.mb);
     d.items = (rg + rgw - 1) / rgw;  // rgw row groups per item
     d.item_begin = (int32_t)total;
@@ -1309,7 +1541,7 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
     while (p + 1 < count && descs[p + 1].item_begin <= g0) ++p;
     blocks.push_back(GemvBlock{descs[p], p, g0, g1, 0});
   }
-  return 16 * fmt + mb;
+  return (chunked ? 2048 : 0) + 16 * fmt + mb;
 }
 
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
@@ -1336,6 +1568,21 @@ hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int3
     return hipGetLastError();
   }
   const GemvBlock *blocks_dev = static_cast<const GemvBlock *>(table);
+  if ((variant >> 11) & 1) {
+#define UG_CHUNKED(F, MBV) \
+  hipLaunchKernelGGL((gemv_chunked_grouped<F, MBV>), g, b, 0, st, plan_dev, blocks_dev, count)
+    if (fmt == UG_W_PACK5) {
+      if (mb == 1) UG_CHUNKED(UG_W_PACK5, 1);
+      else if (mb == 2) UG_CHUNKED(UG_W_PACK5, 2);
+      else UG_CHUNKED(UG_W_PACK5, 4);
+    } else {
+      if (mb == 1) UG_CHUNKED(UG_W_I8, 1);
+      else if (mb == 2) UG_CHUNKED(UG_W_I8, 2);
+      else UG_CHUNKED(UG_W_I8, 4);
+    }
+#undef UG_CHUNKED
+    return hipGetLastError();
+  }
 #define UG_GROUPED(F, MBV) \
   hipLaunchKernelGGL((gemv_stream_grouped<F, MBV>), g, b, 0, st, plan_dev, blocks_dev, count)
   if (fmt == UG_W_PACK5) {
@@ -1392,6 +1639,20 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
   }
   const int grid = (int)blocks.size();
   dim3 g(grid), b(kThreads);
+  if ((variant >> 11) & 1) {
+#define UG_CHUNKED(F, MBV) hipLaunchKernelGGL((gemv_chunked_single<F, MBV>), g, b, 0, st, d)
+    if (wfmt == UG_W_PACK5) {
+      if (d.mb == 1) UG_CHUNKED(UG_W_PACK5, 1);
+      else if (d.mb == 2) UG_CHUNKED(UG_W_PACK5, 2);
+      else UG_CHUNKED(UG_W_PACK5, 4);
+    } else {
+      if (d.mb == 1) UG_CHUNKED(UG_W_I8, 1);
+      else if (d.mb == 2) UG_CHUNKED(UG_W_I8, 2);
+      else UG_CHUNKED(UG_W_I8, 4);
+    }
+#undef UG_CHUNKED
+    return hipGetLastError();
+  }
 #define UG_SINGLE(F, MBV) hipLaunchKernelGGL((gemv_stream_single<F, MBV>), g, b, 0, st, d)
   if (wfmt == UG_W_PACK5) {
     if (d.mb == 1) UG_SINGLE(UG_W_PACK5, 1);

@@ -150,6 +150,45 @@ def test_fine_variants(dev, ci):
     assert_y_close(host(p["y"]), oracle.epilogue(acc_r, s_r, beta), "y")
 
 
+# (wfmt, M, list of (N, K)): groups with a problem whose activation rows do
+# not fit the 64 KB staging area, so the launch stages them chunk by chunk
+# (plan.info.variant bit 11); every row class and both weight formats, ragged
+# N and K, a staged problem in the same launch.
+CHUNKED = [
+    (ug.UG_W_PACK5, 1, [(300, 70001), (100, 640)]),
+    (ug.UG_W_PACK5, 16, [(777, 6912), (50, 333)]),
+    (ug.UG_W_PACK5, 17, [(600, 5000), (33, 4321)]),
+    (ug.UG_W_PACK5, 64, [(513, 2560), (40, 1283)]),
+    (ug.UG_W_I8, 16, [(300, 5000)]),
+    (ug.UG_W_I8, 64, [(200, 1100), (31, 77)]),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CHUNKED)))
+def test_chunked_parity(dev, ci):
+    wfmt, M, shapes = CHUNKED[ci]
+    _case("chunked", ci, wfmt, M)
+    rng = np.random.default_rng([304, ci])
+    probs, refs = [], []
+    for (N, K) in shapes:
+        x = rng.standard_normal((M, K), dtype=np.float32)
+        wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        beta = np.float32(0.01 + 0.002 * len(probs))
+        xq_r, s_r = oracle.quant_act(x)
+        w = pitched(oracle.pack_trits(wq)[0]) if wfmt == ug.UG_W_PACK5 else pitched(wq)
+        probs.append(dict(w=w, wfmt=wfmt, beta=scalar_dev(beta), K=K, xq=pitched(xq_r), s=vec(s_r),
+                          y=ug.empty_pitched(M, N, torch.float32, dev),
+                          acc=ug.empty_pitched(M, N, torch.int32, dev)))
+        acc_r = oracle.matmul_i32(xq_r, wq)
+        refs.append((acc_r, oracle.epilogue(acc_r, s_r, beta)))
+    plan = ug.ug_gemv_plan_init(probs)
+    assert (plan.info.variant >> 11) & 1 == 1, "variant %#x" % plan.info.variant
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for i, (p, (acc_r, y_r)) in enumerate(zip(probs, refs)):
+        assert_bits_equal(host(p["acc"]), acc_r, "acc %d" % i)
+        assert_y_close(host(p["y"]), y_r, "y %d" % i)
+
+
 def test_grouped_many_problems_multi_item_blocks(dev):
     """A group large enough that every block walks several items."""
     rng = np.random.default_rng(301)
