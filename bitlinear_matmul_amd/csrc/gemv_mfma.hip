@@ -129,6 +129,12 @@ __host__ __device__ __forceinline__ int staged_kp(int fmt, int mb, int K) {
   const int sc = sc_of(fmt, mb);
   return ((steps_of(fmt, K) + sc - 1) / sc) * sc * (fmt == UG_W_PACK5 ? 320 : 64);
 }
+// LDS row pitch of M staged rows of Kp bytes: 16 bytes more when they
+// still fit, so that the 16 rows one fragment load reads (a multiple of 64
+// bytes apart otherwise) fall in different banks.
+__host__ __device__ __forceinline__ int stage_pitch(int M, int Kp) {
+  return M > 1 && M * (Kp + 16) <= kXsBytes ? Kp + 16 : Kp;
+}
 __host__ __device__ __forceinline__ int mb_of(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 __host__ __device__ __forceinline__ bool stages_x(int fmt, int M, int K) {
   return (int64_t)M * staged_kp(fmt, mb_of(M), K) <= kXsBytes;
@@ -391,7 +397,7 @@ __device__ __forceinline__ void absmax_tiles(const GemvDesc &d, Smem<FMT> &sh, c
 // Pass 2 on 8 tiles: quantize into the staging rows, K order.
 template <int FMT>
 __device__ __forceinline__ void quant_tiles(const GemvDesc &d, Smem<FMT> &sh, const float4 (&v)[8],
-                                            int t0, int T4, int nt, int Kp) {
+                                            int t0, int T4, int nt, int pitch) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -400,7 +406,7 @@ __device__ __forceinline__ void quant_tiles(const GemvDesc &d, Smem<FMT> &sh, co
       const int m = t / T4, k = (t - m * T4) * 256 + 4 * lane;
       const float s = row_scale(sh, m, d.eps);
       if (k < d.K)
-        *reinterpret_cast<uint32_t *>(sh.xs + m * Kp + k) =
+        *reinterpret_cast<uint32_t *>(sh.xs + m * pitch + k) =
             pack4(q8(v[i].x, s), k + 1 < d.K ? q8(v[i].y, s) : 0, k + 2 < d.K ? q8(v[i].z, s) : 0,
                   k + 3 < d.K ? q8(v[i].w, s) : 0);
     }
@@ -410,14 +416,14 @@ __device__ __forceinline__ void quant_tiles(const GemvDesc &d, Smem<FMT> &sh, co
 // 8 dwords of x_q rows into the staging rows (zeros past K).
 template <int FMT>
 __device__ __forceinline__ void copy_xq4(const GemvDesc &d, Smem<FMT> &sh, const uint32_t (&v)[8],
-                                         int i0, int Kp4, int n4) {
+                                         int i0, int Kp4, int n4, int pitch) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int idx = i0 + i * kThreads, m = idx / Kp4, k = 4 * (idx - m * Kp4);
     if (idx < n4) {
       uint32_t w = v[i];
       if (k + 4 > d.K) w &= k >= d.K ? 0u : (0xffffffffu >> (8 * (k + 4 - d.K)));
-      reinterpret_cast<uint32_t *>(sh.xs + m * 4 * Kp4)[k >> 2] = w;
+      reinterpret_cast<uint32_t *>(sh.xs + m * pitch)[k >> 2] = w;
     }
   }
 }
@@ -426,7 +432,8 @@ __device__ __forceinline__ void copy_xq4(const GemvDesc &d, Smem<FMT> &sh, const
 // here, which keeps the registers free for a caller short of them.
 template <int FMT, bool PRE>
 __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, bool staged, int Kp,
-                                             bool table, bool zero_slots, const XBatch &xb) {
+                                             int pitch, bool table, bool zero_slots,
+                                             const XBatch &xb) {
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   if (FMT == UG_W_PACK5 && table) build_table(sh);
   if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
@@ -447,30 +454,30 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
     }
     __syncthreads();
     if (tid < d.M) sh.sm[tid] = row_scale(sh, tid, d.eps);
-    if (PRE) quant_tiles(d, sh, xb.f, wave, T4, nt, Kp);
+    if (PRE) quant_tiles(d, sh, xb.f, wave, T4, nt, pitch);
     for (int t0 = PRE ? wave + 8 * kWaves : wave; t0 < nt; t0 += 8 * kWaves) {
       float4 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = load_tile(d, xr, t0 + i * kWaves, T4, nt);
-      quant_tiles(d, sh, v, t0, T4, nt, Kp);
+      quant_tiles(d, sh, v, t0, T4, nt, pitch);
     }
     // zeros from the first whole dword past K to the end of the staged row
     const int kz = (d.K + 3) >> 2, nz = Kp4 - kz;
     for (int i = tid; i < d.M * nz; i += kThreads) {
       const int m = i / nz;
-      reinterpret_cast<uint32_t *>(sh.xs + m * Kp)[kz + (i - m * nz)] = 0u;
+      reinterpret_cast<uint32_t *>(sh.xs + m * pitch)[kz + (i - m * nz)] = 0u;
     }
   } else {
     if (tid < d.M) sh.sm[tid] = gp(d.s)[tid];
     if (staged) {
       const int n4 = d.M * Kp4;
       const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
-      if (PRE) copy_xq4(d, sh, xb.q, tid, Kp4, n4);
+      if (PRE) copy_xq4(d, sh, xb.q, tid, Kp4, n4, pitch);
       for (int i0 = PRE ? tid + 8 * kThreads : tid; i0 < n4; i0 += 8 * kThreads) {
         uint32_t v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = load_xq4(d, xr, i0 + i * kThreads, Kp4, n4);
-        copy_xq4(d, sh, v, i0, Kp4, n4);
+        copy_xq4(d, sh, v, i0, Kp4, n4, pitch);
       }
     }
   }
@@ -479,7 +486,7 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
     const int wpr = Kp / 80, nwin = d.M * wpr;
     for (int w0 = tid; w0 < nwin; w0 += kThreads) {
       const int m = w0 / wpr;
-      uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * Kp + (w0 - m * wpr) * 80);
+      uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * pitch + (w0 - m * wpr) * 80);
       uint32_t X[20], F[20];
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
@@ -497,7 +504,7 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
 // The quantized activations and scales as outputs (fused quantization, the
 // problem's first block): undo the staging permutation per K position.
 template <int FMT>
-__device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<FMT> &sh, int Kp) {
+__device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<FMT> &sh, int pitch) {
   const int tid = threadIdx.x;
   if (d.s)
     for (int m = tid; m < d.M; m += kThreads) gp(d.s)[m] = sh.sm[m];
@@ -511,7 +518,7 @@ __device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<
         // t < 4: fragment g/4, dword g%4, byte t; t == 4: fragment 4, dword g/4, byte g%4
         off = 80 * w + (t < 4 ? 16 * (g >> 2) + 4 * (g & 3) + t : 64 + 4 * (g >> 2) + (g & 3));
       }
-      gp(xq)[(int64_t)m * d.ldxq + k] = sh.xs[m * Kp + off];
+      gp(xq)[(int64_t)m * d.ldxq + k] = sh.xs[m * pitch + off];
     }
   }
 }
@@ -528,7 +535,7 @@ struct Wave {
   int xbase[MB];  // staged: LDS offset of this lane's activation row (step 0)
   __amdgpu_buffer_rsrc_t wr, xr;
 
-  __device__ __forceinline__ void init(const GemvDesc &d, bool stg, int Kp) {
+  __device__ __forceinline__ void init(const GemvDesc &d, bool stg, int pitch) {
     const int lane = threadIdx.x & 63, q = lane >> 4;
     S = steps_of(FMT, d.K);
     NC = (S + SC - 1) / SC;
@@ -540,7 +547,7 @@ struct Wave {
       // rows past M read row M-1: MFMA output row m depends only on input
       // row m, and rows past M are never stored
       const int m = min(16 * b + (lane & 15), d.M - 1);
-      xbase[b] = m * Kp + q * Fmt<FMT>::kLaneK;
+      xbase[b] = m * pitch + q * Fmt<FMT>::kLaneK;
     }
   }
 
@@ -729,8 +736,8 @@ struct ItemLoop {
     }
   }
 
-  __device__ __forceinline__ void start(const GemvDesc &d, bool staged, int Kp, int i0, int i1_) {
-    wv.init(d, staged, Kp);
+  __device__ __forceinline__ void start(const GemvDesc &d, bool staged, int pitch, int i0, int i1_) {
+    wv.init(d, staged, pitch);
     const int wave = uniform(threadIdx.x >> 6);
     const int my_items = i0 + wave < i1_ ? (i1_ - i0 - wave + kWaves - 1) / kWaves : 0;
     U = uniform(my_items * wv.NC);
@@ -774,11 +781,14 @@ struct Chunk {
   static constexpr int ROWS = 16 * MB;
   static constexpr int SB = FMT == UG_W_PACK5 ? 320 : 64;  // staged bytes per row and step
   static constexpr int CB = CH * SB;                        // staged bytes per row and chunk
+  // row pitch in LDS: 16 bytes more, so the 16 rows read by one fragment
+  // load (a multiple of 128 bytes apart otherwise) fall in different banks
+  static constexpr int CBP = CB + 16;
   static constexpr int UB = FMT == UG_W_PACK5 ? 80 : 16;    // staging unit (bytes)
   static constexpr int UPR = CB / UB;                        // units per row and chunk
   static constexpr int NU = (ROWS * UPR + kThreads - 1) / kThreads;  // units per thread
   static constexpr int UV = UB / 16;                         // 16-byte loads per unit
-  static_assert(ROWS * CB <= kXsBytes, "a chunk fits the staging area");
+  static_assert(ROWS * CBP <= kXsBytes, "a chunk fits the staging area");
 };
 
 // Loads (issue) this thread's staging units of chunk c: unit u = tid + 512 i
@@ -822,7 +832,7 @@ __device__ __forceinline__ void chunk_store(const GemvDesc &d, int8_t *xs, int c
           X[4 * j + e] = w4[e] & (kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb)))));
         }
       }
-      uint4 *dst = reinterpret_cast<uint4 *>(xs + m * C::CB + w * C::UB);
+      uint4 *dst = reinterpret_cast<uint4 *>(xs + m * C::CBP + w * C::UB);
       if (FMT == UG_W_PACK5) {
         uint32_t F[20];
         permute80(reinterpret_cast<const uint32_t(&)[20]>(X), F);
@@ -851,7 +861,7 @@ __device__ __forceinline__ void chunked_items(const GemvDesc &d, Smem<FMT> &sh, 
   // only on input row m, and rows past M are never stored)
   int xrow[MB];
 #pragma unroll
-  for (int b = 0; b < MB; ++b) xrow[b] = min(16 * b + (lane & 15), d.M - 1) * C::CB;
+  for (int b = 0; b < MB; ++b) xrow[b] = min(16 * b + (lane & 15), d.M - 1) * C::CBP;
 
   // weights of (round r, chunk c): row group g of the wave's item, the
   // chunk's steps; steps past S and items past i1 read nothing
@@ -966,7 +976,7 @@ __device__ __forceinline__ void chunked_block(const GemvDesc *plan, int count, i
     if (e <= g) continue;
     XBatch xb;  // unused
     if (!first) __syncthreads();  // the previous problem is done with the staging area
-    setup_finish<FMT, false>(d, sh, false, 0, first, false, xb);  // table, scales
+    setup_finish<FMT, false>(d, sh, false, 0, 0, first, false, xb);  // table, scales
     first = false;
     chunked_items<FMT, MB>(d, sh, g - d.item_begin, e - d.item_begin);
     g = e;
@@ -1001,15 +1011,15 @@ __device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, in
     const int e = min(g1, d.item_begin + d.items);
     if (e <= g) continue;
     const bool staged = stages_x(FMT, d.M, d.K);
-    const int Kp = staged_kp(FMT, MB, d.K);
+    const int Kp = staged_kp(FMT, MB, d.K), pitch = stage_pitch(d.M, Kp);
     XBatch xb;  // unused: the set-up loads its own batches here
     ItemLoop<FMT, MB> loop;
-    loop.start(d, staged, Kp, g - d.item_begin, e - d.item_begin);
+    loop.start(d, staged, pitch, g - d.item_begin, e - d.item_begin);
     if (!first) __syncthreads();  // the previous problem's staged rows are done
-    setup_finish<FMT, false>(d, sh, staged, Kp, first, false, xb);
+    setup_finish<FMT, false>(d, sh, staged, Kp, pitch, first, false, xb);
     first = false;
     loop.run(d, sh);
-    if (d.x && g == d.item_begin) write_act_outputs<FMT>(d, sh, Kp);
+    if (d.x && g == d.item_begin) write_act_outputs<FMT>(d, sh, pitch);
     g = e;
   }
 }
@@ -1138,7 +1148,8 @@ __device__ __forceinline__ void fine_absmax(Smem<FMT, kFineWaves> &sh, const Til
 // block writes it.  The codes are ug_quant_act's, bit for bit.
 template <int FMT, int NB>
 __device__ __forceinline__ void fine_quant(Smem<FMT, kFineWaves> &sh, const TileBatch<NB> &b, const uint4 (&u)[NB],
-                                           int K, int Kp, float eps, int8_t *xq_out, int ldxq_out) {
+                                           int K, int Kp, int pitch, float eps, int8_t *xq_out,
+                                           int ldxq_out) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -1150,7 +1161,7 @@ __device__ __forceinline__ void fine_quant(Smem<FMT, kFineWaves> &sh, const Tile
       q8x4(v, s, c0, c1, c2, c3);
       const uint32_t w = pack4(k < K ? c0 : 0, k + 1 < K ? c1 : 0, k + 2 < K ? c2 : 0,
                                k + 3 < K ? c3 : 0);
-      stage4<FMT>(sh.xs + m * Kp, k, w);
+      stage4<FMT>(sh.xs + m * pitch, k, w);
       if (xq_out && k < K) {
         int8_t *row = xq_out + m * ldxq_out;
         if (k + 4 <= K) {
@@ -1166,7 +1177,7 @@ __device__ __forceinline__ void fine_quant(Smem<FMT, kFineWaves> &sh, const Tile
 // x_q tiles into the staged rows, bytes past K zeroed.
 template <int FMT, int NB>
 __device__ __forceinline__ void fine_copy(Smem<FMT, kFineWaves> &sh, const TileBatch<NB> &b, const uint4 (&u)[NB],
-                                          int K, int Kp) {
+                                          int K, int Kp, int pitch) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -1176,7 +1187,7 @@ __device__ __forceinline__ void fine_copy(Smem<FMT, kFineWaves> &sh, const TileB
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int kb = K - k - 4 * e;  // bytes of this dword inside the row
-        stage4<FMT>(sh.xs + b.m[i] * Kp, k + 4 * e,
+        stage4<FMT>(sh.xs + b.m[i] * pitch, k + 4 * e,
                     w4[e] & (kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb))))));
       }
     }
@@ -1247,6 +1258,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
 
   const int M = b.shape & 0xff, items = (b.shape >> 8) & 0xff, S = b.shape >> 16, K = b.K;
   const int Kp = S * Fmt<FMT>::kStepK;  // staged row: whole steps, zeros past K
+  const int pitch = stage_pitch(M, Kp);
   const int P = items * S;
   const int p0 = (wave * P) >> kFineWaveShift, p1 = ((wave + 1) * P) >> kFineWaveShift;
   const int T = FUSED ? (Kp + 255) >> 8 : (Kp + 1023) >> 10;  // tiles cover whole staged rows
@@ -1314,23 +1326,23 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
       sh.sm[tid] = s;
       if (b.s) gp(b.s)[tid] = s;
     }
-    fine_quant(sh, b0, x0, K, Kp, b.eps, b.xq_out, b.ldxq_out);
+    fine_quant(sh, b0, x0, K, Kp, pitch, b.eps, b.xq_out, b.ldxq_out);
     for (TileWalk w = rest; w.t < w.te;) {
       TileBatch<NB> bb;
       uint4 u[NB];
       next_batch(w, bb);
       load_batch<true>(xr, b.ldx, K, bb, u);
-      fine_quant(sh, bb, u, K, Kp, b.eps, b.xq_out, b.ldxq_out);
+      fine_quant(sh, bb, u, K, Kp, pitch, b.eps, b.xq_out, b.ldxq_out);
     }
   } else {
     if (tid < M) sh.sm[tid] = s_in;
-    fine_copy(sh, b0, x0, K, Kp);
+    fine_copy(sh, b0, x0, K, Kp, pitch);
     for (TileWalk w = rest; w.t < w.te;) {
       TileBatch<NB> bb;
       uint4 u[NB];
       next_batch(w, bb);
       load_batch<false>(xr, b.ldx, K, bb, u);
-      fine_copy(sh, bb, u, K, Kp);
+      fine_copy(sh, bb, u, K, Kp, pitch);
     }
   }
   __syncthreads();  // table, slots, scales and staged rows
@@ -1338,7 +1350,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
   const char *lut = reinterpret_cast<const char *>(sh.lut);
   // rows past M read row M-1: MFMA output row m depends only on input row m,
   // and rows past M are never stored
-  const int xoff = min(lane & 15, M - 1) * Kp + (lane >> 4) * Fmt<FMT>::kLaneK;
+  const int xoff = min(lane & 15, M - 1) * pitch + (lane >> 4) * Fmt<FMT>::kLaneK;
   v4i xf[Fmt<FMT>::kFrag];
   v4i acc[2], prev[2];
   int it = ws & 0xff, st = (ws >> 8) & 0xff, xst = -1, prev_it = 0;
