@@ -97,6 +97,9 @@ struct Cfg {
       FINE ? 1 : (FMT == UG_W_PACK5 ? (MB == 4 ? 1 : 2) : (MB == 4 ? 2 : 4));
   // independent MFMA chains per output tile
   static constexpr int NACC = FMT == UG_W_PACK5 && MB == 4 ? 1 : 2;
+  // decode table with 8-byte entries (fewer instructions per packed byte,
+  // more registers): one 16-row activation block leaves room for it
+  static constexpr bool WIDE = MB == 1;
 };
 
 __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int K) {
@@ -141,6 +144,25 @@ __host__ __device__ __forceinline__ bool stages_x(int fmt, int M, int K) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A descriptor in scalar registers after one memory round trip: lane i
+// fetches dword i, then each dword is read from its lane.  (Scalar loads of
+// the fields would be issued at their first uses, several round trips apart
+// where a branch depends on an earlier field.)
+template <typename T>
+__device__ __forceinline__ T fetch_uniform(const T *src) {
+  static_assert(sizeof(T) % 4 == 0 && sizeof(T) <= 256, "whole dwords, one per lane");
+  constexpr int N = sizeof(T) / 4;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(src), (short)0, (int)sizeof(T), 0x00020000);
+  const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, 4u * (threadIdx.x & 63), 0, 0);
+  uint32_t out[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_readlane(v, i);
+  T t;
+  __builtin_memcpy(&t, out, sizeof(T));
+  return t;
+}
 
 // x kept in a vector register: arithmetic on the result runs on the wave's
 // SIMD instead of the CU's one scalar unit, which every wave of the block
@@ -311,11 +333,6 @@ __device__ __forceinline__ void table_store(Smem<FMT, NW> &sh, uint2 v) {
   table_store_step<WIDE, 6>(sh, v);
   table_store_step<WIDE, 7>(sh, v);
 }
-// The stream split's (narrow) table.
-template <int FMT>
-__device__ __forceinline__ void build_table(Smem<FMT> &sh) {
-  table_store<false>(sh, table_load());
-}
 
 // s = fl(fl(max|x| / 127) + eps) of row m from the per-wave maxima.
 template <int FMT, int NW>
@@ -327,20 +344,25 @@ __device__ __forceinline__ float row_scale(const Smem<FMT, NW> &sh, int m, float
   return a127 + eps;
 }
 
-// Block set-up for problem d, in two halves.  setup_issue() issues the
-// first batch of activation loads; the caller then issues its weight loads,
-// so that waiting for the activations never waits for the weights (loads
-// complete in issue order).  setup_finish() builds the decode table (first
-// problem of the block), the row scales (fused quantization, else the given
-// s), the activation rows staged in LDS (Kp bytes per row, zeros past K;
-// five trits per byte: every 80-position window permuted as the decoded
-// weights are) and zeroed reduction slots, and ends with a barrier.
+// Block set-up for problem d, in two halves.  pre_issue() issues the loads
+// the set-up needs (decode table entry, first batch of x_q dwords, row
+// scale, beta); the caller then issues its weight loads, so that waiting
+// for the set-up's data never waits for the weights (loads complete in
+// issue order).  setup_finish() builds the decode table (first problem of
+// the block), the row scales (fused quantization, else the given s), the
+// activation rows staged in LDS (Kp bytes per row, zeros past K; five trits
+// per byte: every 80-position window permuted as the decoded weights are)
+// and zeroed reduction slots, and ends with a barrier.
 //
 // Fused quantization reads x in tiles t = (row m, 256 positions c): lane l
 // takes the float4 at 256 c + 4 l, a wave keeps 8 tiles in flight.
-struct XBatch {
-  float4 f[8];    // fused: the first 8 tiles of this wave
-  uint32_t q[8];  // x_q given: the first 8 dwords of this thread
+template <int NQ>
+struct PreLoads {
+  static_assert(NQ == 0 || NQ == 8, "x_q dwords come in batches of 8");
+  uint2 lut;                 // this thread's decode table entry (table_load)
+  uint32_t q[NQ ? NQ : 1];   // x_q given and staged: the first NQ dwords of this thread
+  float s;                   // x_q given: the scale of row tid (tid < M)
+  float beta;
 };
 
 __device__ __forceinline__ float4 load_tile(const GemvDesc &d, __amdgpu_buffer_rsrc_t xr, int t,
@@ -357,21 +379,24 @@ __device__ __forceinline__ uint32_t load_xq4(const GemvDesc &d, __amdgpu_buffer_
   return buffer_load4(xr, idx < n4 && k < d.K ? (uint32_t)(m * (int)d.ldxq + k) : kOOB);
 }
 
-// Both batches are issued without a branch (the one not needed reads past
-// its buffer, i.e. nothing), so every path sees the same loads in flight
-// and waiting for them never has to wait for the caller's later loads.
-__device__ __forceinline__ void setup_issue(const GemvDesc &d, bool staged, int Kp, XBatch &xb) {
-  const int tid = threadIdx.x, wave = uniform(tid >> 6);
-  const int T4 = (d.K + 255) >> 8, nt = d.x ? d.M * T4 : 0;
-  const __amdgpu_buffer_rsrc_t xr =
-      buffer_rsrc(d.x, d.x ? (uint32_t)((int64_t)d.M * d.ldx * 4) : 0u);
+// Every load but the table's is issued without a branch (one not needed
+// reads past its buffer, i.e. nothing).
+template <int FMT, int NQ>
+__device__ __forceinline__ void pre_issue(const GemvDesc &d, bool staged, int Kp, bool table,
+                                          PreLoads<NQ> &pl) {
+  const int tid = threadIdx.x;
+  pl.lut = uint2{0, 0};
+  if (FMT == UG_W_PACK5 && table) pl.lut = table_load();
+  if (NQ) {
+    const int Kp4 = Kp >> 2, n4 = !d.x && staged ? d.M * Kp4 : 0;
+    const __amdgpu_buffer_rsrc_t qr =
+        buffer_rsrc(d.xq, n4 ? (uint32_t)((int64_t)d.M * d.ldxq) : 0u);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) xb.f[i] = load_tile(d, xr, wave + i * kWaves, T4, nt);
-  const int Kp4 = Kp >> 2, n4 = !d.x && staged ? d.M * Kp4 : 0;
-  const __amdgpu_buffer_rsrc_t qr =
-      buffer_rsrc(d.xq, n4 ? (uint32_t)((int64_t)d.M * d.ldxq) : 0u);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) xb.q[i] = load_xq4(d, qr, tid + i * kThreads, Kp4, n4);
+    for (int i = 0; i < NQ; ++i) pl.q[i] = load_xq4(d, qr, tid + i * kThreads, Kp4, n4);
+  }
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(d.s, d.x ? 0u : 4u * (uint32_t)d.M);
+  pl.s = __builtin_bit_cast(float, buffer_load4(sr, tid < d.M ? 4u * tid : kOOB));
+  pl.beta = __builtin_bit_cast(float, buffer_load4(buffer_rsrc(d.beta, 4), 0));
 }
 
 // Pass 1 on 8 tiles t0 + i * 8: per-wave row maxima.
@@ -428,14 +453,14 @@ __device__ __forceinline__ void copy_xq4(const GemvDesc &d, Smem<FMT> &sh, const
   }
 }
 
-// PRE: the first batch is in xb (setup_issue); else every batch is loaded
-// here, which keeps the registers free for a caller short of them.
-template <int FMT, bool PRE>
+// NQ: the first batch of x_q dwords is in pl (0: every batch is loaded
+// here, which keeps the registers free for a caller short of them).
+template <int FMT, int NQ, bool WIDE>
 __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, bool staged, int Kp,
                                              int pitch, bool table, bool zero_slots,
-                                             const XBatch &xb) {
+                                             const PreLoads<NQ> &pl) {
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
-  if (FMT == UG_W_PACK5 && table) build_table(sh);
+  if (FMT == UG_W_PACK5 && table) table_store<WIDE>(sh, pl.lut);
   if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
   if (zero_slots)
     for (int i = tid; i < kFineItems * 64; i += kThreads)
@@ -445,8 +470,7 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
     const int T4 = (d.K + 255) >> 8, nt = d.M * T4;
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.x, (uint32_t)((int64_t)d.M * d.ldx * 4));
     sh.part[wave][lane] = 0.0f;
-    if (PRE) absmax_tiles(d, sh, xb.f, wave, T4, nt);
-    for (int t0 = PRE ? wave + 8 * kWaves : wave; t0 < nt; t0 += 8 * kWaves) {
+    for (int t0 = wave; t0 < nt; t0 += 8 * kWaves) {
       float4 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = load_tile(d, xr, t0 + i * kWaves, T4, nt);
@@ -454,8 +478,7 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
     }
     __syncthreads();
     if (tid < d.M) sh.sm[tid] = row_scale(sh, tid, d.eps);
-    if (PRE) quant_tiles(d, sh, xb.f, wave, T4, nt, pitch);
-    for (int t0 = PRE ? wave + 8 * kWaves : wave; t0 < nt; t0 += 8 * kWaves) {
+    for (int t0 = wave; t0 < nt; t0 += 8 * kWaves) {
       float4 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = load_tile(d, xr, t0 + i * kWaves, T4, nt);
@@ -468,12 +491,12 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
       reinterpret_cast<uint32_t *>(sh.xs + m * pitch)[kz + (i - m * nz)] = 0u;
     }
   } else {
-    if (tid < d.M) sh.sm[tid] = gp(d.s)[tid];
+    if (tid < d.M) sh.sm[tid] = pl.s;
     if (staged) {
       const int n4 = d.M * Kp4;
       const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
-      if (PRE) copy_xq4(d, sh, xb.q, tid, Kp4, n4, pitch);
-      for (int i0 = PRE ? tid + 8 * kThreads : tid; i0 < n4; i0 += 8 * kThreads) {
+      if constexpr (NQ > 0) copy_xq4(d, sh, pl.q, tid, Kp4, n4, pitch);
+      for (int i0 = NQ ? tid + NQ * kThreads : tid; i0 < n4; i0 += 8 * kThreads) {
         uint32_t v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = load_xq4(d, xr, i0 + i * kThreads, Kp4, n4);
@@ -566,6 +589,8 @@ struct Wave {
       // reads real weights for a row past N, whose results are never stored
       const uint32_t voff = (uint32_t)n * (uint32_t)d.ldw + 16u * q + (ok ? 0u : kOOB);
 #pragma unroll
+      // (no non-temporal hint: a row that is not a multiple of 128 bytes
+      // long shares cache lines with its neighbours, which read them later)
       for (int s = 0; s < SC; ++s) wb[r][s] = buffer_load16(wr, voff + (uint32_t)(64 * (ch * SC + s)));
     }
   }
@@ -615,16 +640,24 @@ struct Wave {
   __device__ __forceinline__ void compute(const GemvDesc &d, const int8_t *xs, const char *lut,
                                           int ch, const uint4 (&wb)[kRGW][SC],
                                           v4i (&acc)[kRGW][MB][NACC]) {
-    const uint32_t lr4 = 4u * (threadIdx.x & 63);
     if (FMT == UG_W_PACK5) {
       constexpr int NP = SC * kRGW;
       uint32_t T[2][20];
       auto dec = [&](int p, uint32_t(&t)[20]) {
         const uint4 &w = wb[p % kRGW][p / kRGW];
-        decode4_narrow(w.x, lut, lr4, t, t[16]);
-        decode4_narrow(w.y, lut, lr4, t + 4, t[17]);
-        decode4_narrow(w.z, lut, lr4, t + 8, t[18]);
-        decode4_narrow(w.w, lut, lr4, t + 12, t[19]);
+        if (Cfg<FMT, MB, FINE>::WIDE) {
+          const uint32_t lr8 = 8u * (threadIdx.x & 31);
+          decode4_wide(w.x, lut, lr8, t, t[16]);
+          decode4_wide(w.y, lut, lr8, t + 4, t[17]);
+          decode4_wide(w.z, lut, lr8, t + 8, t[18]);
+          decode4_wide(w.w, lut, lr8, t + 12, t[19]);
+        } else {
+          const uint32_t lr4 = 4u * (threadIdx.x & 63);
+          decode4_narrow(w.x, lut, lr4, t, t[16]);
+          decode4_narrow(w.y, lut, lr4, t + 4, t[17]);
+          decode4_narrow(w.z, lut, lr4, t + 8, t[18]);
+          decode4_narrow(w.w, lut, lr4, t + 12, t[19]);
+        }
       };
       v4i xf[MB][F1];
       dec(0, T[0]);
@@ -746,10 +779,10 @@ struct ItemLoop {
     iss_ch = pro_ch = 0;
     issue(d, A);
     issue(d, B);
-    beta = gp(d.beta)[0];
   }
 
-  // Needs the block's set-up (table, staged rows) to be complete.
+  // Needs the block's set-up (table, staged rows) to be complete.  (Issuing
+  // the third unit before the set-up too measured slower.)
   __device__ __forceinline__ void run(const GemvDesc &d, const Smem<FMT> &sh) {
     for (int u = 0; u < U;) {
       issue(d, C);
@@ -966,20 +999,23 @@ __device__ __forceinline__ void chunked_items(const GemvDesc &d, Smem<FMT> &sh, 
 
 // The block's global items [g0, g1) of the plan, problem by problem.
 template <int FMT, int MB>
-__device__ __forceinline__ void chunked_block(const GemvDesc *plan, int count, int p, int g0,
-                                              int g1) {
+__device__ __forceinline__ void chunked_block(const GemvDesc *plan, int count, const GemvDesc &d0,
+                                              int p0, int g0, int g1) {
   __shared__ Smem<FMT> sh;
   bool first = true;
-  for (int g = g0; g < g1 && p < count; ++p) {
-    const GemvDesc d = plan[p];
+  GemvDesc d = d0;
+  for (int g = g0, p = p0; g < g1 && p < count;) {
     const int e = min(g1, d.item_begin + d.items);
-    if (e <= g) continue;
-    XBatch xb;  // unused
-    if (!first) __syncthreads();  // the previous problem is done with the staging area
-    setup_finish<FMT, false>(d, sh, false, 0, 0, first, false, xb);  // table, scales
-    first = false;
-    chunked_items<FMT, MB>(d, sh, g - d.item_begin, e - d.item_begin);
-    g = e;
+    if (e > g) {
+      PreLoads<0> pl;
+      pre_issue<FMT>(d, false, 0, first, pl);
+      if (!first) __syncthreads();  // the previous problem is done with the staging area
+      setup_finish<FMT, 0, false>(d, sh, false, 0, 0, first, false, pl);  // table, scales
+      first = false;
+      chunked_items<FMT, MB>(d, sh, g - d.item_begin, e - d.item_begin);
+      g = e;
+    }
+    if (++p < count && g < g1) d = fetch_uniform(plan + p);
   }
 }
 
@@ -987,40 +1023,60 @@ template <int FMT, int MB>
 __global__ __launch_bounds__(kThreads) void gemv_chunked_single(GemvDesc d) {
   const int64_t T = d.items;
   const int g0 = (int)(T * blockIdx.x / gridDim.x), g1 = (int)(T * (blockIdx.x + 1) / gridDim.x);
-  if (g0 < g1) chunked_block<FMT, MB>(&d, 1, 0, g0, g1);
+  if (g0 < g1) chunked_block<FMT, MB>(&d, 1, d, 0, g0, g1);
 }
 
 template <int FMT, int MB>
 __global__ __launch_bounds__(kThreads) void gemv_chunked_grouped(const GemvDesc *__restrict__ plan,
                                                                  const GemvBlock *__restrict__ blocks,
                                                                  int count) {
-  const GemvBlock bl = blocks[blockIdx.x];
-  if (bl.i0 < bl.i1) chunked_block<FMT, MB>(plan, count, bl.p, bl.i0, bl.i1);
+  const GemvBlock bl = fetch_uniform(blocks + blockIdx.x);
+  if (bl.i0 < bl.i1) chunked_block<FMT, MB>(plan, count, bl.d, bl.p, bl.i0, bl.i1);
 }
 
-// The block takes the global items [g0, g1) of the plan (problem p holds
-// item g0; problem q owns [item_begin, +items)), crossing into the next
-// problem when its range does.
+// Items [g, e) of problem d (global item numbers).  first: the block's first
+// problem (it builds the decode table, and no earlier problem's waves still
+// read the staging area).
 template <int FMT, int MB>
-__device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, int p, int g0,
-                                             int g1) {
+__device__ __forceinline__ void stream_problem(Smem<FMT> &sh, const GemvDesc &d, int g, int e,
+                                               bool first) {
+  const bool staged = stages_x(FMT, d.M, d.K);
+  const int Kp = staged_kp(FMT, MB, d.K), pitch = stage_pitch(d.M, Kp);
+  // (the set-up's loads leave before the weights': two units of weights
+  // stay in flight while the block sets up)
+  constexpr int NQ = MB <= 2 ? 8 : 0;
+  PreLoads<NQ> pl;
+  pre_issue<FMT>(d, staged, Kp, first, pl);
+  __builtin_amdgcn_sched_barrier(0);
+  ItemLoop<FMT, MB> loop;
+  loop.start(d, staged, pitch, g - d.item_begin, e - d.item_begin);
+  __builtin_amdgcn_sched_barrier(0);
+  if (!first) __syncthreads();  // the previous problem's staged rows are done
+  setup_finish<FMT, NQ, Cfg<FMT, MB, false>::WIDE>(d, sh, staged, Kp, pitch, first, false, pl);
+  // in a scalar register: a use in the loop then waits for no load
+  loop.beta = __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, pl.beta)));
+  loop.run(d, sh);
+  if (d.x && g == d.item_begin) write_act_outputs<FMT>(d, sh, pitch);
+}
+
+// The block takes the global items [g0, g1) of the plan (problem p0 holds
+// item g0; problem q owns [item_begin, +items)), crossing into the next
+// problem when its range does.  d0: problem p0's descriptor, which the
+// block's entry carries (fetched with g0 and g1).
+template <int FMT, int MB>
+__device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, const GemvDesc &d0,
+                                             int p0, int g0, int g1) {
   __shared__ Smem<FMT> sh;
   bool first = true;
-  for (int g = g0; g < g1 && p < count; ++p) {
-    const GemvDesc d = plan[p];
+  GemvDesc d = d0;
+  for (int g = g0, p = p0; g < g1 && p < count;) {
     const int e = min(g1, d.item_begin + d.items);
-    if (e <= g) continue;
-    const bool staged = stages_x(FMT, d.M, d.K);
-    const int Kp = staged_kp(FMT, MB, d.K), pitch = stage_pitch(d.M, Kp);
-    XBatch xb;  // unused: the set-up loads its own batches here
-    ItemLoop<FMT, MB> loop;
-    loop.start(d, staged, pitch, g - d.item_begin, e - d.item_begin);
-    if (!first) __syncthreads();  // the previous problem's staged rows are done
-    setup_finish<FMT, false>(d, sh, staged, Kp, pitch, first, false, xb);
-    first = false;
-    loop.run(d, sh);
-    if (d.x && g == d.item_begin) write_act_outputs<FMT>(d, sh, pitch);
-    g = e;
+    if (e > g) {
+      stream_problem<FMT, MB>(sh, d, g, e, first);
+      first = false;
+      g = e;
+    }
+    if (++p < count && g < g1) d = fetch_uniform(plan + p);
   }
 }
 
@@ -1028,15 +1084,15 @@ template <int FMT, int MB>
 __global__ __launch_bounds__(kThreads) void gemv_stream_single(GemvDesc d) {
   const int64_t T = d.items;
   const int g0 = (int)(T * blockIdx.x / gridDim.x), g1 = (int)(T * (blockIdx.x + 1) / gridDim.x);
-  if (g0 < g1) stream_block<FMT, MB>(&d, 1, 0, g0, g1);
+  if (g0 < g1) stream_block<FMT, MB>(&d, 1, d, 0, g0, g1);
 }
 
 template <int FMT, int MB>
 __global__ __launch_bounds__(kThreads) void gemv_stream_grouped(const GemvDesc *__restrict__ plan,
                                                                 const GemvBlock *__restrict__ blocks,
                                                                 int count) {
-  const GemvBlock bl = blocks[blockIdx.x];
-  if (bl.i0 < bl.i1) stream_block<FMT, MB>(plan, count, bl.p, bl.i0, bl.i1);
+  const GemvBlock bl = fetch_uniform(blocks + blockIdx.x);
+  if (bl.i0 < bl.i1) stream_block<FMT, MB>(plan, count, bl.d, bl.p, bl.i0, bl.i1);
 }
 
 // ---------------------------------------------------------------------------
