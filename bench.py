@@ -70,11 +70,11 @@ def parse():
 # Valid only for the kernel sources they were taken on: `src_sha` is the
 # SHA-256 of the kernel's source file; any other source reports null.
 TRAFFIC = {
-    # profiles/gemv_fine_grouped_decode_stack.md: 2014.5 KiB fetched x 1.9997,
+    # profiles/gemv_fine_grouped_decode_stack.md: 2012.5 KiB fetched x 1.9997,
     # 146.4 KiB written x 1.0000
     "decode_stack": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
-                         src_sha="1a9dc3fa26df027211cf44664a3ce20f0a4fc167751eddb7d2e1c562f383d49f",
-                         bytes_per_launch=4274936),
+                         src_sha="620954f42826ae3101abb962d14387b9248a28a0aaef14634092976b4d5d1839",
+                         bytes_per_launch=4270769),
     # profiles/gemm_i8_large_prefill.md: mean of both shapes, 60190.6 KiB
     # fetched x 1.9997, 75776.0 KiB written x 1.0000
     "prefill": dict(src="bitlinear_matmul_amd/csrc/gemm.hip",
