@@ -58,6 +58,9 @@ def parse():
                    choices=["decode_stack", "sweep", "prefill", "stack", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--sweep-point", default=None, metavar="M,SHAPE",
+                   help="sweep: run only the point with M rows and shape index SHAPE "
+                        "(0: 2560->6912, 1: 6912->2560, 2: 2560->2560), e.g. for profiling")
     p.add_argument("--copy-probe", action="store_true",
                    help="first run one plain 256 MiB device copy (a known-size kernel that "
                         "calibrates the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
@@ -75,6 +78,11 @@ TRAFFIC = {
     "decode_stack": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
                          src_sha="620954f42826ae3101abb962d14387b9248a28a0aaef14634092976b4d5d1839",
                          bytes_per_launch=4270769),
+    # profiles/gemv_stream_grouped_sweep_m1.md: M=1 2560->6912, 37 problems per
+    # launch: 64224.1 KiB fetched x 1.9997, 705.3 KiB written x 1.0000
+    "sweep": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
+                  src_sha="620954f42826ae3101abb962d14387b9248a28a0aaef14634092976b4d5d1839",
+                  bytes_per_launch=132236704),
     # profiles/gemm_i8_large_prefill.md: mean of both shapes, 60190.6 KiB
     # fetched x 1.9997, 75776.0 KiB written x 1.0000
     "prefill": dict(src="bitlinear_matmul_amd/csrc/gemm.hip",
@@ -261,7 +269,11 @@ def run_sweep(args, torch, ug, inputs):
     points = []
     tot_bytes = 0.0
     tot_s = 0.0
+    dom = None
+    only = tuple(int(v) for v in args.sweep_point.split(",")) if args.sweep_point else None
     for si, (K, N) in enumerate(inputs.SWEEP_SHAPES):
+        if only is not None and only[1] != si:
+            continue
         x64, W = inputs.sweep_inputs(si, 64)
         wq, beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
         pk = ug.ug_pack_trits(wq)
@@ -271,6 +283,8 @@ def run_sweep(args, torch, ug, inputs):
         n_sets = max(2, min(warm + steps, (COLD_BYTES // (G * N * ug.packed_pitch(K))) + 1))
         copies = [[pk.clone() for _ in range(G)] for _ in range(n_sets)]
         for M in inputs.SWEEP_MS:
+            if only is not None and only[0] != M:
+                continue
             xq, s = ug.ug_quant_act(torch.from_numpy(x64[:M].copy()).to(dev))
             y = ug.empty_pitched(M, N, torch.float32, dev)
             try:
