@@ -72,6 +72,8 @@ constexpr int kFinePieces = 8;   // fine split: (item, step) pieces per wave
 // activations) 2 tiles per wave, so every wave issues half the loads.
 constexpr int kShortPieces = 4;
 constexpr int kShortTiles = 2;
+constexpr int kTinyPieces = 3;  // the tiny variant: at most 3 pieces and 1 tile per wave
+constexpr int kTinyTiles = 1;
 
 template <int FMT>
 struct Fmt;
@@ -1303,10 +1305,14 @@ __device__ __forceinline__ void fine_flush(int *slots, int it, int M, const v4i 
 // from LDS once for all its items; each piece's sums go to its item's LDS
 // slot (flushed one piece later, when its MFMAs are done).  After a barrier
 // the block writes every item's outputs.
-template <int FMT, bool FUSED, bool SHORT>
+// LEVEL: the loads each wave issues whether or not its share needs them
+// (each costs the CU's texture path about as much as a real one): 0, up to
+// kFinePieces weight loads and a batch of activation tiles; 1 (short),
+// kShortPieces and kShortTiles; 2 (tiny), kTinyPieces and kTinyTiles.
+template <int FMT, bool FUSED, int LEVEL>
 __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
                                            uint2 lut_entry) {
-  constexpr int MP = SHORT ? kShortPieces : kFinePieces;  // weight loads per wave
+  constexpr int MP = LEVEL == 2 ? kTinyPieces : (LEVEL == 1 ? kShortPieces : kFinePieces);
   __shared__ Smem<FMT, kFineWaves> sh;
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   // the table's and the descriptor's loads (the caller's) leave first
@@ -1326,7 +1332,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(b.x, (uint32_t)(M * b.ldx));
   TileWalk walk{(wave * nt) >> kFineWaveShift, ((wave + 1) * nt) >> kFineWaveShift,
                 in_vgpr((ws >> 16) & 0xff), in_vgpr(ws >> 24), T};
-  constexpr int NB = SHORT ? kShortTiles : kTileBatch<FUSED>;
+  constexpr int NB = LEVEL == 2 ? kTinyTiles : (LEVEL == 1 ? kShortTiles : kTileBatch<FUSED>);
   TileBatch<NB> b0;
   uint4 x0[NB];
   next_batch(walk, b0);
@@ -1450,7 +1456,7 @@ struct FineTail {
   int32_t items;
 };
 
-template <int FMT, bool SHORT>
+template <int FMT, int LEVEL>
 __global__ __launch_bounds__(kFineThreads) void gemv_fine_single(const FineBlock b, const FineTail last) {
   const uint2 lut = FMT == UG_W_PACK5 ? table_load() : uint2{0, 0};
   const bool is_last = blockIdx.x + 1 == gridDim.x;
@@ -1461,15 +1467,15 @@ __global__ __launch_bounds__(kFineThreads) void gemv_fine_single(const FineBlock
   FineBlock mine = b;
   mine.i0 = blockIdx.x * ((b.shape >> 8) & 0xff);
   if (is_last) mine.shape = (b.shape & 0xffff00ffu) | ((uint32_t)last.items << 8);
-  fine_block<FMT, false, SHORT>(mine, ws, lut);
+  fine_block<FMT, false, LEVEL>(mine, ws, lut);
 }
 
-template <int FMT, bool FUSED, bool SHORT>
+template <int FMT, bool FUSED, int LEVEL>
 __global__ __launch_bounds__(kFineThreads) void gemv_fine_grouped(const FineBlock *__restrict__ blocks) {
   // the table's load first: both fetches travel together
   const uint2 lut = FMT == UG_W_PACK5 ? table_load() : uint2{0, 0};
   const FineBlock b = blocks[blockIdx.x];
-  fine_block<FMT, FUSED, SHORT>(b, blocks[blockIdx.x].wave_start[uniform(threadIdx.x >> 6)], lut);
+  fine_block<FMT, FUSED, LEVEL>(b, blocks[blockIdx.x].wave_start[uniform(threadIdx.x >> 6)], lut);
 }
 
 // ---------------------------------------------------------------------------
@@ -1577,16 +1583,18 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
       total += descs[i].items;
     }
     // the short variant when every wave of every block fits it
-    bool short_ok = true;
+    // (and the tiny one, a stricter short, when every wave fits that)
+    bool short_ok = true, tiny_ok = true;
     for (const FineBlock &f : fine) {
       const int M = f.shape & 0xff, items = (f.shape >> 8) & 0xff, S = f.shape >> 16;
       const int Kp = S * (fmt == UG_W_PACK5 ? 320 : 64);
       const int T = descs[0].x ? (Kp + 255) >> 8 : (Kp + 1023) >> 10;
-      if ((items * S + kFineWaves - 1) / kFineWaves > kShortPieces ||
-          (M * T + kFineWaves - 1) / kFineWaves > kShortTiles)
-        short_ok = false;
+      const int pw = (items * S + kFineWaves - 1) / kFineWaves, tw = (M * T + kFineWaves - 1) / kFineWaves;
+      if (pw > kShortPieces || tw > kShortTiles) short_ok = false;
+      if (pw > kTinyPieces || tw > kTinyTiles) tiny_ok = false;
     }
-    return (short_ok ? 1024 : 0) + (descs[0].x ? 512 : 0) + 256 + 16 * fmt + 1;
+    return (short_ok && tiny_ok ? 4096 : 0) + (short_ok ? 1024 : 0) + (descs[0].x ? 512 : 0) +
+           256 + 16 * fmt + 1;
   }
   const int mb = mb_of(descs[0].M);
   bool chunked = false;  // some problem's activations do not fit the staging area
@@ -1618,20 +1626,22 @@ bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
 
 hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int32_t count,
                                int32_t grid, int32_t variant, hipStream_t st) {
-  const bool fine = (variant >> 8) & 1, fused = (variant >> 9) & 1, shrt = (variant >> 10) & 1;
+  const bool fine = (variant >> 8) & 1, fused = (variant >> 9) & 1;
+  const int level = (variant >> 12) & 1 ? 2 : ((variant >> 10) & 1);
   const int fmt = (variant >> 4) & 15, mb = variant & 15;
   dim3 g(grid), b(kThreads);
   if (fine) {
     const FineBlock *fb = static_cast<const FineBlock *>(table);
     b = dim3(kFineThreads);
-#define UG_FINE(F, FU, SH) hipLaunchKernelGGL((gemv_fine_grouped<F, FU, SH>), g, b, 0, st, fb)
+#define UG_FINE(F, FU, LV) hipLaunchKernelGGL((gemv_fine_grouped<F, FU, LV>), g, b, 0, st, fb)
+#define UG_FINE_LV(F, FU) \
+  do { if (level == 2) UG_FINE(F, FU, 2); else if (level == 1) UG_FINE(F, FU, 1); else UG_FINE(F, FU, 0); } while (0)
     if (fmt == UG_W_PACK5) {
-      if (fused) { if (shrt) UG_FINE(UG_W_PACK5, true, true); else UG_FINE(UG_W_PACK5, true, false); }
-      else { if (shrt) UG_FINE(UG_W_PACK5, false, true); else UG_FINE(UG_W_PACK5, false, false); }
+      if (fused) UG_FINE_LV(UG_W_PACK5, true); else UG_FINE_LV(UG_W_PACK5, false);
     } else {
-      if (fused) { if (shrt) UG_FINE(UG_W_I8, true, true); else UG_FINE(UG_W_I8, true, false); }
-      else { if (shrt) UG_FINE(UG_W_I8, false, true); else UG_FINE(UG_W_I8, false, false); }
+      if (fused) UG_FINE_LV(UG_W_I8, true); else UG_FINE_LV(UG_W_I8, false);
     }
+#undef UG_FINE_LV
 #undef UG_FINE
     return hipGetLastError();
   }
@@ -1695,14 +1705,14 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
     std::copy(fine.back().wave_start, fine.back().wave_start + kFineWaves, last.wave_start);
     last.items = (int32_t)((fine.back().shape >> 8) & 0xff);
     dim3 g((unsigned)fine.size()), b(kFineThreads);
-    const bool shrt = (variant >> 10) & 1;
+    const int level = (variant >> 12) & 1 ? 2 : ((variant >> 10) & 1);
+#define UG_SINGLE(F, LV) hipLaunchKernelGGL((gemv_fine_single<F, LV>), g, b, 0, st, fine[0], last)
     if (wfmt == UG_W_PACK5) {
-      if (shrt) hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5, true>), g, b, 0, st, fine[0], last);
-      else hipLaunchKernelGGL((gemv_fine_single<UG_W_PACK5, false>), g, b, 0, st, fine[0], last);
+      if (level == 2) UG_SINGLE(UG_W_PACK5, 2); else if (level == 1) UG_SINGLE(UG_W_PACK5, 1); else UG_SINGLE(UG_W_PACK5, 0);
     } else {
-      if (shrt) hipLaunchKernelGGL((gemv_fine_single<UG_W_I8, true>), g, b, 0, st, fine[0], last);
-      else hipLaunchKernelGGL((gemv_fine_single<UG_W_I8, false>), g, b, 0, st, fine[0], last);
+      if (level == 2) UG_SINGLE(UG_W_I8, 2); else if (level == 1) UG_SINGLE(UG_W_I8, 1); else UG_SINGLE(UG_W_I8, 0);
     }
+#undef UG_SINGLE
     return hipGetLastError();
   }
   const int grid = (int)blocks.size();

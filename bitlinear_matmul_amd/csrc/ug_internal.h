@@ -100,9 +100,10 @@ struct GemvBlock {
 // Plans a group of problems for the matrix-core GEMV: picks the split (fine
 // or stream), fills mb, items and item_begin of every descriptor and one
 // table entry per block to launch.  Returns the variant
-// (2048 * chunked + 1024 * short + 512 * fused + 256 * fine + 16 * wfmt + mb;
-// fused: the fine split with fp32 activations; short: the fine split's
-// variant for at most 4 pieces and 2 activation tiles per wave; chunked: the
+// (4096 * tiny + 2048 * chunked + 1024 * short + 512 * fused + 256 * fine +
+// 16 * wfmt + mb; fused: the fine split with fp32 activations; short: the
+// fine split's variant for at most 4 pieces and 2 activation tiles per wave;
+// tiny (with short): at most 3 pieces and 1 tile per wave; chunked: the
 // stream split staging activations chunk by chunk, when some problem's rows
 // do not fit the staging area), or -1 if the problems cannot share a launch.
 // The fine split fills `fine` (and leaves `blocks` empty), the stream split

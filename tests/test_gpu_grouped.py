@@ -109,22 +109,25 @@ def test_grouped_parity(dev, gi, fused):
         assert_y_close(host(p["y"]), y_r, "y %d" % i)
 
 
-# (M, N, K, fused, short): one problem each; plan.info.variant bit 8 = fine
-# split, bit 10 = its short variant (at most 4 pieces and 2 activation tiles
-# per wave).
+# (M, N, K, fused, short, tiny): one problem each; plan.info.variant bit 8 =
+# fine split, bit 10 = its short variant (at most 4 pieces and 2 activation
+# tiles per wave), bit 12 = the tiny one (with bit 10: at most 3 pieces and 1
+# tile per wave).
 FINE_VARIANTS = [
-    (1, 2560, 2560, True, True),     # decode-sized
-    (4, 1000, 384, True, True),      # 12 fp32 tiles: 2 per wave
-    (1, 16, 20000, False, False),    # one item of 63 steps: 8 pieces per wave
-    (16, 6912, 2560, False, False),  # 48 x_q tiles: 6 per wave
-    (16, 512, 2560, True, False),    # 160 fp32 tiles: 20 per wave (3 batches)
+    (1, 2560, 2560, True, True, False),     # decode-sized: 10 fp32 tiles per block
+    (4, 1000, 384, True, True, False),      # 12 fp32 tiles: 2 per wave
+    (1, 16, 20000, False, False, False),    # one item of 63 steps: 8 pieces per wave
+    (16, 6912, 2560, False, False, False),  # 48 x_q tiles: 6 per wave
+    (16, 512, 2560, True, False, False),    # 160 fp32 tiles: 20 per wave (3 batches)
+    (1, 4096, 384, True, True, True),       # 3 fp32 tiles, 2 pieces per block
+    (1, 2560, 2560, False, True, True),     # 3 x_q tiles, 8 pieces per block
 ]
 
 
 @pytest.mark.parametrize("ci", range(len(FINE_VARIANTS)))
 def test_fine_variants(dev, ci):
-    M, N, K, fused, short = FINE_VARIANTS[ci]
-    _case("fine variant", M, N, K, fused, short)
+    M, N, K, fused, short, tiny = FINE_VARIANTS[ci]
+    _case("fine variant", M, N, K, fused, short, tiny)
     rng = np.random.default_rng([303, ci])
     x = rng.standard_normal((M, K), dtype=np.float32)
     wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
@@ -141,6 +144,7 @@ def test_fine_variants(dev, ci):
     plan = ug.ug_gemv_plan_init([p])
     assert (plan.info.variant >> 8) & 1 == 1, "fine split"
     assert bool((plan.info.variant >> 10) & 1) == short, "variant %#x" % plan.info.variant
+    assert bool((plan.info.variant >> 12) & 1) == tiny, "variant %#x" % plan.info.variant
     ug.ug_bitlinear_gemv_grouped(plan)
     if fused:
         assert_bits_equal(host(p["xq"]), xq_r, "x_q")
