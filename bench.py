@@ -73,16 +73,16 @@ def parse():
 # Valid only for the kernel sources they were taken on: `src_sha` is the
 # SHA-256 of the kernel's source file; any other source reports null.
 TRAFFIC = {
-    # profiles/gemv_fine_grouped_decode_stack.md: 2012.5 KiB fetched x 1.9997,
+    # profiles/gemv_fine_grouped_decode_stack.md: 1990.9 KiB fetched x 1.9997,
     # 146.4 KiB written x 1.0000
     "decode_stack": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
-                         src_sha="620954f42826ae3101abb962d14387b9248a28a0aaef14634092976b4d5d1839",
-                         bytes_per_launch=4270769),
+                         src_sha="1aae82af7e9516601044d9b7a23aec2baef46e0964b8951dc49212bf55f17d0a",
+                         bytes_per_launch=4226741),
     # profiles/gemv_stream_grouped_sweep_m1.md: M=1 2560->6912, 37 problems per
-    # launch: 64224.1 KiB fetched x 1.9997, 705.3 KiB written x 1.0000
+    # launch: 64217.2 KiB fetched x 1.9997, 697.6 KiB written x 1.0000
     "sweep": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
-                  src_sha="620954f42826ae3101abb962d14387b9248a28a0aaef14634092976b4d5d1839",
-                  bytes_per_launch=132236704),
+                  src_sha="1aae82af7e9516601044d9b7a23aec2baef46e0964b8951dc49212bf55f17d0a",
+                  bytes_per_launch=132214235),
     # profiles/gemm_i8_large_prefill.md: mean of both shapes, 60190.6 KiB
     # fetched x 1.9997, 75776.0 KiB written x 1.0000
     "prefill": dict(src="bitlinear_matmul_amd/csrc/gemm.hip",
@@ -241,7 +241,7 @@ def run_decode_stack(args, torch, ug, inputs):
                        "us_per_token_pass": ms * 1e3 / steps,
                        "hot_us_per_token_pass": ms_hot * 1e3 / steps,
                        "hot_weight_GBps": per_pass_bytes * steps / (ms_hot / 1e3) / 1e9},
-               roofline=dict(bound="hbm", kernel="gemv_fine_grouped<PACK5, fused, short>",
+               roofline=dict(bound="hbm", kernel="gemv_fine_grouped<PACK5, fused, tiny>",
                              achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("decode_stack"),
                              avg_launch_us=avg_launch_s * 1e6, alg_bytes_per_launch=alg))
