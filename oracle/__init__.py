@@ -16,11 +16,14 @@ through ctypes.  Each function cites the passage of the pages it follows:
 * "ultragraph-1bit 0.12.0" README, sections "A whole ternary GPT" and
   "Layout" -- five ternary values per byte.
 
-Parity unpinned: the exact fp32 bits of the RMSNorm output (and so of
-``rmsnorm_quant_act``) and of beta are fixed only by the summation orders this
-oracle states; the pages give no order.  Their pins are bounds (fsum within
-the rounding-error bound, float64 RMSNorm within its bound) and exact special
-cases, not exact bits.
+The pages give no summation order for beta or for the RMSNorm sum of
+squares; this oracle states one (see ugref.c).  Those orders are pinned
+bit for bit by hand-worked fixtures (tests/golden/absmean_order.txt,
+row_order.txt) on which any other lane map, fold or stage-2 assignment gives
+different bits; the true divisions, round-half-even and the (s*beta)
+grouping of the rescale are pinned by tests/golden/rounding_cases.txt.
+tests/test_oracle_mutants.py plants each of those slips in a copy of
+ugref.c and checks that a pin fails.
 """
 import ctypes
 import os
@@ -47,6 +50,31 @@ def _load():
     path = _build.LIB
     if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
         _build.build()
+    _lib = _open(path)
+    return _lib
+
+
+class use_library:
+    """Context manager that points every function of this module at another
+    build of the oracle for the duration of a with-block (the pin tests use
+    it to check that deliberately wrong builds fail them)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.prev = _lib
+        _lib = _open(self.path)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.prev
+        return False
+
+
+def _open(path):
     lib = ctypes.CDLL(path)
     sig = {
         "ugref_quant_act": (None, [_f32p, _i64, _i64, _i64, _f32, _i8p, _i64, _f32p]),
@@ -68,7 +96,6 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
 
 

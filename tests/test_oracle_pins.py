@@ -476,3 +476,211 @@ def test_oracle_thread_count_invariance():
         outs.append(subprocess.run([sys.executable, "-c", code], env=env, check=True,
                                    capture_output=True, text=True).stdout.strip())
     assert outs[0] == outs[1] and len(outs[0]) == 64
+
+
+# ---------------------------------------------------------------------------
+# Order-sensitive and rounding-sensitive fixtures (tests/golden/*_order.txt,
+# rounding_cases.txt).  The bounds above hold for any summation order and
+# either rounding of a quotient; these cases hold for the stated ones only.
+# ---------------------------------------------------------------------------
+from fractions import Fraction  # noqa: E402
+
+
+def f32_rne(v):
+    """The binary32 value nearest to the exact rational v, ties to even
+    (normal and subnormal range; no overflow handling is needed here)."""
+    v = Fraction(v)
+    if v == 0:
+        return np.float32(0.0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    q = max(e - 23, -149)  # weight of the last significand bit
+    scaled = a / (Fraction(2) ** q)
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return np.float32(sign * float(n * Fraction(2) ** q))
+
+
+def rne_int(v):
+    """Round an exact rational to the nearest integer, ties to even."""
+    v = Fraction(v)
+    n = v.numerator // v.denominator
+    rem = v - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+def half_away_int(v):
+    v = Fraction(v)
+    n = int(abs(v) + Fraction(1, 2))
+    return n if v >= 0 else -n
+
+
+def F(x):
+    return Fraction(float(x))
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.startswith("#") or "|" not in line:
+                continue
+            rows.append([c.strip() for c in line.split("|")])
+    return rows
+
+
+def test_f32_rne_helper():
+    """The test's own rounding agrees with numpy's binary32 arithmetic on
+    sums, products and quotients (each correctly rounded by IEEE 754)."""
+    rng = np.random.default_rng(40)
+    a = rng.standard_normal(2000, dtype=np.float32) * np.float32(37.0)
+    b = rng.standard_normal(2000, dtype=np.float32) + np.float32(0.01)
+    for x, y in zip(a[:400], b[:400]):
+        assert f32_rne(F(x) + F(y)) == np.float32(x + y)
+        assert f32_rne(F(x) * F(y)) == np.float32(x * y)
+        assert f32_rne(F(x) / F(y)) == np.float32(x / y)
+    assert f32_rne(Fraction(2 ** 24 + 1)) == np.float32(2 ** 24)
+    assert f32_rne(Fraction(2 ** 24 + 3)) == np.float32(2 ** 24 + 4)
+    assert f32_rne(Fraction(1, 2 ** 149)) == np.float32(2.0 ** -149)
+
+
+def test_absmean_stated_order_fixtures():
+    """tests/golden/absmean_order.txt: every lane, fold level and stage-2
+    assignment of the stated two-stage order, each case hand-worked."""
+    for name, shape, sets, expect, _why in _read_table("absmean_order.txt"):
+        N, K = (int(v) for v in shape.split())
+        W = np.zeros((N, K), np.float32)
+        for kv in sets.split():
+            pos, val = kv.split("=")
+            W.flat[int(pos)] = np.float32(float(val))
+        T = oracle.absmean_sum(W)
+        assert T == np.float32(float(expect)), (name, float(T))
+        # beta = fl(fl(T / n) + eps) on the same tensor
+        _, beta = oracle.quant_weight_absmean(W)
+        assert beta == f32_rne(F(f32_rne(F(T) / (N * K))) + F(EPS32)), name
+
+
+def test_row_sum_squares_stated_order_fixtures():
+    """tests/golden/row_order.txt: the slot map, the in-slot order and every
+    fold level of the RMSNorm sum of squares, each case hand-worked."""
+    for name, K, sets, expect, _why in _read_table("row_order.txt"):
+        x = np.zeros(int(K), np.float32)
+        for kv in sets.split():
+            pos, val = kv.split("=")
+            x[int(pos)] = np.float32(float(val))
+        T = oracle.row_sum_squares(x)
+        assert T == np.float32(float(expect)), (name, float(T))
+        # the RMSNorm built on it: r = sqrt(fl(fl(T/K) + eps)), x_n = fl(x/r)
+        xn = oracle.rmsnorm(x[None, :])
+        ms = f32_rne(F(T) / int(K))
+        r = np.sqrt(np.float32(f32_rne(F(ms) + F(EPS32))))  # binary32 sqrt, correctly rounded
+        assert xn[0, 0] == f32_rne(F(x[0]) / F(r)), name
+
+
+def _rounding_rows(kind):
+    out = []
+    with open(os.path.join(GOLDEN, "rounding_cases.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            parts = line.split()
+            if parts[0] == kind:
+                out.append(parts[1:])
+    return out
+
+
+def test_act_quant_true_division_cases():
+    """Activation code by the correctly rounded quotient and round half to
+    even ("the bytes"), on rows where a reciprocal product or rounding half
+    away from zero gives a different code."""
+    rows = _rounding_rows("act")
+    assert len(rows) >= 5
+    for a_s, x_s, *_ in rows:
+        a, x = np.float32(float.fromhex(a_s)), np.float32(float.fromhex(x_s))
+        xq, s = oracle.quant_act(np.array([[a, x]], np.float32))
+        s_exp = f32_rne(F(f32_rne(F(a) / 127)) + F(EPS32))
+        assert s[0] == s_exp
+        q = f32_rne(F(x) / F(s_exp))
+        code = max(-127, min(127, rne_int(F(q))))
+        assert int(xq[0, 1]) == code, (a_s, x_s)
+        # the case separates the stated reading from at least one other
+        q_rcp = f32_rne(F(x) * F(f32_rne(Fraction(1) / F(s_exp))))
+        others = {max(-127, min(127, rne_int(F(q_rcp)))),
+                  max(-127, min(127, half_away_int(F(q))))}
+        assert others != {code}, (a_s, x_s)
+
+
+def test_act_scale_divides_by_127():
+    """s = fl(fl(a / 127) + eps) exactly, over many row maxima, and the
+    alternative fl(a * fl(1/127)) differs on some of them."""
+    rng = np.random.default_rng(41)
+    a = np.abs(rng.standard_normal(3000, dtype=np.float32)) * np.float32(9.0)
+    a = np.maximum(a, np.float32(1e-3))
+    _, s = oracle.quant_act(a[:, None])
+    r127 = f32_rne(Fraction(1, 127))
+    differs = 0
+    for ai, si in zip(a, s):
+        assert si == f32_rne(F(f32_rne(F(ai) / 127)) + F(EPS32))
+        differs += f32_rne(F(ai) * F(r127)) != f32_rne(F(ai) / 127)
+    assert differs > 0
+
+
+def test_ternary_true_division_cases():
+    rows = _rounding_rows("tern")
+    assert len(rows) >= 3
+    for A_s, w_s, *_ in rows:
+        A, w = np.float32(float.fromhex(A_s)), np.float32(float.fromhex(w_s))
+        wq, beta = oracle.quant_weight_absmean(np.array([[A, w]], np.float32))
+        T = f32_rne(abs(F(A)) + abs(F(w)))
+        b_exp = f32_rne(F(f32_rne(F(T) / 2)) + F(EPS32))
+        assert beta == b_exp
+        q = f32_rne(F(w) / F(b_exp))
+        code = max(-1, min(1, rne_int(F(q))))
+        assert int(wq[0, 1]) == code, (A_s, w_s)
+        q_rcp = f32_rne(F(w) * F(f32_rne(Fraction(1) / F(b_exp))))
+        others = {max(-1, min(1, rne_int(F(q_rcp)))), max(-1, min(1, half_away_int(F(q))))}
+        assert others != {code}, (A_s, w_s)
+
+
+def test_epilogue_grouping_cases():
+    """y = fl(float(acc) * fl(s * beta)): the grouping of the forward
+    formula ("autograd on a byte-graph"), on inputs where both other
+    groupings round differently."""
+    rows = _rounding_rows("epi")
+    assert len(rows) >= 3
+    for acc_s, s_s, b_s in rows:
+        acc = int(acc_s)
+        s, b = np.float32(float.fromhex(s_s)), np.float32(float.fromhex(b_s))
+        y = oracle.epilogue(np.array([[acc]], np.int32), np.array([s], np.float32), b)
+        exp = f32_rne(acc * F(f32_rne(F(s) * F(b))))
+        assert y[0, 0] == exp, acc_s
+        assert f32_rne(F(f32_rne(acc * F(s))) * F(b)) != exp
+        assert f32_rne(F(f32_rne(acc * F(b))) * F(s)) != exp
+
+
+def test_rmsnorm_exact_given_sum():
+    """Given the row's sum of squares T (whose order the fixtures above pin),
+    every RMSNorm output is r = sqrt(fl(fl(T/K) + eps)) correctly rounded and
+    x_n = fl(fl(x / r) * g) ("attention, as graph ops": divide by the root,
+    then the fp32 gain), checked with exact rationals."""
+    rng = np.random.default_rng(42)
+    for K in (5, 300, 2560):
+        x = rng.standard_normal((3, K), dtype=np.float32) * np.float32(2.5)
+        g = np.float32(1.0) + rng.standard_normal(K, dtype=np.float32) * np.float32(0.2)
+        xn = oracle.rmsnorm(x, g)
+        for m in range(3):
+            T = oracle.row_sum_squares(x[m])
+            v = f32_rne(F(f32_rne(F(T) / K)) + F(EPS32))
+            r = f32_rne(Fraction(math.sqrt(float(v))))  # float64 sqrt, then binary32
+            # r is the correctly rounded binary32 root of v: (r -+ half ulp)^2 bracket v
+            ulp = F(np.spacing(r))
+            assert (F(r) - ulp / 2) ** 2 <= F(v) <= (F(r) + ulp / 2) ** 2
+            for k in range(0, K, max(1, K // 97)):
+                assert xn[m, k] == f32_rne(F(f32_rne(F(x[m, k]) / F(r))) * F(g[k])), (K, m, k)
