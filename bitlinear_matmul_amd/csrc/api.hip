@@ -211,6 +211,7 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
   std::vector<ug::GemvBlock> blocks;
   std::vector<ug::FineBlock> fine;
   const int variant = ug::gemv_plan(descs.data(), count, blocks, fine);
+  if (variant == -2) return UG_ERR_UNSUPPORTED;
   if (variant < 0) return UG_ERR_INVALID_ARG;
   const size_t nblocks = fine.empty() ? blocks.size() : fine.size();
   if (nblocks == 0 || nblocks > (size_t)ug::kGemvBlocks) return UG_ERR_UNSUPPORTED;
@@ -257,25 +258,32 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *i
 size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t wfmt) {
   if (M < 1 || N < 1 || K < 1 || (wfmt != UG_W_I8 && wfmt != UG_W_PACK5)) return 0;
   const size_t dec = wfmt == UG_W_PACK5 ? (size_t)(N * ug::round_up(K, 16)) : 0;
-  return (M >= 512 && N >= 512 ? ug::gemm_split_area_bytes() : 0) + dec;
+  if (M >= 512 && N >= 512) return ug::gemm_split_area_bytes() + dec;
+  return dec ? ug::kGemmCounterBytes + dec : 0;
 }
 
-ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const void *w,
-                            int32_t wfmt, int64_t ldw, const float *beta, int64_t M, int64_t N,
-                            int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy,
-                            void *ws, size_t ws_bytes, void *stream) {
+namespace {
+
+ug_status gemm_common(const int8_t *xq, int64_t ldx, const float *s, const void *w, int32_t wfmt,
+                      int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
+                      int32_t *acc, int64_t ldacc, float *y, int64_t ldy, void *ws,
+                      size_t ws_bytes, int tile, int splits, void *stream) {
   ug_status st = check_matmul(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy);
   if (st != UG_OK) return st;
   hipStream_t hs = as_stream(stream);
   const size_t dec = wfmt == UG_W_PACK5 ? (size_t)(N * ug::round_up(K, 16)) : 0;
+  const size_t cnt = ug::kGemmCounterBytes;
   if (ws != nullptr && !aligned16(ws)) return UG_ERR_WORKSPACE;
-  if (wfmt == UG_W_PACK5 && (ws == nullptr || ws_bytes < dec)) return UG_ERR_WORKSPACE;
+  if (wfmt == UG_W_PACK5 && (ws == nullptr || ws_bytes < cnt + dec)) return UG_ERR_WORKSPACE;
   // Layout, decided by the workspace size alone (so that calls of any shape
-  // sharing one workspace agree): with room for both, the split area starts
-  // the workspace and the decoded weights follow it; otherwise the decoded
-  // weights start it and no block shares a tile.
+  // sharing one workspace agree): the first kGemmCounterBytes always belong
+  // to the K-split counters.  With room for the whole split area and the
+  // decoded weights, the split area starts the workspace and the decoded
+  // weights follow it; otherwise the decoded weights follow the counter
+  // bytes and no block shares a tile.  Decoded weights never land on a
+  // counter word.
   void *split = nullptr;
-  size_t dec_off = 0;
+  size_t dec_off = cnt;
   const size_t area = ug::gemm_split_area_bytes();
   if (ws != nullptr && ws_bytes >= area + dec) {
     split = ws;
@@ -287,10 +295,30 @@ ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const
     hipError_t e = ug::launch_unpack((const uint8_t *)w, ldw, N, K, wu, ldu, nullptr, hs);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(ug::launch_gemm_i8(xq, ldx, s, wu, ldu, beta, M, N, K, acc, ldacc, y, ldy,
-                                         split, hs));
+                                         split, tile, splits, hs));
   }
   return hip_status(ug::launch_gemm_i8(xq, ldx, s, (const int8_t *)w, ldw, beta, M, N, K, acc,
-                                       ldacc, y, ldy, split, hs));
+                                       ldacc, y, ldy, split, tile, splits, hs));
+}
+
+}  // namespace
+
+ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const void *w,
+                            int32_t wfmt, int64_t ldw, const float *beta, int64_t M, int64_t N,
+                            int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy,
+                            void *ws, size_t ws_bytes, void *stream) {
+  return gemm_common(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy, ws, ws_bytes,
+                     -1, -1, stream);
+}
+
+ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s, const void *w,
+                                  int32_t wfmt, int64_t ldw, const float *beta, int64_t M,
+                                  int64_t N, int64_t K, int32_t *acc, int64_t ldacc, float *y,
+                                  int64_t ldy, void *ws, size_t ws_bytes, int32_t tile,
+                                  int32_t k_splits, void *stream) {
+  if (tile < -1 || tile > 1 || k_splits == 0 || k_splits < -1) return UG_ERR_INVALID_ARG;
+  return gemm_common(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy, ws, ws_bytes,
+                     tile, k_splits, stream);
 }
 
 }  // extern "C"

@@ -18,8 +18,8 @@
 #include "ug_internal.h"
 
 #include <atomic>
-#include <cstdio>
-#include <cstdlib>
+#include <chrono>
+#include <random>
 #include <type_traits>
 
 namespace ug {
@@ -652,6 +652,7 @@ namespace {
 
 constexpr int kSplitMaxBlocks = 256;  // blocks (and partial tiles) of a split launch
 constexpr int kSplitCounterBytes = 8 * kSplitMaxBlocks;
+static_assert(kSplitCounterBytes == (int)kGemmCounterBytes, "counter area size");
 
 // the large tiles pay off once there are enough of them; they address the
 // operands with 32-bit buffer offsets
@@ -662,22 +663,40 @@ bool large_tiles(int64_t M, int64_t N, int64_t ldx, int64_t ldw) {
 
 // compute units of the current device (cached per device)
 int device_cus() {
-  static int cache[64];
+  // a value per device; threads that race to fill it store the same value
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
-// Launch epochs of split launches: 56-bit, never 0, one per launch in the
-// process.
+// Launch epochs of split launches: 56-bit, never 0, one per launch.  They
+// start at a random point per process, so counter words left in a
+// workspace by another process, by an earlier run, or by unrelated data
+// (which would have to equal epoch << 8 | arrivals in all 56 upper bits)
+// match a live launch with odds of about 2^-56.
+unsigned long long epoch_base() {
+  unsigned long long b = 0;
+  try {
+    std::random_device rd;
+    b = ((unsigned long long)rd() << 32) ^ (unsigned long long)rd();
+  } catch (...) {
+  }
+  // mixed with the clock and the address of a local, in case the device
+  // above is deterministic
+  b ^= (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() *
+       0x9E3779B97F4A7C15ull;
+  b ^= (unsigned long long)(uintptr_t)&b;
+  return b;
+}
 unsigned long long next_epoch() {
-  static std::atomic<unsigned long long> e{0};
+  static std::atomic<unsigned long long> e{epoch_base()};
   unsigned long long v = (e.fetch_add(1) + 1) & ((1ull << 56) - 1);
   return v == 0 ? 1 : v;
 }
@@ -735,11 +754,6 @@ void launch_large(const LargePlan &p, hipStream_t st, const int8_t *xq, int64_t 
                      cnt, epoch);
 }
 
-long env_int(const char *name, long dflt) {
-  const char *f = std::getenv(name);
-  return f ? std::strtol(f, nullptr, 10) : dflt;
-}
-
 }  // namespace
 
 // The area has a fixed layout (counters at offset 0, then the partial
@@ -755,21 +769,24 @@ size_t gemm_split_area_bytes() {
 hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const int8_t *w,
                           int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
                           int32_t *acc, int64_t ldacc, float *y, int64_t ldy, void *split,
-                          hipStream_t st) {
+                          int tile, int splits, hipStream_t st) {
   if (large_tiles(M, N, ldx, ldw)) {
     const int64_t nk = ceil_div(K, LBK);
     const int cus = device_cus();
     LargePlan p = plan_large(M, N, nk, split != nullptr, cus > 0 ? cus : 256);
-    // test hooks: UG_GEMM_FORCE_SHAPE = 0, 1 (256 x 256, 256 x 160 tiles)
-    // and UG_GEMM_FORCE_SPLITS = n ask for that shape / split count where
-    // they fit
-    const long fs = env_int("UG_GEMM_FORCE_SHAPE", -1), fk = env_int("UG_GEMM_FORCE_SPLITS", -1);
-    if (fs >= 0 && fs < kNumShapes) {
-      p.shape = (int)fs;
-      p.T = ceil_div(M, LBM) * ceil_div(N, 32 * kShapes[fs].nt);
+    // an explicit tile shape (0: 256 x 256, 1: 256 x 160) and split count
+    // replace the model's choice where they fit
+    if (tile >= 0 && tile < kNumShapes) {
+      p.shape = tile;
+      p.T = ceil_div(M, LBM) * ceil_div(N, 32 * kShapes[tile].nt);
       p.S = 1;
     }
-    if (fk >= 1 && split != nullptr && fk <= nk && p.T * fk <= kSplitMaxBlocks) p.S = (int)fk;
+    if (splits >= 1) {
+      if (split != nullptr && splits <= nk && p.T * splits <= kSplitMaxBlocks)
+        p.S = splits;
+      else
+        p.S = 1;
+    }
     int32_t *part = nullptr;
     unsigned long long *cnt = nullptr;
     unsigned long long epoch = 0;
@@ -778,10 +795,6 @@ hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const i
       part = reinterpret_cast<int32_t *>(static_cast<char *>(split) + kSplitCounterBytes);
       epoch = next_epoch();
     }
-    if (env_int("UG_GEMM_VERBOSE", 0))
-      std::fprintf(stderr, "ug gemm M=%lld N=%lld K=%lld: tile 256x%d, %lld tiles, %d K splits\n",
-                   (long long)M, (long long)N, (long long)K, 32 * kShapes[p.shape].nt,
-                   (long long)p.T, p.S);
     if (p.shape == 0)
       launch_large<2, 8>(p, st, xq, ldx, s, w, ldw, beta, M, N, K, acc, ldacc, y, ldy, part, cnt,
                          epoch);

@@ -1609,6 +1609,11 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
     total += d.items;
   }
   if (total > INT32_MAX) return -1;
+  // the chunked kernel reads x_q only: a group that needs it cannot also
+  // quantize fp32 activations in the launch
+  if (chunked)
+    for (int i = 0; i < count; ++i)
+      if (descs[i].x != nullptr) return -2;
   const int grid = gemv_grid(total);
   fine.clear();
   int p = 0;

@@ -105,7 +105,9 @@ struct GemvBlock {
 // fine split's variant for at most 4 pieces and 2 activation tiles per wave;
 // tiny (with short): at most 3 pieces and 1 tile per wave; chunked: the
 // stream split staging activations chunk by chunk, when some problem's rows
-// do not fit the staging area), or -1 if the problems cannot share a launch.
+// do not fit the staging area), -1 if the problems cannot share a launch, or
+// -2 if the group needs the chunked split and also has fp32 activations to
+// quantize (the chunked kernel takes x_q only).
 // The fine split fills `fine` (and leaves `blocks` empty), the stream split
 // fills `blocks`.
 int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
@@ -126,13 +128,18 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
 // Bytes of the GEMM's K-split area (tile counters at offset 0, then one
 // partial tile per block); the same size and layout for every shape.
 size_t gemm_split_area_bytes();
+// Bytes at the start of a GEMM workspace that hold the K-split tile
+// counters; nothing else is ever written there.
+constexpr size_t kGemmCounterBytes = 2048;
 // split: NULL, or gemm_split_area_bytes() bytes of device memory (any
-// contents: counters are tagged per launch).
+// contents: counters are tagged per launch).  tile: -1 (the time model's
+// choice), 0 (256 x 256 tiles) or 1 (256 x 160); splits: -1 (the model's
+// choice) or a K-split count, used where it fits (else 1).
 hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s,
                           const int8_t *w, int64_t ldw, const float *beta,
                           int64_t M, int64_t N, int64_t K, int32_t *acc,
                           int64_t ldacc, float *y, int64_t ldy, void *split,
-                          hipStream_t st);
+                          int tile, int splits, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Device helpers

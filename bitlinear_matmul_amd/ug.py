@@ -52,7 +52,11 @@ SIGNATURES = {
     "ug_bitlinear_gemv_grouped": (_i32, [_vp, _vp, _vp]),
     "ug_bitlinear_gemm": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
                                  _i64, _vp, _i64, _vp, _sz, _vp]),
+    "ug_bitlinear_gemm_tiled": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64,
+                                       _vp, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp]),
 }
+
+UG_GEMM_COUNTER_BYTES = 2048
 
 _lib = None
 
@@ -259,11 +263,12 @@ def gemm_workspace(need, device):
 
 
 def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=False,
-                      want_y=True, ws=None, split=True, stream=None):
+                      want_y=True, ws=None, split=True, tile=None, k_splits=None, stream=None):
     """Prefill GEMM (int8 MFMA): same arguments as the GEMV, any M.
     ws: workspace (default: the shared per-device one); split=False passes
     only what UG_W_PACK5 decoding needs, so every block computes whole
-    tiles."""
+    tiles.  tile / k_splits (ug_bitlinear_gemm_tiled): force the tile shape
+    (0: 256 x 256, 1: 256 x 160) and the K-split count."""
     M = xq.shape[0]
     K = xq.shape[1] if K is None else K
     N, ldw = _weight_args(w, wfmt, K)
@@ -273,20 +278,24 @@ def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=F
         y = empty_pitched(M, N, torch.float32, xq.device)
     need = ug_bitlinear_gemm_workspace_size(M, N, K, wfmt)
     if not split:
-        # a private buffer for the decoded weights alone: written at offset
-        # 0, it must not land on the shared workspace's counters
-        need = N * (-(-K // 16) * 16) if wfmt == UG_W_PACK5 else 0
+        # a private buffer with room for the decoded weights only (they
+        # follow the counter bytes), too small for the split area
+        need = UG_GEMM_COUNTER_BYTES + N * (-(-K // 16) * 16) if wfmt == UG_W_PACK5 else 0
         if ws is None and need:
             ws = torch.empty(need, dtype=torch.uint8, device=xq.device)
     if ws is None and need:
         ws = gemm_workspace(need, xq.device)
     # the whole buffer: the library lays it out by its size alone
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(lib().ug_bitlinear_gemm(_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), M, N, K,
-                                   _p(acc), _ld(acc) if acc is not None else 0, _p(y),
-                                   _ld(y) if y is not None else 0,
-                                   _p(ws) if ws_bytes else None, ws_bytes,
-                                   _stream(stream)), "ug_bitlinear_gemm")
+    args = [_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), M, N, K,
+            _p(acc), _ld(acc) if acc is not None else 0, _p(y), _ld(y) if y is not None else 0,
+            _p(ws) if ws_bytes else None, ws_bytes]
+    if tile is None and k_splits is None:
+        _check(lib().ug_bitlinear_gemm(*args, _stream(stream)), "ug_bitlinear_gemm")
+    else:
+        _check(lib().ug_bitlinear_gemm_tiled(*args, -1 if tile is None else tile,
+                                             -1 if k_splits is None else k_splits,
+                                             _stream(stream)), "ug_bitlinear_gemm_tiled")
     return acc, y
 
 

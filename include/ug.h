@@ -36,8 +36,11 @@
  *  - Errors in the arguments are returned before anything is launched.
  *    Data-dependent problems (bad trits, bad codes) are counted into an
  *    optional caller device counter instead.
- *  - Calls are thread-safe: the library holds no mutable global state
- *    except a per-thread copy of the last HIP error.
+ *  - Calls are thread-safe.  The library's mutable state is: a per-thread
+ *    copy of the last HIP error; a per-device cache of the compute-unit
+ *    count (atomic, filled on first use); and the GEMM's counter of K-split
+ *    launches (atomic, seeded at random per process).  None of it changes
+ *    a result.
  */
 #ifndef UG_H
 #define UG_H
@@ -199,7 +202,11 @@ ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s,
  * UG_ERR_UNSUPPORTED.  Kp = S * U * ceil(ceil(B / 64) / U) with B the packed
  * row length (ceil(K/5) for UG_W_PACK5, K for UG_W_I8), S = 320 (UG_W_PACK5)
  * or 64 (UG_W_I8), and U the steps per unit of the row class: UG_W_PACK5
- * U = 2, 2, 1 for M <= 16, 17..32, 33..64; UG_W_I8 U = 4, 4, 2.  Weights of N * ldw >= 2^31 bytes or
+ * U = 2, 2, 1 for M <= 16, 17..32, 33..64; UG_W_I8 U = 4, 4, 2.  A group
+ * in which some problem's x_q rows do not fit that area (given as x_q) runs
+ * a kernel that takes x_q only; such a group cannot also hold a problem
+ * with x != NULL: UG_ERR_UNSUPPORTED (launch those separately).  Weights of
+ * N * ldw >= 2^31 bytes or
  * activations of M * ldxq >= 2^31 bytes are UG_ERR_UNSUPPORTED (32-bit
  * offsets), here and in ug_bitlinear_gemv.
  */
@@ -253,28 +260,32 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan,
 /*
  * Bytes of workspace ug_bitlinear_gemm can use: for M, N >= 512 the K-split
  * area (UG_GEMM_SPLIT_AREA bytes), plus, for UG_W_PACK5, N*round_up(K,16)
- * bytes of decoded weights.  0 for UG_W_I8 below 512 x 512.
+ * bytes of decoded weights.  Below 512 x 512: 0 for UG_W_I8, and
+ * UG_GEMM_COUNTER_BYTES + the decoded bytes for UG_W_PACK5.
  */
 size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
                                         int32_t wfmt);
 
 /* Size of the K-split area: 2 KB of tile counters, then 256 partial tiles of
  * 256 x 256 int32. */
-#define UG_GEMM_SPLIT_AREA (2048 + 256 * 256 * 256 * 4)
+#define UG_GEMM_COUNTER_BYTES 2048
+#define UG_GEMM_SPLIT_AREA (UG_GEMM_COUNTER_BYTES + 256 * 256 * 256 * 4)
 
 /*
  * Prefill GEMM: the same result as ug_bitlinear_gemv for any M >= 1, as a
  * dense int8 contraction on the matrix cores (ternary values are exact in
  * int8).  Same arguments, plus the workspace ws (device memory, 16-byte
- * aligned, any contents; NULL allowed for UG_W_I8):
+ * aligned, any contents; NULL allowed for UG_W_I8).  Its first
+ * UG_GEMM_COUNTER_BYTES only ever hold K-split tile counters:
  *   - ws_bytes >= UG_GEMM_SPLIT_AREA + decoded bytes: the split area starts
  *     ws and the decoded weights (UG_W_PACK5) follow it.  Problems with few
  *     output tiles may then share a tile's K steps between blocks ("K
  *     split"; integer partial sums, so the result is the same bits).
- *   - otherwise the decoded weights start ws and every block computes whole
- *     tiles.
- * UG_ERR_WORKSPACE if UG_W_PACK5 gets less than the decoded bytes or ws is
- * misaligned.  Calls that run at the same time must not share a workspace.
+ *   - otherwise the decoded weights follow the counter bytes and every
+ *     block computes whole tiles.
+ * UG_ERR_WORKSPACE if UG_W_PACK5 gets less than UG_GEMM_COUNTER_BYTES + the
+ * decoded bytes, or ws is misaligned.  Calls that run at the same time must
+ * not share a workspace.
  */
 ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s,
                             const void *w, int32_t wfmt, int64_t ldw,
@@ -282,6 +293,23 @@ ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s,
                             int64_t K, int32_t *acc, int64_t ldacc, float *y,
                             int64_t ldy, void *ws, size_t ws_bytes,
                             void *stream);
+
+/*
+ * ug_bitlinear_gemm with the tiling chosen by the caller instead of the
+ * library's time model: tile = -1 (model), 0 (256 x 256 output tiles) or 1
+ * (256 x 160), and k_splits = -1 (model) or >= 1 K splits per tile.  Both
+ * apply to problems of at least 512 x 512 only; a split count that does not
+ * fit (more than the K steps, more than 256 blocks, no split area in ws)
+ * runs unsplit.  The result is the same bits whatever the tiling.  For
+ * tests and tuning.  UG_ERR_INVALID_ARG for other tile or k_splits values.
+ */
+ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
+                                  const void *w, int32_t wfmt, int64_t ldw,
+                                  const float *beta, int64_t M, int64_t N,
+                                  int64_t K, int32_t *acc, int64_t ldacc,
+                                  float *y, int64_t ldy, void *ws,
+                                  size_t ws_bytes, int32_t tile,
+                                  int32_t k_splits, void *stream);
 
 #ifdef __cplusplus
 }

@@ -63,7 +63,8 @@ def test_workspace_formulas(ug):
         assert L.ug_quant_weight_absmean_workspace_size(N, K) == 4 * (-(-chunks // 256) * 256)
     assert L.ug_quant_weight_absmean_workspace_size(0, 5) == 0
     assert L.ug_bitlinear_gemm_workspace_size(16, 100, 37, ug.UG_W_I8) == 0
-    assert L.ug_bitlinear_gemm_workspace_size(16, 100, 37, ug.UG_W_PACK5) == 100 * 48
+    # packed weights are decoded after the 2 KB of counter words
+    assert L.ug_bitlinear_gemm_workspace_size(16, 100, 37, ug.UG_W_PACK5) == 2048 + 100 * 48
     # problems of at least 512 x 512 add the K-split area in front: 2 KB of
     # tile counters and 256 partial tiles of 256 KB
     split = 2048 + 256 * 256 * 256 * 4
@@ -72,7 +73,7 @@ def test_workspace_formulas(ug):
         dec = N * (-(-K // 16) * 16)
         assert L.ug_bitlinear_gemm_workspace_size(M, N, K, ug.UG_W_PACK5) == split + dec
     assert L.ug_bitlinear_gemm_workspace_size(511, 4096, 64, ug.UG_W_I8) == 0
-    assert L.ug_bitlinear_gemm_workspace_size(4096, 511, 64, ug.UG_W_PACK5) == 511 * 64
+    assert L.ug_bitlinear_gemm_workspace_size(4096, 511, 64, ug.UG_W_PACK5) == 2048 + 511 * 64
 
 
 def test_k_split_ranges_cover_each_tile_once():
@@ -198,3 +199,51 @@ def test_gemm_rejects(ug):
     assert call(wfmt=1, ldw=32) == ug.UG_ERR_WORKSPACE
     assert call(wfmt=1, ldw=32, ws=ctypes.c_void_p(0x700000), ws_bytes=64 * 128 - 1) == \
         ug.UG_ERR_WORKSPACE
+    # the decoded weights need the counter bytes in front of them too
+    assert call(wfmt=1, ldw=32, ws=ctypes.c_void_p(0x700000), ws_bytes=2048 + 64 * 128 - 1) == \
+        ug.UG_ERR_WORKSPACE
+
+
+def test_gemm_tiled_rejects(ug):
+    L = ug.lib()
+    E = ug.UG_ERR_INVALID_ARG
+
+    def call(tile, splits):
+        return L.ug_bitlinear_gemm_tiled(A, 128, A2, A3, 0, 128, A4, 300, 64, 128, NULL, 0, NULL,
+                                         64, NULL, 0, tile, splits, S)
+
+    assert call(2, -1) == E
+    assert call(-2, -1) == E
+    assert call(0, 0) == E
+    assert call(0, -3) == E
+    assert call(0, 1) == E   # still validates the matmul arguments (no output)
+
+
+def test_grouped_plan_rejects_fused_with_chunked(ug):
+    """A group that needs the chunked kernel (x_q rows too long for the
+    staging area) cannot also quantize fp32 activations in the launch: the
+    plan is refused before anything is copied to the device."""
+    L = ug.lib()
+    fused = ug.GemvProblem(x=0x100000, ldx=2560, eps=1e-5, xq=0, ldxq=0, s=0, w=0x200000,
+                           wfmt=ug.UG_W_PACK5, ldw=512, beta=0x300000, M=16, N=6912, K=2560,
+                           acc=0, ldacc=0, y=0x400000, ldy=6912)
+    given = ug.GemvProblem(x=0, ldx=0, eps=0.0, xq=0x500000, ldxq=6912, s=0x600000,
+                           w=0x700000, wfmt=ug.UG_W_PACK5, ldw=1392, beta=0x800000, M=16,
+                           N=2560, K=6912, acc=0, ldacc=0, y=0x900000, ldy=2560)
+    arr = (ug.GemvProblem * 2)(fused, given)
+    info = ug.GemvPlanInfo()
+    size = L.ug_gemv_plan_size(2)
+    st = L.ug_gemv_plan_init(ctypes.cast(arr, ctypes.c_void_p), 2, ctypes.c_void_p(0xA00000),
+                             size, ctypes.byref(info))
+    assert st == ug.UG_ERR_UNSUPPORTED
+    # each problem on its own passes validation and planning; without a
+    # device the plan copy then fails (with one, the fake address would be
+    # handed to a real copy: not done)
+    import torch
+    if torch.cuda.device_count() > 0:
+        return
+    for p in (fused, given):
+        one = (ug.GemvProblem * 1)(p)
+        st = L.ug_gemv_plan_init(ctypes.cast(one, ctypes.c_void_p), 1, ctypes.c_void_p(0xA00000),
+                                 L.ug_gemv_plan_size(1), ctypes.byref(info))
+        assert st == ug.UG_ERR_HIP

@@ -1,8 +1,8 @@
 """Invariants the pages state, checked on the GPU path itself (plus the
 oracle where a reference value is needed):
   - batch invariance: row m of the GEMM equals the GEMV on row m alone
-    (README "A whole ternary GPT": a cached step is byte-for-byte the full
-    forward), and GEMV at M rows equals GEMV per row;
+    (README "A whole ternary GPT": cached decoding must reproduce the
+    full-forward bits), and GEMV at M rows equals GEMV per row;
   - format invariance: 5-trits-per-byte weights give the same integers as
     one trit per byte (README: deployed logits are byte-exact);
   - row independence of the quantizers ("attention, as graph ops");

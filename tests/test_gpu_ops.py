@@ -301,21 +301,19 @@ def test_gemm_parity(dev, M, N, K, fmt):
 @pytest.mark.parametrize("M,N,K,splits", [(2048, 2560, 6912, None), (512, 6912, 2560, None),
                                           (1100, 1300, 1000, 2), (1100, 1300, 1000, 5),
                                           (600, 700, 197, 4), (512, 512, 64, 1)])
-def test_gemm_split_matches_whole_tiles(dev, M, N, K, splits, monkeypatch):
+def test_gemm_split_matches_whole_tiles(dev, M, N, K, splits):
     """K-split launches (a tile's K steps shared by several blocks, finished
     by the last one in) give the same bits as one whole tile per block, and
     leave the shared workspace ready: a second, smaller call through the
     same workspace is right too.  splits=None keeps the library's choice;
-    otherwise UG_GEMM_FORCE_SPLITS asks for that many (odd counts, counts
+    otherwise ug_bitlinear_gemm_tiled asks for that many (odd counts, counts
     that do not divide the K steps, one K step per split with the K tail in
     the last one)."""
     _print_case("gemm split", M, N, K, splits)
-    if splits is not None:
-        monkeypatch.setenv("UG_GEMM_FORCE_SPLITS", str(splits))
     rng = np.random.default_rng([113, M, N, K])
     xq, wq, s, beta = _rand_problem(rng, M, N, K)
     args = (pitched(xq), vec(s), pitched(wq), ug.UG_W_I8, scalar_dev(beta))
-    acc_s, y_s = ug.ug_bitlinear_gemm(*args, want_acc=True)
+    acc_s, y_s = ug.ug_bitlinear_gemm(*args, want_acc=True, k_splits=splits)
     acc_w, y_w = ug.ug_bitlinear_gemm(*args, want_acc=True, split=False)
     assert_bits_equal(host(acc_s), host(acc_w), "acc split vs whole")
     assert_bits_equal(host(y_s), host(y_w), "y split vs whole")
@@ -331,17 +329,16 @@ def test_gemm_split_matches_whole_tiles(dev, M, N, K, splits, monkeypatch):
 @pytest.mark.parametrize("shape", [0, 1])
 @pytest.mark.parametrize("M,N,K,splits", [(600, 700, 197, 1), (1100, 1300, 1000, 1),
                                           (1100, 1300, 1000, 3), (512, 2560, 6912, 2)])
-def test_gemm_tile_shapes(dev, shape, M, N, K, splits, monkeypatch):
+def test_gemm_tile_shapes(dev, shape, M, N, K, splits):
     """Each large-tile shape (256 x 256 and 256 x 160 output tiles),
     whole or K-split, against the oracle: ragged M, N and K edges, partial
     tiles of every column-piece width in the output pass."""
     _print_case("gemm shape", shape, M, N, K, splits)
-    monkeypatch.setenv("UG_GEMM_FORCE_SHAPE", str(shape))
-    monkeypatch.setenv("UG_GEMM_FORCE_SPLITS", str(splits))
     rng = np.random.default_rng([127, M, N, K])
     xq, wq, s, beta = _rand_problem(rng, M, N, K)
     acc_d, y_d = ug.ug_bitlinear_gemm(pitched(xq), vec(s), pitched(wq), ug.UG_W_I8,
-                                      scalar_dev(beta), want_acc=True)
+                                      scalar_dev(beta), want_acc=True, tile=shape,
+                                      k_splits=splits)
     acc_r = oracle.matmul_i32(xq, wq)
     assert_bits_equal(host(acc_d), acc_r, "acc")
     assert_bits_equal(host(y_d), oracle.epilogue(acc_r, s, beta), "y")
@@ -368,10 +365,13 @@ def test_gemm_split_after_packed_calls(dev):
     assert_bits_equal(host(acc_s), host(acc_w), "split vs whole after packed calls")
 
 
-def test_gemm_split_any_workspace_contents(dev, monkeypatch):
-    """The split counters carry the launch they belong to, so a workspace
-    full of arbitrary bytes (or of counters from earlier launches) is fine."""
-    monkeypatch.setenv("UG_GEMM_FORCE_SPLITS", "3")
+def test_gemm_split_any_workspace_contents(dev):
+    """The split counters carry the launch they belong to (a 56-bit launch
+    number that starts at random per process), so a workspace full of
+    arbitrary bytes, of counter words of small launch numbers (those of
+    launches 1..400 of any process), or of decoded trits (00/01/FF bytes)
+    is fine; and a packed-weight call that decodes into a workspace too
+    small for the split area leaves the counter bytes alone."""
     rng = np.random.default_rng(119)
     M, N, K = 1024, 1024, 1536
     xq, wq, s, beta = _rand_problem(rng, M, N, K)
@@ -380,10 +380,33 @@ def test_gemm_split_any_workspace_contents(dev, monkeypatch):
     ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=g).to("cuda:0")
     args = (pitched(xq), vec(s), pitched(wq), ug.UG_W_I8, scalar_dev(beta))
     acc_r = oracle.matmul_i32(xq, wq)
-    for rep in range(3):
-        acc_s, _ = ug.ug_bitlinear_gemm(*args, want_acc=True, ws=ws)
-        assert_bits_equal(host(acc_s), acc_r, "acc, garbage workspace, call %d" % rep)
-        ws[:2048] = torch.randint(0, 256, (2048,), dtype=torch.uint8, generator=g).to("cuda:0")
+    n_words = ug.UG_GEMM_COUNTER_BYTES // 8
+    fills = {
+        "random bytes": lambda: torch.randint(0, 256, (ug.UG_GEMM_COUNTER_BYTES,),
+                                              dtype=torch.uint8, generator=g),
+        "small epochs": lambda: torch.from_numpy(
+            ((np.arange(n_words, dtype=np.int64) % 400 + 1) << 8
+             | rng.integers(0, 8, n_words)).astype(np.int64)).view(torch.uint8),
+        "trit bytes": lambda: torch.from_numpy(
+            rng.choice(np.array([0, 1, 255], np.uint8), ug.UG_GEMM_COUNTER_BYTES)),
+    }
+    for name, fill in fills.items():
+        for rep in range(2):
+            ws[:ug.UG_GEMM_COUNTER_BYTES] = fill().to("cuda:0")
+            acc_s, _ = ug.ug_bitlinear_gemm(*args, want_acc=True, ws=ws, k_splits=3)
+            assert_bits_equal(host(acc_s), acc_r, "acc, %s, call %d" % (name, rep))
+    # a packed call whose decoded weights do not leave room for the split
+    # area: they go after the counter bytes, which stay as they were
+    before = ws[:ug.UG_GEMM_COUNTER_BYTES].clone()
+    xs, ws5, ss, bs = _rand_problem(rng, 300, 700, 1000)
+    pk = pitched(oracle.pack_trits(ws5)[0])
+    small = ws[:ug.UG_GEMM_COUNTER_BYTES + 700 * 1008]
+    acc5, _ = ug.ug_bitlinear_gemm(pitched(xs), vec(ss), pk, ug.UG_W_PACK5, scalar_dev(bs),
+                                   K=1000, want_acc=True, ws=small)
+    assert_bits_equal(host(acc5), oracle.matmul_i32(xs, ws5), "packed acc, small workspace")
+    assert torch.equal(ws[:ug.UG_GEMM_COUNTER_BYTES], before)
+    acc_s, _ = ug.ug_bitlinear_gemm(*args, want_acc=True, ws=ws, k_splits=3)
+    assert_bits_equal(host(acc_s), acc_r, "acc after the packed call")
 
 
 def test_gemm_extreme_values(dev):

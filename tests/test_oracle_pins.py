@@ -451,7 +451,8 @@ def test_packed_and_byte_formats_agree():
 
 def test_batch_invariance():
     """Row m of the batched result equals the result for row m alone
-    (README: a cached decode step is byte-for-byte the full forward)."""
+    (README "A whole ternary GPT": cached decoding must reproduce the
+    full-forward bits)."""
     x, W = inputs.tiny_layer()
     full = oracle.bitlinear(x, W)
     for m in (0, 13, 31):
