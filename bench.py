@@ -6,9 +6,14 @@ Prints ONE JSON line.  Workloads (default: decode_stack):
   decode_stack  batch-1 decode pass over 8 x {384->1152, 384->384,
                 384->1536, 1536->384} + a 384->4096 head, weights 5 trits per
                 byte; a step = per-row int8 quantization of each matrix's input
-                plus the GEMV of every matrix (33 x); each step reads its own
-                copy of the weights so they stream from HBM (cold).
-                value = packed-weight GB/s.
+                plus the GEMV of every matrix (33 x), one launch.  Every step
+                reads its own copy of the weights, the copies span >= 2 GiB,
+                and a 1 GiB write evicts the caches before each timed region,
+                so weights stream from HBM (cold).  value = packed-weight GB/s.
+                The same line also carries the prefill GEMM (4096 x 2560 ->
+                6912 and 4096 x 6912 -> 2560, int8 TOP/s) and the streaming
+                decode GEMV at M = 1, 2560 -> 6912 (weight GB/s), each with
+                its own roofline, as "prefill_gemm" and "stream_m1".
   sweep         decode GEMV at M in {1,4,16,64} x the three 2B-class shapes
                 (cold, cycling weight copies); value = weight GB/s over all
                 12 points.
@@ -20,11 +25,12 @@ Prints ONE JSON line.  Workloads (default: decode_stack):
   tiny          x[32,128] W[512,128]: the full path incl. weight quant.
 
 Inputs are seeded synthetic tensors (bitlinear_matmul_amd.inputs) already
-resident in HBM when timing starts.  Timing: W untimed steps, then K steps
-between torch.cuda.synchronize() calls (HIP events on the stream the
-kernels run on).  The dominant kernel's roofline fraction uses algorithmic
-bytes (or ops) per launch over its average launch duration, measured here
-with HIP events.  The CPU oracle is timed on a bounded sample of the same
+resident in HBM when timing starts.  Timing: W untimed steps, then exactly K
+steps between torch.cuda.synchronize() calls, timed with HIP events on the
+stream the kernels run on.  The dominant kernel's roofline fraction uses
+algorithmic bytes (or ops) per launch over its average launch duration in
+that timed region; the median over at least 50 further launches is reported
+beside it.  The CPU oracle is timed on a bounded sample of the same
 workload on the host cores.
 """
 import argparse
@@ -43,10 +49,62 @@ METRIC = "BitLinear GEMV weight GB/s (decode) and GEMM int8 TOPS (prefill), % ro
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 COLD_BYTES = 2 << 30  # weight copies to cycle through: >= 8x the 256 MB MALL
+FLUSH_BYTES = 1 << 30  # written before a timed region: evicts L2 and the MALL
+STAT_LAUNCHES = 60     # launches behind each reported median
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+class Flusher:
+    """A 1 GiB device buffer whose rewrite evicts the weights from L2 and
+    the MALL before a timed region (the write itself is never timed)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda:0")
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n)
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def launch_stats(torch, launch, stream, count=STAT_LAUNCHES, flush=None, per=1):
+    """Per-launch durations (us) of `count` timed calls of launch(i) (each
+    runs `per` back-to-back kernel launches), each between HIP events on
+    `stream`, optionally after a cache flush; returns (median, p10, p90)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(count)]
+    torch.cuda.synchronize()
+    for i in range(count):
+        if flush is not None:
+            flush()
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 / per for a, b in ev)
+    return median(us), us[len(us) // 10], us[(9 * len(us)) // 10]
 
 
 def parse():
@@ -57,6 +115,8 @@ def parse():
     p.add_argument("--workload", default="decode_stack",
                    choices=["decode_stack", "sweep", "prefill", "stack", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="decode_stack: skip the prefill-GEMM and M=1 streaming points")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--sweep-point", default=None, metavar="M,SHAPE",
                    help="sweep: run only the point with M rows and shape index SHAPE "
@@ -160,7 +220,7 @@ def setup_decode_stack(torch, ug, inputs, n_copies):
         mats.append(dict(K=K, N=N, x=torch.from_numpy(x).to(dev), pk=pk, beta=beta,
                          xq=ug.empty_pitched(1, K, torch.int8, dev),
                          s=torch.empty(1, dtype=torch.float32, device=dev),
-                         y=ug.empty_pitched(1, N, torch.float32, dev), W=W, x_host=x))
+                         y=ug.empty_pitched(1, N, torch.float32, dev)))
         del wq
     plans = []
     for c in range(n_copies):
@@ -184,13 +244,14 @@ def gemv_alg_bytes(M, N, K, packed=True, fp32_x=False):
     return wb + xb + 4 + 4 * M * N
 
 
-def cpu_decode_stack(oracle, mats, seconds):
-    # oracle state: quantized weights of each matrix (setup, untimed)
+def cpu_decode_stack(oracle, inputs, seconds):
+    # oracle state: quantized + packed weights of each matrix (set-up, untimed)
     prep = []
-    for m in mats:
-        wq, beta = oracle.quant_weight_absmean(m["W"])
+    for (layer, mi, name, K, N) in inputs.decode_stack_shapes():
+        x, W = inputs.decode_stack_matrix(layer, mi, K, N)
+        wq, beta = oracle.quant_weight_absmean(W)
         pk, _ = oracle.pack_trits(wq)
-        prep.append((m["x_host"], pk, m["K"], beta))
+        prep.append((x, pk, K, beta))
     passes = 0
     t0 = time.perf_counter()
     while True:
@@ -208,24 +269,34 @@ def run_decode_stack(args, torch, ug, inputs):
     steps = args.steps if args.steps is not None else 200
     warm = args.warmup if args.warmup is not None else 20
     per_copy = sum(N * ug.packed_pitch(K) for (_, _, _, K, N) in inputs.decode_stack_shapes())
-    n_copies = min(max(1, COLD_BYTES // per_copy), warm + steps)
+    # every launch of the warm-up and the timed region reads its own copy,
+    # and the copies span at least COLD_BYTES whatever the step count
+    n_copies = max(warm + steps, -(-COLD_BYTES // per_copy))
     mats, plans, per_pass_bytes = setup_decode_stack(torch, ug, inputs, n_copies)
-    log("decode_stack: %d matrices, %d packed weight bytes per pass, %d copies, grid %d"
-        % (len(mats), per_pass_bytes, n_copies, plans[0].info.grid))
-    g_warm = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[c % n_copies])
-                                     for c in range(warm)])
-    g_run = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[(warm + c) % n_copies])
+    flush = Flusher(torch)
+    log("decode_stack: %d matrices, %d packed weight bytes per pass, %d copies (%.2f GiB), "
+        "grid %d" % (len(mats), per_pass_bytes, n_copies, n_copies * per_copy / 2 ** 30,
+                     plans[0].info.grid))
+    g_warm = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[c]) for c in range(warm)])
+    g_run = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[warm + c])
                                     for c in range(steps)])
     stream = torch.cuda.current_stream()
     time_graph(torch, g_warm, stream)
+    flush()
     ms = time_graph(torch, g_run, stream)
     log("decode_stack: %d steps in %.3f ms" % (steps, ms))
+    # per-launch spread: STAT_LAUNCHES single cold launches (caches flushed
+    # before each), each on a copy the timed region did not use
+    c0 = (warm + steps) % n_copies
+    med, p10, p90 = launch_stats(
+        torch, lambda i: ug.ug_bitlinear_gemv_grouped(plans[(c0 + i) % n_copies]), stream,
+        flush=flush)
     # hot regime: one weight copy, resident in L2 / MALL (the realistic
     # regime for a 3 MB model); reported beside the cold value
     g_hot = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[0]) for _ in range(steps)])
     time_graph(torch, g_hot, stream)
     ms_hot = time_graph(torch, g_hot, stream)
-    del g_hot
+    del g_hot, g_warm, g_run
     # The step is one launch of the grouped kernel, so the kernel's average
     # launch duration is the step time (inter-launch gap included).
     alg = sum(gemv_alg_bytes(1, m["N"], m["K"], fp32_x=True) for m in mats)
@@ -237,21 +308,109 @@ def run_decode_stack(args, torch, ug, inputs):
                config={"workload": "decode_stack", "batch": 1, "matrices": len(mats),
                        "weight_format": "pack5", "packed_weight_bytes_per_step": per_pass_bytes,
                        "launches_per_step": 1, "weight_copies_cycled": n_copies,
-                       "regime": "cold (each step reads its own weight copy from HBM)",
+                       "weight_copy_bytes_cycled": n_copies * per_copy,
+                       "regime": "cold: each step reads its own weight copy, the copies span "
+                                 ">= 2 GiB, and 1 GiB is written just before the timed region",
                        "us_per_token_pass": ms * 1e3 / steps,
+                       "cold_launch_us_median": med, "cold_launch_us_p10": p10,
+                       "cold_launch_us_p90": p90, "cold_launches_in_median": STAT_LAUNCHES,
                        "hot_us_per_token_pass": ms_hot * 1e3 / steps,
                        "hot_weight_GBps": per_pass_bytes * steps / (ms_hot / 1e3) / 1e9},
                roofline=dict(bound="hbm", kernel="gemv_fine_grouped<PACK5, fused, tiny>",
                              achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("decode_stack"),
-                             avg_launch_us=avg_launch_s * 1e6, alg_bytes_per_launch=alg))
+                             avg_launch_us=avg_launch_s * 1e6, median_launch_us=med,
+                             alg_bytes_per_launch=alg))
+    del plans, mats, flush
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        out["prefill_gemm"] = measure_prefill_gemm(torch, ug, inputs)
+        torch.cuda.empty_cache()
+        out["stream_m1"] = measure_stream_m1(torch, ug, inputs)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle
-        passes, secs = cpu_decode_stack(oracle, mats, args.cpu_seconds)
+        passes, secs = cpu_decode_stack(oracle, inputs, args.cpu_seconds)
         out["cpu_baseline"] = dict(value=per_pass_bytes * passes / secs / 1e9, unit="GB/s",
-                                   cores=oracle.num_threads(), kind="oracle",
+                                   cores=oracle.num_threads(), cpu_model=cpu_model(),
+                                   kind="oracle",
                                    sample="%d full decode passes (33 x quant + unpack + int "
                                           "matmul + rescale) in %.1f s" % (passes, secs))
+    return out
+
+
+def measure_prefill_gemm(torch, ug, inputs):
+    """The int8 MFMA GEMM of the prefill workload (M = 4096; 2560 -> 6912 and
+    6912 -> 2560, I8 weights), alone: the median over STAT_LAUNCHES launches
+    per shape, each between HIP events on the launch stream."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    per_shape = []
+    for j in (0, 1):
+        x, W, _ = inputs.prefill_inputs(j)
+        K, N = inputs.PREFILL_SHAPES[j]
+        M = x.shape[0]
+        wq, beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
+        xq, s = ug.ug_quant_act(torch.from_numpy(x).to(dev))
+        y = ug.empty_pitched(M, N, torch.float32, dev)
+        del x, W
+        for _ in range(3):
+            ug.ug_bitlinear_gemm(xq, s, wq, ug.UG_W_I8, beta, y=y)
+        med, p10, p90 = launch_stats(
+            torch, lambda i: ug.ug_bitlinear_gemm(xq, s, wq, ug.UG_W_I8, beta, y=y), stream)
+        ops = 2 * M * N * K
+        per_shape.append(dict(M=M, K=K, N=N, ops=ops, median_us=med, p10_us=p10, p90_us=p90,
+                              TOPs=ops / (med * 1e-6) / 1e12))
+        log("prefill gemm", per_shape[-1])
+        del wq, xq, s, y
+    ops = sum(p["ops"] for p in per_shape) / 2
+    us = sum(p["median_us"] for p in per_shape) / 2
+    achieved = ops / (us * 1e-6) / 1e12
+    return dict(value=achieved, unit="TOP/s", shapes=per_shape,
+                roofline=dict(bound="mfma", kernel="gemm_i8_large", achieved=achieved,
+                              peak=INT8_PEAK_TOPS, unit="TOP/s", frac=achieved / INT8_PEAK_TOPS,
+                              traffic=traffic_for("prefill"), median_launch_us=us,
+                              alg_ops_per_launch=ops))
+
+
+def measure_stream_m1(torch, ug, inputs, M=1, si=0):
+    """The streaming decode GEMV at one sweep point (default M = 1,
+    2560 -> 6912, PACK5): grouped launches of G distinct weight copies
+    (>= 128 MB each), launch sets cycling through >= 2 GiB of copies (cold);
+    the median over STAT_LAUNCHES launches."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    K, N = inputs.SWEEP_SHAPES[si]
+    x64, W = inputs.sweep_inputs(si, 64)
+    wq, beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
+    pk = ug.ug_pack_trits(wq)
+    del wq, W
+    G = max(1, (128 << 20) // (N * ug.packed_pitch(K)))
+    n_sets = max(2, COLD_BYTES // (G * N * ug.packed_pitch(K)) + 1)
+    copies = [[pk.clone() for _ in range(G)] for _ in range(n_sets)]
+    xq, s = ug.ug_quant_act(torch.from_numpy(x64[:M].copy()).to(dev))
+    y = ug.empty_pitched(M, N, torch.float32, dev)
+    plans = [ug.ug_gemv_plan_init([dict(xq=xq, s=s, w=w, wfmt=ug.UG_W_PACK5, beta=beta, K=K,
+                                         y=y) for w in cs]) for cs in copies]
+    for i in range(2):
+        ug.ug_bitlinear_gemv_grouped(plans[i % n_sets])
+    med, p10, p90 = launch_stats(
+        torch, lambda i: ug.ug_bitlinear_gemv_grouped(plans[(i + 2) % n_sets]), stream)
+    wbytes = N * (-(-K // 5)) * G
+    alg = gemv_alg_bytes(M, N, K) * G
+    achieved = alg / (med * 1e-6) / 1e9
+    out = dict(value=wbytes / (med * 1e-6) / 1e9, unit="GB/s",
+               point="M=%d K=%d N=%d, PACK5, %d weight copies per launch, %d launch sets "
+                     "(%.2f GiB) cycled" % (M, K, N, G, n_sets,
+                                           n_sets * G * N * ug.packed_pitch(K) / 2 ** 30),
+               median_launch_us=med, p10_launch_us=p10, p90_launch_us=p90,
+               roofline=dict(bound="hbm", kernel="gemv_stream_grouped<PACK5, 1>",
+                             achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=achieved / HBM_PEAK_GBS,
+                             traffic=traffic_for("sweep") if (M, si) == (1, 0) else None,
+                             median_launch_us=med, alg_bytes_per_launch=alg))
+    log("stream", out)
+    del plans, copies
     return out
 
 
@@ -280,7 +439,7 @@ def run_sweep(args, torch, ug, inputs):
         del wq
         wbytes = N * (-(-K // 5))
         G = max(1, (128 << 20) // (N * ug.packed_pitch(K)))
-        n_sets = max(2, min(warm + steps, (COLD_BYTES // (G * N * ug.packed_pitch(K))) + 1))
+        n_sets = max(2, COLD_BYTES // (G * N * ug.packed_pitch(K)) + 1)
         copies = [[pk.clone() for _ in range(G)] for _ in range(n_sets)]
         for M in inputs.SWEEP_MS:
             if only is not None and only[0] != M:
@@ -406,7 +565,7 @@ def run_prefill(args, torch, ug, inputs):
             rows += 64
         secs = time.perf_counter() - t0
         out["cpu_baseline"] = dict(value=ops / secs / 1e12, unit="TOP/s",
-                                   cores=oracle.num_threads(), kind="oracle",
+                                   cores=oracle.num_threads(), cpu_model=cpu_model(), kind="oracle",
                                    sample="first %d of 4096 rows of both layers (quant + int "
                                           "matmul + rescale) in %.1f s" % (rows, secs))
     return out
@@ -512,7 +671,7 @@ def run_stack(args, torch, ug, inputs):
             rows += 64
         secs = time.perf_counter() - t0
         out["cpu_baseline"] = dict(value=ops / secs / 1e12, unit="TOP/s",
-                                   cores=oracle.num_threads(), kind="oracle",
+                                   cores=oracle.num_threads(), cpu_model=cpu_model(), kind="oracle",
                                    sample="layer 0 (requant of both masters + RMSNorm/quant + "
                                           "int matmul + rescale, both BitLinears) on %d of "
                                           "2048 rows per pass, %.1f s" % (rows, secs))
@@ -571,7 +730,7 @@ def run_tiny(args, torch, ug, inputs):
             n += 1
         secs = time.perf_counter() - t0
         out["cpu_baseline"] = dict(value=ops * n / secs / 1e12, unit="TOP/s",
-                                   cores=oracle.num_threads(), kind="oracle",
+                                   cores=oracle.num_threads(), cpu_model=cpu_model(), kind="oracle",
                                    sample="%d whole steps (weight quant + act quant + matmul + "
                                           "rescale) in %.1f s" % (n, secs))
     return out
@@ -600,8 +759,9 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
-    if "cpu_baseline" in res:
-        line["cpu_baseline"] = res["cpu_baseline"]
+    for k in ("prefill_gemm", "stream_m1", "cpu_baseline"):
+        if k in res:
+            line[k] = res[k]
     print(json.dumps(line), flush=True)
 
 

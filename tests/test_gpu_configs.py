@@ -102,28 +102,61 @@ def test_sweep_all_points(dev, shape_idx):
         _check_layer(got, x, W, ug.UG_W_PACK5)
 
 
-def test_stack_first_layers_chained(dev):
-    """Requantize the fp32 masters, then RMSNorm + act quant + GEMM, chained
-    through the first two layers (four BitLinears) at M=2048.  The oracle runs
-    its own chain; bit-exact y keeps the two chains identical."""
-    x_ref = inputs.stack_x0()
-    x_d = torch.from_numpy(x_ref).to("cuda:0")
-    for layer in range(2):
+def _stack_rows(M):
+    """Rows of the stack workload whose chain the oracle follows: the first
+    two, the middle, the last, and 60 seeded others."""
+    rng = np.random.default_rng(777)
+    extra = rng.choice(np.arange(2, M - 1), size=60, replace=False)
+    return np.unique(np.concatenate([[0, 1, M // 2 - 1, M - 1], extra])).astype(np.int64)
+
+
+@pytest.mark.timeout(900)
+def test_stack_full_depth_chained(dev):
+    """The whole stack step at M = 2048, as the benchmark runs it: all 60 fp32
+    masters requantized (absmean + ternary) and compared in full (beta and
+    every W_q); then the 60 x (RMSNorm + act quant + GEMM) chain.  Rows are
+    independent ("attention, as graph ops": one scale per token), so at every
+    layer the oracle takes the GPU's own input rows for a sample of 64 rows
+    and checks s, x_q, the whole accumulator row and y bit for bit; the
+    oracle also runs its own chain from x0 on those rows, which must end on
+    the GPU's bits."""
+    M = inputs.STACK_M
+    rows = _stack_rows(M)
+    rows_d = torch.from_numpy(rows).to("cuda:0")
+    dev_ = torch.device("cuda:0")
+    # requantization of every master first (the benchmark's order)
+    ws = torch.empty(max(ug.ug_quant_weight_absmean_workspace_size(N, K)
+                         for (K, N) in inputs.STACK_SHAPES), dtype=torch.uint8, device=dev_)
+    mats = []
+    for layer in range(inputs.STACK_LAYERS):
         for which in (0, 1):
-            _case("stack", layer, which)
-            W = inputs.stack_master(layer, which)
+            _case("stack requant", layer, which)
             K, N = inputs.STACK_SHAPES[which]
-            wq_d, beta_d = ug.ug_quant_weight_absmean(pitched(W))
-            xq_d, s_d = ug.ug_rmsnorm_quant_act(x_d)
-            acc_d, y_d = ug.ug_bitlinear_gemm(xq_d, s_d, wq_d, ug.UG_W_I8, beta_d, want_acc=True)
+            W = inputs.stack_master(layer, which)
+            wq_d = ug.empty_pitched(N, K, torch.int8, dev_)
+            beta_d = torch.empty(1, dtype=torch.float32, device=dev_)
+            ug.ug_quant_weight_absmean(pitched(W), wq=wq_d, beta=beta_d, ws=ws)
             ref_wq, ref_beta = oracle.quant_weight_absmean(W)
-            ref_xq, ref_s = oracle.rmsnorm_quant_act(x_ref)
-            assert host(beta_d)[0] == ref_beta
-            assert_bits_equal(host(wq_d), ref_wq, "W_q")
-            assert_bits_equal(host(s_d), ref_s, "s")
-            assert_bits_equal(host(xq_d), ref_xq, "x_q")
-            acc = oracle.matmul_i32(ref_xq, ref_wq)
-            assert_bits_equal(host(acc_d), acc, "acc")
-            x_ref = oracle.epilogue(acc, ref_s, ref_beta)
-            assert_bits_equal(host(y_d), x_ref, "y")
-            x_d = y_d.contiguous()
+            assert host(beta_d)[0].view(np.uint32) == np.float32(ref_beta).view(np.uint32), \
+                ("beta", layer, which)
+            assert_bits_equal(host(wq_d), ref_wq, "W_q layer %d/%d" % (layer, which))
+            mats.append((K, N, wq_d, beta_d, ref_wq, ref_beta))
+    x0 = inputs.stack_x0()
+    x_d = torch.from_numpy(x0).to(dev_)
+    own = x0[rows]  # the oracle's own chain on the sampled rows
+    for li, (K, N, wq_d, beta_d, ref_wq, ref_beta) in enumerate(mats):
+        _case("stack chain", li // 2, li % 2, K, N)
+        xq_d, s_d = ug.ug_rmsnorm_quant_act(x_d)
+        acc_d, y_d = ug.ug_bitlinear_gemm(xq_d, s_d, wq_d, ug.UG_W_I8, beta_d, want_acc=True)
+        x_in = host(x_d.index_select(0, rows_d))
+        ref_xq, ref_s = oracle.rmsnorm_quant_act(x_in)
+        assert_bits_equal(host(s_d.index_select(0, rows_d)), ref_s, "s %d" % li)
+        assert_bits_equal(host(xq_d.index_select(0, rows_d)), ref_xq, "x_q %d" % li)
+        acc = oracle.matmul_i32(ref_xq, ref_wq)
+        assert_bits_equal(host(acc_d.index_select(0, rows_d)), acc, "acc %d" % li)
+        y = oracle.epilogue(acc, ref_s, ref_beta)
+        assert_bits_equal(host(y_d.index_select(0, rows_d)), y, "y %d" % li)
+        oq, os_ = oracle.rmsnorm_quant_act(own)
+        own = oracle.epilogue(oracle.matmul_i32(oq, ref_wq), os_, ref_beta)
+        x_d = y_d
+    assert_bits_equal(host(x_d.index_select(0, rows_d)), own, "end of the oracle's own chain")
