@@ -153,6 +153,81 @@ __global__ __launch_bounds__(256) void ternary_quant(const float *__restrict__ W
   }
 }
 
+// One PACK5 byte from the five fp32 weights of its group:
+// 121 + sum_j W_q(w_j) 3^j (README "A whole ternary GPT": five ternary values
+// per byte), each W_q as in ternary_quant.
+__device__ inline uint32_t pack5_code(float w0, float w1, float w2, float w3, float w4, float b,
+                                      float rb, bool fast) {
+  int t0, t1, t2, t3, t4;
+  if (fast) {
+    t0 = tern_fast(w0, b, rb);
+    t1 = tern_fast(w1, b, rb);
+    t2 = tern_fast(w2, b, rb);
+    t3 = tern_fast(w3, b, rb);
+    t4 = tern_fast(w4, b, rb);
+  } else {
+    t0 = tern(w0, b);
+    t1 = tern(w1, b);
+    t2 = tern(w2, b);
+    t3 = tern(w3, b);
+    t4 = tern(w4, b);
+  }
+  return (uint32_t)(121 + t0 + 3 * t1 + 9 * t2 + 27 * t3 + 81 * t4);
+}
+
+// Requantization straight to five trits per byte: beta as in ternary_quant,
+// then every output dword (4 bytes = 20 consecutive weights of a row) from
+// five float4 loads.  Row bytes from ceil(K/5) to ldp are 121 (five zero
+// trits); weights past K count as zero trits.  The same bytes as
+// ternary_quant followed by pack_kernel, without the int8 tensor between.
+__global__ __launch_bounds__(256) void ternary_pack5(const float *__restrict__ W, int64_t ldw,
+                                                     int64_t N, int64_t K,
+                                                     const float *__restrict__ partials,
+                                                     int64_t nchunks, float n_f, float eps,
+                                                     float *__restrict__ beta_out,
+                                                     uint8_t *__restrict__ packed, int64_t ldp) {
+  __shared__ float lds[256];
+  const float b = beta_from(partials, nchunks, n_f, eps, lds);
+  if (blockIdx.x == 0 && threadIdx.x == 0) beta_out[0] = b;
+  const bool fast = b >= 0x1p-100f && b <= 0x1p100f;
+  const float rb = fast ? __builtin_amdgcn_rcpf(b) : 0.0f;
+  const int64_t groups = (K + 4) / 5;
+  const int64_t dpr = ldp / 4;  // output dwords per row
+  const int64_t total = N * dpr;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += stride) {
+    const int64_t r = idx / dpr;
+    const int64_t j = idx - r * dpr;
+    const int64_t e0 = 20 * j;  // first weight of the dword's four groups
+    const float *src = W + r * ldw + e0;
+    uint32_t word;
+    if (e0 + 20 <= K) {
+      // 80 contiguous bytes, 16-byte aligned (ldw is a multiple of 4)
+      const float4 a = ld4(src), c = ld4(src + 4), d = ld4(src + 8), e = ld4(src + 12),
+                   f = ld4(src + 16);
+      word = pack5_code(a.x, a.y, a.z, a.w, c.x, b, rb, fast) |
+             pack5_code(c.y, c.z, c.w, d.x, d.y, b, rb, fast) << 8 |
+             pack5_code(d.z, d.w, e.x, e.y, e.z, b, rb, fast) << 16 |
+             pack5_code(e.w, f.x, f.y, f.z, f.w, b, rb, fast) << 24;
+    } else {
+      word = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t g = 4 * j + q;
+        uint32_t code = 121;
+        if (g < groups) {
+          float v[5];
+#pragma unroll
+          for (int i = 0; i < 5; ++i) v[i] = 5 * g + i < K ? src[5 * q + i] : 0.0f;
+          code = pack5_code(v[0], v[1], v[2], v[3], v[4], b, rb, fast);
+        }
+        word |= code << (8 * q);
+      }
+    }
+    *reinterpret_cast<uint32_t *>(packed + r * ldp + 4 * j) = word;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_absmean(const float *W, int64_t ldw, int64_t N, int64_t K, float eps,
@@ -170,6 +245,21 @@ hipError_t launch_absmean(const float *W, int64_t ldw, int64_t N, int64_t K, flo
   if (blocks > 256 * 4) blocks = 256 * 4;
   hipLaunchKernelGGL(ternary_quant, dim3(blocks), dim3(256), 0, st, W, ldw, N, K, partials,
                      nchunks, (float)n, eps, beta, wq, ldq);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmean_pack5(const float *W, int64_t ldw, int64_t N, int64_t K, float eps,
+                                uint8_t *packed, int64_t ldp, float *beta, float *partials,
+                                hipStream_t st) {
+  const int64_t n = N * K;
+  const int64_t nchunks = ceil_div(n, kAbsmeanChunk);
+  hipLaunchKernelGGL(absmean_stage1, dim3(nchunks), dim3(256), 0, st, W, ldw, N, K, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t blocks = ceil_div(N * (ldp / 4), 256);
+  if (blocks > 256 * 4) blocks = 256 * 4;
+  hipLaunchKernelGGL(ternary_pack5, dim3(blocks), dim3(256), 0, st, W, ldw, N, K, partials,
+                     nchunks, (float)n, eps, beta, packed, ldp);
   return hipGetLastError();
 }
 

@@ -105,6 +105,22 @@ ug_status ug_quant_weight_absmean(const float *W, int64_t ldw, int64_t N, int64_
                                        as_stream(stream)));
 }
 
+ug_status ug_quant_weight_absmean_pack5(const float *W, int64_t ldw, int64_t N, int64_t K,
+                                        float eps, uint8_t *packed, int64_t ldp, float *beta,
+                                        void *ws, size_t ws_bytes, void *stream) {
+  if (!ptr_ok(W) || !ptr_ok(packed) || !f32_ok(beta)) return UG_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > INT64_MAX / K) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldw, K, 4) || !pitch_ok(ldp, ug::ceil_div(K, 5), 16) || !eps_ok(eps))
+    return UG_ERR_INVALID_ARG;
+  const int64_t n = N * K;
+  if ((double)(float)n != (double)n || n > (INT64_C(1) << 40)) return UG_ERR_UNSUPPORTED;
+  if (ug::ceil_div(n, ug::kAbsmeanChunk) > INT32_MAX) return UG_ERR_UNSUPPORTED;
+  const size_t need = ug_quant_weight_absmean_workspace_size(N, K);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return UG_ERR_WORKSPACE;
+  return hip_status(ug::launch_absmean_pack5(W, ldw, N, K, eps, packed, ldp, beta, (float *)ws,
+                                             as_stream(stream)));
+}
+
 ug_status ug_pack_trits(const int8_t *wq, int64_t ldq, int64_t N, int64_t K, uint8_t *packed,
                         int64_t ldp, int32_t *bad_count, void *stream) {
   if (!ptr_ok(wq) || !ptr_ok(packed) || !counter_ok(bad_count)) return UG_ERR_INVALID_ARG;

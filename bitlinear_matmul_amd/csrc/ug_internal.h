@@ -30,6 +30,11 @@ hipError_t launch_rmsnorm_quant_act(const float *x, int64_t ldx, const float *g,
 hipError_t launch_absmean(const float *W, int64_t ldw, int64_t N, int64_t K,
                           float eps, int8_t *wq, int64_t ldq, float *beta,
                           float *partials, hipStream_t st);
+// The same beta, then the ternary weights written straight as UG_W_PACK5
+// rows of ldp bytes (ldp a multiple of 16, >= ceil(K/5)).
+hipError_t launch_absmean_pack5(const float *W, int64_t ldw, int64_t N, int64_t K,
+                                float eps, uint8_t *packed, int64_t ldp, float *beta,
+                                float *partials, hipStream_t st);
 hipError_t launch_pack(const int8_t *wq, int64_t ldq, int64_t N, int64_t K,
                        uint8_t *packed, int64_t ldp, int32_t *bad,
                        hipStream_t st);

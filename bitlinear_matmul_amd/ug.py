@@ -42,6 +42,8 @@ SIGNATURES = {
     "ug_quant_weight_absmean_workspace_size": (_sz, [_i64, _i64]),
     "ug_quant_weight_absmean": (_i32, [_vp, _i64, _i64, _i64, _f32, _vp, _i64, _vp, _vp, _sz,
                                        _vp]),
+    "ug_quant_weight_absmean_pack5": (_i32, [_vp, _i64, _i64, _i64, _f32, _vp, _i64, _vp, _vp,
+                                             _sz, _vp]),
     "ug_pack_trits": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "ug_unpack_trits": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "ug_bitlinear_gemv": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
@@ -194,6 +196,24 @@ def ug_quant_weight_absmean(W, eps=1e-5, wq=None, beta=None, ws=None, stream=Non
                                          _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "ug_quant_weight_absmean")
     return wq, beta
+
+
+def ug_quant_weight_absmean_pack5(W, eps=1e-5, packed=None, beta=None, ws=None, stream=None):
+    """Absmean ternary quantization written straight as 5 trits per byte.
+    W fp32 [N,K] -> (packed uint8 [N, ldp] full pitched rows, beta fp32 [1])."""
+    N, K = W.shape
+    if packed is None:
+        packed = torch.empty((N, packed_pitch(K)), dtype=torch.uint8, device=W.device)
+    if beta is None:
+        beta = torch.empty(1, dtype=torch.float32, device=W.device)
+    need = ug_quant_weight_absmean_workspace_size(N, K)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=W.device)
+    _check(lib().ug_quant_weight_absmean_pack5(_p(W), _ld(W), N, K, eps, _p(packed),
+                                               _ld(packed), _p(beta), _p(ws),
+                                               ws.numel() * ws.element_size(), _stream(stream)),
+           "ug_quant_weight_absmean_pack5")
+    return packed, beta
 
 
 def ug_pack_trits(wq, packed=None, bad_count=None, stream=None):

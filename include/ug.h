@@ -145,6 +145,22 @@ ug_status ug_quant_weight_absmean(const float *W, int64_t ldw, int64_t N,
                                   size_t ws_bytes, void *stream);
 
 /*
+ * Requantization straight to the deployed format: the beta and W_q of
+ * ug_quant_weight_absmean (same summation order, same bits), with W_q
+ * written as UG_W_PACK5 rows instead of one trit per byte ("ultragraph ...
+ * part 2", "training the thing": the fp32 masters are requantized after
+ * every optimizer step; README "A whole ternary GPT": deployed weights hold
+ * five ternary values per byte).  The bytes equal ug_pack_trits applied to
+ * ug_quant_weight_absmean's output: packed uint8 [N][ldp], ldp >= ceil(K/5)
+ * and a multiple of 16, row bytes [ceil(K/5), ldp) written as 121.
+ * ws as for ug_quant_weight_absmean (the same size query).
+ */
+ug_status ug_quant_weight_absmean_pack5(const float *W, int64_t ldw, int64_t N,
+                                        int64_t K, float eps, uint8_t *packed,
+                                        int64_t ldp, float *beta, void *ws,
+                                        size_t ws_bytes, void *stream);
+
+/*
  * Pack one-trit-per-byte weights into UG_W_PACK5 (README "A whole ternary
  * GPT"; "Layout": pack.py).  wq int8 [N][ldq] in; packed uint8 [N][ldp]
  * out, ldp >= ceil(K/5); bytes [ceil(K/5), ldp) of every row are written as

@@ -150,6 +150,21 @@ def test_absmean_rejects(ug):
                                       1 << 30, S) == ug.UG_ERR_UNSUPPORTED)
 
 
+def test_absmean_pack5_rejects(ug):
+    L = ug.lib()
+    need = L.ug_quant_weight_absmean_workspace_size(512, 128)
+    E = ug.UG_ERR_INVALID_ARG
+    f = L.ug_quant_weight_absmean_pack5
+    assert f(NULL, 128, 512, 128, 1e-5, A2, 32, A3, A4, need, S) == E
+    assert f(A, 128, 512, 128, 1e-5, A2, 16, A3, A4, need, S) == E      # ldp < ceil(K/5)
+    assert f(A, 128, 512, 128, 1e-5, A2, 40, A3, A4, need, S) == E      # ldp % 16
+    assert f(A, 126, 512, 128, 1e-5, A2, 32, A3, A4, need, S) == E      # ldw < K
+    assert f(A, 128, 512, 128, 0.0, A2, 32, A3, A4, need, S) == E
+    W = ug.UG_ERR_WORKSPACE
+    assert f(A, 128, 512, 128, 1e-5, A2, 32, A3, NULL, need, S) == W
+    assert f(A, 128, 512, 128, 1e-5, A2, 32, A3, A4, need - 4, S) == W
+
+
 def test_pack_rejects(ug):
     L = ug.lib()
     E = ug.UG_ERR_INVALID_ARG
