@@ -15,6 +15,8 @@
 //            of the elements: W_q = clamp(rint(W/beta), -1, 1).
 // Traffic: 4 B/element read twice (the second read mostly hits the MALL for
 // tensors that fit) plus 1 B/element written.
+#include <mutex>
+
 #include "ug_internal.h"
 
 namespace ug {
@@ -228,7 +230,33 @@ __global__ __launch_bounds__(256) void ternary_pack5(const float *__restrict__ W
   }
 }
 
+// Stage-1 partials of the allocation-free entry point: one float per
+// 8192-element chunk, so tensors of up to kStaticChunks * 8192 elements.
+// Each device holds its own copy for the life of the process.
+static __device__ __align__(256) float scratch[kStaticChunks];
+
 }  // namespace
+
+// The device address of this device's `scratch` array, looked up once per
+// device (with that device current) and cached; host code uses only this
+// pointer, never the array's name.
+hipError_t static_scratch(float **out) {
+  static std::mutex mu;
+  static float *ptrs[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = static_cast<float *>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_absmean(const float *W, int64_t ldw, int64_t N, int64_t K, float eps,
                           int8_t *wq, int64_t ldq, float *beta, float *partials,

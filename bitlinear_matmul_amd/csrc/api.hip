@@ -121,6 +121,22 @@ ug_status ug_quant_weight_absmean_pack5(const float *W, int64_t ldw, int64_t N, 
                                              as_stream(stream)));
 }
 
+ug_status ug_quant_weight_absmean_static(const float *W, int64_t ldw, int64_t N, int64_t K,
+                                         float eps, int8_t *wq, int64_t ldq, float *beta,
+                                         void *stream) {
+  if (!ptr_ok(W) || !ptr_ok(wq) || !f32_ok(beta)) return UG_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > INT64_MAX / K) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldw, K, 4) || !pitch_ok(ldq, K, 16) || !eps_ok(eps)) return UG_ERR_INVALID_ARG;
+  const int64_t n = N * K;
+  if ((double)(float)n != (double)n || n > (INT64_C(1) << 40)) return UG_ERR_UNSUPPORTED;
+  if (ug::ceil_div(n, ug::kAbsmeanChunk) > ug::kStaticChunks) return UG_ERR_WORKSPACE;
+  float *partials = nullptr;
+  hipError_t e = ug::static_scratch(&partials);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(ug::launch_absmean(W, ldw, N, K, eps, wq, ldq, beta, partials,
+                                       as_stream(stream)));
+}
+
 ug_status ug_pack_trits(const int8_t *wq, int64_t ldq, int64_t N, int64_t K, uint8_t *packed,
                         int64_t ldp, int32_t *bad_count, void *stream) {
   if (!ptr_ok(wq) || !ptr_ok(packed) || !counter_ok(bad_count)) return UG_ERR_INVALID_ARG;

@@ -35,6 +35,10 @@ hipError_t launch_absmean(const float *W, int64_t ldw, int64_t N, int64_t K,
 hipError_t launch_absmean_pack5(const float *W, int64_t ldw, int64_t N, int64_t K,
                                 float eps, uint8_t *packed, int64_t ldp, float *beta,
                                 float *partials, hipStream_t st);
+// Chunks the allocation-free absmean's static scratch array holds (64 KB).
+constexpr int64_t kStaticChunks = 16384;
+// Device address of the current device's static absmean scratch array.
+hipError_t static_scratch(float **out);
 hipError_t launch_pack(const int8_t *wq, int64_t ldq, int64_t N, int64_t K,
                        uint8_t *packed, int64_t ldp, int32_t *bad,
                        hipStream_t st);

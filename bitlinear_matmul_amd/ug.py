@@ -44,6 +44,8 @@ SIGNATURES = {
                                        _vp]),
     "ug_quant_weight_absmean_pack5": (_i32, [_vp, _i64, _i64, _i64, _f32, _vp, _i64, _vp, _vp,
                                              _sz, _vp]),
+    "ug_quant_weight_absmean_static": (_i32, [_vp, _i64, _i64, _i64, _f32, _vp, _i64, _vp,
+                                              _vp]),
     "ug_pack_trits": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "ug_unpack_trits": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "ug_bitlinear_gemv": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
@@ -214,6 +216,21 @@ def ug_quant_weight_absmean_pack5(W, eps=1e-5, packed=None, beta=None, ws=None, 
                                                ws.numel() * ws.element_size(), _stream(stream)),
            "ug_quant_weight_absmean_pack5")
     return packed, beta
+
+
+def ug_quant_weight_absmean_static(W, eps=1e-5, wq=None, beta=None, stream=None):
+    """ug_quant_weight_absmean through the library's static scratch array
+    (the C call allocates nothing and takes no workspace).  Pass wq and beta
+    to keep this call free of allocations too."""
+    N, K = W.shape
+    if wq is None:
+        wq = empty_pitched(N, K, torch.int8, W.device)
+    if beta is None:
+        beta = torch.empty(1, dtype=torch.float32, device=W.device)
+    _check(lib().ug_quant_weight_absmean_static(_p(W), _ld(W), N, K, eps, _p(wq), _ld(wq),
+                                                _p(beta), _stream(stream)),
+           "ug_quant_weight_absmean_static")
+    return wq, beta
 
 
 def ug_pack_trits(wq, packed=None, bad_count=None, stream=None):

@@ -161,6 +161,26 @@ ug_status ug_quant_weight_absmean_pack5(const float *W, int64_t ldw, int64_t N,
                                         size_t ws_bytes, void *stream);
 
 /*
+ * ug_quant_weight_absmean without a workspace argument and without any
+ * allocation: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The stage-1 chunk sums go to a static 64 KB array in the
+ * library's device code (one per GPU, held until the process ends), so the
+ * tensor may hold at most UG_ABSMEAN_STATIC_MAX_ELEMS elements, else
+ * UG_ERR_WORKSPACE before anything is launched.  Same arguments, results
+ * (bit for bit) and errors as ug_quant_weight_absmean otherwise.  Every
+ * call on a GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (different streams, or different host threads) race and may return
+ * wrong results; serialize them.  The first call on a device looks the
+ * array up (hipGetSymbolAddress) and may return UG_ERR_HIP if that fails.
+ */
+#define UG_ABSMEAN_STATIC_MAX_ELEMS (16384LL * 8192LL)
+ug_status ug_quant_weight_absmean_static(const float *W, int64_t ldw,
+                                         int64_t N, int64_t K, float eps,
+                                         int8_t *wq, int64_t ldq, float *beta,
+                                         void *stream);
+
+/*
  * Pack one-trit-per-byte weights into UG_W_PACK5 (README "A whole ternary
  * GPT"; "Layout": pack.py).  wq int8 [N][ldq] in; packed uint8 [N][ldp]
  * out, ldp >= ceil(K/5); bytes [ceil(K/5), ldp) of every row are written as

@@ -165,6 +165,24 @@ def test_absmean_pack5_rejects(ug):
     assert f(A, 128, 512, 128, 1e-5, A2, 32, A3, A4, need - 4, S) == W
 
 
+def test_absmean_static_rejects(ug):
+    """The allocation-free absmean: the same argument checks, and tensors
+    beyond its static scratch (16384 chunks of 8192 elements) are refused
+    with UG_ERR_WORKSPACE before anything is looked up or launched."""
+    L = ug.lib()
+    E = ug.UG_ERR_INVALID_ARG
+    assert L.ug_quant_weight_absmean_static(NULL, 128, 512, 128, 1e-5, A2, 128, A3, S) == E
+    assert L.ug_quant_weight_absmean_static(A, 128, 512, 128, 0.0, A2, 128, A3, S) == E
+    assert L.ug_quant_weight_absmean_static(A, 128, 512, 128, 1e-5, A2, 120, A3, S) == E
+    K = 8192
+    N = 16384 + 1  # one chunk more than the array holds
+    assert (L.ug_quant_weight_absmean_static(A, K, N, K, 1e-5, A2, K, A3, S)
+            == ug.UG_ERR_WORKSPACE)
+    n_bad = 2 ** 24 + 1
+    assert (L.ug_quant_weight_absmean_static(A, n_bad + 3, 1, n_bad, 1e-5, A2, n_bad + 15, A3,
+                                             S) == ug.UG_ERR_UNSUPPORTED)
+
+
 def test_pack_rejects(ug):
     L = ug.lib()
     E = ug.UG_ERR_INVALID_ARG
