@@ -328,6 +328,8 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["stream_m1"] = measure_stream_m1(torch, ug, inputs)
         torch.cuda.empty_cache()
+        out["requant_pack5"] = measure_requant_pack5(torch, ug, inputs)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle
         passes, secs = cpu_decode_stack(oracle, inputs, args.cpu_seconds)
@@ -371,6 +373,44 @@ def measure_prefill_gemm(torch, ug, inputs):
                               peak=INT8_PEAK_TOPS, unit="TOP/s", frac=achieved / INT8_PEAK_TOPS,
                               traffic=traffic_for("prefill"), median_launch_us=us,
                               alg_ops_per_launch=ops))
+
+
+def measure_requant_pack5(torch, ug, inputs):
+    """Requantization of a 2B-class fp32 master (6912 x 2560, the stack
+    workload's up projection) straight to five trits per byte: the absmean
+    sum, then the fused ternary + pack pass.  Calls cycle through >= 2 GiB of
+    master copies (each read cold); the median over STAT_LAUNCHES calls."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    K, N = inputs.STACK_SHAPES[0]
+    W0 = torch.from_numpy(inputs.stack_master(0, 0)).to(dev)
+    n_copies = -(-COLD_BYTES // (4 * N * K))
+    masters = [W0] + [W0.clone() for _ in range(n_copies - 1)]
+    packed = torch.empty((N, ug.packed_pitch(K)), dtype=torch.uint8, device=dev)
+    beta = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(ug.ug_quant_weight_absmean_workspace_size(N, K), dtype=torch.uint8,
+                     device=dev)
+    for i in range(2):
+        ug.ug_quant_weight_absmean_pack5(masters[i], packed=packed, beta=beta, ws=ws)
+    med, p10, p90 = launch_stats(
+        torch, lambda i: ug.ug_quant_weight_absmean_pack5(masters[(i + 2) % n_copies],
+                                                          packed=packed, beta=beta, ws=ws),
+        stream)
+    # the sum reads W, the fused pass reads it again and writes the bytes
+    alg = 4 * N * K + 4 * N * K + N * (-(-K // 5)) + 4
+    achieved = alg / (med * 1e-6) / 1e9
+    out = dict(value=achieved, unit="GB/s",
+               point="W fp32 [%d, %d] -> PACK5 [%d, %d] + beta; %d master copies (%.2f GiB) "
+                     "cycled" % (N, K, N, ug.packed_pitch(K), n_copies,
+                                 n_copies * 4 * N * K / 2 ** 30),
+               median_call_us=med, p10_call_us=p10, p90_call_us=p90,
+               roofline=dict(bound="hbm", kernel="absmean_stage1 + ternary_pack5",
+                             achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=achieved / HBM_PEAK_GBS, traffic=None,
+                             median_launch_us=med, alg_bytes_per_launch=alg))
+    log("requant pack5", out)
+    del masters
+    return out
 
 
 def measure_stream_m1(torch, ug, inputs, M=1, si=0):
@@ -630,6 +670,18 @@ def run_stack(args, torch, ug, inputs):
     e_all1.record(stream)
     torch.cuda.synchronize()
     ms = t_req + t_chain
+    # requantization straight to five trits per byte (the deployed format)
+    # of the same 60 masters, timed on its own
+    pk_bufs = {K: torch.empty((N, ug.packed_pitch(K)), dtype=torch.uint8, device=dev)
+               for (K, N) in inputs.STACK_SHAPES}
+    e[0].record(stream)
+    for _ in range(steps):
+        for m in mats:
+            ug.ug_quant_weight_absmean_pack5(m["W"], packed=pk_bufs[m["K"]], beta=m["beta"], ws=ws)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    t_req5 = e[0].elapsed_time(e[1]) / steps
+    req5_bytes = sum(8 * m["N"] * m["K"] + m["N"] * (-(-m["K"] // 5)) for m in mats)
     # the GEMMs alone (the dominant kernel), same chain of operands
     e[0].record(stream)
     for _ in range(steps):
@@ -646,6 +698,8 @@ def run_stack(args, torch, ug, inputs):
                        "shapes_KxN": [list(x) for x in inputs.STACK_SHAPES],
                        "weight_format": "i8", "requant_ms_per_step": t_req / steps,
                        "requant_GBps": req_bytes * steps / (t_req / 1e3) / 1e9,
+                       "requant_pack5_ms_per_step": t_req5,
+                       "requant_pack5_GBps": req5_bytes / (t_req5 / 1e3) / 1e9,
                        "chain_ms_per_step": t_chain / steps,
                        "gemm_us_per_launch": gemm_ms * 1e3,
                        "act_quant_alg_bytes_per_step": act_bytes},
@@ -759,7 +813,7 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
-    for k in ("prefill_gemm", "stream_m1", "cpu_baseline"):
+    for k in ("prefill_gemm", "stream_m1", "requant_pack5", "cpu_baseline"):
         if k in res:
             line[k] = res[k]
     print(json.dumps(line), flush=True)

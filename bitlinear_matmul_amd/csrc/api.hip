@@ -49,7 +49,7 @@ size_t plan_table_offset(const void *plan, int32_t count) {
 
 extern "C" {
 
-int32_t ug_version(void) { return 10000; }
+int32_t ug_version(void) { return 10100; }
 
 const char *ug_status_string(ug_status st) {
   switch (st) {
@@ -157,9 +157,10 @@ namespace {
 
 // Shared validation of the two matmul entry points.
 ug_status check_matmul(const int8_t *xq, int64_t ldx, const float *s, const void *w, int32_t wfmt,
-                       int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
-                       const int32_t *acc, int64_t ldacc, const float *y, int64_t ldy) {
+                       int64_t ldw, const float *beta, const float *bias, int64_t M, int64_t N,
+                       int64_t K, const int32_t *acc, int64_t ldacc, const float *y, int64_t ldy) {
   if (!ptr_ok(xq) || !f32_ok(s) || !ptr_ok(w) || !f32_ok(beta)) return UG_ERR_INVALID_ARG;
+  if (!opt_ok(bias)) return UG_ERR_INVALID_ARG;
   if (!opt_ok(acc) || !opt_ok(y) || (acc == nullptr && y == nullptr)) return UG_ERR_INVALID_ARG;
   if (M < 1 || N < 1 || K < 1) return UG_ERR_INVALID_ARG;
   if (wfmt != UG_W_I8 && wfmt != UG_W_PACK5) return UG_ERR_INVALID_ARG;
@@ -175,16 +176,17 @@ ug_status check_matmul(const int8_t *xq, int64_t ldx, const float *s, const void
 }  // namespace
 
 ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s, const void *w,
-                            int32_t wfmt, int64_t ldw, const float *beta, int64_t M, int64_t N,
-                            int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy,
-                            void *stream) {
-  ug_status st = check_matmul(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy);
+                            int32_t wfmt, int64_t ldw, const float *beta, const float *bias,
+                            int64_t M, int64_t N, int64_t K, int32_t *acc, int64_t ldacc, float *y,
+                            int64_t ldy, void *stream) {
+  ug_status st =
+      check_matmul(xq, ldx, s, w, wfmt, ldw, beta, bias, M, N, K, acc, ldacc, y, ldy);
   if (st != UG_OK) return st;
   if (M > UG_GEMV_MAX_M) return UG_ERR_INVALID_ARG;
   // the kernel addresses weights and activations with 32-bit buffer offsets
   if (N * ldw >= (INT64_C(1) << 31) || M * ldx >= (INT64_C(1) << 31)) return UG_ERR_UNSUPPORTED;
-  return hip_status(ug::launch_gemv(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy,
-                                    as_stream(stream)));
+  return hip_status(ug::launch_gemv(xq, ldx, s, w, wfmt, ldw, beta, bias, M, N, K, acc, ldacc, y,
+                                    ldy, as_stream(stream)));
 }
 
 size_t ug_gemv_plan_size(int32_t count) {
@@ -207,8 +209,8 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
     const int8_t *xq_in = fused ? (p.xq ? p.xq : (const int8_t *)p.x) : p.xq;
     const float *s_in = fused ? (p.s ? p.s : (const float *)p.x) : p.s;
     const int64_t ldxq = fused && !p.xq ? ug::round_up(p.K, 16) : p.ldxq;
-    ug_status st = check_matmul(xq_in, ldxq, s_in, p.w, p.wfmt, p.ldw, p.beta, p.M, p.N, p.K,
-                                p.acc, p.ldacc, p.y, p.ldy);
+    ug_status st = check_matmul(xq_in, ldxq, s_in, p.w, p.wfmt, p.ldw, p.beta, p.bias, p.M, p.N,
+                                p.K, p.acc, p.ldacc, p.y, p.ldy);
     if (st != UG_OK) return st;
     if (p.M > UG_GEMV_MAX_M) return UG_ERR_INVALID_ARG;
     if (fused) {
@@ -227,6 +229,7 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
     d.w = (const uint8_t *)p.w;
     d.ldw = p.ldw;
     d.beta = p.beta;
+    d.bias = p.bias;
     d.acc = p.acc;
     d.ldacc = p.ldacc;
     d.y = p.y;
@@ -297,10 +300,11 @@ size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t
 namespace {
 
 ug_status gemm_common(const int8_t *xq, int64_t ldx, const float *s, const void *w, int32_t wfmt,
-                      int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
-                      int32_t *acc, int64_t ldacc, float *y, int64_t ldy, void *ws,
+                      int64_t ldw, const float *beta, const float *bias, int64_t M, int64_t N,
+                      int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy, void *ws,
                       size_t ws_bytes, int tile, int splits, void *stream) {
-  ug_status st = check_matmul(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy);
+  ug_status st =
+      check_matmul(xq, ldx, s, w, wfmt, ldw, beta, bias, M, N, K, acc, ldacc, y, ldy);
   if (st != UG_OK) return st;
   hipStream_t hs = as_stream(stream);
   const size_t dec = wfmt == UG_W_PACK5 ? (size_t)(N * ug::round_up(K, 16)) : 0;
@@ -326,31 +330,31 @@ ug_status gemm_common(const int8_t *xq, int64_t ldx, const float *s, const void 
     int8_t *wu = static_cast<int8_t *>(ws) + dec_off;
     hipError_t e = ug::launch_unpack((const uint8_t *)w, ldw, N, K, wu, ldu, nullptr, hs);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(ug::launch_gemm_i8(xq, ldx, s, wu, ldu, beta, M, N, K, acc, ldacc, y, ldy,
-                                         split, tile, splits, hs));
+    return hip_status(ug::launch_gemm_i8(xq, ldx, s, wu, ldu, beta, bias, M, N, K, acc, ldacc, y,
+                                         ldy, split, tile, splits, hs));
   }
-  return hip_status(ug::launch_gemm_i8(xq, ldx, s, (const int8_t *)w, ldw, beta, M, N, K, acc,
-                                       ldacc, y, ldy, split, tile, splits, hs));
+  return hip_status(ug::launch_gemm_i8(xq, ldx, s, (const int8_t *)w, ldw, beta, bias, M, N, K,
+                                       acc, ldacc, y, ldy, split, tile, splits, hs));
 }
 
 }  // namespace
 
 ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s, const void *w,
-                            int32_t wfmt, int64_t ldw, const float *beta, int64_t M, int64_t N,
-                            int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy,
-                            void *ws, size_t ws_bytes, void *stream) {
-  return gemm_common(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy, ws, ws_bytes,
-                     -1, -1, stream);
+                            int32_t wfmt, int64_t ldw, const float *beta, const float *bias,
+                            int64_t M, int64_t N, int64_t K, int32_t *acc, int64_t ldacc, float *y,
+                            int64_t ldy, void *ws, size_t ws_bytes, void *stream) {
+  return gemm_common(xq, ldx, s, w, wfmt, ldw, beta, bias, M, N, K, acc, ldacc, y, ldy, ws,
+                     ws_bytes, -1, -1, stream);
 }
 
 ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s, const void *w,
-                                  int32_t wfmt, int64_t ldw, const float *beta, int64_t M,
-                                  int64_t N, int64_t K, int32_t *acc, int64_t ldacc, float *y,
-                                  int64_t ldy, void *ws, size_t ws_bytes, int32_t tile,
+                                  int32_t wfmt, int64_t ldw, const float *beta, const float *bias,
+                                  int64_t M, int64_t N, int64_t K, int32_t *acc, int64_t ldacc,
+                                  float *y, int64_t ldy, void *ws, size_t ws_bytes, int32_t tile,
                                   int32_t k_splits, void *stream) {
   if (tile < -1 || tile > 1 || k_splits == 0 || k_splits < -1) return UG_ERR_INVALID_ARG;
-  return gemm_common(xq, ldx, s, w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy, ws, ws_bytes,
-                     tile, k_splits, stream);
+  return gemm_common(xq, ldx, s, w, wfmt, ldw, beta, bias, M, N, K, acc, ldacc, y, ldy, ws,
+                     ws_bytes, tile, k_splits, stream);
 }
 
 }  // extern "C"

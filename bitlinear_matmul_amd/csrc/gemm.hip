@@ -49,7 +49,8 @@ __device__ inline uint4 load_piece(const int8_t *base, int64_t ld, int64_t row, 
 __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ xq, int64_t ldx,
                                                       const float *__restrict__ s,
                                                       const int8_t *__restrict__ w, int64_t ldw,
-                                                      const float *__restrict__ beta, int64_t M,
+                                                      const float *__restrict__ beta,
+                                                      const float *__restrict__ bias, int64_t M,
                                                       int64_t N, int64_t K,
                                                       int32_t *__restrict__ acc, int64_t ldacc,
                                                       float *__restrict__ y, int64_t ldy) {
@@ -132,7 +133,10 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
         if (n >= N) continue;
         const int v = c[i][j][r];
         if (acc) acc[m * ldacc + n] = v;
-        if (y) y[m * ldy + n] = (float)v * scale;
+        if (y) {
+          const float o = (float)v * scale;
+          y[m * ldy + n] = bias ? o + bias[n] : o;
+        }
       }
     }
   }
@@ -240,7 +244,8 @@ struct TileShape {
 template <int WM, int NT>
 __global__ __launch_bounds__(LTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__restrict__ s,
-                   const int8_t *__restrict__ w, int64_t ldw, const float *__restrict__ beta, int M,
+                   const int8_t *__restrict__ w, int64_t ldw, const float *__restrict__ beta,
+                   const float *__restrict__ bias, int M,
                    int N, int K, int32_t *__restrict__ acc, int64_t ldacc, float *__restrict__ y,
                    int64_t ldy, int S, int32_t *__restrict__ part,
                    unsigned long long *__restrict__ cnt, unsigned long long epoch) {
@@ -525,9 +530,28 @@ void gemm_i8_large(const int8_t *__restrict__ xq, int64_t ldx, const float *__re
         float *obase = out == 0 ? y : reinterpret_cast<float *>(acc);
         // rows are 16-byte aligned: the pitch is a multiple of 4 elements
         float *orow = obase + (int64_t)(tm + r0 + rrow) * ld + tn + c0 + col4;
+        // the bias of this lane's four columns, the same for every row
+        float4 b4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const bool add_bias = out == 0 && bias != nullptr;
+        if (add_bias) {
+          const int n = tn + c0 + col4;
+          if (kInside || n + 3 < N) {
+            b4 = *reinterpret_cast<const float4 *>(__builtin_assume_aligned(bias + n, 16));
+          } else {
+            if (n < N) b4.x = bias[n];
+            if (n + 1 < N) b4.y = bias[n + 1];
+            if (n + 2 < N) b4.z = bias[n + 2];
+          }
+        }
 #pragma unroll
         for (int pc = 0; pc < 32 / RPI; ++pc) {
-          const float4 o = *reinterpret_cast<const float4 *>(rbase + RPI * W * pc);
+          float4 o = *reinterpret_cast<const float4 *>(rbase + RPI * W * pc);
+          if (add_bias) {
+            o.x = o.x + b4.x;
+            o.y = o.y + b4.y;
+            o.z = o.z + b4.z;
+            o.w = o.w + b4.w;
+          }
           float *dst = orow + (int64_t)(RPI * pc) * ld;
           if (kInside) {
             *reinterpret_cast<float4 *>(__builtin_assume_aligned(dst, 16)) = o;
@@ -745,12 +769,14 @@ LargePlan plan_large(int64_t M, int64_t N, int64_t nk, bool can_split, int cus) 
 
 template <int WM, int NT>
 void launch_large(const LargePlan &p, hipStream_t st, const int8_t *xq, int64_t ldx,
-                  const float *s, const int8_t *w, int64_t ldw, const float *beta, int64_t M,
+                  const float *s, const int8_t *w, int64_t ldw, const float *beta,
+                  const float *bias, int64_t M,
                   int64_t N, int64_t K, int32_t *acc, int64_t ldacc, float *y, int64_t ldy,
                   int32_t *part, unsigned long long *cnt, unsigned long long epoch) {
   const int64_t blocks = ceil_div(p.T * p.S, kXcds) * kXcds;
   hipLaunchKernelGGL((gemm_i8_large<WM, NT>), dim3((unsigned)blocks), dim3(LTHREADS), 0, st, xq,
-                     ldx, s, w, ldw, beta, (int)M, (int)N, (int)K, acc, ldacc, y, ldy, p.S, part,
+                     ldx, s, w, ldw, beta, bias, (int)M, (int)N, (int)K, acc, ldacc, y, ldy, p.S,
+                     part,
                      cnt, epoch);
 }
 
@@ -767,7 +793,8 @@ size_t gemm_split_area_bytes() {
 }
 
 hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const int8_t *w,
-                          int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
+                          int64_t ldw, const float *beta, const float *bias, int64_t M, int64_t N,
+                          int64_t K,
                           int32_t *acc, int64_t ldacc, float *y, int64_t ldy, void *split,
                           int tile, int splits, hipStream_t st) {
   if (large_tiles(M, N, ldx, ldw)) {
@@ -796,15 +823,15 @@ hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s, const i
       epoch = next_epoch();
     }
     if (p.shape == 0)
-      launch_large<2, 8>(p, st, xq, ldx, s, w, ldw, beta, M, N, K, acc, ldacc, y, ldy, part, cnt,
+      launch_large<2, 8>(p, st, xq, ldx, s, w, ldw, beta, bias, M, N, K, acc, ldacc, y, ldy, part, cnt,
                          epoch);
     else
-      launch_large<4, 5>(p, st, xq, ldx, s, w, ldw, beta, M, N, K, acc, ldacc, y, ldy, part, cnt,
+      launch_large<4, 5>(p, st, xq, ldx, s, w, ldw, beta, bias, M, N, K, acc, ldacc, y, ldy, part, cnt,
                          epoch);
     return hipGetLastError();
   }
   dim3 grid((unsigned)ceil_div(N, BN), (unsigned)ceil_div(M, BM));
-  hipLaunchKernelGGL(gemm_i8_kernel, grid, dim3(256), 0, st, xq, ldx, s, w, ldw, beta, M, N, K,
+  hipLaunchKernelGGL(gemm_i8_kernel, grid, dim3(256), 0, st, xq, ldx, s, w, ldw, beta, bias, M, N, K,
                      acc, ldacc, y, ldy);
   return hipGetLastError();
 }

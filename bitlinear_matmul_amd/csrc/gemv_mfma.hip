@@ -718,7 +718,8 @@ struct Wave {
             if (d.acc) gp(d.acc)[(int64_t)m * d.ldacc + n] = val;
             if (d.y) {
               const float scale = sm[m] * beta;
-              gp(d.y)[(int64_t)m * d.ldy + n] = (float)val * scale;
+              const float v = (float)val * scale;
+              gp(d.y)[(int64_t)m * d.ldy + n] = d.bias ? v + gp(d.bias)[n] : v;
             }
           }
         }
@@ -982,7 +983,10 @@ __device__ __forceinline__ void chunked_items(const GemvDesc &d, Smem<FMT> &sh, 
               if (n < d.N && m < d.M) {
                 const int val = acc[g][b][e];
                 if (d.acc) gp(d.acc)[(int64_t)m * d.ldacc + n] = val;
-                if (d.y) gp(d.y)[(int64_t)m * d.ldy + n] = (float)val * (sh.sm[m] * beta);
+                if (d.y) {
+                  const float v = (float)val * (sh.sm[m] * beta);
+                  gp(d.y)[(int64_t)m * d.ldy + n] = d.bias ? v + gp(d.bias)[n] : v;
+                }
               }
             }
             acc[g][b] = v4i{0, 0, 0, 0};
@@ -1103,7 +1107,7 @@ __global__ __launch_bounds__(kThreads) void gemv_stream_grouped(const GemvDesc *
 // A decode-sized launch is one chain of dependent steps per block: fetch the
 // block's descriptor, issue the activation and weight loads, stage the
 // activations, multiply, reduce, store.  This path keeps that chain short:
-// the descriptor (FineBlock) is one 128-byte fetch that holds every derived
+// the descriptor (FineBlock) is one round trip of scalar loads that holds every derived
 // value (no lane divides by a run-time value), the decode table and the
 // zeroed slots are written while it is in flight, the weight loads leave as
 // soon as it arrives, and the activations are quantized (or copied) straight
@@ -1439,10 +1443,14 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
   if (tid < items * 16) {  // thread (item, n) writes column n of the item, every row
     const int li = tid >> 4, n = tid & 15, ng = (b.i0 + li) * 16 + n;
     if (ng < b.N) {
+      const float bn = b.bias ? gp(b.bias)[ng] : 0.0f;
       for (int m = 0; m < M; ++m) {
         const int val = sh.slots[li * 256 + m * 16 + n];
         if (b.acc) gp(b.acc)[(int64_t)m * b.ldacc + ng] = val;
-        if (b.y) gp(b.y)[(int64_t)m * b.ldy + ng] = (float)val * (sh.sm[m] * beta);
+        if (b.y) {
+          const float v = (float)val * (sh.sm[m] * beta);
+          gp(b.y)[(int64_t)m * b.ldy + ng] = b.bias ? v + bn : v;
+        }
       }
     }
   }
@@ -1489,6 +1497,7 @@ FineBlock fine_block_of(const GemvDesc &d, int i0, int i1, bool first) {
   f.x = fused ? (const void *)d.x : (const void *)d.xq;
   f.w = d.w;
   f.beta = d.beta;
+  f.bias = d.bias;
   f.y = d.y;
   f.acc = d.acc;
   f.s = fused ? (first ? d.s : nullptr) : d.s;
@@ -1682,7 +1691,8 @@ hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int3
 }
 
 hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void *w, int wfmt,
-                       int64_t ldw, const float *beta, int64_t M, int64_t N, int64_t K,
+                       int64_t ldw, const float *beta, const float *bias, int64_t M, int64_t N,
+                       int64_t K,
                        int32_t *acc, int64_t ldacc, float *y, int64_t ldy, hipStream_t st) {
   GemvDesc d{};
   d.x = nullptr;
@@ -1692,6 +1702,7 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
   d.w = (const uint8_t *)w;
   d.ldw = ldw;
   d.beta = beta;
+  d.bias = bias;
   d.acc = acc;
   d.ldacc = ldacc;
   d.y = y;

@@ -56,6 +56,7 @@ struct GemvDesc {
   const uint8_t *w;    // weights, UG_W_I8 or UG_W_PACK5 rows of ldw bytes
   int64_t ldw;
   const float *beta;
+  const float *bias;   // fp32 [N] added to y, or null
   int32_t *acc;
   int64_t ldacc;
   float *y;
@@ -72,12 +73,14 @@ constexpr int kGemvBlocks = 256;    // at most one GEMV block per CU
 constexpr int kGemvFineWaves = 8;   // waves of a fine-split GEMV block
 
 // One block of the fine GEMV split: every value its waves need, precomputed,
-// in 128 bytes that the planner places at a 128-byte boundary, so the
-// block reads all of it in one scalar round trip.
+// in 144 bytes that the planner places in a table starting at a 128-byte
+// boundary; the block reads all of it with scalar loads issued together
+// (one round trip).
 struct FineBlock {
   const void *x;       // fp32 activations (quantized in the launch) or x_q
   const uint8_t *w;    // weight rows of ldw bytes
   const float *beta;
+  const float *bias;   // fp32 [N] added to y, or null
   float *y;            // [M][ldy], or null
   int32_t *acc;        // [M][ldacc], or null
   float *s;            // x_q given: its row scales; fp32 given: output or null
@@ -95,8 +98,9 @@ struct FineBlock {
   // (a block orders its pieces step-major);
   // byte 2 = row and byte 3 = chunk of its first activation tile
   uint32_t wave_start[kGemvFineWaves];
+  int32_t pad[2];
 };
-static_assert(sizeof(FineBlock) == 128, "a fine block is one 128-byte fetch");
+static_assert(sizeof(FineBlock) == 144, "fine block layout");
 
 // One block of a GEMV launch: problem p and its item range [i0, i1) (fine
 // split), or the first problem p and the plan-wide item range (stream split),
@@ -132,6 +136,7 @@ hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int3
                                int32_t grid, int32_t variant, hipStream_t st);
 hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const void *w, int wfmt, int64_t ldw, const float *beta,
+                       const float *bias,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,
                        int64_t ldacc, float *y, int64_t ldy, hipStream_t st);
 // Bytes of the GEMM's K-split area (tile counters at offset 0, then one
@@ -146,6 +151,7 @@ constexpr size_t kGemmCounterBytes = 2048;
 // choice) or a K-split count, used where it fits (else 1).
 hipError_t launch_gemm_i8(const int8_t *xq, int64_t ldx, const float *s,
                           const int8_t *w, int64_t ldw, const float *beta,
+                          const float *bias,
                           int64_t M, int64_t N, int64_t K, int32_t *acc,
                           int64_t ldacc, float *y, int64_t ldy, void *split,
                           int tile, int splits, hipStream_t st);

@@ -48,16 +48,16 @@ SIGNATURES = {
                                               _vp]),
     "ug_pack_trits": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
     "ug_unpack_trits": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
-    "ug_bitlinear_gemv": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
-                                 _i64, _vp, _i64, _vp]),
+    "ug_bitlinear_gemv": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, _i64,
+                                 _vp, _i64, _vp, _i64, _vp]),
     "ug_bitlinear_gemm_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "ug_gemv_plan_size": (_sz, [_i32]),
     "ug_gemv_plan_init": (_i32, [_vp, _i32, _vp, _sz, _vp]),
     "ug_bitlinear_gemv_grouped": (_i32, [_vp, _vp, _vp]),
-    "ug_bitlinear_gemm": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64, _vp,
-                                 _i64, _vp, _i64, _vp, _sz, _vp]),
-    "ug_bitlinear_gemm_tiled": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _i64, _i64, _i64,
-                                       _vp, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp]),
+    "ug_bitlinear_gemm": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, _i64,
+                                 _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "ug_bitlinear_gemm_tiled": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64,
+                                       _i64, _vp, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp]),
 }
 
 UG_GEMM_COUNTER_BYTES = 2048
@@ -69,7 +69,7 @@ class GemvProblem(ctypes.Structure):
     """ug_gemv_problem (include/ug.h)."""
     _fields_ = [("x", _vp), ("ldx", _i64), ("eps", _f32), ("xq", _vp), ("ldxq", _i64),
                 ("s", _vp), ("w", _vp), ("wfmt", _i32), ("ldw", _i64), ("beta", _vp),
-                ("M", _i64), ("N", _i64), ("K", _i64), ("acc", _vp), ("ldacc", _i64),
+                ("bias", _vp), ("M", _i64), ("N", _i64), ("K", _i64), ("acc", _vp), ("ldacc", _i64),
                 ("y", _vp), ("ldy", _i64)]
 
 
@@ -263,9 +263,10 @@ def _weight_args(w, wfmt, K):
 
 
 def ug_bitlinear_gemv(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=False,
-                      want_y=True, stream=None):
+                      want_y=True, bias=None, stream=None):
     """Decode GEMV: xq int8 [M,K] (M <= 64), w int8 [N,K] or packed uint8
-    [N,ldp] -> (acc int32 [M,N] or None, y fp32 [M,N] or None)."""
+    [N,ldp] -> (acc int32 [M,N] or None, y fp32 [M,N] or None); bias: fp32
+    [N] added to y, or None."""
     M = xq.shape[0]
     K = xq.shape[1] if K is None else K
     N, ldw = _weight_args(w, wfmt, K)
@@ -273,8 +274,8 @@ def ug_bitlinear_gemv(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=F
         acc = empty_pitched(M, N, torch.int32, xq.device)
     if want_y and y is None:
         y = empty_pitched(M, N, torch.float32, xq.device)
-    _check(lib().ug_bitlinear_gemv(_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), M, N, K,
-                                   _p(acc), _ld(acc) if acc is not None else 0, _p(y),
+    _check(lib().ug_bitlinear_gemv(_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), _p(bias),
+                                   M, N, K, _p(acc), _ld(acc) if acc is not None else 0, _p(y),
                                    _ld(y) if y is not None else 0, _stream(stream)),
            "ug_bitlinear_gemv")
     return acc, y
@@ -300,7 +301,8 @@ def gemm_workspace(need, device):
 
 
 def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=False,
-                      want_y=True, ws=None, split=True, tile=None, k_splits=None, stream=None):
+                      want_y=True, ws=None, split=True, tile=None, k_splits=None, bias=None,
+                      stream=None):
     """Prefill GEMM (int8 MFMA): same arguments as the GEMV, any M.
     ws: workspace (default: the shared per-device one); split=False passes
     only what UG_W_PACK5 decoding needs, so every block computes whole
@@ -324,7 +326,7 @@ def ug_bitlinear_gemm(xq, s, w, wfmt, beta, K=None, acc=None, y=None, want_acc=F
         ws = gemm_workspace(need, xq.device)
     # the whole buffer: the library lays it out by its size alone
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    args = [_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), M, N, K,
+    args = [_p(xq), _ld(xq), _p(s), _p(w), wfmt, ldw, _p(beta), _p(bias), M, N, K,
             _p(acc), _ld(acc) if acc is not None else 0, _p(y), _ld(y) if y is not None else 0,
             _p(ws) if ws_bytes else None, ws_bytes]
     if tile is None and k_splits is None:
@@ -357,7 +359,7 @@ def ug_gemv_plan_init(problems, device=None):
     arr = (GemvProblem * len(problems))()
     keep = []
     for i, p in enumerate(problems):
-        x, xq, s, w, y, acc = (p.get(k) for k in ("x", "xq", "s", "w", "y", "acc"))
+        x, xq, s, w, y, acc, bias = (p.get(k) for k in ("x", "xq", "s", "w", "y", "acc", "bias"))
         ref = x if x is not None else xq
         M = ref.shape[0]
         K = p.get("K", ref.shape[1])
@@ -366,7 +368,8 @@ def ug_gemv_plan_init(problems, device=None):
         arr[i] = GemvProblem(
             x=_p(x).value, ldx=_ld(x) if x is not None else 0, eps=p.get("eps", 1e-5),
             xq=_p(xq).value, ldxq=_ld(xq) if xq is not None else 0, s=_p(s).value,
-            w=_p(w).value, wfmt=wfmt, ldw=_ld(w), beta=_p(p["beta"]).value, M=M, N=N, K=K,
+            w=_p(w).value, wfmt=wfmt, ldw=_ld(w), beta=_p(p["beta"]).value,
+            bias=_p(bias).value, M=M, N=N, K=K,
             acc=_p(acc).value, ldacc=_ld(acc) if acc is not None else 0,
             y=_p(y).value, ldy=_ld(y) if y is not None else 0)
         keep.append(p)

@@ -201,11 +201,13 @@ ug_status ug_unpack_trits(const uint8_t *packed, int64_t ldp, int64_t N,
                           int32_t *bad_count, void *stream);
 
 /*
- * Decode GEMV: the integer forward y = (x_q W_q^T)(s beta) ("autograd on a
- * byte-graph", no bias) for a few activation rows:
+ * Decode GEMV: the integer forward y = (x_q W_q^T)(s beta) + b ("autograd
+ * on a byte-graph") for a few activation rows:
  *     acc[m][n] = sum_k xq[m][k] * W_q[n][k]      (int32, exact),
- *     y[m][n]   = fl((float)acc[m][n] * fl(s[m] * beta)).
+ *     y[m][n]   = fl((float)acc[m][n] * fl(s[m] * beta))          (bias NULL)
+ *     y[m][n]   = fl(fl((float)acc[m][n] * fl(s[m] * beta)) + bias[n]).
  *  xq int8 [M][ldx]; s fp32 [M]; beta fp32 [1] (device);
+ *  bias fp32 [N] (device, 16-byte aligned) or NULL; acc never includes it;
  *  w: wfmt == UG_W_I8: int8 [N][ldw]; UG_W_PACK5: uint8 [N][ldw] bytes,
  *     ldw >= ceil(K/5);
  *  acc int32 [M][ldacc] out or NULL; y fp32 [M][ldy] out or NULL (not both
@@ -213,9 +215,9 @@ ug_status ug_unpack_trits(const uint8_t *packed, int64_t ldp, int64_t N,
  */
 ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s,
                             const void *w, int32_t wfmt, int64_t ldw,
-                            const float *beta, int64_t M, int64_t N,
-                            int64_t K, int32_t *acc, int64_t ldacc, float *y,
-                            int64_t ldy, void *stream);
+                            const float *beta, const float *bias, int64_t M,
+                            int64_t N, int64_t K, int32_t *acc, int64_t ldacc,
+                            float *y, int64_t ldy, void *stream);
 
 /*
  * Grouped decode GEMV: several independent ug_bitlinear_gemv problems (for
@@ -231,7 +233,8 @@ ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s,
  *   xq, ldxq     int8 [M][ldxq]: input when x == NULL, else optional output
  *                of the quantized activations (NULL: not written);
  *   s            fp32 [M]: input when x == NULL, else optional output;
- *   w, wfmt, ldw, beta, M, N, K, acc, ldacc, y, ldy: as ug_bitlinear_gemv.
+ *   w, wfmt, ldw, beta, bias, M, N, K, acc, ldacc, y, ldy: as
+ *                ug_bitlinear_gemv.
  * Every problem of a group has the same wfmt and the same activation-row
  * class (M <= 16, 17..32 or 33..64).  With x != NULL the quantized rows
  * must fit the kernel's 64 KB staging area: M * Kp <= 65536, else
@@ -257,6 +260,7 @@ typedef struct ug_gemv_problem {
     int32_t wfmt;
     int64_t ldw;
     const float *beta;
+    const float *bias;
     int64_t M, N, K;
     int32_t *acc;
     int64_t ldacc;
@@ -308,9 +312,9 @@ size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
 #define UG_GEMM_SPLIT_AREA (UG_GEMM_COUNTER_BYTES + 256 * 256 * 256 * 4)
 
 /*
- * Prefill GEMM: the same result as ug_bitlinear_gemv for any M >= 1, as a
- * dense int8 contraction on the matrix cores (ternary values are exact in
- * int8).  Same arguments, plus the workspace ws (device memory, 16-byte
+ * Prefill GEMM: the same result as ug_bitlinear_gemv (bias included) for
+ * any M >= 1, as a dense int8 contraction on the matrix cores (ternary
+ * values are exact in int8).  Same arguments, plus the workspace ws (device memory, 16-byte
  * aligned, any contents; NULL allowed for UG_W_I8).  Its first
  * UG_GEMM_COUNTER_BYTES only ever hold K-split tile counters:
  *   - ws_bytes >= UG_GEMM_SPLIT_AREA + decoded bytes: the split area starts
@@ -325,9 +329,9 @@ size_t ug_bitlinear_gemm_workspace_size(int64_t M, int64_t N, int64_t K,
  */
 ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s,
                             const void *w, int32_t wfmt, int64_t ldw,
-                            const float *beta, int64_t M, int64_t N,
-                            int64_t K, int32_t *acc, int64_t ldacc, float *y,
-                            int64_t ldy, void *ws, size_t ws_bytes,
+                            const float *beta, const float *bias, int64_t M,
+                            int64_t N, int64_t K, int32_t *acc, int64_t ldacc,
+                            float *y, int64_t ldy, void *ws, size_t ws_bytes,
                             void *stream);
 
 /*
@@ -341,11 +345,11 @@ ug_status ug_bitlinear_gemm(const int8_t *xq, int64_t ldx, const float *s,
  */
 ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                                   const void *w, int32_t wfmt, int64_t ldw,
-                                  const float *beta, int64_t M, int64_t N,
-                                  int64_t K, int32_t *acc, int64_t ldacc,
-                                  float *y, int64_t ldy, void *ws,
-                                  size_t ws_bytes, int32_t tile,
-                                  int32_t k_splits, void *stream);
+                                  const float *beta, const float *bias,
+                                  int64_t M, int64_t N, int64_t K,
+                                  int32_t *acc, int64_t ldacc, float *y,
+                                  int64_t ldy, void *ws, size_t ws_bytes,
+                                  int32_t tile, int32_t k_splits, void *stream);
 
 #ifdef __cplusplus
 }

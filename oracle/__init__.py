@@ -90,7 +90,7 @@ def _open(path):
         "ugref_matmul_i32": (None, [_i8p, _i64, _i8p, _i64, _i64, _i64, _i64, _i32p, _i64]),
         "ugref_matmul_i32_pairs": (None, [_i8p, _i64, _i8p, _i64, _i64, _i64p, _i64p, _i64,
                                           _i32p]),
-        "ugref_epilogue": (None, [_i32p, _i64, _f32p, _f32, _i64, _i64, _f32p, _i64]),
+        "ugref_epilogue": (None, [_i32p, _i64, _f32p, _f32, _f32p, _i64, _i64, _f32p, _i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -246,25 +246,31 @@ def matmul_i32_pairs(xq, wq, mi, ni):
     return out
 
 
-def epilogue(acc, s, beta):
+def epilogue(acc, s, beta, bias=None):
     """y = fl((float)acc * fl(s * beta)) -- the rescale of
-    y = (x_q W_q^T)(s beta)."""
+    y = (x_q W_q^T)(s beta) + b ("autograd on a byte-graph"); with a bias
+    (fp32 [N]) each output then adds b[n] in one more rounding."""
     acc = _c2d(acc, np.int32)
     M, N = acc.shape
     s = np.ascontiguousarray(np.asarray(s, np.float32).reshape(M))
+    bp = None
+    if bias is not None:
+        bias = np.ascontiguousarray(np.asarray(bias, np.float32).reshape(N))
+        bp = _ptr(bias, ctypes.c_float)
     y = np.empty((M, N), np.float32)
     _load().ugref_epilogue(_ptr(acc, ctypes.c_int32), N, _ptr(s, ctypes.c_float),
-                           float(np.float32(beta)), M, N, _ptr(y, ctypes.c_float), N)
+                           float(np.float32(beta)), bp, M, N, _ptr(y, ctypes.c_float), N)
     return y
 
 
-def bitlinear(x, W, eps=1e-5):
+def bitlinear(x, W, eps=1e-5, bias=None):
     """The whole forward: quantize x per row and W by absmean, integer
-    matmul, rescale.  Returns dict of every intermediate."""
+    matmul, rescale (plus the bias, if given).  Returns dict of every
+    intermediate."""
     xq, s = quant_act(x, eps)
     wq, beta = quant_weight_absmean(W, eps)
     acc = matmul_i32(xq, wq)
-    y = epilogue(acc, s, beta)
+    y = epilogue(acc, s, beta, bias)
     return dict(xq=xq, s=s, wq=wq, beta=beta, acc=acc, y=y)
 
 

@@ -15,7 +15,7 @@
  *     (s = max|x|/127 + eps, x_q = clip(round(x/s), -127, 127)), with the
  *     symmetric range [-127, 127].
  *   - same page, section "autograd on a byte-graph": the integer forward
- *     y = (x_q W_q^T)(s beta) (+ b; no bias here).
+ *     y = (x_q W_q^T)(s beta) + b (the bias optional).
  *   - same page, section "attention, as graph ops": RMSNorm with a learnable
  *     fp32 gain, and the per-token (per-row) scale.
  *   - "ultragraph-1bit 0.12.0" README, sections "A whole ternary GPT" and
@@ -35,7 +35,7 @@
  *   - the 5-trits-per-byte code of trits t_0..t_4 (t_0 at the lowest K) is
  *     121 + sum_j t_j 3^j; trits past K are 0; row bytes past ceil(K/5) are
  *     121; codes 243..255 are invalid and decode to five zero trits;
- *   - y = fl((float)acc * fl(s * beta)).
+ *   - y = fl((float)acc * fl(s * beta)), plus fl(. + b[n]) with a bias.
  *
  * OpenMP runs only over independent rows or independent chunks, so every
  * result is bit-identical at any thread count.
@@ -351,14 +351,22 @@ void ugref_matmul_i32_pairs(const int8_t *xq, int64_t ldx, const int8_t *wq,
     }
 }
 
-/* y[m][n] = fl((float)acc[m][n] * fl(s[m] * beta)). */
+/* y[m][n] = fl((float)acc[m][n] * fl(s[m] * beta)), then, with a bias,
+ * y[m][n] = fl(that + b[n]): the deployed forward y = (x_q W_q^T)(s beta) + b
+ * ("autograd on a byte-graph"), rescale first, one rounding per operation.
+ * b == NULL: no bias. */
 void ugref_epilogue(const int32_t *acc, int64_t ldacc, const float *s,
-                    float beta, int64_t M, int64_t N, float *y, int64_t ldy)
+                    float beta, const float *b, int64_t M, int64_t N, float *y,
+                    int64_t ldy)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         float scale = s[m] * beta;
-        for (int64_t n = 0; n < N; ++n)
-            y[m * ldy + n] = (float)acc[m * ldacc + n] * scale;
+        for (int64_t n = 0; n < N; ++n) {
+            float v = (float)acc[m * ldacc + n] * scale;
+            if (b)
+                v = v + b[n];
+            y[m * ldy + n] = v;
+        }
     }
 }

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(ug):
 
 
 def test_version_and_status_strings(ug):
-    assert ug.ug_version() == 10000
+    assert ug.ug_version() == 10100
     for st in range(5):
         assert ug.status_string(st).startswith(["UG_OK", "UG_ERR_INVALID_ARG",
                                                 "UG_ERR_UNSUPPORTED", "UG_ERR_WORKSPACE",
@@ -195,12 +195,12 @@ def test_pack_rejects(ug):
 
 
 def _gemv(L, **kw):
-    a = dict(xq=A, ldx=128, s=A2, w=A3, wfmt=0, ldw=128, beta=A4, M=4, N=64, K=128,
+    a = dict(xq=A, ldx=128, s=A2, w=A3, wfmt=0, ldw=128, beta=A4, bias=NULL, M=4, N=64, K=128,
              acc=NULL, ldacc=0, y=ctypes.c_void_p(0x500000), ldy=64, st=S)
     a.update(kw)
     return L.ug_bitlinear_gemv(a["xq"], a["ldx"], a["s"], a["w"], a["wfmt"], a["ldw"], a["beta"],
-                               a["M"], a["N"], a["K"], a["acc"], a["ldacc"], a["y"], a["ldy"],
-                               a["st"])
+                               a["bias"], a["M"], a["N"], a["K"], a["acc"], a["ldacc"], a["y"],
+                               a["ldy"], a["st"])
 
 
 def test_gemv_rejects(ug):
@@ -218,6 +218,7 @@ def test_gemv_rejects(ug):
     assert _gemv(L, acc=ctypes.c_void_p(0x600000), ldacc=30) == E
     assert _gemv(L, s=ctypes.c_void_p(0x100002)) == E   # s needs 4-byte alignment
     assert _gemv(L, K=132105, ldx=132112, ldw=132112) == ug.UG_ERR_UNSUPPORTED
+    assert _gemv(L, bias=ctypes.c_void_p(0x600008)) == E   # bias needs 16-byte alignment
 
 
 def test_gemm_rejects(ug):
@@ -225,8 +226,8 @@ def test_gemm_rejects(ug):
     E = ug.UG_ERR_INVALID_ARG
 
     def call(ws=NULL, ws_bytes=0, wfmt=0, ldw=128, y=ctypes.c_void_p(0x500000)):
-        return L.ug_bitlinear_gemm(A, 128, A2, A3, wfmt, ldw, A4, 300, 64, 128, NULL, 0, y, 64,
-                                   ws, ws_bytes, S)
+        return L.ug_bitlinear_gemm(A, 128, A2, A3, wfmt, ldw, A4, NULL, 300, 64, 128, NULL, 0, y,
+                                   64, ws, ws_bytes, S)
 
     assert call(y=NULL) == E
     assert call(wfmt=1, ldw=32) == ug.UG_ERR_WORKSPACE
@@ -242,8 +243,8 @@ def test_gemm_tiled_rejects(ug):
     E = ug.UG_ERR_INVALID_ARG
 
     def call(tile, splits):
-        return L.ug_bitlinear_gemm_tiled(A, 128, A2, A3, 0, 128, A4, 300, 64, 128, NULL, 0, NULL,
-                                         64, NULL, 0, tile, splits, S)
+        return L.ug_bitlinear_gemm_tiled(A, 128, A2, A3, 0, 128, A4, NULL, 300, 64, 128, NULL, 0,
+                                         NULL, 64, NULL, 0, tile, splits, S)
 
     assert call(2, -1) == E
     assert call(-2, -1) == E

@@ -50,6 +50,36 @@ def test_decode_stack_one_launch_fused_quant(dev):
         assert_bits_equal(host(p["y"]), a, "replay")
 
 
+@pytest.mark.parametrize("M,shapes", [(1, [(1152, 384), (384, 384), (1536, 384), (384, 1536)]),
+                                      (4, [(6912, 2560), (2560, 2560)]),
+                                      (1, [(6912, 2560), (2560, 6912)] * 8)])
+def test_grouped_bias_fused(dev, M, shapes):
+    """Grouped launches with a bias per problem (the deployed forward's
+    "+ b", "autograd on a byte-graph"), fp32 activations quantized in the
+    launch: the fine split (the decode pass) and the stream split."""
+    rng = np.random.default_rng([311, M, len(shapes)])
+    probs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        _case("grouped bias", M, i, N, K)
+        x = rng.standard_normal((M, K), dtype=np.float32)
+        W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+        b = rng.standard_normal(N, dtype=np.float32) * np.float32(0.1)
+        wq_r, beta_r = oracle.quant_weight_absmean(W)
+        pk_r, _ = oracle.pack_trits(wq_r)
+        p = dict(x=pitched(x), w=pitched(pk_r), wfmt=ug.UG_W_PACK5, beta=scalar_dev(beta_r),
+                 K=K, bias=vec(b), y=ug.empty_pitched(M, N, torch.float32, dev),
+                 acc=ug.empty_pitched(M, N, torch.int32, dev))
+        probs.append(p)
+        xq_r, s_r = oracle.quant_act(x)
+        acc_r = oracle.matmul_i32(xq_r, wq_r)
+        refs.append((acc_r, oracle.epilogue(acc_r, s_r, beta_r, b)))
+    plan = ug.ug_gemv_plan_init(probs)
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for i, (p, (acc_r, y_r)) in enumerate(zip(probs, refs)):
+        assert_bits_equal(host(p["acc"]), acc_r, "acc %d" % i)
+        assert_bits_equal(host(p["y"]), y_r, "y with bias %d" % i)
+
+
 def _staged_kp(wfmt, M, K):
     rb = -(-K // 5) if wfmt == ug.UG_W_PACK5 else K
     cls = 0 if M <= 16 else (1 if M <= 32 else 2)

@@ -423,3 +423,27 @@ def test_gemm_extreme_values(dev):
     acc_v, _ = ug.ug_bitlinear_gemv(pitched(xq), vec(s), pitched(wq), ug.UG_W_I8,
                                     scalar_dev(np.float32(1)), want_acc=True)
     assert_bits_equal(host(acc_v), oracle.matmul_i32(xq, wq), "acc gemv")
+
+
+@pytest.mark.parametrize("M,N,K,fmt,path", [
+    (1, 1152, 384, 1, "gemv"), (4, 700, 333, 0, "gemv"), (16, 2560, 6912, 1, "gemv"),
+    (64, 2560, 2560, 1, "gemv"), (33, 1000, 640, 0, "gemv"),
+    (32, 512, 128, 0, "gemm"), (300, 700, 197, 0, "gemm"), (2048, 2560, 6912, 0, "gemm"),
+    (4096, 6912, 2560, 0, "gemm"), (600, 1300, 1000, 1, "gemm")])
+def test_bias_epilogue(dev, M, N, K, fmt, path):
+    """The deployed forward with its bias ("autograd on a byte-graph":
+    y = (x_q W_q^T)(s beta) + b): y bit-exact against the oracle's
+    fl(fl(acc * fl(s * beta)) + b[n]); acc unchanged by the bias; every
+    matmul kernel (fine, stream and chunked GEMV splits; small, large and
+    K-split GEMM tiles; ragged edges)."""
+    _print_case("bias", M, N, K, fmt, path)
+    rng = np.random.default_rng([131, M, N, K])
+    xq, wq, s, beta = _rand_problem(rng, M, N, K)
+    bias = rng.standard_normal(N, dtype=np.float32)
+    w = pitched(oracle.pack_trits(wq)[0]) if fmt == ug.UG_W_PACK5 else pitched(wq)
+    fn = ug.ug_bitlinear_gemv if path == "gemv" else ug.ug_bitlinear_gemm
+    acc_d, y_d = fn(pitched(xq), vec(s), w, fmt, scalar_dev(beta), K=K, want_acc=True,
+                    bias=vec(bias))
+    acc_r = oracle.matmul_i32(xq, wq)
+    assert_bits_equal(host(acc_d), acc_r, "acc")
+    assert_bits_equal(host(y_d), oracle.epilogue(acc_r, s, beta, bias), "y with bias")

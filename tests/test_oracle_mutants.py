@@ -108,13 +108,25 @@ MUTANTS = {
         ["test_ternary_golden_ties", "test_ternary_true_division_cases"]),
     # --- the rescale ("autograd on a byte-graph") ---------------------------
     "epilogue_acc_times_s_first": (
-        [("y[m * ldy + n] = (float)acc[m * ldacc + n] * scale;",
-          "y[m * ldy + n] = ((float)acc[m * ldacc + n] * s[m]) * beta;")],
+        [("float v = (float)acc[m * ldacc + n] * scale;",
+          "float v = ((float)acc[m * ldacc + n] * s[m]) * beta;")],
         ["test_epilogue_grouping_cases"]),
     "epilogue_acc_times_beta_first": (
-        [("y[m * ldy + n] = (float)acc[m * ldacc + n] * scale;",
-          "y[m * ldy + n] = ((float)acc[m * ldacc + n] * beta) * s[m];")],
+        [("float v = (float)acc[m * ldacc + n] * scale;",
+          "float v = ((float)acc[m * ldacc + n] * beta) * s[m];")],
         ["test_epilogue_grouping_cases"]),
+    "epilogue_bias_fused_multiply_add": (
+        [("            float v = (float)acc[m * ldacc + n] * scale;\n"
+          "            if (b)\n                v = v + b[n];",
+          "            float v = (float)acc[m * ldacc + n] * scale;\n"
+          "            if (b)\n                v = fmaf((float)acc[m * ldacc + n], scale, b[n]);")],
+        ["test_epilogue_bias_cases"]),
+    "epilogue_bias_before_rescale": (
+        [("            float v = (float)acc[m * ldacc + n] * scale;\n"
+          "            if (b)\n                v = v + b[n];",
+          "            float v = (float)acc[m * ldacc + n] * scale;\n"
+          "            if (b)\n                v = ((float)acc[m * ldacc + n] + b[n]) * scale;")],
+        ["test_epilogue_bias_cases"]),
     # --- five trits per byte (README "A whole ternary GPT") -----------------
     "pack_digits_reversed": (
         [("                int pow3 = 1;\n                for (int j = 0; j < 5; ++j) {",

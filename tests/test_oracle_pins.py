@@ -685,3 +685,31 @@ def test_rmsnorm_exact_given_sum():
             assert (F(r) - ulp / 2) ** 2 <= F(v) <= (F(r) + ulp / 2) ** 2
             for k in range(0, K, max(1, K // 97)):
                 assert xn[m, k] == f32_rne(F(f32_rne(F(x[m, k]) / F(r))) * F(g[k])), (K, m, k)
+
+
+def test_epilogue_bias_cases():
+    """With the bias of the deployed forward ("autograd on a byte-graph":
+    y = (x_q W_q^T)(s beta) + b): the rescale is rounded, then b is added
+    and rounded, on inputs where one fused multiply-add would round
+    differently; and a zero bias changes no bit."""
+    rows = _rounding_rows("bias")
+    assert len(rows) >= 3
+    for acc_s, s_s, b_s, c_s in rows:
+        acc = int(acc_s)
+        s, b, c = (np.float32(float.fromhex(v)) for v in (s_s, b_s, c_s))
+        y = oracle.epilogue(np.array([[acc]], np.int32), np.array([s], np.float32), b,
+                            np.array([c], np.float32))
+        sc = f32_rne(F(s) * F(b))
+        exp = f32_rne(F(f32_rne(acc * F(sc))) + F(c))
+        assert y[0, 0] == exp, acc_s
+        assert f32_rne(acc * F(sc) + F(c)) != exp
+    rng = np.random.default_rng(43)
+    acc = rng.integers(-30000, 30000, size=(5, 40)).astype(np.int32)
+    sv = rng.random(5, dtype=np.float32) + np.float32(0.01)
+    y0 = oracle.epilogue(acc, sv, np.float32(0.02))
+    y1 = oracle.epilogue(acc, sv, np.float32(0.02), np.zeros(40, np.float32))
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    bias = rng.standard_normal(40, dtype=np.float32)
+    y2 = oracle.epilogue(acc, sv, np.float32(0.02), bias)
+    assert np.array_equal(y2, (y0 + bias[None, :]).astype(np.float32))
+
