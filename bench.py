@@ -10,10 +10,14 @@ Prints ONE JSON line.  Workloads (default: decode_stack):
                 reads its own copy of the weights, the copies span >= 2 GiB,
                 and a 1 GiB write evicts the caches before each timed region,
                 so weights stream from HBM (cold).  value = packed-weight GB/s.
-                The same line also carries the prefill GEMM (4096 x 2560 ->
-                6912 and 4096 x 6912 -> 2560, int8 TOP/s) and the streaming
-                decode GEMV at M = 1, 2560 -> 6912 (weight GB/s), each with
-                its own roofline, as "prefill_gemm" and "stream_m1".
+                The same line also carries, each with its own roofline: the
+                prefill GEMM (4096 x 2560 -> 6912 and 4096 x 6912 -> 2560,
+                int8 TOP/s) as "prefill_gemm"; the streaming decode GEMV at
+                M = 1, 2560 -> 6912 (weight GB/s) as "stream_m1"; the
+                requantization of a 6912 x 2560 fp32 master straight to five
+                trits per byte as "requant_pack5"; and one decode step of
+                causal attention over a 4096-position K/V cache (20 heads x
+                128) as "attention_decode".
   sweep         decode GEMV at M in {1,4,16,64} x the three 2B-class shapes
                 (cold, cycling weight copies); value = weight GB/s over all
                 12 points.
@@ -330,6 +334,8 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["requant_pack5"] = measure_requant_pack5(torch, ug, inputs)
         torch.cuda.empty_cache()
+        out["attention_decode"] = measure_attention_decode(torch, ug)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle
         passes, secs = cpu_decode_stack(oracle, inputs, args.cpu_seconds)
@@ -411,6 +417,45 @@ def measure_requant_pack5(torch, ug, inputs):
     log("requant pack5", out)
     del masters
     return out
+
+
+def measure_attention_decode(torch, ug, T=4096, H=20, dh=128):
+    """One decode step of causal attention over a K/V cache of T positions
+    with 2B-class heads (d_model 2560 = 20 x 128): the new token's query
+    against every cached key and value (fp32).  Calls cycle through >= 2 GiB
+    of cache copies (each read cold); the median over STAT_LAUNCHES calls."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    d = H * dh
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    q = torch.randn((1, d), device=dev, generator=g)
+    kv_bytes = 2 * T * d * 4
+    n_copies = -(-COLD_BYTES // kv_bytes)
+    caches = [(torch.randn((T, d), device=dev, generator=g),
+               torch.randn((T, d), device=dev, generator=g)) for _ in range(n_copies)]
+    out = torch.empty((1, d), device=dev)
+    ws = torch.empty(ug.ug_attention_workspace_size(1, T - 1, H, dh), dtype=torch.uint8,
+                     device=dev)
+    for i in range(2):
+        ug.ug_attention_cached(q, caches[i][0], caches[i][1], T - 1, H, out=out, ws=ws)
+    med, p10, p90 = launch_stats(
+        torch, lambda i: ug.ug_attention_cached(q, caches[(i + 2) % n_copies][0],
+                                                caches[(i + 2) % n_copies][1], T - 1, H,
+                                                out=out, ws=ws), stream)
+    alg = kv_bytes + 4 * d + 4 * d  # the cache, the query, the context
+    achieved = alg / (med * 1e-6) / 1e9
+    res = dict(value=achieved, unit="GB/s",
+               point="M=1 at position %d, %d heads x %d, fp32 K/V cache; %d cache copies "
+                     "(%.2f GiB) cycled" % (T - 1, H, dh, n_copies,
+                                           n_copies * kv_bytes / 2 ** 30),
+               median_call_us=med, p10_call_us=p10, p90_call_us=p90,
+               roofline=dict(bound="hbm", kernel="attn_partial<128> + attn_combine<128>",
+                             achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=achieved / HBM_PEAK_GBS, traffic=None, median_launch_us=med,
+                             alg_bytes_per_launch=alg))
+    log("attention decode", res)
+    del caches
+    return res
 
 
 def measure_stream_m1(torch, ug, inputs, M=1, si=0):
@@ -813,7 +858,7 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
-    for k in ("prefill_gemm", "stream_m1", "requant_pack5", "cpu_baseline"):
+    for k in ("prefill_gemm", "stream_m1", "requant_pack5", "attention_decode", "cpu_baseline"):
         if k in res:
             line[k] = res[k]
     print(json.dumps(line), flush=True)

@@ -39,6 +39,10 @@ inline bool pitch_ok(int64_t ld, int64_t cols, int64_t mult) {
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+bool attention_shape_ok(int64_t M, int64_t pos0, int64_t H, int64_t dh) {
+  return M >= 1 && pos0 >= 0 && H >= 1 && (dh == 32 || dh == 64 || dh == 128 || dh == 256);
+}
+
 // The block table of a plan at `plan`: the first 128-byte boundary after the
 // descriptors (plan is 16-byte aligned, so at most 112 bytes of padding).
 size_t plan_table_offset(const void *plan, int32_t count) {
@@ -355,6 +359,32 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
   if (tile < -1 || tile > 1 || k_splits == 0 || k_splits < -1) return UG_ERR_INVALID_ARG;
   return gemm_common(xq, ldx, s, w, wfmt, ldw, beta, bias, M, N, K, acc, ldacc, y, ldy, ws,
                      ws_bytes, tile, k_splits, stream);
+}
+
+size_t ug_attention_workspace_size(int64_t M, int64_t pos0, int64_t H, int64_t dh) {
+  if (!attention_shape_ok(M, pos0, H, dh) || pos0 + M > (INT64_C(1) << 24) || H > 65535 ||
+      M > 65535)
+    return 0;
+  return ug::attention_workspace_bytes(M, pos0, H, dh);
+}
+
+ug_status ug_attention_cached(const float *q, int64_t ldq, const float *kc, int64_t ldk,
+                              const float *vc, int64_t ldv, int64_t M, int64_t pos0, int64_t H,
+                              int64_t dh, float *out, int64_t ldo, void *ws, size_t ws_bytes,
+                              void *stream) {
+  if (!ptr_ok(q) || !ptr_ok(kc) || !ptr_ok(vc) || !ptr_ok(out)) return UG_ERR_INVALID_ARG;
+  if (!attention_shape_ok(M, pos0, H, dh)) return UG_ERR_INVALID_ARG;
+  if (H > INT64_MAX / dh) return UG_ERR_INVALID_ARG;
+  const int64_t HD = H * dh;
+  if (!pitch_ok(ldq, HD, 4) || !pitch_ok(ldk, HD, 4) || !pitch_ok(ldv, HD, 4) ||
+      !pitch_ok(ldo, HD, 4))
+    return UG_ERR_INVALID_ARG;
+  // grid dimensions and 32-bit positions
+  if (pos0 + M > (INT64_C(1) << 24) || H > 65535 || M > 65535) return UG_ERR_UNSUPPORTED;
+  const size_t need = ug::attention_workspace_bytes(M, pos0, H, dh);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return UG_ERR_WORKSPACE;
+  return hip_status(ug::launch_attention(q, ldq, kc, ldk, vc, ldv, M, pos0, H, dh, out, ldo,
+                                         static_cast<float *>(ws), as_stream(stream)));
 }
 
 }  // extern "C"

@@ -139,6 +139,12 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const float *bias,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,
                        int64_t ldacc, float *y, int64_t ldy, hipStream_t st);
+// Causal attention over a key/value cache: partials per 256-key chunk in
+// `part` (attention_workspace_bytes), then one combine per (row, head).
+size_t attention_workspace_bytes(int64_t M, int64_t pos0, int64_t H, int64_t dh);
+hipError_t launch_attention(const float *q, int64_t ldq, const float *kc, int64_t ldk,
+                            const float *vc, int64_t ldv, int64_t M, int64_t pos0, int64_t H,
+                            int64_t dh, float *out, int64_t ldo, float *part, hipStream_t st);
 // Bytes of the GEMM's K-split area (tile counters at offset 0, then one
 // partial tile per block); the same size and layout for every shape.
 size_t gemm_split_area_bytes();

@@ -58,6 +58,9 @@ SIGNATURES = {
                                  _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "ug_bitlinear_gemm_tiled": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64,
                                        _i64, _vp, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp]),
+    "ug_attention_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
+    "ug_attention_cached": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
+                                   _i64, _vp, _sz, _vp]),
 }
 
 UG_GEMM_COUNTER_BYTES = 2048
@@ -386,3 +389,26 @@ def ug_bitlinear_gemv_grouped(plan, stream=None):
     """One launch of every problem of a GemvPlan."""
     _check(lib().ug_bitlinear_gemv_grouped(_p(plan.buf), ctypes.byref(plan.info),
                                            _stream(stream)), "ug_bitlinear_gemv_grouped")
+
+
+def ug_attention_workspace_size(M, pos0, H, dh):
+    return lib().ug_attention_workspace_size(M, pos0, H, dh)
+
+
+def ug_attention_cached(q, kc, vc, pos0, H, out=None, ws=None, stream=None):
+    """Causal attention of q fp32 [M, H*dh] (row m at position pos0 + m)
+    over the cache rows kc, vc fp32 [>= pos0 + M, H*dh] -> out fp32
+    [M, H*dh]."""
+    M, HD = q.shape
+    dh = HD // H
+    if out is None:
+        out = empty_pitched(M, HD, torch.float32, q.device)
+    need = ug_attention_workspace_size(M, pos0, H, dh)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().ug_attention_cached(_p(q), _ld(q), _p(kc), _ld(kc), _p(vc), _ld(vc), M, pos0, H,
+                                     dh, _p(out), _ld(out), _p(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)),
+           "ug_attention_cached")
+    return out
+

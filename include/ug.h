@@ -351,6 +351,37 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                                   int64_t ldy, void *ws, size_t ws_bytes,
                                   int32_t tile, int32_t k_splits, void *stream);
 
+/* Bytes of workspace ug_attention_cached needs:
+ * 4 * M * H * ceil((pos0 + M) / 256) * (dh + 4).  0 for invalid shapes. */
+size_t ug_attention_workspace_size(int64_t M, int64_t pos0, int64_t H,
+                                   int64_t dh);
+
+/*
+ * Causal multi-head attention of M query rows over a key/value cache
+ * ("ultragraph ... part 2", "attention, as graph ops": per head,
+ * scores = Q K^T / sqrt(d_h), a causal mask, A = softmax(scores + mask),
+ * ctx = A V; README "A whole ternary GPT": decoding keeps the earlier
+ * positions' K and V rows in a cache).  Query row m is at position
+ * p = pos0 + m and attends to cache rows 0 .. p; head h uses columns
+ * h*dh .. h*dh + dh - 1 of q, kc, vc and out.  A decode step is M = 1 with
+ * pos0 = the new token's position (its K and V rows already in the cache);
+ * a full forward over T tokens is M = T, pos0 = 0.
+ *  q   fp32 [M][ldq];  kc, vc fp32 [pos0 + M][ldk / ldv] (rows past the
+ *      last query's position are not read);  out fp32 [M][ldo];
+ *  dh in {32, 64, 128, 256}; every pitch >= H*dh, a multiple of 4;
+ *  ws: device workspace of ws_bytes >= ug_attention_workspace_size.
+ * Arithmetic: fp32 with one fixed reduction order for every row whatever
+ * M is, so row m equals, bit for bit, the call with M = 1 at position
+ * pos0 + m (cached decoding reproduces the full forward); exp is the
+ * device's expf.  UG_ERR_UNSUPPORTED if pos0 + M > 2^24, H > 65535 or
+ * M > 65535.  Inputs must be finite.
+ */
+ug_status ug_attention_cached(const float *q, int64_t ldq, const float *kc,
+                              int64_t ldk, const float *vc, int64_t ldv,
+                              int64_t M, int64_t pos0, int64_t H, int64_t dh,
+                              float *out, int64_t ldo, void *ws,
+                              size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

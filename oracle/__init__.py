@@ -91,6 +91,8 @@ def _open(path):
         "ugref_matmul_i32_pairs": (None, [_i8p, _i64, _i8p, _i64, _i64, _i64p, _i64p, _i64,
                                           _i32p]),
         "ugref_epilogue": (None, [_i32p, _i64, _f32p, _f32, _f32p, _i64, _i64, _f32p, _i64]),
+        "ugref_attention": (None, [_f32p, _i64, _f32p, _i64, _f32p, _i64, _i64, _i64, _i64,
+                                   _i64, _f32p, _i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -272,6 +274,27 @@ def bitlinear(x, W, eps=1e-5, bias=None):
     acc = matmul_i32(xq, wq)
     y = epilogue(acc, s, beta, bias)
     return dict(xq=xq, s=s, wq=wq, beta=beta, acc=acc, y=y)
+
+
+def attention(q, kc, vc, pos0, H):
+    """Causal attention over a key/value cache ("attention, as graph ops":
+    softmax(Q K^T / sqrt(d_h) + mask) V per head; README "A whole ternary
+    GPT": cached decoding).  q fp32 [M, H*dh] (row m at position pos0 + m),
+    kc, vc fp32 [>= pos0 + M, H*dh].  Double precision inside, fp32 out
+    [M, H*dh]."""
+    q = _c2d(q, np.float32)
+    kc = _c2d(kc, np.float32)
+    vc = _c2d(vc, np.float32)
+    M, HD = q.shape
+    if HD % H or kc.shape[1] != HD or vc.shape[1] != HD:
+        raise ValueError("head layout mismatch")
+    if kc.shape[0] < pos0 + M or vc.shape[0] < pos0 + M:
+        raise ValueError("cache shorter than the last query position")
+    out = np.empty((M, HD), np.float32)
+    _load().ugref_attention(_ptr(q, ctypes.c_float), HD, _ptr(kc, ctypes.c_float), HD,
+                            _ptr(vc, ctypes.c_float), HD, M, pos0, H, HD // H,
+                            _ptr(out, ctypes.c_float), HD)
+    return out
 
 
 def num_threads():

@@ -370,3 +370,53 @@ void ugref_epilogue(const int32_t *acc, int64_t ldacc, const float *s,
         }
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* Causal attention over a key/value cache                             */
+/* ------------------------------------------------------------------ */
+
+/* "ultragraph - when the graph is the 1-bit LLM, part 2", section
+ * "attention, as graph ops": per head h (columns h*dh .. h*dh+dh-1 of
+ * q, K, V), scores = Q K^T / sqrt(d_h), a causal mask that removes keys
+ * after the query's position, A = softmax(scores + mask), ctx = A V.
+ * "ultragraph-1bit 0.12.0" README, "A whole ternary GPT": decoding keeps
+ * every earlier position's K and V rows in a cache.
+ *
+ * Query row m sits at position p = pos0 + m and sees cache rows 0..p.
+ * Computed in double precision straight from the definition (the exact
+ * softmax up to double rounding), rounded to fp32 once at the end. */
+void ugref_attention(const float *q, int64_t ldq, const float *kc, int64_t ldk,
+                     const float *vc, int64_t ldv, int64_t M, int64_t pos0,
+                     int64_t H, int64_t dh, float *out, int64_t ldo)
+{
+#pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t n = pos0 + m + 1; /* keys 0 .. pos0 + m */
+            double *sc = (double *)malloc((size_t)n * sizeof(double));
+            const float *qr = q + m * ldq + h * dh;
+            double root = sqrt((double)dh);
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < n; ++j) {
+                const float *kr = kc + j * ldk + h * dh;
+                double dot = 0.0;
+                for (int64_t d = 0; d < dh; ++d)
+                    dot += (double)qr[d] * (double)kr[d];
+                sc[j] = dot / root;
+                if (sc[j] > mx)
+                    mx = sc[j];
+            }
+            double sum = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                sc[j] = exp(sc[j] - mx);
+                sum += sc[j];
+            }
+            for (int64_t d = 0; d < dh; ++d) {
+                double o = 0.0;
+                for (int64_t j = 0; j < n; ++j)
+                    o += sc[j] * (double)vc[j * ldv + h * dh + d];
+                out[m * ldo + h * dh + d] = (float)(o / sum);
+            }
+            free(sc);
+        }
+}

@@ -281,3 +281,29 @@ def test_grouped_plan_rejects_fused_with_chunked(ug):
         st = L.ug_gemv_plan_init(ctypes.cast(one, ctypes.c_void_p), 1, ctypes.c_void_p(0xA00000),
                                  L.ug_gemv_plan_size(1), ctypes.byref(info))
         assert st == ug.UG_ERR_HIP
+
+
+def test_attention_rejects_and_sizes(ug):
+    L = ug.lib()
+    E = ug.UG_ERR_INVALID_ARG
+    # workspace: 4 * M * H * ceil((pos0 + M) / 256) * (dh + 4)
+    assert L.ug_attention_workspace_size(1, 4095, 20, 128) == 4 * 1 * 20 * 16 * 132
+    assert L.ug_attention_workspace_size(300, 0, 3, 64) == 4 * 300 * 3 * 2 * 68
+    assert L.ug_attention_workspace_size(1, 0, 1, 48) == 0        # d_h not supported
+    need = L.ug_attention_workspace_size(1, 99, 2, 64)
+
+    def call(q=A, ldq=128, M=1, pos0=99, H=2, dh=64, ws=A4, ws_bytes=need, ldk=128):
+        return L.ug_attention_cached(q, ldq, A2, ldk, A3, 128, M, pos0, H, dh,
+                                     ctypes.c_void_p(0x500000), 128, ws, ws_bytes, S)
+
+    assert call(q=NULL) == E
+    assert call(q=MIS) == E
+    assert call(dh=48) == E
+    assert call(H=0) == E
+    assert call(M=0) == E
+    assert call(pos0=-1) == E
+    assert call(ldq=100) == E            # pitch < H * dh
+    assert call(ldk=130) == E            # pitch % 4
+    assert call(ws=NULL) == ug.UG_ERR_WORKSPACE
+    assert call(ws_bytes=need - 4) == ug.UG_ERR_WORKSPACE
+    assert call(pos0=2 ** 24) == ug.UG_ERR_UNSUPPORTED

@@ -17,6 +17,7 @@ import pytest
 import oracle
 from oracle import build as obuild
 
+import test_oracle_attention as attn_pins
 import test_oracle_pins as pins
 
 SRC = obuild.SRC
@@ -127,6 +128,29 @@ MUTANTS = {
           "            float v = (float)acc[m * ldacc + n] * scale;\n"
           "            if (b)\n                v = ((float)acc[m * ldacc + n] + b[n]) * scale;")],
         ["test_epilogue_bias_cases"]),
+    # --- causal attention over the K/V cache ("attention, as graph ops") ----
+    "attention_no_root_dh_scale": (
+        [("                sc[j] = dot / root;", "                sc[j] = dot;")],
+        ["test_attention_two_keys_closed_form_with_root_dh_scale"]),
+    "attention_scale_by_dh": (
+        [("    double root = sqrt((double)dh);", "    double root = (double)dh;")],
+        ["test_attention_two_keys_closed_form_with_root_dh_scale"]),
+    "attention_mask_drops_own_position": (
+        [("            int64_t n = pos0 + m + 1; /* keys 0 .. pos0 + m */",
+          "            int64_t n = pos0 + m; /* keys 0 .. pos0 + m */")],
+        ["test_attention_single_key_returns_its_value", "test_attention_is_causal"]),
+    "attention_mask_sees_next_position": (
+        [("            int64_t n = pos0 + m + 1; /* keys 0 .. pos0 + m */",
+          "            int64_t n = pos0 + m + 2; /* keys 0 .. pos0 + m */")],
+        ["test_attention_single_key_returns_its_value", "test_attention_is_causal"]),
+    "attention_value_columns_of_head_0": (
+        [("                    o += sc[j] * (double)vc[j * ldv + h * dh + d];",
+          "                    o += sc[j] * (double)vc[j * ldv + d];")],
+        ["test_attention_heads_are_independent"]),
+    "attention_unnormalized": (
+        [("                out[m * ldo + h * dh + d] = (float)(o / sum);",
+          "                out[m * ldo + h * dh + d] = (float)o;")],
+        ["test_attention_equal_keys_average_the_values"]),
     # --- five trits per byte (README "A whole ternary GPT") -----------------
     "pack_digits_reversed": (
         [("                int pow3 = 1;\n                for (int j = 0; j < 5; ++j) {",
@@ -146,6 +170,10 @@ MUTANTS = {
           "                sum += (int64_t)xq[m * ldx + k] * (int64_t)wq[n * ldw + k];")],
         ["test_matmul_brute_force_tiny", "test_matmul_special_cases"]),
 }
+
+
+def _pin(name):
+    return getattr(pins, name, None) or getattr(attn_pins, name)
 
 
 def _compile(text, out):
@@ -174,7 +202,7 @@ def test_pins_catch_mutant(name, tmp_path):
     with oracle.use_library(lib):
         for pin in catchers:
             try:
-                getattr(pins, pin)()
+                _pin(pin)()
             except AssertionError:
                 failed.append(pin)
     assert failed, "no pin caught the planted slip %s" % name
@@ -189,4 +217,4 @@ def test_unmutated_copy_passes_the_same_pins(tmp_path):
     used = sorted({p for _, cs in MUTANTS.values() for p in cs})
     with oracle.use_library(lib):
         for pin in used:
-            getattr(pins, pin)()
+            _pin(pin)()
