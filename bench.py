@@ -17,7 +17,8 @@ Prints ONE JSON line.  Workloads (default: decode_stack):
                 requantization of a 6912 x 2560 fp32 master straight to five
                 trits per byte as "requant_pack5"; and one decode step of
                 causal attention over a 4096-position K/V cache (20 heads x
-                128) as "attention_decode".
+                128) as "attention_decode"; top-100-of-4096 sampling as
+                "sampler".
   sweep         decode GEMV at M in {1,4,16,64} x the three 2B-class shapes
                 (cold, cycling weight copies); value = weight GB/s over all
                 12 points.
@@ -336,6 +337,8 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["attention_decode"] = measure_attention_decode(torch, ug)
         torch.cuda.empty_cache()
+        out["sampler"] = measure_sampler(torch, ug)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle
         passes, secs = cpu_decode_stack(oracle, inputs, args.cpu_seconds)
@@ -455,6 +458,44 @@ def measure_attention_decode(torch, ug, T=4096, H=20, dh=128):
                              alg_bytes_per_launch=alg))
     log("attention decode", res)
     del caches
+    return res
+
+
+def measure_sampler(torch, ug, V=4096, k=100, B=4096):
+    """Top-k sampling of the next token, 100 of 4096 logits ("a 1-bit llm,
+    from scratch"): one row (the latency of a batch-1 decode step) and a
+    batch of B rows (whole-chip throughput, bounded by reading the logits).
+    Batches cycle through >= 2 GiB of logit copies; medians over
+    STAT_LAUNCHES calls."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    n_copies = max(2, -(-COLD_BYTES // (B * V * 4)))
+    rows = [torch.randn((B, V), device=dev, generator=g) * 3.0 for _ in range(n_copies)]
+    u = torch.rand(B, device=dev, generator=g)
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
+    for i in range(2):
+        ug.ug_sample_topk(rows[i], k, 0.8, u, tokens=tok)
+    one_med, one_p10, one_p90 = launch_stats(
+        torch, lambda i: ug.ug_sample_topk(rows[i % n_copies][:1], k, 0.8, u[:1], tokens=tok[:1]),
+        stream)
+    med, p10, p90 = launch_stats(
+        torch, lambda i: ug.ug_sample_topk(rows[(i + 1) % n_copies], k, 0.8, u, tokens=tok),
+        stream)
+    alg = B * V * 4 + B * 4 + B * 4  # the logits, the draws, the tokens
+    achieved = alg / (med * 1e-6) / 1e9
+    res = dict(value=achieved, unit="GB/s",
+               point="top-%d of %d logits, temperature 0.8: batch of %d rows (%d copies, "
+                     "%.2f GiB, cycled) and a single row" % (k, V, B, n_copies,
+                                                            n_copies * B * V * 4 / 2 ** 30),
+               single_row_us_median=one_med, single_row_us_p10=one_p10,
+               single_row_us_p90=one_p90, batch_us_median=med, batch_us_p10=p10,
+               batch_us_p90=p90,
+               roofline=dict(bound="hbm", kernel="topk_sample<true>", achieved=achieved,
+                             peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
+                             traffic=None, median_launch_us=med, alg_bytes_per_launch=alg))
+    log("sampler", res)
+    del rows
     return res
 
 
@@ -858,7 +899,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
-    for k in ("prefill_gemm", "stream_m1", "requant_pack5", "attention_decode", "cpu_baseline"):
+    for k in ("prefill_gemm", "stream_m1", "requant_pack5", "attention_decode", "sampler",
+              "cpu_baseline"):
         if k in res:
             line[k] = res[k]
     print(json.dumps(line), flush=True)

@@ -361,6 +361,25 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                      ws_bytes, tile, k_splits, stream);
 }
 
+ug_status ug_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V, int64_t k,
+                         float temperature, const float *u, int32_t *tokens, int32_t *topk_index,
+                         int64_t ldi, float *topk_logit, int64_t ldl, float *topk_prob,
+                         int64_t ldp, void *stream) {
+  if (!ptr_ok(logits) || !f32_ok(u) || !counter_ok(tokens) || tokens == nullptr)
+    return UG_ERR_INVALID_ARG;
+  if (!counter_ok(topk_index) || !counter_ok(topk_logit) || !counter_ok(topk_prob))
+    return UG_ERR_INVALID_ARG;
+  if (B < 1 || V < 1 || k < 1 || k > V || k > UG_SAMPLE_MAX_K) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ld, V, 4)) return UG_ERR_INVALID_ARG;
+  if ((topk_index && ldi < k) || (topk_logit && ldl < k) || (topk_prob && ldp < k))
+    return UG_ERR_INVALID_ARG;
+  if (!std::isfinite(temperature) || !(temperature > 0.0f)) return UG_ERR_INVALID_ARG;
+  if (B > INT32_MAX || V > INT32_MAX - 256) return UG_ERR_UNSUPPORTED;
+  return hip_status(ug::launch_sample_topk(logits, ld, B, V, k, temperature, u, tokens,
+                                           topk_index, ldi, topk_logit, ldl, topk_prob, ldp,
+                                           as_stream(stream)));
+}
+
 size_t ug_attention_workspace_size(int64_t M, int64_t pos0, int64_t H, int64_t dh) {
   if (!attention_shape_ok(M, pos0, H, dh) || pos0 + M > (INT64_C(1) << 24) || H > 65535 ||
       M > 65535)

@@ -1,0 +1,196 @@
+// Top-k sampling of the next token (gfx950).
+//
+// "a 1-bit llm, from scratch", section "the interesting bit": the sampler
+// picks the next token from the k largest of 4096 logits, and finding them
+// with a size-k heap instead of sorting every logit halved the time per
+// token.  "ultragraph-1bit 0.12.0" README, "A whole ternary GPT": generate()
+// takes a temperature and top_k.
+//
+// One 256-thread block per row, nothing sorted but the k kept logits:
+//   1. every logit becomes an order-preserving 32-bit key (larger logit,
+//      larger key; -0 and +0 the same);
+//   2. four passes of an 8-bit radix select (an LDS histogram of the
+//      digit among the keys that match the digits chosen so far, then a
+//      suffix scan) find the k-th largest key t and how many of the kept
+//      keys equal t;
+//   3. a block scan places every key above t, then the lowest-index keys
+//      equal to t, in LDS as (key, ~index) pairs;
+//   4. a 256-wide bitonic sort orders them (larger logit first, equal
+//      logits by lower index);
+//   5. rank r gets the weight e_r = expf(fl(fl(l_r - l_1) / T)); an
+//      inclusive fp32 scan in one fixed order gives C_r; the token is rank
+//      min(#{r : C_r <= fl(u * C_k)}, k - 1).
+// Rows of at most 4096 logits stay in registers (16 per thread) between the
+// passes; longer rows are read again from memory (L2) for each pass.
+#include "ug_internal.h"
+
+namespace ug {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRegPer = 16;  // logits per thread held in registers
+
+__device__ inline uint32_t rank_key(float x) {
+  const uint32_t b = __float_as_uint(x == 0.0f ? 0.0f : x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ inline float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Inclusive sum over the block's 256 threads in thread order (a scan within
+// each wave, then the waves' totals in order); *total gets the block sum.
+template <typename T>
+__device__ inline T block_scan(T v, T *wsum, T *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T y = __shfl_up(v, off, 64);
+    if (lane >= off) v = v + y;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  T pre = T(0);
+  for (int w = 0; w < wave; ++w) pre = pre + wsum[w];
+  *total = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  __syncthreads();
+  return wave ? pre + v : v;
+}
+
+template <bool REG>
+__global__ __launch_bounds__(kThreads) void topk_sample(
+    const float *__restrict__ logits, int64_t ld, int V, int k, float temp,
+    const float *__restrict__ u, int32_t *__restrict__ tok, int32_t *__restrict__ idx_out,
+    int64_t ldi, float *__restrict__ val_out, int64_t ldv, float *__restrict__ prob_out,
+    int64_t ldp) {
+  __shared__ int hist[256];
+  __shared__ int iws[4];
+  __shared__ float fws[4];
+  __shared__ unsigned long long sel[kThreads];
+  __shared__ uint32_t s_digit;
+  __shared__ int s_above;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float *row = logits + (int64_t)b * ld;
+  const int per = (V + kThreads - 1) / kThreads;  // this thread: [tid * per, tid * per + per)
+  const int i0 = tid * per;
+
+  uint32_t kr[REG ? kRegPer : 1];
+  if (REG) {
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      const int i = i0 + j;
+      kr[j] = j < per && i < V ? rank_key(row[i]) : 0u;
+    }
+  }
+  // f(i, key) for every logit of this thread's span, in index order
+  auto each = [&](auto &&f) __attribute__((always_inline)) {
+    if (REG) {
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j)
+        if (j < per && i0 + j < V) f(i0 + j, kr[j]);
+    } else {
+      const int e = min(i0 + per, V);
+      for (int i = i0; i < e; ++i) f(i, rank_key(row[i]));
+    }
+  };
+
+  // radix select of the k-th largest key
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;  // keys still to keep among those matching the prefix
+  for (int sh = 24; sh >= 0; sh -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    each([&](int, uint32_t key) __attribute__((always_inline)) {
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & 255], 1);
+    });
+    __syncthreads();
+    const int h = hist[255 - tid];  // digits from the top
+    int tot;
+    const int ge = block_scan(h, iws, &tot);  // keys whose digit is >= 255 - tid
+    if (ge >= need && ge - h < need) {
+      s_digit = (uint32_t)(255 - tid);
+      s_above = ge - h;
+    }
+    __syncthreads();
+    prefix |= s_digit << sh;
+    pmask |= 0xffu << sh;
+    need -= s_above;
+    __syncthreads();
+  }
+  const uint32_t t = prefix;  // the k-th largest key; `need` kept keys equal it
+
+  // compaction: keys above t, then the lowest-index keys equal to t
+  int cg = 0, ce = 0;
+  each([&](int, uint32_t key) __attribute__((always_inline)) {
+    cg += key > t;
+    ce += key == t;
+  });
+  int gtot, etot;
+  int pg = block_scan(cg, iws, &gtot) - cg;
+  int pe = block_scan(ce, iws, &etot) - ce;
+  sel[tid] = 0ull;  // padding sorts last
+  __syncthreads();
+  each([&](int i, uint32_t key) __attribute__((always_inline)) {
+    const unsigned long long c = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)i;
+    if (key > t) {
+      sel[pg++] = c;
+    } else if (key == t) {
+      if (pe < need) sel[gtot + pe] = c;
+      ++pe;
+    }
+  });
+  __syncthreads();
+
+  // bitonic sort of the 256 slots, largest first
+  for (int size = 2; size <= kThreads; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int p = tid ^ stride;
+      if (p > tid) {
+        const unsigned long long a = sel[tid], c = sel[p];
+        const bool desc = (tid & size) == 0;
+        if (desc ? a < c : a > c) {
+          sel[tid] = c;
+          sel[p] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // weights, their running sum and the draw
+  const unsigned long long mine = sel[tid];
+  const float l1 = key_logit((uint32_t)(sel[0] >> 32));
+  const float lr = key_logit((uint32_t)(mine >> 32));
+  const float e = tid < k ? expf((lr - l1) / temp) : 0.0f;
+  float total;
+  const float C = block_scan(e, fws, &total);
+  const float thr = u[b] * total;
+  int below;
+  block_scan((int)(tid < k && C <= thr), iws, &below);
+  const int pick = min(below, k - 1);
+  if (tid == pick) tok[b] = (int32_t)~(uint32_t)mine;
+  if (tid < k) {
+    const int32_t ix = (int32_t)~(uint32_t)mine;
+    if (idx_out) idx_out[(int64_t)b * ldi + tid] = ix;
+    if (val_out) val_out[(int64_t)b * ldv + tid] = lr;
+    if (prob_out) prob_out[(int64_t)b * ldp + tid] = e / total;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V, int64_t k,
+                              float temp, const float *u, int32_t *tok, int32_t *idx_out,
+                              int64_t ldi, float *val_out, int64_t ldv, float *prob_out,
+                              int64_t ldp, hipStream_t st) {
+  if (V <= kThreads * kRegPer)
+    hipLaunchKernelGGL(topk_sample<true>, dim3((unsigned)B), dim3(kThreads), 0, st, logits, ld,
+                       (int)V, (int)k, temp, u, tok, idx_out, ldi, val_out, ldv, prob_out, ldp);
+  else
+    hipLaunchKernelGGL(topk_sample<false>, dim3((unsigned)B), dim3(kThreads), 0, st, logits, ld,
+                       (int)V, (int)k, temp, u, tok, idx_out, ldi, val_out, ldv, prob_out, ldp);
+  return hipGetLastError();
+}
+
+}  // namespace ug

@@ -139,6 +139,11 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const float *bias,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,
                        int64_t ldacc, float *y, int64_t ldy, hipStream_t st);
+// Top-k sampling: one block per row of logits.
+hipError_t launch_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V, int64_t k,
+                              float temp, const float *u, int32_t *tok, int32_t *idx_out,
+                              int64_t ldi, float *val_out, int64_t ldv, float *prob_out,
+                              int64_t ldp, hipStream_t st);
 // Causal attention over a key/value cache: partials per 256-key chunk in
 // `part` (attention_workspace_bytes), then one combine per (row, head).
 size_t attention_workspace_bytes(int64_t M, int64_t pos0, int64_t H, int64_t dh);

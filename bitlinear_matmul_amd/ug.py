@@ -58,6 +58,8 @@ SIGNATURES = {
                                  _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "ug_bitlinear_gemm_tiled": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64,
                                        _i64, _vp, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp]),
+    "ug_sample_topk": (_i32, [_vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _i64, _vp, _i64,
+                              _vp, _i64, _vp]),
     "ug_attention_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
     "ug_attention_cached": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
                                    _i64, _vp, _sz, _vp]),
@@ -411,4 +413,25 @@ def ug_attention_cached(q, kc, vc, pos0, H, out=None, ws=None, stream=None):
                                      ws.numel() * ws.element_size(), _stream(stream)),
            "ug_attention_cached")
     return out
+
+
+def ug_sample_topk(logits, k, temperature, u, tokens=None, want_topk=False, stream=None):
+    """Top-k sampling: logits fp32 [B, V], u fp32 [B] uniform draws ->
+    tokens int32 [B] (and, with want_topk, the kept indices, logits and
+    probabilities [B, k] in rank order)."""
+    B, V = logits.shape
+    dev = logits.device
+    if tokens is None:
+        tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    idx = val = prob = None
+    if want_topk:
+        idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+        val = torch.empty((B, k), dtype=torch.float32, device=dev)
+        prob = torch.empty((B, k), dtype=torch.float32, device=dev)
+    _check(lib().ug_sample_topk(_p(logits), _ld(logits), B, V, k, temperature, _p(u), _p(tokens),
+                                _p(idx), k if idx is not None else 0, _p(val),
+                                k if val is not None else 0, _p(prob),
+                                k if prob is not None else 0, _stream(stream)),
+           "ug_sample_topk")
+    return (tokens, idx, val, prob) if want_topk else tokens
 

@@ -351,6 +351,35 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                                   int64_t ldy, void *ws, size_t ws_bytes,
                                   int32_t tile, int32_t k_splits, void *stream);
 
+/* Largest k of ug_sample_topk. */
+#define UG_SAMPLE_MAX_K 256
+
+/*
+ * Top-k sampling of the next token, one row of logits per sequence ("a
+ * 1-bit llm, from scratch", "the interesting bit": the next token comes from
+ * the k largest logits, found without sorting the vocabulary; README "A
+ * whole ternary GPT": generate() with temperature and top_k).  Per row b:
+ *   rank the V logits, larger first, equal values (-0 == +0) by lower index;
+ *   keep ranks 1..k; weight rank r by e_r = expf(fl(fl(l_r - l_1) / T));
+ *   C_r = e_1 + ... + e_r (fp32, one fixed order);
+ *   tokens[b] = the index of rank min(#{r : C_r <= fl(u[b] * C_k)}, k - 1)
+ *   (the first rank whose running weight exceeds u[b] times the total).
+ *  logits fp32 [B][ld] (16-byte aligned, ld >= V, ld % 4 == 0);
+ *  u fp32 [B] uniform draws in [0, 1), supplied by the caller;
+ *  tokens int32 [B] out;  optional outputs (NULL: not written), row pitch
+ *  >= k: topk_index int32 [B][ldi] (the kept indices in rank order),
+ *  topk_logit fp32 [B][ldl] (their logits), topk_prob fp32 [B][ldp]
+ *  (e_r / C_k).  1 <= k <= min(V, UG_SAMPLE_MAX_K); T > 0 and finite.
+ * Logits must be finite.  Which indices are kept, and their order, is exact
+ * (comparisons only); the draw depends on expf and fp32 sums, so a u within
+ * a few ulps of a boundary C_r / C_k may land on either neighbouring rank.
+ */
+ug_status ug_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V,
+                         int64_t k, float temperature, const float *u,
+                         int32_t *tokens, int32_t *topk_index, int64_t ldi,
+                         float *topk_logit, int64_t ldl, float *topk_prob,
+                         int64_t ldp, void *stream);
+
 /* Bytes of workspace ug_attention_cached needs:
  * 4 * M * H * ceil((pos0 + M) / 256) * (dh + 4).  0 for invalid shapes. */
 size_t ug_attention_workspace_size(int64_t M, int64_t pos0, int64_t H,

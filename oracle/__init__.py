@@ -91,6 +91,8 @@ def _open(path):
         "ugref_matmul_i32_pairs": (None, [_i8p, _i64, _i8p, _i64, _i64, _i64p, _i64p, _i64,
                                           _i32p]),
         "ugref_epilogue": (None, [_i32p, _i64, _f32p, _f32, _f32p, _i64, _i64, _f32p, _i64]),
+        "ugref_sample_topk": (None, [_f32p, _i64, _i64, _i64, _i64, _f32, _f32p, _i32p, _i32p,
+                                     _f32p, ctypes.POINTER(ctypes.c_double)]),
         "ugref_attention": (None, [_f32p, _i64, _f32p, _i64, _f32p, _i64, _i64, _i64, _i64,
                                    _i64, _f32p, _i64]),
     }
@@ -295,6 +297,30 @@ def attention(q, kc, vc, pos0, H):
                             _ptr(vc, ctypes.c_float), HD, M, pos0, H, HD // H,
                             _ptr(out, ctypes.c_float), HD)
     return out
+
+
+def sample_topk(logits, k, temp, u):
+    """Top-k sampling ("a 1-bit llm, from scratch", "the interesting bit";
+    README "A whole ternary GPT": temperature and top_k): rank by logit,
+    larger first, equal values by lower index; weights exp((l_r - l_1)/T)
+    over ranks 1..k; token = the first rank whose cumulative weight exceeds
+    u times the total.  logits fp32 [B, V], u [B] in [0, 1).  Returns
+    (tokens int32 [B], ranked indices int32 [B, k], their logits fp32
+    [B, k], normalized cumulative weights float64 [B, k])."""
+    logits = _c2d(logits, np.float32)
+    B, V = logits.shape
+    if not 1 <= k <= V:
+        raise ValueError("k out of range")
+    u = np.ascontiguousarray(np.asarray(u, np.float32).reshape(B))
+    tok = np.empty(B, np.int32)
+    idx = np.empty((B, k), np.int32)
+    val = np.empty((B, k), np.float32)
+    cdf = np.empty((B, k), np.float64)
+    _load().ugref_sample_topk(_ptr(logits, ctypes.c_float), V, B, V, k, float(np.float32(temp)),
+                              _ptr(u, ctypes.c_float), _ptr(tok, ctypes.c_int32),
+                              _ptr(idx, ctypes.c_int32), _ptr(val, ctypes.c_float),
+                              cdf.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    return tok, idx, val, cdf
 
 
 def num_threads():

@@ -420,3 +420,67 @@ void ugref_attention(const float *q, int64_t ldq, const float *kc, int64_t ldk,
             free(sc);
         }
 }
+
+/* ------------------------------------------------------------------ */
+/* Top-k sampling                                                      */
+/* ------------------------------------------------------------------ */
+
+/* "a 1-bit llm, from scratch", section "the interesting bit": the next
+ * token is drawn from the k largest logits (the page keeps them in a size-k
+ * min-heap instead of sorting the whole vocabulary); "ultragraph-1bit
+ * 0.12.0" README, "A whole ternary GPT": generate() takes a temperature and
+ * top_k.  Reading: rank the logits by value, larger first, equal values by
+ * lower index; keep ranks 1..k; weight rank r by exp((l_r - l_1) / T) (the
+ * softmax with temperature T over the kept logits); with the caller's
+ * uniform u in [0, 1), the token is the first rank whose cumulative weight
+ * exceeds u times the total.  Double precision for the weights.  The sort is
+ * the C library's qsort on (value, index) pairs. */
+typedef struct {
+    float v;
+    int32_t i;
+} ugref_vi;
+
+static int ugref_rank_cmp(const void *a, const void *b)
+{
+    const ugref_vi *x = (const ugref_vi *)a, *y = (const ugref_vi *)b;
+    if (x->v > y->v)
+        return -1;
+    if (x->v < y->v)
+        return 1;
+    return (x->i > y->i) - (x->i < y->i);
+}
+
+void ugref_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V,
+                       int64_t k, float temp, const float *u, int32_t *tok,
+                       int32_t *idx_out, float *val_out, double *cdf_out)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        ugref_vi *e = (ugref_vi *)malloc((size_t)V * sizeof(ugref_vi));
+        for (int64_t i = 0; i < V; ++i) {
+            e[i].v = logits[b * ld + i];
+            e[i].i = (int32_t)i;
+        }
+        qsort(e, (size_t)V, sizeof(ugref_vi), ugref_rank_cmp);
+        double *c = cdf_out + b * k;
+        double run = 0.0;
+        for (int64_t r = 0; r < k; ++r) {
+            run += exp(((double)e[r].v - (double)e[0].v) / (double)temp);
+            c[r] = run;
+        }
+        for (int64_t r = 0; r < k; ++r)
+            c[r] /= run;
+        int64_t pick = k - 1;
+        for (int64_t r = 0; r < k; ++r)
+            if ((double)u[b] < c[r]) {
+                pick = r;
+                break;
+            }
+        tok[b] = e[pick].i;
+        for (int64_t r = 0; r < k; ++r) {
+            idx_out[b * k + r] = e[r].i;
+            val_out[b * k + r] = e[r].v;
+        }
+        free(e);
+    }
+}

@@ -307,3 +307,23 @@ def test_attention_rejects_and_sizes(ug):
     assert call(ws=NULL) == ug.UG_ERR_WORKSPACE
     assert call(ws_bytes=need - 4) == ug.UG_ERR_WORKSPACE
     assert call(pos0=2 ** 24) == ug.UG_ERR_UNSUPPORTED
+
+
+def test_sample_topk_rejects(ug):
+    L = ug.lib()
+    E = ug.UG_ERR_INVALID_ARG
+
+    def call(logits=A, ld=4096, B=2, V=4096, k=100, T=1.0, u=A2, tok=A3, idx=NULL, ldi=0):
+        return L.ug_sample_topk(logits, ld, B, V, k, T, u, tok, idx, ldi, NULL, 0, NULL, 0, S)
+
+    assert call(logits=MIS) == E
+    assert call(tok=NULL) == E
+    assert call(k=0) == E
+    assert call(k=257, V=4096) == E          # above UG_SAMPLE_MAX_K
+    assert call(k=10, V=5, ld=8) == E        # k > V
+    assert call(ld=4095) == E                # ld < V
+    assert call(ld=4098) == E                # ld % 4
+    assert call(T=0.0) == E
+    assert call(T=float("inf")) == E
+    assert call(idx=A4, ldi=50) == E         # output pitch < k
+    assert call(u=ctypes.c_void_p(0x200002)) == E

@@ -19,6 +19,7 @@ from oracle import build as obuild
 
 import test_oracle_attention as attn_pins
 import test_oracle_pins as pins
+import test_oracle_sampler as sampler_pins
 
 SRC = obuild.SRC
 
@@ -151,6 +152,22 @@ MUTANTS = {
         [("                out[m * ldo + h * dh + d] = (float)(o / sum);",
           "                out[m * ldo + h * dh + d] = (float)o;")],
         ["test_attention_equal_keys_average_the_values"]),
+    # --- top-k sampling ("a 1-bit llm, from scratch") ----------------------
+    "sampler_ties_to_higher_index": (
+        [("    return (x->i > y->i) - (x->i < y->i);", "    return (x->i < y->i) - (x->i > y->i);")],
+        ["test_k1_is_argmax", "test_ranking_matches_a_stable_sort"]),
+    "sampler_temperature_multiplied": (
+        [("            run += exp(((double)e[r].v - (double)e[0].v) / (double)temp);",
+          "            run += exp(((double)e[r].v - (double)e[0].v) * (double)temp);")],
+        ["test_two_kept_logits_with_temperature"]),
+    "sampler_smallest_first": (
+        [("    if (x->v > y->v)\n        return -1;\n    if (x->v < y->v)\n        return 1;",
+          "    if (x->v < y->v)\n        return -1;\n    if (x->v > y->v)\n        return 1;")],
+        ["test_k1_is_argmax"]),
+    "sampler_cdf_from_the_bottom_rank": (
+        [("            run += exp(((double)e[r].v - (double)e[0].v) / (double)temp);",
+          "            run += exp(((double)e[k - 1 - r].v - (double)e[0].v) / (double)temp);")],
+        ["test_sampling_frequencies_follow_the_softmax", "test_two_kept_logits_with_temperature"]),
     # --- five trits per byte (README "A whole ternary GPT") -----------------
     "pack_digits_reversed": (
         [("                int pow3 = 1;\n                for (int j = 0; j < 5; ++j) {",
@@ -173,7 +190,10 @@ MUTANTS = {
 
 
 def _pin(name):
-    return getattr(pins, name, None) or getattr(attn_pins, name)
+    for mod in (pins, attn_pins, sampler_pins):
+        if hasattr(mod, name):
+            return getattr(mod, name)
+    raise AttributeError(name)
 
 
 def _compile(text, out):
