@@ -18,7 +18,8 @@ Prints ONE JSON line.  Workloads (default: decode_stack):
                 trits per byte as "requant_pack5"; and one decode step of
                 causal attention over a 4096-position K/V cache (20 heads x
                 128) as "attention_decode"; top-100-of-4096 sampling as
-                "sampler".
+                "sampler"; the straight-through backward (dx, dW, db) of a
+                2048-token 6912 x 2560 layer as "backward".
   sweep         decode GEMV at M in {1,4,16,64} x the three 2B-class shapes
                 (cold, cycling weight copies); value = weight GB/s over all
                 12 points.
@@ -339,6 +340,8 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["sampler"] = measure_sampler(torch, ug)
         torch.cuda.empty_cache()
+        out["backward"] = measure_backward(torch, ug)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         import oracle
         passes, secs = cpu_decode_stack(oracle, inputs, args.cpu_seconds)
@@ -496,6 +499,42 @@ def measure_sampler(torch, ug, V=4096, k=100, B=4096):
                              traffic=None, median_launch_us=med, alg_bytes_per_launch=alg))
     log("sampler", res)
     del rows
+    return res
+
+
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def measure_backward(torch, ug, M=2048, N=6912, K=2560):
+    """The straight-through backward of the stack workload's up projection
+    (M = 2048 tokens, W 6912 x 2560): dx = g W and dW = g^T x on the fp32
+    matrix cores (2 M N K flops each) and db; medians over STAT_LAUNCHES
+    calls of each."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda:0").manual_seed(13)
+    g = torch.randn((M, N), device=dev, generator=gen) * 0.01
+    x = torch.randn((M, K), device=dev, generator=gen)
+    W = torch.randn((N, K), device=dev, generator=gen) * 0.02
+    outs = {}
+    for name in ("dx", "dW", "db"):
+        res = ug.ug_bitlinear_backward(g, x, W, want=(name,))
+        med, p10, p90 = launch_stats(
+            torch, lambda i: ug.ug_bitlinear_backward(g, x, W, want=(name,), **res), stream)
+        outs[name] = (med, p10, p90)
+    flops = 2 * M * N * K
+    tf = {k: flops / (outs[k][0] * 1e-6) / 1e12 for k in ("dx", "dW")}
+    achieved = 2 * flops / ((outs["dx"][0] + outs["dW"][0]) * 1e-6) / 1e12
+    res = dict(value=achieved, unit="TFLOP/s",
+               point="g [%d, %d], x [%d, %d], W [%d, %d] fp32" % (M, N, M, K, N, K),
+               dx_us_median=outs["dx"][0], dx_TFLOPs=tf["dx"], dW_us_median=outs["dW"][0],
+               dW_TFLOPs=tf["dW"], db_us_median=outs["db"][0],
+               roofline=dict(bound="mfma", kernel="gemm_f32 (v_mfma_f32_16x16x4f32)",
+                             achieved=achieved, peak=FP32_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                             frac=achieved / FP32_MFMA_PEAK_TFLOPS, traffic=None,
+                             median_launch_us=(outs["dx"][0] + outs["dW"][0]) / 2,
+                             alg_flops_per_launch=flops))
+    log("backward", res)
     return res
 
 
@@ -900,7 +939,7 @@ def main():
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
     for k in ("prefill_gemm", "stream_m1", "requant_pack5", "attention_decode", "sampler",
-              "cpu_baseline"):
+              "backward", "cpu_baseline"):
         if k in res:
             line[k] = res[k]
     print(json.dumps(line), flush=True)

@@ -361,6 +361,34 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                      ws_bytes, tile, k_splits, stream);
 }
 
+size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N) {
+  if (M < 1 || N < 1 || M > INT32_MAX || N > INT32_MAX) return 0;
+  return ug::backward_workspace_bytes(M, N);
+}
+
+ug_status ug_bitlinear_backward(const float *g, int64_t ldg, const float *x, int64_t ldx,
+                                const float *W, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                                float *dx, int64_t lddx, float *dW, int64_t lddw, float *db,
+                                void *ws, size_t ws_bytes, void *stream) {
+  if (!ptr_ok(g) || !opt_ok(dx) || !opt_ok(dW) || !opt_ok(db)) return UG_ERR_INVALID_ARG;
+  if (dx == nullptr && dW == nullptr && db == nullptr) return UG_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1) return UG_ERR_INVALID_ARG;
+  if (!pitch_ok(ldg, N, 4)) return UG_ERR_INVALID_ARG;
+  if (dx && (!ptr_ok(W) || !pitch_ok(ldw, K, 4) || !pitch_ok(lddx, K, 4)))
+    return UG_ERR_INVALID_ARG;
+  if (dW && (!ptr_ok(x) || !pitch_ok(ldx, K, 4) || !pitch_ok(lddw, K, 4)))
+    return UG_ERR_INVALID_ARG;
+  // 32-bit tile indices and the column-sum grid
+  if (M > (INT64_C(1) << 23) || N > (INT64_C(1) << 30) || K > (INT64_C(1) << 30))
+    return UG_ERR_UNSUPPORTED;
+  if (db) {
+    const size_t need = ug::backward_workspace_bytes(M, N);
+    if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return UG_ERR_WORKSPACE;
+  }
+  return hip_status(ug::launch_backward(g, ldg, x, ldx, W, ldw, M, N, K, dx, lddx, dW, lddw, db,
+                                        static_cast<float *>(ws), as_stream(stream)));
+}
+
 ug_status ug_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V, int64_t k,
                          float temperature, const float *u, int32_t *tokens, int32_t *topk_index,
                          int64_t ldi, float *topk_logit, int64_t ldl, float *topk_prob,

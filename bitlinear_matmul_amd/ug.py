@@ -58,6 +58,9 @@ SIGNATURES = {
                                  _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "ug_bitlinear_gemm_tiled": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64,
                                        _i64, _vp, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp]),
+    "ug_bitlinear_backward_workspace_size": (_sz, [_i64, _i64]),
+    "ug_bitlinear_backward": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
+                                     _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
     "ug_sample_topk": (_i32, [_vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _i64, _vp, _i64,
                               _vp, _i64, _vp]),
     "ug_attention_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
@@ -434,4 +437,34 @@ def ug_sample_topk(logits, k, temperature, u, tokens=None, want_topk=False, stre
                                 k if prob is not None else 0, _stream(stream)),
            "ug_sample_topk")
     return (tokens, idx, val, prob) if want_topk else tokens
+
+
+def ug_bitlinear_backward(g, x, W, want=("dx", "dW", "db"), dx=None, dW=None, db=None,
+                          ws=None, stream=None):
+    """Straight-through backward: g fp32 [M, N], x fp32 [M, K], W fp32
+    [N, K] -> dict with dx [M, K], dW [N, K], db [N] (those in `want`)."""
+    M, N = g.shape
+    K = W.shape[1] if W is not None else x.shape[1]
+    dev = g.device
+    if "dx" in want and dx is None:
+        dx = empty_pitched(M, K, torch.float32, dev)
+    if "dW" in want and dW is None:
+        dW = empty_pitched(N, K, torch.float32, dev)
+    if "db" in want and db is None:
+        db = torch.empty(N, dtype=torch.float32, device=dev)
+    if "db" in want and ws is None:
+        ws = torch.empty(max(16, lib().ug_bitlinear_backward_workspace_size(M, N)),
+                         dtype=torch.uint8, device=dev)
+    _check(lib().ug_bitlinear_backward(
+        _p(g), _ld(g), _p(x), _ld(x) if x is not None else 0, _p(W),
+        _ld(W) if W is not None else 0, M, N, K,
+        _p(dx if "dx" in want else None), _ld(dx) if "dx" in want else 0,
+        _p(dW if "dW" in want else None), _ld(dW) if "dW" in want else 0,
+        _p(db if "db" in want else None), _p(ws), ws.numel() if ws is not None else 0,
+        _stream(stream)), "ug_bitlinear_backward")
+    out = {}
+    for name, t in (("dx", dx), ("dW", dW), ("db", db)):
+        if name in want:
+            out[name] = t
+    return out
 

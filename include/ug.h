@@ -351,6 +351,37 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                                   int64_t ldy, void *ws, size_t ws_bytes,
                                   int32_t tile, int32_t k_splits, void *stream);
 
+/* Bytes of workspace ug_bitlinear_backward needs when it computes db:
+ * 4 * ceil(M / 128) * N.  0 for invalid sizes. */
+size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N);
+
+/*
+ * Straight-through backward of the BitLinear layer ("ultragraph ... part
+ * 2", "autograd on a byte-graph": the estimator treats the quantizers and
+ * the per-row scale as the identity and sends the gradient to the fp32
+ * master weights).  With g = dL/dy fp32 [M][ldg] (N used), the layer's
+ * fp32 input x [M][ldx] (K used) and the fp32 masters W [N][ldw]:
+ *     dx[m][k] = sum_n g[m][n] W[n][k]     (dL/dx = g W),
+ *     dW[n][k] = sum_m g[m][n] x[m][k]     (dL/dW = g^T x),
+ *     db[n]    = sum_m g[m][n]             (dL/db = sum g).
+ *  dx fp32 [M][lddx], dW fp32 [N][lddw], db fp32 [N]: each may be NULL
+ *  (not computed; not all three).  x is read only for dW, W only for dx.
+ *  Pitches >= the row length and multiples of 4; matrix pointers 16-byte
+ *  aligned.  ws: device workspace of ws_bytes >= the size query when db is
+ *  wanted (else unused).
+ * Arithmetic: fp32 products and sums on the fp32 matrix cores (dx, dW) and
+ * a fixed-order fp32 column sum (db: 128-row chunks added in order, then
+ * the chunk sums in order); each result is within the fp32 rounding bound
+ * gamma_n * sum |terms| of the exact sum.  UG_ERR_UNSUPPORTED for
+ * M > 2^23 or N, K > 2^30.
+ */
+ug_status ug_bitlinear_backward(const float *g, int64_t ldg, const float *x,
+                                int64_t ldx, const float *W, int64_t ldw,
+                                int64_t M, int64_t N, int64_t K, float *dx,
+                                int64_t lddx, float *dW, int64_t lddw,
+                                float *db, void *ws, size_t ws_bytes,
+                                void *stream);
+
 /* Largest k of ug_sample_topk. */
 #define UG_SAMPLE_MAX_K 256
 

@@ -93,6 +93,8 @@ def _open(path):
         "ugref_epilogue": (None, [_i32p, _i64, _f32p, _f32, _f32p, _i64, _i64, _f32p, _i64]),
         "ugref_sample_topk": (None, [_f32p, _i64, _i64, _i64, _i64, _f32, _f32p, _i32p, _i32p,
                                      _f32p, ctypes.POINTER(ctypes.c_double)]),
+        "ugref_bitlinear_backward": (None, [_f32p, _i64, _f32p, _i64, _f32p, _i64, _i64, _i64,
+                                            _i64, _f32p, _i64, _f32p, _i64, _f32p]),
         "ugref_attention": (None, [_f32p, _i64, _f32p, _i64, _f32p, _i64, _i64, _i64, _i64,
                                    _i64, _f32p, _i64]),
     }
@@ -321,6 +323,31 @@ def sample_topk(logits, k, temp, u):
                               _ptr(idx, ctypes.c_int32), _ptr(val, ctypes.c_float),
                               cdf.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     return tok, idx, val, cdf
+
+
+def bitlinear_backward(g, x, W, want=("dx", "dW", "db")):
+    """The straight-through backward of the BitLinear layer ("autograd on a
+    byte-graph"): with g = dL/dy [M, N], x [M, K] and the fp32 masters
+    W [N, K]: dx = g W, dW = g^T x, db = sum over rows of g.  Double
+    precision sums, fp32 results.  Returns a dict of the outputs asked for."""
+    g = _c2d(g, np.float32)
+    x = _c2d(x, np.float32)
+    W = _c2d(W, np.float32)
+    M, N = g.shape
+    K = x.shape[1]
+    if x.shape[0] != M or W.shape != (N, K):
+        raise ValueError("shape mismatch")
+    out = {}
+    dx = np.empty((M, K), np.float32) if "dx" in want else None
+    dW = np.empty((N, K), np.float32) if "dW" in want else None
+    db = np.empty(N, np.float32) if "db" in want else None
+    p = lambda a: _ptr(a, ctypes.c_float) if a is not None else None  # noqa: E731
+    _load().ugref_bitlinear_backward(p(g), N, p(x), K, p(W), K, M, N, K, p(dx), K, p(dW), K,
+                                     p(db))
+    for name, a in (("dx", dx), ("dW", dW), ("db", db)):
+        if a is not None:
+            out[name] = a
+    return out
 
 
 def num_threads():

@@ -484,3 +484,59 @@ void ugref_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V,
         free(e);
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* Straight-through backward of the BitLinear layer                    */
+/* ------------------------------------------------------------------ */
+
+/* "ultragraph - when the graph is the 1-bit LLM, part 2", section "autograd
+ * on a byte-graph": the straight-through estimator treats the quantizers
+ * and the per-row scale as the identity, so with g = dL/dy [M][N], the
+ * fp32 master weights W [N][K] and the layer's fp32 input x [M][K]:
+ *     dL/dx = g W        dx[m][k] = sum_n g[m][n] W[n][k]
+ *     dL/dW = g^T x      dW[n][k] = sum_m g[m][n] x[m][k]
+ *     dL/db = sum_m g    db[n]    = sum_m g[m][n]
+ * Double-precision sums, rounded to fp32 once.  Any output may be NULL. */
+void ugref_bitlinear_backward(const float *g, int64_t ldg, const float *x,
+                              int64_t ldx, const float *W, int64_t ldw,
+                              int64_t M, int64_t N, int64_t K, float *dx,
+                              int64_t lddx, float *dW, int64_t lddw, float *db)
+{
+    if (dx) {
+#pragma omp parallel for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            double *row = (double *)calloc((size_t)K, sizeof(double));
+            for (int64_t n = 0; n < N; ++n) {
+                double gv = g[m * ldg + n];
+                for (int64_t k = 0; k < K; ++k)
+                    row[k] += gv * (double)W[n * ldw + k];
+            }
+            for (int64_t k = 0; k < K; ++k)
+                dx[m * lddx + k] = (float)row[k];
+            free(row);
+        }
+    }
+    if (dW) {
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            double *row = (double *)calloc((size_t)K, sizeof(double));
+            for (int64_t m = 0; m < M; ++m) {
+                double gv = g[m * ldg + n];
+                for (int64_t k = 0; k < K; ++k)
+                    row[k] += gv * (double)x[m * ldx + k];
+            }
+            for (int64_t k = 0; k < K; ++k)
+                dW[n * lddw + k] = (float)row[k];
+            free(row);
+        }
+    }
+    if (db) {
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; ++m)
+                s += (double)g[m * ldg + n];
+            db[n] = (float)s;
+        }
+    }
+}

@@ -327,3 +327,24 @@ def test_sample_topk_rejects(ug):
     assert call(T=float("inf")) == E
     assert call(idx=A4, ldi=50) == E         # output pitch < k
     assert call(u=ctypes.c_void_p(0x200002)) == E
+
+
+def test_backward_rejects(ug):
+    L = ug.lib()
+    E = ug.UG_ERR_INVALID_ARG
+    need = L.ug_bitlinear_backward_workspace_size(300, 64)
+    assert need == 4 * 3 * 64
+
+    def call(g=A, ldg=64, M=300, N=64, K=128, dx=ctypes.c_void_p(0x500000), dW=NULL, db=NULL,
+             ws=NULL, ws_bytes=0, ldw=128):
+        return L.ug_bitlinear_backward(g, ldg, A2, 128, A3, ldw, M, N, K, dx, 128, dW, 128, db,
+                                       ws, ws_bytes, S)
+
+    assert call(g=NULL) == E
+    assert call(dx=NULL) == E                       # nothing to compute
+    assert call(ldg=62) == E
+    assert call(ldw=100) == E                       # W pitch < K (dx needs W)
+    assert call(dx=MIS) == E
+    assert call(db=ctypes.c_void_p(0x600000)) == ug.UG_ERR_WORKSPACE
+    assert call(db=ctypes.c_void_p(0x600000), ws=A4, ws_bytes=need - 4) == ug.UG_ERR_WORKSPACE
+    assert call(M=2 ** 23 + 1) == ug.UG_ERR_UNSUPPORTED

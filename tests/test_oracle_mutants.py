@@ -18,6 +18,7 @@ import oracle
 from oracle import build as obuild
 
 import test_oracle_attention as attn_pins
+import test_oracle_backward as backward_pins
 import test_oracle_pins as pins
 import test_oracle_sampler as sampler_pins
 
@@ -168,6 +169,27 @@ MUTANTS = {
         [("            run += exp(((double)e[r].v - (double)e[0].v) / (double)temp);",
           "            run += exp(((double)e[k - 1 - r].v - (double)e[0].v) / (double)temp);")],
         ["test_sampling_frequencies_follow_the_softmax", "test_two_kept_logits_with_temperature"]),
+    # --- the straight-through backward ("autograd on a byte-graph") ---------
+    "backward_dx_drops_last_output": (
+        [("            for (int64_t n = 0; n < N; ++n) {\n                double gv = g[m * ldg + n];\n"
+          "                for (int64_t k = 0; k < K; ++k)\n"
+          "                    row[k] += gv * (double)W[n * ldw + k];",
+          "            for (int64_t n = 0; n + 1 < N; ++n) {\n                double gv = g[m * ldg + n];\n"
+          "                for (int64_t k = 0; k < K; ++k)\n"
+          "                    row[k] += gv * (double)W[n * ldw + k];")],
+        ["test_finite_differences_of_the_unquantized_layer", "test_one_hot_upstream_gradient"]),
+    "backward_dW_first_input_row_only": (
+        [("                    row[k] += gv * (double)x[m * ldx + k];",
+          "                    row[k] += gv * (double)x[k];")],
+        ["test_finite_differences_of_the_unquantized_layer", "test_one_hot_upstream_gradient"]),
+    "backward_dx_sign": (
+        [("                    row[k] += gv * (double)W[n * ldw + k];",
+          "                    row[k] -= gv * (double)W[n * ldw + k];")],
+        ["test_finite_differences_of_the_unquantized_layer"]),
+    "backward_db_skips_first_row": (
+        [("            for (int64_t m = 0; m < M; ++m)\n                s += (double)g[m * ldg + n];",
+          "            for (int64_t m = 1; m < M; ++m)\n                s += (double)g[m * ldg + n];")],
+        ["test_finite_differences_of_the_unquantized_layer", "test_one_hot_upstream_gradient"]),
     # --- five trits per byte (README "A whole ternary GPT") -----------------
     "pack_digits_reversed": (
         [("                int pow3 = 1;\n                for (int j = 0; j < 5; ++j) {",
@@ -190,7 +212,7 @@ MUTANTS = {
 
 
 def _pin(name):
-    for mod in (pins, attn_pins, sampler_pins):
+    for mod in (pins, attn_pins, sampler_pins, backward_pins):
         if hasattr(mod, name):
             return getattr(mod, name)
     raise AttributeError(name)
