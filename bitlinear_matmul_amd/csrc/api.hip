@@ -379,7 +379,7 @@ ug_status ug_bitlinear_backward(const float *g, int64_t ldg, const float *x, int
   if (dW && (!ptr_ok(x) || !pitch_ok(ldx, K, 4) || !pitch_ok(lddw, K, 4)))
     return UG_ERR_INVALID_ARG;
   // 32-bit tile indices and the column-sum grid
-  if (M > (INT64_C(1) << 23) || N > (INT64_C(1) << 30) || K > (INT64_C(1) << 30))
+  if (M >= (INT64_C(1) << 21) || N > (INT64_C(1) << 30) || K > (INT64_C(1) << 30))
     return UG_ERR_UNSUPPORTED;
   if (db) {
     const size_t need = ug::backward_workspace_bytes(M, N);

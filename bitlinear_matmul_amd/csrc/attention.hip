@@ -9,21 +9,23 @@
 //
 // A decode step reads the whole cache once (2 * positions * H * d_h * 4
 // bytes) for a few hundred flops per key: HBM-bound.  The keys are split in
-// chunks of 256 so that one query row still spreads over the chip
-// ("flash-decoding"): attn_partial computes, per (chunk, head, row), the
-// chunk's score maximum m_c, its sum l_c of exp(score - m_c) and its
-// unnormalized context o_c; attn_combine rescales the chunks to their common
-// maximum and divides.  Every reduction has one fixed order, the same for
-// every query row whatever the number of rows in the call, so row t of a
-// call over many rows is bit for bit the single-row call at position t:
+// chunks of 64 so that one query row still spreads over the chip
+// ("flash-decoding"): attn_partial, one wave per (chunk, head, row), computes
+// the chunk's score maximum m_c, its sum l_c of exp(score - m_c) and its
+// unnormalized context o_c, with no barrier and 17 KB of LDS, so that a
+// decode step at 4096 positions with 20 heads is 1280 small blocks resident
+// at once; attn_combine rescales the chunks to their common maximum and
+// divides.  Every reduction has one fixed order, the same for every query
+// row whatever the number of rows in the call, so row t of a call over many
+// rows is bit for bit the single-row call at position t:
 //   score_j = fl(dot_j / fl(sqrt(d_h))), dot_j = the 64 lane partials added
 //             in lane order, lane l's partial = its dims l, l+64, ... added
 //             in that order from +0;
 //   m_c     = max over the chunk (exact);
 //   p_j     = expf(score_j - m_c);
-//   l_c     = the 256 p_j folded pairwise (t += t+h, h = 128 .. 1);
-//   o_c[d]  = ((o_0 + o_1) + (o_2 + o_3)), o_w = wave w's 64 keys' fl(p_j v_jd)
-//             added in key order from +0;
+//   l_c     = the 64 p_j summed by a butterfly (lane l adds lane l ^ h for
+//             h = 32, 16, ..., 1: every lane ends with the same bits);
+//   o_c[d]  = the chunk's fl(p_j v_jd) added in key order from +0;
 //   out[d]  = fl(o[d] / l) with M = max_c m_c, e_c = expf(m_c - M),
 //             l = sum_c fl(e_c l_c) and o[d] = sum_c fl(e_c o_c[d]), each
 //             added in chunk order from +0.
@@ -32,8 +34,8 @@
 namespace ug {
 namespace {
 
-constexpr int kChunk = 256;  // keys per partial (one block of 4 waves)
-constexpr int kBatch = 16;   // keys per wave whose loads travel together
+constexpr int kChunk = 64;  // keys per partial (one wave)
+constexpr int kBatch = 32;  // keys whose loads travel together
 
 template <int DH>
 struct AttnDims {
@@ -42,26 +44,21 @@ struct AttnDims {
 };
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_partial(const float *__restrict__ q, int64_t ldq,
-                                                    const float *__restrict__ kc, int64_t ldk,
-                                                    const float *__restrict__ vc, int64_t ldv,
-                                                    int pos0, int H, int nck, float root,
-                                                    float *__restrict__ part) {
+__global__ __launch_bounds__(64) void attn_partial(const float *__restrict__ q, int64_t ldq,
+                                                   const float *__restrict__ kc, int64_t ldk,
+                                                   const float *__restrict__ vc, int64_t ldv,
+                                                   int pos0, int H, int nck, float root,
+                                                   float *__restrict__ part) {
   constexpr int R = AttnDims<DH>::R;
   const int c = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
   const int p = pos0 + m;  // the row's position: it sees keys 0 .. p
   const int j0 = c * kChunk;
   if (j0 > p) return;  // a chunk wholly after the row's position
-  const int jn = min(kChunk, p + 1 - j0);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int kbase = 64 * wave;                    // the wave's keys in the chunk
-  const int nk = max(0, min(64, jn - kbase));     // how many of them exist
+  const int nk = min(kChunk, p + 1 - j0);  // keys of the chunk the row sees
+  const int lane = threadIdx.x;
 
-  __shared__ float tr[4][64 * 65];  // per-wave transpose of key partials (odd pitch)
-  __shared__ float pw[kChunk];      // p_j of the chunk
-  __shared__ float ow[4][DH];       // per-wave context sums
-  __shared__ float wmax[4];
-  __shared__ float fold[256];
+  __shared__ float T[64 * 65];  // key partials, transposed (odd pitch: no bank conflicts)
+  __shared__ float pw[kChunk];
 
   float qv[R];
   const float *qr = q + (int64_t)m * ldq + h * DH;
@@ -73,17 +70,17 @@ __global__ __launch_bounds__(256) void attn_partial(const float *__restrict__ q,
 
   // Scores: lane l's partial products of every key, transposed through LDS
   // so that lane t then adds key t's 64 partials in lane order.
-  float *T = tr[wave];
-  for (int b0 = 0; b0 < 64; b0 += kBatch) {
+  const float *kbase = kc + (int64_t)j0 * ldk + h * DH;
+  for (int b0 = 0; b0 < kChunk; b0 += kBatch) {
+    if (b0 >= nk) break;  // wave-uniform
     float kv[kBatch][R];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const bool ok = b0 + u < nk;  // wave-uniform
-      const float *kr = kc + (int64_t)(j0 + kbase + b0 + u) * ldk + h * DH;
+      const bool ok = b0 + u < nk;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int d = lane + 64 * i;
-        kv[u][i] = ok && d < DH ? kr[d] : 0.0f;
+        kv[u][i] = ok && d < DH ? kbase[(int64_t)(b0 + u) * ldk + d] : 0.0f;
       }
     }
 #pragma unroll
@@ -94,56 +91,54 @@ __global__ __launch_bounds__(256) void attn_partial(const float *__restrict__ q,
       T[lane * 65 + b0 + u] = a;
     }
   }
-  __syncthreads();
+  __syncthreads();  // (one wave) the transposed partials are in LDS
   float dot = 0.0f;
   for (int l = 0; l < 64; ++l) dot = dot + T[l * 65 + lane];
   const bool valid = lane < nk;
   const float s = dot / root;
 
-  // chunk maximum, then p_j and l_c
-  const float mx = wave_max(valid ? s : -INFINITY);
-  if (lane == 0) wmax[wave] = mx;
-  __syncthreads();
-  const float mc = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  // chunk maximum, p_j and l_c
+  const float mc = wave_max(valid ? s : -INFINITY);
   const float pj = valid ? expf(s - mc) : 0.0f;
-  pw[tid] = pj;
-  const float lc = fold256(pj, fold);  // ends with a barrier: pw is visible
+  pw[lane] = pj;
+  float lc = pj;
+#pragma unroll
+  for (int hh = 32; hh >= 1; hh >>= 1) lc = lc + __shfl_xor(lc, hh, 64);
+  __syncthreads();  // p_j are in LDS
 
-  // unnormalized context of the wave's keys
+  // unnormalized context
   float o[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) o[i] = 0.0f;
-  for (int b0 = 0; b0 < 64; b0 += kBatch) {
-    if (b0 >= nk) break;  // wave-uniform
+  const float *vbase = vc + (int64_t)j0 * ldv + h * DH;
+  for (int b0 = 0; b0 < kChunk; b0 += kBatch) {
+    if (b0 >= nk) break;
     float vv[kBatch][R];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const bool ok = b0 + u < nk;
-      const float *vr = vc + (int64_t)(j0 + kbase + b0 + u) * ldv + h * DH;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int d = lane + 64 * i;
-        vv[u][i] = ok && d < DH ? vr[d] : 0.0f;
+        vv[u][i] = ok && d < DH ? vbase[(int64_t)(b0 + u) * ldv + d] : 0.0f;
       }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       if (b0 + u < nk) {
-        const float w = pw[kbase + b0 + u];
+        const float w = pw[b0 + u];
 #pragma unroll
         for (int i = 0; i < R; ++i) o[i] = o[i] + w * vv[u][i];
       }
     }
   }
+  float *rec = part + (((int64_t)m * H + h) * nck + c) * AttnDims<DH>::kRec;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int d = lane + 64 * i;
-    if (d < DH) ow[wave][d] = o[i];
+    if (d < DH) rec[d] = o[i];
   }
-  __syncthreads();
-  float *rec = part + (((int64_t)m * H + h) * nck + c) * AttnDims<DH>::kRec;
-  for (int d = tid; d < DH; d += 256) rec[d] = (ow[0][d] + ow[1][d]) + (ow[2][d] + ow[3][d]);
-  if (tid == 0) {
+  if (lane == 0) {
     rec[DH] = mc;
     rec[DH + 1] = lc;
   }
@@ -186,7 +181,7 @@ hipError_t launch_dh(const float *q, int64_t ldq, const float *kc, int64_t ldk, 
                      hipStream_t st) {
   const int nck = (pos0 + M + kChunk - 1) / kChunk;
   const float root = sqrtf((float)DH);
-  hipLaunchKernelGGL(attn_partial<DH>, dim3(nck, H, M), dim3(256), 0, st, q, ldq, kc, ldk, vc,
+  hipLaunchKernelGGL(attn_partial<DH>, dim3(nck, H, M), dim3(64), 0, st, q, ldq, kc, ldk, vc,
                      ldv, pos0, H, nck, root, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

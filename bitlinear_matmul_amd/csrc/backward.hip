@@ -143,10 +143,10 @@ __global__ __launch_bounds__(256) void gemm_f32(const float *__restrict__ a, int
   }
 }
 
-// db, stage 1: thread n of block (x, y) adds g[m][n] for the 128 rows
-// m in [128 y, 128 y + 128) in increasing m; stage 2: thread n adds the
+// db, stage 1: thread n of block (x, y) adds g[m][n] for the 32 rows
+// m in [32 y, 32 y + 32) in increasing m; stage 2: thread n adds the
 // chunk sums in increasing chunk order.
-constexpr int kColChunk = 128;
+constexpr int kColChunk = 32;
 
 __global__ __launch_bounds__(256) void colsum_chunks(const float *__restrict__ g, int64_t ldg,
                                                      int M, int N, float *__restrict__ part) {

@@ -352,7 +352,7 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                                   int32_t tile, int32_t k_splits, void *stream);
 
 /* Bytes of workspace ug_bitlinear_backward needs when it computes db:
- * 4 * ceil(M / 128) * N.  0 for invalid sizes. */
+ * 4 * ceil(M / 32) * N.  0 for invalid sizes. */
 size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N);
 
 /*
@@ -370,10 +370,10 @@ size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N);
  *  aligned.  ws: device workspace of ws_bytes >= the size query when db is
  *  wanted (else unused).
  * Arithmetic: fp32 products and sums on the fp32 matrix cores (dx, dW) and
- * a fixed-order fp32 column sum (db: 128-row chunks added in order, then
+ * a fixed-order fp32 column sum (db: 32-row chunks added in order, then
  * the chunk sums in order); each result is within the fp32 rounding bound
  * gamma_n * sum |terms| of the exact sum.  UG_ERR_UNSUPPORTED for
- * M > 2^23 or N, K > 2^30.
+ * M >= 2^21 or N, K > 2^30.
  */
 ug_status ug_bitlinear_backward(const float *g, int64_t ldg, const float *x,
                                 int64_t ldx, const float *W, int64_t ldw,
@@ -412,7 +412,7 @@ ug_status ug_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V,
                          int64_t ldp, void *stream);
 
 /* Bytes of workspace ug_attention_cached needs:
- * 4 * M * H * ceil((pos0 + M) / 256) * (dh + 4).  0 for invalid shapes. */
+ * 4 * M * H * ceil((pos0 + M) / 64) * (dh + 4).  0 for invalid shapes. */
 size_t ug_attention_workspace_size(int64_t M, int64_t pos0, int64_t H,
                                    int64_t dh);
 

@@ -286,9 +286,9 @@ def test_grouped_plan_rejects_fused_with_chunked(ug):
 def test_attention_rejects_and_sizes(ug):
     L = ug.lib()
     E = ug.UG_ERR_INVALID_ARG
-    # workspace: 4 * M * H * ceil((pos0 + M) / 256) * (dh + 4)
-    assert L.ug_attention_workspace_size(1, 4095, 20, 128) == 4 * 1 * 20 * 16 * 132
-    assert L.ug_attention_workspace_size(300, 0, 3, 64) == 4 * 300 * 3 * 2 * 68
+    # workspace: 4 * M * H * ceil((pos0 + M) / 64) * (dh + 4)
+    assert L.ug_attention_workspace_size(1, 4095, 20, 128) == 4 * 1 * 20 * 64 * 132
+    assert L.ug_attention_workspace_size(300, 0, 3, 64) == 4 * 300 * 3 * 5 * 68
     assert L.ug_attention_workspace_size(1, 0, 1, 48) == 0        # d_h not supported
     need = L.ug_attention_workspace_size(1, 99, 2, 64)
 
@@ -333,7 +333,7 @@ def test_backward_rejects(ug):
     L = ug.lib()
     E = ug.UG_ERR_INVALID_ARG
     need = L.ug_bitlinear_backward_workspace_size(300, 64)
-    assert need == 4 * 3 * 64
+    assert need == 4 * 10 * 64
 
     def call(g=A, ldg=64, M=300, N=64, K=128, dx=ctypes.c_void_p(0x500000), dW=NULL, db=NULL,
              ws=NULL, ws_bytes=0, ldw=128):
