@@ -122,7 +122,12 @@ def parse():
                    choices=["decode_stack", "sweep", "prefill", "stack", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true",
-                   help="decode_stack: skip the prefill-GEMM and M=1 streaming points")
+                   help="decode_stack: skip the extra measurement points")
+    p.add_argument("--only", default=None,
+                   choices=["prefill_gemm", "stream_m1", "requant_pack5", "attention_decode",
+                            "sampler", "backward"],
+                   help="run just this one of the decode_stack line's extra points and print "
+                        "its JSON object (for profiling a single kernel)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--sweep-point", default=None, metavar="M,SHAPE",
                    help="sweep: run only the point with M rows and shape index SHAPE "
@@ -933,6 +938,15 @@ def main():
     ug.lib()
     if args.copy_probe:
         copy_probe(torch)
+    if args.only is not None:
+        fn = {"prefill_gemm": lambda: measure_prefill_gemm(torch, ug, inputs),
+              "stream_m1": lambda: measure_stream_m1(torch, ug, inputs),
+              "requant_pack5": lambda: measure_requant_pack5(torch, ug, inputs),
+              "attention_decode": lambda: measure_attention_decode(torch, ug),
+              "sampler": lambda: measure_sampler(torch, ug),
+              "backward": lambda: measure_backward(torch, ug)}[args.only]
+        print(json.dumps({"point": args.only, **fn()}), flush=True)
+        return
     runners = {"decode_stack": run_decode_stack, "prefill": run_prefill, "sweep": run_sweep,
                "stack": run_stack, "tiny": run_tiny}
     res = runners[args.workload](args, torch, ug, inputs)

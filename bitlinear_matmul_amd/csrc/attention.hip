@@ -26,9 +26,11 @@
 //   l_c     = the 64 p_j summed by a butterfly (lane l adds lane l ^ h for
 //             h = 32, 16, ..., 1: every lane ends with the same bits);
 //   o_c[d]  = the chunk's fl(p_j v_jd) added in key order from +0;
-//   out[d]  = fl(o[d] / l) with M = max_c m_c, e_c = expf(m_c - M),
-//             l = sum_c fl(e_c l_c) and o[d] = sum_c fl(e_c o_c[d]), each
-//             added in chunk order from +0.
+//   out[d]  = fl(o[d] / l) with M = max_c m_c, e_c = expf(m_c - M);
+//             for w = 0..3, l_w = sum of fl(e_c l_c) and o_w[d] = sum of
+//             fl(e_c o_c[d]) over the chunks c = w, w+4, w+8, ... added in
+//             that order from +0; l = (l_0 + l_1) + (l_2 + l_3), and o[d]
+//             the same way.
 #include "ug_internal.h"
 
 namespace ug {
@@ -145,34 +147,61 @@ __global__ __launch_bounds__(64) void attn_partial(const float *__restrict__ q, 
 }
 
 template <int DH>
-__global__ __launch_bounds__(64) void attn_combine(const float *__restrict__ part, int pos0,
-                                                   int H, int nck, float *__restrict__ out,
-                                                   int64_t ldo) {
-  constexpr int R = AttnDims<DH>::R, REC = AttnDims<DH>::kRec;
-  const int h = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void attn_combine(const float *__restrict__ part, int pos0,
+                                                    int H, int nck, float *__restrict__ out,
+                                                    int64_t ldo) {
+  constexpr int R = AttnDims<DH>::R, REC = AttnDims<DH>::kRec, NB = 8;
+  const int h = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = (pos0 + m) / kChunk + 1;
   const float *base = part + ((int64_t)m * H + h) * nck * REC;
+  __shared__ float wmax[4], wl[4];
+  __shared__ float wo[4][DH];
+  // M = the largest chunk maximum (exact in any order)
   float mx = -INFINITY;
-  for (int c = 0; c < nc; ++c) mx = fmaxf(mx, base[c * REC + DH]);
+  for (int c = tid; c < nc; c += 256) mx = fmaxf(mx, base[(int64_t)c * REC + DH]);
+  mx = wave_max(mx);
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  // wave w: chunks w, w + 4, ... in increasing order, NB at a time in flight
   float l = 0.0f, o[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) o[i] = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float *rec = base + c * REC;
-    const float e = expf(rec[DH] - mx);
-    l = l + e * rec[DH + 1];
+  for (int c0 = wave; c0 < nc; c0 += 4 * NB) {
+    float mc[NB], lc[NB], oc[NB][R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int d = lane + 64 * i;
-      if (d < DH) o[i] = o[i] + e * rec[d];
+    for (int u = 0; u < NB; ++u) {
+      const int c = c0 + 4 * u;
+      const float *rec = base + (int64_t)min(c, nc - 1) * REC;
+      mc[u] = rec[DH];
+      lc[u] = rec[DH + 1];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int d = lane + 64 * i;
+        oc[u][i] = d < DH ? rec[d] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (c0 + 4 * u < nc) {
+        const float e = expf(mc[u] - mx);
+        l = l + e * lc[u];
+#pragma unroll
+        for (int i = 0; i < R; ++i) o[i] = o[i] + e * oc[u][i];
+      }
     }
   }
-  float *orow = out + (int64_t)m * ldo + h * DH;
+  if (lane == 0) wl[wave] = l;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int d = lane + 64 * i;
-    if (d < DH) orow[d] = o[i] / l;
+    if (d < DH) wo[wave][d] = o[i];
   }
+  __syncthreads();
+  const float lt = (wl[0] + wl[1]) + (wl[2] + wl[3]);
+  float *orow = out + (int64_t)m * ldo + h * DH;
+  for (int d = tid; d < DH; d += 256)
+    orow[d] = ((wo[0][d] + wo[1][d]) + (wo[2][d] + wo[3][d])) / lt;
 }
 
 template <int DH>
@@ -185,7 +214,7 @@ hipError_t launch_dh(const float *q, int64_t ldq, const float *kc, int64_t ldk, 
                      ldv, pos0, H, nck, root, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine<DH>, dim3(H, M), dim3(64), 0, st, part, pos0, H, nck, out, ldo);
+  hipLaunchKernelGGL(attn_combine<DH>, dim3(H, M), dim3(256), 0, st, part, pos0, H, nck, out, ldo);
   return hipGetLastError();
 }
 

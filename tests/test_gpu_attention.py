@@ -41,7 +41,8 @@ def _bound(q, k, v, pos0, H):
     |d score_j| <= E_j = gamma(dh + 66) * sum_d |q_d k_jd| / sqrt(dh).  A
     weight a_j = e^{s_j} / sum e^{s_i} then moves by at most 2 max_j E_j
     relative, plus the roundings of its exp (two, with the chunk rescale),
-    of the sums (64 keys in order within a chunk, up to 64 chunks in order)
+    of the sums (64 keys in order within a chunk, up to 16 chunks in order
+    per wave of the combine, then two levels)
     and of the products: at most 256 u relative to sum_j a_j |v_jd| all
     told.  So |out_d - exact_d| <= (2 max E + 256 u) sum_j a_j |v_jd|."""
     M, HD = q.shape
