@@ -360,8 +360,9 @@ def run_decode_stack(args, torch, ug, inputs):
 
 def measure_prefill_gemm(torch, ug, inputs):
     """The int8 MFMA GEMM of the prefill workload (M = 4096; 2560 -> 6912 and
-    6912 -> 2560, I8 weights), alone: the median over STAT_LAUNCHES launches
-    per shape, each between HIP events on the launch stream."""
+    6912 -> 2560, I8 weights), alone: per shape, the median over STAT_LAUNCHES
+    samples of 5 back-to-back launches, each sample between HIP events on
+    the launch stream."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     per_shape = []
@@ -375,8 +376,11 @@ def measure_prefill_gemm(torch, ug, inputs):
         del x, W
         for _ in range(3):
             ug.ug_bitlinear_gemm(xq, s, wq, ug.UG_W_I8, beta, y=y)
+        # a prefill runs its GEMMs back to back: each sample is 5 launches in
+        # a row, per-launch time = their time / 5
         med, p10, p90 = launch_stats(
-            torch, lambda i: ug.ug_bitlinear_gemm(xq, s, wq, ug.UG_W_I8, beta, y=y), stream)
+            torch, lambda i: [ug.ug_bitlinear_gemm(xq, s, wq, ug.UG_W_I8, beta, y=y)
+                              for _ in range(5)], stream, per=5)
         ops = 2 * M * N * K
         per_shape.append(dict(M=M, K=K, N=N, ops=ops, median_us=med, p10_us=p10, p90_us=p90,
                               TOPs=ops / (med * 1e-6) / 1e12))
