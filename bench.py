@@ -526,7 +526,7 @@ def measure_backward(torch, ug, M=2048, N=6912, K=2560):
     x = torch.randn((M, K), device=dev, generator=gen)
     W = torch.randn((N, K), device=dev, generator=gen) * 0.02
     outs = {}
-    ws = torch.empty(ug.lib().ug_bitlinear_backward_workspace_size(M, N), dtype=torch.uint8,
+    ws = torch.empty(ug.lib().ug_bitlinear_backward_workspace_size(M, N, K), dtype=torch.uint8,
                      device=dev)
     for name in ("dx", "dW", "db"):
         res = ug.ug_bitlinear_backward(g, x, W, want=(name,), ws=ws)

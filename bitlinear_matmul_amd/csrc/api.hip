@@ -361,9 +361,11 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                      ws_bytes, tile, k_splits, stream);
 }
 
-size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N) {
-  if (M < 1 || N < 1 || M > INT32_MAX || N > INT32_MAX) return 0;
-  return ug::backward_workspace_bytes(M, N);
+size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1 || M >= (INT64_C(1) << 21) || N > (INT64_C(1) << 30) ||
+      K > (INT64_C(1) << 30))
+    return 0;
+  return ug::backward_workspace_bytes(M, N, K);
 }
 
 ug_status ug_bitlinear_backward(const float *g, int64_t ldg, const float *x, int64_t ldx,
@@ -381,10 +383,8 @@ ug_status ug_bitlinear_backward(const float *g, int64_t ldg, const float *x, int
   // 32-bit tile indices and the column-sum grid
   if (M >= (INT64_C(1) << 21) || N > (INT64_C(1) << 30) || K > (INT64_C(1) << 30))
     return UG_ERR_UNSUPPORTED;
-  if (db) {
-    const size_t need = ug::backward_workspace_bytes(M, N);
-    if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return UG_ERR_WORKSPACE;
-  }
+  const size_t need = ug::backward_workspace_bytes(M, N, K);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < need) return UG_ERR_WORKSPACE;
   return hip_status(ug::launch_backward(g, ldg, x, ldx, W, ldw, M, N, K, dx, lddx, dW, lddw, db,
                                         static_cast<float *>(ws), as_stream(stream)));
 }

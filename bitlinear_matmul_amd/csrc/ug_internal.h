@@ -140,9 +140,9 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,
                        int64_t ldacc, float *y, int64_t ldy, hipStream_t st);
 // Straight-through backward: dx = g W and dW = g^T x on the fp32 matrix
-// cores, db = column sums of g (chunk sums in `part`,
-// backward_workspace_bytes).  Null outputs are skipped.
-size_t backward_workspace_bytes(int64_t M, int64_t N);
+// cores, db = column sums of g; `part` (backward_workspace_bytes) holds the
+// column chunk sums and dx's contraction pieces.  Null outputs are skipped.
+size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_backward(const float *g, int64_t ldg, const float *x, int64_t ldx,
                            const float *W, int64_t ldw, int64_t M, int64_t N, int64_t K,
                            float *dx, int64_t lddx, float *dW, int64_t lddw, float *db,

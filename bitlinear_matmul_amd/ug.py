@@ -58,7 +58,7 @@ SIGNATURES = {
                                  _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "ug_bitlinear_gemm_tiled": (_i32, [_vp, _i64, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64,
                                        _i64, _vp, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp]),
-    "ug_bitlinear_backward_workspace_size": (_sz, [_i64, _i64]),
+    "ug_bitlinear_backward_workspace_size": (_sz, [_i64, _i64, _i64]),
     "ug_bitlinear_backward": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp,
                                      _i64, _vp, _i64, _vp, _vp, _sz, _vp]),
     "ug_sample_topk": (_i32, [_vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _i64, _vp, _i64,
@@ -452,8 +452,8 @@ def ug_bitlinear_backward(g, x, W, want=("dx", "dW", "db"), dx=None, dW=None, db
         dW = empty_pitched(N, K, torch.float32, dev)
     if "db" in want and db is None:
         db = torch.empty(N, dtype=torch.float32, device=dev)
-    if "db" in want and ws is None:
-        ws = torch.empty(max(16, lib().ug_bitlinear_backward_workspace_size(M, N)),
+    if ws is None:
+        ws = torch.empty(max(16, lib().ug_bitlinear_backward_workspace_size(M, N, K)),
                          dtype=torch.uint8, device=dev)
     _check(lib().ug_bitlinear_backward(
         _p(g), _ld(g), _p(x), _ld(x) if x is not None else 0, _p(W),

@@ -351,9 +351,12 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                                   int64_t ldy, void *ws, size_t ws_bytes,
                                   int32_t tile, int32_t k_splits, void *stream);
 
-/* Bytes of workspace ug_bitlinear_backward needs when it computes db:
- * 4 * ceil(M / 32) * N.  0 for invalid sizes. */
-size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N);
+/* Bytes of workspace ug_bitlinear_backward needs: the larger of
+ * 4 * ceil(M / 32) * N (db's chunk sums) and, when dx = g W has fewer than
+ * 1024 output tiles of 128 x 128, 4 * S * M * K for its S contraction
+ * pieces (S the smallest power of two, at most 8, that gives 1024 work
+ * items while each piece stays at least 256 deep).  0 for invalid sizes. */
+size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
  * Straight-through backward of the BitLinear layer ("ultragraph ... part
@@ -367,12 +370,12 @@ size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N);
  *  dx fp32 [M][lddx], dW fp32 [N][lddw], db fp32 [N]: each may be NULL
  *  (not computed; not all three).  x is read only for dW, W only for dx.
  *  Pitches >= the row length and multiples of 4; matrix pointers 16-byte
- *  aligned.  ws: device workspace of ws_bytes >= the size query when db is
- *  wanted (else unused).
- * Arithmetic: fp32 products and sums on the fp32 matrix cores (dx, dW) and
- * a fixed-order fp32 column sum (db: 32-row chunks added in order, then
- * the chunk sums in order); each result is within the fp32 rounding bound
- * gamma_n * sum |terms| of the exact sum.  UG_ERR_UNSUPPORTED for
+ *  aligned.  ws: device workspace of ws_bytes >= the size query.
+ * Arithmetic: fp32 products and sums on the fp32 matrix cores (dx, dW; a
+ * few-tile dx adds its contraction pieces in piece order) and a
+ * fixed-order fp32 column sum (db: 32-row chunks added in order, then the
+ * chunk sums in order); the same bits on every run, each result within the
+ * fp32 rounding bound gamma_(n+8) * sum |terms| of the exact sum.  UG_ERR_UNSUPPORTED for
  * M >= 2^21 or N, K > 2^30.
  */
 ug_status ug_bitlinear_backward(const float *g, int64_t ldg, const float *x,

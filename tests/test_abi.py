@@ -332,8 +332,10 @@ def test_sample_topk_rejects(ug):
 def test_backward_rejects(ug):
     L = ug.lib()
     E = ug.UG_ERR_INVALID_ARG
-    need = L.ug_bitlinear_backward_workspace_size(300, 64)
-    assert need == 4 * 10 * 64
+    need = L.ug_bitlinear_backward_workspace_size(300, 64, 128)
+    assert need == 4 * 10 * 64        # db's chunk sums; dx too shallow (N = 64) to split
+    # dx = g W at 2048 x 2560 (320 tiles), 6912 deep: 4 pieces
+    assert L.ug_bitlinear_backward_workspace_size(2048, 6912, 2560) == 4 * 4 * 2048 * 2560
 
     def call(g=A, ldg=64, M=300, N=64, K=128, dx=ctypes.c_void_p(0x500000), dW=NULL, db=NULL,
              ws=NULL, ws_bytes=0, ldw=128):
@@ -347,4 +349,5 @@ def test_backward_rejects(ug):
     assert call(dx=MIS) == E
     assert call(db=ctypes.c_void_p(0x600000)) == ug.UG_ERR_WORKSPACE
     assert call(db=ctypes.c_void_p(0x600000), ws=A4, ws_bytes=need - 4) == ug.UG_ERR_WORKSPACE
+    assert call(ws=NULL) == ug.UG_ERR_WORKSPACE
     assert call(M=2 ** 23 + 1) == ug.UG_ERR_UNSUPPORTED
