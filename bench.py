@@ -144,21 +144,44 @@ def parse():
 # Valid only for the kernel sources they were taken on: `src_sha` is the
 # SHA-256 of the kernel's source file; any other source reports null.
 TRAFFIC = {
-    # profiles/gemv_fine_grouped_decode_stack.md: 1990.9 KiB fetched x 1.9997,
-    # 146.4 KiB written x 1.0000
-    "decode_stack": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
-                         src_sha="1aae82af7e9516601044d9b7a23aec2baef46e0964b8951dc49212bf55f17d0a",
-                         bytes_per_launch=4226741),
+    # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
+    # dispatch, medians), calibrated by a 256 MiB copy: bytes = FETCH x 1024 x
+    # 1.99977 + WRITE x 1024.  A record holds only while the kernel sources
+    # it was taken on are unchanged.
+    # profiles/gemv_fine_grouped_decode_stack.md: 2005.9 KiB / 146.4 KiB
+    "decode_stack": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
+                              "35eb904b607e06ad24ca802271d2559fb2433d6e7ceb0bf5c5df246c1d6c0f87"},
+                         bytes_per_launch=4257560),
     # profiles/gemv_stream_grouped_sweep_m1.md: M=1 2560->6912, 37 problems per
-    # launch: 64217.2 KiB fetched x 1.9997, 697.6 KiB written x 1.0000
-    "sweep": dict(src="bitlinear_matmul_amd/csrc/gemv_mfma.hip",
-                  src_sha="1aae82af7e9516601044d9b7a23aec2baef46e0964b8951dc49212bf55f17d0a",
-                  bytes_per_launch=132214235),
-    # profiles/gemm_i8_large_prefill.md: mean of both shapes, 60190.6 KiB
-    # fetched x 1.9997, 75776.0 KiB written x 1.0000
-    "prefill": dict(src="bitlinear_matmul_amd/csrc/gemm.hip",
-                    src_sha="11ab35c8fe414afb87b67a3d95e82774ae246e31de0d9e609a3908b361837e64",
-                    bytes_per_launch=200846379),
+    # launch: 64227.3 KiB / 718.1 KiB
+    "sweep": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
+                       "35eb904b607e06ad24ca802271d2559fb2433d6e7ceb0bf5c5df246c1d6c0f87"},
+                  bytes_per_launch=132256303),
+    # profiles/gemm_i8_large_prefill.md: mean of the two shapes' launches
+    "prefill": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
+                         "06fc5d4c90ea64594662b948395ad6f927f071c6413aa61d83a191b11e6da732"},
+                    bytes_per_launch=200755282),
+    # profiles/gemm_i8_large_stack.md: mean of the two shapes' launches
+    "stack": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
+                       "06fc5d4c90ea64594662b948395ad6f927f071c6413aa61d83a191b11e6da732"},
+                  bytes_per_launch=143289344),
+    # profiles/absmean_ternary_pack5_requant.md: stage 1 + fused pass per call
+    "requant_pack5": dict(src={"bitlinear_matmul_amd/csrc/absmean.hip":
+                               "a69523d80a0c82173d06857320485e02857481b5810e490f22fae63e67d95234"},
+                          bytes_per_launch=145415161),
+    # profiles/attention_decode_4096.md: partials + combine per call
+    "attention_decode": dict(src={"bitlinear_matmul_amd/csrc/attention.hip":
+                                  "7e8669c58e2a560ba3cf2cf121f5b634fa8e6f54d005e3178610c944a7eff0fd"},
+                             bytes_per_launch=85623294),
+    # profiles/topk_sample_batch4096.md: the 4096-row launch
+    "sampler": dict(src={"bitlinear_matmul_amd/csrc/sampler.hip":
+                         "eb3e8dfbe3e23ec5170cbb7bcc4453c73935223a4d1f85c2f08e3d12e0272f30"},
+                    bytes_per_launch=67809093),
+    # profiles/gemm_f32_backward.md: mean of the dx call (GEMM + slab sum) and
+    # the dW call
+    "backward": dict(src={"bitlinear_matmul_amd/csrc/backward.hip":
+                          "f681a6da409af86df1788e520aea31319f073d37630bca2cbe2786a31b629458"},
+                     bytes_per_launch=800887323),
 }
 
 
@@ -170,7 +193,7 @@ def source_sha(relpath):
 
 def traffic_for(workload):
     t = TRAFFIC.get(workload)
-    if t is None or source_sha(t["src"]) != t["src_sha"]:
+    if t is None or any(source_sha(f) != h for f, h in t["src"].items()):
         return None
     return t["bytes_per_launch"]
 
@@ -427,7 +450,7 @@ def measure_requant_pack5(torch, ug, inputs):
                median_call_us=med, p10_call_us=p10, p90_call_us=p90,
                roofline=dict(bound="hbm", kernel="absmean_stage1 + ternary_pack5",
                              achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=achieved / HBM_PEAK_GBS, traffic=None,
+                             frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("requant_pack5"),
                              median_launch_us=med, alg_bytes_per_launch=alg))
     log("requant pack5", out)
     del masters
@@ -466,7 +489,8 @@ def measure_attention_decode(torch, ug, T=4096, H=20, dh=128):
                median_call_us=med, p10_call_us=p10, p90_call_us=p90,
                roofline=dict(bound="hbm", kernel="attn_partial<128> + attn_combine<128>",
                              achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=achieved / HBM_PEAK_GBS, traffic=None, median_launch_us=med,
+                             frac=achieved / HBM_PEAK_GBS, traffic=traffic_for("attention_decode"),
+                             median_launch_us=med,
                              alg_bytes_per_launch=alg))
     log("attention decode", res)
     del caches
@@ -505,7 +529,7 @@ def measure_sampler(torch, ug, V=4096, k=100, B=4096):
                batch_us_p90=p90,
                roofline=dict(bound="hbm", kernel="topk_sample<true>", achieved=achieved,
                              peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
-                             traffic=None, median_launch_us=med, alg_bytes_per_launch=alg))
+                             traffic=traffic_for("sampler"), median_launch_us=med, alg_bytes_per_launch=alg))
     log("sampler", res)
     del rows
     return res
@@ -543,7 +567,7 @@ def measure_backward(torch, ug, M=2048, N=6912, K=2560):
                dW_TFLOPs=tf["dW"], db_us_median=outs["db"][0],
                roofline=dict(bound="mfma", kernel="gemm_f32 (v_mfma_f32_16x16x4f32)",
                              achieved=achieved, peak=FP32_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                             frac=achieved / FP32_MFMA_PEAK_TFLOPS, traffic=None,
+                             frac=achieved / FP32_MFMA_PEAK_TFLOPS, traffic=traffic_for("backward"),
                              median_launch_us=(outs["dx"][0] + outs["dW"][0]) / 2,
                              alg_flops_per_launch=flops))
     log("backward", res)
