@@ -124,8 +124,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="decode_stack: skip the extra measurement points")
     p.add_argument("--only", default=None,
-                   choices=["prefill_gemm", "stream_m1", "requant_pack5", "attention_decode",
-                            "sampler", "backward"],
+                   choices=["prefill_gemm", "vendor_int8_gemm", "stream_m1", "requant_pack5",
+                            "attention_decode", "sampler", "backward"],
                    help="run just this one of the decode_stack line's extra points and print "
                         "its JSON object (for profiling a single kernel)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -360,6 +360,8 @@ def run_decode_stack(args, torch, ug, inputs):
     if not args.no_extra:
         out["prefill_gemm"] = measure_prefill_gemm(torch, ug, inputs)
         torch.cuda.empty_cache()
+        out["vendor_int8_gemm"] = measure_vendor_gemm(torch, ug, inputs)
+        torch.cuda.empty_cache()
         out["stream_m1"] = measure_stream_m1(torch, ug, inputs)
         torch.cuda.empty_cache()
         out["requant_pack5"] = measure_requant_pack5(torch, ug, inputs)
@@ -417,6 +419,41 @@ def measure_prefill_gemm(torch, ug, inputs):
                               peak=INT8_PEAK_TOPS, unit="TOP/s", frac=achieved / INT8_PEAK_TOPS,
                               traffic=traffic_for("prefill"), median_launch_us=us,
                               alg_ops_per_launch=ops))
+
+
+def measure_vendor_gemm(torch, ug, inputs):
+    """Context, not this library: the vendor BLAS's int8 GEMM (torch._int_mm,
+    hipBLASLt on ROCm) on the prefill shapes and the same quantized operands,
+    int32 output (no rescale, so less output work than ours), timed as
+    prefill_gemm is: medians of samples of 5 back-to-back launches."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    per_shape = []
+    for j in (0, 1):
+        x, W, _ = inputs.prefill_inputs(j)
+        K, N = inputs.PREFILL_SHAPES[j]
+        M = x.shape[0]
+        wq, _beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
+        xq, _s = ug.ug_quant_act(torch.from_numpy(x).to(dev))
+        a = xq[:, :K].contiguous()
+        bt = wq[:, :K].contiguous().t()  # K x N, column-major: x_q W_q^T
+        del x, W, xq, wq
+        out = torch._int_mm(a, bt)
+        for _ in range(3):
+            torch._int_mm(a, bt, out=out)
+        med, p10, p90 = launch_stats(
+            torch, lambda i: [torch._int_mm(a, bt, out=out) for _ in range(5)], stream, per=5)
+        ops = 2 * M * N * K
+        per_shape.append(dict(M=M, K=K, N=N, median_us=med, p10_us=p10, p90_us=p90,
+                              TOPs=ops / (med * 1e-6) / 1e12))
+        log("vendor int8 gemm", per_shape[-1])
+        del a, bt, out
+    us = sum(p["median_us"] for p in per_shape) / 2
+    ops = 2 * per_shape[0]["M"] * per_shape[0]["N"] * per_shape[0]["K"]
+    return dict(value=ops / (us * 1e-6) / 1e12, unit="TOP/s", library="torch._int_mm",
+                note="context only: the vendor library on the same operands, int32 output",
+                shapes=per_shape, median_launch_us=us,
+                frac_of_int8_peak=ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS)
 
 
 def measure_requant_pack5(torch, ug, inputs):
@@ -968,6 +1005,7 @@ def main():
         copy_probe(torch)
     if args.only is not None:
         fn = {"prefill_gemm": lambda: measure_prefill_gemm(torch, ug, inputs),
+              "vendor_int8_gemm": lambda: measure_vendor_gemm(torch, ug, inputs),
               "stream_m1": lambda: measure_stream_m1(torch, ug, inputs),
               "requant_pack5": lambda: measure_requant_pack5(torch, ug, inputs),
               "attention_decode": lambda: measure_attention_decode(torch, ug),
@@ -983,8 +1021,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
-    for k in ("prefill_gemm", "stream_m1", "requant_pack5", "attention_decode", "sampler",
-              "backward", "cpu_baseline"):
+    for k in ("prefill_gemm", "vendor_int8_gemm", "stream_m1", "requant_pack5",
+              "attention_decode", "sampler", "backward", "cpu_baseline"):
         if k in res:
             line[k] = res[k]
     print(json.dumps(line), flush=True)
