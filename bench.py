@@ -124,8 +124,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="decode_stack: skip the extra measurement points")
     p.add_argument("--only", default=None,
-                   choices=["prefill_gemm", "vendor_int8_gemm", "stream_m1", "requant_pack5",
-                            "attention_decode", "sampler", "backward"],
+                   choices=["prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
+                            "requant_pack5", "attention_decode", "sampler", "backward"],
                    help="run just this one of the decode_stack line's extra points and print "
                         "its JSON object (for profiling a single kernel)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -362,6 +362,8 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["vendor_int8_gemm"] = measure_vendor_gemm(torch, ug, inputs)
         torch.cuda.empty_cache()
+        out["hbm_copy_rate"] = measure_copy_rate(torch)
+        torch.cuda.empty_cache()
         out["stream_m1"] = measure_stream_m1(torch, ug, inputs)
         torch.cuda.empty_cache()
         out["requant_pack5"] = measure_requant_pack5(torch, ug, inputs)
@@ -454,6 +456,29 @@ def measure_vendor_gemm(torch, ug, inputs):
                 note="context only: the vendor library on the same operands, int32 output",
                 shapes=per_shape, median_launch_us=us,
                 frac_of_int8_peak=ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS)
+
+
+def measure_copy_rate(torch):
+    """Context, not this library: the HBM rate of a plain device-to-device
+    copy on this GPU (torch's copy_, 128 MiB read + 128 MiB written per call,
+    sources spanning >= 2 GiB cycled so every call reads cold); bytes read
+    plus written per second, the median over STAT_LAUNCHES calls."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    n = 128 << 20
+    n_copies = -(-COLD_BYTES // n) + 1
+    srcs = [torch.ones(n, dtype=torch.uint8, device=dev) for _ in range(n_copies)]
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    for i in range(2):
+        dst.copy_(srcs[i])
+    med, p10, p90 = launch_stats(torch, lambda i: dst.copy_(srcs[(i + 2) % n_copies]), stream)
+    res = dict(value=2 * n / (med * 1e-6) / 1e9, unit="GB/s", library="torch copy_",
+               note="context only: a vendor copy of 128 MiB per call (read + written), cold",
+               median_call_us=med, p10_call_us=p10, p90_call_us=p90,
+               frac_of_hbm_peak=2 * n / (med * 1e-6) / 1e9 / HBM_PEAK_GBS)
+    log("copy rate", res)
+    del srcs, dst
+    return res
 
 
 def measure_requant_pack5(torch, ug, inputs):
@@ -1006,6 +1031,7 @@ def main():
     if args.only is not None:
         fn = {"prefill_gemm": lambda: measure_prefill_gemm(torch, ug, inputs),
               "vendor_int8_gemm": lambda: measure_vendor_gemm(torch, ug, inputs),
+              "hbm_copy_rate": lambda: measure_copy_rate(torch),
               "stream_m1": lambda: measure_stream_m1(torch, ug, inputs),
               "requant_pack5": lambda: measure_requant_pack5(torch, ug, inputs),
               "attention_decode": lambda: measure_attention_decode(torch, ug),
@@ -1021,8 +1047,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
-    for k in ("prefill_gemm", "vendor_int8_gemm", "stream_m1", "requant_pack5",
-              "attention_decode", "sampler", "backward", "cpu_baseline"):
+    for k in ("prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
+              "requant_pack5", "attention_decode", "sampler", "backward", "cpu_baseline"):
         if k in res:
             line[k] = res[k]
     print(json.dumps(line), flush=True)

@@ -109,10 +109,27 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const float *__restrict_
   }
 }
 
+// fl(v / r) given y = fl(1 / r), without the division sequence: q0 = v y is
+// within an ulp of v / r, the residual v - q0 r is exact with a fused
+// multiply-add, and q0 + residual * y rounded once is the correctly rounded
+// quotient (Markstein's theorem on division by a correctly rounded
+// reciprocal).  Its conditions need v and the quotient in the normal range
+// away from overflow: outside [2^-80, 2^100] the division is done as
+// written.
+__device__ __forceinline__ float div_by(float v, float r, float y) {
+  const float q0 = v * y;
+  const float aq = fabsf(q0);
+  if (__builtin_expect(fabsf(v) >= 0x1p-80f && aq >= 0x1p-80f && aq <= 0x1p100f, 1))
+    return __builtin_fmaf(__builtin_fmaf(-q0, r, v), y, q0);
+  return v == 0.0f ? q0 : v / r;
+}
+
 // RMSNorm + quantization; one 256-thread block per row.  Thread t owns the
 // float4 slices f = t + 256 i, i.e. the elements k with floor(k/4) mod 256
-// = t, which it squares and adds from +0 in increasing k; fold256() then
-// folds the 256 slot sums in the documented order.
+// = t, which it squares and adds from +0 in increasing k.  The 256 slot
+// sums are folded in the documented order (fold256's: v_t + v_t+128, then
+// + (v_t+64 + v_t+192), then lanes t + h for h = 32 .. 1) by every wave
+// itself, which takes lane 0's bits: one barrier instead of four.
 template <int VPT>
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const float *__restrict__ x, int64_t ldx,
                                                             const float *__restrict__ g, int64_t M,
@@ -120,6 +137,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const float *__restr
                                                             int8_t *__restrict__ xq, int64_t ldq,
                                                             float *__restrict__ s) {
   __shared__ float lds[256];
+  __shared__ float red[4];
   const int t = threadIdx.x;
   const int64_t m = blockIdx.x;
   const float *xr = x + m * ldx;
@@ -160,16 +178,26 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const float *__restr
     }
   }
   // Masked lanes contribute +0 (0*0), which leaves a sum >= +0 unchanged.
-  const float T = fold256(acc, lds);
+  lds[t] = acc;
+  __syncthreads();
+  const int lane = t & 63;
+  float u = (lds[lane] + lds[lane + 128]) + (lds[lane + 64] + lds[lane + 192]);
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const float o = __shfl_down(u, h, 64);
+    u = u + o;
+  }
+  const float T = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), 0));
   const float ms = T / (float)K;
   const float r = sqrtf(ms + eps_n);
+  const float y = 1.0f / r;
 
   auto norm4 = [&](float4 u, int64_t k) {
     float4 o;
-    o.x = u.x / r;
-    o.y = u.y / r;
-    o.z = u.z / r;
-    o.w = u.w / r;
+    o.x = div_by(u.x, r, y);
+    o.y = div_by(u.y, r, y);
+    o.z = div_by(u.z, r, y);
+    o.w = div_by(u.w, r, y);
     if (g) {
       // g holds exactly K floats: no vector read past its end.
       float4 gg;
@@ -204,9 +232,9 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(const float *__restr
       a = fmaxf(a, amax4(norm4(mask4(ld4(xr + 4 * f), 4 * f, K), 4 * f)));
   }
   a = wave_max(a);
-  if ((t & 63) == 0) lds[t >> 6] = a;
+  if ((t & 63) == 0) red[t >> 6] = a;
   __syncthreads();
-  a = fmaxf(fmaxf(lds[0], lds[1]), fmaxf(lds[2], lds[3]));
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float a127 = a / 127.0f;
   const float sc = a127 + eps;
   if (t == 0) s[m] = sc;

@@ -235,10 +235,40 @@ def test_grouped_many_problems_multi_item_blocks(dev):
     plan = ug.ug_gemv_plan_init(probs)
     assert plan.info.grid < plan.info.total_items
     ug.ug_bitlinear_gemv_grouped(plan)
-    for i in (0, 17, G - 1):
+    for i in range(G):
         xq_r, s_r = oracle.quant_act(xs[i])
         y_r = oracle.epilogue(oracle.matmul_i32(xq_r, wq), s_r, np.float32(0.02))
         assert_bits_equal(host(probs[i]["y"]), y_r, "y %d" % i)
+
+
+def test_grouped_stream_uneven_problems(dev):
+    """Stream-split block ranges are cut by cost (weight bytes plus a set-up
+    per problem a block enters), so blocks start and end at uneven places:
+    problems of very different sizes (1 item to hundreds), some blocks
+    crossing several problems, every output checked.  (The 21000-long rows
+    have more steps than the fine split takes per item: the stream split
+    runs.)"""
+    rng = np.random.default_rng(305)
+    shapes = [(6912, 2560), (16, 384), (40, 77), (2560, 6912), (33, 5), (4096, 1536),
+              (100, 2560), (1, 1), (6912, 2560), (512, 21000)]
+    probs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        x = rng.standard_normal((1, K), dtype=np.float32)
+        xq_r, s_r = oracle.quant_act(x)
+        beta = np.float32(0.02 + 0.001 * i)
+        probs.append(dict(xq=pitched(xq_r), s=vec(s_r), w=pitched(oracle.pack_trits(wq)[0]),
+                          wfmt=ug.UG_W_PACK5, beta=scalar_dev(beta), K=K,
+                          y=ug.empty_pitched(1, N, torch.float32, dev),
+                          acc=ug.empty_pitched(1, N, torch.int32, dev)))
+        acc_r = oracle.matmul_i32(xq_r, wq)
+        refs.append((acc_r, oracle.epilogue(acc_r, s_r, beta)))
+    plan = ug.ug_gemv_plan_init(probs)
+    assert (plan.info.variant >> 8) & 1 == 0, "stream split expected"
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for i, (p, (acc_r, y_r)) in enumerate(zip(probs, refs)):
+        assert_bits_equal(host(p["acc"]), acc_r, "acc %d" % i)
+        assert_y_close(host(p["y"]), y_r, "y %d" % i)
 
 
 def test_grouped_plan_rejects(dev):

@@ -22,7 +22,9 @@ def _print_case(*a):
 # activation quantization
 # ---------------------------------------------------------------------------
 ACT_SHAPES = [(32, 128), (1, 384), (1, 1536), (7, 13), (3, 1), (5, 4097), (3, 40000),
-              (64, 6912), (513, 2560), (2, 1024), (9, 1023)]
+              (64, 6912), (513, 2560), (2, 1024), (9, 1023),
+              # rows walked several per block, the next row's loads in flight
+              (1700, 6912), (900, 3001), (1540, 1025), (770, 8192), (769, 8193)]
 
 
 @pytest.mark.parametrize("M,K", ACT_SHAPES)
@@ -99,7 +101,8 @@ def test_quant_act_rows_independent(dev):
 # ---------------------------------------------------------------------------
 # RMSNorm + quantization
 # ---------------------------------------------------------------------------
-RMS_SHAPES = [(4, 2560), (3, 6912), (5, 1001), (2, 9000), (6, 1), (8, 384), (2048, 2560)]
+RMS_SHAPES = [(4, 2560), (3, 6912), (5, 1001), (2, 9000), (6, 1), (8, 384), (2048, 2560),
+              (1600, 6912), (800, 3001), (1540, 1025), (769, 8192)]
 
 
 @pytest.mark.parametrize("M,K", RMS_SHAPES)
@@ -117,6 +120,30 @@ def test_rmsnorm_quant_parity(dev, M, K, with_gain):
     xq_r, s_r = oracle.rmsnorm_quant_act(x, g)
     assert_bits_equal(host(s_d), s_r, "s")
     assert_bits_equal(host(xq_d), xq_r, "x_q")
+
+
+def test_rmsnorm_quant_extreme_rows(dev):
+    """RMSNorm's division x / r runs as a corrected product with 1 / r where
+    quotient and input are normal, and as the division itself elsewhere:
+    rows whose values, sums of squares or quotients are tiny, huge, subnormal,
+    zero or overflowing must give the oracle's bits either way (900 rows:
+    several per block)."""
+    rng = np.random.default_rng(103)
+    M, K = 900, 2560
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    scales = [1e-30, 1e-20, 1e-12, 1e12, 1e18, 1e19, 1e20, 1e30, 1e-38, 3e-39, 0.0]
+    for i, sc in enumerate(scales):
+        x[7 * i] *= np.float32(sc)
+    x[100, ::3] = 0.0
+    x[101, :5] = np.float32(1e25)
+    x[102, 7] = np.float32(3e-45)
+    g = np.float32(1) + rng.standard_normal(K, dtype=np.float32) * np.float32(0.1)
+    with np.errstate(over="ignore", under="ignore"):
+        for gain in (None, g):
+            xq_d, s_d = ug.ug_rmsnorm_quant_act(pitched(x), vec(gain) if gain is not None else None)
+            xq_r, s_r = oracle.rmsnorm_quant_act(x, gain)
+            assert_bits_equal(host(s_d), s_r, "s")
+            assert_bits_equal(host(xq_d), xq_r, "x_q")
 
 
 # ---------------------------------------------------------------------------
