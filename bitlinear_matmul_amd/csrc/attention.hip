@@ -70,23 +70,37 @@ __global__ __launch_bounds__(64) void attn_partial(const float *__restrict__ q, 
     qv[i] = d < DH ? qr[d] : 0.0f;
   }
 
-  // Scores: lane l's partial products of every key, transposed through LDS
-  // so that lane t then adds key t's 64 partials in lane order.
+  // Loads in flight together when d_h <= 128: every key row of the chunk,
+  // and the first 32 value rows, which do not depend on the scores.  (With
+  // d_h = 256 the registers hold 32 key rows, then 32 value rows.)
+  constexpr bool kWide = R <= 2;
+  constexpr int KB = kWide ? kChunk : kBatch;
   const float *kbase = kc + (int64_t)j0 * ldk + h * DH;
-  for (int b0 = 0; b0 < kChunk; b0 += kBatch) {
-    if (b0 >= nk) break;  // wave-uniform
-    float kv[kBatch][R];
+  const float *vbase = vc + (int64_t)j0 * ldv + h * DH;
+  auto load_rows = [&](const float *base, int64_t ld, int b0, auto &dst)
+                       __attribute__((always_inline)) {
+    constexpr int n = sizeof(dst) / sizeof(dst[0]);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = 0; u < n; ++u) {
       const bool ok = b0 + u < nk;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int d = lane + 64 * i;
-        kv[u][i] = ok && d < DH ? kbase[(int64_t)(b0 + u) * ldk + d] : 0.0f;
+        dst[u][i] = ok && d < DH ? base[(int64_t)(b0 + u) * ld + d] : 0.0f;
       }
     }
+  };
+  float kv[KB][R], vv[kBatch][R];
+  load_rows(kbase, ldk, 0, kv);
+  if (kWide) load_rows(vbase, ldv, 0, vv);
+
+  // Scores: lane l's partial products of every key, transposed through LDS
+  // so that lane t then adds key t's 64 partials in lane order.
+  for (int b0 = 0; b0 < kChunk; b0 += KB) {
+    if (b0 >= nk) break;  // wave-uniform
+    if (b0 > 0) load_rows(kbase, ldk, b0, kv);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = 0; u < KB; ++u) {
       float a = 0.0f;
 #pragma unroll
       for (int i = 0; i < R; ++i) a = a + qv[i] * kv[u][i];
@@ -108,23 +122,13 @@ __global__ __launch_bounds__(64) void attn_partial(const float *__restrict__ q, 
   for (int hh = 32; hh >= 1; hh >>= 1) lc = lc + __shfl_xor(lc, hh, 64);
   __syncthreads();  // p_j are in LDS
 
-  // unnormalized context
+  // unnormalized context, keys in order
   float o[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) o[i] = 0.0f;
-  const float *vbase = vc + (int64_t)j0 * ldv + h * DH;
   for (int b0 = 0; b0 < kChunk; b0 += kBatch) {
     if (b0 >= nk) break;
-    float vv[kBatch][R];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const bool ok = b0 + u < nk;
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int d = lane + 64 * i;
-        vv[u][i] = ok && d < DH ? vbase[(int64_t)(b0 + u) * ldv + d] : 0.0f;
-      }
-    }
+    if (b0 > 0 || !kWide) load_rows(vbase, ldv, b0, vv);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       if (b0 + u < nk) {
