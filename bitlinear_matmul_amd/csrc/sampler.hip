@@ -10,18 +10,19 @@
 //   1. every logit becomes an order-preserving 32-bit key (larger logit,
 //      larger key; -0 and +0 the same);
 //   2. four passes of an 8-bit radix select (an LDS histogram of the
-//      digit among the keys that match the digits chosen so far, then a
-//      suffix scan) find the k-th largest key t and how many of the kept
-//      keys equal t;
-//   3. a block scan places every key above t, then the lowest-index keys
-//      equal to t, in LDS as (key, ~index) pairs;
-//   4. a 256-wide bitonic sort orders them (larger logit first, equal
-//      logits by lower index);
+//      digit among the keys that match the digits chosen so far; one wave
+//      scans it from the top digit down) find the k-th largest key t and
+//      how many of the kept keys equal t;
+//   3. one block scan places every key above t, then the lowest-index keys
+//      equal to t, in LDS as (key, ~index) pairs: k distinct 64-bit values;
+//   4. each kept pair's rank is the number of kept pairs above it (larger
+//      logit first, equal logits by lower index), and it moves to that slot;
 //   5. rank r gets the weight e_r = expf(fl(fl(l_r - l_1) / T)); an
 //      inclusive fp32 scan in one fixed order gives C_r; the token is rank
 //      min(#{r : C_r <= fl(u * C_k)}, k - 1).
-// Rows of at most 4096 logits stay in registers (16 per thread) between the
-// passes; longer rows are read again from memory (L2) for each pass.
+// Sixteen block barriers in all.  Rows of at most 4096 logits stay in
+// registers (16 per thread) between the passes; longer rows are read again
+// from memory (L2) for each pass.
 #include "ug_internal.h"
 
 namespace ug {
@@ -64,13 +65,15 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
     const float *__restrict__ u, int32_t *__restrict__ tok, int32_t *__restrict__ idx_out,
     int64_t ldi, float *__restrict__ val_out, int64_t ldv, float *__restrict__ prob_out,
     int64_t ldp) {
-  __shared__ int hist[256];
+  __shared__ int hist[2][256];  // pass p counts into hist[p % 2]
   __shared__ int iws[4];
   __shared__ float fws[4];
-  __shared__ unsigned long long sel[kThreads];
+  __shared__ unsigned long long lws[4];
+  __shared__ unsigned long long sel[kThreads];  // kept pairs, in index order
+  __shared__ unsigned long long srt[kThreads];  // kept pairs, by rank
   __shared__ uint32_t s_digit;
   __shared__ int s_above;
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *row = logits + (int64_t)b * ld;
   const int per = (V + kThreads - 1) / kThreads;  // this thread: [tid * per, tid * per + per)
   const int i0 = tid * per;
@@ -95,42 +98,59 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
     }
   };
 
-  // radix select of the k-th largest key
+  // radix select of the k-th largest key.  Pass p counts into hist[p % 2]
+  // (cleared during pass p - 1, after every read of pass p - 2); wave 0
+  // then finds the digit: lane l holds the counts of digits 255 - 4 l ..
+  // 252 - 4 l, and a scan over the lanes gives, for each digit, the number
+  // of matching keys whose digit is at least it.
+  hist[0][tid] = 0;
+  hist[1][tid] = 0;
+  __syncthreads();
   uint32_t prefix = 0, pmask = 0;
   int need = k;  // keys still to keep among those matching the prefix
-  for (int sh = 24; sh >= 0; sh -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int sh = 24 - 8 * p;
+    int *H = hist[p & 1];
     each([&](int, uint32_t key) __attribute__((always_inline)) {
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & 255], 1);
+      if ((key & pmask) == prefix) atomicAdd(&H[(key >> sh) & 255], 1);
     });
     __syncthreads();
-    const int h = hist[255 - tid];  // digits from the top
-    int tot;
-    const int ge = block_scan(h, iws, &tot);  // keys whose digit is >= 255 - tid
-    if (ge >= need && ge - h < need) {
-      s_digit = (uint32_t)(255 - tid);
-      s_above = ge - h;
+    if (wave == 0) {
+      const int c0 = H[255 - 4 * lane], c1 = H[254 - 4 * lane], c2 = H[253 - 4 * lane],
+                c3 = H[252 - 4 * lane];
+      const int t3 = c0 + c1 + c2 + c3;
+      int incl = t3;  // inclusive scan of the lane totals
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const int ge0 = incl - t3 + c0, ge1 = ge0 + c1, ge2 = ge1 + c2, ge3 = ge2 + c3;
+      // the digit where the count of keys at or above it first reaches need
+      if (ge0 >= need && ge0 - c0 < need) { s_digit = 255 - 4 * lane; s_above = ge0 - c0; }
+      if (ge1 >= need && ge1 - c1 < need) { s_digit = 254 - 4 * lane; s_above = ge1 - c1; }
+      if (ge2 >= need && ge2 - c2 < need) { s_digit = 253 - 4 * lane; s_above = ge2 - c2; }
+      if (ge3 >= need && ge3 - c3 < need) { s_digit = 252 - 4 * lane; s_above = ge3 - c3; }
     }
+    hist[(p + 1) & 1][tid] = 0;
     __syncthreads();
     prefix |= s_digit << sh;
     pmask |= 0xffu << sh;
     need -= s_above;
-    __syncthreads();
   }
   const uint32_t t = prefix;  // the k-th largest key; `need` kept keys equal it
 
-  // compaction: keys above t, then the lowest-index keys equal to t
-  int cg = 0, ce = 0;
+  // compaction: keys above t, then the lowest-index keys equal to t (one
+  // scan of both counts, packed in 32-bit halves)
+  unsigned long long cnt = 0;
   each([&](int, uint32_t key) __attribute__((always_inline)) {
-    cg += key > t;
-    ce += key == t;
+    cnt += key > t ? (1ull << 32) : (key == t ? 1ull : 0ull);
   });
-  int gtot, etot;
-  int pg = block_scan(cg, iws, &gtot) - cg;
-  int pe = block_scan(ce, iws, &etot) - ce;
-  sel[tid] = 0ull;  // padding sorts last
-  __syncthreads();
+  unsigned long long tot;
+  const unsigned long long ex = block_scan(cnt, lws, &tot) - cnt;
+  const int gtot = (int)(tot >> 32);
+  int pg = (int)(ex >> 32), pe = (int)(ex & 0xffffffffu);
   each([&](int i, uint32_t key) __attribute__((always_inline)) {
     const unsigned long long c = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)i;
     if (key > t) {
@@ -142,32 +162,28 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
   });
   __syncthreads();
 
-  // bitonic sort of the 256 slots, largest first
-  for (int size = 2; size <= kThreads; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int p = tid ^ stride;
-      if (p > tid) {
-        const unsigned long long a = sel[tid], c = sel[p];
-        const bool desc = (tid & size) == 0;
-        if (desc ? a < c : a > c) {
-          sel[tid] = c;
-          sel[p] = a;
-        }
-      }
-      __syncthreads();
-    }
+  // rank of each kept pair = how many kept pairs are larger (all distinct)
+  if (tid < k) {
+    const unsigned long long c = sel[tid];
+    int r = 0;
+    for (int j = 0; j < k; ++j) r += sel[j] > c;
+    srt[r] = c;
   }
+  __syncthreads();
 
   // weights, their running sum and the draw
-  const unsigned long long mine = sel[tid];
-  const float l1 = key_logit((uint32_t)(sel[0] >> 32));
+  const unsigned long long mine = tid < k ? srt[tid] : 0ull;
+  const float l1 = key_logit((uint32_t)(srt[0] >> 32));
   const float lr = key_logit((uint32_t)(mine >> 32));
   const float e = tid < k ? expf((lr - l1) / temp) : 0.0f;
   float total;
   const float C = block_scan(e, fws, &total);
   const float thr = u[b] * total;
-  int below;
-  block_scan((int)(tid < k && C <= thr), iws, &below);
+  // #{r < k : C_r <= thr}: a ballot per wave
+  const unsigned long long bal = __ballot(tid < k && C <= thr);
+  if (lane == 0) iws[wave] = __popcll(bal);
+  __syncthreads();
+  const int below = ((iws[0] + iws[1]) + iws[2]) + iws[3];
   const int pick = min(below, k - 1);
   if (tid == pick) tok[b] = (int32_t)~(uint32_t)mine;
   if (tid < k) {
