@@ -150,38 +150,38 @@ TRAFFIC = {
     # it was taken on are unchanged.
     # profiles/gemv_fine_grouped_decode_stack.md: 2005.9 KiB / 146.4 KiB
     "decode_stack": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                              "35eb904b607e06ad24ca802271d2559fb2433d6e7ceb0bf5c5df246c1d6c0f87"},
+                              "7a2a5f082270679451eb78a55b2654e6cfb9c9f87e57826f311ea449d1cebe2b"},
                          bytes_per_launch=4257560),
     # profiles/gemv_stream_grouped_sweep_m1.md: M=1 2560->6912, 37 problems per
-    # launch: 64227.3 KiB / 718.1 KiB
+    # launch: 64207.5 KiB / 189.2 KiB
     "sweep": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                       "35eb904b607e06ad24ca802271d2559fb2433d6e7ceb0bf5c5df246c1d6c0f87"},
-                  bytes_per_launch=132256303),
+                       "7a2a5f082270679451eb78a55b2654e6cfb9c9f87e57826f311ea449d1cebe2b"},
+                  bytes_per_launch=131674036),
     # profiles/gemm_i8_large_prefill.md: mean of the two shapes' launches
     "prefill": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
                          "06fc5d4c90ea64594662b948395ad6f927f071c6413aa61d83a191b11e6da732"},
-                    bytes_per_launch=200755282),
+                    bytes_per_launch=200752914),
     # profiles/gemm_i8_large_stack.md: mean of the two shapes' launches
     "stack": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
                        "06fc5d4c90ea64594662b948395ad6f927f071c6413aa61d83a191b11e6da732"},
-                  bytes_per_launch=143289344),
+                  bytes_per_launch=143235735),
     # profiles/absmean_ternary_pack5_requant.md: stage 1 + fused pass per call
     "requant_pack5": dict(src={"bitlinear_matmul_amd/csrc/absmean.hip":
                                "a69523d80a0c82173d06857320485e02857481b5810e490f22fae63e67d95234"},
                           bytes_per_launch=145415161),
     # profiles/attention_decode_4096.md: partials + combine per call
     "attention_decode": dict(src={"bitlinear_matmul_amd/csrc/attention.hip":
-                                  "7e8669c58e2a560ba3cf2cf121f5b634fa8e6f54d005e3178610c944a7eff0fd"},
-                             bytes_per_launch=85623294),
+                                  "fa6c1f4c0af1f44b7f2da103fb678c0d8dd15aa5fb0a245bb6e4e8370b73e5d3"},
+                             bytes_per_launch=85715442),
     # profiles/topk_sample_batch4096.md: the 4096-row launch
     "sampler": dict(src={"bitlinear_matmul_amd/csrc/sampler.hip":
-                         "eb3e8dfbe3e23ec5170cbb7bcc4453c73935223a4d1f85c2f08e3d12e0272f30"},
-                    bytes_per_launch=67809093),
+                         "c2356558fa3c0bdd51c48a1856637ec73dc6367ed023dfad628ded49e7468d6e"},
+                    bytes_per_launch=67728143),
     # profiles/gemm_f32_backward.md: mean of the dx call (GEMM + slab sum) and
     # the dW call
     "backward": dict(src={"bitlinear_matmul_amd/csrc/backward.hip":
                           "f681a6da409af86df1788e520aea31319f073d37630bca2cbe2786a31b629458"},
-                     bytes_per_launch=800887323),
+                     bytes_per_launch=801258028),
 }
 
 
