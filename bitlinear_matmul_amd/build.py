@@ -69,7 +69,9 @@ def build_lib(src_dir, out, verbose=False):
                 sys.stderr.write(r.stdout + r.stderr)
                 raise RuntimeError("hipcc failed compiling " + os.path.basename(obj))
         tmp = out + ".tmp%d" % os.getpid()
-        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC",
+        # -z defs: a symbol left undefined (say a kernel whose launch stub
+        # the host pass did not emit) fails the link instead of the load
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,-z,defs",
                *[o for o, _ in results], "-o", tmp]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
