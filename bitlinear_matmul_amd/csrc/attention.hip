@@ -12,20 +12,24 @@
 // chunks of 64 so that one query row still spreads over the chip
 // ("flash-decoding"): attn_partial, one wave per (chunk, head, row), computes
 // the chunk's score maximum m_c, its sum l_c of exp(score - m_c) and its
-// unnormalized context o_c, with no barrier and 17 KB of LDS, so that a
-// decode step at 4096 positions with 20 heads is 1280 small blocks resident
-// at once; attn_combine rescales the chunks to their common maximum and
+// unnormalized context o_c, with no barrier and at most 17 KB of LDS, so
+// that a decode step at 4096 positions with 20 heads is 1280 small blocks
+// resident at once; every cache load moves 1 KB (16 bytes a lane: 256 / d_h
+// rows).  attn_combine rescales the chunks to their common maximum and
 // divides.  Every reduction has one fixed order, the same for every query
 // row whatever the number of rows in the call, so row t of a call over many
 // rows is bit for bit the single-row call at position t:
-//   score_j = fl(dot_j / fl(sqrt(d_h))), dot_j = the 64 lane partials added
-//             in lane order, lane l's partial = its dims l, l+64, ... added
-//             in that order from +0;
+//   score_j = fl(dot_j / fl(sqrt(d_h))), dot_j = the d_h / 4 partials
+//             of dims 4i .. 4i+3 (each the four products added in dim
+//             order from +0) added in order of i from +0;
 //   m_c     = max over the chunk (exact);
 //   p_j     = expf(score_j - m_c);
 //   l_c     = the 64 p_j summed by a butterfly (lane l adds lane l ^ h for
 //             h = 32, 16, ..., 1: every lane ends with the same bits);
-//   o_c[d]  = the chunk's fl(p_j v_jd) added in key order from +0;
+//   o_c[d]  = with R = 256 / d_h rows per 1 KB load: for each r < R the
+//             chunk's fl(p_j v_jd) over keys j = r mod R added in key order
+//             from +0, then the R sums folded pairwise (sum r takes sum
+//             r + R/2, then r + R/4, ...);
 //   out[d]  = fl(o[d] / l) with M = max_c m_c, e_c = expf(m_c - M);
 //             for w = 0..3, l_w = sum of fl(e_c l_c) and o_w[d] = sum of
 //             fl(e_c o_c[d]) over the chunks c = w, w+4, w+8, ... added in
@@ -41,8 +45,12 @@ constexpr int kBatch = 32;  // keys whose loads travel together
 
 template <int DH>
 struct AttnDims {
-  static constexpr int R = DH >= 64 ? DH / 64 : 1;  // dims per lane
+  static constexpr int R = DH >= 64 ? DH / 64 : 1;  // dims per lane in the combine
   static constexpr int kRec = DH + 4;               // floats per partial: o[DH], m, l, pad
+  // partials: lane l holds dims 4 (l % LPR) .. + 3 of row l / LPR of a
+  // load, which moves RPI key or value rows (1 KB)
+  static constexpr int LPR = DH / 4;
+  static constexpr int RPI = 64 / LPR;
 };
 
 template <int DH>
@@ -51,65 +59,61 @@ __global__ __launch_bounds__(64) void attn_partial(const float *__restrict__ q, 
                                                    const float *__restrict__ vc, int64_t ldv,
                                                    int pos0, int H, int nck, float root,
                                                    float *__restrict__ part) {
-  constexpr int R = AttnDims<DH>::R;
+  constexpr int LPR = AttnDims<DH>::LPR, RPI = AttnDims<DH>::RPI;
   const int c = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
   const int p = pos0 + m;  // the row's position: it sees keys 0 .. p
   const int j0 = c * kChunk;
   if (j0 > p) return;  // a chunk wholly after the row's position
   const int nk = min(kChunk, p + 1 - j0);  // keys of the chunk the row sees
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x, col = lane % LPR, sub = lane / LPR;
 
-  __shared__ float T[64 * 65];  // key partials, transposed (odd pitch: no bank conflicts)
+  __shared__ float T[LPR * 65];  // key partials, transposed (odd pitch: no bank conflicts)
   __shared__ float pw[kChunk];
 
-  float qv[R];
-  const float *qr = q + (int64_t)m * ldq + h * DH;
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int d = lane + 64 * i;
-    qv[i] = d < DH ? qr[d] : 0.0f;
-  }
+  const float4 q4 = *reinterpret_cast<const float4 *>(q + (int64_t)m * ldq + h * DH + 4 * col);
 
   // Loads in flight together when d_h <= 128: every key row of the chunk,
   // and the first 32 value rows, which do not depend on the scores.  (With
   // d_h = 256 the registers hold 32 key rows, then 32 value rows.)
-  constexpr bool kWide = R <= 2;
+  constexpr bool kWide = DH <= 128;
   constexpr int KB = kWide ? kChunk : kBatch;
-  const float *kbase = kc + (int64_t)j0 * ldk + h * DH;
-  const float *vbase = vc + (int64_t)j0 * ldv + h * DH;
+  const float *kbase = kc + (int64_t)j0 * ldk + h * DH + 4 * col;
+  const float *vbase = vc + (int64_t)j0 * ldv + h * DH + 4 * col;
+  // row b0 + RPI u + sub of the chunk for u < n (zeros past the keys the row sees)
   auto load_rows = [&](const float *base, int64_t ld, int b0, auto &dst)
                        __attribute__((always_inline)) {
     constexpr int n = sizeof(dst) / sizeof(dst[0]);
 #pragma unroll
     for (int u = 0; u < n; ++u) {
-      const bool ok = b0 + u < nk;
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int d = lane + 64 * i;
-        dst[u][i] = ok && d < DH ? base[(int64_t)(b0 + u) * ld + d] : 0.0f;
-      }
+      const int j = b0 + RPI * u + sub;
+      dst[u] = j < nk ? *reinterpret_cast<const float4 *>(base + (int64_t)j * ld)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  float kv[KB][R], vv[kBatch][R];
+  float4 kv[KB / RPI], vv[kBatch / RPI];
   load_rows(kbase, ldk, 0, kv);
   if (kWide) load_rows(vbase, ldv, 0, vv);
 
-  // Scores: lane l's partial products of every key, transposed through LDS
-  // so that lane t then adds key t's 64 partials in lane order.
+  // Scores: lane l's partial product of its four dims with every key it
+  // holds, transposed through LDS so that lane t then adds key t's LPR
+  // partials in dimension order.
   for (int b0 = 0; b0 < kChunk; b0 += KB) {
     if (b0 >= nk) break;  // wave-uniform
     if (b0 > 0) load_rows(kbase, ldk, b0, kv);
 #pragma unroll
-    for (int u = 0; u < KB; ++u) {
+    for (int u = 0; u < KB / RPI; ++u) {
       float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < R; ++i) a = a + qv[i] * kv[u][i];
-      T[lane * 65 + b0 + u] = a;
+      a = a + q4.x * kv[u].x;
+      a = a + q4.y * kv[u].y;
+      a = a + q4.z * kv[u].z;
+      a = a + q4.w * kv[u].w;
+      T[col * 65 + b0 + RPI * u + sub] = a;
     }
   }
   __syncthreads();  // (one wave) the transposed partials are in LDS
   float dot = 0.0f;
-  for (int l = 0; l < 64; ++l) dot = dot + T[l * 65 + lane];
+#pragma unroll 8
+  for (int l = 0; l < LPR; ++l) dot = dot + T[l * 65 + lane];
   const bool valid = lane < nk;
   const float s = dot / root;
 
@@ -122,28 +126,34 @@ __global__ __launch_bounds__(64) void attn_partial(const float *__restrict__ q, 
   for (int hh = 32; hh >= 1; hh >>= 1) lc = lc + __shfl_xor(lc, hh, 64);
   __syncthreads();  // p_j are in LDS
 
-  // unnormalized context, keys in order
-  float o[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) o[i] = 0.0f;
+  // unnormalized context: each lane adds fl(p_j v_jd) over its rows j (those
+  // with j % RPI = sub) in increasing j from +0; then the RPI row partials
+  // of each dim are folded (lane l takes lane l + f for f = 32, 16, .., LPR)
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int b0 = 0; b0 < kChunk; b0 += kBatch) {
     if (b0 >= nk) break;
     if (b0 > 0 || !kWide) load_rows(vbase, ldv, b0, vv);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (b0 + u < nk) {
-        const float w = pw[b0 + u];
-#pragma unroll
-        for (int i = 0; i < R; ++i) o[i] = o[i] + w * vv[u][i];
+    for (int u = 0; u < kBatch / RPI; ++u) {
+      const int j = b0 + RPI * u + sub;
+      if (j < nk) {
+        const float w = pw[j];
+        o.x = o.x + w * vv[u].x;
+        o.y = o.y + w * vv[u].y;
+        o.z = o.z + w * vv[u].z;
+        o.w = o.w + w * vv[u].w;
       }
     }
   }
-  float *rec = part + (((int64_t)m * H + h) * nck + c) * AttnDims<DH>::kRec;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int d = lane + 64 * i;
-    if (d < DH) rec[d] = o[i];
+  for (int f = 32; f >= LPR; f >>= 1) {
+    o.x = o.x + __shfl_down(o.x, f, 64);
+    o.y = o.y + __shfl_down(o.y, f, 64);
+    o.z = o.z + __shfl_down(o.z, f, 64);
+    o.w = o.w + __shfl_down(o.w, f, 64);
   }
+  float *rec = part + (((int64_t)m * H + h) * nck + c) * AttnDims<DH>::kRec;
+  if (lane < LPR) *reinterpret_cast<float4 *>(rec + 4 * col) = o;
   if (lane == 0) {
     rec[DH] = mc;
     rec[DH + 1] = lc;

@@ -36,15 +36,16 @@ def _inputs(seed, T, H, dh, M):
 
 def _bound(q, k, v, pos0, H):
     """Per-element error bound of the fp32 kernels against exact attention.
-    A score is a sum of dh products (lane partials of dh/64 terms, then 64
-    lane partials in order: at most dh + 64 roundings) and one division:
-    |d score_j| <= E_j = gamma(dh + 66) * sum_d |q_d k_jd| / sqrt(dh).  A
-    weight a_j = e^{s_j} / sum e^{s_i} then moves by at most 2 max_j E_j
-    relative, plus the roundings of its exp (two, with the chunk rescale),
-    of the sums (64 keys in order within a chunk, up to 16 chunks in order
-    per wave of the combine, then two levels)
-    and of the products: at most 256 u relative to sum_j a_j |v_jd| all
-    told.  So |out_d - exact_d| <= (2 max E + 256 u) sum_j a_j |v_jd|."""
+    A score is a sum of dh products (partials of 4 products, then dh/4
+    partials in order: at most dh + dh/4 <= dh + 64 roundings) and one
+    division: |d score_j| <= E_j = gamma(dh + 66) * sum_d |q_d k_jd| /
+    sqrt(dh).  A weight a_j = e^{s_j} / sum e^{s_i} then moves by at most
+    2 max_j E_j relative, plus the roundings of its exp (two, with the chunk
+    rescale), of the sums (at most 64 keys in order within a chunk and a
+    fold of at most 8 row sums, up to 16 chunks in order per wave of the
+    combine, then two levels) and of the products: at most 256 u relative
+    to sum_j a_j |v_jd| all told.  So |out_d - exact_d| <=
+    (2 max E + 256 u) sum_j a_j |v_jd|."""
     M, HD = q.shape
     dh = HD // H
     tol = np.empty((M, HD))
