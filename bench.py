@@ -171,8 +171,8 @@ TRAFFIC = {
                           bytes_per_launch=145415161),
     # profiles/attention_decode_4096.md: partials + combine per call
     "attention_decode": dict(src={"bitlinear_matmul_amd/csrc/attention.hip":
-                                  "fa6c1f4c0af1f44b7f2da103fb678c0d8dd15aa5fb0a245bb6e4e8370b73e5d3"},
-                             bytes_per_launch=85715442),
+                                  "f500bc9a3ea52e5381ee0eb6127bc07c780c232a6b8544270ba3575ae71151a3"},
+                             bytes_per_launch=85548551),
     # profiles/topk_sample_batch4096.md: the 4096-row launch
     "sampler": dict(src={"bitlinear_matmul_amd/csrc/sampler.hip":
                          "c2356558fa3c0bdd51c48a1856637ec73dc6367ed023dfad628ded49e7468d6e"},
