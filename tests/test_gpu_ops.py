@@ -178,6 +178,26 @@ def test_absmean_pitched_input(dev):
     assert_bits_equal(host(wq_d), wq_r, "W_q")
 
 
+def test_absmean_one_read_limits_and_shared_workspace(dev):
+    """Contiguous tensors of at most 12 chunks of 8192 per CU are read once
+    (one cooperative launch holds them on chip); larger ones take two
+    launches.  Both sides of that limit on a 256-CU part (25,165,824
+    elements), and back-to-back calls that share one workspace (chunk sums
+    of the previous call still cached): every beta and W_q bit-exact."""
+    rng = np.random.default_rng(106)
+    dev_ = torch.device("cuda:0")
+    ws = torch.empty(ug.ug_quant_weight_absmean_workspace_size(6145, 4096), dtype=torch.uint8,
+                     device=dev_)
+    for (N, K) in [(6144, 4096), (6145, 4096), (2560, 6912), (6912, 2560), (384, 1152)]:
+        _print_case("absmean shared ws", N, K)
+        W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+        W[rng.integers(0, N), :] *= np.float32(30.0)
+        wq_d, beta_d = ug.ug_quant_weight_absmean(pitched(W), ws=ws)
+        wq_r, beta_r = oracle.quant_weight_absmean(W)
+        assert_bits_equal(host(beta_d), np.array([beta_r], np.float32), "beta %dx%d" % (N, K))
+        assert_bits_equal(host(wq_d), wq_r, "W_q %dx%d" % (N, K))
+
+
 def test_absmean_special_cases(dev):
     # 2^25 ones: exact 2^25 in the fixed order
     W = torch.ones((4096, 8192), dtype=torch.float32, device="cuda:0")
