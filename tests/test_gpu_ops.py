@@ -179,11 +179,10 @@ def test_absmean_pitched_input(dev):
 
 
 def test_absmean_one_read_limits_and_shared_workspace(dev):
-    """Contiguous tensors of at most 12 chunks of 8192 per CU are read once
-    (one cooperative launch holds them on chip); larger ones take two
-    launches.  Both sides of that limit on a 256-CU part (25,165,824
-    elements), and back-to-back calls that share one workspace (chunk sums
-    of the previous call still cached): every beta and W_q bit-exact."""
+    """Back-to-back calls that share one workspace (the previous call's
+    chunk sums still there), over tensors of 25,165,824 elements (3072
+    chunks of 8192) and one more row, and the 2B-class shapes: every beta
+    and W_q bit-exact."""
     rng = np.random.default_rng(106)
     dev_ = torch.device("cuda:0")
     ws = torch.empty(ug.ug_quant_weight_absmean_workspace_size(6145, 4096), dtype=torch.uint8,
