@@ -125,7 +125,8 @@ def parse():
                    help="decode_stack: skip the extra measurement points")
     p.add_argument("--only", default=None,
                    choices=["prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
-                            "requant_pack5", "attention_decode", "sampler", "backward"],
+                            "pack", "requant_pack5", "attention_decode", "sampler",
+                            "backward"],
                    help="run just this one of the decode_stack line's extra points and print "
                         "its JSON object (for profiling a single kernel)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -366,6 +367,8 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["stream_m1"] = measure_stream_m1(torch, ug, inputs)
         torch.cuda.empty_cache()
+        out["pack"] = measure_pack(torch, ug, inputs)
+        torch.cuda.empty_cache()
         out["requant_pack5"] = measure_requant_pack5(torch, ug, inputs)
         torch.cuda.empty_cache()
         out["attention_decode"] = measure_attention_decode(torch, ug)
@@ -478,6 +481,49 @@ def measure_copy_rate(torch):
                frac_of_hbm_peak=2 * n / (med * 1e-6) / 1e9 / HBM_PEAK_GBS)
     log("copy rate", res)
     del srcs, dst
+    return res
+
+
+def measure_pack(torch, ug, inputs):
+    """Five trits per byte and back (the pack and unpack steps) on a 2B-class
+    matrix (6912 x 2560, the stack workload's up projection): one-trit-per-
+    byte codes -> PACK5, and PACK5 -> codes; inputs cycle through >= 2 GiB
+    of copies (each read cold); medians over STAT_LAUNCHES calls."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    K, N = inputs.STACK_SHAPES[0]
+    W0 = torch.from_numpy(inputs.stack_master(0, 0)).to(dev)
+    wq, _beta = ug.ug_quant_weight_absmean(W0)
+    del W0
+    pk = ug.ug_pack_trits(wq)
+    n_q = -(-COLD_BYTES // (N * ug.packed_pitch(K) * 5)) + 1
+    wqs = [wq] + [wq.clone() for _ in range(n_q - 1)]
+    pks = [pk] + [pk.clone() for _ in range(n_q - 1)]
+    pk_out = torch.empty_like(pk)
+    wq_out = torch.empty_like(wq)
+    for i in range(2):
+        ug.ug_pack_trits(wqs[i], packed=pk_out)
+        ug.ug_unpack_trits(pks[i], K, wq=wq_out)
+    pmed, pp10, pp90 = launch_stats(
+        torch, lambda i: ug.ug_pack_trits(wqs[(i + 2) % n_q], packed=pk_out), stream)
+    umed, up10, up90 = launch_stats(
+        torch, lambda i: ug.ug_unpack_trits(pks[(i + 2) % n_q], K, wq=wq_out), stream)
+    alg = N * K + N * (-(-K // 5))  # codes one way, packed bytes the other
+    res = dict(value=2 * alg / ((pmed + umed) * 1e-6) / 1e9, unit="GB/s",
+               point="W_q [%d, %d] int8 <-> PACK5 [%d, %d]; %d copies of each cycled"
+                     % (N, K, N, ug.packed_pitch(K), n_q),
+               pack_us_median=pmed, pack_us_p10=pp10, pack_us_p90=pp90,
+               pack_GBps=alg / (pmed * 1e-6) / 1e9,
+               unpack_us_median=umed, unpack_us_p10=up10, unpack_us_p90=up90,
+               unpack_GBps=alg / (umed * 1e-6) / 1e9,
+               roofline=dict(bound="hbm", kernel="pack_kernel + unpack_kernel",
+                             achieved=2 * alg / ((pmed + umed) * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
+                             unit="GB/s",
+                             frac=2 * alg / ((pmed + umed) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                             traffic=traffic_for("pack"), median_launch_us=(pmed + umed) / 2,
+                             alg_bytes_per_launch=alg))
+    log("pack", res)
+    del wqs, pks
     return res
 
 
@@ -1032,6 +1078,7 @@ def main():
         fn = {"prefill_gemm": lambda: measure_prefill_gemm(torch, ug, inputs),
               "vendor_int8_gemm": lambda: measure_vendor_gemm(torch, ug, inputs),
               "hbm_copy_rate": lambda: measure_copy_rate(torch),
+              "pack": lambda: measure_pack(torch, ug, inputs),
               "stream_m1": lambda: measure_stream_m1(torch, ug, inputs),
               "requant_pack5": lambda: measure_requant_pack5(torch, ug, inputs),
               "attention_decode": lambda: measure_attention_decode(torch, ug),
@@ -1048,7 +1095,8 @@ def main():
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
     for k in ("prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
-              "requant_pack5", "attention_decode", "sampler", "backward", "cpu_baseline"):
+              "pack", "requant_pack5", "attention_decode", "sampler", "backward",
+              "cpu_baseline"):
         if k in res:
             line[k] = res[k]
     print(json.dumps(line), flush=True)
