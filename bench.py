@@ -166,6 +166,10 @@ TRAFFIC = {
     "stack": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
                        "06fc5d4c90ea64594662b948395ad6f927f071c6413aa61d83a191b11e6da732"},
                   bytes_per_launch=143235735),
+    # profiles/pack_unpack_6912x2560.md: mean of the pack and unpack calls
+    "pack": dict(src={"bitlinear_matmul_amd/csrc/pack.hip":
+                      "1d8b8b40bbf24c07bbb81cb62f544320edd48ee45beb449f291cfe1347b3bd52"},
+                 bytes_per_launch=21314741),
     # profiles/absmean_ternary_pack5_requant.md: stage 1 + fused pass per call
     "requant_pack5": dict(src={"bitlinear_matmul_amd/csrc/absmean.hip":
                                "a69523d80a0c82173d06857320485e02857481b5810e490f22fae63e67d95234"},
