@@ -35,6 +35,10 @@ FLAGS = [
 # gemv_mfma.hip: the hardware preloads the first two kernel-argument dwords
 # (the block table pointer) into SGPRs, saving a memory round trip at the
 # start of every block of a decode launch.
+# -z defs: a symbol left undefined (say a kernel whose launch stub the host
+# pass did not emit) fails the link instead of the first load.  (A build
+# with host sanitizers links without it: their runtime is preloaded.)
+LINK_FLAGS = ["-Wl,-z,defs"]
 FILE_FLAGS = {"gemm.hip": ["-mllvm", "-enable-post-misched=false"],
               "gemv_mfma.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=2"]}
 
@@ -69,9 +73,7 @@ def build_lib(src_dir, out, verbose=False):
                 sys.stderr.write(r.stdout + r.stderr)
                 raise RuntimeError("hipcc failed compiling " + os.path.basename(obj))
         tmp = out + ".tmp%d" % os.getpid()
-        # -z defs: a symbol left undefined (say a kernel whose launch stub
-        # the host pass did not emit) fails the link instead of the load
-        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,-z,defs",
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *LINK_FLAGS,
                *[o for o, _ in results], "-o", tmp]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)

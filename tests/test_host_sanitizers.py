@@ -95,11 +95,12 @@ def test_libug_host_code_under_asan_ubsan(tmp_path):
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=undefined",
            "-Xarch_host", "-fno-omit-frame-pointer"]
-    saved = ubuild.FLAGS
+    saved, saved_link = ubuild.FLAGS, ubuild.LINK_FLAGS
     ubuild.FLAGS = saved + san
+    ubuild.LINK_FLAGS = []  # the sanitizer runtime is preloaded, not linked
     try:
         lib = ubuild.build_lib(ubuild.CSRC, str(tmp_path / "libug_san.so"))
     finally:
-        ubuild.FLAGS = saved
+        ubuild.FLAGS, ubuild.LINK_FLAGS = saved, saved_link
     out = _run(ABI, asan, lib)
     assert "abi checks run:" in out
