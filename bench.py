@@ -168,8 +168,8 @@ TRAFFIC = {
                   bytes_per_launch=143235735),
     # profiles/pack_unpack_6912x2560.md: mean of the pack and unpack calls
     "pack": dict(src={"bitlinear_matmul_amd/csrc/pack.hip":
-                      "1d8b8b40bbf24c07bbb81cb62f544320edd48ee45beb449f291cfe1347b3bd52"},
-                 bytes_per_launch=21314741),
+                      "a752a31dc60e320f1f3841a49c54afa110a55e65614c559d94983a25d7c60f6c"},
+                 bytes_per_launch=21286585),
     # profiles/absmean_ternary_pack5_requant.md: stage 1 + fused pass per call
     "requant_pack5": dict(src={"bitlinear_matmul_amd/csrc/absmean.hip":
                                "a69523d80a0c82173d06857320485e02857481b5810e490f22fae63e67d95234"},

@@ -238,6 +238,49 @@ def test_pack_parity(dev, N, K):
     assert host(bad)[0] == 0
 
 
+@pytest.mark.parametrize("N,K", [(7, 2559), (5, 2561), (3, 5121), (11, 13), (4, 7680)])
+def test_pack_unpack_row_pads(dev, N, K):
+    """Rows a span boundary away from K, in pitched buffers whose pads hold
+    junk: pack ignores the trit bytes past K (0x55 there is no trit), unpack
+    reads no pad byte of the packed rows (0xff there is no code) and writes
+    none past K."""
+    _print_case("pack pads", N, K)
+    rng = np.random.default_rng([107, N, K])
+    wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    ldq = -(-K // 16) * 16 + 16
+    src = torch.full((N, ldq), 0x55, dtype=torch.int8, device="cuda:0")
+    src[:, :K] = torch.from_numpy(wq).to(dev)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    pk = ug.ug_pack_trits(src[:, :K], bad_count=bad)
+    pk_r, _ = oracle.pack_trits(wq, ldp=pk.shape[1])
+    assert_bits_equal(host(pk), pk_r, "packed")
+    assert host(bad)[0] == 0
+    groups = -(-K // 5)
+    ldp = -(-groups // 16) * 16 + 32
+    pin = torch.full((N, ldp), 0xff, dtype=torch.uint8, device="cuda:0")
+    pin[:, :groups] = pk[:, :groups]
+    out = torch.full((N, ldq), 0x33, dtype=torch.int8, device="cuda:0")
+    ug.ug_unpack_trits(pin[:, :groups], K, wq=out[:, :K], bad_count=bad)
+    assert host(bad)[0] == 0
+    o = host(out)
+    assert_bits_equal(o[:, :K], wq, "unpacked")
+    assert bool((o[:, K:] == 0x33).all()), "unpack wrote past K"
+
+
+def test_pack_every_byte_value(dev):
+    """Every int8 value as a trit byte, at every position of a 5-trit group
+    and of a 4-byte word: 253 of the 256 are bad, each clamped to -1 or 1."""
+    vals = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
+    rng = np.random.default_rng(108)
+    rows = [np.roll(vals, r) for r in range(20)] + [rng.permutation(vals) for _ in range(12)]
+    wq = np.stack(rows)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    pk = ug.ug_pack_trits(pitched(wq), bad_count=bad)
+    pk_r, bad_r = oracle.pack_trits(wq, ldp=pk.shape[1])
+    assert bad_r == 253 * wq.shape[0] and host(bad)[0] == bad_r
+    assert_bits_equal(host(pk), pk_r, "packed")
+
+
 def test_pack_bad_entries_and_unpack_bad_codes(dev):
     rng = np.random.default_rng(106)
     wq = rng.integers(-1, 2, size=(40, 37)).astype(np.int8)
