@@ -180,8 +180,8 @@ TRAFFIC = {
                              bytes_per_launch=85548551),
     # profiles/topk_sample_batch4096.md: the 4096-row launch
     "sampler": dict(src={"bitlinear_matmul_amd/csrc/sampler.hip":
-                         "c2356558fa3c0bdd51c48a1856637ec73dc6367ed023dfad628ded49e7468d6e"},
-                    bytes_per_launch=67728143),
+                         "78d5133a50844d2796909a2b72be6daa2940d583098c61789b01ed4c94262c98"},
+                    bytes_per_launch=67654360),
     # profiles/gemm_f32_backward.md: mean of the dx call (GEMM + slab sum) and
     # the dW call
     "backward": dict(src={"bitlinear_matmul_amd/csrc/backward.hip":

@@ -6,23 +6,32 @@
 // token.  "ultragraph-1bit 0.12.0" README, "A whole ternary GPT": generate()
 // takes a temperature and top_k.
 //
-// One 256-thread block per row, nothing sorted but the k kept logits:
-//   1. every logit becomes an order-preserving 32-bit key (larger logit,
-//      larger key; -0 and +0 the same);
-//   2. four passes of an 8-bit radix select (an LDS histogram of the
-//      digit among the keys that match the digits chosen so far; one wave
-//      scans it from the top digit down) find the k-th largest key t and
-//      how many of the kept keys equal t;
-//   3. one block scan places every key above t, then the lowest-index keys
-//      equal to t, in LDS as (key, ~index) pairs: k distinct 64-bit values;
-//   4. each kept pair's rank is the number of kept pairs above it (larger
-//      logit first, equal logits by lower index), and it moves to that slot;
-//   5. rank r gets the weight e_r = expf(fl(fl(l_r - l_1) / T)); an
+// One 256-thread block per row, nothing sorted but the k kept logits.  The
+// kept set is the k largest (key, ~index) pairs, where every logit becomes
+// an order-preserving 32-bit key (larger logit, larger key; -0 and +0 the
+// same) and equal keys rank by lower index: k distinct 64-bit values.
+//   1. a threshold x with at least k keys at or above it: each wave sorts
+//      its 64 threads' largest keys (a bitonic network across the lanes)
+//      and takes the ceil(k/4)-th; x is the least of the four, so at least
+//      4 ceil(k/4) >= k threads hold a key >= x.  On rows whose large
+//      logits are spread over the threads few keys pass (about 1.25 k for
+//      independent logits);
+//   2. the pairs of keys >= x go to LDS (a wave scan and one LDS atomic
+//      per wave place them); if at most 256 did, each one's rank is the
+//      number of candidates above it and the k lowest ranks move to their
+//      slots — no histograms, six block barriers in all;
+//   3. otherwise (many keys tied or packed into few threads) the k-th
+//      largest key t comes from four passes of an 8-bit radix select (an
+//      LDS histogram of the digit among the keys that match the digits
+//      chosen so far; one wave scans it from the top digit down), one
+//      block scan places every key above t, then the lowest-index keys
+//      equal to t, and each kept pair moves to the slot of its rank;
+//   4. rank r gets the weight e_r = expf(fl(fl(l_r - l_1) / T)); an
 //      inclusive fp32 scan in one fixed order gives C_r; the token is rank
 //      min(#{r : C_r <= fl(u * C_k)}, k - 1).
-// Sixteen block barriers in all.  Rows of at most 4096 logits stay in
-// registers (16 per thread) between the passes; longer rows are read again
-// from memory (L2) for each pass.
+// Both selections give the same kept pairs in the same order.  Rows of at
+// most 4096 logits stay in registers (16 per thread) throughout; longer
+// rows are read again from memory (L2) for each pass.
 #include "ug_internal.h"
 
 namespace ug {
@@ -73,6 +82,8 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
   __shared__ unsigned long long srt[kThreads];  // kept pairs, by rank
   __shared__ uint32_t s_digit;
   __shared__ int s_above;
+  __shared__ uint32_t xs[4];
+  __shared__ int s_count;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *row = logits + (int64_t)b * ld;
   const int per = (V + kThreads - 1) / kThreads;  // this thread: [tid * per, tid * per + per)
@@ -80,10 +91,24 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
 
   uint32_t kr[REG ? kRegPer : 1];
   if (REG) {
+    if (per == kRegPer && i0 + kRegPer <= V) {
+      // all 16 inside the row: four 16-byte loads (rows and i0 are
+      // 16-byte aligned: the pitch is a multiple of 4 floats)
+      const float4 *q = reinterpret_cast<const float4 *>(row + i0);
 #pragma unroll
-    for (int j = 0; j < kRegPer; ++j) {
-      const int i = i0 + j;
-      kr[j] = j < per && i < V ? rank_key(row[i]) : 0u;
+      for (int j = 0; j < kRegPer / 4; ++j) {
+        const float4 f = q[j];
+        kr[4 * j] = rank_key(f.x);
+        kr[4 * j + 1] = rank_key(f.y);
+        kr[4 * j + 2] = rank_key(f.z);
+        kr[4 * j + 3] = rank_key(f.w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j) {
+        const int i = i0 + j;
+        kr[j] = j < per && i < V ? rank_key(row[i]) : 0u;
+      }
     }
   }
   // f(i, key) for every logit of this thread's span, in index order
@@ -98,78 +123,131 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
     }
   };
 
-  // radix select of the k-th largest key.  Pass p counts into hist[p % 2]
-  // (cleared during pass p - 1, after every read of pass p - 2); wave 0
-  // then finds the digit: lane l holds the counts of digits 255 - 4 l ..
-  // 252 - 4 l, and a scan over the lanes gives, for each digit, the number
-  // of matching keys whose digit is at least it.
-  hist[0][tid] = 0;
-  hist[1][tid] = 0;
-  __syncthreads();
-  uint32_t prefix = 0, pmask = 0;
-  int need = k;  // keys still to keep among those matching the prefix
+  // 1. the threshold: this wave's ceil(k/4)-th largest thread maximum
+  // (threads without logits hold 0, below every key but a negative NaN's)
+  uint32_t v = 0;
+  each([&](int, uint32_t key) __attribute__((always_inline)) { v = max(v, key); });
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int sh = 24 - 8 * p;
-    int *H = hist[p & 1];
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)v, stride, 64);
+      // blocks of `size` lanes alternate direction; the last one is
+      // descending over all 64
+      const bool desc = (lane & size) == 0, first = (lane & stride) == 0;
+      v = first == desc ? max(v, o) : min(v, o);
+    }
+  // (cross-lane reads stay outside lane-dependent branches: inside one,
+  // the compiler may compute their operands in the branch's lanes only)
+  const uint32_t xw = __builtin_amdgcn_readlane(v, ((k + 3) >> 2) - 1);
+  if (tid == 0) s_count = 0;
+  if (lane == 0) xs[wave] = xw;
+  __syncthreads();
+  const uint32_t x = min(min(xs[0], xs[1]), min(xs[2], xs[3]));
+  // 2. candidates: the pairs of keys >= x, in any order
+  {
+    int n = 0;
+    each([&](int, uint32_t key) __attribute__((always_inline)) { n += key >= x; });
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    int base = 0;
+    if (lane == 63) base = atomicAdd(&s_count, incl);
+    int pos = __shfl(base, 63, 64) + incl - n;
+    each([&](int i, uint32_t key) __attribute__((always_inline)) {
+      if (key >= x) {
+        if (pos < kThreads) sel[pos] = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)i;
+        ++pos;
+      }
+    });
+  }
+  __syncthreads();
+  const int ncand = s_count;
+  if (ncand <= kThreads) {
+    if (tid < ncand) {
+      const unsigned long long c = sel[tid];
+      int r = 0;
+      for (int j = 0; j < ncand; ++j) r += sel[j] > c;
+      if (r < k) srt[r] = c;
+    }
+    __syncthreads();
+  } else {
+    // 3. radix select of the k-th largest key.  Pass p counts into hist[p % 2]
+    // (cleared during pass p - 1, after every read of pass p - 2); wave 0
+    // then finds the digit: lane l holds the counts of digits 255 - 4 l ..
+    // 252 - 4 l, and a scan over the lanes gives, for each digit, the number
+    // of matching keys whose digit is at least it.
+    hist[0][tid] = 0;
+    hist[1][tid] = 0;
+    __syncthreads();
+    uint32_t prefix = 0, pmask = 0;
+    int need = k;  // keys still to keep among those matching the prefix
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int sh = 24 - 8 * p;
+      int *H = hist[p & 1];
+      each([&](int, uint32_t key) __attribute__((always_inline)) {
+        if ((key & pmask) == prefix) atomicAdd(&H[(key >> sh) & 255], 1);
+      });
+      __syncthreads();
+      if (wave == 0) {
+        const int c0 = H[255 - 4 * lane], c1 = H[254 - 4 * lane], c2 = H[253 - 4 * lane],
+                  c3 = H[252 - 4 * lane];
+        const int t3 = c0 + c1 + c2 + c3;
+        int incl = t3;  // inclusive scan of the lane totals
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        const int ge0 = incl - t3 + c0, ge1 = ge0 + c1, ge2 = ge1 + c2, ge3 = ge2 + c3;
+        // the digit where the count of keys at or above it first reaches need
+        if (ge0 >= need && ge0 - c0 < need) { s_digit = 255 - 4 * lane; s_above = ge0 - c0; }
+        if (ge1 >= need && ge1 - c1 < need) { s_digit = 254 - 4 * lane; s_above = ge1 - c1; }
+        if (ge2 >= need && ge2 - c2 < need) { s_digit = 253 - 4 * lane; s_above = ge2 - c2; }
+        if (ge3 >= need && ge3 - c3 < need) { s_digit = 252 - 4 * lane; s_above = ge3 - c3; }
+      }
+      hist[(p + 1) & 1][tid] = 0;
+      __syncthreads();
+      prefix |= s_digit << sh;
+      pmask |= 0xffu << sh;
+      need -= s_above;
+    }
+    const uint32_t t = prefix;  // the k-th largest key; `need` kept keys equal it
+
+    // compaction: keys above t, then the lowest-index keys equal to t (one
+    // scan of both counts, packed in 32-bit halves)
+    unsigned long long cnt = 0;
     each([&](int, uint32_t key) __attribute__((always_inline)) {
-      if ((key & pmask) == prefix) atomicAdd(&H[(key >> sh) & 255], 1);
+      cnt += key > t ? (1ull << 32) : (key == t ? 1ull : 0ull);
+    });
+    unsigned long long tot;
+    const unsigned long long ex = block_scan(cnt, lws, &tot) - cnt;
+    const int gtot = (int)(tot >> 32);
+    int pg = (int)(ex >> 32), pe = (int)(ex & 0xffffffffu);
+    each([&](int i, uint32_t key) __attribute__((always_inline)) {
+      const unsigned long long c = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)i;
+      if (key > t) {
+        sel[pg++] = c;
+      } else if (key == t) {
+        if (pe < need) sel[gtot + pe] = c;
+        ++pe;
+      }
     });
     __syncthreads();
-    if (wave == 0) {
-      const int c0 = H[255 - 4 * lane], c1 = H[254 - 4 * lane], c2 = H[253 - 4 * lane],
-                c3 = H[252 - 4 * lane];
-      const int t3 = c0 + c1 + c2 + c3;
-      int incl = t3;  // inclusive scan of the lane totals
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-      }
-      const int ge0 = incl - t3 + c0, ge1 = ge0 + c1, ge2 = ge1 + c2, ge3 = ge2 + c3;
-      // the digit where the count of keys at or above it first reaches need
-      if (ge0 >= need && ge0 - c0 < need) { s_digit = 255 - 4 * lane; s_above = ge0 - c0; }
-      if (ge1 >= need && ge1 - c1 < need) { s_digit = 254 - 4 * lane; s_above = ge1 - c1; }
-      if (ge2 >= need && ge2 - c2 < need) { s_digit = 253 - 4 * lane; s_above = ge2 - c2; }
-      if (ge3 >= need && ge3 - c3 < need) { s_digit = 252 - 4 * lane; s_above = ge3 - c3; }
+
+    // rank of each kept pair = how many kept pairs are larger (all distinct)
+    if (tid < k) {
+      const unsigned long long c = sel[tid];
+      int r = 0;
+      for (int j = 0; j < k; ++j) r += sel[j] > c;
+      srt[r] = c;
     }
-    hist[(p + 1) & 1][tid] = 0;
     __syncthreads();
-    prefix |= s_digit << sh;
-    pmask |= 0xffu << sh;
-    need -= s_above;
   }
-  const uint32_t t = prefix;  // the k-th largest key; `need` kept keys equal it
-
-  // compaction: keys above t, then the lowest-index keys equal to t (one
-  // scan of both counts, packed in 32-bit halves)
-  unsigned long long cnt = 0;
-  each([&](int, uint32_t key) __attribute__((always_inline)) {
-    cnt += key > t ? (1ull << 32) : (key == t ? 1ull : 0ull);
-  });
-  unsigned long long tot;
-  const unsigned long long ex = block_scan(cnt, lws, &tot) - cnt;
-  const int gtot = (int)(tot >> 32);
-  int pg = (int)(ex >> 32), pe = (int)(ex & 0xffffffffu);
-  each([&](int i, uint32_t key) __attribute__((always_inline)) {
-    const unsigned long long c = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)i;
-    if (key > t) {
-      sel[pg++] = c;
-    } else if (key == t) {
-      if (pe < need) sel[gtot + pe] = c;
-      ++pe;
-    }
-  });
-  __syncthreads();
-
-  // rank of each kept pair = how many kept pairs are larger (all distinct)
-  if (tid < k) {
-    const unsigned long long c = sel[tid];
-    int r = 0;
-    for (int j = 0; j < k; ++j) r += sel[j] > c;
-    srt[r] = c;
-  }
-  __syncthreads();
 
   // weights, their running sum and the draw
   const unsigned long long mine = tid < k ? srt[tid] : 0ull;

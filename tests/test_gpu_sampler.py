@@ -70,8 +70,14 @@ def _check(logits, k, T, u):
     (3, 1000, 50, 1.0, "constant"),    # every logit equal
     (6, 2000, 64, 1.0, "zeros"),       # -0 and +0 mixed
     (4, 4096, 100, 1e30, "normal"),    # uniform over the kept ranks
+    (64, 4096, 150, 1.0, "normal"),    # candidates near 256: rows take either selection
+    (4, 4096, 100, 1.0, "ascending"),  # the largest logits packed into the last threads
+    (4, 4096, 100, 1.0, "descending"),
 ])
 def test_sampler_parity(dev, B, V, k, T, kind):
+    """Rows whose large logits are spread over the block's threads select
+    from the keys above a per-wave threshold; tied, constant, sorted and
+    large-k rows (more than 256 keys above it) take the radix select."""
     _case("sampler", B, V, k, T, kind)
     rng = np.random.default_rng([90, B, V, k])
     x = rng.standard_normal((B, V), dtype=np.float32) * np.float32(3.0)
@@ -79,6 +85,10 @@ def test_sampler_parity(dev, B, V, k, T, kind):
         x = np.round(x).astype(np.float32)
     elif kind == "constant":
         x[:] = np.float32(0.25)
+    elif kind in ("ascending", "descending"):
+        x = np.sort(x, axis=1)
+        if kind == "descending":
+            x = np.ascontiguousarray(x[:, ::-1])
     elif kind == "zeros":
         x = np.where(rng.random((B, V)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
         x[:, ::7] = rng.standard_normal((B, (V + 6) // 7), dtype=np.float32)
