@@ -126,7 +126,7 @@ def parse():
     p.add_argument("--only", default=None,
                    choices=["prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
                             "pack", "requant_pack5", "attention_decode", "sampler",
-                            "backward"],
+                            "backward", "mfma_sustained"],
                    help="run just this one of the decode_stack line's extra points and print "
                         "its JSON object (for profiling a single kernel)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -363,6 +363,8 @@ def run_decode_stack(args, torch, ug, inputs):
     del plans, mats, flush
     torch.cuda.empty_cache()
     if not args.no_extra:
+        out["mfma_sustained"] = measure_mfma_sustained(torch, ug)
+        torch.cuda.empty_cache()
         out["prefill_gemm"] = measure_prefill_gemm(torch, ug, inputs)
         torch.cuda.empty_cache()
         out["vendor_int8_gemm"] = measure_vendor_gemm(torch, ug, inputs)
@@ -381,6 +383,12 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["backward"] = measure_backward(torch, ug)
         torch.cuda.empty_cache()
+        # the matrix-core kernels against what the matrix cores sustain
+        ms = out["mfma_sustained"]
+        out["prefill_gemm"]["roofline"]["frac_of_sustained"] = (
+            out["prefill_gemm"]["roofline"]["achieved"] / ms["int8_TOPs"])
+        out["backward"]["roofline"]["frac_of_sustained"] = (
+            out["backward"]["roofline"]["achieved"] / ms["fp32_TFLOPs"])
     if not args.no_cpu_baseline:
         import oracle
         passes, secs = cpu_decode_stack(oracle, inputs, args.cpu_seconds)
@@ -485,6 +493,32 @@ def measure_copy_rate(torch):
                frac_of_hbm_peak=2 * n / (med * 1e-6) / 1e9 / HBM_PEAK_GBS)
     log("copy rate", res)
     del srcs, dst
+    return res
+
+
+def measure_mfma_sustained(torch, ug, iters=4000):
+    """Context for the matrix-core rooflines: the rate the matrix cores
+    sustain with every CU busy (ug_mfma_rate_probe: one block of four waves
+    per CU, back-to-back int8 32x32x32 or fp32 16x16x4 instructions on
+    register operands that change every instruction, ~1 ms per call, so the
+    clock settles where the board's power limit holds it).  Medians over
+    STAT_LAUNCHES calls of each kind."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(4 * blocks, dtype=torch.int32, device=dev)
+    res = dict(blocks=blocks, iters=iters,
+               note="context: register-only matrix instructions on every CU; the published "
+                    "peaks assume the 2.4 GHz peak clock")
+    for kind, name, peak in ((0, "int8", INT8_PEAK_TOPS), (1, "fp32", FP32_MFMA_PEAK_TFLOPS)):
+        ops = ug.ug_mfma_rate_probe(kind, blocks, iters, sink)
+        med, p10, p90 = launch_stats(torch, lambda i: ug.ug_mfma_rate_probe(kind, blocks, iters,
+                                                                            sink), stream)
+        rate = ops / (med * 1e-6) / 1e12
+        res[name + ("_TOPs" if kind == 0 else "_TFLOPs")] = rate
+        res[name + "_frac_of_peak"] = rate / peak
+        res[name + "_median_call_us"] = med
+    log("mfma sustained", res)
     return res
 
 
@@ -1087,7 +1121,8 @@ def main():
               "requant_pack5": lambda: measure_requant_pack5(torch, ug, inputs),
               "attention_decode": lambda: measure_attention_decode(torch, ug),
               "sampler": lambda: measure_sampler(torch, ug),
-              "backward": lambda: measure_backward(torch, ug)}[args.only]
+              "backward": lambda: measure_backward(torch, ug),
+              "mfma_sustained": lambda: measure_mfma_sustained(torch, ug)}[args.only]
         print(json.dumps({"point": args.only, **fn()}), flush=True)
         return
     runners = {"decode_stack": run_decode_stack, "prefill": run_prefill, "sweep": run_sweep,
@@ -1098,7 +1133,7 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
-    for k in ("prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
+    for k in ("mfma_sustained", "prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
               "pack", "requant_pack5", "attention_decode", "sampler", "backward",
               "cpu_baseline"):
         if k in res:

@@ -408,6 +408,13 @@ ug_status ug_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V, 
                                            as_stream(stream)));
 }
 
+ug_status ug_mfma_rate_probe(int32_t kind, int32_t blocks, int32_t iters, int32_t *sink,
+                             void *stream) {
+  if ((kind != 0 && kind != 1) || blocks < 1 || iters < 1 || !counter_ok(sink) || sink == nullptr)
+    return UG_ERR_INVALID_ARG;
+  return hip_status(ug::launch_mfma_rate(kind, blocks, iters, sink, as_stream(stream)));
+}
+
 size_t ug_attention_workspace_size(int64_t M, int64_t pos0, int64_t H, int64_t dh) {
   if (!attention_shape_ok(M, pos0, H, dh) || pos0 + M > (INT64_C(1) << 24) || H > 65535 ||
       M > 65535)

@@ -148,6 +148,7 @@ hipError_t launch_backward(const float *g, int64_t ldg, const float *x, int64_t 
                            float *dx, int64_t lddx, float *dW, int64_t lddw, float *db,
                            float *part, hipStream_t st);
 // Top-k sampling: one block per row of logits.
+hipError_t launch_mfma_rate(int kind, int blocks, int iters, int32_t *sink, hipStream_t st);
 hipError_t launch_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V, int64_t k,
                               float temp, const float *u, int32_t *tok, int32_t *idx_out,
                               int64_t ldi, float *val_out, int64_t ldv, float *prob_out,

@@ -66,6 +66,7 @@ SIGNATURES = {
     "ug_attention_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
     "ug_attention_cached": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
                                    _i64, _vp, _sz, _vp]),
+    "ug_mfma_rate_probe": (_i32, [_i32, _i32, _i32, _vp, _vp]),
 }
 
 UG_GEMM_COUNTER_BYTES = 2048
@@ -468,3 +469,16 @@ def ug_bitlinear_backward(g, x, W, want=("dx", "dW", "db"), dx=None, dW=None, db
             out[name] = t
     return out
 
+
+MFMA_PROBE_OPS = {0: 2 * 32 * 32 * 32, 1: 2 * 16 * 16 * 4}  # per instruction
+
+
+def ug_mfma_rate_probe(kind, blocks, iters, sink, stream=None):
+    """Measurement helper (not a step of the forward path): iters x 16
+    back-to-back matrix instructions per wave, four waves per block (kind 0:
+    int8 32x32x32, kind 1: fp32 16x16x4); sink int32 [4 * blocks] on the
+    device.  Returns the operation count, for the caller to divide by the
+    time it measures."""
+    _check(lib().ug_mfma_rate_probe(kind, blocks, iters, _p(sink), _stream(stream)),
+           "ug_mfma_rate_probe")
+    return 4 * blocks * iters * 16 * MFMA_PROBE_OPS[kind]

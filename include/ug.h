@@ -445,6 +445,25 @@ ug_status ug_attention_cached(const float *q, int64_t ldq, const float *kc,
                               float *out, int64_t ldo, void *ws,
                               size_t ws_bytes, void *stream);
 
+/*
+ * Measurement helper beside the forward path (not a step of it): the rate
+ * the matrix cores sustain when every CU runs them.  Launches `blocks`
+ * blocks of four waves (one per SIMD; blocks = the CU count loads every
+ * CU once); each wave issues iters x 16 back-to-back matrix instructions on
+ * register operands that change from one instruction to the next, with no
+ * memory traffic:
+ *   kind 0: v_mfma_i32_32x32x32_i8 (65536 int8 ops each),
+ *   kind 1: v_mfma_f32_16x16x4f32 (2048 fp32 flops each).
+ * Each wave writes one int32 derived from its accumulators to sink[w]
+ * (device memory, 4 * blocks words), which keeps every instruction in the
+ * program.  The caller times the call on `stream`: the sustained rate is
+ * 4 * blocks * iters * 16 * (ops per instruction) / time.
+ * UG_ERR_INVALID_ARG for another kind, blocks < 1, iters < 1 or a sink
+ * that is NULL or not 4-byte aligned.
+ */
+ug_status ug_mfma_rate_probe(int32_t kind, int32_t blocks, int32_t iters,
+                             int32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -351,3 +351,14 @@ def test_backward_rejects(ug):
     assert call(db=ctypes.c_void_p(0x600000), ws=A4, ws_bytes=need - 4) == ug.UG_ERR_WORKSPACE
     assert call(ws=NULL) == ug.UG_ERR_WORKSPACE
     assert call(M=2 ** 23 + 1) == ug.UG_ERR_UNSUPPORTED
+
+
+def test_mfma_rate_probe_rejects(ug):
+    L = ug.lib()
+    E = ug.UG_ERR_INVALID_ARG
+    assert L.ug_mfma_rate_probe(2, 256, 10, A, S) == E     # no such kind
+    assert L.ug_mfma_rate_probe(-1, 256, 10, A, S) == E
+    assert L.ug_mfma_rate_probe(0, 0, 10, A, S) == E       # no blocks
+    assert L.ug_mfma_rate_probe(1, 256, 0, A, S) == E      # no iterations
+    assert L.ug_mfma_rate_probe(0, 256, 10, NULL, S) == E
+    assert L.ug_mfma_rate_probe(0, 256, 10, ctypes.c_void_p(0x200002), S) == E

@@ -536,3 +536,21 @@ def test_bias_epilogue(dev, M, N, K, fmt, path):
     acc_r = oracle.matmul_i32(xq, wq)
     assert_bits_equal(host(acc_d), acc_r, "acc")
     assert_bits_equal(host(y_d), oracle.epilogue(acc_r, s, beta, bias), "y with bias")
+
+
+# ---------------------------------------------------------------------------
+# matrix-core rate probe (a measurement helper)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", [0, 1])
+def test_mfma_rate_probe_runs_and_repeats(dev, kind):
+    """The probe's operands come from the block and thread index only, so
+    two calls write the same words, and different waves different ones."""
+    blocks = 8
+    a = torch.zeros(4 * blocks, dtype=torch.int32, device="cuda:0")
+    b = torch.ones(4 * blocks, dtype=torch.int32, device="cuda:0")
+    ops = ug.ug_mfma_rate_probe(kind, blocks, 3, a)
+    ug.ug_mfma_rate_probe(kind, blocks, 3, b)
+    torch.cuda.synchronize()
+    assert ops == 4 * blocks * 3 * 16 * (65536 if kind == 0 else 2048)
+    assert torch.equal(a, b)
+    assert len(set(host(a).tolist())) > 1
