@@ -176,8 +176,8 @@ TRAFFIC = {
                           bytes_per_launch=145415161),
     # profiles/attention_decode_4096.md: partials + combine per call
     "attention_decode": dict(src={"bitlinear_matmul_amd/csrc/attention.hip":
-                                  "f500bc9a3ea52e5381ee0eb6127bc07c780c232a6b8544270ba3575ae71151a3"},
-                             bytes_per_launch=85548551),
+                                  "d056702cf7f6a76a59cc97c7e0e992b33c28afa64e7f83209459662ea53b9377"},
+                             bytes_per_launch=85617150),
     # profiles/topk_sample_batch4096.md: the 4096-row launch
     "sampler": dict(src={"bitlinear_matmul_amd/csrc/sampler.hip":
                          "78d5133a50844d2796909a2b72be6daa2940d583098c61789b01ed4c94262c98"},

@@ -16,9 +16,10 @@
 // that a decode step at 4096 positions with 20 heads is 1280 small blocks
 // resident at once; every cache load moves 1 KB (16 bytes a lane: 256 / d_h
 // rows).  attn_combine rescales the chunks to their common maximum and
-// divides.  Every reduction has one fixed order, the same for every query
-// row whatever the number of rows in the call, so row t of a call over many
-// rows is bit for bit the single-row call at position t:
+// divides (a row of at most 64 chunks, 4096 positions, in one round trip
+// for its records).  Every reduction has one fixed order, the same for
+// every query row whatever the number of rows in the call, so row t of a
+// call over many rows is bit for bit the single-row call at position t:
 //   score_j = fl(dot_j / fl(sqrt(d_h))), dot_j = the d_h / 4 partials
 //             of dims 4i .. 4i+3 (each the four products added in dim
 //             order from +0) added in order of i from +0;
@@ -164,30 +165,25 @@ template <int DH>
 __global__ __launch_bounds__(256) void attn_combine(const float *__restrict__ part, int pos0,
                                                     int H, int nck, float *__restrict__ out,
                                                     int64_t ldo) {
-  constexpr int R = AttnDims<DH>::R, REC = AttnDims<DH>::kRec, NB = 8;
+  constexpr int R = AttnDims<DH>::R, REC = AttnDims<DH>::kRec, NB = 8, NB1 = 16;
   const int h = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = (pos0 + m) / kChunk + 1;
   const float *base = part + ((int64_t)m * H + h) * nck * REC;
   __shared__ float wmax[4], wl[4];
   __shared__ float wo[4][DH];
-  // M = the largest chunk maximum (exact in any order)
-  float mx = -INFINITY;
-  for (int c = tid; c < nc; c += 256) mx = fmaxf(mx, base[(int64_t)c * REC + DH]);
-  mx = wave_max(mx);
-  if (lane == 0) wmax[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  // wave w: chunks w, w + 4, ... in increasing order, NB at a time in flight
   float l = 0.0f, o[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) o[i] = 0.0f;
-  for (int c0 = wave; c0 < nc; c0 += 4 * NB) {
-    float mc[NB], lc[NB], oc[NB][R];
+  if (nc <= 4 * NB1) {
+    // Up to 4 * NB1 chunks: each wave loads all of its records at once (one
+    // round trip), and the waves' maxima meet in LDS.  Same order of sums
+    // as below.
+    float mc[NB1], lc[NB1], oc[NB1][R];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int c = c0 + 4 * u;
+    for (int u = 0; u < NB1; ++u) {
+      const int c = wave + 4 * u;
       const float *rec = base + (int64_t)min(c, nc - 1) * REC;
-      mc[u] = rec[DH];
+      mc[u] = c < nc ? rec[DH] : -INFINITY;
       lc[u] = rec[DH + 1];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
@@ -195,13 +191,52 @@ __global__ __launch_bounds__(256) void attn_combine(const float *__restrict__ pa
         oc[u][i] = d < DH ? rec[d] : 0.0f;
       }
     }
+    float wm = mc[0];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      if (c0 + 4 * u < nc) {
+    for (int u = 1; u < NB1; ++u) wm = fmaxf(wm, mc[u]);
+    if (lane == 0) wmax[wave] = wm;
+    __syncthreads();
+    const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+#pragma unroll
+    for (int u = 0; u < NB1; ++u) {
+      if (wave + 4 * u < nc) {
         const float e = expf(mc[u] - mx);
         l = l + e * lc[u];
 #pragma unroll
         for (int i = 0; i < R; ++i) o[i] = o[i] + e * oc[u][i];
+      }
+    }
+  } else {
+    // M = the largest chunk maximum (exact in any order)
+    float mx = -INFINITY;
+    for (int c = tid; c < nc; c += 256) mx = fmaxf(mx, base[(int64_t)c * REC + DH]);
+    mx = wave_max(mx);
+    if (lane == 0) wmax[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    // wave w: chunks w, w + 4, ... in increasing order, NB at a time in flight
+    for (int c0 = wave; c0 < nc; c0 += 4 * NB) {
+      float mc[NB], lc[NB], oc[NB][R];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int c = c0 + 4 * u;
+        const float *rec = base + (int64_t)min(c, nc - 1) * REC;
+        mc[u] = rec[DH];
+        lc[u] = rec[DH + 1];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int d = lane + 64 * i;
+          oc[u][i] = d < DH ? rec[d] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        if (c0 + 4 * u < nc) {
+          const float e = expf(mc[u] - mx);
+          l = l + e * lc[u];
+#pragma unroll
+          for (int i = 0; i < R; ++i) o[i] = o[i] + e * oc[u][i];
+        }
       }
     }
   }
