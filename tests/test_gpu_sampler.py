@@ -97,6 +97,36 @@ def test_sampler_parity(dev, B, V, k, T, kind):
     _check(x, k, T, u)
 
 
+@pytest.mark.parametrize("B,V,k,kind", [
+    (8, 1000, 3, "normal"),         # k not a multiple of 4: each wave's 1st largest
+    (8, 777, 13, "normal"),         # ragged: the last threads and waves hold no logits
+    (8, 130, 5, "normal"),          # one logit per thread; waves 3 and 4 empty: x = 0
+    (8, 4096, 100, "one_thread"),   # the 16 largest logits in one thread's span
+    (8, 4096, 100, "one_wave"),     # the 1024 largest in one wave's threads
+    (8, 4096, 7, "spikes"),         # a few huge logits far above the rest
+    (8, 4096, 256, "normal"),       # the largest k: x is the least thread maximum
+])
+def test_sampler_threshold_edges(dev, B, V, k, kind):
+    """Rows where the candidate threshold (each wave's ceil(k/4)-th largest
+    thread maximum, the least of the four) is tight, degenerate or lets in
+    many keys: the kept indices and their order stay exact."""
+    _case("sampler edges", B, V, k, kind)
+    rng = np.random.default_rng([92, B, V, k])
+    x = rng.standard_normal((B, V), dtype=np.float32)
+    per = -(-V // 256)
+    if kind == "one_thread":
+        t0 = 97 * per
+        x[:, t0:t0 + per] += np.float32(50.0)
+    elif kind == "one_wave":
+        w0 = 2 * 64 * per
+        x[:, w0:w0 + 64 * per] += np.float32(50.0)
+    elif kind == "spikes":
+        for b in range(B):
+            x[b, rng.choice(V, 5, replace=False)] = np.float32(1e4) * rng.random(5, dtype=np.float32)
+    u = rng.random(B, dtype=np.float32)
+    _check(x, k, 1.0, u)
+
+
 def test_sampler_frequencies(dev):
     """20000 rows of the same logits with evenly spaced draws: each kept
     rank is drawn in proportion to its softmax weight."""
