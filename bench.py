@@ -160,12 +160,12 @@ TRAFFIC = {
                   bytes_per_launch=131674036),
     # profiles/gemm_i8_large_prefill.md: mean of the two shapes' launches
     "prefill": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
-                         "06fc5d4c90ea64594662b948395ad6f927f071c6413aa61d83a191b11e6da732"},
-                    bytes_per_launch=200752914),
+                         "02b27e9db0529ba1b218003a0d600a96eb02f97bdc7bbbc8ef0ed0e7862fabf3"},
+                    bytes_per_launch=200752978),
     # profiles/gemm_i8_large_stack.md: mean of the two shapes' launches
     "stack": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
-                       "06fc5d4c90ea64594662b948395ad6f927f071c6413aa61d83a191b11e6da732"},
-                  bytes_per_launch=143235735),
+                       "02b27e9db0529ba1b218003a0d600a96eb02f97bdc7bbbc8ef0ed0e7862fabf3"},
+                  bytes_per_launch=143287088),
     # profiles/pack_unpack_6912x2560.md: mean of the pack and unpack calls
     "pack": dict(src={"bitlinear_matmul_amd/csrc/pack.hip":
                       "a752a31dc60e320f1f3841a49c54afa110a55e65614c559d94983a25d7c60f6c"},
@@ -219,7 +219,9 @@ def copy_probe(torch):
 # timing helpers
 # ---------------------------------------------------------------------------
 def time_graph(torch, g, stream):
-    """Replay a captured graph once between events on its stream; ms."""
+    """Replay a captured graph once between events on its stream; ms.  (A
+    graph's first replay also pays one-time set-up: callers replay it once
+    untimed first.)"""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -321,6 +323,10 @@ def run_decode_stack(args, torch, ug, inputs):
                                     for c in range(steps)])
     stream = torch.cuda.current_stream()
     time_graph(torch, g_warm, stream)
+    # the timed graph's first replay, untimed (its one-time set-up: a
+    # graph's first replay runs ~1 us per launch slower), then the caches
+    # are flushed again, so the timed replay still reads every copy cold
+    time_graph(torch, g_run, stream)
     flush()
     ms = time_graph(torch, g_run, stream)
     log("decode_stack: %d steps in %.3f ms" % (steps, ms))
@@ -772,6 +778,7 @@ def run_sweep(args, torch, ug, inputs):
     warm = args.warmup if args.warmup is not None else 2
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    flush = Flusher(torch)
     points = []
     tot_bytes = 0.0
     tot_s = 0.0
@@ -802,6 +809,8 @@ def run_sweep(args, torch, ug, inputs):
             if plans is not None:
                 g = capture(torch, lambda: [ug.ug_bitlinear_gemv_grouped(plans[c % n_sets])
                                             for c in range(warm + steps)])
+                time_graph(torch, g, stream)  # first replay untimed (one-time set-up)
+                flush()
                 ms = time_graph(torch, g, stream)
                 launch_us = ms * 1e3 / (warm + steps)
                 gbs = wbytes * G / (launch_us * 1e-6) / 1e9
@@ -813,6 +822,8 @@ def run_sweep(args, torch, ug, inputs):
             g1 = capture(torch, lambda: [ug.ug_bitlinear_gemv(
                 xq, s, copies[c % n_sets][c % G], ug.UG_W_PACK5, beta, K=K, y=y)
                 for c in range(warm + steps)])
+            time_graph(torch, g1, stream)
+            flush()
             ms1 = time_graph(torch, g1, stream)
             del g1
             call_us = ms1 * 1e3 / (warm + steps)

@@ -143,10 +143,10 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Large GEMM on v_mfma_i32_32x32x32_i8 (the 16x16x64 form issues at half the
-// int8 rate on gfx950).  Lane l of that MFMA holds A row l%32 and B column
-// l%32 at K bytes [16 (l/32), +16), and accumulator element i of lane l is
-// D[8 (i/4) + 4 (l/32) + i%4][l%32].
+// Large GEMM on v_mfma_i32_32x32x32_i8 (the same int8 rate as the 16x16x64
+// form, twice its products per fragment byte read from LDS).  Lane l of that
+// MFMA holds A row l%32 and B column l%32 at K bytes [16 (l/32), +16), and
+// accumulator element i of lane l is D[8 (i/4) + 4 (l/32) + i%4][l%32].
 //
 // Output tiles of 256 rows x BN = 32 NT columns per 256-thread block, four
 // waves in a WM x WN grid, each with IT x JT MFMA tiles (int32 accumulators
