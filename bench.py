@@ -180,8 +180,8 @@ TRAFFIC = {
                              bytes_per_launch=85617150),
     # profiles/topk_sample_batch4096.md: the 4096-row launch
     "sampler": dict(src={"bitlinear_matmul_amd/csrc/sampler.hip":
-                         "78d5133a50844d2796909a2b72be6daa2940d583098c61789b01ed4c94262c98"},
-                    bytes_per_launch=67654360),
+                         "5f1175f9cdb00f4849602b68bfa56c0498507360b3ba4421cc3c6fce32a689e7"},
+                    bytes_per_launch=67644186),
     # profiles/gemm_f32_backward.md: mean of the dx call (GEMM + slab sum) and
     # the dW call
     "backward": dict(src={"bitlinear_matmul_amd/csrc/backward.hip":

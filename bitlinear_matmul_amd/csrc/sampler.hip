@@ -49,15 +49,43 @@ __device__ inline float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// Inclusive sum over a wave's 64 lanes, in one fixed order: within each
+// 16-lane row by shifted reads (lane l adds lane l - h for h = 1, 2, 4, 8,
+// in that order; a read from before the row gives 0), then lane 15's sum
+// is added into rows 1 and 3 (lane 47's, the sum of row 2, into row 3),
+// then lane 31's into rows 2 and 3.  Register moves (DPP) only, no LDS
+// round trip.  (int or float; for an fp32 sum this order is the order.)
+template <int CTRL, int ROWS, typename T>
+__device__ inline T dpp_t(T v) {
+  return __builtin_bit_cast(
+      T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, true));
+}
+template <typename T>
+__device__ inline T wave_incl_scan(T v) {
+  v = v + dpp_t<0x111, 0xf>(v);  // row_shr:1
+  v = v + dpp_t<0x112, 0xf>(v);  // row_shr:2
+  v = v + dpp_t<0x114, 0xf>(v);  // row_shr:4
+  v = v + dpp_t<0x118, 0xf>(v);  // row_shr:8
+  v = v + dpp_t<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = v + dpp_t<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Inclusive sum over the block's 256 threads in thread order (a scan within
 // each wave, then the waves' totals in order); *total gets the block sum.
+// 32-bit values scan by DPP (wave_incl_scan's order); 64-bit ones lane
+// l adds lane l - h for h = 1, 2, 4, .., 32.
 template <typename T>
 __device__ inline T block_scan(T v, T *wsum, T *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if constexpr (sizeof(T) == 4) {
+    v = wave_incl_scan(v);
+  } else {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const T y = __shfl_up(v, off, 64);
-    if (lane >= off) v = v + y;
+    for (int off = 1; off < 64; off <<= 1) {
+      const T y = __shfl_up(v, off, 64);
+      if (lane >= off) v = v + y;
+    }
   }
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
@@ -78,7 +106,9 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
   __shared__ int iws[4];
   __shared__ float fws[4];
   __shared__ unsigned long long lws[4];
-  __shared__ unsigned long long sel[kThreads];  // kept pairs, in index order
+  // kept pairs, in index order (the fast path's candidates, in any order,
+  // then zeros up to a whole number of 32-pair blocks)
+  __shared__ __attribute__((aligned(16))) unsigned long long sel[kThreads + 32];
   __shared__ unsigned long long srt[kThreads];  // kept pairs, by rank
   __shared__ uint32_t s_digit;
   __shared__ int s_above;
@@ -142,18 +172,16 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
   const uint32_t xw = __builtin_amdgcn_readlane(v, ((k + 3) >> 2) - 1);
   if (tid == 0) s_count = 0;
   if (lane == 0) xs[wave] = xw;
+  // zeros: a pair that no candidate is below (every kept key is >= 1)
+  sel[tid] = 0ull;
+  if (tid < 32) sel[kThreads + tid] = 0ull;
   __syncthreads();
   const uint32_t x = min(min(xs[0], xs[1]), min(xs[2], xs[3]));
   // 2. candidates: the pairs of keys >= x, in any order
   {
     int n = 0;
     each([&](int, uint32_t key) __attribute__((always_inline)) { n += key >= x; });
-    int incl = n;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
+    const int incl = wave_incl_scan(n);
     int base = 0;
     if (lane == 63) base = atomicAdd(&s_count, incl);
     int pos = __shfl(base, 63, 64) + incl - n;
@@ -170,7 +198,16 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
     if (tid < ncand) {
       const unsigned long long c = sel[tid];
       int r = 0;
-      for (int j = 0; j < ncand; ++j) r += sel[j] > c;
+      // 32 pairs per round, their 16 reads in flight together (the zeros
+      // past ncand count for nothing)
+      const ulonglong2 *s2 = reinterpret_cast<const ulonglong2 *>(sel);
+      for (int j = 0; j < ncand; j += 32) {
+        ulonglong2 p[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) p[u] = s2[(j >> 1) + u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) r += (p[u].x > c) + (p[u].y > c);
+      }
       if (r < k) srt[r] = c;
     }
     __syncthreads();
