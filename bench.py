@@ -180,8 +180,8 @@ TRAFFIC = {
                              bytes_per_launch=85617150),
     # profiles/topk_sample_batch4096.md: the 4096-row launch
     "sampler": dict(src={"bitlinear_matmul_amd/csrc/sampler.hip":
-                         "5f1175f9cdb00f4849602b68bfa56c0498507360b3ba4421cc3c6fce32a689e7"},
-                    bytes_per_launch=67644186),
+                         "5626fcf9f96f214c619bce97c12f84286293f235fe296ac41c7771d47261fa0e"},
+                    bytes_per_launch=67639194),
     # profiles/gemm_f32_backward.md: mean of the dx call (GEMM + slab sum) and
     # the dW call
     "backward": dict(src={"bitlinear_matmul_amd/csrc/backward.hip":

@@ -71,6 +71,40 @@ __device__ inline T wave_incl_scan(T v) {
   return v;
 }
 
+// Lane l ^ S's value: strides 1, 2 and 8 by DPP (quad permutations, a
+// rotation by 8 within 16-lane rows), 4 and 16 by a lane swizzle (xor mask,
+// no memory access), 32 through ds_bpermute.
+template <int S>
+__device__ inline uint32_t xor_lane(uint32_t v) {
+  if constexpr (S == 1)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false);
+  else if constexpr (S == 2)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false);
+  else if constexpr (S == 8)
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+  else if constexpr (S == 4)
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1f | (4 << 10));
+  else if constexpr (S == 16)
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1f | (16 << 10));
+  else
+    return (uint32_t)__shfl_xor((int)v, S, 64);
+}
+
+// Bitonic network over the 64 lanes (descending at the end): merge blocks
+// of SIZE lanes, compare-exchange at STRIDE; blocks alternate direction.
+template <int SIZE, int STRIDE>
+__device__ inline uint32_t bitonic_steps(uint32_t v, int lane) {
+  const uint32_t o = xor_lane<STRIDE>(v);
+  const bool desc = (lane & SIZE) == 0, first = (lane & STRIDE) == 0;
+  v = first == desc ? max(v, o) : min(v, o);
+  if constexpr (STRIDE > 1)
+    return bitonic_steps<SIZE, STRIDE / 2>(v, lane);
+  else if constexpr (SIZE < 64)
+    return bitonic_steps<SIZE * 2, SIZE>(v, lane);
+  else
+    return v;
+}
+
 // Inclusive sum over the block's 256 threads in thread order (a scan within
 // each wave, then the waves' totals in order); *total gets the block sum.
 // 32-bit values scan by DPP (wave_incl_scan's order); 64-bit ones lane
@@ -157,16 +191,7 @@ __global__ __launch_bounds__(kThreads) void topk_sample(
   // (threads without logits hold 0, below every key but a negative NaN's)
   uint32_t v = 0;
   each([&](int, uint32_t key) __attribute__((always_inline)) { v = max(v, key); });
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1)
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)v, stride, 64);
-      // blocks of `size` lanes alternate direction; the last one is
-      // descending over all 64
-      const bool desc = (lane & size) == 0, first = (lane & stride) == 0;
-      v = first == desc ? max(v, o) : min(v, o);
-    }
+  v = bitonic_steps<2, 1>(v, lane);
   // (cross-lane reads stay outside lane-dependent branches: inside one,
   // the compiler may compute their operands in the branch's lanes only)
   const uint32_t xw = __builtin_amdgcn_readlane(v, ((k + 3) >> 2) - 1);
