@@ -1111,7 +1111,7 @@ def run_tiny(args, torch, ug, inputs):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
