@@ -704,6 +704,12 @@ def measure_backward(torch, ug, M=2048, N=6912, K=2560):
     outs = {}
     ws = torch.empty(ug.lib().ug_bitlinear_backward_workspace_size(M, N, K), dtype=torch.uint8,
                      device=dev)
+    # untimed load first: in a fresh process the first tens of milliseconds
+    # of these products measured about 10% slower than the rest
+    warm = ug.ug_bitlinear_backward(g, x, W, want=("dx", "dW"), ws=ws)
+    for _ in range(40):
+        ug.ug_bitlinear_backward(g, x, W, want=("dx", "dW"), ws=ws, **warm)
+    torch.cuda.synchronize()
     for name in ("dx", "dW", "db"):
         res = ug.ug_bitlinear_backward(g, x, W, want=(name,), ws=ws)
         res["ws"] = ws

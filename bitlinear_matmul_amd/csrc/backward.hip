@@ -14,13 +14,25 @@
 // (j contiguous) and A either p-contiguous (A(i, p) = a[i][p]: dx, A = g) or
 // i-contiguous (A(i, p) = a[p][i]: dW, A = g read as g^T).  Blocks of 256
 // threads own 128 x 128 tiles of C, each wave a 64 x 64 quarter (4 x 4 MFMA
-// tiles).  A product with too few tiles to fill the chip for several rounds
-// (dx at 2048 x 2560: 320 tiles on 256 compute units) is cut along the
-// contraction into S pieces whose partial tiles a second kernel adds in
-// piece order (no atomics: the same bits on every run); the reduction moves 16 p at a time through double-buffered LDS
+// tiles); the reduction moves 16 p at a time through double-buffered LDS
 // (p-major rows padded to 144 floats, so the four p-rows one fragment read
 // touches fall in different banks), the next step's loads in registers
 // while the current one multiplies, one barrier per step.
+//
+// Four blocks fit a compute unit, so a launch runs in rounds of 4 x CUs
+// blocks; a tile count just past a whole number of rounds (dW at
+// 6912 x 2560: 1080 tiles on 1024 slots) or short of one round (dx at
+// 2048 x 2560: 320 tiles) would leave most of the chip idle for part of
+// the run.  So the tiles beyond the last whole round are cut along the
+// contraction into S equal pieces, enough for a round of their own (dW: 56
+// tiles x 16 pieces of 8 steps; dx: 320 tiles x 4 pieces of 108 steps),
+// which run after the whole tiles, one block each.  Blocks that run at the
+// same time take the same piece of neighbouring tiles, so they read the
+// same contraction rows of the shared operand at the same time (one XCD's
+// L2 serves them all), as the whole tiles do.  The pieces land as partial
+// tiles in the workspace and a second kernel adds each tile's pieces in
+// piece order (no atomics: the same bits on every run on a given device,
+// since the cut depends only on the shape and the CU count).
 #include "ug_internal.h"
 
 namespace ug {
@@ -32,7 +44,6 @@ constexpr int kTile = 128;     // C tile edge
 constexpr int kStep = 16;      // p per step
 constexpr int kPitch = 144;    // LDS row (one p) in floats
 constexpr int kXcd = 8;
-constexpr int kMaxPieces = 8;  // contraction pieces of a few-tile product
 
 __device__ inline float4 load4_guarded(const float *base, int64_t row, int64_t ld, int col,
                                        int64_t rows, int cols) {
@@ -46,31 +57,34 @@ __device__ inline float4 load4_guarded(const float *base, int64_t row, int64_t l
   return v;
 }
 
+// How one product's tiles are dealt to the blocks (one tile or piece
+// each): blocks 0 .. dp-1 compute tiles 0 .. dp-1 whole; the rem tiles
+// dp .. T-1 are cut into S pieces of the contraction, and the blocks after
+// them compute piece v = piece v / rem of tile dp + v mod rem (v < rem S).
+struct Share {
+  int64_t T;   // tiles of C
+  int64_t dp;  // tiles computed whole (a multiple of kXcd)
+  int nj;      // tiles along j
+  int ns;      // contraction steps (kStep deep) per tile
+  int rem;     // tiles cut into pieces
+  int S;       // pieces per cut tile
+  int npb;     // blocks for the pieces: rem S rounded up to a multiple of kXcd
+};
+
+// floats of one partial tile (row-major, pitch kTile)
+constexpr int kSlotFloats = kTile * kTile;
+
 template <bool A_PCONTIG>
 __global__ __launch_bounds__(256) void gemm_f32(const float *__restrict__ a, int64_t lda,
                                                 const float *__restrict__ b, int64_t ldb, int I,
-                                                int J, int P, int S, float *__restrict__ c,
-                                                int64_t ldc, int64_t slab) {
+                                                int J, int P, float *__restrict__ c,
+                                                int64_t ldc, Share sh, float *__restrict__ part) {
   __shared__ __attribute__((aligned(16))) float As[2][kStep * kPitch];  // [p][i]
   __shared__ __attribute__((aligned(16))) float Bs[2][kStep * kPitch];  // [p][j]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
-  // XCD x runs blocks x, x + 8, ...: give it a contiguous run of tiles
-  // (neighbours along j share the A panel in that XCD's L2)
-  const int nj = (J + kTile - 1) / kTile;
-  const int tiles = nj * ((I + kTile - 1) / kTile);
-  const int per = (int)(gridDim.x / kXcd);
-  const int vb0 = (int)(blockIdx.x % kXcd) * per + (int)(blockIdx.x / kXcd);
-  if (vb0 >= tiles * S) return;
-  // work item vb0: tile vb0 % tiles, contraction piece vb0 / tiles (of S
-  // pieces of whole steps); piece s writes its partial tile to slab s of c
-  const int vb = vb0 % tiles, sp = vb0 / tiles;
-  const int nsteps = (P + kStep - 1) / kStep;
-  const int pb = (int)((int64_t)sp * nsteps / S) * kStep;
-  const int pe = min(P, (int)((int64_t)(sp + 1) * nsteps / S) * kStep);
-  c += (int64_t)sp * slab;
-  const int i0 = (vb / nj) * kTile, j0 = (vb % nj) * kTile;
 
+  int i0 = 0, j0 = 0, pe = 0;  // the current tile's corner and contraction end
   float4 ra[2], rb[2];
   auto gload = [&](int p0) __attribute__((always_inline)) {
 #pragma unroll
@@ -105,53 +119,140 @@ __global__ __launch_bounds__(256) void gemm_f32(const float *__restrict__ a, int
   };
 
   v4f acc[4][4];
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  gload(pb);
-  sstore(0);
-  __syncthreads();
   const int ai = wi * 64 + (lane & 15), bj = wj * 64 + (lane & 15), pq = lane >> 4;
-  int cur = 0;
-  for (int p0 = pb; p0 < pe; p0 += kStep) {
-    const bool more = p0 + kStep < pe;
-    if (more) gload(p0 + kStep);
+  // acc = steps s0 .. s1-1 of tile t's contraction
+  auto run = [&](int64_t t, int s0, int s1) __attribute__((always_inline)) {
+    i0 = (int)(t / sh.nj) * kTile;
+    j0 = (int)(t % sh.nj) * kTile;
+    pe = min(P, s1 * kStep);
 #pragma unroll
-    for (int kk = 0; kk < kStep / 4; ++kk) {
-      const float *arow = &As[cur][(4 * kk + pq) * kPitch + ai];
-      const float *brow = &Bs[cur][(4 * kk + pq) * kPitch + bj];
-      float av[4], bv[4];
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        av[t] = arow[16 * t];
-        bv[t] = brow[16 * t];
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[x], bv[y], acc[x][y], 0, 0, 0);
-    }
-    if (more) sstore(cur ^ 1);
+      for (int y = 0; y < 4; ++y) acc[x][y] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // (the previous run ended with a barrier: no wave still reads buffer 0)
+    gload(s0 * kStep);
+    sstore(0);
     __syncthreads();
-    cur ^= 1;
-  }
-
+    int cur = 0;
+    for (int p0 = s0 * kStep; p0 < pe; p0 += kStep) {
+      const bool more = p0 + kStep < pe;
+      if (more) gload(p0 + kStep);
+#pragma unroll
+      for (int kk = 0; kk < kStep / 4; ++kk) {
+        const float *arow = &As[cur][(4 * kk + pq) * kPitch + ai];
+        const float *brow = &Bs[cur][(4 * kk + pq) * kPitch + bj];
+        float av[4], bv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          av[q] = arow[16 * q];
+          bv[q] = brow[16 * q];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[x], bv[y], acc[x][y], 0, 0, 0);
+      }
+      if (more) sstore(cur ^ 1);
+      __syncthreads();
+      cur ^= 1;
+    }
+  };
   // lane (j = l % 16, q = l / 16) holds C[4 q + r][j] of each 16 x 16 tile
+  auto store_tile = [&](float *dst, int64_t ld, int rows, int cols) __attribute__((always_inline)) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < 4; ++x) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + wi * 64 + 16 * x + 4 * pq + r;
-      if (i >= I) continue;
+      for (int r = 0; r < 4; ++r) {
+        const int i = wi * 64 + 16 * x + 4 * pq + r;
+        if (i >= rows) continue;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int j = j0 + wj * 64 + 16 * y + (lane & 15);
-        if (j < J) c[(int64_t)i * ldc + j] = acc[x][y][r];
+        for (int y = 0; y < 4; ++y) {
+          const int j = wj * 64 + 16 * y + (lane & 15);
+          if (j < cols) dst[(int64_t)i * ld + j] = acc[x][y][r];
+        }
       }
     }
+  };
+
+  // XCD x runs blocks x, x + 8, ...: give it a contiguous range of the
+  // whole tiles and then of the pieces (neighbouring tiles share operand
+  // panels in that XCD's L2)
+  const int64_t bid = blockIdx.x;
+  const int xcd = (int)(bid % kXcd);
+  int64_t t;
+  int s0 = 0, s1 = sh.ns;
+  float *dst;
+  int64_t ld = ldc;
+  int rows, cols;
+  if (bid < sh.dp) {
+    t = xcd * (sh.dp / kXcd) + bid / kXcd;
+    run(t, s0, s1);
+    dst = c + (int64_t)i0 * ldc + j0;
+    rows = I - i0;
+    cols = J - j0;
+  } else {
+    const int v = xcd * (sh.npb / kXcd) + (int)((bid - sh.dp) / kXcd);
+    if (v >= sh.rem * sh.S) return;
+    t = sh.dp + v % sh.rem;
+    const int k = v / sh.rem;
+    s0 = (int)((int64_t)k * sh.ns / sh.S);
+    s1 = (int)((int64_t)(k + 1) * sh.ns / sh.S);
+    run(t, s0, s1);
+    if (sh.S > 1) {
+      dst = part + (int64_t)v * kSlotFloats;
+      ld = kTile;
+      rows = cols = kTile;
+    } else {
+      dst = c + (int64_t)i0 * ldc + j0;
+      rows = I - i0;
+      cols = J - j0;
+    }
+  }
+  store_tile(dst, ld, rows, cols);
+}
+
+// C tiles dp .. dp + rem - 1 = their S partial tiles added in piece order;
+// thread: four consecutive floats of one tile row.
+__global__ __launch_bounds__(256) void sum_pieces(const float *__restrict__ part, int rem, int S,
+                                                  int64_t dp, int nj, int I, int J,
+                                                  float *__restrict__ c, int64_t ldc) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)rem * (kSlotFloats / 4)) return;
+  const int r = (int)(idx / (kSlotFloats / 4)), e = (int)(idx % (kSlotFloats / 4)) * 4;
+  const int64_t t = dp + r;
+  const int i = (int)(t / nj) * kTile + e / kTile, j = (int)(t % nj) * kTile + e % kTile;
+  if (i >= I || j >= J) return;
+  const float4 *p = reinterpret_cast<const float4 *>(part + (int64_t)r * kSlotFloats + e);
+  const int64_t step = (int64_t)rem * (kSlotFloats / 4);  // piece to piece
+  float4 acc = p[0];
+  int s = 1;
+  for (; s + 4 <= S; s += 4) {  // four pieces' loads in flight
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = p[(s + u) * step];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc.x = acc.x + v[u].x;
+      acc.y = acc.y + v[u].y;
+      acc.z = acc.z + v[u].z;
+      acc.w = acc.w + v[u].w;
+    }
+  }
+  for (; s < S; ++s) {
+    const float4 v = p[s * step];
+    acc.x = acc.x + v.x;
+    acc.y = acc.y + v.y;
+    acc.z = acc.z + v.z;
+    acc.w = acc.w + v.w;
+  }
+  float *dst = c + (int64_t)i * ldc + j;
+  if (j + 3 < J) {
+    *reinterpret_cast<float4 *>(dst) = acc;  // ldc % 4 == 0, 16-byte aligned c
+  } else {
+    dst[0] = acc.x;
+    if (j + 1 < J) dst[1] = acc.y;
+    if (j + 2 < J) dst[2] = acc.z;
   }
 }
 
@@ -188,67 +289,65 @@ __global__ __launch_bounds__(64) void colsum_finish(const float *__restrict__ pa
   db[n] = s;
 }
 
-// C = the S partial tiles (slabs of I x J, pitch J) added in slab order.
-__global__ __launch_bounds__(256) void sum_slabs(const float *__restrict__ part, int S,
-                                                 int64_t slab, int I, int J,
-                                                 float *__restrict__ c, int64_t ldc) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int j4 = (J + 3) / 4;
-  if (idx >= (int64_t)I * j4) return;
-  const int i = (int)(idx / j4), j = (int)(idx - (int64_t)i * j4) * 4;
-  const float *p = part + (int64_t)i * J + j;
-  if ((J & 3) == 0 && j + 3 < J) {  // 16-byte aligned: slabs have pitch J
-    float4 acc = *reinterpret_cast<const float4 *>(p);
-    for (int s = 1; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4 *>(p + s * slab);
-      acc.x = acc.x + v.x;
-      acc.y = acc.y + v.y;
-      acc.z = acc.z + v.z;
-      acc.w = acc.w + v.w;
-    }
-    *reinterpret_cast<float4 *>(c + (int64_t)i * ldc + j) = acc;
-  } else {
-    for (int e = j; e < J; ++e) {
-      float acc = p[e - j];
-      for (int s = 1; s < S; ++s) acc = acc + p[e - j + s * slab];
-      c[(int64_t)i * ldc + e] = acc;
-    }
-  }
+// Blocks resident at once: four per compute unit (about 104 VGPRs and
+// 36 KB of LDS each).
+int resident_blocks() {
+  const int cus = device_cus();
+  return 4 * (cus > 0 ? cus : 256);
 }
 
-// Pieces of the contraction: enough work items to fill four rounds of the
-// chip when the tiles alone are fewer, each piece at least 256 deep.
-int contraction_pieces(int64_t I, int64_t J, int64_t P) {
-  const int64_t tiles = ceil_div(I, kTile) * ceil_div(J, kTile);
-  int64_t S = 1;
-  while (S < kMaxPieces && tiles * S < 1024 && P / (2 * S) >= 256) S *= 2;
-  return (int)S;
+// A piece is at least kMinRun steps deep (each costs a 64 KB partial tile
+// written and read back) and no tile is cut into more than kMaxPieces.
+constexpr int kMinRun = 8;
+constexpr int kMaxPieces = 16;
+
+// The tiles beyond the last whole round of B resident blocks (all tiles
+// when there are fewer than B) are cut into enough pieces for a round:
+// S = ceil(B / rem), at most kMaxPieces and each piece at least kMinRun
+// steps deep.
+Share plan_share(int64_t I, int64_t J, int64_t P) {
+  Share sh{};
+  const int B = resident_blocks();
+  sh.nj = (int)ceil_div(J, kTile);
+  sh.T = ceil_div(I, kTile) * sh.nj;
+  sh.ns = (int)ceil_div(P, kStep);
+  sh.rem = (int)(sh.T % B);
+  sh.dp = sh.T - sh.rem;
+  sh.S = 1;
+  if (sh.rem > 0)
+    sh.S = (int)std::max<int64_t>(
+        1, std::min<int64_t>({ceil_div(B, sh.rem), sh.ns / kMinRun, (int64_t)kMaxPieces}));
+  sh.npb = (int)round_up((int64_t)sh.rem * sh.S, kXcd);
+  return sh;
+}
+
+// Workspace of the pieces: one partial tile each (fewer than 2B).
+int64_t share_bytes(const Share &sh) {
+  return sh.S > 1 ? (int64_t)sh.rem * sh.S * kSlotFloats * 4 : 0;
 }
 
 template <bool A_PCONTIG>
 hipError_t launch_gemm_f32(const float *a, int64_t lda, const float *b, int64_t ldb, int64_t I,
-                           int64_t J, int64_t P, float *c, int64_t ldc, float *pieces,
+                           int64_t J, int64_t P, float *c, int64_t ldc, float *part,
                            hipStream_t st) {
-  const int64_t tiles = ceil_div(I, kTile) * ceil_div(J, kTile);
-  const int S = pieces ? contraction_pieces(I, J, P) : 1;
-  const int64_t blocks = ceil_div(tiles * S, kXcd) * kXcd;
-  const int64_t slab = I * J;  // a partial tile set, pitch J
-  hipLaunchKernelGGL(gemm_f32<A_PCONTIG>, dim3((unsigned)blocks), dim3(256), 0, st, a, lda, b,
-                     ldb, (int)I, (int)J, (int)P, S, S > 1 ? pieces : c, S > 1 ? J : ldc, slab);
+  const Share sh = plan_share(I, J, P);
+  hipLaunchKernelGGL(gemm_f32<A_PCONTIG>, dim3((unsigned)(sh.dp + sh.npb)), dim3(256), 0, st, a, lda, b,
+                     ldb, (int)I, (int)J, (int)P, c, ldc, sh, part);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
-  hipLaunchKernelGGL(sum_slabs, dim3((unsigned)ceil_div(I * ceil_div(J, 4), 256)), dim3(256), 0,
-                     st, pieces, S, slab, (int)I, (int)J, c, ldc);
+  if (e != hipSuccess || sh.S == 1) return e;
+  hipLaunchKernelGGL(sum_pieces,
+                     dim3((unsigned)ceil_div((int64_t)sh.rem * (kSlotFloats / 4), 256)),
+                     dim3(256), 0, st, part, sh.rem, sh.S, sh.dp, sh.nj, (int)I, (int)J, c, ldc);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const size_t db = (size_t)(4 * ceil_div(M, kColChunk) * N);
-  const int S = contraction_pieces(M, K, N);  // dx = g W: M x K tiles, N deep
-  const size_t dx = S > 1 ? (size_t)(4 * S * M * K) : 0;
-  return std::max(db, dx);
+  const int64_t db = 4 * ceil_div(M, kColChunk) * N;
+  const int64_t dx = share_bytes(plan_share(M, K, N));  // dx = g W: M x K tiles, N deep
+  const int64_t dw = share_bytes(plan_share(N, K, M));  // dW = g^T x: N x K tiles, M deep
+  return (size_t)std::max({db, dx, dw});
 }
 
 hipError_t launch_backward(const float *g, int64_t ldg, const float *x, int64_t ldx,
@@ -261,7 +360,7 @@ hipError_t launch_backward(const float *g, int64_t ldg, const float *x, int64_t 
     if (e != hipSuccess) return e;
   }
   if (dW) {  // dW[n][k] = sum_m g[m][n] x[m][k]
-    e = launch_gemm_f32<false>(g, ldg, x, ldx, N, K, M, dW, lddw, nullptr, st);
+    e = launch_gemm_f32<false>(g, ldg, x, ldx, N, K, M, dW, lddw, part, st);
     if (e != hipSuccess) return e;
   }
   if (db) {

@@ -685,6 +685,8 @@ bool large_tiles(int64_t M, int64_t N, int64_t ldx, int64_t ldw) {
          N * ldw < (INT64_C(1) << 31) && M <= INT32_MAX && N <= INT32_MAX;
 }
 
+}  // namespace
+
 // compute units of the current device (cached per device)
 int device_cus() {
   // a value per device; threads that race to fill it store the same value
@@ -699,6 +701,8 @@ int device_cus() {
   }
   return n;
 }
+
+namespace {
 
 // Launch epochs of split launches: 56-bit, never 0, one per launch.  They
 // start at a random point per process, so counter words left in a

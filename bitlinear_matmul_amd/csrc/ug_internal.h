@@ -139,16 +139,20 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s,
                        const float *bias,
                        int64_t M, int64_t N, int64_t K, int32_t *acc,
                        int64_t ldacc, float *y, int64_t ldy, hipStream_t st);
+// Compute units of the current device (0 if it cannot be queried).
+int device_cus();
 // Straight-through backward: dx = g W and dW = g^T x on the fp32 matrix
 // cores, db = column sums of g; `part` (backward_workspace_bytes) holds the
-// column chunk sums and dx's contraction pieces.  Null outputs are skipped.
+// column chunk sums and the products' partial tiles.  Null outputs are
+// skipped.
 size_t backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_backward(const float *g, int64_t ldg, const float *x, int64_t ldx,
                            const float *W, int64_t ldw, int64_t M, int64_t N, int64_t K,
                            float *dx, int64_t lddx, float *dW, int64_t lddw, float *db,
                            float *part, hipStream_t st);
-// Top-k sampling: one block per row of logits.
+// Matrix-core issue-rate probe: `blocks` blocks of back-to-back MFMAs.
 hipError_t launch_mfma_rate(int kind, int blocks, int iters, int32_t *sink, hipStream_t st);
+// Top-k sampling: one block per row of logits.
 hipError_t launch_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V, int64_t k,
                               float temp, const float *u, int32_t *tok, int32_t *idx_out,
                               int64_t ldi, float *val_out, int64_t ldv, float *prob_out,

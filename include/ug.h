@@ -351,11 +351,12 @@ ug_status ug_bitlinear_gemm_tiled(const int8_t *xq, int64_t ldx, const float *s,
                                   int64_t ldy, void *ws, size_t ws_bytes,
                                   int32_t tile, int32_t k_splits, void *stream);
 
-/* Bytes of workspace ug_bitlinear_backward needs: the larger of
- * 4 * ceil(M / 32) * N (db's chunk sums) and, when dx = g W has fewer than
- * 1024 output tiles of 128 x 128, 4 * S * M * K for its S contraction
- * pieces (S the smallest power of two, at most 8, that gives 1024 work
- * items while each piece stays at least 256 deep).  0 for invalid sizes. */
+/* Bytes of workspace ug_bitlinear_backward needs on the current device: the
+ * larger of 4 * ceil(M / 32) * N (db's chunk sums) and, for each product,
+ * 64 KB per piece of the 128 x 128 output tiles it cuts along the
+ * contraction (the rem tiles beyond its last whole round of B = 4 x CUs
+ * blocks, each in ceil(B / rem) pieces or fewer: under 2B pieces, 128 MB
+ * on 256 CUs).  0 for invalid sizes. */
 size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -371,11 +372,14 @@ size_t ug_bitlinear_backward_workspace_size(int64_t M, int64_t N, int64_t K);
  *  (not computed; not all three).  x is read only for dW, W only for dx.
  *  Pitches >= the row length and multiples of 4; matrix pointers 16-byte
  *  aligned.  ws: device workspace of ws_bytes >= the size query.
- * Arithmetic: fp32 products and sums on the fp32 matrix cores (dx, dW; a
- * few-tile dx adds its contraction pieces in piece order) and a
- * fixed-order fp32 column sum (db: 32-row chunks added in order, then the
- * chunk sums in order); the same bits on every run, each result within the
- * fp32 rounding bound gamma_(n+8) * sum |terms| of the exact sum.  UG_ERR_UNSUPPORTED for
+ * Arithmetic: fp32 products and sums on the fp32 matrix cores (dx, dW; the
+ * tiles beyond the last whole round of blocks may be computed in pieces
+ * along the contraction, added in piece order) and a fixed-order fp32 column sum
+ * (db: 32-row chunks added in order, then the chunk sums in order); the
+ * same bits on every run on a given device (the cut into pieces depends on
+ * the shape and the CU count), each result within the fp32 rounding bound
+ * gamma_(n+8) * sum |terms| of the exact sum.  Calls that share ws must not
+ * overlap.  UG_ERR_UNSUPPORTED for
  * M >= 2^21 or N, K > 2^30.
  */
 ug_status ug_bitlinear_backward(const float *g, int64_t ldg, const float *x,

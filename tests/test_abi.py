@@ -97,6 +97,61 @@ def test_k_split_ranges_cover_each_tile_once():
             assert slots == set(range(T * S))
 
 
+def _share(I, J, P, B=1024):
+    """Host mirror of the backward products' plan: tiles beyond the last
+    whole round of B blocks (all, if fewer than B) are cut along the
+    contraction into S = ceil(B / rem) pieces of 16-deep steps, at most 16
+    and each piece at least 8 steps."""
+    T = -(-I // 128) * -(-J // 128)
+    ns = -(-P // 16)
+    rem = T % B
+    S = max(1, min(-(-B // rem), ns // 8, 16)) if rem else 1
+    npb = -(-(rem * S) // 8) * 8
+    return T, ns, rem, S, npb
+
+
+def test_backward_pieces_cover_each_tile_once():
+    """Block b < dp computes tile (b mod 8) dp / 8 + b // 8 whole; block
+    dp + b' computes piece v = (b' mod 8) npb / 8 + b' // 8 (if v < rem S):
+    steps [k ns / S, (k+1) ns / S) of tile dp + v mod rem, k = v // rem,
+    into partial slot v.  Every step of every tile is computed once, the
+    slots are distinct, each XCD (block mod 8) gets a contiguous run of
+    tiles and of pieces, and the pieces fill about a round."""
+    for I, J, P in ((6912, 2560, 2048), (2048, 2560, 6912), (2560, 3840, 48), (48, 3840, 2560),
+                    (4096, 4096, 16), (4224, 4096, 96), (96, 4096, 4224), (128, 128, 300),
+                    (8192, 4096, 100), (8320, 4096, 40), (16384, 2048, 64), (300, 64, 128),
+                    (64, 128, 300), (1, 1, 1), (200, 131, 2100), (128, 128, 65536),
+                    (6912, 2048, 2048)):
+        T, ns, rem, S, npb = _share(I, J, P)
+        dp = T - rem
+        assert dp % 1024 == 0 and npb % 8 == 0
+        assert rem * S < 2 * 1024 and (rem * S >= 1024 or S == 16 or S == max(1, ns // 8))
+        done = set()
+        slots = set()
+        per_xcd = {x: [] for x in range(8)}
+        for b in range(dp + npb):
+            if b < dp:
+                t = (b % 8) * (dp // 8) + b // 8
+                steps = range(ns)
+            else:
+                v = (b % 8) * (npb // 8) + (b - dp) // 8
+                if v >= rem * S:
+                    continue
+                assert v not in slots
+                slots.add(v)
+                t, k = dp + v % rem, v // rem
+                steps = range(k * ns // S, (k + 1) * ns // S)
+                assert len(steps) >= min(8, ns)
+            per_xcd[b % 8].append(t)
+            for st in steps:
+                assert (t, st) not in done
+                done.add((t, st))
+        assert len(done) == T * ns
+        for x, ts in per_xcd.items():     # whole tiles: one contiguous, increasing run
+            whole = [t for t in ts if t < dp]
+            assert whole == list(range(whole[0], whole[0] + len(whole))) if whole else True
+
+
 # Fake device addresses: aligned and misaligned.  They are never
 # dereferenced because every call below fails validation.
 A = ctypes.c_void_p(0x100000)
@@ -332,10 +387,17 @@ def test_sample_topk_rejects(ug):
 def test_backward_rejects(ug):
     L = ug.lib()
     E = ug.UG_ERR_INVALID_ARG
+    # (no device here: the library assumes 256 CUs, 1024 resident blocks;
+    # partial tiles of 64 KB)
     need = L.ug_bitlinear_backward_workspace_size(300, 64, 128)
-    assert need == 4 * 10 * 64        # db's chunk sums; dx too shallow (N = 64) to split
-    # dx = g W at 2048 x 2560 (320 tiles), 6912 deep: 4 pieces
-    assert L.ug_bitlinear_backward_workspace_size(2048, 6912, 2560) == 4 * 4 * 2048 * 2560
+    # dx: 3 tiles 4 steps deep, not cut; dW: one tile 19 steps deep, cut in
+    # 2 pieces (at least 8 steps each)
+    assert need == 2 * 65536
+    # db's chunk sums alone: dx one tile of 2 steps, dW 3 tiles of 1 step
+    assert L.ug_bitlinear_backward_workspace_size(20, 32, 300) == 4 * 1 * 32
+    # dx = g W at 2048 x 2560: 320 tiles of 432 steps in 4 pieces each (dW:
+    # 1024 whole tiles and 56 in 16 pieces of 8 steps)
+    assert L.ug_bitlinear_backward_workspace_size(2048, 6912, 2560) == 1280 * 65536
 
     def call(g=A, ldg=64, M=300, N=64, K=128, dx=ctypes.c_void_p(0x500000), dW=NULL, db=NULL,
              ws=NULL, ws_bytes=0, ldw=128):

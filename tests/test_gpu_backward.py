@@ -3,10 +3,10 @@
 a byte-graph": dL/dx = g W, dL/dW = g^T x, dL/db = sum g, with W the fp32
 masters.  Compared with the oracle's double-precision sums within the fp32
 rounding bound: a sum of n products, computed with one rounding per product
-and per addition in any association, is within gamma(n+1) sum |a_i b_i| of
-the exact value; a product cut into up to 8 pieces along the contraction
-adds up to 7 more roundings, and the oracle's own fp32 rounding u |exact|;
-the test allows gamma(n+8) sum |a_i b_i|."""
+and per addition in any association (pieces of the contraction added at the
+end included: no term passes through more than n roundings), is within
+gamma(n) sum |a_i b_i| of the exact value; with the oracle's own fp32
+rounding u |exact| and some slack the test allows gamma(n+8) sum |a_i b_i|."""
 import numpy as np
 import pytest
 
@@ -23,8 +23,7 @@ def _case(*a):
 
 
 def gam(n):
-    # n products and additions, plus up to 8 contraction pieces added at the
-    # end and the oracle's own rounding
+    # n roundings on any term's path, the oracle's own rounding, and slack
     return (n + 8) * U / (1 - (n + 8) * U)
 
 
@@ -49,7 +48,13 @@ def _data(seed, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(64, 96, 80), (130, 257, 33), (1, 1, 1), (7, 300, 129),
                                    (300, 5, 1000), (256, 384, 1536),
                                    (200, 2100, 131),   # dx cut into contraction pieces, K % 4 != 0
-                                   (640, 4100, 300)])  # dx in pieces with a ragged last piece
+                                   (640, 4100, 300),   # dx in pieces with a ragged last piece
+                                   # (on 256 CUs) dx: 30 tiles in 16 pieces each; dW: 600
+                                   # tiles 3 steps deep, too shallow to cut
+                                   (48, 2560, 3840),
+                                   # dx: 32 tiles in 16 pieces; dW: 1024 tiles, one
+                                   # whole round
+                                   (16, 4096, 4096)])
 def test_backward_parity(dev, M, N, K):
     _case("backward", M, N, K)
     g, x, W = _data([95, M, N, K], M, N, K)
@@ -92,3 +97,33 @@ def test_backward_outputs_one_at_a_time(dev):
     for name in ("dx", "dW", "db"):
         one = ug.ug_bitlinear_backward(gd, xd, Wd, want=(name,))
         assert np.array_equal(host(one[name]).view(np.uint32), allr[name].view(np.uint32))
+
+
+def test_backward_repeat_and_junk_workspace(dev):
+    """A workspace full of junk, and the same workspace again on the next
+    call, give the same bits as a fresh one: every partial tile is written
+    before it is read (on 256 CUs: dx's 64 tiles in 16 pieces each; dW's 32
+    tiles beyond a whole round of blocks in 2 pieces each).  Sampled rows
+    of both products against the oracle."""
+    import torch
+    M, N, K = 256, 4224, 4096
+    g, x, W = _data(99, M, N, K)
+    gd, xd, Wd = pitched(g), pitched(x), pitched(W)
+    first = {k: host(v) for k, v in ug.ug_bitlinear_backward(gd, xd, Wd).items()}
+    ws = torch.full((ug.lib().ug_bitlinear_backward_workspace_size(M, N, K),), 0xA5,
+                    dtype=torch.uint8, device=gd.device)
+    for rep in range(3):
+        again = ug.ug_bitlinear_backward(gd, xd, Wd, ws=ws)
+        for name in ("dx", "dW", "db"):
+            assert np.array_equal(host(again[name]).view(np.uint32),
+                                  first[name].view(np.uint32)), (rep, name)
+    rng = np.random.default_rng(100)
+    ms = np.sort(rng.choice(M, 24, replace=False))
+    rx = oracle.bitlinear_backward(g[ms], x[ms], W, want=("dx",))
+    _within(first["dx"][ms], rx["dx"],
+            np.abs(g[ms].astype(np.float64)) @ np.abs(W.astype(np.float64)), N, "dx rows")
+    ns = np.concatenate([np.arange(N - 8, N), rng.choice(N - 8, 16, replace=False)])
+    ns = np.sort(ns)
+    rw = oracle.bitlinear_backward(np.ascontiguousarray(g[:, ns]), x, W[ns], want=("dW",))
+    _within(first["dW"][ns], rw["dW"],
+            np.abs(g[:, ns].astype(np.float64)).T @ np.abs(x.astype(np.float64)), M, "dW rows")
