@@ -121,6 +121,8 @@ def parse():
     p.add_argument("--workload", default="decode_stack",
                    choices=["decode_stack", "sweep", "prefill", "stack", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-marginal", action="store_true",
+                   help="stream_m1: skip the launches of twice the problems (profiling)")
     p.add_argument("--no-extra", action="store_true",
                    help="decode_stack: skip the extra measurement points")
     p.add_argument("--only", default=None,
@@ -149,15 +151,15 @@ TRAFFIC = {
     # dispatch, medians), calibrated by a 256 MiB copy: bytes = FETCH x 1024 x
     # 1.99977 + WRITE x 1024.  A record holds only while the kernel sources
     # it was taken on are unchanged.
-    # profiles/gemv_fine_grouped_decode_stack.md: 2005.9 KiB / 146.4 KiB
+    # profiles/gemv_fine_grouped_decode_stack.md: 2008.4 KiB / 146.4 KiB
     "decode_stack": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                              "7a2a5f082270679451eb78a55b2654e6cfb9c9f87e57826f311ea449d1cebe2b"},
-                         bytes_per_launch=4257560),
+                              "02e04197ab5dde7f92c93653876e80db815573198ad41d01c5e56630d123e498"},
+                         bytes_per_launch=4262676),
     # profiles/gemv_stream_grouped_sweep_m1.md: M=1 2560->6912, 37 problems per
-    # launch: 64207.5 KiB / 189.2 KiB
+    # launch, spread staging: 64139.5 KiB / 191.7 KiB
     "sweep": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                       "7a2a5f082270679451eb78a55b2654e6cfb9c9f87e57826f311ea449d1cebe2b"},
-                  bytes_per_launch=131674036),
+                       "02e04197ab5dde7f92c93653876e80db815573198ad41d01c5e56630d123e498"},
+                  bytes_per_launch=131532314),
     # profiles/gemm_i8_large_prefill.md: mean of the two shapes' launches
     "prefill": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
                          "02b27e9db0529ba1b218003a0d600a96eb02f97bdc7bbbc8ef0ed0e7862fabf3"},
@@ -182,11 +184,11 @@ TRAFFIC = {
     "sampler": dict(src={"bitlinear_matmul_amd/csrc/sampler.hip":
                          "5626fcf9f96f214c619bce97c12f84286293f235fe296ac41c7771d47261fa0e"},
                     bytes_per_launch=67639194),
-    # profiles/gemm_f32_backward.md: mean of the dx call (GEMM + slab sum) and
-    # the dW call
+    # profiles/gemm_f32_backward.md: mean of the dx call and the dW call (each
+    # a GEMM and the sum of its cut tiles' pieces)
     "backward": dict(src={"bitlinear_matmul_amd/csrc/backward.hip":
-                          "f681a6da409af86df1788e520aea31319f073d37630bca2cbe2786a31b629458"},
-                     bytes_per_launch=801258028),
+                          "2582b06d5a06e5dab55f20cf6a235e3908523f6ce3d4c8a9e2384ec04333e669"},
+                     bytes_per_launch=835617886),
 }
 
 
@@ -732,7 +734,7 @@ def measure_backward(torch, ug, M=2048, N=6912, K=2560):
     return res
 
 
-def measure_stream_m1(torch, ug, inputs, M=1, si=0):
+def measure_stream_m1(torch, ug, inputs, M=1, si=0, marginal=True):
     """The streaming decode GEMV at one sweep point (default M = 1,
     2560 -> 6912, PACK5): grouped launches of G distinct weight copies
     (>= 128 MB each), launch sets cycling through >= 2 GiB of copies (cold);
@@ -745,31 +747,47 @@ def measure_stream_m1(torch, ug, inputs, M=1, si=0):
     pk = ug.ug_pack_trits(wq)
     del wq, W
     G = max(1, (128 << 20) // (N * ug.packed_pitch(K)))
-    n_sets = max(2, COLD_BYTES // (G * N * ug.packed_pitch(K)) + 1)
-    copies = [[pk.clone() for _ in range(G)] for _ in range(n_sets)]
     xq, s = ug.ug_quant_act(torch.from_numpy(x64[:M].copy()).to(dev))
     y = ug.empty_pitched(M, N, torch.float32, dev)
-    plans = [ug.ug_gemv_plan_init([dict(xq=xq, s=s, w=w, wfmt=ug.UG_W_PACK5, beta=beta, K=K,
-                                         y=y) for w in cs]) for cs in copies]
-    for i in range(2):
-        ug.ug_bitlinear_gemv_grouped(plans[i % n_sets])
-    med, p10, p90 = launch_stats(
-        torch, lambda i: ug.ug_bitlinear_gemv_grouped(plans[(i + 2) % n_sets]), stream)
+
+    def timed(g):
+        """Median launch time of groups of g weight copies, cold."""
+        n_sets = max(2, COLD_BYTES // (g * N * ug.packed_pitch(K)) + 1)
+        copies = [[pk.clone() for _ in range(g)] for _ in range(n_sets)]
+        plans = [ug.ug_gemv_plan_init([dict(xq=xq, s=s, w=w, wfmt=ug.UG_W_PACK5, beta=beta, K=K,
+                                             y=y) for w in cs]) for cs in copies]
+        for i in range(2):
+            ug.ug_bitlinear_gemv_grouped(plans[i % n_sets])
+        r = launch_stats(
+            torch, lambda i: ug.ug_bitlinear_gemv_grouped(plans[(i + 2) % n_sets]), stream)
+        variant = plans[0].info.variant
+        del plans, copies
+        torch.cuda.empty_cache()
+        return r, n_sets, variant
+
+    (med, p10, p90), n_sets, variant = timed(G)
+    # the same with twice the copies per launch: the difference is the
+    # streaming time of G problems, the rest the launch's fixed cost
+    med2 = timed(2 * G)[0][0] if marginal else med
     wbytes = N * (-(-K // 5)) * G
     alg = gemv_alg_bytes(M, N, K) * G
     achieved = alg / (med * 1e-6) / 1e9
+    rate2 = alg / ((med2 - med) * 1e-6) / 1e9 if med2 > med else None
+    kernel = "gemv_stream_grouped<PACK5, 1%s>" % (", spread" if (variant >> 13) & 1 else "")
     out = dict(value=wbytes / (med * 1e-6) / 1e9, unit="GB/s",
                point="M=%d K=%d N=%d, PACK5, %d weight copies per launch, %d launch sets "
                      "(%.2f GiB) cycled" % (M, K, N, G, n_sets,
                                            n_sets * G * N * ug.packed_pitch(K) / 2 ** 30),
                median_launch_us=med, p10_launch_us=p10, p90_launch_us=p90,
-               roofline=dict(bound="hbm", kernel="gemv_stream_grouped<PACK5, 1>",
+               median_launch_us_2x=med2 if marginal else None,
+               marginal_GBps=rate2, fixed_us_per_launch=2 * med - med2 if marginal else None,
+               roofline=dict(bound="hbm", kernel=kernel,
                              achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=achieved / HBM_PEAK_GBS,
+                             frac_marginal=rate2 / HBM_PEAK_GBS if rate2 else None,
                              traffic=traffic_for("sweep") if (M, si) == (1, 0) else None,
                              median_launch_us=med, alg_bytes_per_launch=alg))
     log("stream", out)
-    del plans, copies
     return out
 
 
@@ -1134,7 +1152,8 @@ def main():
               "vendor_int8_gemm": lambda: measure_vendor_gemm(torch, ug, inputs),
               "hbm_copy_rate": lambda: measure_copy_rate(torch),
               "pack": lambda: measure_pack(torch, ug, inputs),
-              "stream_m1": lambda: measure_stream_m1(torch, ug, inputs),
+              "stream_m1": lambda: measure_stream_m1(torch, ug, inputs,
+                                                     marginal=not args.no_marginal),
               "requant_pack5": lambda: measure_requant_pack5(torch, ug, inputs),
               "attention_decode": lambda: measure_attention_decode(torch, ug),
               "sampler": lambda: measure_sampler(torch, ug),

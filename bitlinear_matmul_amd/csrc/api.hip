@@ -279,12 +279,14 @@ ug_status ug_bitlinear_gemv_grouped(const void *plan, const ug_gemv_plan_info *i
   if (info->count < 1 || info->total_items < 1 || info->grid < 1 ||
       info->grid > ug::kGemvBlocks)
     return UG_ERR_INVALID_ARG;
-  // variant = 4096 * tiny + 2048 * chunked + 1024 * short + 512 * fused +
-  // 256 * fine + 16 * wfmt + mb (short and fused only with fine, tiny only
-  // with short, chunked only without fine)
+  // variant = 8192 * spread + 4096 * tiny + 2048 * chunked + 1024 * short +
+  // 512 * fused + 256 * fine + 16 * wfmt + mb (short and fused only with
+  // fine, tiny only with short, chunked only without fine, spread only with
+  // the plain stream split of five-trit weights and one 16-row block)
   const int hi = info->variant >> 8, fine = hi & 1, fmt = (info->variant >> 4) & 15,
             mb = info->variant & 15;
-  if (hi > 31 || (fine && (hi & 8)) || (!fine && (hi & 6)) || ((hi & 16) && !(hi & 4)) ||
+  if (hi > 63 || (fine && (hi & 8)) || (!fine && (hi & 6)) || ((hi & 16) && !(hi & 4)) ||
+      ((hi & 32) && (fine || (hi & 8) || fmt != UG_W_PACK5 || mb != 1)) ||
       (fmt != UG_W_I8 && fmt != UG_W_PACK5) || (mb != 1 && mb != 2 && mb != 4) ||
       (fine && mb != 1))
     return UG_ERR_INVALID_ARG;

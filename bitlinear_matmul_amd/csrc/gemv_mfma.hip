@@ -23,6 +23,13 @@
 //   the same way (each 80-position window as fragment 0..3 holding
 //   x[5g .. 5g+3] of its bytes g, then fragment 4 holding the x[5g+4]), so
 //   every MFMA adds products of matching K positions.
+//   Stream split with one 16-row activation block (when the rows fit):
+//   spread staging instead.  Each packed byte's five activations take 8
+//   staged bytes [x0 x1 x2 x3 x4 0 0 0], and B operand j is the two wide
+//   table entries of bytes 2j and 2j+1 as they come from LDS (t0..t3, then
+//   t4 in all four bytes, three of which meet zero activations): 8 MFMAs
+//   per 16 weight bytes instead of 5, but 16 instead of ~48 vector
+//   instructions, and no register moves, per 16 bytes.
 //   The table fills 64 KB: wide (t0..t3, then t4 in all four bytes), 32
 //   replicas of each 8-byte entry (code e, replica r at byte e * 256 + 8 r),
 //   lane l reads replica l % 32, and each half wave's 32 eight-byte reads
@@ -143,6 +150,25 @@ __host__ __device__ __forceinline__ int stage_pitch(int M, int Kp) {
 __host__ __device__ __forceinline__ int mb_of(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 __host__ __device__ __forceinline__ bool stages_x(int fmt, int M, int K) {
   return (int64_t)M * staged_kp(fmt, mb_of(M), K) <= kXsBytes;
+}
+// Spread staging (stream split, five trits per byte, at most 16 rows): the
+// five codes of every packed weight byte take 8 staged bytes,
+// [x0 x1 x2 x3 x4 0 0 0], so one wide table entry (t0..t3, then t4 in all
+// four bytes) is half of a B operand as it leaves LDS.  A 16-byte weight
+// piece is then 8 matrix instructions instead of 5, with no byte permutes
+// between the table reads and the matrix instructions.  The spread rows
+// (512 bytes per step) sit after the K-order rows, which stay intact.
+constexpr int kSpreadStep = 512;  // spread bytes per row and 64-byte step
+__host__ __device__ __forceinline__ int spread_base(int M, int pitch) {
+  return (M * pitch + 15) & ~15;
+}
+__host__ __device__ __forceinline__ int spread_pitch(int M, int Kp) {
+  return (Kp / 320) * kSpreadStep + (M > 1 ? 16 : 0);
+}
+__host__ __device__ __forceinline__ bool stages_spread(int M, int K) {
+  const int Kp = staged_kp(UG_W_PACK5, 1, K), pitch = stage_pitch(M, Kp);
+  return M <= 16 &&
+         (int64_t)spread_base(M, pitch) + (int64_t)M * spread_pitch(M, Kp) <= kXsBytes;
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -457,10 +483,11 @@ __device__ __forceinline__ void copy_xq4(const GemvDesc &d, Smem<FMT> &sh, const
 
 // NQ: the first batch of x_q dwords is in pl (0: every batch is loaded
 // here, which keeps the registers free for a caller short of them).
-template <int FMT, int NQ, bool WIDE>
+template <int FMT, int NQ, bool WIDE, bool SPREAD = false>
 __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, bool staged, int Kp,
                                              int pitch, bool table, bool zero_slots,
-                                             const PreLoads<NQ> &pl) {
+                                             const PreLoads<NQ> &pl, int sbase = 0,
+                                             int spitch = 0) {
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   if (FMT == UG_W_PACK5 && table) table_store<WIDE>(sh, pl.lut);
   if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
@@ -507,20 +534,37 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
     }
   }
   __syncthreads();
-  if (FMT == UG_W_PACK5 && staged) {  // permute every 80-position window in place, one per thread
+  // every 80-position window, one per thread: permuted in place, or spread
+  // into its 128-byte window of the spread rows
+  if (FMT == UG_W_PACK5 && staged) {
     const int wpr = Kp / 80, nwin = d.M * wpr;
     for (int w0 = tid; w0 < nwin; w0 += kThreads) {
-      const int m = w0 / wpr;
-      uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * pitch + (w0 - m * wpr) * 80);
-      uint32_t X[20], F[20];
+      const int m = w0 / wpr, w = w0 - m * wpr;
+      uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * pitch + w * 80);
+      uint32_t X[20], F[SPREAD ? 32 : 20];
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
         const uint4 q = win[i];
         X[4 * i] = q.x; X[4 * i + 1] = q.y; X[4 * i + 2] = q.z; X[4 * i + 3] = q.w;
       }
-      permute80(X, F);
+      if constexpr (SPREAD) {
+        // weight byte b: codes 5b .. 5b+3 in the first dword, 5b+4 in the
+        // low byte of the second
 #pragma unroll
-      for (int i = 0; i < 5; ++i) win[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
+        for (int b = 0; b < 16; ++b) {
+          const int o = 5 * b, o4 = o + 4;
+          F[2 * b] = (o & 3) ? __builtin_amdgcn_alignbyte(X[(o >> 2) + 1], X[o >> 2], o & 3)
+                             : X[o >> 2];
+          F[2 * b + 1] = (X[o4 >> 2] >> (8 * (o4 & 3))) & 0xffu;
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(sh.xs + sbase + m * spitch + w * 128);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
+      } else {
+        permute80(X, F);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) win[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
+      }
     }
     __syncthreads();
   }
@@ -528,7 +572,7 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
 
 // The quantized activations and scales as outputs (fused quantization, the
 // problem's first block): undo the staging permutation per K position.
-template <int FMT>
+template <int FMT, bool SPREAD = false>
 __device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<FMT> &sh, int pitch) {
   const int tid = threadIdx.x;
   if (d.s)
@@ -538,7 +582,7 @@ __device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<
     for (int idx = tid; idx < d.M * d.K; idx += kThreads) {
       const int m = idx / d.K, k = idx - m * d.K;
       int off = k;
-      if (FMT == UG_W_PACK5) {
+      if (FMT == UG_W_PACK5 && !SPREAD) {  // (spread staging keeps the K-order rows)
         const int w = k / 80, r = k - 80 * w, g = r / 5, t = r - 5 * g;
         // t < 4: fragment g/4, dword g%4, byte t; t == 4: fragment 4, dword g/4, byte g%4
         off = 80 * w + (t < 4 ? 16 * (g >> 2) + 4 * (g & 3) + t : 64 + 4 * (g >> 2) + (g & 3));
@@ -548,9 +592,11 @@ __device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<
   }
 }
 
-template <int FMT, int MB, bool FINE>
+// SPREAD: the spread staging (five trits per byte, MB == 1, stream split).
+template <int FMT, int MB, bool FINE, bool SPREAD = false>
 struct Wave {
-  static constexpr int F1 = Fmt<FMT>::kFrag;
+  static_assert(!SPREAD || (FMT == UG_W_PACK5 && MB == 1 && !FINE), "spread staging");
+  static constexpr int F1 = SPREAD ? 8 : Fmt<FMT>::kFrag;
   static constexpr int SC = Cfg<FMT, MB, FINE>::SC;
   static constexpr int NACC = Cfg<FMT, MB, FINE>::NACC;
   static constexpr int kRGW = Cfg<FMT, MB, FINE>::RGW;
@@ -560,7 +606,9 @@ struct Wave {
   int xbase[MB];  // staged: LDS offset of this lane's activation row (step 0)
   __amdgpu_buffer_rsrc_t wr, xr;
 
-  __device__ __forceinline__ void init(const GemvDesc &d, bool stg, int pitch) {
+  // (spread staging: row m of the spread rows at sbase + m * spitch)
+  __device__ __forceinline__ void init(const GemvDesc &d, bool stg, int pitch, int sbase = 0,
+                                       int spitch = 0) {
     const int lane = threadIdx.x & 63, q = lane >> 4;
     S = steps_of(FMT, d.K);
     NC = (S + SC - 1) / SC;
@@ -572,7 +620,7 @@ struct Wave {
       // rows past M read row M-1: MFMA output row m depends only on input
       // row m, and rows past M are never stored
       const int m = min(16 * b + (lane & 15), d.M - 1);
-      xbase[b] = m * pitch + q * Fmt<FMT>::kLaneK;
+      xbase[b] = SPREAD ? sbase + m * spitch + q * 128 : m * pitch + q * Fmt<FMT>::kLaneK;
     }
   }
 
@@ -600,8 +648,8 @@ struct Wave {
   // Activation fragments of step st for M-block b.
   __device__ __forceinline__ void xfrags(const GemvDesc &d, const int8_t *xs, int st, int b,
                                          v4i (&xf)[F1]) {
-    if (FINE || staged) {
-      const int off = xbase[b] + st * Fmt<FMT>::kStepK;
+    if (SPREAD || FINE || staged) {
+      const int off = xbase[b] + st * (SPREAD ? kSpreadStep : Fmt<FMT>::kStepK);
 #pragma unroll
       for (int j = 0; j < F1; ++j) xf[j] = *reinterpret_cast<const v4i *>(xs + off + 16 * j);
       return;
@@ -642,7 +690,37 @@ struct Wave {
   __device__ __forceinline__ void compute(const GemvDesc &d, const int8_t *xs, const char *lut,
                                           int ch, const uint4 (&wb)[kRGW][SC],
                                           v4i (&acc)[kRGW][MB][NACC]) {
-    if (FMT == UG_W_PACK5) {
+    if constexpr (SPREAD) {
+      // piece p: byte i of the 16 weight bytes -> its table entry; matrix
+      // instruction j takes the entries of bytes 2j and 2j+1 as its B
+      // operand and spread fragment j (their codes) as its A operand
+      constexpr int NP = SC * kRGW;
+      uint2 E[2][16];
+      auto dec = [&](int p, uint2(&e)[16]) {
+        const uint4 &w = wb[p % kRGW][p / kRGW];
+        const uint32_t lr8 = 8u * (threadIdx.x & 31);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          e[i] = *reinterpret_cast<const uint2 *>(
+              lut + __builtin_amdgcn_perm(wd[i >> 2], lr8, 0x0c0c0400u + ((uint32_t)(i & 3) << 8)));
+      };
+      v4i xf[MB][F1];
+      dec(0, E[0]);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int s = p / kRGW, r = p % kRGW;
+        if (r == 0) xfrags(d, xs, ch * SC + s, 0, xf[0]);
+        if (p + 1 < NP) dec(p + 1, E[(p + 1) & 1]);
+        const uint2(&e)[16] = E[p & 1];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const v4i B = {(int)e[2 * j].x, (int)e[2 * j].y, (int)e[2 * j + 1].x, (int)e[2 * j + 1].y};
+          acc[r][0][j % NACC] =
+              __builtin_amdgcn_mfma_i32_16x16x64_i8(xf[0][j], B, acc[r][0][j % NACC], 0, 0, 0);
+        }
+      }
+    } else if (FMT == UG_W_PACK5) {
       constexpr int NP = SC * kRGW;
       uint32_t T[2][20];
       auto dec = [&](int p, uint32_t(&t)[20]) {
@@ -734,9 +812,9 @@ struct Wave {
 // Items [i0, i1) of problem d: wave w takes items i0 + w, i0 + w + 8, ...,
 // each NC units, with the weights of the next two units in flight.  start()
 // issues the first two units' loads, so they travel while the block sets up.
-template <int FMT, int MB>
+template <int FMT, int MB, bool SPREAD = false>
 struct ItemLoop {
-  using W = Wave<FMT, MB, false>;
+  using W = Wave<FMT, MB, false, SPREAD>;
   static constexpr int SC = W::SC, NACC = W::NACC, kRGW = W::kRGW;
   W wv;
   uint4 A[kRGW][SC], B[kRGW][SC], C[kRGW][SC];
@@ -772,8 +850,9 @@ struct ItemLoop {
     }
   }
 
-  __device__ __forceinline__ void start(const GemvDesc &d, bool staged, int pitch, int i0, int i1_) {
-    wv.init(d, staged, pitch);
+  __device__ __forceinline__ void start(const GemvDesc &d, bool staged, int pitch, int i0, int i1_,
+                                        int sbase = 0, int spitch = 0) {
+    wv.init(d, staged, pitch, sbase, spitch);
     const int wave = uniform(threadIdx.x >> 6);
     const int my_items = i0 + wave < i1_ ? (i1_ - i0 - wave + kWaves - 1) / kWaves : 0;
     U = uniform(my_items * wv.NC);
@@ -1045,33 +1124,36 @@ __global__ __launch_bounds__(kThreads) void gemv_chunked_grouped(const GemvDesc 
 // Items [g, e) of problem d (global item numbers).  first: the block's first
 // problem (it builds the decode table, and no earlier problem's waves still
 // read the staging area).
-template <int FMT, int MB>
+template <int FMT, int MB, bool SPREAD>
 __device__ __forceinline__ void stream_problem(Smem<FMT> &sh, const GemvDesc &d, int g, int e,
                                                bool first) {
-  const bool staged = stages_x(FMT, d.M, d.K);
+  const bool staged = SPREAD || stages_x(FMT, d.M, d.K);
   const int Kp = staged_kp(FMT, MB, d.K), pitch = stage_pitch(d.M, Kp);
+  const int sbase = SPREAD ? spread_base(d.M, pitch) : 0;
+  const int spitch = SPREAD ? spread_pitch(d.M, Kp) : 0;
   // (the set-up's loads leave before the weights': two units of weights
   // stay in flight while the block sets up)
   constexpr int NQ = MB <= 2 ? 8 : 0;
   PreLoads<NQ> pl;
   pre_issue<FMT>(d, staged, Kp, first, pl);
   __builtin_amdgcn_sched_barrier(0);
-  ItemLoop<FMT, MB> loop;
-  loop.start(d, staged, pitch, g - d.item_begin, e - d.item_begin);
+  ItemLoop<FMT, MB, SPREAD> loop;
+  loop.start(d, staged, pitch, g - d.item_begin, e - d.item_begin, sbase, spitch);
   __builtin_amdgcn_sched_barrier(0);
   if (!first) __syncthreads();  // the previous problem's staged rows are done
-  setup_finish<FMT, NQ, Cfg<FMT, MB, false>::WIDE>(d, sh, staged, Kp, pitch, first, false, pl);
+  setup_finish<FMT, NQ, Cfg<FMT, MB, false>::WIDE, SPREAD>(d, sh, staged, Kp, pitch, first, false,
+                                                          pl, sbase, spitch);
   // in a scalar register: a use in the loop then waits for no load
   loop.beta = __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, pl.beta)));
   loop.run(d, sh);
-  if (d.x && g == d.item_begin) write_act_outputs<FMT>(d, sh, pitch);
+  if (d.x && g == d.item_begin) write_act_outputs<FMT, SPREAD>(d, sh, pitch);
 }
 
 // The block takes the global items [g0, g1) of the plan (problem p0 holds
 // item g0; problem q owns [item_begin, +items)), crossing into the next
 // problem when its range does.  d0: problem p0's descriptor, which the
 // block's entry carries (fetched with g0 and g1).
-template <int FMT, int MB>
+template <int FMT, int MB, bool SPREAD>
 __device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, const GemvDesc &d0,
                                              int p0, int g0, int g1) {
   __shared__ Smem<FMT> sh;
@@ -1080,7 +1162,7 @@ __device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, co
   for (int g = g0, p = p0; g < g1 && p < count;) {
     const int e = min(g1, d.item_begin + d.items);
     if (e > g) {
-      stream_problem<FMT, MB>(sh, d, g, e, first);
+      stream_problem<FMT, MB, SPREAD>(sh, d, g, e, first);
       first = false;
       g = e;
     }
@@ -1088,19 +1170,19 @@ __device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, co
   }
 }
 
-template <int FMT, int MB>
+template <int FMT, int MB, bool SPREAD = false>
 __global__ __launch_bounds__(kThreads) void gemv_stream_single(GemvDesc d) {
   const int64_t T = d.items;
   const int g0 = (int)(T * blockIdx.x / gridDim.x), g1 = (int)(T * (blockIdx.x + 1) / gridDim.x);
-  if (g0 < g1) stream_block<FMT, MB>(&d, 1, d, 0, g0, g1);
+  if (g0 < g1) stream_block<FMT, MB, SPREAD>(&d, 1, d, 0, g0, g1);
 }
 
-template <int FMT, int MB>
+template <int FMT, int MB, bool SPREAD = false>
 __global__ __launch_bounds__(kThreads) void gemv_stream_grouped(const GemvDesc *__restrict__ plan,
                                                                 const GemvBlock *__restrict__ blocks,
                                                                 int count) {
   const GemvBlock bl = fetch_uniform(blocks + blockIdx.x);
-  if (bl.i0 < bl.i1) stream_block<FMT, MB>(plan, count, bl.d, bl.p, bl.i0, bl.i1);
+  if (bl.i0 < bl.i1) stream_block<FMT, MB, SPREAD>(plan, count, bl.d, bl.p, bl.i0, bl.i1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1712,7 +1794,11 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
     blocks.push_back(GemvBlock{descs[p], p, g0, g1, 0});
     g0 = g1;
   }
-  return (chunked ? 2048 : 0) + 16 * fmt + mb;
+  // the spread staging when every problem's rows fit it
+  bool spread = !chunked && fmt == UG_W_PACK5 && mb == 1;
+  for (int i = 0; i < count && spread; ++i)
+    if (!stages_spread(descs[i].M, descs[i].K)) spread = false;
+  return (spread ? 8192 : 0) + (chunked ? 2048 : 0) + 16 * fmt + mb;
 }
 
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
@@ -1758,7 +1844,10 @@ hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int3
   }
 #define UG_GROUPED(F, MBV) \
   hipLaunchKernelGGL((gemv_stream_grouped<F, MBV>), g, b, 0, st, plan_dev, blocks_dev, count)
-  if (fmt == UG_W_PACK5) {
+  if ((variant >> 13) & 1) {
+    hipLaunchKernelGGL((gemv_stream_grouped<UG_W_PACK5, 1, true>), g, b, 0, st, plan_dev,
+                       blocks_dev, count);
+  } else if (fmt == UG_W_PACK5) {
     if (mb == 1) UG_GROUPED(UG_W_PACK5, 1);
     else if (mb == 2) UG_GROUPED(UG_W_PACK5, 2);
     else UG_GROUPED(UG_W_PACK5, 4);
@@ -1829,7 +1918,9 @@ hipError_t launch_gemv(const int8_t *xq, int64_t ldx, const float *s, const void
     return hipGetLastError();
   }
 #define UG_SINGLE(F, MBV) hipLaunchKernelGGL((gemv_stream_single<F, MBV>), g, b, 0, st, d)
-  if (wfmt == UG_W_PACK5) {
+  if ((variant >> 13) & 1) {
+    hipLaunchKernelGGL((gemv_stream_single<UG_W_PACK5, 1, true>), g, b, 0, st, d);
+  } else if (wfmt == UG_W_PACK5) {
     if (d.mb == 1) UG_SINGLE(UG_W_PACK5, 1);
     else if (d.mb == 2) UG_SINGLE(UG_W_PACK5, 2);
     else UG_SINGLE(UG_W_PACK5, 4);

@@ -113,8 +113,10 @@ struct GemvBlock {
 // Plans a group of problems for the matrix-core GEMV: picks the split (fine
 // or stream), fills mb, items and item_begin of every descriptor and one
 // table entry per block to launch.  Returns the variant
-// (4096 * tiny + 2048 * chunked + 1024 * short + 512 * fused + 256 * fine +
-// 16 * wfmt + mb; fused: the fine split with fp32 activations; short: the
+// (8192 * spread + 4096 * tiny + 2048 * chunked + 1024 * short + 512 * fused +
+// 256 * fine + 16 * wfmt + mb; spread: the stream split of five-trit weights
+// at mb 1 with the spread activation staging (every problem's rows fit it);
+// fused: the fine split with fp32 activations; short: the
 // fine split's variant for at most 4 pieces and 2 activation tiles per wave;
 // tiny (with short): at most 3 pieces and 1 tile per wave; chunked: the
 // stream split staging activations chunk by chunk, when some problem's rows

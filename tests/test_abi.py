@@ -338,6 +338,24 @@ def test_grouped_plan_rejects_fused_with_chunked(ug):
         assert st == ug.UG_ERR_HIP
 
 
+def test_grouped_launch_rejects_bad_variants(ug):
+    """ug_bitlinear_gemv_grouped checks the plan's variant before launching:
+    the spread staging (bit 13) goes only with the plain stream split of
+    five-trit weights and one 16-row block; no other combination is a kernel."""
+    L = ug.lib()
+    plan = ctypes.create_string_buffer(4096 + 16)
+    addr = (ctypes.addressof(plan) + 15) & ~15
+    fmt5 = 16 * ug.UG_W_PACK5
+    for variant in (8192 + 256 + fmt5 + 1,           # with the fine split
+                    8192 + 2048 + fmt5 + 1,          # with the chunked split
+                    8192 + 16 * ug.UG_W_I8 + 1,      # one trit per byte
+                    8192 + fmt5 + 2, 8192 + fmt5 + 4,  # more than 16 rows
+                    16384 + fmt5 + 1):               # no such bit
+        info = ug.GemvPlanInfo(count=1, total_items=1, variant=variant, grid=1)
+        st = L.ug_bitlinear_gemv_grouped(ctypes.c_void_p(addr), ctypes.byref(info), None)
+        assert st == ug.UG_ERR_INVALID_ARG, hex(variant)
+
+
 def test_attention_rejects_and_sizes(ug):
     L = ug.lib()
     E = ug.UG_ERR_INVALID_ARG

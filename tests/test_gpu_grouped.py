@@ -223,6 +223,59 @@ def test_chunked_parity(dev, ci):
         assert_y_close(host(p["y"]), y_r, "y %d" % i)
 
 
+# (M, list of (N, K), fused, spread): stream-split groups (more 16-row
+# pieces than the fine split takes).  Five trits per byte at M <= 16 take
+# the spread staging (each packed byte's five activations in 8 staged bytes,
+# plan.info.variant bit 13) when every problem's K-order and spread rows fit
+# the 64 KB staging area together; otherwise the permuted staging.  Ragged
+# K (tail bytes with fewer than five trits), ragged N, fp32 activations
+# quantized in the launch or x_q given.
+SPREAD = [
+    (1, [(6912, 2560)] * 4 + [(2560, 6913), (77, 5), (300, 81)], False, True),
+    (1, [(6912, 2560)] * 4 + [(2560, 6912), (513, 7)], True, True),
+    (2, [(6912, 2560)] * 5 + [(100, 1001)], False, True),
+    (3, [(6912, 2560)] * 5 + [(64, 3000)], True, True),
+    (16, [(131200, 640), (77, 333)], False, True),
+    (4, [(6912, 2560)] * 4 + [(2560, 6912)], False, False),  # 4 rows of 6912: too long to spread
+    (16, [(6912, 2560)] * 5, True, False),
+]
+
+
+@pytest.mark.parametrize("si", range(len(SPREAD)))
+def test_stream_spread_staging(dev, si):
+    M, shapes, fused, spread = SPREAD[si]
+    _case("spread", si, M, fused, spread)
+    rng = np.random.default_rng([306, si])
+    probs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x = rng.standard_normal((M, K), dtype=np.float32)
+        wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        beta = np.float32(0.02 + 0.001 * i)
+        xq_r, s_r = oracle.quant_act(x)
+        p = dict(w=pitched(oracle.pack_trits(wq)[0]), wfmt=ug.UG_W_PACK5, beta=scalar_dev(beta),
+                 K=K, y=ug.empty_pitched(M, N, torch.float32, dev),
+                 acc=ug.empty_pitched(M, N, torch.int32, dev))
+        if fused:
+            p.update(x=pitched(x), xq=ug.empty_pitched(M, K, torch.int8, dev),
+                     s=torch.empty(M, dtype=torch.float32, device=dev))
+        else:
+            p.update(xq=pitched(xq_r), s=vec(s_r))
+        probs.append(p)
+        acc_r = oracle.matmul_i32(xq_r, wq)
+        refs.append((xq_r, s_r, acc_r, oracle.epilogue(acc_r, s_r, beta)))
+    plan = ug.ug_gemv_plan_init(probs)
+    v = plan.info.variant
+    assert (v >> 8) & 1 == 0 and (v >> 11) & 1 == 0, "stream split expected, variant %#x" % v
+    assert bool((v >> 13) & 1) == spread, "variant %#x" % v
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for i, (p, (xq_r, s_r, acc_r, y_r)) in enumerate(zip(probs, refs)):
+        if fused:
+            assert_bits_equal(host(p["xq"]), xq_r, "x_q %d" % i)
+            assert_bits_equal(host(p["s"]), s_r, "s %d" % i)
+        assert_bits_equal(host(p["acc"]), acc_r, "acc %d" % i)
+        assert_bits_equal(host(p["y"]), y_r, "y %d" % i)
+
+
 def test_grouped_many_problems_multi_item_blocks(dev):
     """A group large enough that every block walks several items."""
     rng = np.random.default_rng(301)
