@@ -744,15 +744,16 @@ def measure_stream_m1(torch, ug, inputs, M=1, si=0, marginal=True):
     K, N = inputs.SWEEP_SHAPES[si]
     x64, W = inputs.sweep_inputs(si, 64)
     wq, beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
-    pk = ug.ug_pack_trits(wq)
+    pk = ug.ug_pack_trits(wq, packed=torch.empty((N, ug.stream_pitch(K)), dtype=torch.uint8,
+                                                  device=dev))
     del wq, W
-    G = max(1, (128 << 20) // (N * ug.packed_pitch(K)))
+    G = max(1, (128 << 20) // (N * ug.stream_pitch(K)))
     xq, s = ug.ug_quant_act(torch.from_numpy(x64[:M].copy()).to(dev))
     y = ug.empty_pitched(M, N, torch.float32, dev)
 
     def timed(g):
         """Median launch time of groups of g weight copies, cold."""
-        n_sets = max(2, COLD_BYTES // (g * N * ug.packed_pitch(K)) + 1)
+        n_sets = max(2, COLD_BYTES // (g * N * ug.stream_pitch(K)) + 1)
         copies = [[pk.clone() for _ in range(g)] for _ in range(n_sets)]
         plans = [ug.ug_gemv_plan_init([dict(xq=xq, s=s, w=w, wfmt=ug.UG_W_PACK5, beta=beta, K=K,
                                              y=y) for w in cs]) for cs in copies]
@@ -777,7 +778,7 @@ def measure_stream_m1(torch, ug, inputs, M=1, si=0, marginal=True):
     out = dict(value=wbytes / (med * 1e-6) / 1e9, unit="GB/s",
                point="M=%d K=%d N=%d, PACK5, %d weight copies per launch, %d launch sets "
                      "(%.2f GiB) cycled" % (M, K, N, G, n_sets,
-                                           n_sets * G * N * ug.packed_pitch(K) / 2 ** 30),
+                                           n_sets * G * N * ug.stream_pitch(K) / 2 ** 30),
                median_launch_us=med, p10_launch_us=p10, p90_launch_us=p90,
                median_launch_us_2x=med2 if marginal else None,
                marginal_GBps=rate2, fixed_us_per_launch=2 * med - med2 if marginal else None,
@@ -813,11 +814,13 @@ def run_sweep(args, torch, ug, inputs):
             continue
         x64, W = inputs.sweep_inputs(si, 64)
         wq, beta = ug.ug_quant_weight_absmean(torch.from_numpy(W).to(dev))
-        pk = ug.ug_pack_trits(wq)
+        # rows of at least 1 KB start on a cache line (ug.stream_pitch)
+        pk = ug.ug_pack_trits(wq, packed=torch.empty((N, ug.stream_pitch(K)), dtype=torch.uint8,
+                                                      device=dev))
         del wq
         wbytes = N * (-(-K // 5))
-        G = max(1, (128 << 20) // (N * ug.packed_pitch(K)))
-        n_sets = max(2, COLD_BYTES // (G * N * ug.packed_pitch(K)) + 1)
+        G = max(1, (128 << 20) // (N * ug.stream_pitch(K)))
+        n_sets = max(2, COLD_BYTES // (G * N * ug.stream_pitch(K)) + 1)
         copies = [[pk.clone() for _ in range(G)] for _ in range(n_sets)]
         for M in inputs.SWEEP_MS:
             if only is not None and only[0] != M:
@@ -861,7 +864,9 @@ def run_sweep(args, torch, ug, inputs):
                 tot_bytes += wbytes * G
                 tot_s += launch_us * 1e-6
                 if M == 1 and si == 0:
-                    dom = dict(bound="hbm", kernel="gemv_stream_grouped<PACK5, 1>",
+                    spread = (plans[0].info.variant >> 13) & 1
+                    dom = dict(bound="hbm",
+                               kernel="gemv_stream_grouped<PACK5, 1%s>" % (", spread" * spread),
                                achieved=alg / (launch_us * 1e-6) / 1e9, peak=HBM_PEAK_GBS,
                                unit="GB/s", frac=alg / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                traffic=traffic_for("sweep"), avg_launch_us=launch_us,

@@ -155,6 +155,15 @@ def packed_pitch(K):
     return round_up(-(-K // 5), 16)
 
 
+def stream_pitch(K):
+    """UG_W_PACK5 row pitch for weights the GEMV streams: rows of at least
+    1 KB start on a 128-byte cache line (at most 1/8 more bytes), so no
+    64-byte piece of a row straddles two lines; shorter rows keep the
+    smallest pitch."""
+    rb = -(-K // 5)
+    return round_up(rb, 128) if rb >= 1024 else packed_pitch(K)
+
+
 def ug_version():
     return lib().ug_version()
 

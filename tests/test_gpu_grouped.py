@@ -276,6 +276,38 @@ def test_stream_spread_staging(dev, si):
         assert_bits_equal(host(p["y"]), y_r, "y %d" % i)
 
 
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_stream_cache_line_pitch(dev, M):
+    """Packed rows on a 128-byte pitch (ug.stream_pitch: 1408 bytes for the
+    1383-byte rows of K = 6912) through the stream split and, at M = 16, the
+    chunked split; the pad bytes hold junk, which meets zero activations."""
+    _case("stream pitch", M)
+    rng = np.random.default_rng([307, M])
+    K, N, G = 6912, 2560, 7
+    ldp = ug.stream_pitch(K)
+    assert ldp == 1408
+    probs, refs = [], []
+    for i in range(G):
+        wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        x = rng.standard_normal((M, K), dtype=np.float32)
+        xq_r, s_r = oracle.quant_act(x)
+        pk = np.full((N, ldp), 0xA7, dtype=np.uint8)
+        pk[:, :-(-K // 5)] = oracle.pack_trits(wq)[0][:, :-(-K // 5)]
+        beta = np.float32(0.02 + 0.001 * i)
+        probs.append(dict(xq=pitched(xq_r), s=vec(s_r), w=torch.from_numpy(pk).to(dev),
+                          wfmt=ug.UG_W_PACK5, beta=scalar_dev(beta), K=K,
+                          y=ug.empty_pitched(M, N, torch.float32, dev),
+                          acc=ug.empty_pitched(M, N, torch.int32, dev)))
+        acc_r = oracle.matmul_i32(xq_r, wq)
+        refs.append((acc_r, oracle.epilogue(acc_r, s_r, beta)))
+    plan = ug.ug_gemv_plan_init(probs)
+    assert (plan.info.variant >> 8) & 1 == 0, "variant %#x" % plan.info.variant
+    ug.ug_bitlinear_gemv_grouped(plan)
+    for i, (p, (acc_r, y_r)) in enumerate(zip(probs, refs)):
+        assert_bits_equal(host(p["acc"]), acc_r, "acc %d" % i)
+        assert_bits_equal(host(p["y"]), y_r, "y %d" % i)
+
+
 def test_grouped_many_problems_multi_item_blocks(dev):
     """A group large enough that every block walks several items."""
     rng = np.random.default_rng(301)
