@@ -126,7 +126,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="decode_stack: skip the extra measurement points")
     p.add_argument("--only", default=None,
-                   choices=["prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
+                   choices=["prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "hbm_read_rate",
+                            "stream_m1",
                             "pack", "requant_pack5", "attention_decode", "sampler",
                             "backward", "mfma_sustained"],
                    help="run just this one of the decode_stack line's extra points and print "
@@ -153,13 +154,13 @@ TRAFFIC = {
     # it was taken on are unchanged.
     # profiles/gemv_fine_grouped_decode_stack.md: 2008.4 KiB / 146.4 KiB
     "decode_stack": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                              "02e04197ab5dde7f92c93653876e80db815573198ad41d01c5e56630d123e498"},
-                         bytes_per_launch=4262676),
+                              "3bbfdf1daef4184e091551e0b4f061323ec9d680cf9ca9fb81bf1725ecac8022"},
+                         bytes_per_launch=4262684),
     # profiles/gemv_stream_grouped_sweep_m1.md: M=1 2560->6912, 37 problems per
-    # launch, spread staging: 64139.5 KiB / 191.7 KiB
+    # launch, spread staging: 64124.6 KiB / 190.6 KiB
     "sweep": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                       "02e04197ab5dde7f92c93653876e80db815573198ad41d01c5e56630d123e498"},
-                  bytes_per_launch=131532314),
+                       "3bbfdf1daef4184e091551e0b4f061323ec9d680cf9ca9fb81bf1725ecac8022"},
+                  bytes_per_launch=131506088),
     # profiles/gemm_i8_large_prefill.md: mean of the two shapes' launches
     "prefill": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
                          "02b27e9db0529ba1b218003a0d600a96eb02f97bdc7bbbc8ef0ed0e7862fabf3"},
@@ -379,7 +380,9 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["hbm_copy_rate"] = measure_copy_rate(torch)
         torch.cuda.empty_cache()
-        out["stream_m1"] = measure_stream_m1(torch, ug, inputs)
+        out["hbm_read_rate"] = measure_hbm_read(torch, ug)
+        torch.cuda.empty_cache()
+        out["stream_m1"] = measure_stream_m1(torch, ug, inputs, read=out["hbm_read_rate"])
         torch.cuda.empty_cache()
         out["pack"] = measure_pack(torch, ug, inputs)
         torch.cuda.empty_cache()
@@ -501,6 +504,56 @@ def measure_copy_rate(torch):
                frac_of_hbm_peak=2 * n / (med * 1e-6) / 1e9 / HBM_PEAK_GBS)
     log("copy rate", res)
     del srcs, dst
+    return res
+
+
+def measure_hbm_read(torch, ug):
+    """The measured streaming-read ceiling (ug_hbm_read_probe: every wave
+    load reads 1 KB contiguous, eight loads in flight per thread): calls of
+    128 MiB and of 256 MiB, each region read once in a cycle spanning
+    >= 2 GiB (cold); the difference of the medians gives the marginal read
+    rate and the fixed cost per call, as for the streaming GEMV.  A few walks
+    and grid sizes are timed (more loads in flight is not faster: one block
+    of four waves per CU with a grid stride measured best); the fastest
+    per-call configuration is the ceiling."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    configs = [(0, cus), (0, 2 * cus), (1, 2 * cus), (1, 16 * cus)]
+    sink = torch.zeros(4 * 16 * cus, dtype=torch.int32, device=dev)
+    n1 = 128 << 20
+    span = COLD_BYTES + 2 * n1
+    buf = torch.ones(span // 4, dtype=torch.int32, device=dev)
+
+    def timed(n, walk, blocks):
+        regions = span // n
+        views = [buf[i * (n // 4):(i + 1) * (n // 4)] for i in range(regions)]
+        for i in range(2):
+            ug.ug_hbm_read_probe(views[i], blocks, sink, walk=walk)
+        return launch_stats(torch, lambda i: ug.ug_hbm_read_probe(
+            views[(i + 2) % regions], blocks, sink, walk=walk), stream)
+
+    tried = []
+    for walk, blocks in configs:
+        med, p10, p90 = timed(n1, walk, blocks)
+        med2 = timed(2 * n1, walk, blocks)[0]
+        tried.append(dict(walk=walk, blocks=blocks, median_call_us=med, p10_call_us=p10,
+                          p90_call_us=p90, median_call_us_2x=med2))
+    best = min(tried, key=lambda t: t["median_call_us"])
+    med, med2 = best["median_call_us"], best["median_call_us_2x"]
+    rate = n1 / (med * 1e-6) / 1e9
+    marginal = n1 / ((med2 - med) * 1e-6) / 1e9 if med2 > med else None
+    res = dict(value=rate, unit="GB/s", kernel="hbm_read_kernel (ug_hbm_read_probe)",
+               note="measured streaming-read ceiling: 128 MiB read per call, cold",
+               walk=best["walk"], blocks=best["blocks"], median_call_us=med,
+               p10_call_us=best["p10_call_us"], p90_call_us=best["p90_call_us"],
+               median_call_us_2x=med2, marginal_GBps=marginal, fixed_us_per_call=2 * med - med2,
+               frac_of_hbm_peak=rate / HBM_PEAK_GBS,
+               marginal_frac_of_hbm_peak=marginal / HBM_PEAK_GBS if marginal else None,
+               configs=[{k: (round(v, 2) if isinstance(v, float) else v) for k, v in t.items()}
+                        for t in tried])
+    log("read rate", res)
+    del buf, sink
     return res
 
 
@@ -734,7 +787,7 @@ def measure_backward(torch, ug, M=2048, N=6912, K=2560):
     return res
 
 
-def measure_stream_m1(torch, ug, inputs, M=1, si=0, marginal=True):
+def measure_stream_m1(torch, ug, inputs, M=1, si=0, marginal=True, read=None):
     """The streaming decode GEMV at one sweep point (default M = 1,
     2560 -> 6912, PACK5): grouped launches of G distinct weight copies
     (>= 128 MB each), launch sets cycling through >= 2 GiB of copies (cold);
@@ -786,6 +839,12 @@ def measure_stream_m1(torch, ug, inputs, M=1, si=0, marginal=True):
                              achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=achieved / HBM_PEAK_GBS,
                              frac_marginal=rate2 / HBM_PEAK_GBS if rate2 else None,
+                             # against the measured streaming-read ceiling
+                             # (ug_hbm_read_probe, same size per call)
+                             frac_of_read_ceiling=achieved / read["value"] if read else None,
+                             marginal_frac_of_read_ceiling=(
+                                 rate2 / read["marginal_GBps"]
+                                 if read and rate2 and read["marginal_GBps"] else None),
                              traffic=traffic_for("sweep") if (M, si) == (1, 0) else None,
                              median_launch_us=med, alg_bytes_per_launch=alg))
     log("stream", out)
@@ -1159,6 +1218,7 @@ def main():
               "pack": lambda: measure_pack(torch, ug, inputs),
               "stream_m1": lambda: measure_stream_m1(torch, ug, inputs,
                                                      marginal=not args.no_marginal),
+              "hbm_read_rate": lambda: measure_hbm_read(torch, ug),
               "requant_pack5": lambda: measure_requant_pack5(torch, ug, inputs),
               "attention_decode": lambda: measure_attention_decode(torch, ug),
               "sampler": lambda: measure_sampler(torch, ug),
@@ -1174,7 +1234,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": res["dtype"], "data": "synthetic (seeded numpy, shapes of the workload)",
             "config": res["config"], "roofline": res["roofline"]}
-    for k in ("mfma_sustained", "prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate", "stream_m1",
+    for k in ("mfma_sustained", "prefill_gemm", "vendor_int8_gemm", "hbm_copy_rate",
+              "hbm_read_rate", "stream_m1",
               "pack", "requant_pack5", "attention_decode", "sampler", "backward",
               "cpu_baseline"):
         if k in res:

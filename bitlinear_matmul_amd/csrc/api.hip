@@ -417,6 +417,15 @@ ug_status ug_mfma_rate_probe(int32_t kind, int32_t blocks, int32_t iters, int32_
   return hip_status(ug::launch_mfma_rate(kind, blocks, iters, sink, as_stream(stream)));
 }
 
+ug_status ug_hbm_read_probe(const void *buf, size_t bytes, int32_t blocks, int32_t walk,
+                            uint32_t *sink, void *stream) {
+  if (buf == nullptr || !aligned16(buf) || bytes == 0 || bytes % 16 != 0 || blocks < 1 ||
+      blocks > 65535 || (walk != 0 && walk != 1) || sink == nullptr || !counter_ok(sink))
+    return UG_ERR_INVALID_ARG;
+  return hip_status(
+      ug::launch_hbm_read(buf, (uint64_t)bytes, blocks, walk, sink, as_stream(stream)));
+}
+
 size_t ug_attention_workspace_size(int64_t M, int64_t pos0, int64_t H, int64_t dh) {
   if (!attention_shape_ok(M, pos0, H, dh) || pos0 + M > (INT64_C(1) << 24) || H > 65535 ||
       M > 65535)

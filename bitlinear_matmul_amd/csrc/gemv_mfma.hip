@@ -810,12 +810,18 @@ struct Wave {
 // Stream split.
 //
 // Items [i0, i1) of problem d: wave w takes items i0 + w, i0 + w + 8, ...,
-// each NC units, with the weights of the next two units in flight.  start()
-// issues the first two units' loads, so they travel while the block sets up.
+// each NC units, with the weights of the next two units (spread staging:
+// the next unit) in flight.  start() issues those loads, so they travel
+// while the block sets up.
 template <int FMT, int MB, bool SPREAD = false>
 struct ItemLoop {
   using W = Wave<FMT, MB, false, SPREAD>;
   static constexpr int SC = W::SC, NACC = W::NACC, kRGW = W::kRGW;
+  // Spread staging: one unit of weights in flight while the wave decodes
+  // the current one (its decode is short; 32 KB in flight per compute unit
+  // streams faster on this GPU than 64 KB, as the read probe also shows);
+  // otherwise two.
+  static constexpr bool kShallow = SPREAD;
   W wv;
   uint4 A[kRGW][SC], B[kRGW][SC], C[kRGW][SC];
   v4i acc[kRGW][MB][NACC];
@@ -860,7 +866,7 @@ struct ItemLoop {
     iss_it = pro_it = i0 + wave;
     iss_ch = pro_ch = 0;
     issue(d, A);
-    issue(d, B);
+    if (!kShallow) issue(d, B);
   }
 
   // Needs the block's set-up (table, staged rows) to be complete.  (Issuing
@@ -868,6 +874,17 @@ struct ItemLoop {
   // fourth buffer keeping three units in flight: 37.3 against 34.0 us for
   // 37 problems of 2560 -> 6912 at M = 1.)
   __device__ __forceinline__ void run(const GemvDesc &d, const Smem<FMT> &sh) {
+    if constexpr (kShallow) {
+      for (int u = 0; u < U;) {
+        issue(d, B);
+        process(d, sh, A);
+        if (++u >= U) break;
+        issue(d, A);
+        process(d, sh, B);
+        ++u;
+      }
+      return;
+    }
     for (int u = 0; u < U;) {
       issue(d, C);
       process(d, sh, A);

@@ -1,6 +1,7 @@
-// Matrix-core rate probe (gfx950): a measurement helper beside the forward
-// path, not a step of it.
+// Rate probes (gfx950): measurement helpers beside the forward path, not
+// steps of it.
 //
+// Matrix-core rate.
 // The published dense peaks (5.0 POP/s int8, 157.3 TFLOP/s fp32) assume
 // the 2.4 GHz peak engine clock on all 256 CUs.  Under a full matrix-core
 // load the board's power limit lowers that clock, so the rate a GEMM can
@@ -82,7 +83,59 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, int32_t *__re
   if (lane == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = (int32_t)word;
 }
 
+// HBM read rate: the rate a plain streaming read reaches on this GPU, the
+// measured ceiling for the bandwidth-bound kernels (which read far more
+// than they write).  Threads walk the buffer's 16-byte words (a wave's load
+// instruction reads 1 KB contiguous), eight loads in flight, and fold each
+// word into an XOR; each wave writes the XOR over its lanes, so the XOR of
+// all sink words is the XOR of every 32-bit word of the buffer.  Walk 0:
+// one grid stride over the whole buffer; walk 1: block b takes the b-th of
+// gridDim.x contiguous ranges (whole 16-byte words) and its threads walk
+// that range with a block stride, as the streaming GEMV's blocks each walk
+// their own range of weight rows.
+template <int WALK>
+__global__ __launch_bounds__(256) void hbm_read_kernel(const uint4 *__restrict__ buf, uint64_t n16,
+                                                       uint32_t *__restrict__ sink) {
+  uint64_t stride, i, end;
+  if (WALK == 0) {
+    stride = (uint64_t)gridDim.x * 256;
+    i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    end = n16;
+  } else {
+    stride = 256;
+    i = n16 * blockIdx.x / gridDim.x + threadIdx.x;
+    end = n16 * (blockIdx.x + 1) / gridDim.x;
+  }
+  const uint64_t n16_ = end;  // (walk 0: the whole buffer)
+  uint32_t x = 0;
+  for (; i + 7 * stride < n16_; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = buf[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  for (; i < n16_; i += stride) {
+    const uint4 v = buf[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) x ^= (uint32_t)__shfl_xor((int)x, h, 64);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = x;
+}
+
 }  // namespace
+
+hipError_t launch_hbm_read(const void *buf, uint64_t bytes, int blocks, int walk, uint32_t *sink,
+                           hipStream_t st) {
+  if (walk == 0)
+    hipLaunchKernelGGL(hbm_read_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const uint4 *>(buf), bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(hbm_read_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const uint4 *>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_rate(int kind, int blocks, int iters, int32_t *sink, hipStream_t st) {
   if (kind == 0)

@@ -154,6 +154,8 @@ hipError_t launch_backward(const float *g, int64_t ldg, const float *x, int64_t 
                            float *part, hipStream_t st);
 // Matrix-core issue-rate probe: `blocks` blocks of back-to-back MFMAs.
 hipError_t launch_mfma_rate(int kind, int blocks, int iters, int32_t *sink, hipStream_t st);
+hipError_t launch_hbm_read(const void *buf, uint64_t bytes, int blocks, int walk, uint32_t *sink,
+                           hipStream_t st);
 // Top-k sampling: one block per row of logits.
 hipError_t launch_sample_topk(const float *logits, int64_t ld, int64_t B, int64_t V, int64_t k,
                               float temp, const float *u, int32_t *tok, int32_t *idx_out,

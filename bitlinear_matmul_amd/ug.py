@@ -67,6 +67,7 @@ SIGNATURES = {
     "ug_attention_cached": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
                                    _i64, _vp, _sz, _vp]),
     "ug_mfma_rate_probe": (_i32, [_i32, _i32, _i32, _vp, _vp]),
+    "ug_hbm_read_probe": (_i32, [_vp, _sz, _i32, _i32, _vp, _vp]),
 }
 
 UG_GEMM_COUNTER_BYTES = 2048
@@ -491,3 +492,15 @@ def ug_mfma_rate_probe(kind, blocks, iters, sink, stream=None):
     _check(lib().ug_mfma_rate_probe(kind, blocks, iters, _p(sink), _stream(stream)),
            "ug_mfma_rate_probe")
     return 4 * blocks * iters * 16 * MFMA_PROBE_OPS[kind]
+
+
+def ug_hbm_read_probe(buf, blocks, sink, walk=1, nbytes=None, stream=None):
+    """Measurement helper (not a step of the forward path): reads nbytes
+    (default: all) of the device tensor buf once (walk 0: one grid stride;
+    walk 1: a contiguous range per block); sink uint32/int32 [4 * blocks]
+    on the device, whose XOR is the XOR of every 32-bit word read.  Returns
+    the byte count, for the caller to divide by the time it measures."""
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(lib().ug_hbm_read_probe(_p(buf), n, blocks, walk, _p(sink), _stream(stream)),
+           "ug_hbm_read_probe")
+    return n

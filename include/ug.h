@@ -468,6 +468,24 @@ ug_status ug_attention_cached(const float *q, int64_t ldq, const float *kc,
 ug_status ug_mfma_rate_probe(int32_t kind, int32_t blocks, int32_t iters,
                              int32_t *sink, void *stream);
 
+/*
+ * Measurement helper beside the forward path (not a step of it): the rate
+ * a plain streaming read reaches on this GPU, the measured ceiling for the
+ * bandwidth-bound kernels.  Reads the `bytes` bytes at `buf` (device
+ * memory, 16-byte aligned, bytes a positive multiple of 16) once, with
+ * `blocks` blocks of four waves walking its 16-byte words (every load
+ * instruction of a wave reads 1 KB contiguous, eight in flight per thread):
+ * walk 0, one grid stride over the whole buffer; walk 1, block b reads the
+ * b-th of `blocks` contiguous ranges.  Writes to sink (device memory,
+ * 4 * blocks uint32 words) one word per wave such that the XOR of all sink
+ * words is the XOR of every 32-bit word of the buffer.  The caller times
+ * the call on `stream`: the read rate is bytes / time.  UG_ERR_INVALID_ARG
+ * for a NULL or misaligned pointer, bytes not a positive multiple of 16,
+ * blocks outside [1, 65535] or another walk.
+ */
+ug_status ug_hbm_read_probe(const void *buf, size_t bytes, int32_t blocks, int32_t walk,
+                            uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -433,6 +433,22 @@ def test_backward_rejects(ug):
     assert call(M=2 ** 23 + 1) == ug.UG_ERR_UNSUPPORTED
 
 
+def test_hbm_read_probe_rejects(ug):
+    L = ug.lib()
+    E, S, NULL = ug.UG_ERR_INVALID_ARG, None, None
+    A, B = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert L.ug_hbm_read_probe(NULL, 1024, 8, 1, B, S) == E                     # no buffer
+    assert L.ug_hbm_read_probe(ctypes.c_void_p(0x100008), 1024, 8, 1, B, S) == E  # misaligned
+    assert L.ug_hbm_read_probe(A, 0, 8, 1, B, S) == E                           # no bytes
+    assert L.ug_hbm_read_probe(A, 1000, 8, 1, B, S) == E                        # not 16-byte words
+    assert L.ug_hbm_read_probe(A, 1024, 0, 1, B, S) == E                        # no blocks
+    assert L.ug_hbm_read_probe(A, 1024, 65536, 1, B, S) == E
+    assert L.ug_hbm_read_probe(A, 1024, 8, 2, B, S) == E                        # no such walk
+    assert L.ug_hbm_read_probe(A, 1024, 8, -1, B, S) == E
+    assert L.ug_hbm_read_probe(A, 1024, 8, 1, NULL, S) == E                     # no sink
+    assert L.ug_hbm_read_probe(A, 1024, 8, 1, ctypes.c_void_p(0x200002), S) == E
+
+
 def test_mfma_rate_probe_rejects(ug):
     L = ug.lib()
     E = ug.UG_ERR_INVALID_ARG

@@ -554,3 +554,20 @@ def test_mfma_rate_probe_runs_and_repeats(dev, kind):
     assert ops == 4 * blocks * 3 * 16 * (65536 if kind == 0 else 2048)
     assert torch.equal(a, b)
     assert len(set(host(a).tolist())) > 1
+
+
+# HBM read-rate probe (a measurement helper)
+@pytest.mark.parametrize("walk", [0, 1])
+@pytest.mark.parametrize("words,blocks", [(4, 1), (4, 3), (1000 * 4, 3), (262144 * 4 + 12, 2048),
+                                          (262144 * 4 + 12, 1000)])
+def test_hbm_read_probe_reads_every_word(dev, words, blocks, walk):
+    """The XOR of the probe's sink words is the XOR of every 32-bit word of
+    the buffer (ragged tails, blocks with empty ranges: each word read once)."""
+    rng = np.random.default_rng([540, words])
+    host_words = rng.integers(0, 2 ** 32, size=words, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host_words.view(np.int32)).to(dev)
+    sink = torch.zeros(4 * blocks, dtype=torch.int32, device=dev)
+    n = ug.ug_hbm_read_probe(buf, blocks, sink, walk=walk)
+    assert n == 4 * words
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host_words)
