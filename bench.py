@@ -152,10 +152,12 @@ TRAFFIC = {
     # dispatch, medians), calibrated by a 256 MiB copy: bytes = FETCH x 1024 x
     # 1.99977 + WRITE x 1024.  A record holds only while the kernel sources
     # it was taken on are unchanged.
-    # profiles/gemv_fine_grouped_decode_stack.md: 2008.4 KiB / 146.4 KiB
+    # profiles/gemv_fine_grouped_decode_stack.md: 1772.2 KiB / 146.4 KiB
     "decode_stack": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                              "3bbfdf1daef4184e091551e0b4f061323ec9d680cf9ca9fb81bf1725ecac8022"},
-                         bytes_per_launch=4262684),
+                              "60c412659a98b9ad0107b1c961034a3e9cda4463f52993e7904f4d94ed7ec1a5",
+                              "bitlinear_matmul_amd/csrc/api.hip":
+                              "fc7393bcd0906b1442f9491311fb3f3f27b63ac92f6563fd8603fae300f9762c"},
+                         bytes_per_launch=3779017),
     # profiles/gemv_stream_grouped_sweep_m1.md: M=1 2560->6912, 37 problems per
     # launch, spread staging: 64124.6 KiB / 190.6 KiB
     "sweep": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":

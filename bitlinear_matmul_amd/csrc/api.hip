@@ -252,6 +252,7 @@ ug_status ug_gemv_plan_init(const ug_gemv_problem *problems, int32_t count, void
   const int variant = ug::gemv_plan(descs.data(), count, blocks, fine);
   if (variant == -2) return UG_ERR_UNSUPPORTED;
   if (variant < 0) return UG_ERR_INVALID_ARG;
+  ug::fine_xcd_order(fine);  // (the grouped kernel takes its block by table position)
   const size_t nblocks = fine.empty() ? blocks.size() : fine.size();
   if (nblocks == 0 || nblocks > (size_t)ug::kGemvBlocks) return UG_ERR_UNSUPPORTED;
   int64_t total_items = 0;

@@ -1818,6 +1818,20 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
   return (spread ? 8192 : 0) + (chunked ? 2048 : 0) + 16 * fmt + mb;
 }
 
+void fine_xcd_order(std::vector<FineBlock> &fine) {
+  // block b runs on XCD b % 8 (blocks are dealt to the XCDs round-robin):
+  // the table's i-th block goes to the i-th slot in XCD-major order, so
+  // each problem's consecutive blocks land on one XCD (or two, at a seam)
+  constexpr int kXcd = 8;
+  const int nb = (int)fine.size();
+  if (nb <= kXcd) return;
+  std::vector<FineBlock> out((size_t)nb);
+  int src = 0;
+  for (int x = 0; x < kXcd; ++x)
+    for (int i = x; i < nb; i += kXcd) out[(size_t)i] = fine[(size_t)src++];
+  fine.swap(out);
+}
+
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
   return K <= UG_MAX_K && M <= 64 && stages_x(wfmt, (int)M, (int)K);
 }

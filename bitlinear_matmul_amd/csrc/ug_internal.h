@@ -129,6 +129,10 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
               std::vector<FineBlock> &fine);
 // Blocks to launch for `total_items` items of the stream split.
 int gemv_grid(int64_t total_items);
+// Reorders a grouped launch's fine-split block table so that the blocks of
+// one problem run on as few XCDs as possible: each XCD's L2 then fetches the
+// problem's activation row once instead of every XCD fetching it.
+void fine_xcd_order(std::vector<FineBlock> &fine);
 // Whether the activations of a problem fit the kernel's LDS staging area
 // (required when the launch quantizes fp32 activations).
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K);
