@@ -23,8 +23,9 @@
 //   the same way (each 80-position window as fragment 0..3 holding
 //   x[5g .. 5g+3] of its bytes g, then fragment 4 holding the x[5g+4]), so
 //   every MFMA adds products of matching K positions.
-//   Stream split with one 16-row activation block (when the rows fit):
-//   spread staging instead.  Each packed byte's five activations take 8
+//   Stream split with one 16-row activation block (when the rows fit the
+//   stream split's 80 KB staging area; given x_q, the spread rows are built
+//   straight from it): spread staging instead.  Each packed byte's five activations take 8
 //   staged bytes [x0 x1 x2 x3 x4 0 0 0], and B operand j is the two wide
 //   table entries of bytes 2j and 2j+1 as they come from LDS (t0..t3, then
 //   t4 in all four bytes, three of which meet zero activations): 8 MFMAs
@@ -70,8 +71,10 @@ constexpr int kFineWaves = kFineThreads / 64;
 constexpr int kFineWaveShift = 3;  // work splits by wave: (w * P) >> 3
 static_assert(kFineWaves == kGemvFineWaves && kFineWaves == 1 << kFineWaveShift, "fine waves");
 constexpr int kTableBytes = 65536;  // the decode table in LDS (wide or narrow)
-constexpr int kXsBytes = 65536;    // staged activations
-constexpr int kZero = kXsBytes;    // 80 zero bytes right after them
+constexpr int kXsBytes = 65536;    // staged activations (fine split)
+// The stream and chunked splits use no reduction slots, so their staging
+// area is larger.
+constexpr int kXsStream = 81920;
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every buffer used here
 constexpr int kFineItems = 16;   // fine split: items (16-row groups) per block
 constexpr int kFinePieces = 8;   // fine split: (item, step) pieces per wave
@@ -144,12 +147,13 @@ __host__ __device__ __forceinline__ int staged_kp(int fmt, int mb, int K) {
 // LDS row pitch of M staged rows of Kp bytes: 16 bytes more when they
 // still fit, so that the 16 rows one fragment load reads (a multiple of 64
 // bytes apart otherwise) fall in different banks.
-__host__ __device__ __forceinline__ int stage_pitch(int M, int Kp) {
-  return M > 1 && M * (Kp + 16) <= kXsBytes ? Kp + 16 : Kp;
+__host__ __device__ __forceinline__ int stage_pitch(int M, int Kp, int xs) {
+  return M > 1 && M * (Kp + 16) <= xs ? Kp + 16 : Kp;
 }
 __host__ __device__ __forceinline__ int mb_of(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+// The K-order rows of a problem fit the stream split's staging area.
 __host__ __device__ __forceinline__ bool stages_x(int fmt, int M, int K) {
-  return (int64_t)M * staged_kp(fmt, mb_of(M), K) <= kXsBytes;
+  return (int64_t)M * staged_kp(fmt, mb_of(M), K) <= kXsStream;
 }
 // Spread staging (stream split, five trits per byte, at most 16 rows): the
 // five codes of every packed weight byte take 8 staged bytes,
@@ -157,7 +161,9 @@ __host__ __device__ __forceinline__ bool stages_x(int fmt, int M, int K) {
 // four bytes) is half of a B operand as it leaves LDS.  A 16-byte weight
 // piece is then 8 matrix instructions instead of 5, with no byte permutes
 // between the table reads and the matrix instructions.  The spread rows
-// (512 bytes per step) sit after the K-order rows, which stay intact.
+// (512 bytes per step) sit after the K-order rows, which stay intact, when
+// the launch quantizes fp32 activations; given x_q, the spread rows are
+// built straight from it and are the only staged rows.
 constexpr int kSpreadStep = 512;  // spread bytes per row and 64-byte step
 __host__ __device__ __forceinline__ int spread_base(int M, int pitch) {
   return (M * pitch + 15) & ~15;
@@ -165,10 +171,11 @@ __host__ __device__ __forceinline__ int spread_base(int M, int pitch) {
 __host__ __device__ __forceinline__ int spread_pitch(int M, int Kp) {
   return (Kp / 320) * kSpreadStep + (M > 1 ? 16 : 0);
 }
-__host__ __device__ __forceinline__ bool stages_spread(int M, int K) {
-  const int Kp = staged_kp(UG_W_PACK5, 1, K), pitch = stage_pitch(M, Kp);
-  return M <= 16 &&
-         (int64_t)spread_base(M, pitch) + (int64_t)M * spread_pitch(M, Kp) <= kXsBytes;
+__host__ __device__ __forceinline__ bool stages_spread(int M, int K, bool fused) {
+  const int Kp = staged_kp(UG_W_PACK5, 1, K), pitch = stage_pitch(M, Kp, kXsStream);
+  return M <= 16 && (int64_t)M * Kp <= kXsStream &&
+         (fused ? (int64_t)spread_base(M, pitch) : 0) + (int64_t)M * spread_pitch(M, Kp) <=
+             kXsStream;
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -319,14 +326,21 @@ __device__ __forceinline__ void permute80(const uint32_t (&X)[20], uint32_t (&F)
                 (X[5 * i + 4] & 0xff000000u);
 }
 
-template <int FMT, int NW = kWaves>
+// STREAM: the stream and chunked splits' layout (no reduction slots, a
+// larger staging area).
+template <int FMT, int NW = kWaves, bool STREAM = false>
 struct Smem {
-  uint4 lut[FMT == UG_W_PACK5 ? kTableBytes / 16 : 1];  // the decode table
-  alignas(16) int8_t xs[kXsBytes + 80];  // staged rows, then 80 zero bytes
-  alignas(16) int slots[kFineItems * 256];  // fine split: [item][m][n] int32 sums
-  float part[NW][64];                       // per-wave row maxima (fused quantization)
-  float sm[64];                             // row scales s
+  static constexpr int kXs = STREAM ? kXsStream : kXsBytes;  // staging bytes
+  static constexpr int kNW = NW;
+  uint4 lut[FMT == UG_W_PACK5 ? kTableBytes / 16 : 1];    // the decode table
+  alignas(16) int8_t xs[kXs + 80];                       // staged rows, then 80 zero bytes
+  alignas(16) int slots[STREAM ? 4 : kFineItems * 256];  // fine split: [item][m][n] int32 sums
+  float part[NW][64];                                    // per-wave row maxima (fused quantization)
+  float sm[64];                                          // row scales s
 };
+template <int FMT>
+using SmemS = Smem<FMT, kWaves, true>;
+static_assert(sizeof(SmemS<UG_W_PACK5>) <= 163840, "stream layout fits LDS");
 
 // The decode table in 16-byte chunks, chunk j of code e at e * 16 + j
 // (256 bytes per code): wide, entries for lanes 2j and 2j + 1 (mod 32);
@@ -344,14 +358,14 @@ template <int I>
 __device__ __forceinline__ uint32_t row_broadcast(uint32_t v) {  // lane I of each 16-lane row
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + I, 0xf, 0xf, false);
 }
-template <bool WIDE, int I, int FMT, int NW>
-__device__ __forceinline__ void table_store_step(Smem<FMT, NW> &sh, uint2 v) {
+template <bool WIDE, int I, class SM>
+__device__ __forceinline__ void table_store_step(SM &sh, uint2 v) {
   const uint32_t lo = row_broadcast<I>(v.x), hi = row_broadcast<I>(v.y);
   sh.lut[threadIdx.x + 512 * I] = WIDE ? make_uint4(lo, hi, lo, hi) : make_uint4(lo, lo, lo, lo);
 }
 // (with every lane active: the broadcasts read other lanes)
-template <bool WIDE, int FMT, int NW>
-__device__ __forceinline__ void table_store(Smem<FMT, NW> &sh, uint2 v) {
+template <bool WIDE, class SM>
+__device__ __forceinline__ void table_store(SM &sh, uint2 v) {
   table_store_step<WIDE, 0>(sh, v);
   table_store_step<WIDE, 1>(sh, v);
   table_store_step<WIDE, 2>(sh, v);
@@ -363,11 +377,11 @@ __device__ __forceinline__ void table_store(Smem<FMT, NW> &sh, uint2 v) {
 }
 
 // s = fl(fl(max|x| / 127) + eps) of row m from the per-wave maxima.
-template <int FMT, int NW>
-__device__ __forceinline__ float row_scale(const Smem<FMT, NW> &sh, int m, float eps) {
+template <class SM>
+__device__ __forceinline__ float row_scale(const SM &sh, int m, float eps) {
   float a = sh.part[0][m];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) a = fmaxf(a, sh.part[w][m]);
+  for (int w = 1; w < SM::kNW; ++w) a = fmaxf(a, sh.part[w][m]);
   const float a127 = a / 127.0f;
   return a127 + eps;
 }
@@ -428,8 +442,8 @@ __device__ __forceinline__ void pre_issue(const GemvDesc &d, bool staged, int Kp
 }
 
 // Pass 1 on 8 tiles t0 + i * 8: per-wave row maxima.
-template <int FMT>
-__device__ __forceinline__ void absmax_tiles(const GemvDesc &d, Smem<FMT> &sh, const float4 (&v)[8],
+template <int FMT, class SM>
+__device__ __forceinline__ void absmax_tiles(const GemvDesc &d, SM &sh, const float4 (&v)[8],
                                              int t0, int T4, int nt) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -448,8 +462,8 @@ __device__ __forceinline__ void absmax_tiles(const GemvDesc &d, Smem<FMT> &sh, c
 }
 
 // Pass 2 on 8 tiles: quantize into the staging rows, K order.
-template <int FMT>
-__device__ __forceinline__ void quant_tiles(const GemvDesc &d, Smem<FMT> &sh, const float4 (&v)[8],
+template <int FMT, class SM>
+__device__ __forceinline__ void quant_tiles(const GemvDesc &d, SM &sh, const float4 (&v)[8],
                                             int t0, int T4, int nt, int pitch) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -467,8 +481,8 @@ __device__ __forceinline__ void quant_tiles(const GemvDesc &d, Smem<FMT> &sh, co
 }
 
 // 8 dwords of x_q rows into the staging rows (zeros past K).
-template <int FMT>
-__device__ __forceinline__ void copy_xq4(const GemvDesc &d, Smem<FMT> &sh, const uint32_t (&v)[8],
+template <int FMT, class SM>
+__device__ __forceinline__ void copy_xq4(const GemvDesc &d, SM &sh, const uint32_t (&v)[8],
                                          int i0, int Kp4, int n4, int pitch) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -481,16 +495,31 @@ __device__ __forceinline__ void copy_xq4(const GemvDesc &d, Smem<FMT> &sh, const
   }
 }
 
+// One 80-position window of codes (20 dwords, K order) -> its 128 spread
+// bytes: weight byte b's codes 5b .. 5b+3 in dword 2b, code 5b+4 in the low
+// byte of dword 2b+1.
+__device__ __forceinline__ void spread_window(const uint32_t (&X)[20], uint4 *dst) {
+  uint32_t F[32];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    const int o = 5 * b, o4 = o + 4;
+    F[2 * b] = (o & 3) ? __builtin_amdgcn_alignbyte(X[(o >> 2) + 1], X[o >> 2], o & 3) : X[o >> 2];
+    F[2 * b + 1] = (X[o4 >> 2] >> (8 * (o4 & 3))) & 0xffu;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
+}
+
 // NQ: the first batch of x_q dwords is in pl (0: every batch is loaded
 // here, which keeps the registers free for a caller short of them).
-template <int FMT, int NQ, bool WIDE, bool SPREAD = false>
-__device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, bool staged, int Kp,
+template <int FMT, int NQ, bool WIDE, bool SPREAD = false, class SM>
+__device__ __forceinline__ void setup_finish(const GemvDesc &d, SM &sh, bool staged, int Kp,
                                              int pitch, bool table, bool zero_slots,
                                              const PreLoads<NQ> &pl, int sbase = 0,
                                              int spitch = 0) {
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   if (FMT == UG_W_PACK5 && table) table_store<WIDE>(sh, pl.lut);
-  if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + kZero)[tid] = 0;
+  if (tid < 20) reinterpret_cast<uint32_t *>(sh.xs + SM::kXs)[tid] = 0;
   if (zero_slots)
     for (int i = tid; i < kFineItems * 64; i += kThreads)
       reinterpret_cast<uint4 *>(sh.slots)[i] = make_uint4(0, 0, 0, 0);
@@ -503,7 +532,7 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
       float4 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = load_tile(d, xr, t0 + i * kWaves, T4, nt);
-      absmax_tiles(d, sh, v, t0, T4, nt);
+      absmax_tiles<FMT>(d, sh, v, t0, T4, nt);
     }
     __syncthreads();
     if (tid < d.M) sh.sm[tid] = row_scale(sh, tid, d.eps);
@@ -511,7 +540,7 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
       float4 v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = load_tile(d, xr, t0 + i * kWaves, T4, nt);
-      quant_tiles(d, sh, v, t0, T4, nt, pitch);
+      quant_tiles<FMT>(d, sh, v, t0, T4, nt, pitch);
     }
     // zeros from the first whole dword past K to the end of the staged row
     const int kz = (d.K + 3) >> 2, nz = Kp4 - kz;
@@ -519,47 +548,60 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
       const int m = i / nz;
       reinterpret_cast<uint32_t *>(sh.xs + m * pitch)[kz + (i - m * nz)] = 0u;
     }
+  } else if (SPREAD) {
+    // x_q given: every 80-position window straight from memory into its
+    // 128 spread bytes (16-byte loads: a load at k < K is inside the row,
+    // ldxq >= round_up(K, 16); bytes past K zeroed)
+    if (tid < d.M) sh.sm[tid] = pl.s;
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
+    const int wpr = Kp / 80, nwin = d.M * wpr;
+    for (int w0 = tid; w0 < nwin; w0 += kThreads) {
+      const int m = w0 / wpr, w = w0 - m * wpr, k0 = 80 * w;
+      uint32_t X[20];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int k = k0 + 16 * i;
+        const uint4 v = buffer_load16(xr, k < d.K ? (uint32_t)(m * (int)d.ldxq + k) : kOOB);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kb = d.K - k - 4 * e;  // bytes of this dword inside the row
+          X[4 * i + e] =
+              w4[e] & (kb >= 4 ? 0xffffffffu : (kb <= 0 ? 0u : (0xffffffffu >> (8 * (4 - kb)))));
+        }
+      }
+      spread_window(X, reinterpret_cast<uint4 *>(sh.xs + sbase + m * spitch + w * 128));
+    }
   } else {
     if (tid < d.M) sh.sm[tid] = pl.s;
     if (staged) {
       const int n4 = d.M * Kp4;
       const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(d.xq, (uint32_t)((int64_t)d.M * d.ldxq));
-      if constexpr (NQ > 0) copy_xq4(d, sh, pl.q, tid, Kp4, n4, pitch);
+      if constexpr (NQ > 0) copy_xq4<FMT>(d, sh, pl.q, tid, Kp4, n4, pitch);
       for (int i0 = NQ ? tid + NQ * kThreads : tid; i0 < n4; i0 += 8 * kThreads) {
         uint32_t v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = load_xq4(d, xr, i0 + i * kThreads, Kp4, n4);
-        copy_xq4(d, sh, v, i0, Kp4, n4, pitch);
+        copy_xq4<FMT>(d, sh, v, i0, Kp4, n4, pitch);
       }
     }
   }
   __syncthreads();
   // every 80-position window, one per thread: permuted in place, or spread
-  // into its 128-byte window of the spread rows
-  if (FMT == UG_W_PACK5 && staged) {
+  // into its 128-byte window of the spread rows (x_q given and spread: done)
+  if (FMT == UG_W_PACK5 && staged && !(SPREAD && !d.x)) {
     const int wpr = Kp / 80, nwin = d.M * wpr;
     for (int w0 = tid; w0 < nwin; w0 += kThreads) {
       const int m = w0 / wpr, w = w0 - m * wpr;
       uint4 *win = reinterpret_cast<uint4 *>(sh.xs + m * pitch + w * 80);
-      uint32_t X[20], F[SPREAD ? 32 : 20];
+      uint32_t X[20], F[20];
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
         const uint4 q = win[i];
         X[4 * i] = q.x; X[4 * i + 1] = q.y; X[4 * i + 2] = q.z; X[4 * i + 3] = q.w;
       }
       if constexpr (SPREAD) {
-        // weight byte b: codes 5b .. 5b+3 in the first dword, 5b+4 in the
-        // low byte of the second
-#pragma unroll
-        for (int b = 0; b < 16; ++b) {
-          const int o = 5 * b, o4 = o + 4;
-          F[2 * b] = (o & 3) ? __builtin_amdgcn_alignbyte(X[(o >> 2) + 1], X[o >> 2], o & 3)
-                             : X[o >> 2];
-          F[2 * b + 1] = (X[o4 >> 2] >> (8 * (o4 & 3))) & 0xffu;
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(sh.xs + sbase + m * spitch + w * 128);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = make_uint4(F[4 * i], F[4 * i + 1], F[4 * i + 2], F[4 * i + 3]);
+        spread_window(X, reinterpret_cast<uint4 *>(sh.xs + sbase + m * spitch + w * 128));
       } else {
         permute80(X, F);
 #pragma unroll
@@ -572,8 +614,8 @@ __device__ __forceinline__ void setup_finish(const GemvDesc &d, Smem<FMT> &sh, b
 
 // The quantized activations and scales as outputs (fused quantization, the
 // problem's first block): undo the staging permutation per K position.
-template <int FMT, bool SPREAD = false>
-__device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const Smem<FMT> &sh, int pitch) {
+template <int FMT, bool SPREAD = false, class SM>
+__device__ __forceinline__ void write_act_outputs(const GemvDesc &d, const SM &sh, int pitch) {
   const int tid = threadIdx.x;
   if (d.s)
     for (int m = tid; m < d.M; m += kThreads) gp(d.s)[m] = sh.sm[m];
@@ -838,7 +880,7 @@ struct ItemLoop {
     }
   }
 
-  __device__ __forceinline__ void process(const GemvDesc &d, const Smem<FMT> &sh,
+  __device__ __forceinline__ void process(const GemvDesc &d, const SmemS<FMT> &sh,
                                           const uint4 (&buf)[kRGW][SC]) {
     if (pro_ch == 0) {
 #pragma unroll
@@ -873,7 +915,7 @@ struct ItemLoop {
   // the third unit before the set-up too measured slower, and so did a
   // fourth buffer keeping three units in flight: 37.3 against 34.0 us for
   // 37 problems of 2560 -> 6912 at M = 1.)
-  __device__ __forceinline__ void run(const GemvDesc &d, const Smem<FMT> &sh) {
+  __device__ __forceinline__ void run(const GemvDesc &d, const SmemS<FMT> &sh) {
     if constexpr (kShallow) {
       for (int u = 0; u < U;) {
         issue(d, B);
@@ -980,7 +1022,7 @@ __device__ __forceinline__ void chunk_store(const GemvDesc &d, int8_t *xs, int c
 }
 
 template <int FMT, int MB>
-__device__ __forceinline__ void chunked_items(const GemvDesc &d, Smem<FMT> &sh, int i0, int i1) {
+__device__ __forceinline__ void chunked_items(const GemvDesc &d, SmemS<FMT> &sh, int i0, int i1) {
   using C = Chunk<FMT, MB>;
   constexpr int RG = C::RG, CH = C::CH, F1 = Fmt<FMT>::kFrag;
   const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63, q = lane >> 4;
@@ -1105,7 +1147,7 @@ __device__ __forceinline__ void chunked_items(const GemvDesc &d, Smem<FMT> &sh, 
 template <int FMT, int MB>
 __device__ __forceinline__ void chunked_block(const GemvDesc *plan, int count, const GemvDesc &d0,
                                               int p0, int g0, int g1) {
-  __shared__ Smem<FMT> sh;
+  __shared__ SmemS<FMT> sh;
   bool first = true;
   GemvDesc d = d0;
   for (int g = g0, p = p0; g < g1 && p < count;) {
@@ -1142,15 +1184,16 @@ __global__ __launch_bounds__(kThreads) void gemv_chunked_grouped(const GemvDesc 
 // problem (it builds the decode table, and no earlier problem's waves still
 // read the staging area).
 template <int FMT, int MB, bool SPREAD>
-__device__ __forceinline__ void stream_problem(Smem<FMT> &sh, const GemvDesc &d, int g, int e,
+__device__ __forceinline__ void stream_problem(SmemS<FMT> &sh, const GemvDesc &d, int g, int e,
                                                bool first) {
   const bool staged = SPREAD || stages_x(FMT, d.M, d.K);
-  const int Kp = staged_kp(FMT, MB, d.K), pitch = stage_pitch(d.M, Kp);
-  const int sbase = SPREAD ? spread_base(d.M, pitch) : 0;
+  const int Kp = staged_kp(FMT, MB, d.K), pitch = stage_pitch(d.M, Kp, kXsStream);
+  // (spread rows after the K-order rows when the launch quantizes them)
+  const int sbase = SPREAD && d.x ? spread_base(d.M, pitch) : 0;
   const int spitch = SPREAD ? spread_pitch(d.M, Kp) : 0;
   // (the set-up's loads leave before the weights': two units of weights
   // stay in flight while the block sets up)
-  constexpr int NQ = MB <= 2 ? 8 : 0;
+  constexpr int NQ = MB <= 2 && !SPREAD ? 8 : 0;
   PreLoads<NQ> pl;
   pre_issue<FMT>(d, staged, Kp, first, pl);
   __builtin_amdgcn_sched_barrier(0);
@@ -1173,7 +1216,7 @@ __device__ __forceinline__ void stream_problem(Smem<FMT> &sh, const GemvDesc &d,
 template <int FMT, int MB, bool SPREAD>
 __device__ __forceinline__ void stream_block(const GemvDesc *plan, int count, const GemvDesc &d0,
                                              int p0, int g0, int g1) {
-  __shared__ Smem<FMT> sh;
+  __shared__ SmemS<FMT> sh;
   bool first = true;
   GemvDesc d = d0;
   for (int g = g0, p = p0; g < g1 && p < count;) {
@@ -1425,7 +1468,7 @@ __device__ __forceinline__ void fine_block(const FineBlock &b, uint32_t ws,
 
   const int M = b.shape & 0xff, items = (b.shape >> 8) & 0xff, S = b.shape >> 16, K = b.K;
   const int Kp = S * Fmt<FMT>::kStepK;  // staged row: whole steps, zeros past K
-  const int pitch = stage_pitch(M, Kp);
+  const int pitch = stage_pitch(M, Kp, kXsBytes);
   const int P = items * S;
   const int p0 = (wave * P) >> kFineWaveShift, p1 = ((wave + 1) * P) >> kFineWaveShift;
   const int T = FUSED ? (Kp + 255) >> 8 : (Kp + 1023) >> 10;  // tiles cover whole staged rows
@@ -1814,7 +1857,7 @@ int gemv_plan(GemvDesc *descs, int count, std::vector<GemvBlock> &blocks,
   // the spread staging when every problem's rows fit it
   bool spread = !chunked && fmt == UG_W_PACK5 && mb == 1;
   for (int i = 0; i < count && spread; ++i)
-    if (!stages_spread(descs[i].M, descs[i].K)) spread = false;
+    if (!stages_spread(descs[i].M, descs[i].K, descs[i].x != nullptr)) spread = false;
   return (spread ? 8192 : 0) + (chunked ? 2048 : 0) + 16 * fmt + mb;
 }
 
@@ -1833,7 +1876,9 @@ void fine_xcd_order(std::vector<FineBlock> &fine) {
 }
 
 bool gemv_stages_x(int wfmt, int64_t M, int64_t K) {
-  return K <= UG_MAX_K && M <= 64 && stages_x(wfmt, (int)M, (int)K);
+  // (the documented limit for activations quantized in the launch: 64 KB of
+  // staged rows, inside the stream split's larger area)
+  return K <= UG_MAX_K && M <= 64 && (int64_t)M * staged_kp(wfmt, mb_of((int)M), (int)K) <= kXsBytes;
 }
 
 hipError_t launch_gemv_grouped(const GemvDesc *plan_dev, const void *table, int32_t count,

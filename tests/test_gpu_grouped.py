@@ -185,16 +185,16 @@ def test_fine_variants(dev, ci):
 
 
 # (wfmt, M, list of (N, K)): groups with a problem whose activation rows do
-# not fit the 64 KB staging area, so the launch stages them chunk by chunk
+# not fit the stream split's 80 KB staging area, so the launch stages them chunk by chunk
 # (plan.info.variant bit 11); every row class and both weight formats, ragged
 # N and K, a staged problem in the same launch.
 CHUNKED = [
-    (ug.UG_W_PACK5, 1, [(300, 70001), (100, 640)]),
+    (ug.UG_W_PACK5, 1, [(300, 90001), (100, 640)]),
     (ug.UG_W_PACK5, 16, [(777, 6912), (50, 333)]),
     (ug.UG_W_PACK5, 17, [(600, 5000), (33, 4321)]),
     (ug.UG_W_PACK5, 64, [(513, 2560), (40, 1283)]),
-    (ug.UG_W_I8, 16, [(300, 5000)]),
-    (ug.UG_W_I8, 64, [(200, 1100), (31, 77)]),
+    (ug.UG_W_I8, 16, [(300, 5200)]),
+    (ug.UG_W_I8, 64, [(200, 1400), (31, 77)]),
 ]
 
 
@@ -226,18 +226,21 @@ def test_chunked_parity(dev, ci):
 # (M, list of (N, K), fused, spread): stream-split groups (more 16-row
 # pieces than the fine split takes).  Five trits per byte at M <= 16 take
 # the spread staging (each packed byte's five activations in 8 staged bytes,
-# plan.info.variant bit 13) when every problem's K-order and spread rows fit
-# the 64 KB staging area together; otherwise the permuted staging.  Ragged
-# K (tail bytes with fewer than five trits), ragged N, fp32 activations
-# quantized in the launch or x_q given.
+# plan.info.variant bit 13) when every problem's staged rows fit the 80 KB
+# staging area: the spread rows alone when x_q is given, the K-order rows
+# and the spread rows when the launch quantizes fp32 activations; otherwise
+# the permuted staging.  Ragged K (tail bytes with fewer than five trits),
+# ragged N, fp32 activations quantized in the launch or x_q given.
 SPREAD = [
     (1, [(6912, 2560)] * 4 + [(2560, 6913), (77, 5), (300, 81)], False, True),
     (1, [(6912, 2560)] * 4 + [(2560, 6912), (513, 7)], True, True),
     (2, [(6912, 2560)] * 5 + [(100, 1001)], False, True),
     (3, [(6912, 2560)] * 5 + [(64, 3000)], True, True),
     (16, [(131200, 640), (77, 333)], False, True),
-    (4, [(6912, 2560)] * 4 + [(2560, 6912)], False, False),  # 4 rows of 6912: too long to spread
-    (16, [(6912, 2560)] * 5, True, False),
+    (4, [(6912, 2560)] * 4 + [(2560, 6912)], False, True),
+    (8, [(6912, 2560)] * 4 + [(2560, 6912)], False, False),  # 8 rows of 6912: too long to spread
+    (16, [(6912, 2560)] * 5 + [(33, 2557)], False, True),
+    (16, [(6912, 2560)] * 5, True, False),  # fused: K-order and spread rows do not both fit
 ]
 
 
