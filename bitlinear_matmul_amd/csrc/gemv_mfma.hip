@@ -943,7 +943,7 @@ struct ItemLoop {
 
 // ---------------------------------------------------------------------------
 // Chunked stream: for launches with problems whose activation rows do not
-// fit the staging area (x_q input; M * Kp > 64 KB), where the stream split
+// fit the staging area (x_q input; M * Kp > 80 KB), where the stream split
 // would read every activation fragment from memory once per piece.  Waves
 // take a problem's items in rounds (wave w: item i0 + w + 8 r); each round
 // walks K in chunks of CH steps.  The block stages a chunk's activations

@@ -241,10 +241,11 @@ ug_status ug_bitlinear_gemv(const int8_t *xq, int64_t ldx, const float *s,
  * UG_ERR_UNSUPPORTED.  Kp = S * U * ceil(ceil(B / 64) / U) with B the packed
  * row length (ceil(K/5) for UG_W_PACK5, K for UG_W_I8), S = 320 (UG_W_PACK5)
  * or 64 (UG_W_I8), and U the steps per unit of the row class: UG_W_PACK5
- * U = 2, 2, 1 for M <= 16, 17..32, 33..64; UG_W_I8 U = 4, 4, 2.  A group
- * in which some problem's x_q rows do not fit that area (given as x_q) runs
- * a kernel that takes x_q only; such a group cannot also hold a problem
- * with x != NULL: UG_ERR_UNSUPPORTED (launch those separately).  Weights of
+ * U = 2, 2, 1 for M <= 16, 17..32, 33..64; UG_W_I8 U = 4, 4, 2.  Rows
+ * given as x_q may take up to 80 KB (M * Kp <= 81920); a group in which
+ * some problem's x_q rows do not fit that either runs a kernel that takes
+ * x_q only; such a group cannot also hold a problem with x != NULL:
+ * UG_ERR_UNSUPPORTED (launch those separately).  Weights of
  * N * ldw >= 2^31 bytes or
  * activations of M * ldxq >= 2^31 bytes are UG_ERR_UNSUPPORTED (32-bit
  * offsets), here and in ug_bitlinear_gemv.
