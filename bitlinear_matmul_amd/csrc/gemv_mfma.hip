@@ -25,12 +25,12 @@
 //   every MFMA adds products of matching K positions.
 //   Stream split with one 16-row activation block (when the rows fit the
 //   stream split's 80 KB staging area; given x_q, the spread rows are built
-//   straight from it): spread staging instead.  Each packed byte's five activations take 8
-//   staged bytes [x0 x1 x2 x3 x4 0 0 0], and B operand j is the two wide
-//   table entries of bytes 2j and 2j+1 as they come from LDS (t0..t3, then
-//   t4 in all four bytes, three of which meet zero activations): 8 MFMAs
-//   per 16 weight bytes instead of 5, but 16 instead of ~48 vector
-//   instructions, and no register moves, per 16 bytes.
+//   straight from it): spread staging instead.  Each packed byte's five
+//   activations take 8 staged bytes [x0 x1 x2 x3 x4 0 0 0], and B operand
+//   j is the two wide table entries of bytes 2j and 2j+1 as they come from
+//   LDS (t0..t3, then t4 in all four bytes, three of which meet zero
+//   activations): 8 MFMAs per 16 weight bytes instead of 5, but 16 instead
+//   of ~48 vector instructions, and no register moves, per 16 bytes.
 //   The table fills 64 KB: wide (t0..t3, then t4 in all four bytes), 32
 //   replicas of each 8-byte entry (code e, replica r at byte e * 256 + 8 r),
 //   lane l reads replica l % 32, and each half wave's 32 eight-byte reads
@@ -41,8 +41,8 @@
 // Work: one block of 8 waves per CU.  Two ways to split a launch:
 //   stream: a block takes a range of items (32 weight rows over the whole
 //     K); each wave walks whole items unit by unit (SC steps), keeping the
-//     weights of the next two units in flight.  For groups with megabytes of
-//     weights per CU.
+//     weights of the next two units (spread staging: the next one) in
+//     flight.  For groups with megabytes of weights per CU.
 //   fine: a block takes up to 16 items of 16 rows of one problem, and its
 //     waves split the (item, step) pieces evenly, so every wave issues all
 //     its weight loads at once and the K steps of one item run on several
@@ -1191,8 +1191,8 @@ __device__ __forceinline__ void stream_problem(SmemS<FMT> &sh, const GemvDesc &d
   // (spread rows after the K-order rows when the launch quantizes them)
   const int sbase = SPREAD && d.x ? spread_base(d.M, pitch) : 0;
   const int spitch = SPREAD ? spread_pitch(d.M, Kp) : 0;
-  // (the set-up's loads leave before the weights': two units of weights
-  // stay in flight while the block sets up)
+  // (the set-up's loads leave before the weights': the first units of
+  // weights stay in flight while the block sets up)
   constexpr int NQ = MB <= 2 && !SPREAD ? 8 : 0;
   PreLoads<NQ> pl;
   pre_issue<FMT>(d, staged, Kp, first, pl);
