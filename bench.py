@@ -154,15 +154,15 @@ TRAFFIC = {
     # it was taken on are unchanged.
     # profiles/gemv_fine_grouped_decode_stack.md: 1772.2 KiB / 146.4 KiB
     "decode_stack": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                              "9bf1a05297d7cf16b458722a88b74d775297546e886a98f2fe6efb5665e9d4e2",
+                              "5a7201909a6c70fc24447ce66b28b5bb130889ea0c88c05aeb51149d3e4516d8",
                               "bitlinear_matmul_amd/csrc/api.hip":
                               "fc7393bcd0906b1442f9491311fb3f3f27b63ac92f6563fd8603fae300f9762c"},
-                         bytes_per_launch=3779026),
+                         bytes_per_launch=3779031),
     # profiles/gemv_stream_grouped_sweep_m1.md: M=1 2560->6912, 37 problems per
-    # launch, spread staging: 64107.3 KiB / 190.8 KiB
+    # launch, spread staging: 64107.3 KiB / 191.3 KiB
     "sweep": dict(src={"bitlinear_matmul_amd/csrc/gemv_mfma.hip":
-                       "9bf1a05297d7cf16b458722a88b74d775297546e886a98f2fe6efb5665e9d4e2"},
-                  bytes_per_launch=131470018),
+                       "5a7201909a6c70fc24447ce66b28b5bb130889ea0c88c05aeb51149d3e4516d8"},
+                  bytes_per_launch=131466773),
     # profiles/gemm_i8_large_prefill.md: mean of the two shapes' launches
     "prefill": dict(src={"bitlinear_matmul_amd/csrc/gemm.hip":
                          "02b27e9db0529ba1b218003a0d600a96eb02f97bdc7bbbc8ef0ed0e7862fabf3"},
