@@ -396,6 +396,12 @@ def run_decode_stack(args, torch, ug, inputs):
         torch.cuda.empty_cache()
         out["backward"] = measure_backward(torch, ug)
         torch.cuda.empty_cache()
+        # each HBM-bound point against a plain read of its algorithmic bytes
+        attach_plain_read(torch, ug, out["roofline"], out["roofline"]["median_launch_us"])
+        for k in ("stream_m1", "pack", "requant_pack5", "attention_decode", "sampler"):
+            r = out[k]["roofline"]
+            attach_plain_read(torch, ug, r, r["median_launch_us"])
+        torch.cuda.empty_cache()
         # the matrix-core kernels against what the matrix cores sustain
         ms = out["mfma_sustained"]
         out["prefill_gemm"]["roofline"]["frac_of_sustained"] = (
@@ -557,6 +563,37 @@ def measure_hbm_read(torch, ug):
     log("read rate", res)
     del buf, sink
     return res
+
+
+def plain_read_us(torch, ug, nbytes):
+    """Median time (us, over STAT_LAUNCHES cold calls) of a plain streaming
+    read of nbytes (ug_hbm_read_probe, one block of four waves per CU, the
+    fastest configuration of the read-rate point), regions cycled over
+    >= 2 GiB: what moving a point's algorithmic bytes costs when nothing
+    else is done, fixed launch cost included."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    n = max(16, int(nbytes) // 16 * 16)
+    regions = max(2, COLD_BYTES // n + 1)
+    buf = torch.ones(regions * n // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4 * blocks, dtype=torch.int32, device=dev)
+    views = [buf[i * (n // 4):(i + 1) * (n // 4)] for i in range(regions)]
+    for i in range(2):
+        ug.ug_hbm_read_probe(views[i], blocks, sink, walk=0)
+    med = launch_stats(torch, lambda i: ug.ug_hbm_read_probe(views[(i + 2) % regions], blocks,
+                                                             sink, walk=0), stream)[0]
+    del views, buf, sink
+    torch.cuda.empty_cache()
+    return med
+
+
+def attach_plain_read(torch, ug, roof, launch_us):
+    """Adds to an HBM-bound point's roofline the time of a plain read of its
+    algorithmic bytes and the ratio of the two (both single cold calls)."""
+    us = plain_read_us(torch, ug, roof["alg_bytes_per_launch"])
+    roof["plain_read_same_bytes_us"] = us
+    roof["frac_of_plain_read"] = us / launch_us
 
 
 def measure_mfma_sustained(torch, ug, iters=4000):
